@@ -1,0 +1,316 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``check_*`` function takes a loaded oracle library handle and raises
+``AssertionError`` on disagreement.  ``test_oracle_pins.py`` runs them on the
+real oracle; ``test_oracle_mutants.py`` runs them on copies of the oracle with
+a planted mistake and requires that at least one check fails for each.
+
+What pins what:
+
+* wire rounding        -- exhaustive over all 2^32 binary32 patterns against
+                          torch's CPU bfloat16 / float16 conversions (IEEE
+                          round-to-nearest-even), numpy's float16 conversion on
+                          a sample, and the hand-worked rows of
+                          ``golden/worked_examples.txt``;
+* widening             -- exhaustive over all 2^16 patterns against torch and
+                          numpy;
+* each binary32 add    -- a theorem: for binary32 a, b, RN32(a+b) equals
+                          float32(float64(a) + float64(b)) because binary64 has
+                          at least 2p+2 significand bits (double rounding is
+                          innocuous, Figueroa 1995);
+* the ordered fold     -- numpy's sequential float32 accumulation, the fp64
+                          route above, brute force over every ordered tuple of
+                          a grid of edge values, and the hand-worked rows;
+* the whole reduce     -- a closed form: partials k * 2^-6 with |k| <= 127 are
+                          exact in every wire type and every partial sum for
+                          R <= 16 is exact in binary32, so the result is
+                          (sum k) * 2^-6, computed with integers.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+F32, F16, BF16 = oracle.F32, oracle.F16, oracle.BF16
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.txt")
+WIRE_BY_NAME = {"f32": F32, "f16": F16, "bf16": BF16}
+
+
+# --- independent routes built only from library routines ---------------------
+
+def lib_round_bits(x: np.ndarray, wire: int) -> np.ndarray:
+    """Wire pattern of each float32 via torch's CPU conversion (uint16)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if wire == BF16:
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if wire == F16:
+        return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(wire)
+
+
+def lib_wire_value(x: np.ndarray, wire: int) -> np.ndarray:
+    """float32 value of round_W(x), via torch's conversions both ways."""
+    if wire == F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    dt = torch.bfloat16 if wire == BF16 else torch.float16
+    return t.to(dt).to(torch.float32).numpy()
+
+
+def fp64_route_fold(ws: list[np.ndarray]) -> np.ndarray:
+    """Left fold where each binary32 add is done as float32(float64 + float64)."""
+    acc = ws[0].astype(np.float32)
+    for w in ws[1:]:
+        acc = (acc.astype(np.float64) + w.astype(np.float64)).astype(np.float32)
+    return acc
+
+
+def is_nan16(h: np.ndarray, wire: int) -> np.ndarray:
+    h = h.astype(np.uint32)
+    if wire == BF16:
+        return ((h & 0x7F80) == 0x7F80) & ((h & 0x007F) != 0)
+    return ((h & 0x7C00) == 0x7C00) & ((h & 0x03FF) != 0)
+
+
+def assert_same_f32(got: np.ndarray, want: np.ndarray, what: str) -> None:
+    """Bit equality of float32 arrays, NaN compared only as 'is a NaN'."""
+    got = np.ascontiguousarray(got, dtype=np.float32)
+    want = np.ascontiguousarray(want, dtype=np.float32)
+    gn, wn = np.isnan(got), np.isnan(want)
+    if not np.array_equal(gn, wn):
+        i = int(np.flatnonzero(gn != wn)[0])
+        raise AssertionError(f"{what}: NaN mismatch at {i}: got {got[i]!r} want {want[i]!r}")
+    gb = got.view(np.uint32)[~gn]
+    wb = want.view(np.uint32)[~wn]
+    if not np.array_equal(gb, wb):
+        j = int(np.flatnonzero(gb != wb)[0])
+        raise AssertionError(f"{what}: bits differ (first non-NaN mismatch {gb[j]:#010x} vs {wb[j]:#010x})")
+
+
+# --- golden worked examples --------------------------------------------------
+
+def load_golden() -> list[dict]:
+    rows = []
+    with open(GOLDEN) as fh:
+        for line in fh:
+            body = line.split("#", 1)[0].strip()
+            if not body:
+                continue
+            parts = body.split()
+            rid, op, wire, inputs, expected = parts[0], parts[1], parts[2], parts[3], parts[4]
+            rows.append({
+                "id": rid, "op": op, "wire": WIRE_BY_NAME[wire],
+                "inputs": [int(h, 16) for h in inputs.split(",")],
+                "expected": None if expected == "NAN" else int(expected, 16),
+            })
+    return rows
+
+
+def check_golden(lib) -> None:
+    rows = load_golden()
+    assert len(rows) >= 25
+    for row in rows:
+        x = np.array(row["inputs"], dtype=np.uint32)
+        if row["op"] == "round":
+            fn = oracle.round_bf16_bits if row["wire"] == BF16 else oracle.round_f16_bits
+            got = int(fn(x, lib)[0])
+            if row["expected"] is None:
+                assert bool(is_nan16(np.array([got]), row["wire"])[0]), row["id"]
+            else:
+                assert got == row["expected"], f"{row['id']}: {got:#06x} != {row['expected']:#06x}"
+        else:
+            srcs = [x[i:i + 1].view(np.float32) for i in range(len(x))]
+            got = oracle.reduce(srcs, row["wire"], lib=lib)[0, 0]
+            if row["expected"] is None:
+                assert np.isnan(got), row["id"]
+            else:
+                gb = int(np.array([got], dtype=np.float32).view(np.uint32)[0])
+                assert gb == row["expected"], f"{row['id']}: {gb:#010x} != {row['expected']:#010x}"
+
+
+# --- conversions -------------------------------------------------------------
+
+def _round_chunk_ok(lib, wire: int, start: int, size: int) -> None:
+    x = np.arange(start, start + size, dtype=np.uint64).astype(np.uint32)
+    fn = oracle.round_bf16_bits if wire == BF16 else oracle.round_f16_bits
+    got = fn(x, lib)
+    want = lib_round_bits(x.view(np.float32), wire)
+    gn, wn = is_nan16(got, wire), is_nan16(want, wire)
+    if not np.array_equal(gn, wn):
+        i = int(np.flatnonzero(gn != wn)[0])
+        raise AssertionError(f"wire {wire}: NaN class differs at input {int(x[i]):#010x}")
+    bad = (got != want) & ~gn
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"wire {wire}: round({int(x[i]):#010x}) = {int(got[i]):#06x}, "
+                             f"library gives {int(want[i]):#06x}")
+
+
+def check_round_exhaustive(lib, wire: int, chunk_log2: int = 22, workers: int = 8) -> None:
+    """All 2^32 binary32 patterns against torch's conversion."""
+    size = 1 << chunk_log2
+    starts = range(0, 1 << 32, size)
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)            # parallelism comes from the chunk pool
+    try:
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(lambda s: _round_chunk_ok(lib, wire, s, size), starts))
+    finally:
+        torch.set_num_threads(threads)
+
+
+def check_round_sampled(lib, wire: int, n: int = 1 << 20, seed: int = 7) -> None:
+    """Random patterns plus the edge grid (cheap form of the exhaustive pin)."""
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32),
+                        workloads.special_values().view(np.uint32),
+                        workloads.nan_values().view(np.uint32)])
+    fn = oracle.round_bf16_bits if wire == BF16 else oracle.round_f16_bits
+    got = fn(x, lib)
+    want = lib_round_bits(x.view(np.float32), wire)
+    gn, wn = is_nan16(got, wire), is_nan16(want, wire)
+    assert np.array_equal(gn, wn), f"wire {wire}: NaN class differs"
+    bad = (got != want) & ~gn
+    assert not bad.any(), f"wire {wire}: {int(bad.sum())} rounding mismatches"
+
+
+def check_round_f16_numpy_sample(lib, n: int = 1 << 22, seed: int = 11) -> None:
+    """Second witness for float16: numpy's own conversion on a random sample."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    got = oracle.round_f16_bits(x, lib)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = x.view(np.float32).astype(np.float16).view(np.uint16)
+    gn, wn = is_nan16(got, F16), is_nan16(want, F16)
+    assert np.array_equal(gn, wn)
+    assert np.array_equal(got[~gn], want[~wn])
+
+
+def check_widen_exhaustive(lib) -> None:
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got_b = oracle.widen_bf16_bits(h, lib).view(np.float32)
+    want_b = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    assert_same_f32(got_b, want_b, "widen bf16 vs torch")
+    got_h = oracle.widen_f16_bits(h, lib).view(np.float32)
+    want_h = h.view(np.float16).astype(np.float32)
+    assert_same_f32(got_h, want_h, "widen f16 vs numpy")
+    want_h2 = torch.from_numpy(h.view(np.int16).copy()).view(torch.float16).to(torch.float32).numpy()
+    assert_same_f32(got_h, want_h2, "widen f16 vs torch")
+
+
+# --- additions and folds -----------------------------------------------------
+
+def _edge_grid() -> np.ndarray:
+    return np.concatenate([workloads.special_values(), workloads.nan_values()[:1]])
+
+
+def check_add_theorem(lib, n: int = 1 << 20, seed: int = 3) -> None:
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    b = (a.view(np.uint32) ^ rng.integers(0, 1 << 12, n, dtype=np.uint32)).view(np.float32)
+    # near-cancellations, random far-apart pairs and the full edge grid x grid
+    g = _edge_grid()
+    ga, gb = np.meshgrid(g, g, indexing="ij")
+    a = np.concatenate([a, -b, ga.ravel()])
+    b = np.concatenate([b, rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32).view(np.float32),
+                        gb.ravel()])
+    got = oracle.add_f32(a, b, lib)
+    with np.errstate(all="ignore"):
+        want64 = (a.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+        want32 = a + b
+    assert_same_f32(got, want64, "add vs fp64 route")
+    assert_same_f32(got, want32, "add vs numpy float32")
+
+
+def check_fold_bruteforce(lib, R: int, grid: np.ndarray | None = None) -> None:
+    """Every ordered R-tuple of the edge grid, every wire type, fp64 route."""
+    g = _edge_grid() if grid is None else grid
+    cols = [c.ravel() for c in np.meshgrid(*([g] * R), indexing="ij")]
+    for wire in (F32, BF16, F16):
+        got = oracle.reduce(cols, wire, lib=lib)[0]
+        with np.errstate(all="ignore"):
+            want = fp64_route_fold([lib_wire_value(c, wire) for c in cols])
+        assert_same_f32(got, want, f"fold R={R} wire={wire}")
+
+
+def check_ordered_sum(lib, R: int = 5, n: int = 1 << 16, seed: int = 5) -> None:
+    """fp32 wire: the result is the plain left-to-right float32 sum."""
+    srcs = workloads.random_partials(900 + seed, 0, R, n, dist="wide")
+    got = oracle.reduce(srcs, F32, lib=lib)[0]
+    acc = srcs[0].copy()
+    with np.errstate(all="ignore"):
+        for s in srcs[1:]:
+            acc += s
+    assert_same_f32(got, acc, "fp32-wire ordered sum")
+    # the same reduce through any narrower wire equals the sum of the library-rounded partials
+    for wire in (BF16, F16):
+        got_w = oracle.reduce(srcs, wire, lib=lib)[0]
+        ws = [lib_wire_value(s, wire) for s in srcs]
+        acc = ws[0].copy()
+        with np.errstate(all="ignore"):
+            for w in ws[1:]:
+                acc += w
+        assert_same_f32(got_w, acc, f"wire {wire} ordered sum")
+
+
+def check_closed_form(lib, seed: int = 17) -> None:
+    """k * 2^-6 partials: result must be (sum k) * 2^-6 exactly, any wire, any R."""
+    rng = np.random.default_rng(seed)
+    for R in (2, 3, 4, 7, 8, 16):
+        n = 4099
+        ks = [rng.integers(-127, 128, n) for _ in range(R)]
+        srcs = [(k.astype(np.float32) * np.float32(2.0 ** -6)) for k in ks]
+        total = np.sum(ks, axis=0)                       # integer arithmetic
+        want = total.astype(np.float32) * np.float32(2.0 ** -6)
+        for wire in (F32, BF16, F16):
+            got = oracle.reduce(srcs, wire, n_dst=2, lib=lib)
+            assert_same_f32(got[0], want, f"closed form R={R} wire={wire}")
+            assert np.array_equal(got[0].view(np.uint32), got[1].view(np.uint32))
+            if wire != F32:
+                pre = [lib_round_bits(s, wire) for s in srcs]
+                got_w = oracle.reduce(pre, wire, src_type=wire, lib=lib)[0]
+                assert_same_f32(got_w, want, f"closed form (wire-typed srcs) R={R} wire={wire}")
+
+
+def check_order_sensitivity(lib) -> None:
+    """The fold is taken in rank order: a reordered sum must differ where rounding bites."""
+    a = np.array([2.0 ** 24], dtype=np.float32)
+    one = np.array([1.0], dtype=np.float32)
+    fwd = oracle.reduce([a, one, one], F32, lib=lib)[0, 0]
+    rev = oracle.reduce([one, one, a], F32, lib=lib)[0, 0]
+    assert fwd == np.float32(2.0 ** 24) and rev == np.float32(2.0 ** 24 + 2)
+
+
+def check_broadcast_and_wire_srcs(lib, seed: int = 23) -> None:
+    """Every destination row is identical; pre-rounded wire-typed sources give the same bytes."""
+    srcs = workloads.random_partials(950, seed, 6, 3001, dist="wide")
+    for wire in (F32, BF16, F16):
+        out = oracle.reduce(srcs, wire, n_dst=6, lib=lib)
+        for d in range(1, 6):
+            assert np.array_equal(out[0].view(np.uint32), out[d].view(np.uint32))
+        if wire != F32:
+            pre = [lib_round_bits(s, wire) for s in srcs]
+            out_w = oracle.reduce(pre, wire, src_type=wire, lib=lib)[0]
+            assert_same_f32(out_w, out[0], f"wire-typed sources wire={wire}")
+
+
+def cheap_checks():
+    """Checks fast enough to run against every planted-mistake build."""
+    return [
+        ("golden", check_golden),
+        ("round_bf16_sampled", lambda lib: check_round_sampled(lib, BF16, n=1 << 18)),
+        ("round_f16_sampled", lambda lib: check_round_sampled(lib, F16, n=1 << 18)),
+        ("widen", check_widen_exhaustive),
+        ("add", lambda lib: check_add_theorem(lib, n=1 << 14)),
+        ("fold_R2", lambda lib: check_fold_bruteforce(lib, 2)),
+        ("ordered_sum", check_ordered_sum),
+        ("closed_form", check_closed_form),
+        ("order", check_order_sensitivity),
+        ("broadcast", check_broadcast_and_wire_srcs),
+    ]

@@ -1,0 +1,78 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies ``oracle/ar_oracle.c`` with one plausible mistake written in
+(a dropped rank, a reversed order, a wrong tie rule, an off-by-one shift, a lost
+sign, ...), builds it into a temporary directory and runs the cheap pins
+against it.  The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_checks as oc
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ar_oracle.c")
+
+# (name, [(exact text in ar_oracle.c, replacement), ...])
+MUTANTS = [
+    ("drop_last_rank", [("for (int r = 1; r < R; ++r)", "for (int r = 1; r < R - 1; ++r)")]),
+    ("fold_from_plus_zero", [
+        ("float acc = orc_wire_value(srcs[0], i, src_type, wire_type);", "float acc = 0.0f;"),
+        ("for (int r = 1; r < R; ++r)", "for (int r = 0; r < R; ++r)")]),
+    ("reverse_rank_order", [
+        ("float acc = orc_wire_value(srcs[0], i, src_type, wire_type);",
+         "float acc = orc_wire_value(srcs[R - 1], i, src_type, wire_type);"),
+        ("const float w = orc_wire_value(srcs[r], i, src_type, wire_type);",
+         "const float w = orc_wire_value(srcs[R - 1 - r], i, src_type, wire_type);")]),
+    ("local_partial_not_rounded", [
+        ("float acc = orc_wire_value(srcs[0], i, src_type, wire_type);",
+         "float acc = src_type == ORC_F32 ? ((const float *)srcs[0])[i]"
+         " : orc_wire_value(srcs[0], i, src_type, wire_type);")]),
+    ("accumulate_in_double", [
+        ("float acc = orc_wire_value", "double acc = orc_wire_value")]),
+    ("bf16_truncates", [
+        ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) {", "if (0) {")]),
+    ("bf16_ties_away", [
+        ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")]),
+    ("bf16_nan_to_inf", [
+        ("if (exp_field == 0x7F800000u && frac != 0) {", "if (0) {")]),
+    ("f16_ties_away", [
+        ("(dropped == 0x1000u && (kept & 1u))", "(dropped == 0x1000u)")]),
+    ("f16_subnormal_shift_off_by_one", [("int s = -(E + 1);", "int s = -E;")]),
+    ("f16_overflow_threshold", [("if (E > 15) {", "if (E > 16) {")]),
+    ("f16_lost_sign", [("const uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);",
+                        "const uint16_t sign = 0;")]),
+    ("f16_subnormal_ties_away", [
+        ("(dropped == half && (kept & 1ull))", "(dropped == half)")]),
+    ("widen_f16_bias", [("((uint32_t)(e + 112) << 23)", "((uint32_t)(e + 111) << 23)")]),
+    ("widen_f16_subnormal_as_zero", [("if (m == 0) {\n            return sign;", "if (1) {\n            return sign;")]),
+    ("broadcast_only_first", [("for (int d = 0; d < n_dst; ++d)", "for (int d = 0; d < 1; ++d)")]),
+    ("add_keeps_ftz", [("_mm_setcsr(saved & ~((1u << 15) | (1u << 6)));",
+                        "_mm_setcsr(saved | (1u << 15) | (1u << 6));")]),
+]
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, edits):
+    text = open(SRC).read()
+    for old, new in edits:
+        assert text.count(old) >= 1, f"anchor for {name} not found in the oracle source: {old!r}"
+        text = text.replace(old, new)
+    src = tmp_path / f"mutant_{name}.c"
+    src.write_text(text)
+    so = tmp_path / f"libmutant_{name}.so"
+    oracle.build(str(src), str(so))
+    lib = oracle.load(str(so))
+    caught = []
+    for check_name, check in oc.cheap_checks():
+        try:
+            check(lib)
+        except AssertionError:
+            caught.append(check_name)
+    assert caught, f"no pin caught the planted mistake {name!r}"
+
+
+def test_real_oracle_passes_cheap_checks(orc):
+    for _, check in oc.cheap_checks():
+        check(orc)
