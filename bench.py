@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X mixed-precision partial-sum reduce (one GPU).
+
+A step is one ``ar_reduce`` call over one batch of synthetic input: the
+prefill-shaped reduce of R=2 fp32 partials [2048 x 4096] through a bf16 wire
+into an fp32 destination, CHUNKED schedule with 4 MiB chunks (validation,
+plan, load, cast-to-wire, ordered fp32 fold, store -- all in one launch).
+Inputs are resident in HBM before the timed region and rotate over several
+sets so that the 256 MiB Infinity Cache cannot serve them.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S]
+                    [--no-cpu-baseline] [--no-decode] [--extras]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_prefill_bf16.json")
+KERNEL_SRC = os.path.join(ROOT, "mixed_precision_partial_amd", "csrc", "ar_kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(algo_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when absent or taken on a different kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--sets", type=int, default=8, help="rotated input/output sets (>= 6 defeats the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--extras", action="store_true", help="also time the other schedules (stderr lines)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the reduce is run with every "
+              "rank simulated on a single MI355X, so there is no multi-GPU figure", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mixed_precision_partial_amd as ar
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    ar.load_library()   # fails loudly when the HIP library was not built
+    w = wl.WORKLOADS["prefill_bf16"]
+    R, n = w.R, w.n
+    S = max(1, args.sets)
+
+    log(f"generating {S} sets of R={R} x n={n} fp32 partials")
+    host_sets = [wl.partials(w, s) for s in range(S)]
+    dev_src = [[torch.from_numpy(p).cuda() for p in srcs] for srcs in host_sets]
+    dev_dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(S)]
+    torch.cuda.synchronize()
+
+    ctx = ar.ar_init(0)
+    mode = ar.AR_MODE_CHUNKED
+    rc, plan = ar.ar_plan_query([dev_dst[0]], dev_src[0], n, ar.AR_F32, w.wire, mode)
+    assert rc == ar.AR_OK
+    algo_bytes = int(plan.algo_bytes)
+    stream = torch.cuda.current_stream()
+
+    def step(k: int) -> None:
+        s = k % S
+        ar.ar_reduce(ctx, [dev_dst[s]], dev_src[s], n, ar.AR_F32, w.wire, mode, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(k)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{ms_per_step * 1e3:.2f} us/step, {gbs:.1f} GB/s effective (wall {wall:.3f} s)")
+
+    # parity of the timed path on set 0 against the oracle (outside the timed region)
+    parity = None
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        step(0)
+        torch.cuda.synchronize()
+        got = dev_dst[0].cpu().numpy()
+        log("oracle on one full set (parity of the timed path)")
+        t = time.perf_counter()
+        want = oracle.reduce(host_sets[0], w.wire)[0]
+        one = time.perf_counter() - t
+        parity = "bit-exact" if np.array_equal(got.view(np.uint32), want.view(np.uint32)) else "MISMATCH"
+        reps = max(1, int(args.cpu_seconds / max(one, 1e-3)))
+        log(f"cpu baseline: oracle x{reps} (one call {one:.3f} s)")
+        t = time.perf_counter()
+        for _ in range(reps):
+            oracle.reduce(host_sets[0], w.wire)
+        cpu_s = time.perf_counter() - t
+        cpu_baseline = {
+            "value": round(algo_bytes * reps / cpu_s / 1e9, 3),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps + 1} full calls of the same 2048x4096 R=2 bf16-wire reduce "
+                      f"({cpu_s + one:.1f} s, single-threaded scalar C oracle)",
+        }
+
+    extras = {}
+    if not args.no_decode:
+        extras["decode_bf16"] = decode_latency(torch, ar, wl)
+    if args.extras:
+        extras.update(other_schedules(torch, ar, wl))
+
+    traffic = measured_traffic(algo_bytes)
+    torch.cuda.synchronize()
+    ar.ar_free(ctx)
+
+    result = {
+        "metric": "effective GB/s and % of HBM peak (prefill reduce); us/call (decode-size)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill reduce: R=2 fp32 partials [2048x4096] N(0,1)+0.1% x100 outliers, "
+                        "bf16 wire, fp32 dst, CHUNKED 4 MiB chunks",
+            "R": R, "n": n, "wire": "bf16", "dst": "f32", "rotated_sets": S,
+            "algo_bytes_per_step": algo_bytes,
+        },
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu_baseline,
+        "parity": parity,
+        "extras": extras,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def decode_latency(torch, ar, wl):
+    """10,000 sequential single-shot calls on fresh seeded data (all pre-staged in HBM)."""
+    w = wl.WORKLOADS["decode_bf16"]
+    calls, n, R = w.calls, w.n, w.R
+    log(f"decode: staging {calls} calls of R={R} x n={n}")
+    host = np.empty((calls, R, n), dtype=np.float32)
+    for c in range(calls):
+        for r, p in enumerate(wl.partials(w, c)):
+            host[c, r] = p
+    dev = torch.from_numpy(host).cuda()
+    out = torch.empty((calls, n), dtype=torch.float32, device="cuda")
+    ctx = ar.ar_init(0)
+    stream = torch.cuda.current_stream()
+    bi, bo = dev.data_ptr(), out.data_ptr()
+    srcs = [[bi + (c * R + r) * n * 4 for r in range(R)] for c in range(calls)]
+    dsts = [[bo + c * n * 4] for c in range(calls)]
+
+    def call(c):
+        ar.ar_reduce(ctx, dsts[c], srcs[c], n, ar.AR_F32, w.wire, ar.AR_MODE_SINGLE_SHOT, stream=stream)
+
+    for c in range(200):
+        call(c)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for c in range(calls):
+        call(c)
+    end.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t0
+    us_async = start.elapsed_time(end) * 1e3 / calls
+    # per-call round trip: enqueue + stream synchronize, wall clock
+    lat = np.empty(2000)
+    for i in range(lat.size):
+        t = time.perf_counter()
+        call(i)
+        torch.cuda.synchronize()
+        lat[i] = (time.perf_counter() - t) * 1e6
+    ar.ar_free(ctx)
+    res = {
+        "us_per_call_async": round(us_async, 3),
+        "host_enqueue_us_per_call": round(host_s * 1e6 / calls, 3),
+        "us_per_call_sync_p50": round(float(np.percentile(lat, 50)), 2),
+        "us_per_call_sync_p99": round(float(np.percentile(lat, 99)), 2),
+        "calls": calls,
+    }
+    log(f"decode: {res}")
+    return res
+
+
+def other_schedules(torch, ar, wl):
+    """Broadcast-slice and R=8 shapes from HBM plus the host-staged mode (stderr + extras)."""
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    ctx = ar.ar_init(0)
+    w = wl.WORKLOADS["slice_bcast_f16"]
+    srcs = [torch.from_numpy(p).cuda() for p in wl.partials(w, 0)]
+    dsts = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.R)]
+    ms = timed(lambda: ar.ar_reduce(ctx, dsts, srcs, w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
+                                    stream=stream), 50)
+    b = 2 * w.R * w.n * 4
+    out["slice_bcast_f16"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"slice_bcast_f16: {out['slice_bcast_f16']}")
+    del srcs, dsts
+
+    w = wl.WORKLOADS["host_staged_bf16"]
+    parts = wl.partials(w, 0)
+    srcs32 = [torch.from_numpy(p).cuda() for p in parts]
+    dst = torch.empty(w.n, dtype=torch.float32, device="cuda")
+    ms = timed(lambda: ar.ar_reduce(ctx, [dst], srcs32, w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                    stream=stream), 20)
+    b = w.R * w.n * 4 + w.n * 4
+    out["r8_hbm_fp32_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"r8_hbm_fp32_src: {out['r8_hbm_fp32_src']}")
+    del srcs32
+    pre = [wl.as_wire_typed(p, w.wire) for p in parts]
+    srcs16 = [torch.from_numpy(p.view(np.int16)).cuda() for p in pre]
+    ms = timed(lambda: ar.ar_reduce(ctx, [dst], srcs16, w.n, ar.AR_F32, w.wire,
+                                    ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, stream=stream), 20)
+    b = w.R * w.n * 2 + w.n * 4
+    out["r8_hbm_bf16_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"r8_hbm_bf16_src: {out['r8_hbm_bf16_src']}")
+    del srcs16
+    pinned = []
+    for p in pre:
+        t = torch.empty(p.size, dtype=torch.int16, pin_memory=True)
+        t.copy_(torch.from_numpy(p.view(np.int16)))
+        pinned.append(t)
+    ms = timed(lambda: ar.ar_reduce(ctx, [dst], pinned, w.n, ar.AR_F32, w.wire,
+                                    ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
+    pcie_bytes = w.R * w.n * 2
+    # plain pinned H2D copy of the same byte count, for the achievable PCIe ceiling
+    big = torch.empty(pcie_bytes // 2, dtype=torch.int16, pin_memory=True)
+    dev_big = torch.empty_like(big, device="cuda")
+    ms_copy = timed(lambda: dev_big.copy_(big, non_blocking=True), 5)
+    out["host_staged_bf16"] = {"ms": round(ms, 3), "pcie_GB/s": round(pcie_bytes / ms / 1e6, 2),
+                               "h2d_copy_GB/s": round(pcie_bytes / ms_copy / 1e6, 2),
+                               "frac_of_h2d_copy": round(ms_copy / ms, 3)}
+    log(f"host_staged_bf16: {out['host_staged_bf16']}")
+    ar.ar_free(ctx)
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,187 @@
+/*
+ * ar.h -- C ABI of the MI355X (gfx950) mixed-precision partial-sum reduce.
+ *
+ * The operation: R partial activations (one per tensor-parallel rank) are
+ * summed element-wise into a binary32 result.  Every partial -- the
+ * receiving rank's own included -- is first rounded through a possibly
+ * narrower "wire" type, and the rounded values are added in binary32 in the
+ * fixed rank order 0, 1, ..., R-1, so every rank computes the same bits.
+ *
+ *   for 0 <= i < n, for every destination d:
+ *       w_r       = widen(round_W(src_r[i]))          r = 0 .. R-1
+ *       dst_d[i]  = ((w_0 + w_1) + w_2) + ... + w_{R-1}   (binary32, RNE)
+ *
+ * Passages this follows (page title, then the passage):
+ *   - "CUDA allreduce.cu" page (toy 0.8.0 diff of ggml-cuda/allreduce.cu):
+ *     the comment block "Chunked kernel AllReduce" (phase 1 casts the
+ *     caller-typed partial to the wire type; phase 3 rounds the local
+ *     partial through the same type and adds in float) and the comment on
+ *     the "Combined load-convert-add kernel".
+ *   - "Hexagon allreduce-ops.c" page (llama.cpp fork, ggml-hexagon/htp):
+ *     allreduce_thread_dma_1d (fixed-order sum s0+s1, then +s2 ..., and the
+ *     write of each block to every destination; each rank reduces its own
+ *     element range) and op_allreduce (rank-count checks, n_dsts).
+ *   - "llama.cpp commit log" page: the Vulkan comm hook commit (partials
+ *     narrowed to F16 before the host transfer and added into the fp32
+ *     result; a chunked pipeline for prefill and a single-shot path for
+ *     decode) and the SYCL tensor-parallel commit (BF16-compressed large
+ *     path, no per-call host synchronisation).
+ *
+ * All R ranks live on one GPU here: each rank's partial is a separate
+ * buffer, in HBM or (host-staged mode) in pinned host memory.
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: an ar_status code.  Nothing aborts the process.
+ *   - A call that fails validation enqueues no GPU work.
+ *   - ar_reduce is asynchronous: work is enqueued on `hip_stream` (a
+ *     hipStream_t, NULL = the null stream) and the call returns without
+ *     waiting.  No host synchronisation happens inside it.
+ *   - The caller owns every dst / src buffer; they must stay alive and
+ *     unmodified until the enqueued work completes in stream order.
+ *   - A context is not thread-safe: one host thread at a time per ar_ctx.
+ */
+#ifndef MPP_AR_H
+#define MPP_AR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque, library-owned state: device, internal copy stream and events,
+ * lazily allocated HBM scratch for host-staged mode. */
+typedef struct ar_ctx ar_ctx;
+
+/* Element types.  dst_type must be AR_F32 in this version. */
+typedef enum { AR_F32 = 0, AR_F16 = 1, AR_BF16 = 2 } ar_dtype;
+
+/* Schedules, in the low 8 bits of `mode`.
+ *   AR_MODE_AUTO         SINGLE_SHOT when n * sizeof(wire) is below the
+ *                        single-shot limit, CHUNKED otherwise; sources in
+ *                        pinned host memory select HOST_STAGED.
+ *   AR_MODE_SINGLE_SHOT  one low-latency launch for decode-sized vectors.
+ *   AR_MODE_CHUNKED      one bandwidth-bound launch over the whole tensor,
+ *                        work planned in chunks of `chunk_bytes` wire bytes
+ *                        per rank.
+ *   AR_MODE_RS_BCAST     per-rank slice schedule: simulated rank r reduces
+ *                        its own slice and writes it to all R destinations
+ *                        (n_dst = R; `dst` holds R pointers).
+ *   AR_MODE_HOST_STAGED  sources are pinned host buffers; chunks are copied
+ *                        to HBM scratch on an internal copy stream while the
+ *                        add kernel runs on `hip_stream`.
+ * The result bytes do not depend on the mode, the chunk size or the launch
+ * shape. */
+enum {
+    AR_MODE_AUTO        = 0,
+    AR_MODE_SINGLE_SHOT = 1,
+    AR_MODE_CHUNKED     = 2,
+    AR_MODE_RS_BCAST    = 3,
+    AR_MODE_HOST_STAGED = 4
+};
+#define AR_MODE_MASK 0xFFu
+/* Flag: the sources already hold wire_type values (a peer narrowed them),
+ * so round_W is the identity and each element is read at the wire width. */
+#define AR_SRC_WIRE 0x100u
+
+#define AR_MAX_RANKS 16
+
+typedef enum {
+    AR_OK              = 0,
+    AR_ERR_INVALID     = 1,  /* bad argument: see ar_reduce                */
+    AR_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    AR_ERR_NOMEM       = 3,  /* allocation failed                           */
+    AR_ERR_RUNTIME     = 4   /* a HIP runtime call failed                   */
+} ar_status;
+
+/* Optional tuning, read once by ar_init.  Zero fields take the defaults;
+ * environment variables AR_SINGLE_SHOT_MAX_BYTES, AR_CHUNK_BYTES,
+ * AR_HOST_CHUNK_BYTES and AR_HOST_SLOTS override the defaults when cfg is
+ * NULL or the field is zero. */
+typedef struct {
+    size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank; 0 -> 1 MiB */
+    size_t chunk_bytes;           /* CHUNKED / RS_BCAST plan unit, wire bytes per rank; 0 -> 4 MiB */
+    size_t host_chunk_bytes;      /* HOST_STAGED copy unit, source bytes per rank;
+                                     0 -> clamp(bytes/4, 512 KiB, 2 MiB) per call */
+    int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
+    int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
+    int    stream_kernel;         /* 0 auto, 1 register-staged, 2 LDS-staged */
+} ar_config;
+
+/* Create a context on HIP device `hip_device`.
+ *   out  : receives the context (set to NULL on failure).
+ *   cfg  : NULL for defaults (plus AR_* environment overrides).
+ * Errors: AR_ERR_INVALID (out NULL, device index out of range, negative or
+ *         inconsistent cfg fields), AR_ERR_RUNTIME (stream / event creation),
+ *         AR_ERR_NOMEM.  Nothing leaks on failure.
+ * The context makes `hip_device` current on the calling thread while it
+ * creates its resources and restores the previous device afterwards. */
+int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
+
+/* Enqueue one reduce.
+ *   dst       : array of n_dst pointers to binary32 buffers of n elements
+ *               (n_dst = R for AR_MODE_RS_BCAST, else 1); device memory of
+ *               the context's device.
+ *   srcs      : array of R pointers to the partials, n elements each, of
+ *               dst_type (default) or wire_type (with AR_SRC_WIRE).  Device
+ *               memory, or pinned host memory for AR_MODE_HOST_STAGED.
+ *   R         : 2 .. AR_MAX_RANKS.
+ *   n         : elements per partial; 0 is a no-op returning AR_OK.
+ *   dst_type  : AR_F32 (AR_F16 / AR_BF16 -> AR_ERR_UNSUPPORTED).
+ *   wire_type : AR_F32, AR_F16 or AR_BF16; not wider than dst_type.
+ *   mode      : AR_MODE_* | optional AR_SRC_WIRE.
+ *   hip_stream: hipStream_t to enqueue on (NULL = null stream).
+ * Errors (all detected on the host before anything is enqueued):
+ *   AR_ERR_INVALID for a NULL ctx / array / entry, R outside 2..16, a
+ *   pointer not 16-byte aligned, an unknown type / mode / flag, a wire type
+ *   wider than the destination, a destination that overlaps another
+ *   destination or a source other than exactly in place (dst[d] == srcs[d]
+ *   with equal element widths), n * element size overflowing size_t, or
+ *   memory of the wrong kind for the mode (device pointers of another device,
+ *   pageable host memory, host sources outside AR_MODE_HOST_STAGED);
+ *   AR_ERR_UNSUPPORTED for dst_type != AR_F32;
+ *   AR_ERR_NOMEM if host-staged scratch cannot be allocated;
+ *   AR_ERR_RUNTIME if a launch or copy cannot be enqueued.  Faults of
+ *   enqueued work surface at the caller's next synchronisation. */
+int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
+              int dst_type, int wire_type, unsigned mode, void *hip_stream);
+
+/* Drain the context's internal stream and release everything it owns.
+ * NULL is accepted and returns AR_OK.  Work already enqueued by ar_reduce
+ * on caller streams must be complete or ordered before any reuse of the
+ * buffers, as usual; ar_free waits for the context's own copy stream. */
+int ar_free(ar_ctx *ctx);
+
+/* Static, human-readable name of a status code ("AR_OK", ...). */
+const char *ar_status_str(int status);
+
+/* ---------------------------------------------------------------------
+ * Host-only helpers (no HIP calls; usable without a GPU).
+ * ------------------------------------------------------------------- */
+
+/* The plan ar_reduce would execute for these arguments. */
+typedef struct {
+    int    mode;          /* resolved AR_MODE_* (never AUTO)               */
+    int    n_dst;         /* destinations written                           */
+    int    src_bytes;     /* bytes per source element                       */
+    int    wire_bytes;    /* bytes per wire element                         */
+    size_t chunk_elems;   /* plan unit in elements per rank                 */
+    size_t n_chunks;      /* ceil(n / chunk_elems)                          */
+    size_t slice_start[AR_MAX_RANKS]; /* RS_BCAST: first element of rank r  */
+    size_t slice_len[AR_MAX_RANKS];   /* RS_BCAST: elements of rank r       */
+    size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*4   */
+} ar_plan;
+
+/* Validate the arguments exactly as ar_reduce does, except the memory-kind
+ * checks (which need the HIP runtime), and fill `plan` (may be NULL).
+ * `srcs_on_host` != 0 tells AUTO that the sources are pinned host memory.
+ * `cfg` NULL means defaults.  Returns an ar_status code. */
+int ar_plan_query(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
+                  size_t n, int dst_type, int wire_type, unsigned mode, int srcs_on_host,
+                  ar_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPP_AR_H */

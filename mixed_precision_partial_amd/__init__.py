@@ -1,0 +1,206 @@
+"""Python binding of the MI355X mixed-precision partial-sum reduce (``include/ar.h``).
+
+Argument marshalling only: every step of the reduce runs in the HIP library
+``libmpp_ar.so`` built from ``csrc/`` for gfx950.  The binding loads that
+library and nothing else; if it is missing, importing succeeds but the first
+call raises ``RuntimeError`` -- there is no fallback path.
+
+The functions carry the C names:
+
+    ctx = ar_init(device=0, config=None)
+    ar_reduce(ctx, dsts, srcs, n, dst_type, wire_type, mode, stream=None)
+    ar_free(ctx)
+    ar_status_str(code)
+    ar_plan_query(...)
+
+``dsts`` / ``srcs`` are sequences of torch tensors or raw integer addresses;
+``stream`` is a ``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None
+for the null stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+AR_F32, AR_F16, AR_BF16 = 0, 1, 2
+AR_MODE_AUTO, AR_MODE_SINGLE_SHOT, AR_MODE_CHUNKED, AR_MODE_RS_BCAST, AR_MODE_HOST_STAGED = 0, 1, 2, 3, 4
+AR_MODE_MASK = 0xFF
+AR_SRC_WIRE = 0x100
+AR_MAX_RANKS = 16
+
+AR_OK, AR_ERR_INVALID, AR_ERR_UNSUPPORTED, AR_ERR_NOMEM, AR_ERR_RUNTIME = 0, 1, 2, 3, 4
+
+MODE_NAMES = {
+    AR_MODE_AUTO: "auto", AR_MODE_SINGLE_SHOT: "single_shot", AR_MODE_CHUNKED: "chunked",
+    AR_MODE_RS_BCAST: "rs_bcast", AR_MODE_HOST_STAGED: "host_staged",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmpp_ar.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ar.h")
+
+
+class ArConfig(ctypes.Structure):
+    _fields_ = [
+        ("single_shot_max_bytes", ctypes.c_size_t),
+        ("chunk_bytes", ctypes.c_size_t),
+        ("host_chunk_bytes", ctypes.c_size_t),
+        ("host_slots", ctypes.c_int),
+        ("grid_wgs", ctypes.c_int),
+        ("stream_kernel", ctypes.c_int),
+    ]
+
+
+class ArPlan(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int),
+        ("n_dst", ctypes.c_int),
+        ("src_bytes", ctypes.c_int),
+        ("wire_bytes", ctypes.c_int),
+        ("chunk_elems", ctypes.c_size_t),
+        ("n_chunks", ctypes.c_size_t),
+        ("slice_start", ctypes.c_size_t * AR_MAX_RANKS),
+        ("slice_len", ctypes.c_size_t * AR_MAX_RANKS),
+        ("algo_bytes", ctypes.c_size_t),
+    ]
+
+
+class ArError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {ar_status_str(status)} ({status})" if what else ar_status_str(status))
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmpp_ar.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing: build it with "
+            "`python -m mixed_precision_partial_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.ar_init.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ArConfig)]
+    lib.ar_init.restype = ctypes.c_int
+    lib.ar_reduce.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, sz,
+                              ctypes.c_int, ctypes.c_int, ctypes.c_uint, vp]
+    lib.ar_reduce.restype = ctypes.c_int
+    lib.ar_free.argtypes = [vp]
+    lib.ar_free.restype = ctypes.c_int
+    lib.ar_status_str.argtypes = [ctypes.c_int]
+    lib.ar_status_str.restype = ctypes.c_char_p
+    lib.ar_plan_query.argtypes = [ctypes.POINTER(ArConfig), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                  ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
+                                  ctypes.c_int, ctypes.POINTER(ArPlan)]
+    lib.ar_plan_query.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _addr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    raise TypeError(f"expected a tensor or an integer address, got {type(x).__name__}")
+
+
+def _ptr_array(xs):
+    if xs is None:
+        return None
+    vals = [_addr(x) for x in xs]
+    return (ctypes.c_void_p * max(1, len(vals)))(*vals)
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _config(config) -> ArConfig | None:
+    if config is None:
+        return None
+    if isinstance(config, ArConfig):
+        return config
+    return ArConfig(**config)
+
+
+def ar_status_str(status: int) -> str:
+    return load_library().ar_status_str(int(status)).decode()
+
+
+def ar_init(device: int = 0, config=None) -> ctypes.c_void_p:
+    """Create a reduce context on HIP device ``device`` (raises ArError)."""
+    lib = load_library()
+    out = ctypes.c_void_p()
+    cfg = _config(config)
+    rc = lib.ar_init(ctypes.byref(out), int(device), ctypes.byref(cfg) if cfg is not None else None)
+    if rc != AR_OK:
+        raise ArError(rc, "ar_init")
+    return out
+
+
+def ar_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = AR_BF16,
+              mode: int = AR_MODE_AUTO, stream=None, check: bool = True) -> int:
+    """Enqueue one reduce; returns the status (raises ArError on failure if ``check``)."""
+    lib = load_library()
+    R = len(srcs) if srcs is not None else 0
+    rc = lib.ar_reduce(ctx, _ptr_array(dsts), _ptr_array(srcs), R, int(n), int(dst_type),
+                       int(wire_type), int(mode), _stream_handle(stream))
+    if check and rc != AR_OK:
+        raise ArError(rc, "ar_reduce")
+    return rc
+
+
+def ar_free(ctx) -> None:
+    rc = load_library().ar_free(ctx)
+    if rc != AR_OK:
+        raise ArError(rc, "ar_free")
+
+
+def ar_plan_query(dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = AR_BF16,
+                  mode: int = AR_MODE_AUTO, srcs_on_host: bool = False, config=None,
+                  R: int | None = None):
+    """Host-only validation + plan; returns (status, ArPlan)."""
+    lib = load_library()
+    plan = ArPlan()
+    cfg = _config(config)
+    R = (len(srcs) if srcs is not None else 0) if R is None else R
+    rc = lib.ar_plan_query(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
+                           _ptr_array(srcs), R, int(n), int(dst_type), int(wire_type), int(mode),
+                           int(bool(srcs_on_host)), ctypes.byref(plan))
+    return rc, plan
+
+
+class Reducer:
+    """Owns one context; ``reducer(dsts, srcs, ...)`` enqueues a reduce."""
+
+    def __init__(self, device: int = 0, config=None):
+        self.ctx = ar_init(device, config)
+
+    def __call__(self, dsts, srcs, n=None, dst_type=AR_F32, wire_type=AR_BF16,
+                 mode=AR_MODE_AUTO, stream=None):
+        if n is None:
+            n = srcs[0].numel()
+        return ar_reduce(self.ctx, dsts, srcs, n, dst_type, wire_type, mode, stream)
+
+    def close(self):
+        if self.ctx is not None:
+            ar_free(self.ctx)
+            self.ctx = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -1,0 +1,542 @@
+// ar_api.cpp -- host runtime behind the C ABI in ar.h: argument validation,
+// the mode / chunk / slice plan, launches on the caller's stream and the
+// host-staged copy pipeline.
+//
+// Passages this follows:
+//   - "CUDA allreduce.cu" page: the size-based choice between a low-overhead
+//     single-kernel path for small reductions and a chunked copy-engine path
+//     for large ones (file header comment, size constants); launches stay on
+//     the caller's stream because same-stream order already provides the
+//     hand-off (chunked-kernel launch loop); the copy-engine path records an
+//     event on the compute stream, has the copy stream wait for it, copies in
+//     chunks with one event each, then runs the add kernel (copy_impl, stage
+//     2) -- re-shaped here for one GPU, where the peers' sends are pinned host
+//     buffers that already hold the partials; init returns a failure instead
+//     of crashing, and free drains before releasing.
+//   - "Hexagon allreduce-ops.c" page: rank-count checks and status codes in
+//     op_allreduce / validate_allreduce; each rank owns an element range and
+//     writes it to every destination.
+//   - "llama.cpp commit log" page, SYCL tensor-parallel commit: no per-call
+//     host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ar.h"
+#include "ar_internal.h"
+
+#define AR_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kMiB = size_t(1) << 20;
+constexpr size_t kDefaultSingleShotMax = 1 * kMiB;
+constexpr size_t kDefaultChunkBytes = 4 * kMiB;
+constexpr size_t kHostChunkMin = 512 * 1024;
+constexpr size_t kHostChunkMax = 2 * kMiB;
+constexpr int kDefaultHostSlots = 3;
+constexpr int kMaxHostSlots = 64;
+
+int elem_bytes(int t) { return t == AR_F32 ? 4 : 2; }
+bool valid_type(int t) { return t == AR_F32 || t == AR_F16 || t == AR_BF16; }
+
+size_t env_size(const char *name, size_t fallback) {
+    const char *v = std::getenv(name);
+    if (v == nullptr || *v == '\0') return fallback;
+    char *end = nullptr;
+    const unsigned long long x = std::strtoull(v, &end, 10);
+    return end != v ? static_cast<size_t>(x) : fallback;
+}
+
+// Resolved configuration: explicit fields first, then AR_* environment
+// variables, then the defaults.
+struct Config {
+    size_t single_shot_max_bytes = kDefaultSingleShotMax;
+    size_t chunk_bytes = kDefaultChunkBytes;
+    size_t host_chunk_bytes = 0;   // 0: per-call heuristic
+    int host_slots = kDefaultHostSlots;
+    int grid_wgs = 0;
+    int stream_kernel = 0;
+};
+
+int resolve_config(const ar_config *cfg, Config *out) {
+    Config c;
+    c.single_shot_max_bytes = env_size("AR_SINGLE_SHOT_MAX_BYTES", kDefaultSingleShotMax);
+    c.chunk_bytes = env_size("AR_CHUNK_BYTES", kDefaultChunkBytes);
+    c.host_chunk_bytes = env_size("AR_HOST_CHUNK_BYTES", 0);
+    c.host_slots = static_cast<int>(env_size("AR_HOST_SLOTS", kDefaultHostSlots));
+    c.grid_wgs = static_cast<int>(env_size("AR_GRID_WGS", 0));
+    c.stream_kernel = static_cast<int>(env_size("AR_STREAM_KERNEL", 0));
+    if (cfg != nullptr) {
+        if (cfg->host_slots < 0 || cfg->grid_wgs < 0 || cfg->stream_kernel < 0 || cfg->stream_kernel > 2) {
+            return AR_ERR_INVALID;
+        }
+        if (cfg->single_shot_max_bytes) c.single_shot_max_bytes = cfg->single_shot_max_bytes;
+        if (cfg->chunk_bytes) c.chunk_bytes = cfg->chunk_bytes;
+        if (cfg->host_chunk_bytes) c.host_chunk_bytes = cfg->host_chunk_bytes;
+        if (cfg->host_slots) c.host_slots = cfg->host_slots;
+        if (cfg->grid_wgs) c.grid_wgs = cfg->grid_wgs;
+        if (cfg->stream_kernel) c.stream_kernel = cfg->stream_kernel;
+    }
+    if (c.host_slots < 1 || c.host_slots > kMaxHostSlots) return AR_ERR_INVALID;
+    if (c.stream_kernel < 0 || c.stream_kernel > 2) return AR_ERR_INVALID;
+    if (c.grid_wgs < 0 || c.grid_wgs > 65535) return AR_ERR_INVALID;
+    *out = c;
+    return AR_OK;
+}
+
+bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
+    return a < b + nb && b < a + na;
+}
+
+size_t round_down(size_t x, size_t m) { return x / m * m; }
+
+// Everything ar_reduce checks without the HIP runtime, plus the plan.
+int validate_and_plan(const Config &cfg, void *const *dst, const void *const *srcs, int R, size_t n,
+                      int dst_type, int wire_type, unsigned mode, bool srcs_on_host, ar_plan *plan) {
+    if (R < 2 || R > AR_MAX_RANKS) return AR_ERR_INVALID;
+    if (!valid_type(dst_type) || !valid_type(wire_type)) return AR_ERR_INVALID;
+    if ((mode & ~(AR_MODE_MASK | AR_SRC_WIRE)) != 0) return AR_ERR_INVALID;
+    const int base = static_cast<int>(mode & AR_MODE_MASK);
+    if (base < AR_MODE_AUTO || base > AR_MODE_HOST_STAGED) return AR_ERR_INVALID;
+    if (elem_bytes(wire_type) > elem_bytes(dst_type)) return AR_ERR_INVALID;
+    if (dst_type != AR_F32) return AR_ERR_UNSUPPORTED;
+    if (dst == nullptr || srcs == nullptr) return AR_ERR_INVALID;
+
+    const bool src_wire = (mode & AR_SRC_WIRE) != 0;
+    const int src_bytes = src_wire ? elem_bytes(wire_type) : elem_bytes(dst_type);
+    const int wire_bytes = elem_bytes(wire_type);
+
+    int resolved = base;
+    if (base == AR_MODE_AUTO) {
+        if (srcs_on_host) {
+            resolved = AR_MODE_HOST_STAGED;
+        } else if (n <= SIZE_MAX / 4 && n * static_cast<size_t>(wire_bytes) < cfg.single_shot_max_bytes) {
+            resolved = AR_MODE_SINGLE_SHOT;
+        } else {
+            resolved = AR_MODE_CHUNKED;
+        }
+    }
+    const int n_dst = resolved == AR_MODE_RS_BCAST ? R : 1;
+
+    for (int d = 0; d < n_dst; ++d) {
+        if (dst[d] == nullptr) return AR_ERR_INVALID;
+        if (reinterpret_cast<uintptr_t>(dst[d]) % 16 != 0) return AR_ERR_INVALID;
+    }
+    for (int r = 0; r < R; ++r) {
+        if (srcs[r] == nullptr) return AR_ERR_INVALID;
+        if (reinterpret_cast<uintptr_t>(srcs[r]) % 16 != 0) return AR_ERR_INVALID;
+    }
+    if (n > (SIZE_MAX / 8) / AR_MAX_RANKS) return AR_ERR_INVALID;
+
+    const size_t dst_len = n * 4;
+    const size_t src_len = n * static_cast<size_t>(src_bytes);
+    if (n > 0) {
+        for (int d = 0; d < n_dst; ++d) {
+            const uintptr_t pd = reinterpret_cast<uintptr_t>(dst[d]);
+            for (int e = d + 1; e < n_dst; ++e) {
+                if (ranges_overlap(pd, dst_len, reinterpret_cast<uintptr_t>(dst[e]), dst_len)) {
+                    return AR_ERR_INVALID;
+                }
+            }
+            for (int r = 0; r < R; ++r) {
+                const uintptr_t ps = reinterpret_cast<uintptr_t>(srcs[r]);
+                if (!ranges_overlap(pd, dst_len, ps, src_len)) continue;
+                // exactly in place with equal element width is the one allowed overlap:
+                // every element is read from all sources before the same thread writes it
+                if (!(ps == pd && src_bytes == 4)) return AR_ERR_INVALID;
+            }
+        }
+    }
+
+    if (plan != nullptr) {
+        std::memset(plan, 0, sizeof(*plan));
+        plan->mode = resolved;
+        plan->n_dst = n_dst;
+        plan->src_bytes = src_bytes;
+        plan->wire_bytes = wire_bytes;
+        size_t chunk;
+        if (resolved == AR_MODE_HOST_STAGED) {
+            size_t hb = cfg.host_chunk_bytes;
+            if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, src_len / 4));
+            chunk = hb / static_cast<size_t>(src_bytes);
+        } else {
+            chunk = cfg.chunk_bytes / static_cast<size_t>(wire_bytes);
+        }
+        chunk = round_down(chunk, mpp::kWaveTile);
+        if (chunk < mpp::kWaveTile) chunk = mpp::kWaveTile;
+        if (chunk > mpp::kMaxLaunchElems) chunk = mpp::kMaxLaunchElems;
+        if (resolved == AR_MODE_SINGLE_SHOT) chunk = n > 0 ? n : 1;
+        plan->chunk_elems = chunk;
+        plan->n_chunks = n == 0 ? 0 : (n + chunk - 1) / chunk;
+        if (resolved == AR_MODE_RS_BCAST) {
+            // rank r owns [floor(r n / R), floor((r+1) n / R)), boundaries on wave tiles
+            for (int r = 0; r < R; ++r) {
+                const size_t s = round_down(static_cast<size_t>(r) * (n / R) + (static_cast<size_t>(r) * (n % R)) / R,
+                                            mpp::kWaveTile);
+                const size_t e = r + 1 == R ? n
+                                            : round_down(static_cast<size_t>(r + 1) * (n / R) +
+                                                             (static_cast<size_t>(r + 1) * (n % R)) / R,
+                                                         mpp::kWaveTile);
+                plan->slice_start[r] = s;
+                plan->slice_len[r] = e - s;
+            }
+        }
+        plan->algo_bytes = static_cast<size_t>(R) * src_len + static_cast<size_t>(n_dst) * dst_len;
+    }
+    return AR_OK;
+}
+
+}  // namespace
+
+struct ar_ctx {
+    int device = -1;
+    int cu_count = 0;
+    Config cfg;
+    hipStream_t copy_stream = nullptr;
+    // host-staged scratch ring: slots x R x chunk source elements
+    void *scratch = nullptr;
+    size_t scratch_bytes = 0;
+    std::vector<hipEvent_t> ev_h2d;    // per slot: its H2D copies landed
+    std::vector<hipEvent_t> ev_free;   // per slot: the add kernel reading it finished
+    std::vector<char> slot_used;
+    hipEvent_t ev_start = nullptr;     // caller-stream order point before the copies
+    unsigned next_slot = 0;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok = true;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+void destroy(ar_ctx *c) {
+    if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
+    for (hipEvent_t e : c->ev_free) {
+        if (e) (void)hipEventSynchronize(e);
+    }
+    if (c->scratch) (void)hipFree(c->scratch);
+    for (hipEvent_t e : c->ev_h2d) if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->ev_free) if (e) (void)hipEventDestroy(e);
+    if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+    if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+    delete c;
+}
+
+enum class Kind { Device, PinnedHost, Other };
+
+// Memory kind of [p, p + bytes) and whether the whole range lies inside one
+// allocation of the runtime.  Clears the runtime's sticky last-error on a
+// failed lookup so the caller's next HIP call does not see it.
+Kind memory_kind(const void *p, size_t bytes, int device) {
+    hipPointerAttribute_t at;
+    std::memset(&at, 0, sizeof(at));
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return Kind::Other;
+    }
+    Kind k;
+    if (at.type == hipMemoryTypeDevice && at.device == device) {
+        k = Kind::Device;
+    } else if (at.type == hipMemoryTypeHost) {
+        k = Kind::PinnedHost;
+    } else {
+        return Kind::Other;
+    }
+    void *base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return Kind::Other;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    const uintptr_t q = reinterpret_cast<uintptr_t>(p);
+    if (q < b || q - b > size || bytes > size - (q - b)) return Kind::Other;
+    return k;
+}
+
+mpp::Family stream_family(const Config &cfg) {
+    return cfg.stream_kernel == 2 ? mpp::Family::StreamLds : mpp::Family::StreamReg;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_RUNTIME; }
+
+// SINGLE_SHOT / CHUNKED / RS_BCAST: launches on the caller's stream, at most
+// kMaxLaunchElems elements per launch.
+int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
+               int wire_type, bool src_wire, hipStream_t stream) {
+    const mpp::Family family = plan.mode == AR_MODE_SINGLE_SHOT ? mpp::Family::SingleShot : stream_family(c->cfg);
+    const size_t sb = static_cast<size_t>(plan.src_bytes);
+
+    if (plan.mode == AR_MODE_RS_BCAST) {
+        // gridDim.y = the ranks' slices; a slice longer than one launch covers
+        // is cut into pieces at the same relative offset in every slice
+        size_t longest = 0;
+        for (int r = 0; r < R; ++r) longest = std::max(longest, static_cast<size_t>(plan.slice_len[r]));
+        for (size_t p0 = 0; p0 < longest; p0 += mpp::kMaxLaunchElems) {
+            mpp::KernelArgs a{};
+            a.R = R;
+            a.n_dst = R;
+            a.chunk_elems = 0;
+            unsigned max_len = 0;
+            for (int r = 0; r < R; ++r) {
+                const size_t len = plan.slice_len[r] > p0 ? std::min(mpp::kMaxLaunchElems, plan.slice_len[r] - p0) : 0;
+                a.slice_start[r] = plan.slice_start[r] + p0;
+                a.slice_len[r] = static_cast<unsigned>(len);
+                max_len = std::max<unsigned>(max_len, static_cast<unsigned>(len));
+                a.src[r] = srcs[r];
+                a.dst[r] = static_cast<float *>(dst[r]);
+            }
+            const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, max_len,
+                                                           static_cast<unsigned>(R), c->cu_count, c->cfg.grid_wgs);
+            if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, a, shape, stream))) return rc;
+        }
+        return AR_OK;
+    }
+
+    for (size_t p0 = 0; p0 < n; p0 += mpp::kMaxLaunchElems) {
+        const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);
+        mpp::KernelArgs a{};
+        a.R = R;
+        a.n_dst = 1;
+        a.n = static_cast<unsigned>(len);
+        for (int r = 0; r < R; ++r) a.src[r] = static_cast<const char *>(srcs[r]) + p0 * sb;
+        a.dst[0] = static_cast<float *>(dst[0]) + p0;
+        unsigned n_ranges = 1;
+        unsigned range_len = static_cast<unsigned>(len);
+        if (plan.mode == AR_MODE_CHUNKED) {
+            a.chunk_elems = static_cast<unsigned>(std::min(plan.chunk_elems, len));
+            n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
+            if (n_ranges > 65535) {
+                a.chunk_elems = static_cast<unsigned>(round_down((len + 65534) / 65535 + mpp::kWaveTile - 1,
+                                                                 mpp::kWaveTile));
+                n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
+            }
+            range_len = a.chunk_elems;
+        } else {
+            a.chunk_elems = 0;
+            a.slice_start[0] = 0;
+            a.slice_len[0] = static_cast<unsigned>(len);
+        }
+        const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, range_len, n_ranges,
+                                                       c->cu_count, c->cfg.grid_wgs);
+        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, a, shape, stream))) return rc;
+    }
+    return AR_OK;
+}
+
+int ensure_scratch(ar_ctx *c, size_t bytes) {
+    if (c->scratch_bytes >= bytes) return AR_OK;
+    // the old ring may still be read by enqueued kernels or written by copies
+    if (hipStreamSynchronize(c->copy_stream) != hipSuccess) return AR_ERR_RUNTIME;
+    for (size_t s = 0; s < c->ev_free.size(); ++s) {
+        if (c->slot_used[s] && hipEventSynchronize(c->ev_free[s]) != hipSuccess) return AR_ERR_RUNTIME;
+    }
+    if (c->scratch) {
+        if (hipFree(c->scratch) != hipSuccess) return AR_ERR_RUNTIME;
+        c->scratch = nullptr;
+        c->scratch_bytes = 0;
+    }
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return AR_ERR_NOMEM;
+    }
+    c->scratch = p;
+    c->scratch_bytes = bytes;
+    std::fill(c->slot_used.begin(), c->slot_used.end(), 0);
+    return AR_OK;
+}
+
+// HOST_STAGED: chunk c of every rank is copied host -> HBM slot (c mod K) on
+// the internal copy stream; the caller's stream waits for that slot's copies,
+// runs the add kernel over the slot and marks the slot free again.  The copy
+// of a later chunk into the same slot waits for that mark, so copies run ahead
+// of the adds by up to K chunks.
+int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
+                    int wire_type, bool src_wire, hipStream_t stream) {
+    const size_t sb = static_cast<size_t>(plan.src_bytes);
+    const size_t chunk = plan.chunk_elems;
+    const size_t K = static_cast<size_t>(c->cfg.host_slots);
+    const size_t rank_stride = chunk * sb;
+    const size_t slot_stride = rank_stride * static_cast<size_t>(R);
+    if (int rc = ensure_scratch(c, slot_stride * K)) return rc;
+
+    if (hipEventRecord(c->ev_start, stream) != hipSuccess) return AR_ERR_RUNTIME;
+    if (hipStreamWaitEvent(c->copy_stream, c->ev_start, 0) != hipSuccess) return AR_ERR_RUNTIME;
+
+    const mpp::Family family = stream_family(c->cfg);
+    for (size_t ch = 0; ch < plan.n_chunks; ++ch) {
+        const size_t e0 = ch * chunk;
+        const size_t len = std::min(chunk, n - e0);
+        const unsigned slot = c->next_slot;
+        c->next_slot = (c->next_slot + 1) % static_cast<unsigned>(K);
+        char *slot_base = static_cast<char *>(c->scratch) + slot * slot_stride;
+
+        if (c->slot_used[slot] && hipStreamWaitEvent(c->copy_stream, c->ev_free[slot], 0) != hipSuccess) {
+            return AR_ERR_RUNTIME;
+        }
+        for (int r = 0; r < R; ++r) {
+            if (hipMemcpyAsync(slot_base + r * rank_stride, static_cast<const char *>(srcs[r]) + e0 * sb, len * sb,
+                               hipMemcpyHostToDevice, c->copy_stream) != hipSuccess) {
+                return AR_ERR_RUNTIME;
+            }
+        }
+        if (hipEventRecord(c->ev_h2d[slot], c->copy_stream) != hipSuccess) return AR_ERR_RUNTIME;
+        if (hipStreamWaitEvent(stream, c->ev_h2d[slot], 0) != hipSuccess) return AR_ERR_RUNTIME;
+
+        mpp::KernelArgs a{};
+        a.R = R;
+        a.n_dst = 1;
+        a.n = static_cast<unsigned>(len);
+        a.chunk_elems = 0;
+        a.slice_start[0] = 0;
+        a.slice_len[0] = static_cast<unsigned>(len);
+        for (int r = 0; r < R; ++r) a.src[r] = slot_base + r * rank_stride;
+        a.dst[0] = static_cast<float *>(dst[0]) + e0;
+        const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, static_cast<unsigned>(len), 1,
+                                                       c->cu_count, c->cfg.grid_wgs);
+        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, a, shape, stream))) return rc;
+        if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
+        c->slot_used[slot] = 1;
+    }
+    return AR_OK;
+}
+
+}  // namespace
+
+AR_API const char *ar_status_str(int status) {
+    switch (status) {
+    case AR_OK: return "AR_OK";
+    case AR_ERR_INVALID: return "AR_ERR_INVALID";
+    case AR_ERR_UNSUPPORTED: return "AR_ERR_UNSUPPORTED";
+    case AR_ERR_NOMEM: return "AR_ERR_NOMEM";
+    case AR_ERR_RUNTIME: return "AR_ERR_RUNTIME";
+    default: return "AR_ERR_UNKNOWN";
+    }
+}
+
+AR_API int ar_plan_query(const ar_config *cfg, void *const *dst, const void *const *srcs, int R, size_t n,
+                         int dst_type, int wire_type, unsigned mode, int srcs_on_host, ar_plan *plan) {
+    Config c;
+    if (int rc = resolve_config(cfg, &c)) return rc;
+    return validate_and_plan(c, dst, srcs, R, n, dst_type, wire_type, mode, srcs_on_host != 0, plan);
+}
+
+AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
+    if (out == nullptr) return AR_ERR_INVALID;
+    *out = nullptr;
+    Config conf;
+    if (int rc = resolve_config(cfg, &conf)) return rc;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess) {
+        (void)hipGetLastError();
+        return AR_ERR_RUNTIME;
+    }
+    if (hip_device < 0 || hip_device >= count) return AR_ERR_INVALID;
+
+    DeviceGuard guard(hip_device);
+    if (!guard.ok) return AR_ERR_RUNTIME;
+
+    ar_ctx *c = new (std::nothrow) ar_ctx();
+    if (c == nullptr) return AR_ERR_NOMEM;
+    c->device = hip_device;
+    c->cfg = conf;
+    int rc = AR_OK;
+    if (hipDeviceGetAttribute(&c->cu_count, hipDeviceAttributeMultiprocessorCount, hip_device) != hipSuccess ||
+        c->cu_count <= 0) {
+        rc = AR_ERR_RUNTIME;
+    }
+    if (rc == AR_OK && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess) {
+        c->copy_stream = nullptr;
+        rc = AR_ERR_RUNTIME;
+    }
+    if (rc == AR_OK && hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming) != hipSuccess) {
+        c->ev_start = nullptr;
+        rc = AR_ERR_RUNTIME;
+    }
+    if (rc == AR_OK) {
+        const size_t K = static_cast<size_t>(conf.host_slots);
+        c->ev_h2d.assign(K, nullptr);
+        c->ev_free.assign(K, nullptr);
+        c->slot_used.assign(K, 0);
+        for (size_t s = 0; s < K && rc == AR_OK; ++s) {
+            if (hipEventCreateWithFlags(&c->ev_h2d[s], hipEventDisableTiming) != hipSuccess) {
+                c->ev_h2d[s] = nullptr;
+                rc = AR_ERR_RUNTIME;
+            } else if (hipEventCreateWithFlags(&c->ev_free[s], hipEventDisableTiming) != hipSuccess) {
+                c->ev_free[s] = nullptr;
+                rc = AR_ERR_RUNTIME;
+            }
+        }
+    }
+    if (rc != AR_OK) {
+        (void)hipGetLastError();
+        destroy(c);
+        return rc;
+    }
+    *out = c;
+    return AR_OK;
+}
+
+AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
+                     int wire_type, unsigned mode, void *hip_stream) {
+    if (ctx == nullptr) return AR_ERR_INVALID;
+    // cheap checks first, without touching the runtime
+    ar_plan plan;
+    const bool auto_mode = (mode & AR_MODE_MASK) == AR_MODE_AUTO;
+    int rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, false, &plan);
+    if (rc != AR_OK) return rc;
+
+    const bool src_wire = (mode & AR_SRC_WIRE) != 0;
+    const size_t src_len = n * static_cast<size_t>(plan.src_bytes);
+    const size_t dst_len = n * 4;
+
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return AR_ERR_RUNTIME;
+
+    if (n > 0 && (auto_mode || plan.mode == AR_MODE_HOST_STAGED)) {
+        // memory kinds decide AUTO between host-staged and device modes
+        const Kind k0 = memory_kind(srcs[0], src_len, ctx->device);
+        if (k0 == Kind::Other) return AR_ERR_INVALID;
+        if (auto_mode && k0 == Kind::PinnedHost) {
+            rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, true, &plan);
+            if (rc != AR_OK) return rc;
+        }
+    }
+    if (n == 0) return AR_OK;
+
+    const Kind want_src = plan.mode == AR_MODE_HOST_STAGED ? Kind::PinnedHost : Kind::Device;
+    for (int r = 0; r < R; ++r) {
+        if (memory_kind(srcs[r], src_len, ctx->device) != want_src) return AR_ERR_INVALID;
+    }
+    for (int d = 0; d < plan.n_dst; ++d) {
+        if (memory_kind(dst[d], dst_len, ctx->device) != Kind::Device) return AR_ERR_INVALID;
+    }
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (plan.mode == AR_MODE_HOST_STAGED) {
+        return run_host_staged(ctx, plan, dst, srcs, R, n, wire_type, src_wire, stream);
+    }
+    return run_device(ctx, plan, dst, srcs, R, n, wire_type, src_wire, stream);
+}
+
+AR_API int ar_free(ar_ctx *ctx) {
+    if (ctx == nullptr) return AR_OK;
+    DeviceGuard guard(ctx->device);
+    destroy(ctx);
+    return AR_OK;
+}

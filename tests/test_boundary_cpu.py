@@ -1,0 +1,185 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+declared entry point, and its host-side validation / planning behaves as
+``include/ar.h`` states.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_partial_amd as ar
+
+MiB = 1 << 20
+# Well separated fake addresses: validation never dereferences them.
+A = [0x10_0000_0000 + i * 0x1_0000_0000 for i in range(40)]
+
+
+def declared_functions():
+    text = open(ar.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ar_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ar.load_library()
+    names = declared_functions()
+    assert {"ar_init", "ar_reduce", "ar_free", "ar_status_str", "ar_plan_query"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in ar.h but not exported"
+
+
+def test_exports_nothing_else():
+    out = os.popen(f"nm -D --defined-only {ar.LIB_PATH}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
+def test_status_strings():
+    assert ar.ar_status_str(ar.AR_OK) == "AR_OK"
+    assert ar.ar_status_str(ar.AR_ERR_INVALID) == "AR_ERR_INVALID"
+    assert ar.ar_status_str(ar.AR_ERR_UNSUPPORTED) == "AR_ERR_UNSUPPORTED"
+    assert ar.ar_status_str(ar.AR_ERR_NOMEM) == "AR_ERR_NOMEM"
+    assert ar.ar_status_str(ar.AR_ERR_RUNTIME) == "AR_ERR_RUNTIME"
+    assert ar.ar_status_str(1234) == "AR_ERR_UNKNOWN"
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 3 * 4 + 4   # padded to 8
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8
+
+
+def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
+      host=False, config=None):
+    srcs = A[1:1 + R] if srcs is None else srcs
+    dsts = [A[20 + d] for d in range(R)] if dsts is None else dsts
+    return ar.ar_plan_query(dsts, srcs, n, dst_type, wire, mode, host, config, R=len(srcs))
+
+
+def test_rank_count_bounds():
+    assert q(4096, R=2)[0] == ar.AR_OK
+    assert q(4096, R=16)[0] == ar.AR_OK
+    assert q(4096, srcs=A[1:2])[0] == ar.AR_ERR_INVALID
+    assert q(4096, srcs=A[1:18])[0] == ar.AR_ERR_INVALID
+
+
+def test_type_checks():
+    assert q(64, wire=7)[0] == ar.AR_ERR_INVALID
+    assert q(64, dst_type=9)[0] == ar.AR_ERR_INVALID
+    # a wire wider than the destination is invalid, a narrow destination unsupported
+    assert q(64, dst_type=ar.AR_F16, wire=ar.AR_F32)[0] == ar.AR_ERR_INVALID
+    assert q(64, dst_type=ar.AR_F16, wire=ar.AR_F16)[0] == ar.AR_ERR_UNSUPPORTED
+    assert q(64, dst_type=ar.AR_BF16, wire=ar.AR_BF16)[0] == ar.AR_ERR_UNSUPPORTED
+
+
+def test_mode_and_flag_checks():
+    assert q(64, mode=5)[0] == ar.AR_ERR_INVALID
+    assert q(64, mode=ar.AR_MODE_CHUNKED | 0x200)[0] == ar.AR_ERR_INVALID
+    assert q(64, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[0] == ar.AR_OK
+
+
+def test_null_and_alignment():
+    assert ar.ar_plan_query(None, A[1:3], 64, R=2)[0] == ar.AR_ERR_INVALID
+    assert ar.ar_plan_query([A[20]], None, 64, R=2)[0] == ar.AR_ERR_INVALID
+    assert q(64, srcs=[A[1], 0])[0] == ar.AR_ERR_INVALID
+    assert q(64, dsts=[0])[0] == ar.AR_ERR_INVALID
+    assert q(64, srcs=[A[1], A[2] + 8])[0] == ar.AR_ERR_INVALID
+    assert q(64, dsts=[A[20] + 4])[0] == ar.AR_ERR_INVALID
+    assert q(64, srcs=[A[1], A[2] + 16])[0] == ar.AR_OK
+
+
+def test_overlap_rules():
+    n = 1 << 20
+    # exactly in place with fp32 sources: allowed
+    assert q(n, mode=ar.AR_MODE_CHUNKED, dsts=[A[1]], srcs=[A[1], A[2]])[0] == ar.AR_OK
+    assert q(n, mode=ar.AR_MODE_CHUNKED, dsts=[A[2]], srcs=[A[1], A[2]])[0] == ar.AR_OK
+    # partial overlap: invalid
+    assert q(n, mode=ar.AR_MODE_CHUNKED, dsts=[A[1] + 4096], srcs=[A[1], A[2]])[0] == ar.AR_ERR_INVALID
+    # in place with wire-typed sources (different widths): invalid
+    assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, dsts=[A[1]], srcs=[A[1], A[2]])[0] == ar.AR_ERR_INVALID
+    # destinations overlapping each other (broadcast schedule): invalid
+    d = [A[20], A[20] + 4 * n - 16]
+    assert q(n, mode=ar.AR_MODE_RS_BCAST, dsts=d)[0] == ar.AR_ERR_INVALID
+    # sources may alias each other (read only)
+    assert q(n, mode=ar.AR_MODE_CHUNKED, srcs=[A[1], A[1]])[0] == ar.AR_OK
+    # n = 0: nothing overlaps
+    assert q(0, mode=ar.AR_MODE_CHUNKED, dsts=[A[1] + 16], srcs=[A[1], A[2]])[0] == ar.AR_OK
+
+
+def test_auto_mode_threshold():
+    # below 1 MiB of wire bytes per rank -> single shot, else chunked
+    rc, p = q(4096, wire=ar.AR_F32)
+    assert rc == ar.AR_OK and p.mode == ar.AR_MODE_SINGLE_SHOT and p.n_chunks == 1
+    rc, p = q((1 * MiB) // 2 - 1, wire=ar.AR_BF16)
+    assert p.mode == ar.AR_MODE_SINGLE_SHOT
+    rc, p = q((1 * MiB) // 2, wire=ar.AR_BF16)
+    assert p.mode == ar.AR_MODE_CHUNKED
+    rc, p = q(4096, host=True)
+    assert p.mode == ar.AR_MODE_HOST_STAGED
+    rc, p = q(4096, config={"single_shot_max_bytes": 1024})
+    assert p.mode == ar.AR_MODE_CHUNKED
+
+
+def test_prefill_chunk_plan():
+    # 2048 x 4096 with a bf16 wire in 4 MiB chunks of wire bytes per rank -> 4 chunks of 2 Mi elements
+    n = 2048 * 4096
+    rc, p = q(n, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16)
+    assert rc == ar.AR_OK
+    assert p.chunk_elems == 2 * MiB and p.n_chunks == 4
+    assert p.algo_bytes == 2 * n * 4 + n * 4 == 100_663_296
+    rc, p = q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
+    assert p.src_bytes == 2 and p.algo_bytes == 2 * n * 2 + n * 4
+
+
+def test_slice_plan_partitions_range():
+    for n, R in [(2048 * 8192, 4), (100_003, 3), (1000, 8), (7, 2), (513 * 16 + 5, 16)]:
+        rc, p = q(n, R=R, mode=ar.AR_MODE_RS_BCAST)
+        assert rc == ar.AR_OK and p.n_dst == R
+        pos = 0
+        for r in range(R):
+            assert p.slice_start[r] == pos
+            assert p.slice_start[r] % 512 == 0
+            pos += p.slice_len[r]
+        assert pos == n
+    rc, p = q(2048 * 8192, R=4, mode=ar.AR_MODE_RS_BCAST, wire=ar.AR_F16)
+    assert [p.slice_len[r] for r in range(4)] == [2048 * 8192 // 4] * 4
+    assert p.algo_bytes == 4 * 2048 * 8192 * 4 * 2 == 536_870_912
+
+
+def test_host_chunk_heuristic():
+    # clamp(bytes / 4, 512 KiB, 2 MiB) of source bytes per rank
+    n = 8192 * 8192
+    rc, p = q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
+    assert p.chunk_elems == (2 * MiB) // 2 and p.n_chunks == n // ((2 * MiB) // 2)
+    rc, p = q(100_000, mode=ar.AR_MODE_HOST_STAGED)
+    assert p.chunk_elems == (512 * 1024) // 4
+    rc, p = q(n, mode=ar.AR_MODE_HOST_STAGED, config={"host_chunk_bytes": 1 << 16})
+    assert p.chunk_elems == (1 << 16) // 4
+
+
+def test_bad_config_rejected():
+    assert q(64, config={"host_slots": -1})[0] == ar.AR_ERR_INVALID
+    assert q(64, config={"stream_kernel": 3})[0] == ar.AR_ERR_INVALID
+    assert q(64, config={"grid_wgs": -2})[0] == ar.AR_ERR_INVALID
+
+
+def test_zero_elements_is_ok():
+    rc, p = q(0, mode=ar.AR_MODE_CHUNKED)
+    assert rc == ar.AR_OK and p.n_chunks == 0 and p.algo_bytes == 0
+
+
+def test_ar_free_null_and_init_errors():
+    assert ar.load_library().ar_free(None) == ar.AR_OK
+    out = ctypes.c_void_p()
+    assert ar.load_library().ar_init(None, 0, None) == ar.AR_ERR_INVALID
+    bad = ar.ArConfig(host_slots=-3)
+    assert ar.load_library().ar_init(ctypes.byref(out), 0, ctypes.byref(bad)) == ar.AR_ERR_INVALID
+    assert out.value is None
+
+
+@pytest.mark.parametrize("rank", [2, 5, 16])
+def test_reduce_rejects_before_runtime(rank):
+    # a NULL context is rejected without touching the GPU
+    lib = ar.load_library()
+    srcs = (ctypes.c_void_p * rank)(*A[1:1 + rank])
+    dsts = (ctypes.c_void_p * 1)(A[30])
+    assert lib.ar_reduce(None, dsts, srcs, rank, 64, ar.AR_F32, ar.AR_BF16, 0, None) == ar.AR_ERR_INVALID

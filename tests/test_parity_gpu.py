@@ -1,0 +1,337 @@
+"""HIP path against the CPU oracle, bit for bit (0 ulp; NaN compared as NaN).
+
+Every call goes through the C ABI (``libmpp_ar.so``) via the thin binding.
+The five workload shapes run at full size; tails, edge values, every schedule,
+every wire type, source widths, in-place use, guard bands and error paths run
+at sizes the oracle finishes in seconds.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_partial_amd as ar
+import oracle
+import workloads as wl
+from gpu_util import (GuardedDst, assert_bits_equal, assert_no_sentinel, log_case, oracle_result,
+                      to_device, to_pinned)
+
+pytestmark = pytest.mark.gpu
+
+MODES = {
+    "single_shot": ar.AR_MODE_SINGLE_SHOT,
+    "chunked": ar.AR_MODE_CHUNKED,
+    "rs_bcast": ar.AR_MODE_RS_BCAST,
+    "host_staged": ar.AR_MODE_HOST_STAGED,
+}
+WIRES = {"f32": ar.AR_F32, "bf16": ar.AR_BF16, "f16": ar.AR_F16}
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    c = ar.ar_init(0)
+    yield c
+    torch.cuda.synchronize()
+    ar.ar_free(c)
+
+
+def run_case(ctx, srcs_np, wire, mode, src_wire=False, R=None, config_ctx=None, guarded=True):
+    """Run one reduce on the GPU and return the list of destination arrays."""
+    c = config_ctx or ctx
+    R = len(srcs_np)
+    n = srcs_np[0].size
+    base = mode & ar.AR_MODE_MASK
+    n_dst = R if base == ar.AR_MODE_RS_BCAST else 1
+    if src_wire:
+        srcs_np = [wl.as_wire_typed(s, wire) if s.dtype == np.float32 else s for s in srcs_np]
+    if base == ar.AR_MODE_HOST_STAGED:
+        srcs_t = [to_pinned(s) for s in srcs_np]
+    else:
+        srcs_t = [to_device(s) for s in srcs_np]
+    dsts = [GuardedDst(n) for _ in range(n_dst)]
+    flags = ar.AR_SRC_WIRE if src_wire else 0
+    ar.ar_reduce(c, [d.ptr() for d in dsts], srcs_t, n, ar.AR_F32, wire, mode | flags)
+    torch.cuda.synchronize()
+    return [d.result() for d in dsts], srcs_np
+
+
+def check_against_oracle(ctx, srcs_np, wire, mode, src_wire=False, what="", config_ctx=None):
+    outs, used = run_case(ctx, srcs_np, wire, mode, src_wire, config_ctx=config_ctx)
+    src_type = wire if src_wire and wire != ar.AR_F32 else None
+    want = oracle_result(used, wire, src_type=src_type)
+    for d, got in enumerate(outs):
+        assert_bits_equal(got, want, f"{what} dst {d}")
+    return outs, want
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size
+# --------------------------------------------------------------------------
+
+def test_decode_fp32_wire(ctx):
+    w = wl.WORKLOADS["decode_f32"]
+    log_case(f"decode_f32 R={w.R} n={w.n} single_shot")
+    srcs = wl.partials(w, 0)
+    outs, want = check_against_oracle(ctx, srcs, w.wire, ar.AR_MODE_SINGLE_SHOT, what="decode_f32")
+    # fp32 wire: the plain ordered float32 sum
+    assert_bits_equal(outs[0], srcs[0] + srcs[1], "decode_f32 vs float32 sum")
+
+
+def test_decode_bf16_wire_all_calls(ctx):
+    """10,000 sequential single-shot calls, each with fresh seeded data; every output checked."""
+    w = wl.WORKLOADS["decode_bf16"]
+    log_case(f"decode_bf16 R={w.R} n={w.n} calls={w.calls}")
+    n, calls = w.n, w.calls
+    host = np.empty((calls, w.R, n), dtype=np.float32)
+    for c in range(calls):
+        for r, p in enumerate(wl.partials(w, c)):
+            host[c, r] = p
+    dev = torch.from_numpy(host).cuda()
+    out = torch.empty((calls, n), dtype=torch.float32, device="cuda")
+    esz = 4
+    base_in, base_out = dev.data_ptr(), out.data_ptr()
+    for c in range(calls):
+        srcs = [base_in + (c * w.R + r) * n * esz for r in range(w.R)]
+        ar.ar_reduce(ctx, [base_out + c * n * esz], srcs, n, ar.AR_F32, w.wire, ar.AR_MODE_SINGLE_SHOT)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.reduce([host[:, r, :].ravel() for r in range(w.R)], w.wire)[0]
+    assert_bits_equal(got.ravel(), want, "decode_bf16 all calls")
+
+
+def test_prefill_bf16_chunked(ctx):
+    w = wl.WORKLOADS["prefill_bf16"]
+    log_case(f"prefill_bf16 R={w.R} n={w.n} chunked 4MiB")
+    srcs = wl.partials(w, 0)
+    check_against_oracle(ctx, srcs, w.wire, ar.AR_MODE_CHUNKED, what="prefill_bf16")
+
+
+def test_prefill_bf16_auto_selects_chunked(ctx):
+    w = wl.WORKLOADS["prefill_bf16"]
+    rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], w.n,
+                                ar.AR_F32, w.wire, ar.AR_MODE_AUTO)
+    assert rc == ar.AR_OK and plan.mode == ar.AR_MODE_CHUNKED and plan.n_chunks == 4
+    log_case("prefill_bf16 auto")
+    srcs = wl.partials(w, 1)
+    check_against_oracle(ctx, srcs, w.wire, ar.AR_MODE_AUTO, what="prefill_bf16 auto")
+
+
+def test_slice_bcast_f16(ctx):
+    w = wl.WORKLOADS["slice_bcast_f16"]
+    log_case(f"slice_bcast_f16 R={w.R} n={w.n} rs_bcast")
+    srcs = wl.partials(w, 0)
+    outs, want = check_against_oracle(ctx, srcs, w.wire, ar.AR_MODE_RS_BCAST, what="slice_bcast_f16")
+    assert len(outs) == 4
+    for d in range(1, 4):
+        assert np.array_equal(outs[0].view(np.uint32), outs[d].view(np.uint32))
+
+
+def test_host_staged_bf16_and_hbm(ctx):
+    """R=8, 8192 x 8192: wire-typed partials in pinned host memory, then the same shape from HBM."""
+    w = wl.WORKLOADS["host_staged_bf16"]
+    n = w.n
+    log_case(f"host_staged_bf16 R={w.R} n={n}")
+    srcs32 = wl.partials(w, 0)
+    pre = [wl.as_wire_typed(s, w.wire) for s in srcs32]
+    want_wire = oracle.reduce(pre, w.wire, src_type=w.wire)[0]
+    outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_HOST_STAGED, src_wire=True)
+    assert_bits_equal(outs[0], want_wire, "host_staged bf16")
+    log_case("host_staged_bf16 same shape from HBM, wire-typed sources")
+    outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_CHUNKED, src_wire=True)
+    assert_bits_equal(outs[0], want_wire, "hbm chunked bf16 sources")
+    log_case("host_staged_bf16 same shape from HBM, fp32 sources")
+    want32 = oracle.reduce(srcs32, w.wire)[0]
+    outs, _ = run_case(ctx, srcs32, w.wire, ar.AR_MODE_CHUNKED)
+    assert_bits_equal(outs[0], want32, "hbm chunked fp32 sources")
+
+
+# --------------------------------------------------------------------------
+# tails, rank counts, wire types, source widths, schedules
+# --------------------------------------------------------------------------
+
+TAIL_N = [1, 3, 7, 8, 9, 63, 64, 65, 511, 512, 513, 1023, 1025, 2047, 2048, 2049, 4095, 4097,
+          8191, 8193, 12289, 65537, 131071]
+
+
+@pytest.mark.parametrize("mode_name", ["single_shot", "chunked", "rs_bcast"])
+def test_tails_all_wires_and_widths(ctx, mode_name):
+    mode = MODES[mode_name]
+    rng = np.random.default_rng(1234)
+    for i, n in enumerate(TAIL_N):
+        R = int(rng.choice([2, 3, 4, 5, 8, 9, 16]))
+        for wire_name, wire in WIRES.items():
+            for src_wire in ([False, True] if wire != ar.AR_F32 else [False]):
+                what = f"{mode_name} n={n} R={R} wire={wire_name} src_wire={src_wire}"
+                log_case(what)
+                srcs = wl.random_partials(2000 + i, wire, R, n, dist="wide")
+                check_against_oracle(ctx, srcs, wire, mode, src_wire, what)
+
+
+def test_small_chunks_many_ranges(ctx):
+    """Chunk plan with many chunks and a ragged last chunk."""
+    cfg = ar.ar_init(0, {"chunk_bytes": 4096})
+    try:
+        for n in [2048 * 3 + 17, 100_003, 1 << 18]:
+            for wire in (ar.AR_BF16, ar.AR_F16, ar.AR_F32):
+                what = f"chunked 4 KiB chunks n={n} wire={wire}"
+                log_case(what)
+                srcs = wl.random_partials(3000, n % 97, 3, n, dist="normal")
+                check_against_oracle(ctx, srcs, wire, ar.AR_MODE_CHUNKED, what=what, config_ctx=cfg)
+    finally:
+        torch.cuda.synchronize()
+        ar.ar_free(cfg)
+
+
+# --------------------------------------------------------------------------
+# edge values and exact rounding
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode_name", ["single_shot", "chunked", "rs_bcast", "host_staged"])
+def test_edge_value_pairs(ctx, mode_name):
+    """Every ordered pair (R=2) and a grid of triples (R=3) of edge values, NaN included."""
+    g = np.concatenate([wl.special_values(), wl.nan_values()])
+    a, b = np.meshgrid(g, g, indexing="ij")
+    pairs = [a.ravel().copy(), b.ravel().copy()]
+    g3 = g[::3]
+    x, y, z = np.meshgrid(g3, g3, g3, indexing="ij")
+    triples = [x.ravel().copy(), y.ravel().copy(), z.ravel().copy()]
+    for wire_name, wire in WIRES.items():
+        for srcs in (pairs, triples):
+            what = f"edge {mode_name} R={len(srcs)} wire={wire_name} n={srcs[0].size}"
+            log_case(what)
+            check_against_oracle(ctx, srcs, wire, MODES[mode_name], what=what)
+
+
+@pytest.mark.parametrize("wire_name", ["bf16", "f16"])
+def test_rounding_sampled_patterns(ctx, wire_name):
+    """round_W over every upper 16 bits x 64 lower patterns (4 Mi inputs): src1 = -0 keeps
+    x + (-0) == x exactly, so the destination is the widened wire value of src0."""
+    wire = WIRES[wire_name]
+    rng = np.random.default_rng(99)
+    hi = np.repeat(np.arange(1 << 16, dtype=np.uint32) << 16, 64)
+    lo = rng.integers(0, 1 << 16, hi.size, dtype=np.uint32)
+    lo[::64] = 0x8000            # exact ties for bf16
+    lo[1::64] = 0x1000 & 0xFFFF  # ties for f16 in the low bits
+    x = (hi | lo).view(np.float32)
+    negz = np.full(x.size, -0.0, dtype=np.float32)
+    log_case(f"rounding sampled {wire_name} n={x.size}")
+    check_against_oracle(ctx, [x, negz], wire, ar.AR_MODE_CHUNKED, what=f"rounding {wire_name}")
+
+
+# --------------------------------------------------------------------------
+# schedules agree, in place, streams, host-staged pipelining
+# --------------------------------------------------------------------------
+
+def test_all_schedules_byte_identical(ctx):
+    n = 300_001
+    srcs = wl.random_partials(4000, 0, 5, n, dist="normal+outliers")
+    results = {}
+    for name in ("single_shot", "chunked", "rs_bcast", "host_staged"):
+        log_case(f"schedule {name} n={n}")
+        outs, _ = run_case(ctx, srcs, ar.AR_BF16, MODES[name])
+        results[name] = outs
+    ref = results["chunked"][0].view(np.uint32)
+    for name, outs in results.items():
+        for d, o in enumerate(outs):
+            assert np.array_equal(o.view(np.uint32), ref), f"{name} dst {d} differs from chunked"
+    assert_bits_equal(results["chunked"][0], oracle_result(srcs, ar.AR_BF16), "schedules vs oracle")
+
+
+def test_in_place(ctx):
+    n = 70_001
+    for mode_name in ("single_shot", "chunked", "rs_bcast"):
+        R = 4
+        srcs = wl.random_partials(5000, 1, R, n, dist="wide")
+        want = oracle_result(srcs, ar.AR_BF16)
+        dev = [to_device(s) for s in srcs]
+        base = MODES[mode_name]
+        dsts = dev if base == ar.AR_MODE_RS_BCAST else [dev[0]]
+        log_case(f"in place {mode_name}")
+        ar.ar_reduce(ctx, dsts, dev, n, ar.AR_F32, ar.AR_BF16, base)
+        torch.cuda.synchronize()
+        for d in dsts:
+            assert_bits_equal(d.cpu().numpy(), want, f"in place {mode_name}")
+
+
+def test_non_default_stream(ctx):
+    n = 1 << 20
+    srcs = wl.random_partials(6000, 0, 2, n)
+    dev = [to_device(s) for s in srcs]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    log_case("non-default stream")
+    with torch.cuda.stream(s):
+        ar.ar_reduce(ctx, [out], dev, n, ar.AR_F32, ar.AR_F16, ar.AR_MODE_CHUNKED, stream=s)
+    s.synchronize()
+    assert_bits_equal(out.cpu().numpy(), oracle_result(srcs, ar.AR_F16), "side stream")
+
+
+@pytest.mark.parametrize("slots", [1, 2, 4])
+def test_host_staged_back_to_back(ctx, slots):
+    """Several host-staged calls enqueued without a sync in between, small chunks,
+    few slots: a missing wait on slot reuse would mix chunks of different calls."""
+    c = ar.ar_init(0, {"host_slots": slots, "host_chunk_bytes": 1 << 16})
+    try:
+        n, R, calls = 200_000 + slots, 3, 4
+        inputs = [wl.random_partials(7000 + slots, k, R, n) for k in range(calls)]
+        pinned = [[to_pinned(s) for s in srcs] for srcs in inputs]
+        outs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(calls)]
+        log_case(f"host staged back to back slots={slots}")
+        for k in range(calls):
+            ar.ar_reduce(c, [outs[k]], pinned[k], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_HOST_STAGED)
+        torch.cuda.synchronize()
+        for k in range(calls):
+            assert_bits_equal(outs[k].cpu().numpy(), oracle_result(inputs[k], ar.AR_BF16), f"call {k}")
+    finally:
+        torch.cuda.synchronize()
+        ar.ar_free(c)
+
+
+def test_zero_elements_no_op(ctx):
+    d = GuardedDst(16)
+    s = [to_device(np.ones(16, dtype=np.float32)) for _ in range(2)]
+    ar.ar_reduce(ctx, [d.ptr()], s, 0, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED)
+    torch.cuda.synchronize()
+    got = d.result()
+    assert np.all(got.view(np.uint32) == np.uint32(0x7FA5A5A5))
+
+
+# --------------------------------------------------------------------------
+# errors detected on the host before anything is enqueued
+# --------------------------------------------------------------------------
+
+def test_error_paths(ctx):
+    n = 4096
+    dev = [to_device(np.ones(n, dtype=np.float32)) for _ in range(2)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    host_pageable = [np.ones(n, dtype=np.float32) for _ in range(2)]
+    pinned = [to_pinned(np.ones(n, dtype=np.float32)) for _ in range(2)]
+    E = ar.AR_ERR_INVALID
+    log_case("error paths")
+    # pageable host memory as a source of a device mode
+    rc = ar.ar_reduce(ctx, [out], [h.ctypes.data for h in host_pageable], n, ar.AR_F32, ar.AR_BF16,
+                      ar.AR_MODE_CHUNKED, check=False)
+    assert rc == E
+    # pinned host sources outside host-staged mode
+    assert ar.ar_reduce(ctx, [out], pinned, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, check=False) == E
+    # device sources in host-staged mode
+    assert ar.ar_reduce(ctx, [out], dev, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_HOST_STAGED, check=False) == E
+    # host destination
+    assert ar.ar_reduce(ctx, [pinned[0]], dev, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, check=False) == E
+    # a range running past the allocation
+    assert ar.ar_reduce(ctx, [out], dev, 1 << 28, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, check=False) == E
+    # misaligned source
+    assert ar.ar_reduce(ctx, [out], [dev[0].data_ptr() + 4, dev[1]], n - 4, ar.AR_F32, ar.AR_BF16,
+                        ar.AR_MODE_CHUNKED, check=False) == E
+    # narrow destination type
+    assert ar.ar_reduce(ctx, [out], dev, n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_CHUNKED,
+                        check=False) == ar.AR_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    # the context still works afterwards
+    ar.ar_reduce(ctx, [out], dev, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == 2.0)

@@ -110,7 +110,8 @@ def as_wire_typed(x: np.ndarray, wire: int) -> np.ndarray:
     if wire == BF16:
         return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
     if wire == F16:
-        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+        with np.errstate(over="ignore"):
+            return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
     raise ValueError(wire)
 
 
