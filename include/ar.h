@@ -96,8 +96,9 @@ typedef enum {
 
 /* Optional tuning, read once by ar_init.  Zero fields take the defaults;
  * environment variables AR_SINGLE_SHOT_MAX_BYTES, AR_CHUNK_BYTES,
- * AR_HOST_CHUNK_BYTES and AR_HOST_SLOTS override the defaults when cfg is
- * NULL or the field is zero. */
+ * AR_HOST_CHUNK_BYTES, AR_HOST_SLOTS, AR_GRID_WGS, AR_STREAM_KERNEL and
+ * AR_STORE_POLICY override the defaults when cfg is NULL or the field is
+ * zero. */
 typedef struct {
     size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank; 0 -> 1 MiB */
     size_t chunk_bytes;           /* CHUNKED / RS_BCAST plan unit, wire bytes per rank; 0 -> 4 MiB */
@@ -106,6 +107,8 @@ typedef struct {
     int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
     int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
     int    stream_kernel;         /* 0 auto, 1 register-staged, 2 LDS-staged */
+    int    store_policy;          /* destination stores: 0 auto (by size), 1 cached
+                                     write-back, 2 streaming (non-temporal) */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.
@@ -135,8 +138,8 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *   AR_ERR_INVALID for a NULL ctx / array / entry, R outside 2..16, a
  *   pointer not 16-byte aligned, an unknown type / mode / flag, a wire type
  *   wider than the destination, a destination that overlaps another
- *   destination or a source other than exactly in place (dst[d] == srcs[d]
- *   with equal element widths), n * element size overflowing size_t, or
+ *   destination or a source other than exactly in place (dst[d] equal to
+ *   some srcs[r], both binary32), n * element size overflowing size_t, or
  *   memory of the wrong kind for the mode (device pointers of another device,
  *   pageable host memory, host sources outside AR_MODE_HOST_STAGED);
  *   AR_ERR_UNSUPPORTED for dst_type != AR_F32;
@@ -170,6 +173,7 @@ typedef struct {
     size_t slice_start[AR_MAX_RANKS]; /* RS_BCAST: first element of rank r  */
     size_t slice_len[AR_MAX_RANKS];   /* RS_BCAST: elements of rank r       */
     size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*4   */
+    int    store_nt;      /* 1: streaming (non-temporal) destination stores */
 } ar_plan;
 
 /* Validate the arguments exactly as ar_reduce does, except the memory-kind

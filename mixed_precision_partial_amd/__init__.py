@@ -48,6 +48,7 @@ class ArConfig(ctypes.Structure):
         ("host_slots", ctypes.c_int),
         ("grid_wgs", ctypes.c_int),
         ("stream_kernel", ctypes.c_int),
+        ("store_policy", ctypes.c_int),
     ]
 
 
@@ -62,6 +63,7 @@ class ArPlan(ctypes.Structure):
         ("slice_start", ctypes.c_size_t * AR_MAX_RANKS),
         ("slice_len", ctypes.c_size_t * AR_MAX_RANKS),
         ("algo_bytes", ctypes.c_size_t),
+        ("store_nt", ctypes.c_int),
     ]
 
 

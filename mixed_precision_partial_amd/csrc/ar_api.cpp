@@ -41,6 +41,10 @@ constexpr size_t kDefaultChunkBytes = 4 * kMiB;
 constexpr size_t kHostChunkMin = 512 * 1024;
 constexpr size_t kHostChunkMax = 2 * kMiB;
 constexpr int kDefaultHostSlots = 3;
+// Destination writes above this many bytes per call use non-temporal stores;
+// smaller results are written back through L2 and the Infinity Cache, where
+// they drain while the next kernel reads (measured on MI355X).
+constexpr size_t kStoreStreamingMinBytes = 128 * kMiB;
 constexpr int kMaxHostSlots = 64;
 
 int elem_bytes(int t) { return t == AR_F32 ? 4 : 2; }
@@ -63,6 +67,7 @@ struct Config {
     int host_slots = kDefaultHostSlots;
     int grid_wgs = 0;
     int stream_kernel = 0;
+    int store_policy = 0;
 };
 
 int resolve_config(const ar_config *cfg, Config *out) {
@@ -73,8 +78,10 @@ int resolve_config(const ar_config *cfg, Config *out) {
     c.host_slots = static_cast<int>(env_size("AR_HOST_SLOTS", kDefaultHostSlots));
     c.grid_wgs = static_cast<int>(env_size("AR_GRID_WGS", 0));
     c.stream_kernel = static_cast<int>(env_size("AR_STREAM_KERNEL", 0));
+    c.store_policy = static_cast<int>(env_size("AR_STORE_POLICY", 0));
     if (cfg != nullptr) {
-        if (cfg->host_slots < 0 || cfg->grid_wgs < 0 || cfg->stream_kernel < 0 || cfg->stream_kernel > 2) {
+        if (cfg->host_slots < 0 || cfg->grid_wgs < 0 || cfg->stream_kernel < 0 || cfg->stream_kernel > 2 ||
+            cfg->store_policy < 0 || cfg->store_policy > 2) {
             return AR_ERR_INVALID;
         }
         if (cfg->single_shot_max_bytes) c.single_shot_max_bytes = cfg->single_shot_max_bytes;
@@ -83,10 +90,12 @@ int resolve_config(const ar_config *cfg, Config *out) {
         if (cfg->host_slots) c.host_slots = cfg->host_slots;
         if (cfg->grid_wgs) c.grid_wgs = cfg->grid_wgs;
         if (cfg->stream_kernel) c.stream_kernel = cfg->stream_kernel;
+        if (cfg->store_policy) c.store_policy = cfg->store_policy;
     }
     if (c.host_slots < 1 || c.host_slots > kMaxHostSlots) return AR_ERR_INVALID;
     if (c.stream_kernel < 0 || c.stream_kernel > 2) return AR_ERR_INVALID;
     if (c.grid_wgs < 0 || c.grid_wgs > 65535) return AR_ERR_INVALID;
+    if (c.store_policy < 0 || c.store_policy > 2) return AR_ERR_INVALID;
     *out = c;
     return AR_OK;
 }
@@ -189,6 +198,8 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             }
         }
         plan->algo_bytes = static_cast<size_t>(R) * src_len + static_cast<size_t>(n_dst) * dst_len;
+        const size_t written = static_cast<size_t>(n_dst) * dst_len;
+        plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written > kStoreStreamingMinBytes);
     }
     return AR_OK;
 }
@@ -291,6 +302,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             a.R = R;
             a.n_dst = R;
             a.chunk_elems = 0;
+            a.store_nt = plan.store_nt;
             unsigned max_len = 0;
             for (int r = 0; r < R; ++r) {
                 const size_t len = plan.slice_len[r] > p0 ? std::min(mpp::kMaxLaunchElems, plan.slice_len[r] - p0) : 0;
@@ -302,7 +314,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             }
             const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, max_len,
                                                            static_cast<unsigned>(R), c->cu_count, c->cfg.grid_wgs);
-            if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, a, shape, stream))) return rc;
+            if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, true, a, shape, stream))) return rc;
         }
         return AR_OK;
     }
@@ -313,27 +325,22 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         a.R = R;
         a.n_dst = 1;
         a.n = static_cast<unsigned>(len);
+        a.store_nt = plan.mode == AR_MODE_SINGLE_SHOT ? 0 : plan.store_nt;
         for (int r = 0; r < R; ++r) a.src[r] = static_cast<const char *>(srcs[r]) + p0 * sb;
         a.dst[0] = static_cast<float *>(dst[0]) + p0;
-        unsigned n_ranges = 1;
-        unsigned range_len = static_cast<unsigned>(len);
+        // CHUNKED: gridDim.y walks the plan's chunks; SINGLE_SHOT: one range
+        a.chunk_elems = static_cast<unsigned>(len);
         if (plan.mode == AR_MODE_CHUNKED) {
             a.chunk_elems = static_cast<unsigned>(std::min(plan.chunk_elems, len));
-            n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
-            if (n_ranges > 65535) {
+            if ((len + a.chunk_elems - 1) / a.chunk_elems > 65535) {
                 a.chunk_elems = static_cast<unsigned>(round_down((len + 65534) / 65535 + mpp::kWaveTile - 1,
                                                                  mpp::kWaveTile));
-                n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
             }
-            range_len = a.chunk_elems;
-        } else {
-            a.chunk_elems = 0;
-            a.slice_start[0] = 0;
-            a.slice_len[0] = static_cast<unsigned>(len);
         }
-        const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, range_len, n_ranges,
+        const unsigned n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
+        const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, a.chunk_elems, n_ranges,
                                                        c->cu_count, c->cfg.grid_wgs);
-        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, a, shape, stream))) return rc;
+        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, false, a, shape, stream))) return rc;
     }
     return AR_OK;
 }
@@ -402,14 +409,13 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         a.R = R;
         a.n_dst = 1;
         a.n = static_cast<unsigned>(len);
-        a.chunk_elems = 0;
-        a.slice_start[0] = 0;
-        a.slice_len[0] = static_cast<unsigned>(len);
+        a.store_nt = plan.store_nt;
+        a.chunk_elems = static_cast<unsigned>(len);
         for (int r = 0; r < R; ++r) a.src[r] = slot_base + r * rank_stride;
         a.dst[0] = static_cast<float *>(dst[0]) + e0;
         const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, static_cast<unsigned>(len), 1,
                                                        c->cu_count, c->cfg.grid_wgs);
-        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, a, shape, stream))) return rc;
+        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, false, a, shape, stream))) return rc;
         if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
         c->slot_used[slot] = 1;
     }

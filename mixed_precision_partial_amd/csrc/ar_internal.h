@@ -15,22 +15,27 @@ namespace mpp {
 // remainder of a range (< 512 elements) is done element by element.
 constexpr unsigned kWaveTile = 512;
 
-// Kernel arguments, passed by value (kernarg segment, ~470 B).  The launch
+// Kernel arguments, passed by value (kernarg segment, ~480 B).  The launch
 // covers R sources and n_dst destinations over gridDim.y ranges, each walked
-// by gridDim.x workgroups:
-//   chunk_elems > 0: range y is the plan chunk [y * chunk_elems,
-//                    min((y + 1) * chunk_elems, n));
-//   chunk_elems == 0: range y is the slice [slice_start[y], slice_start[y] +
-//                    slice_len[y]) (per-rank slices; gridDim.y <= AR_MAX_RANKS).
+// by the `waves` waves of gridDim.x workgroups:
+//   chunk ranges (CHUNKED, SINGLE_SHOT, host-staged chunks): range y is
+//       [y * chunk_elems, min((y + 1) * chunk_elems, n));
+//   slice ranges (RS_BCAST, a separate kernel instance): range y is
+//       [slice_start[y], slice_start[y] + slice_len[y]), gridDim.y <= R.
+// The scalars a wave needs first sit at the front so that one batch of
+// scalar loads fetches them together with the pointers.
 struct KernelArgs {
+    unsigned    n;
+    unsigned    chunk_elems;
+    unsigned    waves;      // waves per range: gridDim.x * (block / 64)
+    int         R;
+    int         n_dst;
+    int         store_nt;   // 1: non-temporal stores, 0: ordinary (cached) stores;
+                            // selects the kernel instance, not read on the GPU
     const void *src[AR_MAX_RANKS];
     float      *dst[AR_MAX_RANKS];
     uint64_t    slice_start[AR_MAX_RANKS];
     unsigned    slice_len[AR_MAX_RANKS];
-    unsigned    n;
-    unsigned    chunk_elems;
-    int         R;
-    int         n_dst;
 };
 
 // Largest element count one launch covers (32-bit element indices inside the
@@ -51,9 +56,10 @@ struct LaunchShape {
 };
 
 // Launch one kernel of `family` for the given element types on `stream`.
-// `wire` is an ar_dtype; `src_is_wire` selects 16-bit sources.  The caller
-// has validated every argument and sized the shape with plan_shape().
-hipError_t launch(Family family, int wire, bool src_is_wire, const KernelArgs &args,
+// `wire` is an ar_dtype; `src_is_wire` selects 16-bit sources; `sliced`
+// selects the slice-range instance.  The caller has validated every argument
+// and sized the shape with plan_shape(); launch() fills args.waves.
+hipError_t launch(Family family, int wire, bool src_is_wire, bool sliced, KernelArgs args,
                   const LaunchShape &shape, hipStream_t stream);
 
 // Pick a launch shape for `family` covering `max_slice_len` elements per

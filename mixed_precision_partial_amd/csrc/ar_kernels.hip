@@ -153,7 +153,7 @@ __device__ __forceinline__ void tile_values(const u32x4 (&raw)[Tile<SW>::kRaw], 
 }
 
 template <bool SW, bool NT>
-__device__ __forceinline__ void tile_store(float *dst, size_t t, int lane, const float (&acc)[8]) {
+__device__ __forceinline__ void tile_store_as(float *dst, size_t t, int lane, const float (&acc)[8]) {
     if constexpr (SW) {
         float *p = dst + t + 8 * lane;
         store16<NT>(p, acc[0], acc[1], acc[2], acc[3]);
@@ -165,12 +165,13 @@ __device__ __forceinline__ void tile_store(float *dst, size_t t, int lane, const
     }
 }
 
-// U consecutive wave tiles starting at element `t` (already slice-relative
-// plus slice offset).  All loads of the batch are issued before the fold.
+
+
+// Issue every load of a batch of U consecutive wave tiles starting at
+// element `t` (slice offset included) for the first R of RB sources.
 template <int W, bool SW, int RB, int U, bool NT>
-__device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int lane) {
-    constexpr int K = Tile<SW>::kRaw;
-    u32x4 raw[RB][U][K];
+__device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int lane,
+                                           u32x4 (&raw)[RB][U][Tile<SW>::kRaw]) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         if (r < 2 || r < a.R) {
@@ -178,6 +179,17 @@ __device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int 
             for (int u = 0; u < U; ++u) tile_load<W, SW, NT>(a.src[r], t + u * kWaveTile, lane, raw[r][u]);
         }
     }
+}
+
+// Fold the batch in rank order and store it to every destination.  Loads
+// use NT; stores use ST (non-temporal for writes far larger than the caches,
+// ordinary write-back stores otherwise, so a prefill-sized result drains from
+// L2 / Infinity Cache while the next kernel is already reading).  The store
+// policy is a template parameter: two stores that differ only in their cache
+// hint would be merged into one by the compiler.
+template <int W, bool SW, int RB, int U, bool NT, bool ST = NT>
+__device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int lane,
+                                           const u32x4 (&raw)[RB][U][Tile<SW>::kRaw]) {
     float acc[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) tile_values<W, SW>(raw[0][u], acc[u]);
@@ -197,9 +209,16 @@ __device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int 
     for (int d = 0; d < RB; ++d) {
         if (d < a.n_dst) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) tile_store<SW, NT>(a.dst[d], t + u * kWaveTile, lane, acc[u]);
+            for (int u = 0; u < U; ++u) tile_store_as<SW, ST>(a.dst[d], t + u * kWaveTile, lane, acc[u]);
         }
     }
+}
+
+template <int W, bool SW, int RB, int U, bool NT, bool ST = NT>
+__device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int lane) {
+    u32x4 raw[RB][U][Tile<SW>::kRaw];
+    load_batch<W, SW, RB, U, NT>(a, t, lane, raw);
+    fold_store<W, SW, RB, U, NT, ST>(a, t, lane, raw);
 }
 
 // Elements [begin, end) of the launch, one per lane per step (end - begin is
@@ -219,60 +238,269 @@ __device__ __forceinline__ void reduce_scalar(const KernelArgs &a, size_t begin,
     }
 }
 
-// Walk the wave tiles of this workgroup's slice: batches of U tiles first,
-// then single tiles, then the element remainder on wave 0 of workgroup 0.
-template <int W, bool SW, int RB, int U, bool NT>
-__device__ __forceinline__ void reduce_slice(const KernelArgs &a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const unsigned wpb = blockDim.x / kWave;
-    const unsigned gw = blockIdx.x * wpb + threadIdx.x / kWave;
-    const unsigned nw = gridDim.x * wpb;
-    size_t off;
-    unsigned len;
-    if (a.chunk_elems != 0) {
-        const unsigned start = blockIdx.y * a.chunk_elems;
-        off = start;
-        len = (a.n - start) < a.chunk_elems ? (a.n - start) : a.chunk_elems;
+// The element range [off, off + len) of this workgroup's gridDim.y index.
+// Both forms only read launch arguments at fixed offsets (the slice form
+// indexes with blockIdx.y, which is known at wave start), so a wave fetches
+// everything it needs in one batch of scalar loads.
+template <bool SLICED>
+__device__ __forceinline__ void range_of(const KernelArgs &a, size_t &off, unsigned &len) {
+    const unsigned y = blockIdx.y;
+    if constexpr (SLICED) {
+        off = a.slice_start[y];
+        len = a.slice_len[y];
     } else {
-        off = a.slice_start[blockIdx.y];
-        len = a.slice_len[blockIdx.y];
+        const unsigned start = y * a.chunk_elems;
+        const unsigned left = a.n - start;
+        off = start;
+        len = left < a.chunk_elems ? left : a.chunk_elems;
     }
+}
 
-    const unsigned big = kWaveTile * U;
-    const unsigned n_big = len / big;
-    for (unsigned t = gw; t < n_big; t += nw) {
-        reduce_tiles<W, SW, RB, U, NT>(a, off + (size_t)t * big, lane);
-    }
-    const unsigned done = n_big * big;
+// Whole wave tiles after the batched part, then the element remainder on
+// wave 0 of workgroup 0 of the range.
+template <int W, bool SW, int RB, int U, bool NT, bool ST>
+__device__ __forceinline__ void reduce_rest(const KernelArgs &a, size_t off, unsigned len, unsigned done,
+                                            unsigned gw, unsigned nw, int lane) {
     if constexpr (U > 1) {
         const unsigned n_one = (len - done) / kWaveTile;
         for (unsigned t = gw; t < n_one; t += nw) {
-            reduce_tiles<W, SW, RB, 1, NT>(a, off + done + (size_t)t * kWaveTile, lane);
+            reduce_tiles<W, SW, RB, 1, NT, ST>(a, off + done + (size_t)t * kWaveTile, lane);
         }
     }
     const unsigned vec_end = (len / kWaveTile) * kWaveTile;
-    if (vec_end < len && blockIdx.x == 0 && threadIdx.x < kWave) {
+    if (vec_end < len && gw == 0) {
         reduce_scalar<W, SW, RB>(a, off + vec_end, off + len, lane);
     }
 }
 
-template <int W, bool SW, int RB>
-__global__ __launch_bounds__(256) void k_single_shot(KernelArgs a) {
-    reduce_slice<W, SW, RB, 1, false>(a);
+// Walk the wave tiles of this workgroup's range: batches of U tiles strided
+// over the `a.waves` waves of the range, then the remainder.  BLOCK is the
+// workgroup size the kernel is always launched with (no read of blockDim).
+template <int W, bool SW, int RB, int U, bool NT, bool ST, int BLOCK, bool SLICED>
+__device__ __forceinline__ void reduce_range(const KernelArgs &a) {
+    constexpr unsigned wpb = BLOCK / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned gw = blockIdx.x * wpb + threadIdx.x / kWave;
+    const unsigned nw = a.waves;
+    size_t off;
+    unsigned len;
+    range_of<SLICED>(a, off, len);
+
+    constexpr unsigned big = kWaveTile * U;
+    const unsigned n_big = len / big;
+    for (unsigned t = gw; t < n_big; t += nw) {
+        reduce_tiles<W, SW, RB, U, NT, ST>(a, off + (size_t)t * big, lane);
+    }
+    reduce_rest<W, SW, RB, U, NT, ST>(a, off, len, n_big * big, gw, nw, lane);
 }
 
-// Tiles per batch of the streaming kernel: about 16 dwordx4 loads in flight
-// per lane (R x U x loads-per-tile), at least 1 and at most 4 tiles.
+constexpr int kSingleShotBlock = 64;
+constexpr int kStreamBlock = 256;
+constexpr int kLdsBlock = 64;
+
+template <int W, bool SW, int RB>
+__global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(KernelArgs a) {
+    reduce_range<W, SW, RB, 1, false, false, kSingleShotBlock, false>(a);
+}
+
+// Streaming-kernel tuning (compile-time; measured on MI355X):
+//   MPP_STREAM_LOADS  target dwordx4 loads per lane per batch (R x U x K)
+//   MPP_STREAM_MAXU   cap on tiles per batch
+//   MPP_STREAM_NT     1: non-temporal loads (streaming, no reuse); the store
+//                     policy is a launch argument
+//   MPP_STREAM_WG_PER_CU  0: one-shot grid (one batch per wave, the hardware
+//                     back-fills CUs as waves retire); k > 0: persistent grid
+//                     of k workgroups per CU
+#ifndef MPP_STREAM_LOADS
+#define MPP_STREAM_LOADS 8
+#endif
+#ifndef MPP_STREAM_MAXU
+#define MPP_STREAM_MAXU 4
+#endif
+#ifndef MPP_STREAM_NT
+#define MPP_STREAM_NT 1
+#endif
+#ifndef MPP_STREAM_WG_PER_CU
+#define MPP_STREAM_WG_PER_CU 0u
+#endif
+
+// Tiles per batch of the streaming kernel: about MPP_STREAM_LOADS dwordx4
+// loads per lane (R x U x loads-per-tile), at least 1 and at most MAXU tiles.
 constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
     const int per_tile = (src_is_wire ? 1 : 2) * rank_bucket;
-    const int u = 16 / per_tile;
-    return u < 1 ? 1 : (u > 4 ? 4 : u);
+    const int u = MPP_STREAM_LOADS / per_tile;
+    return u < 1 ? 1 : (u > MPP_STREAM_MAXU ? MPP_STREAM_MAXU : u);
 }
 
-template <int W, bool SW, int RB>
-__global__ __launch_bounds__(256) void k_stream_reg(KernelArgs a) {
-    reduce_slice<W, SW, RB, stream_batch(SW, RB), true>(a);
+// Register-staged streaming kernel: ST = non-temporal stores, SLICED = the
+// per-rank slice ranges of the broadcast schedule.
+#define MPP_STREAM_REG(NAME, ST, SLICED)                                                           \
+    template <int W, bool SW, int RB>                                                            \
+    __global__ __launch_bounds__(kStreamBlock) void NAME(KernelArgs a) {                         \
+        reduce_range<W, SW, RB, stream_batch(SW, RB), MPP_STREAM_NT != 0, ST, kStreamBlock, SLICED>(a); \
+    }
+MPP_STREAM_REG(k_stream_reg, false, false)
+MPP_STREAM_REG(k_stream_reg_nts, true, false)
+MPP_STREAM_REG(k_stream_reg_sl, false, true)
+MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
+#undef MPP_STREAM_REG
+
+// ---------------------------------------------------------------------------
+// LDS-staged streaming kernel (one wave per workgroup).  Each wave owns two
+// LDS stages of R x U x K blocks of 1 KiB.  global_load_lds_dwordx4 writes a
+// lane's 16 B straight into the stage (no VGPRs held while the load is in
+// flight); while the wave folds and stores the batch in one stage, the loads
+// of its next batch stream into the other.  A lane only ever reads back the
+// 16 B it loaded itself, so the stages need no barrier, only the wait on the
+// wave's own vector-memory counter.
+// ---------------------------------------------------------------------------
+#ifndef MPP_LDS_U
+#define MPP_LDS_U 1
+#endif
+#ifndef MPP_LDS_WG_PER_CU
+#define MPP_LDS_WG_PER_CU 16u
+#endif
+
+// Tiles per stage: MPP_LDS_U, reduced so one stage is at most 32 loads per
+// lane (the stage wait uses the 6-bit vector-memory counter).
+constexpr int lds_batch(bool src_is_wire, int rank_bucket) {
+    const int per_tile = (src_is_wire ? 1 : 2) * rank_bucket;
+    const int cap = 32 / per_tile;
+    const int u = MPP_LDS_U;
+    return u < 1 ? 1 : (u > cap ? (cap < 1 ? 1 : cap) : u);
 }
+
+template <int W, bool SW, int RB, int U>
+struct LdsStage {
+    static constexpr int kBlocks = RB * U * Tile<SW>::kRaw;   // 1 KiB each
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int W, bool SW, int RB, int U>
+__device__ __forceinline__ void lds_issue(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+    constexpr int K = Tile<SW>::kRaw;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        if (r < 2 || r < a.R) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const size_t e = SW ? t + u * kWaveTile + 8 * lane : t + u * kWaveTile + 256 * j + 4 * lane;
+                    const char *g = static_cast<const char *>(a.src[r]) + e * (SW ? 2 : 4);
+                    __builtin_amdgcn_global_load_lds(g, (lds_void *)(&stage[(r * U + u) * K + j][0]),
+                                                     16, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The loads of a stage are the oldest `L + (later loads)` in flight when the
+// next stage's L loads have just been issued: vector-memory loads retire in
+// order, so vmcnt(L) means every load of the older stage has landed in LDS.
+// L = R x U x K is only known at run time, hence the table of immediates.
+template <int MaxL>
+__device__ __forceinline__ void wait_stage(int L) {
+    if constexpr (MaxL >= 0) {
+        if (L == MaxL) {
+            wait_vm<MaxL>();
+            return;
+        }
+        wait_stage<MaxL - 1>(L);
+    } else {
+        wait_vm<0>();
+    }
+}
+
+// 16 B read of LDS at byte address `addr`, completed before it returns.  The
+// read is opaque to the compiler on purpose: its own wait insertion would
+// otherwise drain every outstanding LDS load (both stages) before any read.
+__device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+template <int W, bool SW, int RB, int U, bool ST>
+__device__ __forceinline__ void lds_consume(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+    constexpr int K = Tile<SW>::kRaw;
+    const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void *)(&stage[0][lane])));
+    u32x4 raw[RB][U][K];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        if (r < 2 || r < a.R) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < K; ++j) raw[r][u][j] = lds_read16(base + ((r * U + u) * K + j) * kWave * 16);
+        }
+    }
+    fold_store<W, SW, RB, U, true, ST>(a, t, lane, raw);
+}
+
+template <int W, bool SW, int RB, bool ST, bool SLICED>
+__device__ __forceinline__ void stream_lds(const KernelArgs &a) {
+    constexpr int U = lds_batch(SW, RB);
+    constexpr int NB = LdsStage<W, SW, RB, U>::kBlocks;
+    __shared__ u32x4 stage0[NB][kWave];
+    __shared__ u32x4 stage1[NB][kWave];
+    const int lane = threadIdx.x;
+    const unsigned gw = blockIdx.x;
+    const unsigned nw = a.waves;
+    size_t off;
+    unsigned len;
+    range_of<SLICED>(a, off, len);
+    constexpr unsigned big = kWaveTile * U;
+    const unsigned n_big = len / big;
+
+    // loads per stage (vector-memory instructions): R x U x K
+    const int L = (a.R < RB ? a.R : RB) * U * Tile<SW>::kRaw;
+    constexpr int kMaxL = RB * U * Tile<SW>::kRaw;
+
+    unsigned t = gw;
+    if (t < n_big) lds_issue<W, SW, RB, U>(a, off + (size_t)t * big, lane, stage0);
+    while (t < n_big) {
+        const unsigned t1 = t + nw;
+        if (t1 < n_big) {
+            lds_issue<W, SW, RB, U>(a, off + (size_t)t1 * big, lane, stage1);
+            wait_stage<kMaxL>(L);
+        } else {
+            wait_vm<0>();
+        }
+        lds_consume<W, SW, RB, U, ST>(a, off + (size_t)t * big, lane, stage0);
+        if (t1 >= n_big) break;
+        const unsigned t2 = t1 + nw;
+        if (t2 < n_big) {
+            lds_issue<W, SW, RB, U>(a, off + (size_t)t2 * big, lane, stage0);
+            wait_stage<kMaxL>(L);
+        } else {
+            wait_vm<0>();
+        }
+        lds_consume<W, SW, RB, U, ST>(a, off + (size_t)t1 * big, lane, stage1);
+        t = t2;
+    }
+    reduce_rest<W, SW, RB, U, true, ST>(a, off, len, n_big * big, gw, nw, lane);
+}
+
+#define MPP_STREAM_LDS(NAME, ST, SLICED)                                     \
+    template <int W, bool SW, int RB>                                      \
+    __global__ __launch_bounds__(kLdsBlock) void NAME(KernelArgs a) {      \
+        stream_lds<W, SW, RB, ST, SLICED>(a);                              \
+    }
+MPP_STREAM_LDS(k_stream_lds, false, false)
+MPP_STREAM_LDS(k_stream_lds_nts, true, false)
+MPP_STREAM_LDS(k_stream_lds_sl, false, true)
+MPP_STREAM_LDS(k_stream_lds_nts_sl, true, true)
+#undef MPP_STREAM_LDS
 
 // ---------------------------------------------------------------------------
 // Dispatch tables.  Combination index: 0 (f32 wire, f32 src), 1 (bf16 wire,
@@ -288,7 +516,13 @@ __global__ __launch_bounds__(256) void k_stream_reg(KernelArgs a) {
      MPP_ROW(KERNEL, AR_BF16, true), MPP_ROW(KERNEL, AR_F16, true)}
 
 const void *const kSingleShot[5][4] = MPP_TABLE(k_single_shot);
-const void *const kStreamReg[5][4] = MPP_TABLE(k_stream_reg);
+// [store_nt][sliced][combination][rank bucket]
+const void *const kStreamReg[2][2][5][4] = {
+    {MPP_TABLE(k_stream_reg), MPP_TABLE(k_stream_reg_sl)},
+    {MPP_TABLE(k_stream_reg_nts), MPP_TABLE(k_stream_reg_nts_sl)}};
+const void *const kStreamLds[2][2][5][4] = {
+    {MPP_TABLE(k_stream_lds), MPP_TABLE(k_stream_lds_sl)},
+    {MPP_TABLE(k_stream_lds_nts), MPP_TABLE(k_stream_lds_nts_sl)}};
 
 int combo_index(int wire, bool src_is_wire) {
     if (wire == AR_F32) return 0;
@@ -310,6 +544,7 @@ int bucket_ranks(int R) {
 
 unsigned batch_tiles(Family family, bool src_is_wire, int R) {
     if (family == Family::SingleShot) return 1;
+    if (family == Family::StreamLds) return static_cast<unsigned>(lds_batch(src_is_wire, bucket_ranks(R)));
     return static_cast<unsigned>(stream_batch(src_is_wire, bucket_ranks(R)));
 }
 
@@ -328,7 +563,7 @@ LaunchShape plan_shape(Family family, int wire, bool src_is_wire, int R, unsigne
     if (family == Family::SingleShot) {
         // One wave per tile, 64-thread workgroups: a decode vector spreads over
         // as many CUs as it has tiles, and no workgroup waits on a sibling.
-        s.block = 64;
+        s.block = kSingleShotBlock;
         const unsigned tiles = (max_slice_len + kWaveTile - 1) / kWaveTile;
         unsigned g = tiles == 0 ? 1 : tiles;
         const unsigned cap = static_cast<unsigned>(cu_count) * 16u;
@@ -336,31 +571,41 @@ LaunchShape plan_shape(Family family, int wire, bool src_is_wire, int R, unsigne
         s.grid_x = grid_override > 0 ? static_cast<unsigned>(grid_override) : g;
         return s;
     }
-    s.block = 256;
+    s.block = family == Family::StreamLds ? kLdsBlock : kStreamBlock;
     const unsigned wpb = s.block / kWave;
     const unsigned per_wave = stream_tile_elems(family, src_is_wire, R);
     const unsigned batches = (max_slice_len + per_wave - 1) / per_wave;
     unsigned g = (batches + wpb - 1) / wpb;
     if (g == 0) g = 1;
-    // resident-grid cap: 8 workgroups of 4 waves per CU, shared by the slices
-    unsigned cap = static_cast<unsigned>(cu_count) * 8u / (n_slices ? n_slices : 1u);
+    // optional persistent-grid cap (k workgroups per CU, shared by the ranges
+    // of the launch); 0 keeps the one-shot grid
+    const unsigned per_cu = family == Family::StreamLds ? MPP_LDS_WG_PER_CU : MPP_STREAM_WG_PER_CU;
+    unsigned cap = per_cu == 0 ? 65535u : static_cast<unsigned>(cu_count) * per_cu / (n_slices ? n_slices : 1u);
     if (cap < 1) cap = 1;
+    if (cap > 65535u) cap = 65535u;
     if (g > cap) g = cap;
     s.grid_x = grid_override > 0 ? static_cast<unsigned>(grid_override) : g;
     return s;
 }
 
-hipError_t launch(Family family, int wire, bool src_is_wire, const KernelArgs &args,
+hipError_t launch(Family family, int wire, bool src_is_wire, bool sliced, KernelArgs a,
                   const LaunchShape &shape, hipStream_t stream) {
     const int c = combo_index(wire, src_is_wire);
-    const int b = bucket_index(args.R);
+    const int b = bucket_index(a.R);
+    const int nt = a.store_nt ? 1 : 0;
+    const int sl = sliced ? 1 : 0;
     const void *fn = nullptr;
     switch (family) {
-    case Family::SingleShot: fn = kSingleShot[c][b]; break;
-    case Family::StreamReg:  fn = kStreamReg[c][b]; break;
-    default:                 return hipErrorNotSupported;
+    case Family::SingleShot:
+        if (sliced) return hipErrorNotSupported;
+        fn = kSingleShot[c][b];
+        break;
+    case Family::StreamReg: fn = kStreamReg[nt][sl][c][b]; break;
+    case Family::StreamLds: fn = kStreamLds[nt][sl][c][b]; break;
+    default: return hipErrorNotSupported;
     }
-    KernelArgs a = args;
+    if (shape.block % kWave != 0) return hipErrorInvalidValue;
+    a.waves = shape.grid_x * (shape.block / kWave);
     void *kargs[] = {&a};
     return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1), kargs,
                            shape.lds_bytes, stream);

@@ -44,8 +44,8 @@ def test_status_strings():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 3 * 4 + 4   # padded to 8
-    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8
+    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 4 * 4
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 8   # int + pad
 
 
 def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
