@@ -57,18 +57,32 @@ def measured_traffic(algo_bytes: int):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--sets", type=int, default=8, help="rotated input/output sets (>= 6 defeats the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--extras", action="store_true", help="also time the other schedules (stderr lines)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="write profiles/ summary of a rocprofv3 --kernel-trace --stats output dir")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/ HBM-traffic summary from two rocprofv3 --pmc runs "
+                        "(FETCH_SIZE, WRITE_SIZE) of --profile-pass")
+    p.add_argument("--profile-pass", action="store_true",
+                   help="short run for hardware-counter collection: a few reduce steps, then a "
+                        "plain elementwise copy of known size used to calibrate the counters")
     return p.parse_args()
 
 
 def main() -> int:
     args = parse()
+    if args.summarize_trace or args.summarize_pmc:
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace)
+        if args.summarize_pmc:
+            summarize_pmc(*args.summarize_pmc)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the reduce is run with every "
               "rank simulated on a single MI355X, so there is no multi-GPU figure", file=sys.stderr)
@@ -83,6 +97,8 @@ def main() -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     ar.load_library()   # fails loudly when the HIP library was not built
+    if args.profile_pass:
+        return profile_pass(torch, ar, wl, args)
     w = wl.WORKLOADS["prefill_bf16"]
     R, n = w.R, w.n
     S = max(1, args.sets)
@@ -197,6 +213,119 @@ def main() -> int:
         "extras": extras,
     }
     print(json.dumps(result), flush=True)
+    return 0
+
+
+CALIBRATION_BYTES = 64 << 20   # read and written once per calibration launch
+REDUCE_KERNEL = "k_stream_reg<2, false, 2>"   # bf16 wire, fp32 sources, R bucket 2
+CALIBRATION_KERNEL = "vectorized_elementwise_kernel"
+TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py"
+PMC_CMD = ("cd /tmp && rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {tag} -- "
+           "python3 bench.py --profile-pass")
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_trace(directory: str) -> None:
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    out = os.path.join(ROOT, "profiles", "kernel_trace_prefill_bf16.md")
+    lines = ["# rocprofv3 kernel trace: bench.py default run (prefill reduce + decode calls)", "",
+             f"Command: `{TRACE_CMD}`", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows[:8]:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("|", "/")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
+    red = [r for r in rows if REDUCE_KERNEL in r["Name"]]
+    if red:
+        avg_us = float(red[0]["AverageNs"]) / 1e3
+        algo = 100_663_296
+        lines += ["", f"Prefill reduce kernel `{REDUCE_KERNEL}`: average {avg_us:.3f} us per launch = "
+                      f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch)."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
+    def per_kernel(directory):
+        rows = _csv_rows(directory, "counter_collection.csv")
+        red = [float(r["Counter_Value"]) for r in rows if REDUCE_KERNEL in r["Kernel_Name"]]
+        cal = [float(r["Counter_Value"]) for r in rows if CALIBRATION_KERNEL in r["Kernel_Name"]]
+        if not red or not cal:
+            raise RuntimeError(f"missing dispatches in {directory}")
+        return sum(red) / len(red), len(red), sum(cal) / len(cal), len(cal)
+
+    f_red, nf, f_cal, ncf = per_kernel(fetch_dir)
+    w_red, nw, w_cal, ncw = per_kernel(write_dir)
+    known_kib = CALIBRATION_BYTES / 1024
+    f_scale, w_scale = known_kib / f_cal, known_kib / w_cal
+    fetch_b = f_red * f_scale * 1024
+    write_b = w_red * w_scale * 1024
+    algo = 100_663_296
+    traffic = {
+        "kernel": REDUCE_KERNEL,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": round(f_red, 1), "fetch_dispatches": nf,
+        "write_size_kib_per_dispatch": round(w_red, 1), "write_dispatches": nw,
+        "calibration": {"kernel": "torch.neg on 64 MiB (reads and writes CALIBRATION_BYTES)",
+                        "fetch_kib": round(f_cal, 1), "write_kib": round(w_cal, 1),
+                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+        "algo_bytes_per_launch": algo,
+        "traffic_over_algo": round((fetch_b + write_b) / algo, 4),
+        "commands": [PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"),
+                     PMC_CMD.format(counter="WRITE_SIZE", tag="write")],
+    }
+    with open(PROFILE_TRAFFIC, "w") as fh:
+        json.dump(traffic, fh, indent=1)
+    md = os.path.join(ROOT, "profiles", "traffic_prefill_bf16.md")
+    with open(md, "w") as fh:
+        fh.write("# HBM traffic of the prefill reduce kernel (rocprofv3 --pmc)\n\n")
+        for c in traffic["commands"]:
+            fh.write(f"- `{c}`\n")
+        fh.write(f"\nKernel `{REDUCE_KERNEL}`, {nf} dispatches (rotated input sets).\n\n")
+        fh.write("| counter | reduce KiB/dispatch | calibration KiB/dispatch (64 MiB known) | scale | "
+                 "reduce bytes after scaling |\n|---|---|---|---|---|\n")
+        fh.write(f"| FETCH_SIZE | {f_red:.1f} | {f_cal:.1f} | {f_scale:.4f} | {fetch_b:.0f} |\n")
+        fh.write(f"| WRITE_SIZE | {w_red:.1f} | {w_cal:.1f} | {w_scale:.4f} | {write_b:.0f} |\n\n")
+        fh.write(f"HBM traffic per launch {fetch_b + write_b:.0f} B against {algo} algorithmic B "
+                 f"(ratio {(fetch_b + write_b) / algo:.4f}); kernel source hash "
+                 f"{traffic['kernel_source_sha256_16']}.\n")
+    print(PROFILE_TRAFFIC, md)
+
+
+def profile_pass(torch, ar, wl, args):
+    """Counter pass: 8 rotated prefill reduces x 3, then 8 torch.neg launches that
+    read and write CALIBRATION_BYTES each (a plain copy-shaped kernel)."""
+    w = wl.WORKLOADS["prefill_bf16"]
+    S = max(1, args.sets)
+    srcs = [[torch.randn(w.n, device="cuda") for _ in range(w.R)] for _ in range(S)]
+    dsts = [torch.empty(w.n, device="cuda") for _ in range(S)]
+    ctx = ar.ar_init(0)
+    stream = torch.cuda.current_stream()
+    for k in range(3 * S):
+        ar.ar_reduce(ctx, [dsts[k % S]], srcs[k % S], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED, stream=stream)
+    torch.cuda.synchronize()
+    n = CALIBRATION_BYTES // 4
+    a = [torch.randn(n, device="cuda") for _ in range(4)]
+    b = [torch.empty(n, device="cuda") for _ in range(4)]
+    for k in range(8):
+        torch.neg(a[k % 4], out=b[k % 4])
+    torch.cuda.synchronize()
+    ar.ar_free(ctx)
+    log(f"profile pass done: {3 * S} reduces of {w.n} elements, 8 calibration copies of {CALIBRATION_BYTES} B")
     return 0
 
 

@@ -107,8 +107,10 @@ typedef struct {
     int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
     int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
     int    stream_kernel;         /* 0 auto, 1 register-staged, 2 LDS-staged */
-    int    store_policy;          /* destination stores: 0 auto (by size), 1 cached
-                                     write-back, 2 streaming (non-temporal) */
+    int    store_policy;          /* destination stores: 0 auto (streaming when the
+                                     call writes at least as many bytes as it
+                                     reads), 1 cached write-back, 2 streaming
+                                     (non-temporal) */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.

@@ -41,10 +41,7 @@ constexpr size_t kDefaultChunkBytes = 4 * kMiB;
 constexpr size_t kHostChunkMin = 512 * 1024;
 constexpr size_t kHostChunkMax = 2 * kMiB;
 constexpr int kDefaultHostSlots = 3;
-// Destination writes above this many bytes per call use non-temporal stores;
-// smaller results are written back through L2 and the Infinity Cache, where
-// they drain while the next kernel reads (measured on MI355X).
-constexpr size_t kStoreStreamingMinBytes = 128 * kMiB;
+
 constexpr int kMaxHostSlots = 64;
 
 int elem_bytes(int t) { return t == AR_F32 ? 4 : 2; }
@@ -198,8 +195,14 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             }
         }
         plan->algo_bytes = static_cast<size_t>(R) * src_len + static_cast<size_t>(n_dst) * dst_len;
+        // Automatic store policy, measured on MI355X: when the call writes at
+        // least as many bytes as it reads (broadcast to R destinations, 16-bit
+        // sources at R = 2) non-temporal stores are faster; when reads dominate,
+        // ordinary write-back stores drain from L2 / Infinity Cache while the
+        // reads stream and are faster.
         const size_t written = static_cast<size_t>(n_dst) * dst_len;
-        plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written > kStoreStreamingMinBytes);
+        const size_t read = static_cast<size_t>(R) * src_len;
+        plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written >= read);
     }
     return AR_OK;
 }

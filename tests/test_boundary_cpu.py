@@ -183,3 +183,17 @@ def test_reduce_rejects_before_runtime(rank):
     srcs = (ctypes.c_void_p * rank)(*A[1:1 + rank])
     dsts = (ctypes.c_void_p * 1)(A[30])
     assert lib.ar_reduce(None, dsts, srcs, rank, 64, ar.AR_F32, ar.AR_BF16, 0, None) == ar.AR_ERR_INVALID
+
+
+def test_store_policy_rule():
+    n = 2048 * 4096
+    # fp32 sources, R=2, one destination: reads dominate -> cached stores
+    assert q(n, mode=ar.AR_MODE_CHUNKED)[1].store_nt == 0
+    # 16-bit sources, R=2: as many bytes written as read -> streaming stores
+    assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].store_nt == 1
+    # broadcast to every rank -> streaming stores
+    assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST, wire=ar.AR_F16)[1].store_nt == 1
+    # explicit policies win
+    assert q(n, mode=ar.AR_MODE_CHUNKED, config={"store_policy": 2})[1].store_nt == 1
+    assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST, config={"store_policy": 1})[1].store_nt == 0
+    assert q(64, config={"store_policy": 3})[0] == ar.AR_ERR_INVALID
