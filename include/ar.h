@@ -69,7 +69,8 @@ typedef enum { AR_F32 = 0, AR_F16 = 1, AR_BF16 = 2 } ar_dtype;
  *                        (n_dst = R; `dst` holds R pointers).
  *   AR_MODE_HOST_STAGED  sources are pinned host buffers; chunks are copied
  *                        to HBM scratch on an internal copy stream while the
- *                        add kernel runs on `hip_stream`.
+ *                        add kernel runs on `hip_stream` (or, with host_path
+ *                        2, the kernel reads the pinned buffers directly).
  * The result bytes do not depend on the mode, the chunk size or the launch
  * shape. */
 enum {
@@ -96,14 +97,14 @@ typedef enum {
 
 /* Optional tuning, read once by ar_init.  Zero fields take the defaults;
  * environment variables AR_SINGLE_SHOT_MAX_BYTES, AR_CHUNK_BYTES,
- * AR_HOST_CHUNK_BYTES, AR_HOST_SLOTS, AR_GRID_WGS, AR_STREAM_KERNEL and
- * AR_STORE_POLICY override the defaults when cfg is NULL or the field is
- * zero. */
+ * AR_HOST_CHUNK_BYTES, AR_HOST_SLOTS, AR_GRID_WGS, AR_STREAM_KERNEL,
+ * AR_STORE_POLICY and AR_HOST_PATH override the defaults when cfg is NULL or
+ * the field is zero. */
 typedef struct {
     size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank; 0 -> 1 MiB */
     size_t chunk_bytes;           /* CHUNKED / RS_BCAST plan unit, wire bytes per rank; 0 -> 4 MiB */
     size_t host_chunk_bytes;      /* HOST_STAGED copy unit, source bytes per rank;
-                                     0 -> clamp(bytes/4, 512 KiB, 2 MiB) per call */
+                                     0 -> clamp(bytes/4, 512 KiB, 16 MiB) per call */
     int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
     int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
     int    stream_kernel;         /* 0 auto, 1 register-staged, 2 LDS-staged */
@@ -111,6 +112,9 @@ typedef struct {
                                      call writes at least as many bytes as it
                                      reads), 1 cached write-back, 2 streaming
                                      (non-temporal) */
+    int    host_path;             /* HOST_STAGED: 0 auto, 1 copy-engine chunks into HBM
+                                     scratch, 2 the kernel reads the pinned buffers
+                                     directly over PCIe (no scratch) */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.
@@ -176,6 +180,7 @@ typedef struct {
     size_t slice_len[AR_MAX_RANKS];   /* RS_BCAST: elements of rank r       */
     size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*4   */
     int    store_nt;      /* 1: streaming (non-temporal) destination stores */
+    int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
 } ar_plan;
 
 /* Validate the arguments exactly as ar_reduce does, except the memory-kind

@@ -49,6 +49,7 @@ class ArConfig(ctypes.Structure):
         ("grid_wgs", ctypes.c_int),
         ("stream_kernel", ctypes.c_int),
         ("store_policy", ctypes.c_int),
+        ("host_path", ctypes.c_int),
     ]
 
 
@@ -64,6 +65,7 @@ class ArPlan(ctypes.Structure):
         ("slice_len", ctypes.c_size_t * AR_MAX_RANKS),
         ("algo_bytes", ctypes.c_size_t),
         ("store_nt", ctypes.c_int),
+        ("host_direct", ctypes.c_int),
     ]
 
 

@@ -38,8 +38,11 @@ namespace {
 constexpr size_t kMiB = size_t(1) << 20;
 constexpr size_t kDefaultSingleShotMax = 1 * kMiB;
 constexpr size_t kDefaultChunkBytes = 4 * kMiB;
+// Host-staged copy chunk: clamp(bytes per rank / 4, 512 KiB, 16 MiB) of source
+// bytes per rank -- about four chunks in flight, each large enough that the
+// fixed cost of a copy is small next to its transfer time over PCIe.
 constexpr size_t kHostChunkMin = 512 * 1024;
-constexpr size_t kHostChunkMax = 2 * kMiB;
+constexpr size_t kHostChunkMax = 16 * kMiB;
 constexpr int kDefaultHostSlots = 3;
 
 constexpr int kMaxHostSlots = 64;
@@ -65,6 +68,7 @@ struct Config {
     int grid_wgs = 0;
     int stream_kernel = 0;
     int store_policy = 0;
+    int host_path = 0;
 };
 
 int resolve_config(const ar_config *cfg, Config *out) {
@@ -76,9 +80,10 @@ int resolve_config(const ar_config *cfg, Config *out) {
     c.grid_wgs = static_cast<int>(env_size("AR_GRID_WGS", 0));
     c.stream_kernel = static_cast<int>(env_size("AR_STREAM_KERNEL", 0));
     c.store_policy = static_cast<int>(env_size("AR_STORE_POLICY", 0));
+    c.host_path = static_cast<int>(env_size("AR_HOST_PATH", 0));
     if (cfg != nullptr) {
         if (cfg->host_slots < 0 || cfg->grid_wgs < 0 || cfg->stream_kernel < 0 || cfg->stream_kernel > 2 ||
-            cfg->store_policy < 0 || cfg->store_policy > 2) {
+            cfg->store_policy < 0 || cfg->store_policy > 2 || cfg->host_path < 0 || cfg->host_path > 2) {
             return AR_ERR_INVALID;
         }
         if (cfg->single_shot_max_bytes) c.single_shot_max_bytes = cfg->single_shot_max_bytes;
@@ -88,11 +93,13 @@ int resolve_config(const ar_config *cfg, Config *out) {
         if (cfg->grid_wgs) c.grid_wgs = cfg->grid_wgs;
         if (cfg->stream_kernel) c.stream_kernel = cfg->stream_kernel;
         if (cfg->store_policy) c.store_policy = cfg->store_policy;
+        if (cfg->host_path) c.host_path = cfg->host_path;
     }
     if (c.host_slots < 1 || c.host_slots > kMaxHostSlots) return AR_ERR_INVALID;
     if (c.stream_kernel < 0 || c.stream_kernel > 2) return AR_ERR_INVALID;
     if (c.grid_wgs < 0 || c.grid_wgs > 65535) return AR_ERR_INVALID;
     if (c.store_policy < 0 || c.store_policy > 2) return AR_ERR_INVALID;
+    if (c.host_path < 0 || c.host_path > 2) return AR_ERR_INVALID;
     *out = c;
     return AR_OK;
 }
@@ -203,6 +210,9 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         const size_t written = static_cast<size_t>(n_dst) * dst_len;
         const size_t read = static_cast<size_t>(R) * src_len;
         plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written >= read);
+        // host-staged sources: copy-engine pipeline (1) or the kernel reading
+        // the pinned buffers over PCIe directly (2)
+        plan->host_direct = resolved == AR_MODE_HOST_STAGED && cfg.host_path == 2;
     }
     return AR_OK;
 }
@@ -255,7 +265,7 @@ enum class Kind { Device, PinnedHost, Other };
 // Memory kind of [p, p + bytes) and whether the whole range lies inside one
 // allocation of the runtime.  Clears the runtime's sticky last-error on a
 // failed lookup so the caller's next HIP call does not see it.
-Kind memory_kind(const void *p, size_t bytes, int device) {
+Kind memory_kind(const void *p, size_t bytes, int device, const void **device_view = nullptr) {
     hipPointerAttribute_t at;
     std::memset(&at, 0, sizeof(at));
     if (hipPointerGetAttributes(&at, p) != hipSuccess) {
@@ -279,6 +289,12 @@ Kind memory_kind(const void *p, size_t bytes, int device) {
     const uintptr_t b = reinterpret_cast<uintptr_t>(base);
     const uintptr_t q = reinterpret_cast<uintptr_t>(p);
     if (q < b || q - b > size || bytes > size - (q - b)) return Kind::Other;
+    if (device_view != nullptr) {
+        // the address kernels use for this memory (pinned host memory is mapped
+        // into the device's address space; the runtime reports where)
+        *device_view = k == Kind::PinnedHost ? at.devicePointer : p;
+        if (*device_view == nullptr) return Kind::Other;
+    }
     return k;
 }
 
@@ -529,8 +545,9 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
     if (n == 0) return AR_OK;
 
     const Kind want_src = plan.mode == AR_MODE_HOST_STAGED ? Kind::PinnedHost : Kind::Device;
+    const void *src_view[AR_MAX_RANKS];
     for (int r = 0; r < R; ++r) {
-        if (memory_kind(srcs[r], src_len, ctx->device) != want_src) return AR_ERR_INVALID;
+        if (memory_kind(srcs[r], src_len, ctx->device, &src_view[r]) != want_src) return AR_ERR_INVALID;
     }
     for (int d = 0; d < plan.n_dst; ++d) {
         if (memory_kind(dst[d], dst_len, ctx->device) != Kind::Device) return AR_ERR_INVALID;
@@ -538,6 +555,13 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (plan.mode == AR_MODE_HOST_STAGED) {
+        if (plan.host_direct) {
+            // one streaming launch whose loads cross PCIe: the kernel reads the
+            // pinned partials through their device mapping, no HBM staging
+            ar_plan direct = plan;
+            direct.mode = AR_MODE_CHUNKED;
+            return run_device(ctx, direct, dst, src_view, R, n, wire_type, src_wire, stream);
+        }
         return run_host_staged(ctx, plan, dst, srcs, R, n, wire_type, src_wire, stream);
     }
     return run_device(ctx, plan, dst, srcs, R, n, wire_type, src_wire, stream);

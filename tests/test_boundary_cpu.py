@@ -44,8 +44,8 @@ def test_status_strings():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 4 * 4
-    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 8   # int + pad
+    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 5 * 4 + 4   # padded to 8
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 2 * 4
 
 
 def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
@@ -146,10 +146,15 @@ def test_slice_plan_partitions_range():
 
 
 def test_host_chunk_heuristic():
-    # clamp(bytes / 4, 512 KiB, 2 MiB) of source bytes per rank
+    # clamp(bytes / 4, 512 KiB, 16 MiB) of source bytes per rank
     n = 8192 * 8192
     rc, p = q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
-    assert p.chunk_elems == (2 * MiB) // 2 and p.n_chunks == n // ((2 * MiB) // 2)
+    assert p.chunk_elems == (16 * MiB) // 2 and p.n_chunks == n // ((16 * MiB) // 2)
+    assert p.host_direct == 0
+    rc, p = q(n // 4, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
+    assert p.chunk_elems == (n // 4 * 2 // 4) // 2
+    rc, p = q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, config={"host_path": 2})
+    assert p.host_direct == 1
     rc, p = q(100_000, mode=ar.AR_MODE_HOST_STAGED)
     assert p.chunk_elems == (512 * 1024) // 4
     rc, p = q(n, mode=ar.AR_MODE_HOST_STAGED, config={"host_chunk_bytes": 1 << 16})

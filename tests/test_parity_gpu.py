@@ -139,6 +139,14 @@ def test_host_staged_bf16_and_hbm(ctx):
     want_wire = oracle.reduce(pre, w.wire, src_type=w.wire)[0]
     outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_HOST_STAGED, src_wire=True)
     assert_bits_equal(outs[0], want_wire, "host_staged bf16")
+    log_case("host_staged_bf16 direct reads of pinned memory")
+    c = ar.ar_init(0, {"host_path": 2})
+    try:
+        outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_HOST_STAGED, src_wire=True, config_ctx=c)
+        assert_bits_equal(outs[0], want_wire, "host_staged bf16 direct")
+    finally:
+        torch.cuda.synchronize()
+        ar.ar_free(c)
     log_case("host_staged_bf16 same shape from HBM, wire-typed sources")
     outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_CHUNKED, src_wire=True)
     assert_bits_equal(outs[0], want_wire, "hbm chunked bf16 sources")
@@ -156,6 +164,28 @@ TAIL_N = [1, 3, 7, 8, 9, 63, 64, 65, 511, 512, 513, 1023, 1025, 2047, 2048, 2049
           8191, 8193, 12289, 65537, 131071]
 
 
+# Kernel instances: register / LDS-staged streaming family x cached / streaming stores
+KERNEL_CONFIGS = {
+    "reg_cached": {"stream_kernel": 1, "store_policy": 1},
+    "reg_streaming": {"stream_kernel": 1, "store_policy": 2},
+    "lds_cached": {"stream_kernel": 2, "store_policy": 1},
+    "lds_streaming": {"stream_kernel": 2, "store_policy": 2},
+    "host_direct": {"host_path": 2},
+}
+
+
+@pytest.fixture(scope="module")
+def kctx():
+    """One context per kernel-instance configuration."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    ctxs = {k: ar.ar_init(0, v) for k, v in KERNEL_CONFIGS.items()}
+    yield ctxs
+    torch.cuda.synchronize()
+    for c in ctxs.values():
+        ar.ar_free(c)
+
+
 @pytest.mark.parametrize("mode_name", ["single_shot", "chunked", "rs_bcast"])
 def test_tails_all_wires_and_widths(ctx, mode_name):
     mode = MODES[mode_name]
@@ -168,6 +198,23 @@ def test_tails_all_wires_and_widths(ctx, mode_name):
                 log_case(what)
                 srcs = wl.random_partials(2000 + i, wire, R, n, dist="wide")
                 check_against_oracle(ctx, srcs, wire, mode, src_wire, what)
+
+
+@pytest.mark.parametrize("kname", list(KERNEL_CONFIGS))
+@pytest.mark.parametrize("mode_name", ["chunked", "rs_bcast", "host_staged"])
+def test_every_kernel_instance(kctx, kname, mode_name):
+    """Both streaming families x both store policies x chunk / slice ranges, every rank
+    bucket, both source widths, ragged tails."""
+    mode = MODES[mode_name]
+    cases = [(2, 70_001), (3, 4097), (4, 131_072 + 515), (7, 9_000), (8, 65_536 + 1), (13, 2_049),
+             (16, 20_480 + 3)]
+    for i, (R, n) in enumerate(cases):
+        for wire_name, wire in WIRES.items():
+            for src_wire in ([False, True] if wire != ar.AR_F32 else [False]):
+                what = f"{kname} {mode_name} R={R} n={n} wire={wire_name} src_wire={src_wire}"
+                log_case(what)
+                srcs = wl.random_partials(8000 + i, wire, R, n, dist="wide")
+                check_against_oracle(kctx[kname], srcs, wire, mode, src_wire, what)
 
 
 def test_small_chunks_many_ranges(ctx):
