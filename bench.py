@@ -170,7 +170,7 @@ def main() -> int:
                       f"({cpu_s + one:.1f} s, single-threaded scalar C oracle)",
         }
 
-    extras = {}
+    extras = {"ceilings_prefill_size": ceilings(torch, n, S)}
     if not args.no_decode:
         extras["decode_bf16"] = decode_latency(torch, ar, wl)
     if args.extras:
@@ -329,6 +329,32 @@ def profile_pass(torch, ar, wl, args):
     return 0
 
 
+def ceilings(torch, n, sets):
+    """Achievable rates at the prefill size on random data, same rotation: a
+    plain device copy and torch's two-read / one-write add (GB/s of bytes moved)."""
+    stream = torch.cuda.current_stream()
+    a = [torch.rand(n, device="cuda") - 0.5 for _ in range(sets)]
+    b = [torch.rand(n, device="cuda") - 0.5 for _ in range(sets)]
+    c = [torch.empty(n, device="cuda") for _ in range(sets)]
+
+    def rate(fn, nbytes, reps=400):
+        for i in range(sets):
+            fn(i)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for k in range(reps):
+            fn(k % sets)
+        e.record(stream)
+        torch.cuda.synchronize()
+        return round(nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9, 1)
+
+    out = {"copy_GB/s": rate(lambda i: c[i].copy_(a[i]), 2 * 4 * n),
+           "add_2r1w_GB/s": rate(lambda i: torch.add(a[i], b[i], out=c[i]), 3 * 4 * n)}
+    log(f"ceilings at the prefill size: {out}")
+    return out
+
+
 def decode_latency(torch, ar, wl):
     """10,000 sequential single-shot calls on fresh seeded data (all pre-staged in HBM)."""
     w = wl.WORKLOADS["decode_bf16"]
@@ -362,6 +388,24 @@ def decode_latency(torch, ar, wl):
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t0
     us_async = start.elapsed_time(end) * 1e3 / calls
+    # the same calls captured once into a HIP graph and replayed: the
+    # per-call cost without Python or runtime launch overhead
+    graph_calls = 1000
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        gs = torch.cuda.current_stream()
+        for c in range(graph_calls):
+            ar.ar_reduce(ctx, dsts[c], srcs[c], n, ar.AR_F32, w.wire, ar.AR_MODE_SINGLE_SHOT, stream=gs)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = calls // graph_calls
+    start.record(stream)
+    for _ in range(reps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us_graph = start.elapsed_time(end) * 1e3 / (reps * graph_calls)
+    del g
     # per-call round trip: enqueue + stream synchronize, wall clock
     lat = np.empty(2000)
     for i in range(lat.size):
@@ -372,6 +416,7 @@ def decode_latency(torch, ar, wl):
     ar.ar_free(ctx)
     res = {
         "us_per_call_async": round(us_async, 3),
+        "us_per_call_graph_replay": round(us_graph, 3),
         "host_enqueue_us_per_call": round(host_s * 1e6 / calls, 3),
         "us_per_call_sync_p50": round(float(np.percentile(lat, 50)), 2),
         "us_per_call_sync_p99": round(float(np.percentile(lat, 99)), 2),

@@ -107,7 +107,9 @@ typedef struct {
                                      0 -> clamp(bytes/4, 512 KiB, 16 MiB) per call */
     int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
     int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
-    int    stream_kernel;         /* 0 auto, 1 register-staged, 2 LDS-staged */
+    int    stream_kernel;         /* 0 auto (LDS-staged for two 16-bit sources,
+                                     register-staged otherwise), 1 register-staged,
+                                     2 LDS-staged */
     int    store_policy;          /* destination stores: 0 auto (streaming when the
                                      call writes at least as many bytes as it
                                      reads), 1 cached write-back, 2 streaming
@@ -181,6 +183,7 @@ typedef struct {
     size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*4   */
     int    store_nt;      /* 1: streaming (non-temporal) destination stores */
     int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
+    int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged   */
 } ar_plan;
 
 /* Validate the arguments exactly as ar_reduce does, except the memory-kind

@@ -66,6 +66,7 @@ class ArPlan(ctypes.Structure):
         ("algo_bytes", ctypes.c_size_t),
         ("store_nt", ctypes.c_int),
         ("host_direct", ctypes.c_int),
+        ("stream_kernel", ctypes.c_int),
     ]
 
 

@@ -213,6 +213,16 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // host-staged sources: copy-engine pipeline (1) or the kernel reading
         // the pinned buffers over PCIe directly (2)
         plan->host_direct = resolved == AR_MODE_HOST_STAGED && cfg.host_path == 2;
+        // streaming kernel family: explicit choice, else measured on MI355X --
+        // the LDS-staged double buffer wins for two 16-bit sources (as many
+        // bytes written as read, short tiles), the register kernel elsewhere
+        if (resolved == AR_MODE_SINGLE_SHOT) {
+            plan->stream_kernel = 0;
+        } else if (cfg.stream_kernel != 0) {
+            plan->stream_kernel = cfg.stream_kernel;
+        } else {
+            plan->stream_kernel = (src_wire && R == 2) ? 2 : 1;
+        }
     }
     return AR_OK;
 }
@@ -298,8 +308,8 @@ Kind memory_kind(const void *p, size_t bytes, int device, const void **device_vi
     return k;
 }
 
-mpp::Family stream_family(const Config &cfg) {
-    return cfg.stream_kernel == 2 ? mpp::Family::StreamLds : mpp::Family::StreamReg;
+mpp::Family stream_family(const ar_plan &plan) {
+    return plan.stream_kernel == 2 ? mpp::Family::StreamLds : mpp::Family::StreamReg;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_RUNTIME; }
@@ -308,7 +318,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_RUNTIME; 
 // kMaxLaunchElems elements per launch.
 int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
                int wire_type, bool src_wire, hipStream_t stream) {
-    const mpp::Family family = plan.mode == AR_MODE_SINGLE_SHOT ? mpp::Family::SingleShot : stream_family(c->cfg);
+    const mpp::Family family = plan.mode == AR_MODE_SINGLE_SHOT ? mpp::Family::SingleShot : stream_family(plan);
     const size_t sb = static_cast<size_t>(plan.src_bytes);
 
     if (plan.mode == AR_MODE_RS_BCAST) {
@@ -404,7 +414,7 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
     if (hipEventRecord(c->ev_start, stream) != hipSuccess) return AR_ERR_RUNTIME;
     if (hipStreamWaitEvent(c->copy_stream, c->ev_start, 0) != hipSuccess) return AR_ERR_RUNTIME;
 
-    const mpp::Family family = stream_family(c->cfg);
+    const mpp::Family family = stream_family(plan);
     for (size_t ch = 0; ch < plan.n_chunks; ++ch) {
         const size_t e0 = ch * chunk;
         const size_t len = std::min(chunk, n - e0);

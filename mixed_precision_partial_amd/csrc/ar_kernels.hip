@@ -168,48 +168,47 @@ __device__ __forceinline__ void tile_store_as(float *dst, size_t t, int lane, co
 
 
 // Issue every load of a batch of U consecutive wave tiles starting at
-// element `t` (slice offset included) for the first R of RB sources.
+// element `t` (slice offset included) for the first R of RB sources, tile by
+// tile: the loads of tile 0 are the oldest in flight, so tile 0 can be folded
+// and stored while the later tiles' loads are still arriving.
 template <int W, bool SW, int RB, int U, bool NT>
 __device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int lane,
                                            u32x4 (&raw)[RB][U][Tile<SW>::kRaw]) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        if (r < 2 || r < a.R) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) tile_load<W, SW, NT>(a.src[r], t + u * kWaveTile, lane, raw[r][u]);
+        for (int r = 0; r < RB; ++r) {
+            if (r < 2 || r < a.R) tile_load<W, SW, NT>(a.src[r], t + u * kWaveTile, lane, raw[r][u]);
         }
     }
 }
 
-// Fold the batch in rank order and store it to every destination.  Loads
-// use NT; stores use ST (non-temporal for writes far larger than the caches,
-// ordinary write-back stores otherwise, so a prefill-sized result drains from
-// L2 / Infinity Cache while the next kernel is already reading).  The store
-// policy is a template parameter: two stores that differ only in their cache
-// hint would be merged into one by the compiler.
+// Fold each tile of the batch in rank order and store it to every
+// destination before the next tile is folded.  Loads use NT; stores use ST
+// (non-temporal for calls that write at least as much as they read,
+// ordinary write-back stores otherwise, which drain from L2 / Infinity Cache
+// while the next kernel reads).  The store policy is a template parameter:
+// two stores that differ only in their cache hint would be merged into one
+// by the compiler.
 template <int W, bool SW, int RB, int U, bool NT, bool ST = NT>
 __device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int lane,
                                            const u32x4 (&raw)[RB][U][Tile<SW>::kRaw]) {
-    float acc[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) tile_values<W, SW>(raw[0][u], acc[u]);
+    for (int u = 0; u < U; ++u) {
+        float acc[8];
+        tile_values<W, SW>(raw[0][u], acc);
 #pragma unroll
-    for (int r = 1; r < RB; ++r) {
-        if (r < 2 || r < a.R) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
+        for (int r = 1; r < RB; ++r) {
+            if (r < 2 || r < a.R) {
                 float w[8];
                 tile_values<W, SW>(raw[r][u], w);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[u][k] = acc[u][k] + w[k];
+                for (int k = 0; k < 8; ++k) acc[k] = acc[k] + w[k];
             }
         }
-    }
 #pragma unroll
-    for (int d = 0; d < RB; ++d) {
-        if (d < a.n_dst) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) tile_store_as<SW, ST>(a.dst[d], t + u * kWaveTile, lane, acc[u]);
+        for (int d = 0; d < RB; ++d) {
+            if (d < a.n_dst) tile_store_as<SW, ST>(a.dst[d], t + u * kWaveTile, lane, acc);
         }
     }
 }
@@ -358,7 +357,7 @@ MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
 #define MPP_LDS_U 1
 #endif
 #ifndef MPP_LDS_WG_PER_CU
-#define MPP_LDS_WG_PER_CU 16u
+#define MPP_LDS_WG_PER_CU 32u
 #endif
 
 // Tiles per stage: MPP_LDS_U, reduced so one stage is at most 32 loads per

@@ -45,7 +45,7 @@ def test_status_strings():
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 5 * 4 + 4   # padded to 8
-    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 2 * 4
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 3 * 4 + 4   # padded to 8
 
 
 def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
@@ -202,3 +202,13 @@ def test_store_policy_rule():
     assert q(n, mode=ar.AR_MODE_CHUNKED, config={"store_policy": 2})[1].store_nt == 1
     assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST, config={"store_policy": 1})[1].store_nt == 0
     assert q(64, config={"store_policy": 3})[0] == ar.AR_ERR_INVALID
+
+
+def test_stream_kernel_choice():
+    n = 2048 * 4096
+    assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    assert q(n, mode=ar.AR_MODE_CHUNKED)[1].stream_kernel == 1
+    assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 2
+    assert q(n, R=8, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 1
+    assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 1})[1].stream_kernel == 1
+    assert q(n, mode=ar.AR_MODE_CHUNKED, config={"stream_kernel": 2})[1].stream_kernel == 2

@@ -382,3 +382,37 @@ def test_error_paths(ctx):
     ar.ar_reduce(ctx, [out], dev, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED)
     torch.cuda.synchronize()
     assert np.all(out.cpu().numpy() == 2.0)
+
+
+def test_graph_capture_replays(ctx):
+    """Decode-sized calls captured into a HIP graph (torch.cuda.CUDAGraph) and replayed
+    several times, with eager work and synchronisation between replays; every replay is
+    checked against the oracle.  The device schedules enqueue kernels only (no memsets,
+    no host synchronisation), so they can be captured."""
+    w = wl.WORKLOADS["decode_bf16"]
+    calls, n, R = 16, w.n, w.R
+    host = np.stack([np.stack(wl.partials(w, c)) for c in range(calls)])   # (calls, R, n)
+    want = oracle.reduce([host[:, r, :].ravel() for r in range(R)], w.wire)[0].reshape(calls, n)
+    dev = torch.from_numpy(host).cuda()
+    out = torch.empty((calls, n), dtype=torch.float32, device="cuda")
+    big_n = 300_001
+    big_src = [to_device(s) for s in wl.random_partials(9100, 0, 3, big_n)]
+    big_want = oracle_result([s.cpu().numpy() for s in big_src], ar.AR_F16)
+    big_out = torch.empty(big_n, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log_case("graph capture: 16 single-shot calls + 1 chunked call")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        st = torch.cuda.current_stream()
+        for c in range(calls):
+            ar.ar_reduce(ctx, [out[c]], [dev[c, r] for r in range(R)], n, ar.AR_F32, w.wire,
+                         ar.AR_MODE_SINGLE_SHOT, stream=st)
+        ar.ar_reduce(ctx, [big_out], big_src, big_n, ar.AR_F32, ar.AR_F16, ar.AR_MODE_CHUNKED, stream=st)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        big_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(out.cpu().numpy(), want, f"graph replay {rep} decode")
+        assert_bits_equal(big_out.cpu().numpy(), big_want, f"graph replay {rep} chunked")
