@@ -416,3 +416,37 @@ def test_graph_capture_replays(ctx):
         torch.cuda.synchronize()
         assert_bits_equal(out.cpu().numpy(), want, f"graph replay {rep} decode")
         assert_bits_equal(big_out.cpu().numpy(), big_want, f"graph replay {rep} chunked")
+
+
+@pytest.mark.parametrize("wire_name", ["bf16", "f16"])
+def test_rounding_exhaustive_all_patterns(ctx, wire_name):
+    """Every one of the 2^32 binary32 patterns through the GPU cast: src0 = the pattern,
+    src1 = -0.0, so dst = widen(round_W(x)) exactly (x + (-0) == x for every x, NaN aside).
+    Expected values come from the oracle's conversion, computed in parallel on the host."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    wire = WIRES[wire_name]
+    orc = oracle.load()
+    chunk = 1 << 28
+    negz = torch.full((chunk,), -0.0, dtype=torch.float32, device="cuda")
+    out = torch.empty(chunk, dtype=torch.float32, device="cuda")
+    round_fn = oracle.round_bf16_bits if wire == ar.AR_BF16 else oracle.round_f16_bits
+    widen_fn = oracle.widen_bf16_bits if wire == ar.AR_BF16 else oracle.widen_f16_bits
+
+    def expected(start):
+        x = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        parts = np.array_split(x, 16)
+        with ThreadPoolExecutor(16) as pool:
+            res = list(pool.map(lambda p: widen_fn(round_fn(p, orc), orc), parts))
+        return np.concatenate(res).view(np.float32)
+
+    for k in range(1 << 32 >> 28):
+        start = k * chunk
+        log_case(f"exhaustive rounding {wire_name} chunk {k}")
+        x = torch.arange(start, start + chunk, dtype=torch.int64, device="cuda").to(torch.int32)
+        x = x.view(torch.float32)
+        ar.ar_reduce(ctx, [out], [x, negz], chunk, ar.AR_F32, wire, ar.AR_MODE_CHUNKED)
+        torch.cuda.synchronize()
+        del x
+        got = out.cpu().numpy()
+        assert_bits_equal(got, expected(start), f"exhaustive {wire_name} chunk {k}")
