@@ -84,6 +84,11 @@ enum {
 /* Flag: the sources already hold wire_type values (a peer narrowed them),
  * so round_W is the identity and each element is read at the wire width. */
 #define AR_SRC_WIRE 0x100u
+/* Flag: a NULL entry in srcs is an inactive rank (it skipped its compute);
+ * its partial is +0.0 everywhere and still takes part in the fold, as the
+ * CUDA allreduce.cu page does by zeroing such a shard before reducing.
+ * Without the flag a NULL source is AR_ERR_INVALID. */
+#define AR_SRC_INACTIVE_NULL 0x200u
 
 #define AR_MAX_RANKS 16
 
@@ -140,7 +145,7 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *   n         : elements per partial; 0 is a no-op returning AR_OK.
  *   dst_type  : AR_F32 (AR_F16 / AR_BF16 -> AR_ERR_UNSUPPORTED).
  *   wire_type : AR_F32, AR_F16 or AR_BF16; not wider than dst_type.
- *   mode      : AR_MODE_* | optional AR_SRC_WIRE.
+ *   mode      : AR_MODE_* | optional AR_SRC_WIRE | optional AR_SRC_INACTIVE_NULL.
  *   hip_stream: hipStream_t to enqueue on (NULL = null stream).
  * Errors (all detected on the host before anything is enqueued):
  *   AR_ERR_INVALID for a NULL ctx / array / entry, R outside 2..16, a
@@ -184,6 +189,7 @@ typedef struct {
     int    store_nt;      /* 1: streaming (non-temporal) destination stores */
     int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
     int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged   */
+    unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
 } ar_plan;
 
 /* Validate the arguments exactly as ar_reduce does, except the memory-kind

@@ -26,6 +26,7 @@ AR_F32, AR_F16, AR_BF16 = 0, 1, 2
 AR_MODE_AUTO, AR_MODE_SINGLE_SHOT, AR_MODE_CHUNKED, AR_MODE_RS_BCAST, AR_MODE_HOST_STAGED = 0, 1, 2, 3, 4
 AR_MODE_MASK = 0xFF
 AR_SRC_WIRE = 0x100
+AR_SRC_INACTIVE_NULL = 0x200
 AR_MAX_RANKS = 16
 
 AR_OK, AR_ERR_INVALID, AR_ERR_UNSUPPORTED, AR_ERR_NOMEM, AR_ERR_RUNTIME = 0, 1, 2, 3, 4
@@ -67,6 +68,7 @@ class ArPlan(ctypes.Structure):
         ("store_nt", ctypes.c_int),
         ("host_direct", ctypes.c_int),
         ("stream_kernel", ctypes.c_int),
+        ("active_mask", ctypes.c_uint),
     ]
 
 

@@ -115,7 +115,8 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                       int dst_type, int wire_type, unsigned mode, bool srcs_on_host, ar_plan *plan) {
     if (R < 2 || R > AR_MAX_RANKS) return AR_ERR_INVALID;
     if (!valid_type(dst_type) || !valid_type(wire_type)) return AR_ERR_INVALID;
-    if ((mode & ~(AR_MODE_MASK | AR_SRC_WIRE)) != 0) return AR_ERR_INVALID;
+    if ((mode & ~(AR_MODE_MASK | AR_SRC_WIRE | AR_SRC_INACTIVE_NULL)) != 0) return AR_ERR_INVALID;
+    const bool allow_inactive = (mode & AR_SRC_INACTIVE_NULL) != 0;
     const int base = static_cast<int>(mode & AR_MODE_MASK);
     if (base < AR_MODE_AUTO || base > AR_MODE_HOST_STAGED) return AR_ERR_INVALID;
     if (elem_bytes(wire_type) > elem_bytes(dst_type)) return AR_ERR_INVALID;
@@ -142,8 +143,13 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         if (dst[d] == nullptr) return AR_ERR_INVALID;
         if (reinterpret_cast<uintptr_t>(dst[d]) % 16 != 0) return AR_ERR_INVALID;
     }
+    unsigned active = 0;
     for (int r = 0; r < R; ++r) {
-        if (srcs[r] == nullptr) return AR_ERR_INVALID;
+        if (srcs[r] == nullptr) {
+            if (!allow_inactive) return AR_ERR_INVALID;
+            continue;
+        }
+        active |= 1u << r;
         if (reinterpret_cast<uintptr_t>(srcs[r]) % 16 != 0) return AR_ERR_INVALID;
     }
     if (n > (SIZE_MAX / 8) / AR_MAX_RANKS) return AR_ERR_INVALID;
@@ -159,6 +165,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 }
             }
             for (int r = 0; r < R; ++r) {
+                if (srcs[r] == nullptr) continue;
                 const uintptr_t ps = reinterpret_cast<uintptr_t>(srcs[r]);
                 if (!ranges_overlap(pd, dst_len, ps, src_len)) continue;
                 // exactly in place with equal element width is the one allowed overlap:
@@ -172,6 +179,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         std::memset(plan, 0, sizeof(*plan));
         plan->mode = resolved;
         plan->n_dst = n_dst;
+        plan->active_mask = active;
         plan->src_bytes = src_bytes;
         plan->wire_bytes = wire_bytes;
         size_t chunk;
@@ -332,6 +340,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             a.n_dst = R;
             a.chunk_elems = 0;
             a.store_nt = plan.store_nt;
+            a.active = plan.active_mask;
             unsigned max_len = 0;
             for (int r = 0; r < R; ++r) {
                 const size_t len = plan.slice_len[r] > p0 ? std::min(mpp::kMaxLaunchElems, plan.slice_len[r] - p0) : 0;
@@ -355,7 +364,10 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         a.n_dst = 1;
         a.n = static_cast<unsigned>(len);
         a.store_nt = plan.mode == AR_MODE_SINGLE_SHOT ? 0 : plan.store_nt;
-        for (int r = 0; r < R; ++r) a.src[r] = static_cast<const char *>(srcs[r]) + p0 * sb;
+        a.active = plan.active_mask;
+        for (int r = 0; r < R; ++r) {
+            a.src[r] = srcs[r] == nullptr ? nullptr : static_cast<const char *>(srcs[r]) + p0 * sb;
+        }
         a.dst[0] = static_cast<float *>(dst[0]) + p0;
         // CHUNKED: gridDim.y walks the plan's chunks; SINGLE_SHOT: one range
         a.chunk_elems = static_cast<unsigned>(len);
@@ -426,6 +438,7 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
             return AR_ERR_RUNTIME;
         }
         for (int r = 0; r < R; ++r) {
+            if (srcs[r] == nullptr) continue;   // inactive rank: nothing crosses PCIe
             if (hipMemcpyAsync(slot_base + r * rank_stride, static_cast<const char *>(srcs[r]) + e0 * sb, len * sb,
                                hipMemcpyHostToDevice, c->copy_stream) != hipSuccess) {
                 return AR_ERR_RUNTIME;
@@ -439,8 +452,9 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         a.n_dst = 1;
         a.n = static_cast<unsigned>(len);
         a.store_nt = plan.store_nt;
+        a.active = plan.active_mask;
         a.chunk_elems = static_cast<unsigned>(len);
-        for (int r = 0; r < R; ++r) a.src[r] = slot_base + r * rank_stride;
+        for (int r = 0; r < R; ++r) a.src[r] = srcs[r] == nullptr ? nullptr : slot_base + r * rank_stride;
         a.dst[0] = static_cast<float *>(dst[0]) + e0;
         const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, static_cast<unsigned>(len), 1,
                                                        c->cu_count, c->cfg.grid_wgs);
@@ -543,9 +557,13 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return AR_ERR_RUNTIME;
 
-    if (n > 0 && (auto_mode || plan.mode == AR_MODE_HOST_STAGED)) {
+    int first_active = -1;
+    for (int r = 0; r < R && first_active < 0; ++r) {
+        if (srcs[r] != nullptr) first_active = r;
+    }
+    if (n > 0 && first_active >= 0 && (auto_mode || plan.mode == AR_MODE_HOST_STAGED)) {
         // memory kinds decide AUTO between host-staged and device modes
-        const Kind k0 = memory_kind(srcs[0], src_len, ctx->device);
+        const Kind k0 = memory_kind(srcs[first_active], src_len, ctx->device);
         if (k0 == Kind::Other) return AR_ERR_INVALID;
         if (auto_mode && k0 == Kind::PinnedHost) {
             rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, true, &plan);
@@ -557,6 +575,8 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
     const Kind want_src = plan.mode == AR_MODE_HOST_STAGED ? Kind::PinnedHost : Kind::Device;
     const void *src_view[AR_MAX_RANKS];
     for (int r = 0; r < R; ++r) {
+        src_view[r] = nullptr;
+        if (srcs[r] == nullptr) continue;   // inactive rank (validated above)
         if (memory_kind(srcs[r], src_len, ctx->device, &src_view[r]) != want_src) return AR_ERR_INVALID;
     }
     for (int d = 0; d < plan.n_dst; ++d) {

@@ -32,6 +32,7 @@ struct KernelArgs {
     int         n_dst;
     int         store_nt;   // 1: non-temporal stores, 0: ordinary (cached) stores;
                             // selects the kernel instance, not read on the GPU
+    unsigned    active;     // bit r: rank r has a partial; an inactive rank is +0.0
     const void *src[AR_MAX_RANKS];
     float      *dst[AR_MAX_RANKS];
     uint64_t    slice_start[AR_MAX_RANKS];

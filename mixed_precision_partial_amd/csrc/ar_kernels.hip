@@ -167,6 +167,11 @@ __device__ __forceinline__ void tile_store_as(float *dst, size_t t, int lane, co
 
 
 
+// Rank r takes part with a partial (bit r of the launch's mask); an inactive
+// rank's partial is +0.0 everywhere: nothing is loaded and +0.0 is added in
+// its place, which keeps -0 + inactive == +0 like a zeroed shard.
+__device__ __forceinline__ bool rank_active(const KernelArgs &a, int r) { return (a.active >> r) & 1u; }
+
 // Issue every load of a batch of U consecutive wave tiles starting at
 // element `t` (slice offset included) for the first R of RB sources, tile by
 // tile: the loads of tile 0 are the oldest in flight, so tile 0 can be folded
@@ -178,7 +183,9 @@ __device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int la
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            if (r < 2 || r < a.R) tile_load<W, SW, NT>(a.src[r], t + u * kWaveTile, lane, raw[r][u]);
+            if ((r < 2 || r < a.R) && rank_active(a, r)) {
+                tile_load<W, SW, NT>(a.src[r], t + u * kWaveTile, lane, raw[r][u]);
+            }
         }
     }
 }
@@ -196,12 +203,22 @@ __device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int la
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float acc[8];
-        tile_values<W, SW>(raw[0][u], acc);
+        if (rank_active(a, 0)) {
+            tile_values<W, SW>(raw[0][u], acc);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+        }
 #pragma unroll
         for (int r = 1; r < RB; ++r) {
             if (r < 2 || r < a.R) {
                 float w[8];
-                tile_values<W, SW>(raw[r][u], w);
+                if (rank_active(a, r)) {
+                    tile_values<W, SW>(raw[r][u], w);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) w[k] = 0.0f;
+                }
 #pragma unroll
                 for (int k = 0; k < 8; ++k) acc[k] = acc[k] + w[k];
             }
@@ -225,10 +242,10 @@ __device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int 
 template <int W, bool SW, int RB>
 __device__ __forceinline__ void reduce_scalar(const KernelArgs &a, size_t begin, size_t end, int lane) {
     for (size_t e = begin + lane; e < end; e += kWave) {
-        float acc = wire_one<W, SW>(a.src[0], e);
+        float acc = rank_active(a, 0) ? wire_one<W, SW>(a.src[0], e) : 0.0f;
 #pragma unroll
         for (int r = 1; r < RB; ++r) {
-            if (r < 2 || r < a.R) acc = acc + wire_one<W, SW>(a.src[r], e);
+            if (r < 2 || r < a.R) acc = acc + (rank_active(a, r) ? wire_one<W, SW>(a.src[r], e) : 0.0f);
         }
 #pragma unroll
         for (int d = 0; d < RB; ++d) {
@@ -381,7 +398,7 @@ __device__ __forceinline__ void lds_issue(const KernelArgs &a, size_t t, int lan
     constexpr int K = Tile<SW>::kRaw;
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        if (r < 2 || r < a.R) {
+        if ((r < 2 || r < a.R) && rank_active(a, r)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -436,7 +453,7 @@ __device__ __forceinline__ void lds_consume(const KernelArgs &a, size_t t, int l
     u32x4 raw[RB][U][K];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        if (r < 2 || r < a.R) {
+        if ((r < 2 || r < a.R) && rank_active(a, r)) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -461,8 +478,9 @@ __device__ __forceinline__ void stream_lds(const KernelArgs &a) {
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
 
-    // loads per stage (vector-memory instructions): R x U x K
-    const int L = (a.R < RB ? a.R : RB) * U * Tile<SW>::kRaw;
+    // loads per stage (vector-memory instructions): active ranks x U x K
+    const unsigned ranks_mask = (a.R < RB ? a.R : RB) >= 32 ? ~0u : ((1u << (a.R < RB ? a.R : RB)) - 1u);
+    const int L = __builtin_popcount(a.active & ranks_mask) * U * Tile<SW>::kRaw;
     constexpr int kMaxL = RB * U * Tile<SW>::kRaw;
 
     unsigned t = gw;

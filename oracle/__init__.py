@@ -145,24 +145,28 @@ def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
 
     ``srcs``: sequence of R equally sized 1-D arrays.  float32 arrays are the
     caller-typed partials; uint16 arrays hold wire-typed bit patterns (then
-    ``src_type`` must equal ``wire_type``).
+    ``src_type`` must equal ``wire_type``).  A ``None`` entry is an inactive
+    rank (its partial is all +0.0).
     Returns an ``(n_dst, n)`` float32 array (every row holds the same bits).
     """
     lib = lib or load()
-    srcs = [np.ascontiguousarray(s) for s in srcs]
+    srcs = [None if s is None else np.ascontiguousarray(s) for s in srcs]
     R = len(srcs)
-    n = srcs[0].size
+    live = [s for s in srcs if s is not None]
+    if not live:
+        raise ValueError("at least one active source is needed to know n")
+    n = live[0].size
     if src_type is None:
-        src_type = F32 if srcs[0].dtype == np.float32 else wire_type
+        src_type = F32 if live[0].dtype == np.float32 else wire_type
     want = np.float32 if src_type == F32 else np.uint16
-    for s in srcs:
+    for s in live:
         if s.size != n:
             raise ValueError("sources differ in length")
         if s.dtype != want:
             raise TypeError(f"source dtype {s.dtype} does not match src_type {src_type}")
     out = np.empty((n_dst, n), dtype=np.float32)
     dst_ptrs = (ctypes.c_void_p * n_dst)(*[out[d].ctypes.data for d in range(n_dst)])
-    src_ptrs = (ctypes.c_void_p * R)(*[s.ctypes.data for s in srcs])
+    src_ptrs = (ctypes.c_void_p * R)(*[None if s is None else s.ctypes.data for s in srcs])
     rc = lib.orc_reduce(dst_ptrs, n_dst, src_ptrs, R, n, src_type, wire_type)
     if rc != 0:
         raise ValueError(f"oracle rejected arguments (rc={rc})")

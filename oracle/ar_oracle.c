@@ -25,6 +25,12 @@
  *     s0 + s1, then + s2, ... and the block is written to every destination
  *     (n_dsts defaults to n_ranks in op_allreduce).
  *
+ * Inactive ranks: a NULL source is a rank that skipped its compute; its
+ * partial is all +0.0, which the CUDA page obtains by zeroing such a shard
+ * before the same reduce runs (comments on inactive shards and NCCL /
+ * meta-backend semantics in ggml_cuda_ar_allreduce).  Its wire value is
+ * therefore +0.0 and it still takes part in the fold (so -0 + inactive = +0).
+ *
  * Readings where the pages leave a step open (all pinned by the tests):
  *   - round_W is IEEE round-to-nearest-ties-to-even for both bf16 and fp16
  *     (the conversion routine itself is not printed on the pages).  NaN maps
@@ -179,6 +185,9 @@ uint32_t orc_widen_f16(uint16_t h) {
  * rounding is the identity and only the widening remains.
  * ------------------------------------------------------------------------- */
 static float orc_wire_value(const void *src, size_t i, int src_type, int wire_type) {
+    if (src == NULL) {
+        return 0.0f;                                      /* inactive rank */
+    }
     if (src_type == ORC_F32) {
         const uint32_t bits = ((const uint32_t *)src)[i];
         switch (wire_type) {
@@ -204,7 +213,8 @@ static void orc_leave_ieee(unsigned saved) {
 }
 
 /* ---------------------------------------------------------------------------
- * The reduce.  dst: n_dst binary32 arrays; srcs: R arrays of src_type.
+ * The reduce.  dst: n_dst binary32 arrays; srcs: R arrays of src_type (a NULL
+ * entry is an inactive rank contributing +0.0).
  * Returns 0 on success, -1 on an argument the oracle does not define.
  * ------------------------------------------------------------------------- */
 int orc_reduce(float *const *dst, int n_dst, const void *const *srcs, int R,

@@ -106,7 +106,7 @@ def load_golden() -> list[dict]:
             rid, op, wire, inputs, expected = parts[0], parts[1], parts[2], parts[3], parts[4]
             rows.append({
                 "id": rid, "op": op, "wire": WIRE_BY_NAME[wire],
-                "inputs": [int(h, 16) for h in inputs.split(",")],
+                "inputs": [None if h == "-" else int(h, 16) for h in inputs.split(",")],
                 "expected": None if expected == "NAN" else int(expected, 16),
             })
     return rows
@@ -114,8 +114,21 @@ def load_golden() -> list[dict]:
 
 def check_golden(lib) -> None:
     rows = load_golden()
-    assert len(rows) >= 25
+    assert len(rows) >= 35
     for row in rows:
+        if row["op"] == "reduce":
+            srcs = [None if v is None else np.array([v], dtype=np.uint32).view(np.float32)
+                    for v in row["inputs"]]
+            if all(s is None for s in srcs):
+                got = _reduce_all_inactive(lib, len(row["inputs"]), row["wire"])
+            else:
+                got = oracle.reduce(srcs, row["wire"], lib=lib)[0, 0]
+            if row["expected"] is None:
+                assert np.isnan(got), row["id"]
+            else:
+                gb = int(np.array([got], dtype=np.float32).view(np.uint32)[0])
+                assert gb == row["expected"], f"{row['id']}: {gb:#010x} != {row['expected']:#010x}"
+            continue
         x = np.array(row["inputs"], dtype=np.uint32)
         if row["op"] == "round":
             fn = oracle.round_bf16_bits if row["wire"] == BF16 else oracle.round_f16_bits
@@ -132,6 +145,43 @@ def check_golden(lib) -> None:
             else:
                 gb = int(np.array([got], dtype=np.float32).view(np.uint32)[0])
                 assert gb == row["expected"], f"{row['id']}: {gb:#010x} != {row['expected']:#010x}"
+
+
+def _reduce_all_inactive(lib, R: int, wire: int) -> float:
+    """The oracle with every rank inactive (n = 1), through the raw C entry point."""
+    import ctypes
+
+    out = np.empty(1, dtype=np.float32)
+    dst = (ctypes.c_void_p * 1)(out.ctypes.data)
+    srcs = (ctypes.c_void_p * R)(*([None] * R))
+    rc = lib.orc_reduce(dst, 1, srcs, R, 1, F32, wire)
+    assert rc == 0
+    return out[0]
+
+
+def check_inactive_ranks(lib, seed: int = 31) -> None:
+    """An inactive (NULL) rank equals an all-(+0.0) partial: compared with the fp64
+    route over library-rounded partials where inactive ranks are zero arrays."""
+    rng = np.random.default_rng(seed)
+    g = _edge_grid()
+    for R in (2, 3, 5, 8, 16):
+        n = 2000
+        srcs = workloads.random_partials(960, R, R, n, dist="wide")
+        srcs[0][:g.size] = g                      # edge values incl. -0 and NaN
+        for trial in range(3):
+            active = rng.random(R) < 0.6
+            if trial == 0:
+                active[0] = False                 # rank 0 inactive: the fold starts at +0
+            mixed = [s if a else None for s, a in zip(srcs, active)]
+            if not any(active):
+                continue
+            for wire in (F32, BF16, F16):
+                got = oracle.reduce(mixed, wire, n_dst=2, lib=lib)
+                zeros = [s if a else np.zeros(n, dtype=np.float32) for s, a in zip(srcs, active)]
+                with np.errstate(all="ignore"):
+                    want = fp64_route_fold([lib_wire_value(z, wire) for z in zeros])
+                assert_same_f32(got[0], want, f"inactive R={R} wire={wire} active={active.tolist()}")
+                assert np.array_equal(got[0].view(np.uint32), got[1].view(np.uint32))
 
 
 # --- conversions -------------------------------------------------------------
@@ -313,4 +363,5 @@ def cheap_checks():
         ("closed_form", check_closed_form),
         ("order", check_order_sensitivity),
         ("broadcast", check_broadcast_and_wire_srcs),
+        ("inactive", check_inactive_ranks),
     ]

@@ -45,7 +45,7 @@ def test_status_strings():
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 5 * 4 + 4   # padded to 8
-    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 3 * 4 + 4   # padded to 8
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 4 * 4
 
 
 def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
@@ -73,7 +73,8 @@ def test_type_checks():
 
 def test_mode_and_flag_checks():
     assert q(64, mode=5)[0] == ar.AR_ERR_INVALID
-    assert q(64, mode=ar.AR_MODE_CHUNKED | 0x200)[0] == ar.AR_ERR_INVALID
+    assert q(64, mode=ar.AR_MODE_CHUNKED | 0x400)[0] == ar.AR_ERR_INVALID
+    assert q(64, mode=ar.AR_MODE_CHUNKED | 0x10000)[0] == ar.AR_ERR_INVALID
     assert q(64, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[0] == ar.AR_OK
 
 
@@ -212,3 +213,18 @@ def test_stream_kernel_choice():
     assert q(n, R=8, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 1})[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED, config={"stream_kernel": 2})[1].stream_kernel == 2
+
+
+def test_inactive_ranks_flag():
+    n = 1 << 20
+    srcs = [A[1], 0, A[3]]
+    # NULL is invalid without the flag
+    assert q(n, srcs=srcs, mode=ar.AR_MODE_CHUNKED)[0] == ar.AR_ERR_INVALID
+    rc, p = q(n, srcs=srcs, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL)
+    assert rc == ar.AR_OK and p.active_mask == 0b101
+    rc, p = q(n, srcs=[0, 0], mode=ar.AR_MODE_RS_BCAST | ar.AR_SRC_INACTIVE_NULL)
+    assert rc == ar.AR_OK and p.active_mask == 0 and p.n_dst == 2
+    rc, p = q(n, mode=ar.AR_MODE_CHUNKED)
+    assert p.active_mask == 0b11
+    # a NULL destination stays invalid
+    assert q(n, dsts=[0], srcs=srcs, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL)[0] == ar.AR_ERR_INVALID

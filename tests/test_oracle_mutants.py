@@ -3,9 +3,13 @@
 Each case copies ``oracle/ar_oracle.c`` with one plausible mistake written in
 (a dropped rank, a reversed order, a wrong tie rule, an off-by-one shift, a lost
 sign, ...), builds it into a temporary directory and runs the cheap pins
-against it.  The real oracle is never modified.
+against it in a child process (a planted mistake may also crash, e.g. by
+reading an inactive rank's NULL pointer; a crash counts as caught).  The real
+oracle is never modified.
 """
 import os
+import subprocess
+import sys
 
 import pytest
 
@@ -48,6 +52,11 @@ MUTANTS = [
     ("widen_f16_bias", [("((uint32_t)(e + 112) << 23)", "((uint32_t)(e + 111) << 23)")]),
     ("widen_f16_subnormal_as_zero", [("if (m == 0) {\n            return sign;", "if (1) {\n            return sign;")]),
     ("broadcast_only_first", [("for (int d = 0; d < n_dst; ++d)", "for (int d = 0; d < 1; ++d)")]),
+    ("inactive_rank_skipped", [
+        ("const float w = orc_wire_value(srcs[r], i, src_type, wire_type);\n            acc = acc + w;",
+         "if (srcs[r] == NULL) continue;\n            const float w = orc_wire_value(srcs[r], i, src_type, wire_type);\n            acc = acc + w;")]),
+    ("inactive_rank_as_minus_zero", [("        return 0.0f;                                      /* inactive rank */",
+                                      "        return -0.0f;")]),
     ("add_keeps_ftz", [("_mm_setcsr(saved & ~((1u << 15) | (1u << 6)));",
                         "_mm_setcsr(saved | (1u << 15) | (1u << 6));")]),
 ]
@@ -63,14 +72,26 @@ def test_planted_mistake_is_caught(tmp_path, name, edits):
     src.write_text(text)
     so = tmp_path / f"libmutant_{name}.so"
     oracle.build(str(src), str(so))
-    lib = oracle.load(str(so))
-    caught = []
-    for check_name, check in oc.cheap_checks():
-        try:
-            check(lib)
-        except AssertionError:
-            caught.append(check_name)
-    assert caught, f"no pin caught the planted mistake {name!r}"
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = (
+        "import sys\n"
+        f"sys.path[:0] = [{here!r}, {os.path.dirname(here)!r}]\n"
+        "import oracle, oracle_checks as oc\n"
+        f"lib = oracle.load({str(so)!r})\n"
+        "caught = []\n"
+        "for name, check in oc.cheap_checks():\n"
+        "    try:\n"
+        "        check(lib)\n"
+        "    except AssertionError:\n"
+        "        caught.append(name)\n"
+        "print('caught:', caught)\n"
+        "sys.exit(3 if caught else 0)\n"
+    )
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    # 3: a pin's assertion failed; < 0: the planted mistake crashed the process.
+    # Anything else (0, or a Python error outside the pins) is not a catch.
+    assert res.returncode == 3 or res.returncode < 0, \
+        f"planted mistake {name!r} not caught (rc={res.returncode}): {res.stdout}{res.stderr[-2000:]}"
 
 
 def test_real_oracle_passes_cheap_checks(orc):

@@ -54,6 +54,10 @@ def test_broadcast_and_wire_typed_sources(orc):
     oc.check_broadcast_and_wire_srcs(orc)
 
 
+def test_inactive_ranks(orc):
+    oc.check_inactive_ranks(orc)
+
+
 def test_empty_and_single_element(orc):
     z = np.zeros(0, dtype=np.float32)
     assert oracle.reduce([z, z], oracle.BF16, lib=orc).shape == (1, 0)

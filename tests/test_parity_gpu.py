@@ -450,3 +450,47 @@ def test_rounding_exhaustive_all_patterns(ctx, wire_name):
         del x
         got = out.cpu().numpy()
         assert_bits_equal(got, expected(start), f"exhaustive {wire_name} chunk {k}")
+
+
+@pytest.mark.parametrize("kname", ["reg_cached", "reg_streaming", "lds_cached", "lds_streaming", "host_direct"])
+@pytest.mark.parametrize("mode_name", ["single_shot", "chunked", "rs_bcast", "host_staged"])
+def test_inactive_ranks(kctx, kname, mode_name):
+    """NULL sources with AR_SRC_INACTIVE_NULL: inactive ranks contribute +0.0 (rank 0
+    inactive, middle ranks inactive, all inactive), edge values included."""
+    mode = MODES[mode_name] | ar.AR_SRC_INACTIVE_NULL
+    g = np.concatenate([wl.special_values(), wl.nan_values()])
+    rng = np.random.default_rng(77)
+    for i, (R, n) in enumerate([(2, 4097), (3, 70_001), (5, 2_048), (8, 65_536 + 9), (16, 9_001)]):
+        srcs = wl.random_partials(9500 + i, 0, R, n, dist="wide")
+        srcs[-1][:g.size] = g
+        for trial in range(3):
+            active = rng.random(R) < 0.5
+            if trial == 0:
+                active[0] = False
+            if trial == 2:
+                active[:] = False
+            for wire_name, wire in WIRES.items():
+                for src_wire in ([False, True] if wire != ar.AR_F32 else [False]):
+                    what = (f"inactive {kname} {mode_name} R={R} n={n} wire={wire_name} "
+                            f"src_wire={src_wire} active={active.astype(int).tolist()}")
+                    log_case(what)
+                    used = [wl.as_wire_typed(s, wire) if src_wire else s for s in srcs]
+                    c = kctx[kname]
+                    base = mode & ar.AR_MODE_MASK
+                    n_dst = R if base == ar.AR_MODE_RS_BCAST else 1
+                    if base == ar.AR_MODE_HOST_STAGED:
+                        ts = [to_pinned(s) if a else None for s, a in zip(used, active)]
+                    else:
+                        ts = [to_device(s) if a else None for s, a in zip(used, active)]
+                    dsts = [GuardedDst(n) for _ in range(n_dst)]
+                    flags = ar.AR_SRC_WIRE if src_wire else 0
+                    ar.ar_reduce(c, [d.ptr() for d in dsts], [0 if t is None else t for t in ts], n,
+                                 ar.AR_F32, wire, mode | flags)
+                    torch.cuda.synchronize()
+                    if active.any():
+                        want = oracle.reduce([s if a else None for s, a in zip(used, active)], wire,
+                                             src_type=wire if src_wire else None)[0]
+                    else:
+                        want = np.zeros(n, dtype=np.float32)   # +0.0 everywhere
+                    for d in dsts:
+                        assert_bits_equal(d.result(), want, what)
