@@ -170,23 +170,39 @@ __device__ __forceinline__ void tile_store_as(float *dst, size_t t, int lane, co
 // Rank r takes part with a partial (bit r of the launch's mask); an inactive
 // rank's partial is +0.0 everywhere: nothing is loaded and +0.0 is added in
 // its place, which keeps -0 + inactive == +0 like a zeroed shard.
-__device__ __forceinline__ bool rank_active(const KernelArgs &a, int r) { return (a.active >> r) & 1u; }
+// MASKED = false is the common case (every rank active): the test folds away
+// and the loads of a batch stay one straight-line sequence.  The host picks
+// the masked kernel instance only when some rank is inactive: per-rank
+// branches around loads make the compiler drain each rank's loads before
+// issuing the next, so the common case must not carry them.
+template <bool MASKED>
+__device__ __forceinline__ bool rank_active(const KernelArgs &a, int r) {
+    if constexpr (MASKED) {
+        return (a.active >> r) & 1u;
+    } else {
+        return true;
+    }
+}
+
 
 // Issue every load of a batch of U consecutive wave tiles starting at
 // element `t` (slice offset included) for the first R of RB sources, tile by
 // tile: the loads of tile 0 are the oldest in flight, so tile 0 can be folded
 // and stored while the later tiles' loads are still arriving.
-template <int W, bool SW, int RB, int U, bool NT>
+template <int W, bool SW, int RB, int U, bool NT, bool MASKED>
 __device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int lane,
                                            u32x4 (&raw)[RB][U][Tile<SW>::kRaw]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            if ((r < 2 || r < a.R) && rank_active(a, r)) {
+            if ((r < 2 || r < a.R) && rank_active<MASKED>(a, r)) {
                 tile_load<W, SW, NT>(a.src[r], t + u * kWaveTile, lane, raw[r][u]);
             }
         }
+        // keep tile order: the scheduler must not hoist a later tile's loads
+        // above this one's
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -197,13 +213,13 @@ __device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int la
 // while the next kernel reads).  The store policy is a template parameter:
 // two stores that differ only in their cache hint would be merged into one
 // by the compiler.
-template <int W, bool SW, int RB, int U, bool NT, bool ST = NT>
+template <int W, bool SW, int RB, int U, bool NT, bool ST, bool MASKED>
 __device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int lane,
                                            const u32x4 (&raw)[RB][U][Tile<SW>::kRaw]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float acc[8];
-        if (rank_active(a, 0)) {
+        if (rank_active<MASKED>(a, 0)) {
             tile_values<W, SW>(raw[0][u], acc);
         } else {
 #pragma unroll
@@ -213,7 +229,7 @@ __device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int la
         for (int r = 1; r < RB; ++r) {
             if (r < 2 || r < a.R) {
                 float w[8];
-                if (rank_active(a, r)) {
+                if (rank_active<MASKED>(a, r)) {
                     tile_values<W, SW>(raw[r][u], w);
                 } else {
 #pragma unroll
@@ -230,11 +246,11 @@ __device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int la
     }
 }
 
-template <int W, bool SW, int RB, int U, bool NT, bool ST = NT>
+template <int W, bool SW, int RB, int U, bool NT, bool ST, bool MASKED>
 __device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int lane) {
     u32x4 raw[RB][U][Tile<SW>::kRaw];
-    load_batch<W, SW, RB, U, NT>(a, t, lane, raw);
-    fold_store<W, SW, RB, U, NT, ST>(a, t, lane, raw);
+    load_batch<W, SW, RB, U, NT, MASKED>(a, t, lane, raw);
+    fold_store<W, SW, RB, U, NT, ST, MASKED>(a, t, lane, raw);
 }
 
 // Elements [begin, end) of the launch, one per lane per step (end - begin is
@@ -242,10 +258,10 @@ __device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int 
 template <int W, bool SW, int RB>
 __device__ __forceinline__ void reduce_scalar(const KernelArgs &a, size_t begin, size_t end, int lane) {
     for (size_t e = begin + lane; e < end; e += kWave) {
-        float acc = rank_active(a, 0) ? wire_one<W, SW>(a.src[0], e) : 0.0f;
+        float acc = rank_active<true>(a, 0) ? wire_one<W, SW>(a.src[0], e) : 0.0f;
 #pragma unroll
         for (int r = 1; r < RB; ++r) {
-            if (r < 2 || r < a.R) acc = acc + (rank_active(a, r) ? wire_one<W, SW>(a.src[r], e) : 0.0f);
+            if (r < 2 || r < a.R) acc = acc + (rank_active<true>(a, r) ? wire_one<W, SW>(a.src[r], e) : 0.0f);
         }
 #pragma unroll
         for (int d = 0; d < RB; ++d) {
@@ -274,13 +290,13 @@ __device__ __forceinline__ void range_of(const KernelArgs &a, size_t &off, unsig
 
 // Whole wave tiles after the batched part, then the element remainder on
 // wave 0 of workgroup 0 of the range.
-template <int W, bool SW, int RB, int U, bool NT, bool ST>
+template <int W, bool SW, int RB, int U, bool NT, bool ST, bool MASKED>
 __device__ __forceinline__ void reduce_rest(const KernelArgs &a, size_t off, unsigned len, unsigned done,
                                             unsigned gw, unsigned nw, int lane) {
     if constexpr (U > 1) {
         const unsigned n_one = (len - done) / kWaveTile;
         for (unsigned t = gw; t < n_one; t += nw) {
-            reduce_tiles<W, SW, RB, 1, NT, ST>(a, off + done + (size_t)t * kWaveTile, lane);
+            reduce_tiles<W, SW, RB, 1, NT, ST, MASKED>(a, off + done + (size_t)t * kWaveTile, lane);
         }
     }
     const unsigned vec_end = (len / kWaveTile) * kWaveTile;
@@ -292,7 +308,7 @@ __device__ __forceinline__ void reduce_rest(const KernelArgs &a, size_t off, uns
 // Walk the wave tiles of this workgroup's range: batches of U tiles strided
 // over the `a.waves` waves of the range, then the remainder.  BLOCK is the
 // workgroup size the kernel is always launched with (no read of blockDim).
-template <int W, bool SW, int RB, int U, bool NT, bool ST, int BLOCK, bool SLICED>
+template <int W, bool SW, int RB, int U, bool NT, bool ST, int BLOCK, bool SLICED, bool MASKED>
 __device__ __forceinline__ void reduce_range(const KernelArgs &a) {
     constexpr unsigned wpb = BLOCK / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -305,10 +321,12 @@ __device__ __forceinline__ void reduce_range(const KernelArgs &a) {
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
     for (unsigned t = gw; t < n_big; t += nw) {
-        reduce_tiles<W, SW, RB, U, NT, ST>(a, off + (size_t)t * big, lane);
+        reduce_tiles<W, SW, RB, U, NT, ST, MASKED>(a, off + (size_t)t * big, lane);
     }
-    reduce_rest<W, SW, RB, U, NT, ST>(a, off, len, n_big * big, gw, nw, lane);
+    reduce_rest<W, SW, RB, U, NT, ST, MASKED>(a, off, len, n_big * big, gw, nw, lane);
 }
+
+
 
 constexpr int kSingleShotBlock = 64;
 constexpr int kStreamBlock = 256;
@@ -316,7 +334,12 @@ constexpr int kLdsBlock = 64;
 
 template <int W, bool SW, int RB>
 __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(KernelArgs a) {
-    reduce_range<W, SW, RB, 1, false, false, kSingleShotBlock, false>(a);
+    reduce_range<W, SW, RB, 1, false, false, kSingleShotBlock, false, false>(a);
+}
+
+template <int W, bool SW, int RB>
+__global__ __launch_bounds__(kSingleShotBlock) void k_single_shot_m(KernelArgs a) {
+    reduce_range<W, SW, RB, 1, false, false, kSingleShotBlock, false, true>(a);
 }
 
 // Streaming-kernel tuning (compile-time; measured on MI355X):
@@ -349,16 +372,20 @@ constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
 }
 
 // Register-staged streaming kernel: ST = non-temporal stores, SLICED = the
-// per-rank slice ranges of the broadcast schedule.
-#define MPP_STREAM_REG(NAME, ST, SLICED)                                                           \
-    template <int W, bool SW, int RB>                                                            \
-    __global__ __launch_bounds__(kStreamBlock) void NAME(KernelArgs a) {                         \
-        reduce_range<W, SW, RB, stream_batch(SW, RB), MPP_STREAM_NT != 0, ST, kStreamBlock, SLICED>(a); \
+// per-rank slice ranges of the broadcast schedule, M = some rank inactive.
+#define MPP_STREAM_REG(NAME, ST, SLICED, M)                                                         \
+    template <int W, bool SW, int RB>                                                             \
+    __global__ __launch_bounds__(kStreamBlock) void NAME(KernelArgs a) {                          \
+        reduce_range<W, SW, RB, stream_batch(SW, RB), MPP_STREAM_NT != 0, ST, kStreamBlock, SLICED, M>(a); \
     }
-MPP_STREAM_REG(k_stream_reg, false, false)
-MPP_STREAM_REG(k_stream_reg_nts, true, false)
-MPP_STREAM_REG(k_stream_reg_sl, false, true)
-MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
+MPP_STREAM_REG(k_stream_reg, false, false, false)
+MPP_STREAM_REG(k_stream_reg_nts, true, false, false)
+MPP_STREAM_REG(k_stream_reg_sl, false, true, false)
+MPP_STREAM_REG(k_stream_reg_nts_sl, true, true, false)
+MPP_STREAM_REG(k_stream_reg_m, false, false, true)
+MPP_STREAM_REG(k_stream_reg_nts_m, true, false, true)
+MPP_STREAM_REG(k_stream_reg_sl_m, false, true, true)
+MPP_STREAM_REG(k_stream_reg_nts_sl_m, true, true, true)
 #undef MPP_STREAM_REG
 
 // ---------------------------------------------------------------------------
@@ -393,12 +420,12 @@ struct LdsStage {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int W, bool SW, int RB, int U>
+template <int W, bool SW, int RB, int U, bool MASKED>
 __device__ __forceinline__ void lds_issue(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
     constexpr int K = Tile<SW>::kRaw;
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        if ((r < 2 || r < a.R) && rank_active(a, r)) {
+        if ((r < 2 || r < a.R) && rank_active<MASKED>(a, r)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -446,29 +473,26 @@ __device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
     return v;
 }
 
-template <int W, bool SW, int RB, int U, bool ST>
+template <int W, bool SW, int RB, int U, bool ST, bool MASKED>
 __device__ __forceinline__ void lds_consume(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
     constexpr int K = Tile<SW>::kRaw;
     const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void *)(&stage[0][lane])));
     u32x4 raw[RB][U][K];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        if ((r < 2 || r < a.R) && rank_active(a, r)) {
+        if ((r < 2 || r < a.R) && rank_active<MASKED>(a, r)) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int j = 0; j < K; ++j) raw[r][u][j] = lds_read16(base + ((r * U + u) * K + j) * kWave * 16);
         }
     }
-    fold_store<W, SW, RB, U, true, ST>(a, t, lane, raw);
+    fold_store<W, SW, RB, U, true, ST, MASKED>(a, t, lane, raw);
 }
 
-template <int W, bool SW, int RB, bool ST, bool SLICED>
-__device__ __forceinline__ void stream_lds(const KernelArgs &a) {
+template <int W, bool SW, int RB, bool ST, bool SLICED, bool MASKED>
+__device__ __forceinline__ void stream_lds_as(const KernelArgs &a, u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
     constexpr int U = lds_batch(SW, RB);
-    constexpr int NB = LdsStage<W, SW, RB, U>::kBlocks;
-    __shared__ u32x4 stage0[NB][kWave];
-    __shared__ u32x4 stage1[NB][kWave];
     const int lane = threadIdx.x;
     const unsigned gw = blockIdx.x;
     const unsigned nw = a.waves;
@@ -484,39 +508,51 @@ __device__ __forceinline__ void stream_lds(const KernelArgs &a) {
     constexpr int kMaxL = RB * U * Tile<SW>::kRaw;
 
     unsigned t = gw;
-    if (t < n_big) lds_issue<W, SW, RB, U>(a, off + (size_t)t * big, lane, stage0);
+    if (t < n_big) lds_issue<W, SW, RB, U, MASKED>(a, off + (size_t)t * big, lane, stage0);
     while (t < n_big) {
         const unsigned t1 = t + nw;
         if (t1 < n_big) {
-            lds_issue<W, SW, RB, U>(a, off + (size_t)t1 * big, lane, stage1);
+            lds_issue<W, SW, RB, U, MASKED>(a, off + (size_t)t1 * big, lane, stage1);
             wait_stage<kMaxL>(L);
         } else {
             wait_vm<0>();
         }
-        lds_consume<W, SW, RB, U, ST>(a, off + (size_t)t * big, lane, stage0);
+        lds_consume<W, SW, RB, U, ST, MASKED>(a, off + (size_t)t * big, lane, stage0);
         if (t1 >= n_big) break;
         const unsigned t2 = t1 + nw;
         if (t2 < n_big) {
-            lds_issue<W, SW, RB, U>(a, off + (size_t)t2 * big, lane, stage0);
+            lds_issue<W, SW, RB, U, MASKED>(a, off + (size_t)t2 * big, lane, stage0);
             wait_stage<kMaxL>(L);
         } else {
             wait_vm<0>();
         }
-        lds_consume<W, SW, RB, U, ST>(a, off + (size_t)t1 * big, lane, stage1);
+        lds_consume<W, SW, RB, U, ST, MASKED>(a, off + (size_t)t1 * big, lane, stage1);
         t = t2;
     }
-    reduce_rest<W, SW, RB, U, true, ST>(a, off, len, n_big * big, gw, nw, lane);
+    reduce_rest<W, SW, RB, U, true, ST, MASKED>(a, off, len, n_big * big, gw, nw, lane);
 }
 
-#define MPP_STREAM_LDS(NAME, ST, SLICED)                                     \
+template <int W, bool SW, int RB, bool ST, bool SLICED, bool MASKED>
+__device__ __forceinline__ void stream_lds(const KernelArgs &a) {
+    constexpr int NB = LdsStage<W, SW, RB, lds_batch(SW, RB)>::kBlocks;
+    __shared__ u32x4 stage0[NB][kWave];
+    __shared__ u32x4 stage1[NB][kWave];
+    stream_lds_as<W, SW, RB, ST, SLICED, MASKED>(a, stage0, stage1);
+}
+
+#define MPP_STREAM_LDS(NAME, ST, SLICED, M)                                  \
     template <int W, bool SW, int RB>                                      \
     __global__ __launch_bounds__(kLdsBlock) void NAME(KernelArgs a) {      \
-        stream_lds<W, SW, RB, ST, SLICED>(a);                              \
+        stream_lds<W, SW, RB, ST, SLICED, M>(a);                           \
     }
-MPP_STREAM_LDS(k_stream_lds, false, false)
-MPP_STREAM_LDS(k_stream_lds_nts, true, false)
-MPP_STREAM_LDS(k_stream_lds_sl, false, true)
-MPP_STREAM_LDS(k_stream_lds_nts_sl, true, true)
+MPP_STREAM_LDS(k_stream_lds, false, false, false)
+MPP_STREAM_LDS(k_stream_lds_nts, true, false, false)
+MPP_STREAM_LDS(k_stream_lds_sl, false, true, false)
+MPP_STREAM_LDS(k_stream_lds_nts_sl, true, true, false)
+MPP_STREAM_LDS(k_stream_lds_m, false, false, true)
+MPP_STREAM_LDS(k_stream_lds_nts_m, true, false, true)
+MPP_STREAM_LDS(k_stream_lds_sl_m, false, true, true)
+MPP_STREAM_LDS(k_stream_lds_nts_sl_m, true, true, true)
 #undef MPP_STREAM_LDS
 
 // ---------------------------------------------------------------------------
@@ -532,14 +568,19 @@ MPP_STREAM_LDS(k_stream_lds_nts_sl, true, true)
     {MPP_ROW(KERNEL, AR_F32, false), MPP_ROW(KERNEL, AR_BF16, false), MPP_ROW(KERNEL, AR_F16, false), \
      MPP_ROW(KERNEL, AR_BF16, true), MPP_ROW(KERNEL, AR_F16, true)}
 
-const void *const kSingleShot[5][4] = MPP_TABLE(k_single_shot);
-// [store_nt][sliced][combination][rank bucket]
-const void *const kStreamReg[2][2][5][4] = {
-    {MPP_TABLE(k_stream_reg), MPP_TABLE(k_stream_reg_sl)},
-    {MPP_TABLE(k_stream_reg_nts), MPP_TABLE(k_stream_reg_nts_sl)}};
-const void *const kStreamLds[2][2][5][4] = {
-    {MPP_TABLE(k_stream_lds), MPP_TABLE(k_stream_lds_sl)},
-    {MPP_TABLE(k_stream_lds_nts), MPP_TABLE(k_stream_lds_nts_sl)}};
+// [masked][combination][rank bucket]
+const void *const kSingleShot[2][5][4] = {MPP_TABLE(k_single_shot), MPP_TABLE(k_single_shot_m)};
+// [masked][store_nt][sliced][combination][rank bucket]
+const void *const kStreamReg[2][2][2][5][4] = {
+    {{MPP_TABLE(k_stream_reg), MPP_TABLE(k_stream_reg_sl)},
+     {MPP_TABLE(k_stream_reg_nts), MPP_TABLE(k_stream_reg_nts_sl)}},
+    {{MPP_TABLE(k_stream_reg_m), MPP_TABLE(k_stream_reg_sl_m)},
+     {MPP_TABLE(k_stream_reg_nts_m), MPP_TABLE(k_stream_reg_nts_sl_m)}}};
+const void *const kStreamLds[2][2][2][5][4] = {
+    {{MPP_TABLE(k_stream_lds), MPP_TABLE(k_stream_lds_sl)},
+     {MPP_TABLE(k_stream_lds_nts), MPP_TABLE(k_stream_lds_nts_sl)}},
+    {{MPP_TABLE(k_stream_lds_m), MPP_TABLE(k_stream_lds_sl_m)},
+     {MPP_TABLE(k_stream_lds_nts_m), MPP_TABLE(k_stream_lds_nts_sl_m)}}};
 
 int combo_index(int wire, bool src_is_wire) {
     if (wire == AR_F32) return 0;
@@ -611,14 +652,16 @@ hipError_t launch(Family family, int wire, bool src_is_wire, bool sliced, Kernel
     const int b = bucket_index(a.R);
     const int nt = a.store_nt ? 1 : 0;
     const int sl = sliced ? 1 : 0;
+    const unsigned full = a.R >= 32 ? ~0u : ((1u << a.R) - 1u);
+    const int m = (a.active & full) == full ? 0 : 1;   // some rank inactive
     const void *fn = nullptr;
     switch (family) {
     case Family::SingleShot:
         if (sliced) return hipErrorNotSupported;
-        fn = kSingleShot[c][b];
+        fn = kSingleShot[m][c][b];
         break;
-    case Family::StreamReg: fn = kStreamReg[nt][sl][c][b]; break;
-    case Family::StreamLds: fn = kStreamLds[nt][sl][c][b]; break;
+    case Family::StreamReg: fn = kStreamReg[m][nt][sl][c][b]; break;
+    case Family::StreamLds: fn = kStreamLds[m][nt][sl][c][b]; break;
     default: return hipErrorNotSupported;
     }
     if (shape.block % kWave != 0) return hipErrorInvalidValue;
