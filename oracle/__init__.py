@@ -12,7 +12,12 @@ Every function here follows the passages cited in ``ar_oracle.c``:
   partial ("CUDA allreduce.cu" page, "Chunked kernel AllReduce" comment block,
   phases 1 and 3, and the "Combined load-convert-add kernel" comment);
 * the fixed rank order of the sum and the write to every destination
-  ("Hexagon allreduce-ops.c" page, allreduce_thread_dma_1d and op_allreduce).
+  ("Hexagon allreduce-ops.c" page, allreduce_thread_dma_1d and op_allreduce);
+* the residual added after the ranks, element-wise or as one broadcast row
+  (same page, the HAS_ADD and IS_ROW_BCAST forms of the 1-D / 2-D loops);
+* narrow destinations that accumulate in their own type (CUDA page, the
+  half / nv_bfloat16 instances of the chunked kernel; Hexagon page, the f16
+  instances).
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (exhaustive conversions against torch / numpy, a double-rounding theorem for
@@ -69,6 +74,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_reduce.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp),
                                ctypes.c_int, sz, ctypes.c_int, ctypes.c_int]
     lib.orc_reduce.restype = ctypes.c_int
+    lib.orc_reduce_ex.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
+                                  ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, vp, sz]
+    lib.orc_reduce_ex.restype = ctypes.c_int
     return lib
 
 
@@ -140,14 +148,19 @@ def add_f32(a: np.ndarray, b: np.ndarray, lib=None) -> np.ndarray:
 # --- the reduce ------------------------------------------------------------
 
 def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
-           lib=None) -> np.ndarray:
+           lib=None, dst_type: int = F32, residual=None) -> np.ndarray:
     """Reference result of the partial-sum reduce.
 
     ``srcs``: sequence of R equally sized 1-D arrays.  float32 arrays are the
     caller-typed partials; uint16 arrays hold wire-typed bit patterns (then
     ``src_type`` must equal ``wire_type``).  A ``None`` entry is an inactive
     rank (its partial is all +0.0).
-    Returns an ``(n_dst, n)`` float32 array (every row holds the same bits).
+    ``dst_type``: F32, or F16 / BF16 (then wire and sources have that type).
+    ``residual``: None, or a 1-D array of the destination type (float32, or
+    uint16 bit patterns for a narrow destination) whose length is n (added
+    element-wise) or divides n (one row added to every row).
+    Returns an ``(n_dst, n)`` array of the destination type (float32, or
+    uint16 bit patterns); every row holds the same bits.
     """
     lib = lib or load()
     srcs = [None if s is None else np.ascontiguousarray(s) for s in srcs]
@@ -164,10 +177,17 @@ def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
             raise ValueError("sources differ in length")
         if s.dtype != want:
             raise TypeError(f"source dtype {s.dtype} does not match src_type {src_type}")
-    out = np.empty((n_dst, n), dtype=np.float32)
+    out_dtype = np.float32 if dst_type == F32 else np.uint16
+    res_ptr, res_len = None, 0
+    if residual is not None:
+        residual = np.ascontiguousarray(residual)
+        if residual.dtype != out_dtype:
+            raise TypeError(f"residual dtype {residual.dtype} does not match dst_type {dst_type}")
+        res_ptr, res_len = residual.ctypes.data, residual.size
+    out = np.empty((n_dst, n), dtype=out_dtype)
     dst_ptrs = (ctypes.c_void_p * n_dst)(*[out[d].ctypes.data for d in range(n_dst)])
     src_ptrs = (ctypes.c_void_p * R)(*[None if s is None else s.ctypes.data for s in srcs])
-    rc = lib.orc_reduce(dst_ptrs, n_dst, src_ptrs, R, n, src_type, wire_type)
+    rc = lib.orc_reduce_ex(dst_ptrs, n_dst, dst_type, src_ptrs, R, n, src_type, wire_type, res_ptr, res_len)
     if rc != 0:
         raise ValueError(f"oracle rejected arguments (rc={rc})")
     return out

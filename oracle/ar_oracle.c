@@ -9,8 +9,13 @@
  *
  *     w_r      = widen(round_W(src_r[i]))        r = 0 .. R-1
  *     acc      = w_0
- *     acc      = RN32(acc + w_r)                 r = 1 .. R-1, rank order
- *     dst_d[i] = acc                             (binary32, not re-rounded)
+ *     acc      = RN_D(acc + w_r)                 r = 1 .. R-1, rank order
+ *     acc      = RN_D(acc + res[i mod L])        only with a residual
+ *     dst_d[i] = acc                             (not re-rounded to the wire)
+ *
+ * RN_D is one rounding to the destination type D: binary32 (the common
+ * case), or binary16 / bfloat16 when the destination, the wire and the
+ * sources all have that type.
  *
  * Sources (the pages are cited by title and passage):
  *   - "CUDA allreduce.cu" page (toy 0.8.0 diff of ggml-cuda/allreduce.cu),
@@ -40,6 +45,12 @@
  *   - The accumulator is binary32 with one rounding per add; no wider or
  *     compensated arithmetic.
  *   - Subnormals are kept everywhere (no flush-to-zero on input or output).
+ *   - A narrow destination (binary16 / bfloat16, with the same wire and
+ *     source type, the only narrow combinations the CUDA page launches)
+ *     rounds to its type after every add, the residual add included; for
+ *     R = 2 this is the CUDA page's float add followed by the cast to T_dst.
+ *   - The residual is added once, after the last rank, in the destination
+ *     type, and is not rounded through the wire type.
  *
  * Build with:  gcc -O2 -fno-fast-math -ffp-contract=off -shared -fPIC
  * The float additions below are ordinary C float additions; on x86-64
@@ -213,15 +224,68 @@ static void orc_leave_ieee(unsigned saved) {
 }
 
 /* ---------------------------------------------------------------------------
- * The reduce.  dst: n_dst binary32 arrays; srcs: R arrays of src_type (a NULL
- * entry is an inactive rank contributing +0.0).
+ * Narrowing of a binary32 value to the destination type and back (exact
+ * widening): the identity for binary32, RNE for binary16 / bfloat16.
+ * ------------------------------------------------------------------------- */
+static float orc_to_dst(float x, int dst_type) {
+    const uint32_t bits = orc_float_to_bits(x);
+    switch (dst_type) {
+    case ORC_BF16: return orc_bits_to_float(orc_widen_bf16(orc_round_bf16(bits)));
+    case ORC_F16:  return orc_bits_to_float(orc_widen_f16(orc_round_f16(bits)));
+    default:       return x;
+    }
+}
+
+/* Element i of a destination-typed array, widened exactly. */
+static float orc_dst_value(const void *p, size_t i, int dst_type) {
+    if (dst_type == ORC_F32) return ((const float *)p)[i];
+    const uint16_t h = ((const uint16_t *)p)[i];
+    return orc_bits_to_float(dst_type == ORC_BF16 ? orc_widen_bf16(h) : orc_widen_f16(h));
+}
+
+/* Store a value that already lies in the destination type. */
+static void orc_store_dst(void *p, size_t i, float v, int dst_type) {
+    if (dst_type == ORC_F32) {
+        ((float *)p)[i] = v;
+    } else {
+        const uint32_t bits = orc_float_to_bits(v);
+        ((uint16_t *)p)[i] = dst_type == ORC_BF16 ? orc_round_bf16(bits) : orc_round_f16(bits);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * The reduce, general form.
+ *   dst      : n_dst arrays of dst_type, n elements each.
+ *   srcs     : R arrays of src_type (a NULL entry is an inactive rank
+ *              contributing +0.0).
+ *   residual : NULL, or residual_len elements of dst_type added after the
+ *              last rank ("Hexagon allreduce-ops.c" page, the HAS_ADD forms
+ *              of allreduce_thread_dma_1d / _2d: once the ranks are summed,
+ *              src[2 * n_ranks] is added, element-wise, or one row added to
+ *              every row in the IS_ROW_BCAST form).  residual_len == n is the
+ *              element-wise form; a smaller residual_len that divides n is
+ *              one row broadcast over the n / residual_len rows, element i
+ *              taking residual[i mod residual_len].  The residual is local to
+ *              the receiving rank and never crosses the wire, so it is not
+ *              rounded through the wire type.
+ *   dst_type : binary32, or binary16 / bfloat16 with wire_type == dst_type.
+ *              A narrow destination accumulates in its own type: every add
+ *              is rounded to dst_type ("CUDA allreduce.cu" page, the
+ *              half / nv_bfloat16 instances of the chunked kernel, whose sum
+ *              is cast to T_dst; "Hexagon allreduce-ops.c" page, the f16
+ *              instances adding natively in __fp16).  The add is done in
+ *              binary32 and then rounded once to dst_type; binary32 has at
+ *              least 2p + 2 significand bits for p = 11 and p = 8, so this
+ *              equals a correctly rounded add in dst_type.
  * Returns 0 on success, -1 on an argument the oracle does not define.
  * ------------------------------------------------------------------------- */
-int orc_reduce(float *const *dst, int n_dst, const void *const *srcs, int R,
-               size_t n, int src_type, int wire_type) {
+int orc_reduce_ex(void *const *dst, int n_dst, int dst_type, const void *const *srcs, int R,
+                  size_t n, int src_type, int wire_type, const void *residual, size_t residual_len) {
     if (R < 1 || n_dst < 1 || dst == NULL || srcs == NULL) return -1;
     if (wire_type < ORC_F32 || wire_type > ORC_BF16) return -1;
     if (src_type != ORC_F32 && src_type != wire_type) return -1;
+    if (dst_type != ORC_F32 && (dst_type != wire_type || src_type != wire_type)) return -1;
+    if (residual != NULL && (residual_len == 0 || n % residual_len != 0)) return -1;
 
     const unsigned saved = orc_enter_ieee();
     for (size_t i = 0; i < n; ++i) {
@@ -229,13 +293,24 @@ int orc_reduce(float *const *dst, int n_dst, const void *const *srcs, int R,
         for (int r = 1; r < R; ++r) {
             const float w = orc_wire_value(srcs[r], i, src_type, wire_type);
             acc = acc + w;
+            if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);
+        }
+        if (residual != NULL) {
+            acc = acc + orc_dst_value(residual, i % residual_len, dst_type);
+            if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);
         }
         for (int d = 0; d < n_dst; ++d) {
-            dst[d][i] = acc;
+            orc_store_dst(dst[d], i, acc, dst_type);
         }
     }
     orc_leave_ieee(saved);
     return 0;
+}
+
+/* The reduce into binary32 destinations without a residual. */
+int orc_reduce(float *const *dst, int n_dst, const void *const *srcs, int R,
+               size_t n, int src_type, int wire_type) {
+    return orc_reduce_ex((void *const *)dst, n_dst, ORC_F32, srcs, R, n, src_type, wire_type, NULL, 0);
 }
 
 /* Array forms of the conversions, used by the exhaustive pins. */

@@ -24,7 +24,18 @@ What pins what:
 * the whole reduce     -- a closed form: partials k * 2^-6 with |k| <= 127 are
                           exact in every wire type and every partial sum for
                           R <= 16 is exact in binary32, so the result is
-                          (sum k) * 2^-6, computed with integers.
+                          (sum k) * 2^-6, computed with integers;
+* the residual         -- the fp64 route with the residual as one more,
+                          unrounded, last term; the closed form with a k * 2^-6
+                          residual; a broadcast row equals the element-wise
+                          residual tiled over the rows; hand-worked rows;
+* narrow destinations  -- numpy's float16 and torch's CPU bfloat16 arithmetic
+                          (each add correctly rounded in that type, since
+                          binary32 has >= 2p+2 bits for p = 11 and p = 8),
+                          binary64 then one conversion for float16, brute force
+                          over ordered pairs and triples of 16-bit edge
+                          patterns, a closed form exact in the narrow type, and
+                          hand-worked rows.
 """
 from __future__ import annotations
 
@@ -114,8 +125,17 @@ def load_golden() -> list[dict]:
 
 def check_golden(lib) -> None:
     rows = load_golden()
-    assert len(rows) >= 35
+    assert len(rows) >= 50
     for row in rows:
+        if row["op"] in ("dreduce", "dradd"):
+            _check_golden_narrow(lib, row)
+            continue
+        if row["op"] == "radd":
+            vals = np.array(row["inputs"], dtype=np.uint32).view(np.float32)
+            srcs = [vals[i:i + 1] for i in range(len(vals) - 1)]
+            got = oracle.reduce(srcs, row["wire"], lib=lib, residual=vals[-1:])[0, 0]
+            _check_golden_f32(row, got)
+            continue
         if row["op"] == "reduce":
             srcs = [None if v is None else np.array([v], dtype=np.uint32).view(np.float32)
                     for v in row["inputs"]]
@@ -123,11 +143,7 @@ def check_golden(lib) -> None:
                 got = _reduce_all_inactive(lib, len(row["inputs"]), row["wire"])
             else:
                 got = oracle.reduce(srcs, row["wire"], lib=lib)[0, 0]
-            if row["expected"] is None:
-                assert np.isnan(got), row["id"]
-            else:
-                gb = int(np.array([got], dtype=np.float32).view(np.uint32)[0])
-                assert gb == row["expected"], f"{row['id']}: {gb:#010x} != {row['expected']:#010x}"
+            _check_golden_f32(row, got)
             continue
         x = np.array(row["inputs"], dtype=np.uint32)
         if row["op"] == "round":
@@ -138,13 +154,28 @@ def check_golden(lib) -> None:
             else:
                 assert got == row["expected"], f"{row['id']}: {got:#06x} != {row['expected']:#06x}"
         else:
-            srcs = [x[i:i + 1].view(np.float32) for i in range(len(x))]
-            got = oracle.reduce(srcs, row["wire"], lib=lib)[0, 0]
-            if row["expected"] is None:
-                assert np.isnan(got), row["id"]
-            else:
-                gb = int(np.array([got], dtype=np.float32).view(np.uint32)[0])
-                assert gb == row["expected"], f"{row['id']}: {gb:#010x} != {row['expected']:#010x}"
+            raise AssertionError(f"unknown golden op {row['op']!r} in {row['id']}")
+
+
+def _check_golden_f32(row, got) -> None:
+    if row["expected"] is None:
+        assert np.isnan(got), row["id"]
+    else:
+        gb = int(np.array([got], dtype=np.float32).view(np.uint32)[0])
+        assert gb == row["expected"], f"{row['id']}: {gb:#010x} != {row['expected']:#010x}"
+
+
+def _check_golden_narrow(lib, row) -> None:
+    w = row["wire"]
+    vals = np.array(row["inputs"], dtype=np.uint16)
+    k = len(vals) - 1 if row["op"] == "dradd" else len(vals)
+    srcs = [vals[i:i + 1] for i in range(k)]
+    res = vals[k:k + 1] if row["op"] == "dradd" else None
+    got = int(oracle.reduce(srcs, w, src_type=w, dst_type=w, residual=res, lib=lib)[0, 0])
+    if row["expected"] is None:
+        assert bool(is_nan16(np.array([got]), w)[0]), row["id"]
+    else:
+        assert got == row["expected"], f"{row['id']}: {got:#06x} != {row['expected']:#06x}"
 
 
 def _reduce_all_inactive(lib, R: int, wire: int) -> float:
@@ -350,6 +381,142 @@ def check_broadcast_and_wire_srcs(lib, seed: int = 23) -> None:
             assert_same_f32(out_w, out[0], f"wire-typed sources wire={wire}")
 
 
+# --- residual ------------------------------------------------------------------
+
+def check_residual(lib, seed: int = 41) -> None:
+    """The residual is one more binary32 add after the last rank, never wire-rounded:
+    the fp64 route over library-rounded partials with the raw residual appended."""
+    g = _edge_grid()
+    for R in (2, 3, 8):
+        n = 3000
+        srcs = workloads.random_partials(970, seed, R, n, dist="wide")
+        res = workloads.residual(970, seed, n, dist="wide")
+        res[:g.size] = g
+        srcs[-1][g.size:2 * g.size] = g
+        for wire in (F32, BF16, F16):
+            got = oracle.reduce(srcs, wire, n_dst=2, residual=res, lib=lib)
+            with np.errstate(all="ignore"):
+                want = fp64_route_fold([lib_wire_value(s, wire) for s in srcs] + [res])
+            assert_same_f32(got[0], want, f"residual R={R} wire={wire}")
+            assert np.array_equal(got[0].view(np.uint32), got[1].view(np.uint32))
+            # one broadcast row == the element-wise residual tiled over the rows
+            row = res[:600]
+            got_row = oracle.reduce(srcs, wire, residual=row, lib=lib)[0]
+            want_row = oracle.reduce(srcs, wire, residual=np.tile(row, n // 600), lib=lib)[0]
+            assert_same_f32(got_row, want_row, f"row broadcast R={R} wire={wire}")
+            with np.errstate(all="ignore"):
+                want_row2 = fp64_route_fold([lib_wire_value(s, wire) for s in srcs] + [np.tile(row, n // 600)])
+            assert_same_f32(got_row, want_row2, f"row broadcast fp64 route R={R} wire={wire}")
+    # closed form: k * 2^-6 residual, exact everywhere
+    rng = np.random.default_rng(seed)
+    for R in (2, 5, 15):
+        n = 2053
+        ks = [rng.integers(-127, 128, n) for _ in range(R + 1)]
+        vals = [k.astype(np.float32) * np.float32(2.0 ** -6) for k in ks]
+        want = np.sum(ks, axis=0).astype(np.float32) * np.float32(2.0 ** -6)
+        for wire in (F32, BF16, F16):
+            got = oracle.reduce(vals[:R], wire, residual=vals[R], lib=lib)[0]
+            assert_same_f32(got, want, f"residual closed form R={R} wire={wire}")
+    # inactive ranks with a residual: zeros in their place
+    srcs = workloads.random_partials(971, seed, 4, 999, dist="wide")
+    res = workloads.residual(971, seed, 999)
+    got = oracle.reduce([srcs[0], None, srcs[2], None], BF16, residual=res, lib=lib)[0]
+    z = np.zeros(999, dtype=np.float32)
+    with np.errstate(all="ignore"):
+        want = fp64_route_fold([lib_wire_value(s, BF16) for s in (srcs[0], z, srcs[2], z)] + [res])
+    assert_same_f32(got, want, "residual with inactive ranks")
+
+
+# --- narrow destinations --------------------------------------------------------
+
+def lib_narrow_fold(ws16: list[np.ndarray], dtype: int) -> np.ndarray:
+    """Left fold of 16-bit values with every add done by a library in that type:
+    numpy float16 arithmetic, torch CPU bfloat16 arithmetic.  Returns uint16."""
+    if dtype == F16:
+        acc = ws16[0].view(np.float16).copy()
+        with np.errstate(all="ignore"):
+            for w in ws16[1:]:
+                acc = acc + w.view(np.float16)
+        return acc.view(np.uint16)
+    acc = torch.from_numpy(ws16[0].view(np.int16).copy()).view(torch.bfloat16)
+    for w in ws16[1:]:
+        acc = acc + torch.from_numpy(w.view(np.int16).copy()).view(torch.bfloat16)
+    return acc.view(torch.int16).numpy().view(np.uint16)
+
+
+def f64_narrow_fold_f16(ws16: list[np.ndarray]) -> np.ndarray:
+    """binary16 fold where each add is float64(a) + float64(b) converted once to binary16."""
+    acc = ws16[0].view(np.float16)
+    with np.errstate(all="ignore"):
+        for w in ws16[1:]:
+            acc = (acc.astype(np.float64) + w.view(np.float16).astype(np.float64)).astype(np.float16)
+    return acc.view(np.uint16)
+
+
+def assert_same_16(got: np.ndarray, want: np.ndarray, wire: int, what: str) -> None:
+    """Bit equality of 16-bit patterns, NaN compared only as 'is a NaN'."""
+    got = np.ascontiguousarray(got, dtype=np.uint16)
+    want = np.ascontiguousarray(want, dtype=np.uint16)
+    gn, wn = is_nan16(got, wire), is_nan16(want, wire)
+    if not np.array_equal(gn, wn):
+        i = int(np.flatnonzero(gn != wn)[0])
+        raise AssertionError(f"{what}: NaN mismatch at {i}: got {int(got[i]):#06x} want {int(want[i]):#06x}")
+    bad = (got != want) & ~gn
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} differ, first at {i}: "
+                             f"{int(got[i]):#06x} vs {int(want[i]):#06x}")
+
+
+def _grid16(dtype: int) -> np.ndarray:
+    return np.concatenate([workloads.special_values16(dtype), workloads.nan_values16(dtype)[:1]])
+
+
+def check_narrow_dst(lib, seed: int = 43) -> None:
+    """fp16 / bf16 destinations accumulate in their own type, one rounding per add."""
+    for dtype in (F16, BF16):
+        g = _grid16(dtype)
+        # brute force: every ordered pair and triple of the edge grid
+        for R in (2, 3):
+            cols = [c.ravel().astype(np.uint16) for c in np.meshgrid(*([g] * R), indexing="ij")]
+            got = oracle.reduce(cols, dtype, src_type=dtype, dst_type=dtype, lib=lib)[0]
+            assert_same_16(got, lib_narrow_fold(cols, dtype), dtype, f"narrow brute force R={R} dtype={dtype}")
+            if dtype == F16:
+                assert_same_16(got, f64_narrow_fold_f16(cols), dtype, f"narrow fp64 route R={R}")
+        # random partials, several rank counts, residual element-wise and broadcast
+        for R in (2, 4, 7, 16):
+            n = 2400
+            srcs = workloads.random_narrow(980, seed + R, R, n, dtype, dist="wide")
+            srcs[0][:g.size] = g
+            res = workloads.residual(980, seed + R, n, dtype, dist="wide")
+            out = oracle.reduce(srcs, dtype, n_dst=3, src_type=dtype, dst_type=dtype, lib=lib)
+            assert_same_16(out[0], lib_narrow_fold(srcs, dtype), dtype, f"narrow R={R} dtype={dtype}")
+            for d in (1, 2):
+                assert np.array_equal(out[0], out[d])
+            got = oracle.reduce(srcs, dtype, src_type=dtype, dst_type=dtype, residual=res, lib=lib)[0]
+            assert_same_16(got, lib_narrow_fold(srcs + [res], dtype), dtype, f"narrow residual R={R}")
+            row = res[:480]
+            got = oracle.reduce(srcs, dtype, src_type=dtype, dst_type=dtype, residual=row, lib=lib)[0]
+            assert_same_16(got, lib_narrow_fold(srcs + [np.tile(row, n // 480)], dtype), dtype,
+                           f"narrow row residual R={R}")
+            # inactive ranks are +0 in the destination type
+            mixed = [s if r % 3 else None for r, s in enumerate(srcs)]
+            zero = np.zeros(n, dtype=np.uint16)
+            got = oracle.reduce(mixed, dtype, src_type=dtype, dst_type=dtype, lib=lib)[0]
+            assert_same_16(got, lib_narrow_fold([zero if s is None else s for s in mixed], dtype), dtype,
+                           f"narrow inactive R={R}")
+        # closed form: k * 2^-6, every partial sum exact in the narrow type
+        rng = np.random.default_rng(seed)
+        kmax = 127 if dtype == F16 else 7
+        for R in (2, 8, 16):
+            n = 1031
+            ks = [rng.integers(-kmax, kmax + 1, n) for _ in range(R)]
+            srcs = [workloads.as_wire_typed(k.astype(np.float32) * np.float32(2.0 ** -6), dtype) for k in ks]
+            want = workloads.as_wire_typed(np.sum(ks, axis=0).astype(np.float32) * np.float32(2.0 ** -6), dtype)
+            got = oracle.reduce(srcs, dtype, src_type=dtype, dst_type=dtype, lib=lib)[0]
+            assert_same_16(got, want, dtype, f"narrow closed form R={R} dtype={dtype}")
+
+
 def cheap_checks():
     """Checks fast enough to run against every planted-mistake build."""
     return [
@@ -364,4 +531,6 @@ def cheap_checks():
         ("order", check_order_sensitivity),
         ("broadcast", check_broadcast_and_wire_srcs),
         ("inactive", check_inactive_ranks),
+        ("residual", check_residual),
+        ("narrow", check_narrow_dst),
     ]

@@ -59,6 +59,25 @@ MUTANTS = [
                                       "        return -0.0f;")]),
     ("add_keeps_ftz", [("_mm_setcsr(saved & ~((1u << 15) | (1u << 6)));",
                         "_mm_setcsr(saved | (1u << 15) | (1u << 6));")]),
+    ("residual_skipped", [("if (residual != NULL) {", "if (0) {")]),
+    ("residual_before_ranks", [
+        ("float acc = orc_wire_value(srcs[0], i, src_type, wire_type);",
+         "float acc = orc_wire_value(srcs[0], i, src_type, wire_type);\n"
+         "        if (residual != NULL) acc = acc + orc_dst_value(residual, i % residual_len, dst_type);"),
+        ("acc = acc + orc_dst_value(residual, i % residual_len, dst_type);\n            if",
+         "(void)0;\n            if")]),
+    ("residual_rounded_to_wire", [
+        ("acc = acc + orc_dst_value(residual, i % residual_len, dst_type);\n            if",
+         "acc = acc + orc_to_dst(orc_dst_value(residual, i % residual_len, dst_type), wire_type);\n            if")]),
+    ("residual_row_index_swapped", [
+        ("orc_dst_value(residual, i % residual_len, dst_type)",
+         "orc_dst_value(residual, residual_len == n ? i : (i / residual_len) % residual_len, dst_type)")]),
+    ("narrow_rounds_once_at_end", [
+        ("            if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);\n        }\n        if (residual",
+         "        }\n        if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);\n        if (residual")]),
+    ("narrow_store_wrong_format", [
+        ("dst_type == ORC_BF16 ? orc_round_bf16(bits) : orc_round_f16(bits)",
+         "dst_type == ORC_BF16 ? orc_round_f16(bits) : orc_round_bf16(bits)")]),
 ]
 
 

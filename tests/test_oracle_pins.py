@@ -69,3 +69,25 @@ def test_rejects_mismatched_source_type(orc):
     a = np.zeros(4, dtype=np.uint16)
     with pytest.raises(ValueError):
         oracle.reduce([a, a], oracle.BF16, src_type=oracle.F16, lib=orc)
+
+
+def test_residual(orc):
+    oc.check_residual(orc)
+
+
+def test_narrow_destinations(orc):
+    oc.check_narrow_dst(orc)
+
+
+def test_rejects_undefined_residual_and_narrow_combinations(orc):
+    a = np.ones(12, dtype=np.float32)
+    with pytest.raises(ValueError):      # residual length must divide n
+        oracle.reduce([a, a], oracle.BF16, residual=np.ones(5, dtype=np.float32), lib=orc)
+    with pytest.raises(ValueError):      # a narrow destination needs the same wire type
+        oracle.reduce([a, a], oracle.BF16, dst_type=oracle.F16, lib=orc)
+    h = np.zeros(12, dtype=np.uint16)
+    with pytest.raises(ValueError):
+        oracle.reduce([h, h], oracle.BF16, src_type=oracle.BF16, dst_type=oracle.F16, lib=orc)
+    with pytest.raises(TypeError):       # residual of the wrong type
+        oracle.reduce([h, h], oracle.F16, src_type=oracle.F16, dst_type=oracle.F16,
+                      residual=np.ones(12, dtype=np.float32), lib=orc)

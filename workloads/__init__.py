@@ -145,3 +145,38 @@ def special_values() -> np.ndarray:
 def nan_values() -> np.ndarray:
     """A few NaN encodings (quiet, signalling, negative)."""
     return np.array([0x7FC00000, 0x7F800001, 0xFFC00001, 0x7FBFFFFF], dtype=np.uint32).view(np.float32)
+
+
+def special_values16(wire: int) -> np.ndarray:
+    """16-bit edge patterns of a wire / destination type (uint16 bit constants):
+    signed zeros, smallest / largest subnormals, smallest normal, +-1 and its
+    neighbours, the largest finite values, infinities and a few small powers
+    of two that tie when added to 1."""
+    if wire == F16:
+        bits = [0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x83FF, 0x0400, 0x8400,
+                0x3C00, 0xBC00, 0x3C01, 0x3BFF, 0x1000, 0x9000, 0x1400, 0x0C00,
+                0x7BFF, 0xFBFF, 0x7BFE, 0x7C00, 0xFC00, 0x5BFF, 0x4000, 0xC000]
+    elif wire == BF16:
+        bits = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x8080,
+                0x3F80, 0xBF80, 0x3F81, 0x3F7F, 0x3B80, 0xBB80, 0x3C00, 0x3B00,
+                0x7F7F, 0xFF7F, 0x7F7E, 0x7F80, 0xFF80, 0x4B80, 0x4000, 0xC000]
+    else:
+        raise ValueError(wire)
+    return np.array(bits, dtype=np.uint16)
+
+
+def nan_values16(wire: int) -> np.ndarray:
+    """Two NaN encodings of a 16-bit type."""
+    return np.array([0x7E00, 0xFD01] if wire == F16 else [0x7FC0, 0xFF81], dtype=np.uint16)
+
+
+def random_narrow(case: int, set_idx: int, R: int, n: int, dtype: int, dist: str = "normal") -> list[np.ndarray]:
+    """R partials already held in a 16-bit type (uint16 bit patterns), made from
+    float32 draws by the same generator choice as ``as_wire_typed``."""
+    return [as_wire_typed(x, dtype) for x in random_partials(case, set_idx, R, n, dist)]
+
+
+def residual(case: int, set_idx: int, length: int, dtype: int = F32, dist: str = "normal") -> np.ndarray:
+    """A residual stream of the destination type: float32, or uint16 bit patterns."""
+    x = draw(dist, length, rng_for(case, set_idx, 1000))
+    return x if dtype == F32 else as_wire_typed(x, dtype)
