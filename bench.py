@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_prefill_bf16.json")
-KERNEL_SRC = os.path.join(ROOT, "mixed_precision_partial_amd", "csrc", "ar_kernels.hip")
+CSRC = os.path.join(ROOT, "mixed_precision_partial_amd", "csrc")
 
 
 def log(msg: str) -> None:
@@ -37,8 +37,14 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of every device-code source (the kernel templates and their instance files)."""
+    import glob
+
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(algo_bytes: int):
@@ -217,7 +223,17 @@ def main() -> int:
 
 
 CALIBRATION_BYTES = 64 << 20   # read and written once per calibration launch
-REDUCE_KERNEL = "k_stream_reg<2, false, 2>"   # bf16 wire, fp32 sources, R bucket 2
+# the prefill reduce's kernel instance: register-staged, bf16 wire, fp32 sources,
+# fp32 destination, rank bucket 2, every rank active, no residual, cached stores
+REDUCE_KERNEL = "k_stream_reg<Cfg<2, false, false, 2, false, false>>"
+
+
+def _plain_name(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").replace("mpp::", "").replace(" ", "")
+
+
+def is_reduce_kernel(name: str) -> bool:
+    return _plain_name(REDUCE_KERNEL) in _plain_name(name)
 CALIBRATION_KERNEL = "vectorized_elementwise_kernel"
 TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py"
 PMC_CMD = ("cd /tmp && rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {tag} -- "
@@ -242,12 +258,12 @@ def summarize_trace(directory: str) -> None:
              f"Command: `{TRACE_CMD}`", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows[:8]:
-        name = r["Name"].replace("(anonymous namespace)::", "").replace("|", "/")
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("mpp::", "").replace("|", "/")
         if len(name) > 90:
             name = name[:87] + "..."
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
-    red = [r for r in rows if REDUCE_KERNEL in r["Name"]]
+    red = [r for r in rows if is_reduce_kernel(r["Name"])]
     if red:
         avg_us = float(red[0]["AverageNs"]) / 1e3
         algo = 100_663_296
@@ -261,7 +277,7 @@ def summarize_trace(directory: str) -> None:
 def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
     def per_kernel(directory):
         rows = _csv_rows(directory, "counter_collection.csv")
-        red = [float(r["Counter_Value"]) for r in rows if REDUCE_KERNEL in r["Kernel_Name"]]
+        red = [float(r["Counter_Value"]) for r in rows if is_reduce_kernel(r["Kernel_Name"])]
         cal = [float(r["Counter_Value"]) for r in rows if CALIBRATION_KERNEL in r["Kernel_Name"]]
         if not red or not cal:
             raise RuntimeError(f"missing dispatches in {directory}")
@@ -451,6 +467,54 @@ def other_schedules(torch, ar, wl):
     b = 2 * w.R * w.n * 4
     out["slice_bcast_f16"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"slice_bcast_f16: {out['slice_bcast_f16']}")
+    del srcs, dsts
+
+    # fused residual add on the prefill shape (element-wise hidden state, and a
+    # broadcast row of 4096), and narrow destinations; rotated sets so the
+    # Infinity Cache cannot serve them
+    w = wl.WORKLOADS["prefill_bf16"]
+    sets = 4
+    srcs = [[torch.from_numpy(p).cuda() for p in wl.partials(w, k)] for k in range(sets)]
+    dsts = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(sets)]
+    ress = [torch.from_numpy(wl.residual(w.case, k, w.n)).cuda() for k in range(sets)]
+    row = torch.from_numpy(wl.residual(w.case, 9, 4096)).cuda()
+    k = [0]
+
+    def rot(fn):
+        def call():
+            i = k[0] % sets
+            k[0] += 1
+            fn(i)
+        return call
+
+    ms = timed(rot(lambda i: ar.ar_reduce_add(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                              ress[i], w.n, stream=stream)), 200)
+    b = w.R * w.n * 4 + w.n * 4 + w.n * 4
+    out["prefill_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"prefill_residual: {out['prefill_residual']}")
+    ms = timed(rot(lambda i: ar.ar_reduce_add(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                              row, 4096, stream=stream)), 200)
+    b = w.R * w.n * 4 + w.n * 4 + 4096 * 4
+    out["prefill_row_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"prefill_row_residual: {out['prefill_row_residual']}")
+    del srcs, dsts, ress
+    srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_BF16).view(np.int16)).cuda() for p in wl.partials(w, k)]
+            for k in range(sets)]
+    dsts = [torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(sets)]
+    ms = timed(rot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                                          stream=stream)), 200)
+    b = w.R * w.n * 2 + w.n * 2
+    out["prefill_bf16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"prefill_bf16_dst: {out['prefill_bf16_dst']}")
+    del srcs, dsts
+    w = wl.WORKLOADS["slice_bcast_f16"]
+    srcs = [torch.from_numpy(wl.as_wire_typed(p, ar.AR_F16).view(np.int16)).cuda() for p in wl.partials(w, 0)]
+    dsts = [torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(w.R)]
+    ms = timed(lambda: ar.ar_reduce(ctx, dsts, srcs, w.n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_RS_BCAST,
+                                    stream=stream), 50)
+    b = w.R * w.n * 2 + w.R * w.n * 2
+    out["slice_bcast_f16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"slice_bcast_f16_dst: {out['slice_bcast_f16_dst']}")
     del srcs, dsts
 
     w = wl.WORKLOADS["host_staged_bf16"]

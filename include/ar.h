@@ -2,14 +2,20 @@
  * ar.h -- C ABI of the MI355X (gfx950) mixed-precision partial-sum reduce.
  *
  * The operation: R partial activations (one per tensor-parallel rank) are
- * summed element-wise into a binary32 result.  Every partial -- the
- * receiving rank's own included -- is first rounded through a possibly
- * narrower "wire" type, and the rounded values are added in binary32 in the
- * fixed rank order 0, 1, ..., R-1, so every rank computes the same bits.
+ * summed element-wise into a binary32 result (or, for 16-bit tensors, a
+ * result of their own type).  Every partial -- the receiving rank's own
+ * included -- is first rounded through a possibly narrower "wire" type, and
+ * the rounded values are added in the destination type in the fixed rank
+ * order 0, 1, ..., R-1, so every rank computes the same bits.
  *
  *   for 0 <= i < n, for every destination d:
  *       w_r       = widen(round_W(src_r[i]))          r = 0 .. R-1
- *       dst_d[i]  = ((w_0 + w_1) + w_2) + ... + w_{R-1}   (binary32, RNE)
+ *       acc       = w_0
+ *       acc       = RN_D(acc + w_r)                   r = 1 .. R-1
+ *       acc       = RN_D(acc + res[i mod L])          ar_reduce_add only
+ *       dst_d[i]  = acc
+ *   RN_D rounds to nearest even in the destination type D: binary32, or
+ *   binary16 / bfloat16 when destination, wire and sources share that type.
  *
  * Passages this follows (page title, then the passage):
  *   - "CUDA allreduce.cu" page (toy 0.8.0 diff of ggml-cuda/allreduce.cu):
@@ -20,7 +26,13 @@
  *   - "Hexagon allreduce-ops.c" page (llama.cpp fork, ggml-hexagon/htp):
  *     allreduce_thread_dma_1d (fixed-order sum s0+s1, then +s2 ..., and the
  *     write of each block to every destination; each rank reduces its own
- *     element range) and op_allreduce (rank-count checks, n_dsts).
+ *     element range), its HAS_ADD forms and the 2-D IS_ROW_BCAST form (a
+ *     residual added after the ranks, element-wise or one row per row), the
+ *     f16 instances (sums kept in the tensor's own 16-bit type), and
+ *     op_allreduce (rank-count checks, n_dsts).
+ *   - "CUDA allreduce.cu" page, the chunked kernel's (half, half) and
+ *     (nv_bfloat16, nv_bfloat16) instances: 16-bit tensors are reduced in
+ *     their own type, the float sum cast back to it.
  *   - "llama.cpp commit log" page: the Vulkan comm hook commit (partials
  *     narrowed to F16 before the host transfer and added into the fp32
  *     result; a chunked pipeline for prefill and a single-shot path for
@@ -53,7 +65,8 @@ extern "C" {
  * lazily allocated HBM scratch for host-staged mode. */
 typedef struct ar_ctx ar_ctx;
 
-/* Element types.  dst_type must be AR_F32 in this version. */
+/* Element types.  A 16-bit dst_type needs wire_type == dst_type (its sources
+ * hold that type too). */
 typedef enum { AR_F32 = 0, AR_F16 = 1, AR_BF16 = 2 } ar_dtype;
 
 /* Schedules, in the low 8 bits of `mode`.
@@ -135,7 +148,7 @@ typedef struct {
 int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
 
 /* Enqueue one reduce.
- *   dst       : array of n_dst pointers to binary32 buffers of n elements
+ *   dst       : array of n_dst pointers to buffers of n dst_type elements
  *               (n_dst = R for AR_MODE_RS_BCAST, else 1); device memory of
  *               the context's device.
  *   srcs      : array of R pointers to the partials, n elements each, of
@@ -143,7 +156,9 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *               memory, or pinned host memory for AR_MODE_HOST_STAGED.
  *   R         : 2 .. AR_MAX_RANKS.
  *   n         : elements per partial; 0 is a no-op returning AR_OK.
- *   dst_type  : AR_F32 (AR_F16 / AR_BF16 -> AR_ERR_UNSUPPORTED).
+ *   dst_type  : AR_F32; or AR_F16 / AR_BF16 with wire_type == dst_type, in
+ *               which case the sources hold dst_type and every add is
+ *               rounded to it (a different wire -> AR_ERR_UNSUPPORTED).
  *   wire_type : AR_F32, AR_F16 or AR_BF16; not wider than dst_type.
  *   mode      : AR_MODE_* | optional AR_SRC_WIRE | optional AR_SRC_INACTIVE_NULL.
  *   hip_stream: hipStream_t to enqueue on (NULL = null stream).
@@ -152,15 +167,37 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *   pointer not 16-byte aligned, an unknown type / mode / flag, a wire type
  *   wider than the destination, a destination that overlaps another
  *   destination or a source other than exactly in place (dst[d] equal to
- *   some srcs[r], both binary32), n * element size overflowing size_t, or
+ *   some srcs[r], same element width), n * element size overflowing size_t, or
  *   memory of the wrong kind for the mode (device pointers of another device,
  *   pageable host memory, host sources outside AR_MODE_HOST_STAGED);
- *   AR_ERR_UNSUPPORTED for dst_type != AR_F32;
+ *   AR_ERR_UNSUPPORTED for a 16-bit dst_type with a different wire_type;
  *   AR_ERR_NOMEM if host-staged scratch cannot be allocated;
  *   AR_ERR_RUNTIME if a launch or copy cannot be enqueued.  Faults of
  *   enqueued work surface at the caller's next synchronisation. */
 int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
               int dst_type, int wire_type, unsigned mode, void *hip_stream);
+
+/* Enqueue one reduce followed by a residual add: after the last rank,
+ * res[i mod residual_len] is added in the destination type, element-wise
+ * (residual_len == n) or as one row broadcast to every row (residual_len
+ * divides n), as the "Hexagon allreduce-ops.c" page's HAS_ADD forms of
+ * allreduce_thread_dma_1d / _2d and its IS_ROW_BCAST form do.  The residual
+ * is the receiving rank's own tensor: it is not rounded through the wire.
+ *   residual     : residual_len elements of dst_type in device memory of the
+ *                  context's device, 16-byte aligned (also for host-staged
+ *                  sources).  It may be exactly one of the destinations when
+ *                  element-wise (x += reduce(partials)); any other overlap
+ *                  with a destination is invalid.  It may overlap sources.
+ *   residual_len : n (element-wise), or a divisor of n that is a multiple of
+ *                  8 (broadcast row; other divisors -> AR_ERR_UNSUPPORTED).
+ * Every other argument, the ownership rules and the error codes are those
+ * of ar_reduce; residual NULL, residual_len 0 or not dividing n ->
+ * AR_ERR_INVALID (n = 0 is a no-op and checks only residual != NULL).  Calls
+ * with a residual run on the register-staged kernels (stream_kernel 2 is
+ * not used for them). */
+int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
+                  int dst_type, int wire_type, unsigned mode, const void *residual,
+                  size_t residual_len, void *hip_stream);
 
 /* Drain the context's internal stream and release everything it owns.
  * NULL is accepted and returns AR_OK.  Work already enqueued by ar_reduce
@@ -185,11 +222,14 @@ typedef struct {
     size_t n_chunks;      /* ceil(n / chunk_elems)                          */
     size_t slice_start[AR_MAX_RANKS]; /* RS_BCAST: first element of rank r  */
     size_t slice_len[AR_MAX_RANKS];   /* RS_BCAST: elements of rank r       */
-    size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*4   */
+    size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*dst_bytes
+                             (+ residual_len*dst_bytes with a residual)      */
     int    store_nt;      /* 1: streaming (non-temporal) destination stores */
     int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
     int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged   */
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
+    int    dst_bytes;     /* bytes per destination element                  */
+    int    residual_kind; /* 0 none, 1 element-wise, 2 broadcast row        */
 } ar_plan;
 
 /* Validate the arguments exactly as ar_reduce does, except the memory-kind
@@ -199,6 +239,12 @@ typedef struct {
 int ar_plan_query(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
                   size_t n, int dst_type, int wire_type, unsigned mode, int srcs_on_host,
                   ar_plan *plan);
+
+/* The same for ar_reduce_add (residual checks included). */
+int ar_plan_query_add(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
+                      size_t n, int dst_type, int wire_type, unsigned mode,
+                      const void *residual, size_t residual_len, int srcs_on_host,
+                      ar_plan *plan);
 
 #ifdef __cplusplus
 }

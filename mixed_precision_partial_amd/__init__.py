@@ -9,9 +9,10 @@ The functions carry the C names:
 
     ctx = ar_init(device=0, config=None)
     ar_reduce(ctx, dsts, srcs, n, dst_type, wire_type, mode, stream=None)
+    ar_reduce_add(ctx, dsts, srcs, n, dst_type, wire_type, mode, residual, residual_len, stream=None)
     ar_free(ctx)
     ar_status_str(code)
-    ar_plan_query(...)
+    ar_plan_query(...), ar_plan_query_add(...)
 
 ``dsts`` / ``srcs`` are sequences of torch tensors or raw integer addresses;
 ``stream`` is a ``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None
@@ -69,6 +70,8 @@ class ArPlan(ctypes.Structure):
         ("host_direct", ctypes.c_int),
         ("stream_kernel", ctypes.c_int),
         ("active_mask", ctypes.c_uint),
+        ("dst_bytes", ctypes.c_int),
+        ("residual_kind", ctypes.c_int),
     ]
 
 
@@ -105,6 +108,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
                                   ctypes.c_int, ctypes.POINTER(ArPlan)]
     lib.ar_plan_query.restype = ctypes.c_int
+    lib.ar_reduce_add.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, sz,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_uint, vp, sz, vp]
+    lib.ar_reduce_add.restype = ctypes.c_int
+    lib.ar_plan_query_add.argtypes = [ctypes.POINTER(ArConfig), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                      ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
+                                      vp, sz, ctypes.c_int, ctypes.POINTER(ArPlan)]
+    lib.ar_plan_query_add.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -169,6 +179,24 @@ def ar_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = 
     return rc
 
 
+def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual,
+                  residual_len: int | None = None, stream=None, check: bool = True) -> int:
+    """Enqueue one reduce followed by a residual add (element-wise when
+    ``residual_len == n``, else one broadcast row); ``residual_len`` defaults to
+    the residual tensor's element count.  Returns the status (raises ArError on
+    failure if ``check``)."""
+    lib = load_library()
+    R = len(srcs) if srcs is not None else 0
+    if residual_len is None:
+        residual_len = residual.numel()
+    rc = lib.ar_reduce_add(ctx, _ptr_array(dsts), _ptr_array(srcs), R, int(n), int(dst_type),
+                           int(wire_type), int(mode), _addr(residual), int(residual_len),
+                           _stream_handle(stream))
+    if check and rc != AR_OK:
+        raise ArError(rc, "ar_reduce_add")
+    return rc
+
+
 def ar_free(ctx) -> None:
     rc = load_library().ar_free(ctx)
     if rc != AR_OK:
@@ -186,6 +214,20 @@ def ar_plan_query(dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = A
     rc = lib.ar_plan_query(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
                            _ptr_array(srcs), R, int(n), int(dst_type), int(wire_type), int(mode),
                            int(bool(srcs_on_host)), ctypes.byref(plan))
+    return rc, plan
+
+
+def ar_plan_query_add(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual,
+                      residual_len: int, srcs_on_host: bool = False, config=None, R: int | None = None):
+    """Host-only validation + plan of ar_reduce_add; returns (status, ArPlan)."""
+    lib = load_library()
+    plan = ArPlan()
+    cfg = _config(config)
+    R = (len(srcs) if srcs is not None else 0) if R is None else R
+    rc = lib.ar_plan_query_add(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
+                               _ptr_array(srcs), R, int(n), int(dst_type), int(wire_type), int(mode),
+                               _addr(residual), int(residual_len), int(bool(srcs_on_host)),
+                               ctypes.byref(plan))
     return rc, plan
 
 

@@ -1,12 +1,17 @@
 """Build the gfx950 shared library ``libmpp_ar.so`` in-tree with hipcc.
 
+Every source compiles to an object of its own (in parallel: the kernel tables
+are spread over several files), then one hipcc line links the library.
+
 Usage:  python -m mixed_precision_partial_amd.build   (or build_library())
 """
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -15,14 +20,18 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmpp_ar.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = [os.path.join(CSRC, "ar_api.cpp"), os.path.join(CSRC, "ar_kernels.hip")]
+OBJ_DIR = os.path.join(HERE, "_build")
+
+
+def sources() -> list[str]:
+    return [os.path.join(CSRC, "ar_api.cpp")] + sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
 
 HIPCC_FLAGS = [
     "-O3",
     "--offload-arch=gfx950",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fvisibility=hidden",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -39,19 +48,42 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build_library(out: str = LIB_PATH, verbose: bool = False) -> str:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+# hipcc's host pass does not know the packed-fp32 feature and says so; that is expected
+_NOISE = "'-packed-fp32-ops' is not a recognized feature"
+
+
+def _run(cmd: list[str]) -> tuple[int, list[str]]:
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature and says so; that is expected
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l and l.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if msgs and verbose:
-        print("\n".join(msgs), file=sys.stderr)
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if _NOISE not in l and l.strip()]
+    return res.returncode, msgs
+
+
+def build_library(out: str = LIB_PATH, verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s) + ".o") for s in srcs]
+    inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
+    cmds = [[hipcc(), *HIPCC_FLAGS, *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        results = list(pool.map(_run, cmds))
+    failed = [(c, m) for c, (rc, m) in zip(cmds, results) if rc != 0]
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join("\n".join(m) for _, m in failed))
+    tmp = out + ".tmp"
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, msgs = _run(link)
+    if rc != 0:
+        raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
+    if verbose:
+        for _, m in results:
+            if m:
+                print("\n".join(m), file=sys.stderr)
     os.replace(tmp, out)
     return out
 

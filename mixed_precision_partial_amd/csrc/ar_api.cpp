@@ -110,9 +110,17 @@ bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
 
 size_t round_down(size_t x, size_t m) { return x / m * m; }
 
+// The optional residual of ar_reduce_add: `len` elements of the destination
+// type, added element-wise (len == n) or as one row broadcast to every row.
+struct Residual {
+    const void *ptr = nullptr;
+    size_t len = 0;
+};
+
 // Everything ar_reduce checks without the HIP runtime, plus the plan.
 int validate_and_plan(const Config &cfg, void *const *dst, const void *const *srcs, int R, size_t n,
-                      int dst_type, int wire_type, unsigned mode, bool srcs_on_host, ar_plan *plan) {
+                      int dst_type, int wire_type, unsigned mode, const Residual &res, bool srcs_on_host,
+                      ar_plan *plan) {
     if (R < 2 || R > AR_MAX_RANKS) return AR_ERR_INVALID;
     if (!valid_type(dst_type) || !valid_type(wire_type)) return AR_ERR_INVALID;
     if ((mode & ~(AR_MODE_MASK | AR_SRC_WIRE | AR_SRC_INACTIVE_NULL)) != 0) return AR_ERR_INVALID;
@@ -120,12 +128,26 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
     const int base = static_cast<int>(mode & AR_MODE_MASK);
     if (base < AR_MODE_AUTO || base > AR_MODE_HOST_STAGED) return AR_ERR_INVALID;
     if (elem_bytes(wire_type) > elem_bytes(dst_type)) return AR_ERR_INVALID;
-    if (dst_type != AR_F32) return AR_ERR_UNSUPPORTED;
+    // a narrow destination is built for its own wire type only (the narrow
+    // combinations the CUDA page launches: half/half and bf16/bf16)
+    if (dst_type != AR_F32 && wire_type != dst_type) return AR_ERR_UNSUPPORTED;
     if (dst == nullptr || srcs == nullptr) return AR_ERR_INVALID;
 
-    const bool src_wire = (mode & AR_SRC_WIRE) != 0;
+    const bool dst_narrow = dst_type != AR_F32;
+    // a narrow destination's sources hold its type (AR_SRC_WIRE or not)
+    const bool src_wire = (mode & AR_SRC_WIRE) != 0 || dst_narrow;
     const int src_bytes = src_wire ? elem_bytes(wire_type) : elem_bytes(dst_type);
     const int wire_bytes = elem_bytes(wire_type);
+    const int dst_bytes = elem_bytes(dst_type);
+    int res_kind = 0;
+    if (res.ptr != nullptr && n > 0) {
+        if (res.len == 0 || res.len > n || n % res.len != 0) return AR_ERR_INVALID;
+        if (reinterpret_cast<uintptr_t>(res.ptr) % 16 != 0) return AR_ERR_INVALID;
+        res_kind = res.len == n ? 1 : 2;
+        // a broadcast row is read 16 bytes at a time by lanes whose 4 or 8
+        // consecutive elements must stay inside one row
+        if (res_kind == 2 && (res.len % 8 != 0 || res.len > mpp::kMaxLaunchElems)) return AR_ERR_UNSUPPORTED;
+    }
 
     int resolved = base;
     if (base == AR_MODE_AUTO) {
@@ -154,8 +176,9 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
     }
     if (n > (SIZE_MAX / 8) / AR_MAX_RANKS) return AR_ERR_INVALID;
 
-    const size_t dst_len = n * 4;
+    const size_t dst_len = n * static_cast<size_t>(dst_bytes);
     const size_t src_len = n * static_cast<size_t>(src_bytes);
+    const size_t res_bytes = res_kind != 0 ? res.len * static_cast<size_t>(dst_bytes) : 0;
     if (n > 0) {
         for (int d = 0; d < n_dst; ++d) {
             const uintptr_t pd = reinterpret_cast<uintptr_t>(dst[d]);
@@ -170,7 +193,16 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 if (!ranges_overlap(pd, dst_len, ps, src_len)) continue;
                 // exactly in place with equal element width is the one allowed overlap:
                 // every element is read from all sources before the same thread writes it
-                if (!(ps == pd && src_bytes == 4)) return AR_ERR_INVALID;
+                if (!(ps == pd && src_bytes == dst_bytes)) return AR_ERR_INVALID;
+            }
+            if (res_kind != 0) {
+                // an element-wise residual may be a destination itself (x += reduce):
+                // each element's residual is read by the thread that writes it; a
+                // broadcast row is read by every row, so it must not be written
+                const uintptr_t pr = reinterpret_cast<uintptr_t>(res.ptr);
+                if (ranges_overlap(pd, dst_len, pr, res_bytes) && !(res_kind == 1 && pr == pd)) {
+                    return AR_ERR_INVALID;
+                }
             }
         }
     }
@@ -209,14 +241,16 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 plan->slice_len[r] = e - s;
             }
         }
-        plan->algo_bytes = static_cast<size_t>(R) * src_len + static_cast<size_t>(n_dst) * dst_len;
+        plan->algo_bytes = static_cast<size_t>(R) * src_len + static_cast<size_t>(n_dst) * dst_len + res_bytes;
+        plan->dst_bytes = dst_bytes;
+        plan->residual_kind = res_kind;
         // Automatic store policy, measured on MI355X: when the call writes at
         // least as many bytes as it reads (broadcast to R destinations, 16-bit
         // sources at R = 2) non-temporal stores are faster; when reads dominate,
         // ordinary write-back stores drain from L2 / Infinity Cache while the
         // reads stream and are faster.
         const size_t written = static_cast<size_t>(n_dst) * dst_len;
-        const size_t read = static_cast<size_t>(R) * src_len;
+        const size_t read = static_cast<size_t>(R) * src_len + (res_kind == 1 ? res_bytes : 0);
         plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written >= read);
         // host-staged sources: copy-engine pipeline (1) or the kernel reading
         // the pinned buffers over PCIe directly (2)
@@ -224,12 +258,15 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // streaming kernel family: explicit choice, else measured on MI355X --
         // the LDS-staged double buffer wins for two 16-bit sources (as many
         // bytes written as read, short tiles), the register kernel elsewhere
+        // (the LDS-staged kernel has no residual form)
         if (resolved == AR_MODE_SINGLE_SHOT) {
             plan->stream_kernel = 0;
+        } else if (res_kind != 0) {
+            plan->stream_kernel = 1;
         } else if (cfg.stream_kernel != 0) {
             plan->stream_kernel = cfg.stream_kernel;
         } else {
-            plan->stream_kernel = (src_wire && R == 2) ? 2 : 1;
+            plan->stream_kernel = (src_wire && !dst_narrow && R == 2) ? 2 : 1;
         }
     }
     return AR_OK;
@@ -322,16 +359,38 @@ mpp::Family stream_family(const ar_plan &plan) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_RUNTIME; }
 
+mpp::Types launch_types(const ar_plan &plan, int wire_type) {
+    return mpp::Types{wire_type, plan.src_bytes == 2, plan.dst_bytes == 2};
+}
+
+// Residual fields of a launch whose element 0 is element `first` of the call.
+void set_residual(mpp::KernelArgs &a, const Residual &res, size_t n, size_t first, int dst_bytes) {
+    if (res.ptr == nullptr) return;
+    if (res.len == n) {
+        a.res = static_cast<const char *>(res.ptr) + first * static_cast<size_t>(dst_bytes);
+        a.res_len = 0;
+        a.res_phase = 0;
+    } else {
+        a.res = res.ptr;
+        a.res_len = static_cast<unsigned>(res.len);
+        a.res_phase = static_cast<unsigned>(first % res.len);
+    }
+}
+
 // SINGLE_SHOT / CHUNKED / RS_BCAST: launches on the caller's stream, at most
 // kMaxLaunchElems elements per launch.
 int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
-               int wire_type, bool src_wire, hipStream_t stream) {
+               int wire_type, const Residual &res, hipStream_t stream) {
     const mpp::Family family = plan.mode == AR_MODE_SINGLE_SHOT ? mpp::Family::SingleShot : stream_family(plan);
+    const mpp::Types types = launch_types(plan, wire_type);
     const size_t sb = static_cast<size_t>(plan.src_bytes);
+    const size_t db = static_cast<size_t>(plan.dst_bytes);
 
     if (plan.mode == AR_MODE_RS_BCAST) {
         // gridDim.y = the ranks' slices; a slice longer than one launch covers
-        // is cut into pieces at the same relative offset in every slice
+        // is cut into pieces at the same relative offset in every slice.  The
+        // slice ranges are element indices of the whole call, so the residual
+        // is indexed from element 0.
         size_t longest = 0;
         for (int r = 0; r < R; ++r) longest = std::max(longest, static_cast<size_t>(plan.slice_len[r]));
         for (size_t p0 = 0; p0 < longest; p0 += mpp::kMaxLaunchElems) {
@@ -341,6 +400,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             a.chunk_elems = 0;
             a.store_nt = plan.store_nt;
             a.active = plan.active_mask;
+            set_residual(a, res, n, 0, plan.dst_bytes);
             unsigned max_len = 0;
             for (int r = 0; r < R; ++r) {
                 const size_t len = plan.slice_len[r] > p0 ? std::min(mpp::kMaxLaunchElems, plan.slice_len[r] - p0) : 0;
@@ -348,11 +408,11 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
                 a.slice_len[r] = static_cast<unsigned>(len);
                 max_len = std::max<unsigned>(max_len, static_cast<unsigned>(len));
                 a.src[r] = srcs[r];
-                a.dst[r] = static_cast<float *>(dst[r]);
+                a.dst[r] = dst[r];
             }
-            const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, max_len,
+            const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, max_len,
                                                            static_cast<unsigned>(R), c->cu_count, c->cfg.grid_wgs);
-            if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, true, a, shape, stream))) return rc;
+            if (int rc = hip_status(mpp::launch(family, types, true, a, shape, stream))) return rc;
         }
         return AR_OK;
     }
@@ -368,7 +428,8 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         for (int r = 0; r < R; ++r) {
             a.src[r] = srcs[r] == nullptr ? nullptr : static_cast<const char *>(srcs[r]) + p0 * sb;
         }
-        a.dst[0] = static_cast<float *>(dst[0]) + p0;
+        a.dst[0] = static_cast<char *>(dst[0]) + p0 * db;
+        set_residual(a, res, n, p0, plan.dst_bytes);
         // CHUNKED: gridDim.y walks the plan's chunks; SINGLE_SHOT: one range
         a.chunk_elems = static_cast<unsigned>(len);
         if (plan.mode == AR_MODE_CHUNKED) {
@@ -379,9 +440,9 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             }
         }
         const unsigned n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
-        const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, a.chunk_elems, n_ranges,
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, a.chunk_elems, n_ranges,
                                                        c->cu_count, c->cfg.grid_wgs);
-        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, false, a, shape, stream))) return rc;
+        if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
     }
     return AR_OK;
 }
@@ -415,8 +476,10 @@ int ensure_scratch(ar_ctx *c, size_t bytes) {
 // of a later chunk into the same slot waits for that mark, so copies run ahead
 // of the adds by up to K chunks.
 int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
-                    int wire_type, bool src_wire, hipStream_t stream) {
+                    int wire_type, const Residual &res, hipStream_t stream) {
+    const mpp::Types types = launch_types(plan, wire_type);
     const size_t sb = static_cast<size_t>(plan.src_bytes);
+    const size_t db = static_cast<size_t>(plan.dst_bytes);
     const size_t chunk = plan.chunk_elems;
     const size_t K = static_cast<size_t>(c->cfg.host_slots);
     const size_t rank_stride = chunk * sb;
@@ -455,10 +518,11 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         a.active = plan.active_mask;
         a.chunk_elems = static_cast<unsigned>(len);
         for (int r = 0; r < R; ++r) a.src[r] = srcs[r] == nullptr ? nullptr : slot_base + r * rank_stride;
-        a.dst[0] = static_cast<float *>(dst[0]) + e0;
-        const mpp::LaunchShape shape = mpp::plan_shape(family, wire_type, src_wire, R, static_cast<unsigned>(len), 1,
+        a.dst[0] = static_cast<char *>(dst[0]) + e0 * db;
+        set_residual(a, res, n, e0, plan.dst_bytes);
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(len), 1,
                                                        c->cu_count, c->cfg.grid_wgs);
-        if (int rc = hip_status(mpp::launch(family, wire_type, src_wire, false, a, shape, stream))) return rc;
+        if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
         if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
         c->slot_used[slot] = 1;
     }
@@ -482,7 +546,19 @@ AR_API int ar_plan_query(const ar_config *cfg, void *const *dst, const void *con
                          int dst_type, int wire_type, unsigned mode, int srcs_on_host, ar_plan *plan) {
     Config c;
     if (int rc = resolve_config(cfg, &c)) return rc;
-    return validate_and_plan(c, dst, srcs, R, n, dst_type, wire_type, mode, srcs_on_host != 0, plan);
+    return validate_and_plan(c, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, srcs_on_host != 0, plan);
+}
+
+AR_API int ar_plan_query_add(const ar_config *cfg, void *const *dst, const void *const *srcs, int R, size_t n,
+                             int dst_type, int wire_type, unsigned mode, const void *residual, size_t residual_len,
+                             int srcs_on_host, ar_plan *plan) {
+    Config c;
+    if (int rc = resolve_config(cfg, &c)) return rc;
+    if (residual == nullptr) return AR_ERR_INVALID;
+    Residual res;
+    res.ptr = residual;
+    res.len = residual_len;
+    return validate_and_plan(c, dst, srcs, R, n, dst_type, wire_type, mode, res, srcs_on_host != 0, plan);
 }
 
 AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
@@ -541,18 +617,19 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
     return AR_OK;
 }
 
-AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
-                     int wire_type, unsigned mode, void *hip_stream) {
+namespace {
+
+int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
+                int wire_type, unsigned mode, const Residual &res, void *hip_stream) {
     if (ctx == nullptr) return AR_ERR_INVALID;
     // cheap checks first, without touching the runtime
     ar_plan plan;
     const bool auto_mode = (mode & AR_MODE_MASK) == AR_MODE_AUTO;
-    int rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, false, &plan);
+    int rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, res, false, &plan);
     if (rc != AR_OK) return rc;
 
-    const bool src_wire = (mode & AR_SRC_WIRE) != 0;
     const size_t src_len = n * static_cast<size_t>(plan.src_bytes);
-    const size_t dst_len = n * 4;
+    const size_t dst_len = n * static_cast<size_t>(plan.dst_bytes);
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return AR_ERR_RUNTIME;
@@ -566,7 +643,7 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
         const Kind k0 = memory_kind(srcs[first_active], src_len, ctx->device);
         if (k0 == Kind::Other) return AR_ERR_INVALID;
         if (auto_mode && k0 == Kind::PinnedHost) {
-            rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, true, &plan);
+            rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, res, true, &plan);
             if (rc != AR_OK) return rc;
         }
     }
@@ -582,6 +659,10 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
     for (int d = 0; d < plan.n_dst; ++d) {
         if (memory_kind(dst[d], dst_len, ctx->device) != Kind::Device) return AR_ERR_INVALID;
     }
+    if (res.ptr != nullptr &&
+        memory_kind(res.ptr, res.len * static_cast<size_t>(plan.dst_bytes), ctx->device) != Kind::Device) {
+        return AR_ERR_INVALID;
+    }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (plan.mode == AR_MODE_HOST_STAGED) {
@@ -590,11 +671,27 @@ AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int
             // pinned partials through their device mapping, no HBM staging
             ar_plan direct = plan;
             direct.mode = AR_MODE_CHUNKED;
-            return run_device(ctx, direct, dst, src_view, R, n, wire_type, src_wire, stream);
+            return run_device(ctx, direct, dst, src_view, R, n, wire_type, res, stream);
         }
-        return run_host_staged(ctx, plan, dst, srcs, R, n, wire_type, src_wire, stream);
+        return run_host_staged(ctx, plan, dst, srcs, R, n, wire_type, res, stream);
     }
-    return run_device(ctx, plan, dst, srcs, R, n, wire_type, src_wire, stream);
+    return run_device(ctx, plan, dst, srcs, R, n, wire_type, res, stream);
+}
+
+}  // namespace
+
+AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
+                     int wire_type, unsigned mode, void *hip_stream) {
+    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, hip_stream);
+}
+
+AR_API int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
+                         int wire_type, unsigned mode, const void *residual, size_t residual_len, void *hip_stream) {
+    if (residual == nullptr) return AR_ERR_INVALID;
+    Residual res;
+    res.ptr = residual;
+    res.len = residual_len;
+    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, res, hip_stream);
 }
 
 AR_API int ar_free(ar_ctx *ctx) {

@@ -1,0 +1,738 @@
+// ar_device.h -- gfx950 device code of the mixed-precision partial-sum reduce
+// (templates only; the ar_k_*.hip files instantiate them into kernel tables).
+//
+// Every kernel computes, for each element i of its range and every
+// destination d:
+//     acc = wire(src_0[i]); acc = RN_D(acc + wire(src_r[i])) for r = 1 .. R-1
+//     acc = RN_D(acc + res[i])         (with a residual only)
+//     dst_d[i] = acc
+// where wire(x) rounds a binary32 partial to the wire type (RNE) and widens it
+// back exactly, or just widens when the source already holds the wire type,
+// and RN_D is one rounding to the destination type (binary32, or binary16 /
+// bfloat16 when destination, wire and sources share that type).
+//   * The fold runs in rank order with one rounding per add ("Hexagon
+//     allreduce-ops.c" page, allreduce_thread_dma_1d: s0 + s1, then + s2 ...),
+//     and the local partial is rounded like the peers' ("CUDA allreduce.cu"
+//     page, "Chunked kernel AllReduce" comment block, phase 3).
+//   * The residual is added after the last rank, element-wise or as one row
+//     broadcast to every row (Hexagon page, the HAS_ADD / IS_ROW_BCAST forms),
+//     in the destination type, never rounded through the wire.
+//   * Narrow destinations accumulate in their own type (CUDA page, the half /
+//     nv_bfloat16 chunked-kernel instances; Hexagon page, the f16 instances):
+//     the add is done in binary32 and rounded once to the 16-bit type, which
+//     is the correctly rounded 16-bit add (binary32 has >= 2p + 2 bits).
+//
+// The path is a stream over HBM with at most 0.1 flop per byte, so nothing
+// here is a contraction and nothing uses MFMA.  What matters is keeping
+// enough 16-byte loads in flight per CU and writing whole cache lines:
+//   * A wave owns a "wave tile" of 512 elements: 64 lanes x 8 elements.
+//     binary32 sources are read as two dwordx4 loads per lane, each covering
+//     1 KiB contiguous per wave instruction; 16-bit sources are one dwordx4 per
+//     lane (8 consecutive elements).
+//   * The single-shot kernel gives each wave one tile and exits: the decode
+//     case is bound by launch latency, so it issues every load of the tile at
+//     once and keeps the grid just large enough.
+//   * The streaming kernel gives each wave a batch of U tiles, issuing all
+//     R x U x 16 B loads of the batch before the first add so that many
+//     independent loads are in flight per lane.
+//   * The rank count is a template bucket (2, 4, 8, 16) with the real R tested
+//     against compile-time rank indices, so every kernarg access uses a
+//     constant offset (no private-memory copies) and all loads of a batch can
+//     issue back to back.
+#pragma once
+
+#include "ar_internal.h"
+
+namespace mpp {
+namespace {
+
+constexpr int kWave = 64;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Compile-time description of one kernel instance.
+//   W      wire type (ar_dtype)
+//   SW     sources already hold the wire type (16-bit loads)
+//   DN     narrow destination: destination type == W (16-bit stores); implies SW
+//   RB     rank bucket: the kernel handles R <= RB
+//   MASKED some rank may be inactive (bit r of KernelArgs::active clear)
+//   RES    a residual is added after the fold
+template <int W_, bool SW_, bool DN_, int RB_, bool MASKED_, bool RES_>
+struct Cfg {
+    static constexpr int W = W_;
+    static constexpr bool SW = SW_;
+    static constexpr bool DN = DN_;
+    static constexpr int RB = RB_;
+    static constexpr bool MASKED = MASKED_;
+    static constexpr bool RES = RES_;
+    static_assert(!DN || (SW && W != AR_F32), "a narrow destination has 16-bit sources of its own type");
+    static constexpr int kSrcRaw = SW ? 1 : 2;   // dwordx4 loads per lane per source per tile
+    static constexpr int kResRaw = DN ? 1 : 2;   // dwordx4 loads per lane of the residual per tile
+    static constexpr int kDstBytes = DN ? 2 : 4;
+};
+
+__device__ __forceinline__ float f32_from_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t bits_from_f32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    } else {
+        return *reinterpret_cast<const u32x4 *>(p);
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(void *p, u32x4 v) {
+    if constexpr (NT) {
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+    } else {
+        *reinterpret_cast<u32x4 *>(p) = v;
+    }
+}
+
+// Round two binary32 values to the 16-bit type W (round to nearest even,
+// subnormals kept, NaN stays NaN: gfx950's v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 under the default mode) and return them packed, x in the
+// low half.
+template <int W>
+__device__ __forceinline__ uint32_t round_pack(float x, float y) {
+    if constexpr (W == AR_BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+    }
+}
+
+// Widen a pair of 16-bit values packed in one dword (element 2k in the low
+// half, 2k+1 in the high half); exact.
+template <int W>
+__device__ __forceinline__ void widen_pair(uint32_t w, float &x, float &y) {
+    if constexpr (W == AR_BF16) {
+        x = f32_from_bits(w << 16);
+        y = f32_from_bits(w & 0xFFFF0000u);
+    } else {
+        const f16x2 p = __builtin_bit_cast(f16x2, w);
+        x = static_cast<float>(p.x);
+        y = static_cast<float>(p.y);
+    }
+}
+
+// round_W then widen, two binary32 values at a time; the identity for a
+// binary32 wire.
+template <int W>
+__device__ __forceinline__ void wire_pair(float &x, float &y) {
+    if constexpr (W != AR_F32) widen_pair<W>(round_pack<W>(x, y), x, y);
+}
+
+// One element of a source, scalar path (range remainders).
+template <int W, bool SW>
+__device__ __forceinline__ float wire_one(const void *src, size_t i) {
+    if constexpr (SW) {
+        const uint32_t h = reinterpret_cast<const uint16_t *>(src)[i];
+        float x, y;
+        widen_pair<W>(h, x, y);
+        return x;
+    } else {
+        float x = reinterpret_cast<const float *>(src)[i];
+        float y = 0.0f;
+        wire_pair<W>(x, y);
+        return x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Lane layout of one wave tile (512 elements starting at element `t`):
+//   binary32 sources, and their destinations and residual:
+//       part j in {0,1}: elements t + 256 j + 4 lane + {0..3}
+//   16-bit sources: elements t + 8 lane + {0..7} (one dwordx4)
+//       binary32 destinations / residual: t + 8 lane + 4 j + {0..3}
+//       16-bit destinations / residual:   t + 8 lane + {0..7} (one dwordx4)
+// Values v[0..7] of a lane are ordered as v[4 j + k] for the binary32 forms
+// and v[k] = element t + 8 lane + k for the 16-bit forms.
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ size_t part_elem(size_t t, int lane, int j) {
+    return C::SW ? t + 8 * lane + 4 * j : t + 256 * j + 4 * lane;
+}
+
+template <class C, bool NT>
+__device__ __forceinline__ void tile_load(const void *src, size_t t, int lane, u32x4 (&raw)[C::kSrcRaw]) {
+    if constexpr (C::SW) {
+        raw[0] = load16<NT>(reinterpret_cast<const uint16_t *>(src) + t + 8 * lane);
+    } else {
+        const float *s = reinterpret_cast<const float *>(src) + t + 4 * lane;
+        raw[0] = load16<NT>(s);
+        raw[1] = load16<NT>(s + 256);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void tile_values(const u32x4 (&raw)[C::kSrcRaw], float (&v)[8]) {
+    if constexpr (C::SW) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) widen_pair<C::W>(raw[0][k], v[2 * k], v[2 * k + 1]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {
+                float x = f32_from_bits(raw[j][k]);
+                float y = f32_from_bits(raw[j][k + 1]);
+                wire_pair<C::W>(x, y);
+                v[4 * j + k] = x;
+                v[4 * j + k + 1] = y;
+            }
+        }
+    }
+}
+
+// Index of launch element e in the residual: e itself (element-wise), or its
+// column in the broadcast row.  res_len is a multiple of 8, so the 4 or 8
+// consecutive elements of one lane part never straddle a row boundary.
+__device__ __forceinline__ size_t res_index(const KernelArgs &a, size_t e) {
+    if (a.res_len == 0) return e;
+    return (static_cast<unsigned>(e) + a.res_phase) % a.res_len;
+}
+
+// Residual loads of one tile: streaming loads for the element-wise form
+// (read once), ordinary cached loads for a broadcast row (read by every row).
+// Both forms issue the same number of loads, so the branch does not change
+// how many loads are outstanding after it.
+template <class C, bool NT>
+__device__ __forceinline__ void res_load(const KernelArgs &a, size_t t, int lane, u32x4 (&raw)[C::kResRaw]) {
+    if (a.res_len == 0) {
+#pragma unroll
+        for (int j = 0; j < C::kResRaw; ++j) {
+            const size_t e = part_elem<C>(t, lane, j);
+            raw[j] = load16<NT>(static_cast<const char *>(a.res) + e * C::kDstBytes);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < C::kResRaw; ++j) {
+            const size_t e = res_index(a, part_elem<C>(t, lane, j));
+            raw[j] = load16<false>(static_cast<const char *>(a.res) + e * C::kDstBytes);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void res_values(const u32x4 (&raw)[C::kResRaw], float (&v)[8]) {
+    if constexpr (C::DN) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) widen_pair<C::W>(raw[0][k], v[2 * k], v[2 * k + 1]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[4 * j + k] = f32_from_bits(raw[j][k]);
+    }
+}
+
+// One rounding of every accumulator to the destination type (no-op for
+// binary32 destinations).
+template <class C>
+__device__ __forceinline__ void round_dst(float (&acc)[8]) {
+    if constexpr (C::DN) {
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) wire_pair<C::W>(acc[k], acc[k + 1]);
+    }
+}
+
+template <class C, bool ST>
+__device__ __forceinline__ void tile_store(void *dst, size_t t, int lane, const float (&acc)[8]) {
+    if constexpr (C::DN) {
+        // the values already lie in the destination type: the packing is exact
+        const u32x4 v = {round_pack<C::W>(acc[0], acc[1]), round_pack<C::W>(acc[2], acc[3]),
+                         round_pack<C::W>(acc[4], acc[5]), round_pack<C::W>(acc[6], acc[7])};
+        store16<ST>(static_cast<uint16_t *>(dst) + t + 8 * lane, v);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 v = {bits_from_f32(acc[4 * j]), bits_from_f32(acc[4 * j + 1]),
+                             bits_from_f32(acc[4 * j + 2]), bits_from_f32(acc[4 * j + 3])};
+            store16<ST>(static_cast<float *>(dst) + part_elem<C>(t, lane, j), v);
+        }
+    }
+}
+
+// Rank r takes part with a partial (bit r of the launch's mask); an inactive
+// rank's partial is +0.0 everywhere: nothing is loaded and +0.0 is added in
+// its place, which keeps -0 + inactive == +0 like a zeroed shard.
+// MASKED = false is the common case (every rank active): the test folds away
+// and the loads of a batch stay one straight-line sequence.  The host picks
+// the masked kernel instance only when some rank is inactive: per-rank
+// branches around loads make the compiler drain each rank's loads before
+// issuing the next, so the common case must not carry them.
+template <class C>
+__device__ __forceinline__ bool rank_active(const KernelArgs &a, int r) {
+    if constexpr (C::MASKED) {
+        return (a.active >> r) & 1u;
+    } else {
+        return true;
+    }
+}
+
+template <class C>
+__device__ __forceinline__ bool rank_used(const KernelArgs &a, int r) {
+    return r < 2 || r < a.R;
+}
+
+// Registers of one batch of U wave tiles.
+template <class C, int U>
+struct Batch {
+    u32x4 src[C::RB][U][C::kSrcRaw];
+    u32x4 res[U][C::kResRaw];
+};
+
+// Issue every load of a batch of U consecutive wave tiles starting at
+// element `t` (range offset included) for the first R of RB sources, tile by
+// tile: the loads of tile 0 are the oldest in flight, so tile 0 can be folded
+// and stored while the later tiles' loads are still arriving.  The residual
+// loads of the batch come last.
+template <class C, int U, bool NT>
+__device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int lane, Batch<C, U> &b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < C::RB; ++r) {
+            if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
+                tile_load<C, NT>(a.src[r], t + u * kWaveTile, lane, b.src[r][u]);
+            }
+        }
+        // keep tile order: the scheduler must not hoist a later tile's loads
+        // above this one's
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (C::RES) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) res_load<C, NT>(a, t + u * kWaveTile, lane, b.res[u]);
+    }
+}
+
+// Fold one tile in rank order (one rounding to the destination type per add),
+// add the residual, and store to every destination.
+template <class C, bool ST>
+__device__ __forceinline__ void fold_store_tile(const KernelArgs &a, size_t t, int lane,
+                                                const u32x4 (&src)[C::RB][C::kSrcRaw], const u32x4 *res) {
+    float acc[8];
+    if (rank_active<C>(a, 0)) {
+        tile_values<C>(src[0], acc);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    }
+#pragma unroll
+    for (int r = 1; r < C::RB; ++r) {
+        if (rank_used<C>(a, r)) {
+            float w[8];
+            if (rank_active<C>(a, r)) {
+                tile_values<C>(src[r], w);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) w[k] = 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = acc[k] + w[k];
+            round_dst<C>(acc);
+        }
+    }
+    if constexpr (C::RES) {
+        u32x4 rr[C::kResRaw];
+#pragma unroll
+        for (int j = 0; j < C::kResRaw; ++j) rr[j] = res[j];
+        float rv[8];
+        res_values<C>(rr, rv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = acc[k] + rv[k];
+        round_dst<C>(acc);
+    }
+#pragma unroll
+    for (int d = 0; d < C::RB; ++d) {
+        if (d < a.n_dst) tile_store<C, ST>(a.dst[d], t, lane, acc);
+    }
+}
+
+// Fold each tile of the batch and store it before the next tile is folded.
+// Stores use ST (non-temporal for calls that write at least as much as they
+// read, ordinary write-back stores otherwise, which drain from L2 / Infinity
+// Cache while the next kernel reads).  The store policy is a template
+// parameter: two stores that differ only in their cache hint would be merged
+// into one by the compiler.
+template <class C, int U, bool ST>
+__device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int lane, const Batch<C, U> &b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        u32x4 src[C::RB][C::kSrcRaw];
+#pragma unroll
+        for (int r = 0; r < C::RB; ++r)
+#pragma unroll
+            for (int j = 0; j < C::kSrcRaw; ++j) src[r][j] = b.src[r][u][j];
+        fold_store_tile<C, ST>(a, t + u * kWaveTile, lane, src, b.res[u]);
+    }
+}
+
+template <class C, int U, bool NT, bool ST>
+__device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int lane) {
+    Batch<C, U> b;
+    load_batch<C, U, NT>(a, t, lane, b);
+    fold_store<C, U, ST>(a, t, lane, b);
+}
+
+// Elements [begin, end) of the launch, one per lane per step (end - begin is
+// below one wave tile, so this is at most 8 steps).
+template <class C>
+__device__ __forceinline__ void reduce_scalar(const KernelArgs &a, size_t begin, size_t end, int lane) {
+    for (size_t e = begin + lane; e < end; e += kWave) {
+        float acc = rank_active<C>(a, 0) ? wire_one<C::W, C::SW>(a.src[0], e) : 0.0f;
+#pragma unroll
+        for (int r = 1; r < C::RB; ++r) {
+            if (rank_used<C>(a, r)) {
+                acc = acc + (rank_active<C>(a, r) ? wire_one<C::W, C::SW>(a.src[r], e) : 0.0f);
+                if constexpr (C::DN) {
+                    float y = 0.0f;
+                    wire_pair<C::W>(acc, y);
+                }
+            }
+        }
+        if constexpr (C::RES) {
+            const size_t ri = res_index(a, e);
+            if constexpr (C::DN) {
+                acc = acc + wire_one<C::W, true>(a.res, ri);
+                float y = 0.0f;
+                wire_pair<C::W>(acc, y);
+            } else {
+                acc = acc + static_cast<const float *>(a.res)[ri];
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < C::RB; ++d) {
+            if (d < a.n_dst) {
+                if constexpr (C::DN) {
+                    static_cast<uint16_t *>(a.dst[d])[e] = static_cast<uint16_t>(round_pack<C::W>(acc, 0.0f));
+                } else {
+                    static_cast<float *>(a.dst[d])[e] = acc;
+                }
+            }
+        }
+    }
+}
+
+// The element range [off, off + len) of this workgroup's gridDim.y index.
+// Both forms only read launch arguments at fixed offsets (the slice form
+// indexes with blockIdx.y, which is known at wave start), so a wave fetches
+// everything it needs in one batch of scalar loads.
+template <bool SLICED>
+__device__ __forceinline__ void range_of(const KernelArgs &a, size_t &off, unsigned &len) {
+    const unsigned y = blockIdx.y;
+    if constexpr (SLICED) {
+        off = a.slice_start[y];
+        len = a.slice_len[y];
+    } else {
+        const unsigned start = y * a.chunk_elems;
+        const unsigned left = a.n - start;
+        off = start;
+        len = left < a.chunk_elems ? left : a.chunk_elems;
+    }
+}
+
+// Whole wave tiles after the batched part, then the element remainder on
+// wave 0 of workgroup 0 of the range.
+template <class C, int U, bool NT, bool ST>
+__device__ __forceinline__ void reduce_rest(const KernelArgs &a, size_t off, unsigned len, unsigned done,
+                                            unsigned gw, unsigned nw, int lane) {
+    if constexpr (U > 1) {
+        const unsigned n_one = (len - done) / kWaveTile;
+        for (unsigned t = gw; t < n_one; t += nw) {
+            reduce_tiles<C, 1, NT, ST>(a, off + done + (size_t)t * kWaveTile, lane);
+        }
+    }
+    const unsigned vec_end = (len / kWaveTile) * kWaveTile;
+    if (vec_end < len && gw == 0) {
+        reduce_scalar<C>(a, off + vec_end, off + len, lane);
+    }
+}
+
+// Walk the wave tiles of this workgroup's range: batches of U tiles strided
+// over the `a.waves` waves of the range, then the remainder.  BLOCK is the
+// workgroup size the kernel is always launched with (no read of blockDim).
+template <class C, int U, bool NT, bool ST, int BLOCK, bool SLICED>
+__device__ __forceinline__ void reduce_range(const KernelArgs &a) {
+    constexpr unsigned wpb = BLOCK / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned gw = blockIdx.x * wpb + threadIdx.x / kWave;
+    const unsigned nw = a.waves;
+    size_t off;
+    unsigned len;
+    range_of<SLICED>(a, off, len);
+
+    constexpr unsigned big = kWaveTile * U;
+    const unsigned n_big = len / big;
+    for (unsigned t = gw; t < n_big; t += nw) {
+        reduce_tiles<C, U, NT, ST>(a, off + (size_t)t * big, lane);
+    }
+    reduce_rest<C, U, NT, ST>(a, off, len, n_big * big, gw, nw, lane);
+}
+
+constexpr int kSingleShotBlock = 64;
+constexpr int kStreamBlock = 256;
+constexpr int kLdsBlock = 64;
+
+// Streaming-kernel tuning (compile-time; measured on MI355X):
+//   MPP_STREAM_LOADS  target dwordx4 loads per lane per batch (R x U x K)
+//   MPP_STREAM_MAXU   cap on tiles per batch
+//   MPP_STREAM_NT     1: non-temporal loads (streaming, no reuse); the store
+//                     policy is a launch argument
+//   MPP_STREAM_WG_PER_CU  0: one-shot grid (one batch per wave, the hardware
+//                     back-fills CUs as waves retire); k > 0: persistent grid
+//                     of k workgroups per CU
+#ifndef MPP_STREAM_LOADS
+#define MPP_STREAM_LOADS 8
+#endif
+#ifndef MPP_STREAM_MAXU
+#define MPP_STREAM_MAXU 4
+#endif
+#ifndef MPP_STREAM_NT
+#define MPP_STREAM_NT 1
+#endif
+#ifndef MPP_STREAM_WG_PER_CU
+#define MPP_STREAM_WG_PER_CU 0u
+#endif
+
+// Tiles per batch of the streaming kernel: about MPP_STREAM_LOADS dwordx4
+// loads per lane (R x U x loads-per-tile), at least 1 and at most MAXU tiles.
+constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
+    const int per_tile = (src_is_wire ? 1 : 2) * rank_bucket;
+    const int u = MPP_STREAM_LOADS / per_tile;
+    return u < 1 ? 1 : (u > MPP_STREAM_MAXU ? MPP_STREAM_MAXU : u);
+}
+
+template <class C, bool ST, bool SLICED>
+__device__ __forceinline__ void stream_reg(const KernelArgs &a) {
+    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, kStreamBlock, SLICED>(a);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged streaming kernel (one wave per workgroup).  Each wave owns two
+// LDS stages of R x U x K blocks of 1 KiB.  global_load_lds_dwordx4 writes a
+// lane's 16 B straight into the stage (no VGPRs held while the load is in
+// flight); while the wave folds and stores the batch in one stage, the loads
+// of its next batch stream into the other.  A lane only ever reads back the
+// 16 B it loaded itself, so the stages need no barrier, only the wait on the
+// wave's own vector-memory counter.  (No residual form: calls with a residual
+// use the register-staged kernel.)
+// ---------------------------------------------------------------------------
+#ifndef MPP_LDS_U
+#define MPP_LDS_U 1
+#endif
+#ifndef MPP_LDS_WG_PER_CU
+#define MPP_LDS_WG_PER_CU 32u
+#endif
+
+// Tiles per stage: MPP_LDS_U, reduced so one stage is at most 32 loads per
+// lane (the stage wait uses the 6-bit vector-memory counter).
+constexpr int lds_batch(bool src_is_wire, int rank_bucket) {
+    const int per_tile = (src_is_wire ? 1 : 2) * rank_bucket;
+    const int cap = 32 / per_tile;
+    const int u = MPP_LDS_U;
+    return u < 1 ? 1 : (u > cap ? (cap < 1 ? 1 : cap) : u);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <class C, int U>
+__device__ __forceinline__ void lds_issue(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+    constexpr int K = C::kSrcRaw;
+#pragma unroll
+    for (int r = 0; r < C::RB; ++r) {
+        if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const size_t e = C::SW ? t + u * kWaveTile + 8 * lane : t + u * kWaveTile + 256 * j + 4 * lane;
+                    const char *g = static_cast<const char *>(a.src[r]) + e * (C::SW ? 2 : 4);
+                    __builtin_amdgcn_global_load_lds(g, (lds_void *)(&stage[(r * U + u) * K + j][0]),
+                                                     16, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The loads of a stage are the oldest `L + (later loads)` in flight when the
+// next stage's L loads have just been issued: vector-memory loads retire in
+// order, so vmcnt(L) means every load of the older stage has landed in LDS.
+// L = R x U x K is only known at run time, hence the table of immediates.
+template <int MaxL>
+__device__ __forceinline__ void wait_stage(int L) {
+    if constexpr (MaxL >= 0) {
+        if (L == MaxL) {
+            wait_vm<MaxL>();
+            return;
+        }
+        wait_stage<MaxL - 1>(L);
+    } else {
+        wait_vm<0>();
+    }
+}
+
+// 16 B read of LDS at byte address `addr`, completed before it returns.  The
+// read is opaque to the compiler on purpose: its own wait insertion would
+// otherwise drain every outstanding LDS load (both stages) before any read.
+__device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+template <class C, int U, bool ST>
+__device__ __forceinline__ void lds_consume(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+    static_assert(!C::RES, "the LDS-staged kernel has no residual form");
+    constexpr int K = C::kSrcRaw;
+    const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void *)(&stage[0][lane])));
+    Batch<C, U> b;
+#pragma unroll
+    for (int r = 0; r < C::RB; ++r) {
+        if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < K; ++j) b.src[r][u][j] = lds_read16(base + ((r * U + u) * K + j) * kWave * 16);
+        }
+    }
+    fold_store<C, U, ST>(a, t, lane, b);
+}
+
+template <class C, bool ST, bool SLICED>
+__device__ __forceinline__ void stream_lds_as(const KernelArgs &a, u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
+    constexpr int U = lds_batch(C::SW, C::RB);
+    const int lane = threadIdx.x;
+    const unsigned gw = blockIdx.x;
+    const unsigned nw = a.waves;
+    size_t off;
+    unsigned len;
+    range_of<SLICED>(a, off, len);
+    constexpr unsigned big = kWaveTile * U;
+    const unsigned n_big = len / big;
+
+    // loads per stage (vector-memory instructions): active ranks x U x K
+    const int RU = a.R < C::RB ? a.R : C::RB;
+    const unsigned ranks_mask = RU >= 32 ? ~0u : ((1u << RU) - 1u);
+    const int L = __builtin_popcount(a.active & ranks_mask) * U * C::kSrcRaw;
+    constexpr int kMaxL = C::RB * U * C::kSrcRaw;
+
+    unsigned t = gw;
+    if (t < n_big) lds_issue<C, U>(a, off + (size_t)t * big, lane, stage0);
+    while (t < n_big) {
+        const unsigned t1 = t + nw;
+        if (t1 < n_big) {
+            lds_issue<C, U>(a, off + (size_t)t1 * big, lane, stage1);
+            wait_stage<kMaxL>(L);
+        } else {
+            wait_vm<0>();
+        }
+        lds_consume<C, U, ST>(a, off + (size_t)t * big, lane, stage0);
+        if (t1 >= n_big) break;
+        const unsigned t2 = t1 + nw;
+        if (t2 < n_big) {
+            lds_issue<C, U>(a, off + (size_t)t2 * big, lane, stage0);
+            wait_stage<kMaxL>(L);
+        } else {
+            wait_vm<0>();
+        }
+        lds_consume<C, U, ST>(a, off + (size_t)t1 * big, lane, stage1);
+        t = t2;
+    }
+    reduce_rest<C, U, true, ST>(a, off, len, n_big * big, gw, nw, lane);
+}
+
+template <class C, bool ST, bool SLICED>
+__device__ __forceinline__ void stream_lds(const KernelArgs &a) {
+    constexpr int NB = C::RB * lds_batch(C::SW, C::RB) * C::kSrcRaw;   // 1 KiB blocks per stage
+    __shared__ u32x4 stage0[NB][kWave];
+    __shared__ u32x4 stage1[NB][kWave];
+    stream_lds_as<C, ST, SLICED>(a, stage0, stage1);
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.  Single-shot: one wave tile per wave.  Streaming (register-staged
+// or LDS-staged): ST = non-temporal stores, SLICED = the per-rank slice
+// ranges of the broadcast schedule.
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(KernelArgs a) {
+    reduce_range<C, 1, false, false, kSingleShotBlock, false>(a);
+}
+
+#define MPP_STREAM_REG(NAME, ST, SLICED)                                   \
+    template <class C>                                                   \
+    __global__ __launch_bounds__(kStreamBlock) void NAME(KernelArgs a) { \
+        stream_reg<C, ST, SLICED>(a);                                    \
+    }
+MPP_STREAM_REG(k_stream_reg, false, false)
+MPP_STREAM_REG(k_stream_reg_nts, true, false)
+MPP_STREAM_REG(k_stream_reg_sl, false, true)
+MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
+#undef MPP_STREAM_REG
+
+#define MPP_STREAM_LDS(NAME, ST, SLICED)                                \
+    template <class C>                                                \
+    __global__ __launch_bounds__(kLdsBlock) void NAME(KernelArgs a) { \
+        stream_lds<C, ST, SLICED>(a);                                 \
+    }
+MPP_STREAM_LDS(k_stream_lds, false, false)
+MPP_STREAM_LDS(k_stream_lds_nts, true, false)
+MPP_STREAM_LDS(k_stream_lds_sl, false, true)
+MPP_STREAM_LDS(k_stream_lds_nts_sl, true, true)
+#undef MPP_STREAM_LDS
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Kernel tables.  Combination index (element types):
+//   0 f32 wire, f32 src       1 bf16 wire, f32 src     2 f16 wire, f32 src
+//   3 bf16 wire, bf16 src     4 f16 wire, f16 src
+//   5 bf16 src / wire / dst   6 f16 src / wire / dst
+// Rank bucket index: 0 -> R <= 2, 1 -> <= 4, 2 -> <= 8, 3 -> <= 16.
+// ---------------------------------------------------------------------------
+constexpr int kCombos = 7;
+constexpr int kBuckets = 4;
+
+#define MPP_ROW(KERNEL, W, SW, DN, M, RES)                                                   \
+    {reinterpret_cast<const void *>(&KERNEL<Cfg<W, SW, DN, 2, M, RES>>),                   \
+     reinterpret_cast<const void *>(&KERNEL<Cfg<W, SW, DN, 4, M, RES>>),                   \
+     reinterpret_cast<const void *>(&KERNEL<Cfg<W, SW, DN, 8, M, RES>>),                   \
+     reinterpret_cast<const void *>(&KERNEL<Cfg<W, SW, DN, 16, M, RES>>)}
+
+#define MPP_TABLE(KERNEL, M, RES)                                                            \
+    {MPP_ROW(KERNEL, AR_F32, false, false, M, RES), MPP_ROW(KERNEL, AR_BF16, false, false, M, RES), \
+     MPP_ROW(KERNEL, AR_F16, false, false, M, RES), MPP_ROW(KERNEL, AR_BF16, true, false, M, RES),  \
+     MPP_ROW(KERNEL, AR_F16, true, false, M, RES), MPP_ROW(KERNEL, AR_BF16, true, true, M, RES),    \
+     MPP_ROW(KERNEL, AR_F16, true, true, M, RES)}
+
+// Defined in the ar_k_*.hip files (one table group per file, so the files
+// compile in parallel).  Indices of the streaming tables: [store_nt][sliced]
+// [combination][rank bucket]; the name says residual (Res) and masked (M)
+// instances.  The single-shot table is [residual][masked][combination]
+// [rank bucket].
+typedef const void *const StreamTable[2][2][kCombos][kBuckets];
+extern const void *const kSingleShot[2][2][kCombos][kBuckets];
+extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM;
+
+#define MPP_STREAM_TABLE(FAMILY, M, RES)                                                         \
+    {{MPP_TABLE(k_stream_##FAMILY, M, RES), MPP_TABLE(k_stream_##FAMILY##_sl, M, RES)},          \
+     {MPP_TABLE(k_stream_##FAMILY##_nts, M, RES), MPP_TABLE(k_stream_##FAMILY##_nts_sl, M, RES)}}
+
+}  // namespace mpp

@@ -1,5 +1,6 @@
 // ar_internal.h -- interface between the host runtime (ar_api.cpp) and the
-// gfx950 kernels (ar_kernels.hip).  Not installed; not part of the C ABI.
+// gfx950 kernels (ar_device.h, ar_k_*.hip, ar_launch.hip).  Not installed; not
+// part of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,8 +34,12 @@ struct KernelArgs {
     int         store_nt;   // 1: non-temporal stores, 0: ordinary (cached) stores;
                             // selects the kernel instance, not read on the GPU
     unsigned    active;     // bit r: rank r has a partial; an inactive rank is +0.0
+    unsigned    res_len;    // residual: 0 = element-wise (index = launch element),
+                            // else the broadcast row's length (a multiple of 8)
+    unsigned    res_phase;  // row form: column of launch element 0 in the row
+    const void *res;        // residual in the destination type, or nullptr
     const void *src[AR_MAX_RANKS];
-    float      *dst[AR_MAX_RANKS];
+    void       *dst[AR_MAX_RANKS];   // binary32, or 16-bit for a narrow destination
     uint64_t    slice_start[AR_MAX_RANKS];
     unsigned    slice_len[AR_MAX_RANKS];
 };
@@ -56,18 +61,27 @@ struct LaunchShape {
     unsigned lds_bytes;   // dynamic LDS per workgroup
 };
 
+// Element types of a launch: wire type (ar_dtype), 16-bit sources, and a
+// narrow destination (destination type == wire type; implies 16-bit sources).
+struct Types {
+    int wire;
+    bool src_is_wire;
+    bool dst_narrow;
+};
+
 // Launch one kernel of `family` for the given element types on `stream`.
-// `wire` is an ar_dtype; `src_is_wire` selects 16-bit sources; `sliced`
-// selects the slice-range instance.  The caller has validated every argument
-// and sized the shape with plan_shape(); launch() fills args.waves.
-hipError_t launch(Family family, int wire, bool src_is_wire, bool sliced, KernelArgs args,
-                  const LaunchShape &shape, hipStream_t stream);
+// `sliced` selects the slice-range instance; a non-null args.res selects the
+// residual instance (register-staged or single-shot families only).  The
+// caller has validated every argument and sized the shape with plan_shape();
+// launch() fills args.waves.
+hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs args, const LaunchShape &shape,
+                  hipStream_t stream);
 
 // Pick a launch shape for `family` covering `max_slice_len` elements per
 // slice.  `cu_count` is the device's compute-unit count; `grid_override`
 // (> 0) fixes the workgroups per slice.
-LaunchShape plan_shape(Family family, int wire, bool src_is_wire, int R, unsigned max_slice_len,
-                       unsigned n_slices, int cu_count, int grid_override);
+LaunchShape plan_shape(Family family, bool src_is_wire, int R, unsigned max_slice_len, unsigned n_slices,
+                       int cu_count, int grid_override);
 
 // Elements processed per wave per loop iteration (a multiple of kWaveTile).
 unsigned stream_tile_elems(Family family, bool src_is_wire, int R);

@@ -1,0 +1,104 @@
+// ar_launch.hip -- launch shapes and kernel selection for the tables that
+// the ar_k_*.hip files define.
+#include "ar_device.h"
+
+namespace mpp {
+namespace {
+
+int combo_index(const Types &t) {
+    if (t.dst_narrow) return t.wire == AR_BF16 ? 5 : 6;
+    if (t.wire == AR_F32) return 0;
+    if (!t.src_is_wire) return t.wire == AR_BF16 ? 1 : 2;
+    return t.wire == AR_BF16 ? 3 : 4;
+}
+
+int bucket_index(int R) {
+    if (R <= 2) return 0;
+    if (R <= 4) return 1;
+    if (R <= 8) return 2;
+    return 3;
+}
+
+int bucket_ranks(int R) {
+    static const int kB[4] = {2, 4, 8, 16};
+    return kB[bucket_index(R)];
+}
+
+unsigned batch_tiles(Family family, bool src_is_wire, int R) {
+    if (family == Family::SingleShot) return 1;
+    if (family == Family::StreamLds) return static_cast<unsigned>(lds_batch(src_is_wire, bucket_ranks(R)));
+    return static_cast<unsigned>(stream_batch(src_is_wire, bucket_ranks(R)));
+}
+
+}  // namespace
+
+unsigned stream_tile_elems(Family family, bool src_is_wire, int R) {
+    return kWaveTile * batch_tiles(family, src_is_wire, R);
+}
+
+LaunchShape plan_shape(Family family, bool src_is_wire, int R, unsigned max_slice_len, unsigned n_slices,
+                       int cu_count, int grid_override) {
+    LaunchShape s{};
+    s.grid_y = n_slices;
+    s.lds_bytes = 0;
+    if (family == Family::SingleShot) {
+        // One wave per tile, 64-thread workgroups: a decode vector spreads over
+        // as many CUs as it has tiles, and no workgroup waits on a sibling.
+        s.block = kSingleShotBlock;
+        const unsigned tiles = (max_slice_len + kWaveTile - 1) / kWaveTile;
+        unsigned g = tiles == 0 ? 1 : tiles;
+        const unsigned cap = static_cast<unsigned>(cu_count) * 16u;
+        if (g > cap) g = cap;
+        s.grid_x = grid_override > 0 ? static_cast<unsigned>(grid_override) : g;
+        return s;
+    }
+    s.block = family == Family::StreamLds ? kLdsBlock : kStreamBlock;
+    const unsigned wpb = s.block / kWave;
+    const unsigned per_wave = stream_tile_elems(family, src_is_wire, R);
+    const unsigned batches = (max_slice_len + per_wave - 1) / per_wave;
+    unsigned g = (batches + wpb - 1) / wpb;
+    if (g == 0) g = 1;
+    // optional persistent-grid cap (k workgroups per CU, shared by the ranges
+    // of the launch); 0 keeps the one-shot grid
+    const unsigned per_cu = family == Family::StreamLds ? MPP_LDS_WG_PER_CU : MPP_STREAM_WG_PER_CU;
+    unsigned cap = per_cu == 0 ? 65535u : static_cast<unsigned>(cu_count) * per_cu / (n_slices ? n_slices : 1u);
+    if (cap < 1) cap = 1;
+    if (cap > 65535u) cap = 65535u;
+    if (g > cap) g = cap;
+    s.grid_x = grid_override > 0 ? static_cast<unsigned>(grid_override) : g;
+    return s;
+}
+
+hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, const LaunchShape &shape,
+                  hipStream_t stream) {
+    if (types.dst_narrow && (!types.src_is_wire || types.wire == AR_F32)) return hipErrorInvalidValue;
+    const int c = combo_index(types);
+    const int b = bucket_index(a.R);
+    const int nt = a.store_nt ? 1 : 0;
+    const int sl = sliced ? 1 : 0;
+    const int res = a.res != nullptr ? 1 : 0;
+    const unsigned full = a.R >= 32 ? ~0u : ((1u << a.R) - 1u);
+    const int m = (a.active & full) == full ? 0 : 1;   // some rank inactive
+    const void *fn = nullptr;
+    switch (family) {
+    case Family::SingleShot:
+        if (sliced) return hipErrorNotSupported;
+        fn = kSingleShot[res][m][c][b];
+        break;
+    case Family::StreamReg:
+        fn = res ? (m ? kStreamRegResM : kStreamRegRes)[nt][sl][c][b] : (m ? kStreamRegM : kStreamReg)[nt][sl][c][b];
+        break;
+    case Family::StreamLds:
+        if (res) return hipErrorNotSupported;
+        fn = (m ? kStreamLdsM : kStreamLds)[nt][sl][c][b];
+        break;
+    default: return hipErrorNotSupported;
+    }
+    if (shape.block % kWave != 0) return hipErrorInvalidValue;
+    a.waves = shape.grid_x * (shape.block / kWave);
+    void *kargs[] = {&a};
+    return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1), kargs,
+                           shape.lds_bytes, stream);
+}
+
+}  // namespace mpp

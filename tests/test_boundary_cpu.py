@@ -23,7 +23,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ar.load_library()
     names = declared_functions()
-    assert {"ar_init", "ar_reduce", "ar_free", "ar_status_str", "ar_plan_query"} <= set(names)
+    assert {"ar_init", "ar_reduce", "ar_reduce_add", "ar_free", "ar_status_str", "ar_plan_query",
+            "ar_plan_query_add"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in ar.h but not exported"
 
@@ -45,7 +46,7 @@ def test_status_strings():
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 5 * 4 + 4   # padded to 8
-    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 4 * 4
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 4 * 4 + 2 * 4
 
 
 def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
@@ -65,10 +66,12 @@ def test_rank_count_bounds():
 def test_type_checks():
     assert q(64, wire=7)[0] == ar.AR_ERR_INVALID
     assert q(64, dst_type=9)[0] == ar.AR_ERR_INVALID
-    # a wire wider than the destination is invalid, a narrow destination unsupported
+    # a wire wider than the destination is invalid; a narrow destination needs its own wire type
     assert q(64, dst_type=ar.AR_F16, wire=ar.AR_F32)[0] == ar.AR_ERR_INVALID
-    assert q(64, dst_type=ar.AR_F16, wire=ar.AR_F16)[0] == ar.AR_ERR_UNSUPPORTED
-    assert q(64, dst_type=ar.AR_BF16, wire=ar.AR_BF16)[0] == ar.AR_ERR_UNSUPPORTED
+    assert q(64, dst_type=ar.AR_F16, wire=ar.AR_BF16)[0] == ar.AR_ERR_UNSUPPORTED
+    assert q(64, dst_type=ar.AR_BF16, wire=ar.AR_F16)[0] == ar.AR_ERR_UNSUPPORTED
+    assert q(64, dst_type=ar.AR_F16, wire=ar.AR_F16)[0] == ar.AR_OK
+    assert q(64, dst_type=ar.AR_BF16, wire=ar.AR_BF16)[0] == ar.AR_OK
 
 
 def test_mode_and_flag_checks():
@@ -228,3 +231,73 @@ def test_inactive_ranks_flag():
     assert p.active_mask == 0b11
     # a NULL destination stays invalid
     assert q(n, dsts=[0], srcs=srcs, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL)[0] == ar.AR_ERR_INVALID
+
+
+def test_narrow_destination_plan():
+    n = 2048 * 4096
+    for t in (ar.AR_F16, ar.AR_BF16):
+        # sources hold the destination type with or without AR_SRC_WIRE
+        for flags in (0, ar.AR_SRC_WIRE):
+            rc, p = q(n, mode=ar.AR_MODE_CHUNKED | flags, wire=t, dst_type=t)
+            assert rc == ar.AR_OK
+            assert p.src_bytes == 2 and p.dst_bytes == 2 and p.algo_bytes == 2 * n * 2 + n * 2
+        rc, p = q(n, R=4, mode=ar.AR_MODE_RS_BCAST, wire=t, dst_type=t)
+        assert p.n_dst == 4 and p.algo_bytes == 4 * n * 2 + 4 * n * 2
+    rc, p = q(n, mode=ar.AR_MODE_CHUNKED)
+    assert p.dst_bytes == 4
+    # in place is allowed for equal widths
+    assert q(n, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_F16, dst_type=ar.AR_F16, dsts=[A[1]],
+             srcs=[A[1], A[2]])[0] == ar.AR_OK
+    # the destination is n * 2 bytes long: a destination just past the end of a source is fine
+    assert q(n, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_F16, dst_type=ar.AR_F16, dsts=[A[1] + 2 * n],
+             srcs=[A[1], A[2]])[0] == ar.AR_OK
+    assert q(n, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_F16, dst_type=ar.AR_F16, dsts=[A[1] + 2 * n - 16],
+             srcs=[A[1], A[2]])[0] == ar.AR_ERR_INVALID
+
+
+def qa(n, res, res_len, R=2, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None,
+       srcs=None, config=None):
+    srcs = A[1:1 + R] if srcs is None else srcs
+    dsts = [A[20 + d] for d in range(R)] if dsts is None else dsts
+    return ar.ar_plan_query_add(dsts, srcs, n, dst_type, wire, mode, res, res_len, False, config,
+                                R=len(srcs))
+
+
+def test_residual_rules():
+    n = 2048 * 4096
+    rc, p = qa(n, A[35], n)
+    assert rc == ar.AR_OK and p.residual_kind == 1 and p.algo_bytes == 2 * n * 4 + n * 4 + n * 4
+    rc, p = qa(n, A[35], 4096)
+    assert rc == ar.AR_OK and p.residual_kind == 2 and p.algo_bytes == 2 * n * 4 + n * 4 + 4096 * 4
+    # NULL residual, zero length, a length that does not divide n, or longer than n
+    assert qa(n, 0, n)[0] == ar.AR_ERR_INVALID
+    assert qa(n, A[35], 0)[0] == ar.AR_ERR_INVALID
+    assert qa(n, A[35], 4095)[0] == ar.AR_ERR_INVALID
+    assert qa(n, A[35], 2 * n)[0] == ar.AR_ERR_INVALID
+    # a broadcast row must be a multiple of 8 elements
+    assert qa(4 * 12, A[35], 12)[0] == ar.AR_ERR_UNSUPPORTED
+    assert qa(4 * 16, A[35], 16)[0] == ar.AR_OK
+    # misaligned residual
+    assert qa(n, A[35] + 8, n)[0] == ar.AR_ERR_INVALID
+    # element-wise residual may be the destination itself (x += reduce); a row may not
+    assert qa(n, A[20], n)[0] == ar.AR_OK
+    assert qa(n, A[20] + 16, n)[0] == ar.AR_ERR_INVALID
+    assert qa(n, A[20], 4096)[0] == ar.AR_ERR_INVALID
+    # and it may overlap the sources (read only)
+    assert qa(n, A[1], n)[0] == ar.AR_OK
+    # a residual selects the register-staged kernel
+    rc, p = qa(n, A[35], n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)
+    assert p.stream_kernel == 1
+    rc, p = qa(n, A[35], n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 2})
+    assert p.stream_kernel == 1
+    # narrow destination: the residual has the destination type
+    rc, p = qa(n, A[35], n, wire=ar.AR_F16, dst_type=ar.AR_F16)
+    assert rc == ar.AR_OK and p.algo_bytes == 2 * n * 2 + n * 2 + n * 2
+    # n = 0 is a no-op
+    assert qa(0, A[35], 0)[0] == ar.AR_OK
+    # a NULL context is rejected by ar_reduce_add before anything else
+    lib = ar.load_library()
+    srcs = (ctypes.c_void_p * 2)(*A[1:3])
+    dsts = (ctypes.c_void_p * 1)(A[30])
+    assert lib.ar_reduce_add(None, dsts, srcs, 2, 64, ar.AR_F32, ar.AR_BF16, 0, A[35], 64, None) == \
+        ar.AR_ERR_INVALID

@@ -374,8 +374,8 @@ def test_error_paths(ctx):
     # misaligned source
     assert ar.ar_reduce(ctx, [out], [dev[0].data_ptr() + 4, dev[1]], n - 4, ar.AR_F32, ar.AR_BF16,
                         ar.AR_MODE_CHUNKED, check=False) == E
-    # narrow destination type
-    assert ar.ar_reduce(ctx, [out], dev, n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_CHUNKED,
+    # a narrow destination with a different wire type
+    assert ar.ar_reduce(ctx, [out], dev, n, ar.AR_F16, ar.AR_BF16, ar.AR_MODE_CHUNKED,
                         check=False) == ar.AR_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     # the context still works afterwards
