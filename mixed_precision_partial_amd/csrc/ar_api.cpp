@@ -255,10 +255,14 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // host-staged sources: copy-engine pipeline (1) or the kernel reading
         // the pinned buffers over PCIe directly (2)
         plan->host_direct = resolved == AR_MODE_HOST_STAGED && cfg.host_path == 2;
-        // streaming kernel family: explicit choice, else measured on MI355X --
-        // the LDS-staged double buffer wins for two 16-bit sources (as many
-        // bytes written as read, short tiles), the register kernel elsewhere
-        // (the LDS-staged kernel has no residual form)
+        // streaming kernel family: explicit choice, else measured on MI355X
+        // with inputs that are not in any cache -- the LDS-staged kernel for
+        // the broadcast schedule (R loads per lane staged in LDS instead of
+        // VGPRs while R stores stream out: 88 against 95 us at R = 4, fp32
+        // sources) and for two 16-bit sources (short tiles, as many bytes
+        // written as read), the register kernel elsewhere (up to 16 % faster
+        // for fp32 sources with few destinations).  The LDS-staged kernel has
+        // no residual form.
         if (resolved == AR_MODE_SINGLE_SHOT) {
             plan->stream_kernel = 0;
         } else if (res_kind != 0) {
@@ -266,7 +270,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         } else if (cfg.stream_kernel != 0) {
             plan->stream_kernel = cfg.stream_kernel;
         } else {
-            plan->stream_kernel = (src_wire && !dst_narrow && R == 2) ? 2 : 1;
+            plan->stream_kernel = (resolved == AR_MODE_RS_BCAST || (src_wire && R == 2)) ? 2 : 1;
         }
     }
     return AR_OK;

@@ -479,8 +479,19 @@ __device__ __forceinline__ void reduce_range(const KernelArgs &a) {
 }
 
 constexpr int kSingleShotBlock = 64;
-constexpr int kStreamBlock = 256;
 constexpr int kLdsBlock = 64;
+
+// Workgroup size of the register-staged streaming kernel per rank bucket
+// (measured on MI355X): 64-thread workgroups for the 8-rank bucket, whose
+// batches hold 16 loads per lane and so limit how many waves fit on a CU --
+// small workgroups pack the CUs more evenly (cold R = 8 fp32 reduce: 6.38
+// against 6.13 TB/s); 256 threads elsewhere.
+#ifndef MPP_STREAM_BLOCK
+#define MPP_STREAM_BLOCK 0
+#endif
+constexpr int stream_block(int rank_bucket) {
+    return MPP_STREAM_BLOCK > 0 ? MPP_STREAM_BLOCK : (rank_bucket == 8 ? 64 : 256);
+}
 
 // Streaming-kernel tuning (compile-time; measured on MI355X):
 //   MPP_STREAM_LOADS  target dwordx4 loads per lane per batch (R x U x K)
@@ -513,7 +524,7 @@ constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
 
 template <class C, bool ST, bool SLICED>
 __device__ __forceinline__ void stream_reg(const KernelArgs &a) {
-    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, kStreamBlock, SLICED>(a);
+    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, stream_block(C::RB), SLICED>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -529,8 +540,17 @@ __device__ __forceinline__ void stream_reg(const KernelArgs &a) {
 #ifndef MPP_LDS_U
 #define MPP_LDS_U 1
 #endif
+// Grid of the LDS-staged kernel: 0 = one-shot (one batch per wave, the
+// hardware back-fills CUs as waves retire; measured best on MI355X), k > 0 =
+// persistent grid of k workgroups per CU that double-buffers its batches.
 #ifndef MPP_LDS_WG_PER_CU
-#define MPP_LDS_WG_PER_CU 32u
+#define MPP_LDS_WG_PER_CU 0u
+#endif
+// Cache-policy bits of the LDS-staged loads: 2 = non-temporal (streaming
+// data read once; with cached loads the kernel only looked faster when the
+// inputs were still in the Infinity Cache), 0 = default.
+#ifndef MPP_LDS_AUX
+#define MPP_LDS_AUX 2
 #endif
 
 // Tiles per stage: MPP_LDS_U, reduced so one stage is at most 32 loads per
@@ -557,7 +577,7 @@ __device__ __forceinline__ void lds_issue(const KernelArgs &a, size_t t, int lan
                     const size_t e = C::SW ? t + u * kWaveTile + 8 * lane : t + u * kWaveTile + 256 * j + 4 * lane;
                     const char *g = static_cast<const char *>(a.src[r]) + e * (C::SW ? 2 : 4);
                     __builtin_amdgcn_global_load_lds(g, (lds_void *)(&stage[(r * U + u) * K + j][0]),
-                                                     16, 0, 0);
+                                                     16, 0, MPP_LDS_AUX);
                 }
             }
         }
@@ -678,7 +698,7 @@ __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(KernelArgs a) 
 
 #define MPP_STREAM_REG(NAME, ST, SLICED)                                   \
     template <class C>                                                   \
-    __global__ __launch_bounds__(kStreamBlock) void NAME(KernelArgs a) { \
+    __global__ __launch_bounds__(stream_block(C::RB)) void NAME(KernelArgs a) { \
         stream_reg<C, ST, SLICED>(a);                                    \
     }
 MPP_STREAM_REG(k_stream_reg, false, false)

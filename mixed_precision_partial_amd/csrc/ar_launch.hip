@@ -52,7 +52,7 @@ LaunchShape plan_shape(Family family, bool src_is_wire, int R, unsigned max_slic
         s.grid_x = grid_override > 0 ? static_cast<unsigned>(grid_override) : g;
         return s;
     }
-    s.block = family == Family::StreamLds ? kLdsBlock : kStreamBlock;
+    s.block = family == Family::StreamLds ? kLdsBlock : static_cast<unsigned>(stream_block(bucket_ranks(R)));
     const unsigned wpb = s.block / kWave;
     const unsigned per_wave = stream_tile_elems(family, src_is_wire, R);
     const unsigned batches = (max_slice_len + per_wave - 1) / per_wave;

@@ -216,6 +216,12 @@ def test_stream_kernel_choice():
     assert q(n, R=8, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 1})[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED, config={"stream_kernel": 2})[1].stream_kernel == 2
+    # broadcast schedule: LDS-staged for any source width
+    assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST, wire=ar.AR_F16)[1].stream_kernel == 2
+    assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST | ar.AR_SRC_WIRE, wire=ar.AR_F16)[1].stream_kernel == 2
+    # two 16-bit sources into a narrow destination: LDS-staged; more ranks: register-staged
+    assert q(n, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == 2
+    assert q(n, R=3, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == 1
 
 
 def test_inactive_ranks_flag():
