@@ -385,8 +385,9 @@ def decode_latency(torch, ar, wl):
     ctx = ar.ar_init(0)
     stream = torch.cuda.current_stream()
     bi, bo = dev.data_ptr(), out.data_ptr()
-    srcs = [[bi + (c * R + r) * n * 4 for r in range(R)] for c in range(calls)]
-    dsts = [[bo + c * n * 4] for c in range(calls)]
+    # pointer arrays built once (the binding passes ready-made arrays through)
+    srcs = [ar.ptr_array([bi + (c * R + r) * n * 4 for r in range(R)]) for c in range(calls)]
+    dsts = [ar.ptr_array([bo + c * n * 4]) for c in range(calls)]
 
     def call(c):
         ar.ar_reduce(ctx, dsts[c], srcs[c], n, ar.AR_F32, w.wire, ar.AR_MODE_SINGLE_SHOT, stream=stream)

@@ -14,9 +14,11 @@ The functions carry the C names:
     ar_status_str(code)
     ar_plan_query(...), ar_plan_query_add(...)
 
-``dsts`` / ``srcs`` are sequences of torch tensors or raw integer addresses;
-``stream`` is a ``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None
-for the null stream.
+``dsts`` / ``srcs`` are sequences of torch tensors or raw integer addresses, or
+ready-made ``ptr_array(...)`` arrays (passed through unchanged, which keeps
+the per-call marshalling cost low for latency-bound callers); ``stream`` is a
+``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None for the null
+stream.
 """
 from __future__ import annotations
 
@@ -129,11 +131,18 @@ def _addr(x) -> int | None:
     raise TypeError(f"expected a tensor or an integer address, got {type(x).__name__}")
 
 
-def _ptr_array(xs):
+def ptr_array(xs):
+    """A C array of pointers (``void *[]``) for dsts / srcs; build it once and
+    reuse it across calls on the same buffers."""
     if xs is None:
         return None
+    if isinstance(xs, ctypes.Array):
+        return xs
     vals = [_addr(x) for x in xs]
     return (ctypes.c_void_p * max(1, len(vals)))(*vals)
+
+
+_ptr_array = ptr_array
 
 
 def _stream_handle(stream) -> int | None:

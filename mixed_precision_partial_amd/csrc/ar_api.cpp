@@ -295,14 +295,24 @@ struct ar_ctx {
 
 namespace {
 
+// Makes `dev` current for the scope and restores the caller's device; no
+// runtime call beyond the query when `dev` is already current (the common
+// case, and the cheap one on a latency-bound decode call).
 struct DeviceGuard {
     int prev = -1;
     bool ok = false;
+    bool switched = false;
     explicit DeviceGuard(int dev) {
-        if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok = true;
+        if (hipGetDevice(&prev) != hipSuccess) return;
+        if (prev == dev) {
+            ok = true;
+        } else if (hipSetDevice(dev) == hipSuccess) {
+            ok = true;
+            switched = true;
+        }
     }
     ~DeviceGuard() {
-        if (prev >= 0) (void)hipSetDevice(prev);
+        if (switched) (void)hipSetDevice(prev);
     }
 };
 

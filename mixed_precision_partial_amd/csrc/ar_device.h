@@ -58,7 +58,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 //   SW     sources already hold the wire type (16-bit loads)
 //   DN     narrow destination: destination type == W (16-bit stores); implies SW
 //   RB     rank bucket: the kernel handles R <= RB
-//   MASKED some rank may be inactive (bit r of KernelArgs::active clear)
+//   MASKED some rank may be inactive (bit r of LaunchArgs::active clear)
 //   RES    a residual is added after the fold
 template <int W_, bool SW_, bool DN_, int RB_, bool MASKED_, bool RES_>
 struct Cfg {
@@ -194,7 +194,8 @@ __device__ __forceinline__ void tile_values(const u32x4 (&raw)[C::kSrcRaw], floa
 // Index of launch element e in the residual: e itself (element-wise), or its
 // column in the broadcast row.  res_len is a multiple of 8, so the 4 or 8
 // consecutive elements of one lane part never straddle a row boundary.
-__device__ __forceinline__ size_t res_index(const KernelArgs &a, size_t e) {
+template <class A>
+__device__ __forceinline__ size_t res_index(const A &a, size_t e) {
     if (a.res_len == 0) return e;
     return (static_cast<unsigned>(e) + a.res_phase) % a.res_len;
 }
@@ -204,7 +205,7 @@ __device__ __forceinline__ size_t res_index(const KernelArgs &a, size_t e) {
 // Both forms issue the same number of loads, so the branch does not change
 // how many loads are outstanding after it.
 template <class C, bool NT>
-__device__ __forceinline__ void res_load(const KernelArgs &a, size_t t, int lane, u32x4 (&raw)[C::kResRaw]) {
+__device__ __forceinline__ void res_load(const LaunchArgs<C::RB> &a, size_t t, int lane, u32x4 (&raw)[C::kResRaw]) {
     if (a.res_len == 0) {
 #pragma unroll
         for (int j = 0; j < C::kResRaw; ++j) {
@@ -269,7 +270,7 @@ __device__ __forceinline__ void tile_store(void *dst, size_t t, int lane, const 
 // branches around loads make the compiler drain each rank's loads before
 // issuing the next, so the common case must not carry them.
 template <class C>
-__device__ __forceinline__ bool rank_active(const KernelArgs &a, int r) {
+__device__ __forceinline__ bool rank_active(const LaunchArgs<C::RB> &a, int r) {
     if constexpr (C::MASKED) {
         return (a.active >> r) & 1u;
     } else {
@@ -278,7 +279,7 @@ __device__ __forceinline__ bool rank_active(const KernelArgs &a, int r) {
 }
 
 template <class C>
-__device__ __forceinline__ bool rank_used(const KernelArgs &a, int r) {
+__device__ __forceinline__ bool rank_used(const LaunchArgs<C::RB> &a, int r) {
     return r < 2 || r < a.R;
 }
 
@@ -295,7 +296,7 @@ struct Batch {
 // and stored while the later tiles' loads are still arriving.  The residual
 // loads of the batch come last.
 template <class C, int U, bool NT>
-__device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int lane, Batch<C, U> &b) {
+__device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, size_t t, int lane, Batch<C, U> &b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -317,7 +318,7 @@ __device__ __forceinline__ void load_batch(const KernelArgs &a, size_t t, int la
 // Fold one tile in rank order (one rounding to the destination type per add),
 // add the residual, and store to every destination.
 template <class C, bool ST>
-__device__ __forceinline__ void fold_store_tile(const KernelArgs &a, size_t t, int lane,
+__device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size_t t, int lane,
                                                 const u32x4 (&src)[C::RB][C::kSrcRaw], const u32x4 *res) {
     float acc[8];
     if (rank_active<C>(a, 0)) {
@@ -364,7 +365,7 @@ __device__ __forceinline__ void fold_store_tile(const KernelArgs &a, size_t t, i
 // parameter: two stores that differ only in their cache hint would be merged
 // into one by the compiler.
 template <class C, int U, bool ST>
-__device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int lane, const Batch<C, U> &b) {
+__device__ __forceinline__ void fold_store(const LaunchArgs<C::RB> &a, size_t t, int lane, const Batch<C, U> &b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         u32x4 src[C::RB][C::kSrcRaw];
@@ -377,7 +378,7 @@ __device__ __forceinline__ void fold_store(const KernelArgs &a, size_t t, int la
 }
 
 template <class C, int U, bool NT, bool ST>
-__device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int lane) {
+__device__ __forceinline__ void reduce_tiles(const LaunchArgs<C::RB> &a, size_t t, int lane) {
     Batch<C, U> b;
     load_batch<C, U, NT>(a, t, lane, b);
     fold_store<C, U, ST>(a, t, lane, b);
@@ -386,7 +387,7 @@ __device__ __forceinline__ void reduce_tiles(const KernelArgs &a, size_t t, int 
 // Elements [begin, end) of the launch, one per lane per step (end - begin is
 // below one wave tile, so this is at most 8 steps).
 template <class C>
-__device__ __forceinline__ void reduce_scalar(const KernelArgs &a, size_t begin, size_t end, int lane) {
+__device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, size_t begin, size_t end, int lane) {
     for (size_t e = begin + lane; e < end; e += kWave) {
         float acc = rank_active<C>(a, 0) ? wire_one<C::W, C::SW>(a.src[0], e) : 0.0f;
 #pragma unroll
@@ -426,8 +427,8 @@ __device__ __forceinline__ void reduce_scalar(const KernelArgs &a, size_t begin,
 // Both forms only read launch arguments at fixed offsets (the slice form
 // indexes with blockIdx.y, which is known at wave start), so a wave fetches
 // everything it needs in one batch of scalar loads.
-template <bool SLICED>
-__device__ __forceinline__ void range_of(const KernelArgs &a, size_t &off, unsigned &len) {
+template <bool SLICED, class A>
+__device__ __forceinline__ void range_of(const A &a, size_t &off, unsigned &len) {
     const unsigned y = blockIdx.y;
     if constexpr (SLICED) {
         off = a.slice_start[y];
@@ -443,7 +444,7 @@ __device__ __forceinline__ void range_of(const KernelArgs &a, size_t &off, unsig
 // Whole wave tiles after the batched part, then the element remainder on
 // wave 0 of workgroup 0 of the range.
 template <class C, int U, bool NT, bool ST>
-__device__ __forceinline__ void reduce_rest(const KernelArgs &a, size_t off, unsigned len, unsigned done,
+__device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, size_t off, unsigned len, unsigned done,
                                             unsigned gw, unsigned nw, int lane) {
     if constexpr (U > 1) {
         const unsigned n_one = (len - done) / kWaveTile;
@@ -461,7 +462,7 @@ __device__ __forceinline__ void reduce_rest(const KernelArgs &a, size_t off, uns
 // over the `a.waves` waves of the range, then the remainder.  BLOCK is the
 // workgroup size the kernel is always launched with (no read of blockDim).
 template <class C, int U, bool NT, bool ST, int BLOCK, bool SLICED>
-__device__ __forceinline__ void reduce_range(const KernelArgs &a) {
+__device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a) {
     constexpr unsigned wpb = BLOCK / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const unsigned gw = blockIdx.x * wpb + threadIdx.x / kWave;
@@ -523,7 +524,7 @@ constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
 }
 
 template <class C, bool ST, bool SLICED>
-__device__ __forceinline__ void stream_reg(const KernelArgs &a) {
+__device__ __forceinline__ void stream_reg(const LaunchArgs<C::RB> &a) {
     reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, stream_block(C::RB), SLICED>(a);
 }
 
@@ -565,7 +566,7 @@ constexpr int lds_batch(bool src_is_wire, int rank_bucket) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <class C, int U>
-__device__ __forceinline__ void lds_issue(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+__device__ __forceinline__ void lds_issue(const LaunchArgs<C::RB> &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
     constexpr int K = C::kSrcRaw;
 #pragma unroll
     for (int r = 0; r < C::RB; ++r) {
@@ -618,7 +619,7 @@ __device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
 }
 
 template <class C, int U, bool ST>
-__device__ __forceinline__ void lds_consume(const KernelArgs &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+__device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
     static_assert(!C::RES, "the LDS-staged kernel has no residual form");
     constexpr int K = C::kSrcRaw;
     const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void *)(&stage[0][lane])));
@@ -636,7 +637,7 @@ __device__ __forceinline__ void lds_consume(const KernelArgs &a, size_t t, int l
 }
 
 template <class C, bool ST, bool SLICED>
-__device__ __forceinline__ void stream_lds_as(const KernelArgs &a, u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
+__device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
     constexpr int U = lds_batch(C::SW, C::RB);
     const int lane = threadIdx.x;
     const unsigned gw = blockIdx.x;
@@ -679,7 +680,7 @@ __device__ __forceinline__ void stream_lds_as(const KernelArgs &a, u32x4 (*stage
 }
 
 template <class C, bool ST, bool SLICED>
-__device__ __forceinline__ void stream_lds(const KernelArgs &a) {
+__device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a) {
     constexpr int NB = C::RB * lds_batch(C::SW, C::RB) * C::kSrcRaw;   // 1 KiB blocks per stage
     __shared__ u32x4 stage0[NB][kWave];
     __shared__ u32x4 stage1[NB][kWave];
@@ -692,13 +693,13 @@ __device__ __forceinline__ void stream_lds(const KernelArgs &a) {
 // ranges of the broadcast schedule.
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(KernelArgs a) {
+__global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(LaunchArgs<C::RB> a) {
     reduce_range<C, 1, false, false, kSingleShotBlock, false>(a);
 }
 
 #define MPP_STREAM_REG(NAME, ST, SLICED)                                   \
     template <class C>                                                   \
-    __global__ __launch_bounds__(stream_block(C::RB)) void NAME(KernelArgs a) { \
+    __global__ __launch_bounds__(stream_block(C::RB)) void NAME(LaunchArgs<C::RB> a) { \
         stream_reg<C, ST, SLICED>(a);                                    \
     }
 MPP_STREAM_REG(k_stream_reg, false, false)
@@ -709,7 +710,7 @@ MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
 
 #define MPP_STREAM_LDS(NAME, ST, SLICED)                                \
     template <class C>                                                \
-    __global__ __launch_bounds__(kLdsBlock) void NAME(KernelArgs a) { \
+    __global__ __launch_bounds__(kLdsBlock) void NAME(LaunchArgs<C::RB> a) { \
         stream_lds<C, ST, SLICED>(a);                                 \
     }
 MPP_STREAM_LDS(k_stream_lds, false, false)

@@ -16,32 +16,42 @@ namespace mpp {
 // remainder of a range (< 512 elements) is done element by element.
 constexpr unsigned kWaveTile = 512;
 
-// Kernel arguments, passed by value (kernarg segment, ~480 B).  The launch
-// covers R sources and n_dst destinations over gridDim.y ranges, each walked
-// by the `waves` waves of gridDim.x workgroups:
+// Kernel arguments for a kernel whose rank bucket is NR, passed by value: the
+// kernarg segment of a launch holds exactly this struct, so the small buckets
+// launch with small argument blocks (the runtime's per-launch host cost grows
+// with the argument size on MI355X: about 0.8 us more for ~500 B than for a
+// few bytes, a quarter of a decode-sized call).  The launch covers R sources
+// and n_dst destinations over gridDim.y ranges, each walked by the `waves`
+// waves of gridDim.x workgroups:
 //   chunk ranges (CHUNKED, SINGLE_SHOT, host-staged chunks): range y is
 //       [y * chunk_elems, min((y + 1) * chunk_elems, n));
 //   slice ranges (RS_BCAST, a separate kernel instance): range y is
 //       [slice_start[y], slice_start[y] + slice_len[y]), gridDim.y <= R.
 // The scalars a wave needs first sit at the front so that one batch of
 // scalar loads fetches them together with the pointers.
-struct KernelArgs {
+template <int NR>
+struct LaunchArgs {
     unsigned    n;
     unsigned    chunk_elems;
     unsigned    waves;      // waves per range: gridDim.x * (block / 64)
     int         R;
     int         n_dst;
-    int         store_nt;   // 1: non-temporal stores, 0: ordinary (cached) stores;
-                            // selects the kernel instance, not read on the GPU
     unsigned    active;     // bit r: rank r has a partial; an inactive rank is +0.0
     unsigned    res_len;    // residual: 0 = element-wise (index = launch element),
                             // else the broadcast row's length (a multiple of 8)
     unsigned    res_phase;  // row form: column of launch element 0 in the row
     const void *res;        // residual in the destination type, or nullptr
-    const void *src[AR_MAX_RANKS];
-    void       *dst[AR_MAX_RANKS];   // binary32, or 16-bit for a narrow destination
-    uint64_t    slice_start[AR_MAX_RANKS];
-    unsigned    slice_len[AR_MAX_RANKS];
+    const void *src[NR];
+    void       *dst[NR];    // binary32, or 16-bit for a narrow destination
+    uint64_t    slice_start[NR];
+    unsigned    slice_len[NR];
+};
+
+// What the host fills in for any rank count; launch() copies it into the
+// LaunchArgs of the chosen kernel's bucket.
+struct KernelArgs : LaunchArgs<AR_MAX_RANKS> {
+    int store_nt;   // 1: non-temporal stores, 0: ordinary (cached) stores;
+                    // selects the kernel instance, not passed to the GPU
 };
 
 // Largest element count one launch covers (32-bit element indices inside the

@@ -30,6 +30,29 @@ unsigned batch_tiles(Family family, bool src_is_wire, int R) {
     return static_cast<unsigned>(stream_batch(src_is_wire, bucket_ranks(R)));
 }
 
+template <int NR>
+hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &shape, hipStream_t stream) {
+    LaunchArgs<NR> b;
+    b.n = a.n;
+    b.chunk_elems = a.chunk_elems;
+    b.waves = a.waves;
+    b.R = a.R;
+    b.n_dst = a.n_dst;
+    b.active = a.active;
+    b.res_len = a.res_len;
+    b.res_phase = a.res_phase;
+    b.res = a.res;
+    for (int r = 0; r < NR; ++r) {
+        b.src[r] = a.src[r];
+        b.dst[r] = a.dst[r];
+        b.slice_start[r] = a.slice_start[r];
+        b.slice_len[r] = a.slice_len[r];
+    }
+    void *kargs[] = {&b};
+    return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1), kargs,
+                           shape.lds_bytes, stream);
+}
+
 }  // namespace
 
 unsigned stream_tile_elems(Family family, bool src_is_wire, int R) {
@@ -96,9 +119,12 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
     }
     if (shape.block % kWave != 0) return hipErrorInvalidValue;
     a.waves = shape.grid_x * (shape.block / kWave);
-    void *kargs[] = {&a};
-    return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1), kargs,
-                           shape.lds_bytes, stream);
+    switch (b) {
+    case 0: return launch_as<2>(fn, a, shape, stream);
+    case 1: return launch_as<4>(fn, a, shape, stream);
+    case 2: return launch_as<8>(fn, a, shape, stream);
+    default: return launch_as<16>(fn, a, shape, stream);
+    }
 }
 
 }  // namespace mpp
