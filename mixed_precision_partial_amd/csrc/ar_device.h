@@ -193,11 +193,15 @@ __device__ __forceinline__ void tile_values(const u32x4 (&raw)[C::kSrcRaw], floa
 
 // Index of launch element e in the residual: e itself (element-wise), or its
 // column in the broadcast row.  res_len is a multiple of 8, so the 4 or 8
-// consecutive elements of one lane part never straddle a row boundary.
+// consecutive elements of one lane part never straddle a row boundary.  The
+// slice schedule indexes whole calls, which can pass 2^32 elements: those
+// positions take a 64-bit remainder, all others the cheaper 32-bit one.
 template <class A>
 __device__ __forceinline__ size_t res_index(const A &a, size_t e) {
     if (a.res_len == 0) return e;
-    return (static_cast<unsigned>(e) + a.res_phase) % a.res_len;
+    const uint64_t x = static_cast<uint64_t>(e) + a.res_phase;
+    if (x < (uint64_t(1) << 32)) return static_cast<unsigned>(x) % a.res_len;
+    return x % a.res_len;
 }
 
 // Residual loads of one tile: streaming loads for the element-wise form

@@ -1,0 +1,122 @@
+"""Maximum sizes: calls longer than one launch covers (2^30 elements) and, on
+the slice + broadcast schedule, calls past 2^32 elements, through the C ABI.
+
+The inputs are drawn on the device with torch's seeded generator; the oracle
+checks sampled outputs one by one (every launch-piece, chunk and slice
+boundary, the ragged tail and random positions), gathering the same input
+elements back to the host.  Properties that hold at any size (all
+destinations byte-identical) are checked over the whole tensors.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_partial_amd as ar
+import oracle
+from gpu_util import assert_bits_equal, log_case
+
+pytestmark = pytest.mark.gpu
+
+LAUNCH = 1 << 30   # elements one launch covers
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    c = ar.ar_init(0)
+    yield c
+    torch.cuda.synchronize()
+    ar.ar_free(c)
+
+
+def sample_indices(n: int, boundaries, seed: int) -> np.ndarray:
+    near = []
+    for b in boundaries:
+        near.extend(range(max(0, b - 9), min(n, b + 9)))
+    near.extend(range(max(0, n - 700), n))
+    rnd = np.random.default_rng(seed).integers(0, n, 20_000)
+    return np.unique(np.concatenate([np.array(near, dtype=np.int64), rnd.astype(np.int64)]))
+
+
+def gather(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
+    g = t[torch.from_numpy(idx).to(t.device)].cpu()
+    if g.dtype == torch.float32:
+        return g.numpy()
+    return g.view(torch.int16).numpy().view(np.uint16)
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_beyond_one_launch(ctx):
+    """n = 2^30 + 2^20 + 4099 fp32 partials, bf16 wire: every schedule cuts the call into
+    launch pieces; with an element-wise residual and without."""
+    n = LAUNCH + (1 << 20) + 4099
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20_001)
+    srcs = [torch.randn(n, device="cuda", generator=g) for _ in range(2)]
+    res = torch.randn(n, device="cuda", generator=g)
+    rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_F32, ar.AR_BF16,
+                                ar.AR_MODE_CHUNKED)
+    chunk_bounds = list(range(0, n, plan.chunk_elems))
+    idx = sample_indices(n, [LAUNCH, 1 << 29, 3 << 28] + chunk_bounds[:64] + chunk_bounds[-64:], 7)
+    s_host = [gather(s, idx) for s in srcs]
+    r_host = gather(res, idx)
+    want_plain = oracle.reduce(s_host, ar.AR_BF16)[0]
+    want_res = oracle.reduce(s_host, ar.AR_BF16, residual=r_host)[0]
+    out = torch.empty(n, device="cuda")
+    for mode_name, mode in (("chunked", ar.AR_MODE_CHUNKED), ("single_shot", ar.AR_MODE_SINGLE_SHOT)):
+        for with_res in (False, True):
+            what = f"n={n} {mode_name} residual={with_res}"
+            log_case(what)
+            out.fill_(float("nan"))
+            if with_res:
+                ar.ar_reduce_add(ctx, [out], srcs, n, ar.AR_F32, ar.AR_BF16, mode, res, n)
+            else:
+                ar.ar_reduce(ctx, [out], srcs, n, ar.AR_F32, ar.AR_BF16, mode)
+            torch.cuda.synchronize()
+            assert not torch.isnan(out).any().item(), f"{what}: some element left unwritten"
+            assert_bits_equal(gather(out, idx), want_res if with_res else want_plain, what)
+    del out
+    # slice + broadcast: both destinations identical over the whole tensor
+    log_case(f"n={n} rs_bcast residual")
+    dsts = [torch.empty(n, device="cuda") for _ in range(2)]
+    ar.ar_reduce_add(ctx, dsts, srcs, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_RS_BCAST, res, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dsts[0].view(torch.int32), dsts[1].view(torch.int32))
+    assert_bits_equal(gather(dsts[1], idx), want_res, "rs_bcast residual")
+    del dsts, srcs, res
+    free()
+
+
+def test_slice_broadcast_past_2_32(ctx):
+    """n = 2^32 + 3 * 8192 bf16 partials (R=2), slice + broadcast to 2 fp32 destinations,
+    with a broadcast row of 8192: element positions past 2^32 inside one launch."""
+    L = 8192
+    n = (1 << 32) + 3 * L
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20_002)
+    srcs = [torch.randn(n, device="cuda", dtype=torch.bfloat16, generator=g) for _ in range(2)]
+    row = torch.randn(L, device="cuda", generator=g)
+    fake = [k << 40 for k in range(1, 5)]   # well separated addresses: the plan only reads them
+    rc, plan = ar.ar_plan_query(fake[:2], fake[2:], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_RS_BCAST | ar.AR_SRC_WIRE)
+    assert rc == ar.AR_OK
+    bounds = [plan.slice_start[r] for r in range(2)] + [LAUNCH, 2 * LAUNCH, 3 * LAUNCH, 1 << 32]
+    bounds += [plan.slice_start[1] + LAUNCH, plan.slice_start[1] + 2 * LAUNCH]
+    idx = sample_indices(n, bounds, 8)
+    s_host = [gather(s, idx) for s in srcs]
+    r_host = row.cpu().numpy()[idx % L]
+    want = oracle.reduce(s_host, ar.AR_BF16, src_type=ar.AR_BF16, residual=r_host)[0]
+    dsts = [torch.empty(n, device="cuda") for _ in range(2)]
+    log_case(f"n={n} rs_bcast bf16 sources, row residual L={L}")
+    ar.ar_reduce_add(ctx, dsts, srcs, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_RS_BCAST | ar.AR_SRC_WIRE, row, L)
+    torch.cuda.synchronize()
+    assert torch.equal(dsts[0].view(torch.int32), dsts[1].view(torch.int32))
+    assert_bits_equal(gather(dsts[0], idx), want, "past 2^32 rs_bcast row residual")
+    del dsts, srcs
+    free()
