@@ -95,10 +95,13 @@ def test_beyond_one_launch(ctx):
 
 
 def test_slice_broadcast_past_2_32(ctx):
-    """n = 2^32 + 3 * 8192 bf16 partials (R=2), slice + broadcast to 2 fp32 destinations,
-    with a broadcast row of 8192: element positions past 2^32 inside one launch."""
-    L = 8192
-    n = (1 << 32) + 3 * L
+    """n = 8200 x 523,779 (past 2^32) bf16 partials (R=2), slice + broadcast to 2 fp32
+    destinations, with a broadcast row of 8200 elements (which does not divide 2^32, so a
+    row index taken from a position cut to 32 bits would be wrong): element positions
+    past 2^32 inside one launch."""
+    L = 8200
+    n = L * (-(-(1 << 32) // L) + 1)
+    assert n > (1 << 32) and (1 << 32) % L != 0
     g = torch.Generator(device="cuda")
     g.manual_seed(20_002)
     srcs = [torch.randn(n, device="cuda", dtype=torch.bfloat16, generator=g) for _ in range(2)]
