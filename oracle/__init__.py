@@ -17,7 +17,9 @@ Every function here follows the passages cited in ``ar_oracle.c``:
   (same page, the HAS_ADD and IS_ROW_BCAST forms of the 1-D / 2-D loops);
 * narrow destinations that accumulate in their own type (CUDA page, the
   half / nv_bfloat16 instances of the chunked kernel; Hexagon page, the f16
-  instances).
+  instances);
+* row-strided tensors and the residual row added to every row (Hexagon
+  page, allreduce_thread_dma_2d and its IS_ROW_BCAST form).
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (exhaustive conversions against torch / numpy, a double-rounding theorem for
@@ -77,6 +79,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_reduce_ex.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
                                   ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, vp, sz]
     lib.orc_reduce_ex.restype = ctypes.c_int
+    lib.orc_reduce_rows.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
+                                    ctypes.c_int, sz, sz, sz, sz, ctypes.c_int, ctypes.c_int, vp, sz]
+    lib.orc_reduce_rows.restype = ctypes.c_int
     return lib
 
 
@@ -188,6 +193,55 @@ def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
     dst_ptrs = (ctypes.c_void_p * n_dst)(*[out[d].ctypes.data for d in range(n_dst)])
     src_ptrs = (ctypes.c_void_p * R)(*[None if s is None else s.ctypes.data for s in srcs])
     rc = lib.orc_reduce_ex(dst_ptrs, n_dst, dst_type, src_ptrs, R, n, src_type, wire_type, res_ptr, res_len)
+    if rc != 0:
+        raise ValueError(f"oracle rejected arguments (rc={rc})")
+    return out
+
+
+def reduce_rows(srcs, wire_type: int, rows: int, cols: int, src_stride: int, dst_stride: int,
+                n_dst: int = 1, src_type: int | None = None, dst_type: int = F32, residual=None,
+                res_stride: int = 0, dst_init=None, lib=None) -> np.ndarray:
+    """Reference result of the reduce over row-strided tensors.
+
+    ``srcs``: R flat arrays holding ``rows`` rows of ``cols`` elements at row stride
+    ``src_stride`` (float32, or uint16 patterns of the wire type; None = inactive).
+    Destinations are flat arrays of ``(rows - 1) * dst_stride + cols`` elements, copied
+    from ``dst_init`` (default: zeros) so the bytes between rows are whatever the
+    caller had there.  ``residual``: None, or a flat array of the destination type
+    with row stride ``res_stride`` (0 = one row added to every row).
+    Returns an ``(n_dst, extent)`` array of the destination type.
+    """
+    lib = lib or load()
+    srcs = [None if s is None else np.ascontiguousarray(s) for s in srcs]
+    R = len(srcs)
+    live = [s for s in srcs if s is not None]
+    if not live:
+        raise ValueError("at least one active source is needed")
+    if src_type is None:
+        src_type = F32 if live[0].dtype == np.float32 else wire_type
+    want = np.float32 if src_type == F32 else np.uint16
+    need = 0 if rows == 0 else (rows - 1) * src_stride + cols
+    for s in live:
+        if s.dtype != want or s.size < need:
+            raise ValueError("source too short or of the wrong type")
+    out_dtype = np.float32 if dst_type == F32 else np.uint16
+    extent = 0 if rows == 0 else (rows - 1) * dst_stride + cols
+    out = np.zeros((n_dst, extent), dtype=out_dtype)
+    if dst_init is not None:
+        out[:] = np.asarray(dst_init, dtype=out_dtype)[:extent]
+    res_ptr = None
+    if residual is not None:
+        residual = np.ascontiguousarray(residual)
+        if residual.dtype != out_dtype:
+            raise TypeError("residual type does not match the destination type")
+        res_need = 0 if rows == 0 else (cols if res_stride == 0 else (rows - 1) * res_stride + cols)
+        if residual.size < res_need:
+            raise ValueError("residual too short")
+        res_ptr = residual.ctypes.data
+    dst_ptrs = (ctypes.c_void_p * n_dst)(*[out[d].ctypes.data for d in range(n_dst)])
+    src_ptrs = (ctypes.c_void_p * R)(*[None if s is None else s.ctypes.data for s in srcs])
+    rc = lib.orc_reduce_rows(dst_ptrs, n_dst, dst_type, src_ptrs, R, rows, cols, src_stride, dst_stride,
+                             src_type, wire_type, res_ptr, res_stride)
     if rc != 0:
         raise ValueError(f"oracle rejected arguments (rc={rc})")
     return out

@@ -313,6 +313,47 @@ int orc_reduce(float *const *dst, int n_dst, const void *const *srcs, int R,
     return orc_reduce_ex((void *const *)dst, n_dst, ORC_F32, srcs, R, n, src_type, wire_type, NULL, 0);
 }
 
+/* ---------------------------------------------------------------------------
+ * The reduce over row-strided tensors ("Hexagon allreduce-ops.c" page,
+ * allreduce_thread_dma_2d: each rank's rows are fetched with the tensor's
+ * row stride nb[1] and ne0 elements per row; with IS_ROW_BCAST one residual
+ * row is added to every row).  Row i, column j of a tensor lives at element
+ * i * stride + j; the columns cols .. stride-1 of each row are not part of
+ * the tensor and are never written.  The arithmetic of every element is that
+ * of orc_reduce_ex.  res_stride 0 with a residual is the broadcast row.
+ * ------------------------------------------------------------------------- */
+int orc_reduce_rows(void *const *dst, int n_dst, int dst_type, const void *const *srcs, int R,
+                    size_t rows, size_t cols, size_t src_stride, size_t dst_stride, int src_type,
+                    int wire_type, const void *residual, size_t res_stride) {
+    if (R < 1 || n_dst < 1 || dst == NULL || srcs == NULL) return -1;
+    if (wire_type < ORC_F32 || wire_type > ORC_BF16) return -1;
+    if (src_type != ORC_F32 && src_type != wire_type) return -1;
+    if (dst_type != ORC_F32 && (dst_type != wire_type || src_type != wire_type)) return -1;
+    if (src_stride < cols || dst_stride < cols) return -1;
+    if (residual != NULL && res_stride != 0 && res_stride < cols) return -1;
+
+    const unsigned saved = orc_enter_ieee();
+    for (size_t i = 0; i < rows; ++i) {
+        for (size_t j = 0; j < cols; ++j) {
+            const size_t si = i * src_stride + j;
+            float acc = orc_wire_value(srcs[0], si, src_type, wire_type);
+            for (int r = 1; r < R; ++r) {
+                acc = acc + orc_wire_value(srcs[r], si, src_type, wire_type);
+                if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);
+            }
+            if (residual != NULL) {
+                acc = acc + orc_dst_value(residual, i * res_stride + j, dst_type);
+                if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);
+            }
+            for (int d = 0; d < n_dst; ++d) {
+                orc_store_dst(dst[d], i * dst_stride + j, acc, dst_type);
+            }
+        }
+    }
+    orc_leave_ieee(saved);
+    return 0;
+}
+
 /* Array forms of the conversions, used by the exhaustive pins. */
 void orc_round_bf16_array(const uint32_t *x, uint16_t *out, size_t n) {
     for (size_t i = 0; i < n; ++i) out[i] = orc_round_bf16(x[i]);

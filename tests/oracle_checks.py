@@ -35,7 +35,12 @@ What pins what:
                           binary64 then one conversion for float16, brute force
                           over ordered pairs and triples of 16-bit edge
                           patterns, a closed form exact in the narrow type, and
-                          hand-worked rows.
+                          hand-worked rows;
+* row-strided tensors  -- the rows gathered by numpy slicing and reduced by the
+                          1-D routes above (fp64 route, library 16-bit
+                          arithmetic), scattered back by slicing; the bytes
+                          between rows keep their prior contents; a stride
+                          equal to the row length is the 1-D reduce.
 """
 from __future__ import annotations
 
@@ -517,6 +522,64 @@ def check_narrow_dst(lib, seed: int = 43) -> None:
             assert_same_16(got, want, dtype, f"narrow closed form R={R} dtype={dtype}")
 
 
+# --- row-strided tensors ----------------------------------------------------------
+
+def _scatter_rows(flat_init, rows_vals, rows, cols, stride):
+    out = flat_init.copy()
+    for i in range(rows):
+        out[i * stride:i * stride + cols] = rows_vals[i]
+    return out
+
+
+def check_rows(lib, seed: int = 47) -> None:
+    """Row-strided reduce: gathered rows through the independent 1-D routes."""
+    rng = np.random.default_rng(seed)
+    cases = [(5, 16, 20, 24, 16), (3, 520, 528, 520, 0), (7, 9, 12, 16, 9), (1, 33, 33, 40, 40),
+             (4, 8, 8, 8, 0), (0, 8, 8, 8, 8)]
+    for k, (rows, cols, ss, ds, rs) in enumerate(cases):
+        R = 2 + k % 3
+        n_src = max(1, (rows - 1) * ss + cols) if rows else 1
+        srcs = workloads.random_partials(990 + k, seed, R, n_src, dist="wide")
+        extent = (rows - 1) * ds + cols if rows else 0
+        init = rng.integers(0, 1 << 32, extent, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        for wire in (F32, BF16, F16):
+            for with_res in (False, True):
+                res = None
+                if with_res:
+                    res_n = cols if rs == 0 else max(1, (rows - 1) * rs + cols)
+                    res = workloads.residual(991 + k, seed, res_n, dist="wide")
+                got = oracle.reduce_rows(srcs, wire, rows, cols, ss, ds, n_dst=2, residual=res,
+                                         res_stride=rs, dst_init=init, lib=lib)
+                g_rows = [np.stack([s[i * ss:i * ss + cols] for i in range(rows)]) if rows else
+                          np.zeros((0, cols), np.float32) for s in srcs]
+                terms = [lib_wire_value(g.ravel(), wire) for g in g_rows]
+                if with_res:
+                    r_rows = np.stack([res[(0 if rs == 0 else i * rs):(0 if rs == 0 else i * rs) + cols]
+                                       for i in range(rows)]) if rows else np.zeros((0, cols), np.float32)
+                    terms.append(r_rows.ravel())
+                with np.errstate(all="ignore"):
+                    flat = fp64_route_fold(terms) if rows else np.zeros(0, np.float32)
+                want = _scatter_rows(init, flat.reshape(rows, cols), rows, cols, ds)
+                what = f"rows case {k} wire={wire} residual={with_res}"
+                assert_same_f32(got[0], want, what)
+                assert np.array_equal(got[0].view(np.uint32), got[1].view(np.uint32)), what
+    # narrow destination with row-strided tensors, through library 16-bit arithmetic
+    for t in (F16, BF16):
+        rows, cols, ss, ds = 6, 24, 32, 40
+        srcs = workloads.random_narrow(995, seed, 3, (rows - 1) * ss + cols, t, dist="wide")
+        res = workloads.residual(996, seed, cols, t, dist="wide")
+        init = rng.integers(0, 1 << 16, (rows - 1) * ds + cols, dtype=np.uint32).astype(np.uint16)
+        got = oracle.reduce_rows(srcs, t, rows, cols, ss, ds, src_type=t, dst_type=t, residual=res,
+                                 res_stride=0, dst_init=init, lib=lib)[0]
+        g = [np.concatenate([s[i * ss:i * ss + cols] for i in range(rows)]) for s in srcs]
+        flat = lib_narrow_fold(g + [np.tile(res, rows)], t)
+        assert_same_16(got, _scatter_rows(init, flat.reshape(rows, cols), rows, cols, ds), t, f"rows narrow {t}")
+    # a stride equal to the row length is the 1-D reduce
+    srcs = workloads.random_partials(997, seed, 4, 12 * 64, dist="wide")
+    got = oracle.reduce_rows(srcs, BF16, 12, 64, 64, 64, lib=lib)[0]
+    assert_same_f32(got, oracle.reduce(srcs, BF16, lib=lib)[0], "rows with stride == cols")
+
+
 def cheap_checks():
     """Checks fast enough to run against every planted-mistake build."""
     return [
@@ -533,4 +596,5 @@ def cheap_checks():
         ("inactive", check_inactive_ranks),
         ("residual", check_residual),
         ("narrow", check_narrow_dst),
+        ("rows", check_rows),
     ]

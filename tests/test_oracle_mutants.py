@@ -75,6 +75,14 @@ MUTANTS = [
     ("narrow_rounds_once_at_end", [
         ("            if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);\n        }\n        if (residual",
          "        }\n        if (dst_type != ORC_F32) acc = orc_to_dst(acc, dst_type);\n        if (residual")]),
+    ("rows_src_index_uses_dst_stride", [("const size_t si = i * src_stride + j;",
+                                        "const size_t si = i * dst_stride + j;")]),
+    ("rows_broadcast_residual_advances", [("orc_dst_value(residual, i * res_stride + j, dst_type)",
+                                          "orc_dst_value(residual, i * (res_stride ? res_stride : cols) + j, dst_type)")]),
+    ("rows_writes_between_rows", [("orc_store_dst(dst[d], i * dst_stride + j, acc, dst_type);",
+                                   "orc_store_dst(dst[d], i * dst_stride + j, acc, dst_type);\n"
+                                   "                if (j + 1 == cols && cols < dst_stride && i + 1 < rows) "
+                                   "orc_store_dst(dst[d], i * dst_stride + cols, acc, dst_type);")]),
     ("narrow_store_wrong_format", [
         ("dst_type == ORC_BF16 ? orc_round_bf16(bits) : orc_round_f16(bits)",
          "dst_type == ORC_BF16 ? orc_round_f16(bits) : orc_round_bf16(bits)")]),

@@ -91,3 +91,7 @@ def test_rejects_undefined_residual_and_narrow_combinations(orc):
     with pytest.raises(TypeError):       # residual of the wrong type
         oracle.reduce([h, h], oracle.F16, src_type=oracle.F16, dst_type=oracle.F16,
                       residual=np.ones(12, dtype=np.float32), lib=orc)
+
+
+def test_row_strided(orc):
+    oc.check_rows(orc)
