@@ -377,17 +377,24 @@ mpp::Types launch_types(const ar_plan &plan, int wire_type) {
     return mpp::Types{wire_type, plan.src_bytes == 2, plan.dst_bytes == 2};
 }
 
-// Residual fields of a launch whose element 0 is element `first` of the call.
-void set_residual(mpp::KernelArgs &a, const Residual &res, size_t n, size_t first, int dst_bytes) {
+// Residual fields of a 1-D launch whose element 0 is element `first` of the
+// call; consecutive ranges of `cols` elements (strides = cols).
+void set_ranges_1d(mpp::KernelArgs &a, const Residual &res, size_t n, size_t first, size_t cols, int dst_bytes) {
+    a.cols = static_cast<unsigned>(cols);
+    a.src_stride = cols;
+    a.dst_stride = cols;
+    a.res_stride = cols;
     if (res.ptr == nullptr) return;
     if (res.len == n) {
         a.res = static_cast<const char *>(res.ptr) + first * static_cast<size_t>(dst_bytes);
         a.res_len = 0;
         a.res_phase = 0;
+        a.res_reuse = 0;
     } else {
         a.res = res.ptr;
         a.res_len = static_cast<unsigned>(res.len);
         a.res_phase = static_cast<unsigned>(first % res.len);
+        a.res_reuse = 1;
     }
 }
 
@@ -411,10 +418,9 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             mpp::KernelArgs a{};
             a.R = R;
             a.n_dst = R;
-            a.chunk_elems = 0;
             a.store_nt = plan.store_nt;
             a.active = plan.active_mask;
-            set_residual(a, res, n, 0, plan.dst_bytes);
+            set_ranges_1d(a, res, n, 0, 0, plan.dst_bytes);
             unsigned max_len = 0;
             for (int r = 0; r < R; ++r) {
                 const size_t len = plan.slice_len[r] > p0 ? std::min(mpp::kMaxLaunchElems, plan.slice_len[r] - p0) : 0;
@@ -436,26 +442,24 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         mpp::KernelArgs a{};
         a.R = R;
         a.n_dst = 1;
-        a.n = static_cast<unsigned>(len);
+        a.n = len;
         a.store_nt = plan.mode == AR_MODE_SINGLE_SHOT ? 0 : plan.store_nt;
         a.active = plan.active_mask;
         for (int r = 0; r < R; ++r) {
             a.src[r] = srcs[r] == nullptr ? nullptr : static_cast<const char *>(srcs[r]) + p0 * sb;
         }
         a.dst[0] = static_cast<char *>(dst[0]) + p0 * db;
-        set_residual(a, res, n, p0, plan.dst_bytes);
         // CHUNKED: gridDim.y walks the plan's chunks; SINGLE_SHOT: one range
-        a.chunk_elems = static_cast<unsigned>(len);
+        size_t cols = len;
         if (plan.mode == AR_MODE_CHUNKED) {
-            a.chunk_elems = static_cast<unsigned>(std::min(plan.chunk_elems, len));
-            if ((len + a.chunk_elems - 1) / a.chunk_elems > 65535) {
-                a.chunk_elems = static_cast<unsigned>(round_down((len + 65534) / 65535 + mpp::kWaveTile - 1,
-                                                                 mpp::kWaveTile));
-            }
+            cols = std::min(plan.chunk_elems, len);
+            if ((len + cols - 1) / cols > 65535) cols = round_down((len + 65534) / 65535 + mpp::kWaveTile - 1,
+                                                                   mpp::kWaveTile);
         }
-        const unsigned n_ranges = static_cast<unsigned>((len + a.chunk_elems - 1) / a.chunk_elems);
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, a.chunk_elems, n_ranges,
-                                                       c->cu_count, c->cfg.grid_wgs);
+        set_ranges_1d(a, res, n, p0, cols, plan.dst_bytes);
+        const unsigned n_ranges = static_cast<unsigned>((len + cols - 1) / cols);
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(cols),
+                                                       n_ranges, c->cu_count, c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
     }
     return AR_OK;
@@ -527,13 +531,12 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         mpp::KernelArgs a{};
         a.R = R;
         a.n_dst = 1;
-        a.n = static_cast<unsigned>(len);
+        a.n = len;
         a.store_nt = plan.store_nt;
         a.active = plan.active_mask;
-        a.chunk_elems = static_cast<unsigned>(len);
         for (int r = 0; r < R; ++r) a.src[r] = srcs[r] == nullptr ? nullptr : slot_base + r * rank_stride;
         a.dst[0] = static_cast<char *>(dst[0]) + e0 * db;
-        set_residual(a, res, n, e0, plan.dst_bytes);
+        set_ranges_1d(a, res, n, e0, len, plan.dst_bytes);
         const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(len), 1,
                                                        c->cu_count, c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;

@@ -191,37 +191,53 @@ __device__ __forceinline__ void tile_values(const u32x4 (&raw)[C::kSrcRaw], floa
     }
 }
 
-// Index of launch element e in the residual: e itself (element-wise), or its
-// column in the broadcast row.  res_len is a multiple of 8, so the 4 or 8
-// consecutive elements of one lane part never straddle a row boundary.  The
-// slice schedule indexes whole calls, which can pass 2^32 elements: those
-// positions take a 64-bit remainder, all others the cheaper 32-bit one.
+// Where one gridDim.y range of a launch starts in each tensor: element
+// offsets of the range's first element in the sources, the destinations and
+// an element-wise residual (they differ when the tensors are row-strided),
+// and the range's position in the whole call (for a broadcast row's column).
+struct RangeOff {
+    size_t src;
+    size_t dst;
+    size_t res;
+    uint64_t pos;
+};
+
+// Column of call position `pos` in a broadcast row of res_len elements (a
+// multiple of 8, so the 4 or 8 consecutive elements of one lane part never
+// straddle a row boundary).  Calls can pass 2^32 elements: those positions
+// take a 64-bit remainder, all others the cheaper 32-bit one.
 template <class A>
-__device__ __forceinline__ size_t res_index(const A &a, size_t e) {
-    if (a.res_len == 0) return e;
-    const uint64_t x = static_cast<uint64_t>(e) + a.res_phase;
+__device__ __forceinline__ size_t res_column(const A &a, uint64_t pos) {
+    const uint64_t x = pos + a.res_phase;
     if (x < (uint64_t(1) << 32)) return static_cast<unsigned>(x) % a.res_len;
     return x % a.res_len;
 }
 
-// Residual loads of one tile: streaming loads for the element-wise form
-// (read once), ordinary cached loads for a broadcast row (read by every row).
-// Both forms issue the same number of loads, so the branch does not change
-// how many loads are outstanding after it.
+// Residual element of range element e: element-wise (o.res + e, which is the
+// same row for every range when the residual's row stride is 0), or the
+// column of a 1-D broadcast row.
+template <class A>
+__device__ __forceinline__ size_t res_index(const A &a, const RangeOff &o, size_t e) {
+    return a.res_len == 0 ? o.res + e : res_column(a, o.pos + e);
+}
+
+// Residual loads of one tile: streaming loads when each residual element is
+// read once, ordinary cached loads when a row is read by every row.  Both
+// forms issue the same number of loads, so the branch does not change how
+// many loads are outstanding after it.
 template <class C, bool NT>
-__device__ __forceinline__ void res_load(const LaunchArgs<C::RB> &a, size_t t, int lane, u32x4 (&raw)[C::kResRaw]) {
-    if (a.res_len == 0) {
+__device__ __forceinline__ void res_load(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
+                                         u32x4 (&raw)[C::kResRaw]) {
+    size_t e[C::kResRaw];
 #pragma unroll
-        for (int j = 0; j < C::kResRaw; ++j) {
-            const size_t e = part_elem<C>(t, lane, j);
-            raw[j] = load16<NT>(static_cast<const char *>(a.res) + e * C::kDstBytes);
-        }
+    for (int j = 0; j < C::kResRaw; ++j) e[j] = res_index(a, o, part_elem<C>(t, lane, j));
+    const char *base = static_cast<const char *>(a.res);
+    if (a.res_reuse) {
+#pragma unroll
+        for (int j = 0; j < C::kResRaw; ++j) raw[j] = load16<false>(base + e[j] * C::kDstBytes);
     } else {
 #pragma unroll
-        for (int j = 0; j < C::kResRaw; ++j) {
-            const size_t e = res_index(a, part_elem<C>(t, lane, j));
-            raw[j] = load16<false>(static_cast<const char *>(a.res) + e * C::kDstBytes);
-        }
+        for (int j = 0; j < C::kResRaw; ++j) raw[j] = load16<NT>(base + e[j] * C::kDstBytes);
     }
 }
 
@@ -294,19 +310,20 @@ struct Batch {
     u32x4 res[U][C::kResRaw];
 };
 
-// Issue every load of a batch of U consecutive wave tiles starting at
-// element `t` (range offset included) for the first R of RB sources, tile by
-// tile: the loads of tile 0 are the oldest in flight, so tile 0 can be folded
-// and stored while the later tiles' loads are still arriving.  The residual
-// loads of the batch come last.
+// Issue every load of a batch of U consecutive wave tiles starting at range
+// element `t` for the first R of RB sources, tile by tile: the loads of tile
+// 0 are the oldest in flight, so tile 0 can be folded and stored while the
+// later tiles' loads are still arriving.  The residual loads of the batch
+// come last.
 template <class C, int U, bool NT>
-__device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, size_t t, int lane, Batch<C, U> &b) {
+__device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
+                                           Batch<C, U> &b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int r = 0; r < C::RB; ++r) {
             if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
-                tile_load<C, NT>(a.src[r], t + u * kWaveTile, lane, b.src[r][u]);
+                tile_load<C, NT>(a.src[r], o.src + t + u * kWaveTile, lane, b.src[r][u]);
             }
         }
         // keep tile order: the scheduler must not hoist a later tile's loads
@@ -315,14 +332,14 @@ __device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, size_t t,
     }
     if constexpr (C::RES) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) res_load<C, NT>(a, t + u * kWaveTile, lane, b.res[u]);
+        for (int u = 0; u < U; ++u) res_load<C, NT>(a, o, t + u * kWaveTile, lane, b.res[u]);
     }
 }
 
 // Fold one tile in rank order (one rounding to the destination type per add),
-// add the residual, and store to every destination.
+// add the residual, and store to every destination at element `td`.
 template <class C, bool ST>
-__device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size_t t, int lane,
+__device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size_t td, int lane,
                                                 const u32x4 (&src)[C::RB][C::kSrcRaw], const u32x4 *res) {
     float acc[8];
     if (rank_active<C>(a, 0)) {
@@ -358,7 +375,7 @@ __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size
     }
 #pragma unroll
     for (int d = 0; d < C::RB; ++d) {
-        if (d < a.n_dst) tile_store<C, ST>(a.dst[d], t, lane, acc);
+        if (d < a.n_dst) tile_store<C, ST>(a.dst[d], td, lane, acc);
     }
 }
 
@@ -369,7 +386,8 @@ __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size
 // parameter: two stores that differ only in their cache hint would be merged
 // into one by the compiler.
 template <class C, int U, bool ST>
-__device__ __forceinline__ void fold_store(const LaunchArgs<C::RB> &a, size_t t, int lane, const Batch<C, U> &b) {
+__device__ __forceinline__ void fold_store(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
+                                           const Batch<C, U> &b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         u32x4 src[C::RB][C::kSrcRaw];
@@ -377,27 +395,29 @@ __device__ __forceinline__ void fold_store(const LaunchArgs<C::RB> &a, size_t t,
         for (int r = 0; r < C::RB; ++r)
 #pragma unroll
             for (int j = 0; j < C::kSrcRaw; ++j) src[r][j] = b.src[r][u][j];
-        fold_store_tile<C, ST>(a, t + u * kWaveTile, lane, src, b.res[u]);
+        fold_store_tile<C, ST>(a, o.dst + t + u * kWaveTile, lane, src, b.res[u]);
     }
 }
 
 template <class C, int U, bool NT, bool ST>
-__device__ __forceinline__ void reduce_tiles(const LaunchArgs<C::RB> &a, size_t t, int lane) {
+__device__ __forceinline__ void reduce_tiles(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane) {
     Batch<C, U> b;
-    load_batch<C, U, NT>(a, t, lane, b);
-    fold_store<C, U, ST>(a, t, lane, b);
+    load_batch<C, U, NT>(a, o, t, lane, b);
+    fold_store<C, U, ST>(a, o, t, lane, b);
 }
 
-// Elements [begin, end) of the launch, one per lane per step (end - begin is
-// below one wave tile, so this is at most 8 steps).
+// Range elements [begin, end), one per lane per step (end - begin is below one
+// wave tile, so this is at most 8 steps).
 template <class C>
-__device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, size_t begin, size_t end, int lane) {
+__device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t begin,
+                                              size_t end, int lane) {
     for (size_t e = begin + lane; e < end; e += kWave) {
-        float acc = rank_active<C>(a, 0) ? wire_one<C::W, C::SW>(a.src[0], e) : 0.0f;
+        const size_t es = o.src + e;
+        float acc = rank_active<C>(a, 0) ? wire_one<C::W, C::SW>(a.src[0], es) : 0.0f;
 #pragma unroll
         for (int r = 1; r < C::RB; ++r) {
             if (rank_used<C>(a, r)) {
-                acc = acc + (rank_active<C>(a, r) ? wire_one<C::W, C::SW>(a.src[r], e) : 0.0f);
+                acc = acc + (rank_active<C>(a, r) ? wire_one<C::W, C::SW>(a.src[r], es) : 0.0f);
                 if constexpr (C::DN) {
                     float y = 0.0f;
                     wire_pair<C::W>(acc, y);
@@ -405,7 +425,7 @@ __device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, size_t
             }
         }
         if constexpr (C::RES) {
-            const size_t ri = res_index(a, e);
+            const size_t ri = res_index(a, o, e);
             if constexpr (C::DN) {
                 acc = acc + wire_one<C::W, true>(a.res, ri);
                 float y = 0.0f;
@@ -414,51 +434,59 @@ __device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, size_t
                 acc = acc + static_cast<const float *>(a.res)[ri];
             }
         }
+        const size_t ed = o.dst + e;
 #pragma unroll
         for (int d = 0; d < C::RB; ++d) {
             if (d < a.n_dst) {
                 if constexpr (C::DN) {
-                    static_cast<uint16_t *>(a.dst[d])[e] = static_cast<uint16_t>(round_pack<C::W>(acc, 0.0f));
+                    static_cast<uint16_t *>(a.dst[d])[ed] = static_cast<uint16_t>(round_pack<C::W>(acc, 0.0f));
                 } else {
-                    static_cast<float *>(a.dst[d])[e] = acc;
+                    static_cast<float *>(a.dst[d])[ed] = acc;
                 }
             }
         }
     }
 }
 
-// The element range [off, off + len) of this workgroup's gridDim.y index.
-// Both forms only read launch arguments at fixed offsets (the slice form
-// indexes with blockIdx.y, which is known at wave start), so a wave fetches
-// everything it needs in one batch of scalar loads.
+// Offsets and length of this workgroup's gridDim.y range.  Slice ranges
+// (broadcast schedule): [slice_start[y], + slice_len[y]) of every tensor.
+// Strided ranges (everything else): range y has min(cols, n - y * cols)
+// elements starting at element y * stride of each tensor class -- 1-D chunks
+// (stride = cols) and the rows of row-strided tensors alike.  Both forms only
+// read launch arguments at fixed offsets (blockIdx.y is known at wave
+// start), so a wave fetches everything it needs in one batch of scalar loads.
 template <bool SLICED, class A>
-__device__ __forceinline__ void range_of(const A &a, size_t &off, unsigned &len) {
+__device__ __forceinline__ void range_of(const A &a, RangeOff &o, unsigned &len) {
     const unsigned y = blockIdx.y;
     if constexpr (SLICED) {
-        off = a.slice_start[y];
+        o.src = o.dst = o.res = a.slice_start[y];
+        o.pos = a.slice_start[y];
         len = a.slice_len[y];
     } else {
-        const unsigned start = y * a.chunk_elems;
-        const unsigned left = a.n - start;
-        off = start;
-        len = left < a.chunk_elems ? left : a.chunk_elems;
+        const uint64_t start = static_cast<uint64_t>(y) * a.cols;
+        const uint64_t left = a.n - start;
+        len = left < a.cols ? static_cast<unsigned>(left) : a.cols;
+        o.src = static_cast<size_t>(y) * a.src_stride;
+        o.dst = static_cast<size_t>(y) * a.dst_stride;
+        o.res = static_cast<size_t>(y) * a.res_stride;
+        o.pos = start;
     }
 }
 
 // Whole wave tiles after the batched part, then the element remainder on
 // wave 0 of workgroup 0 of the range.
 template <class C, int U, bool NT, bool ST>
-__device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, size_t off, unsigned len, unsigned done,
-                                            unsigned gw, unsigned nw, int lane) {
+__device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len,
+                                            unsigned done, unsigned gw, unsigned nw, int lane) {
     if constexpr (U > 1) {
         const unsigned n_one = (len - done) / kWaveTile;
         for (unsigned t = gw; t < n_one; t += nw) {
-            reduce_tiles<C, 1, NT, ST>(a, off + done + (size_t)t * kWaveTile, lane);
+            reduce_tiles<C, 1, NT, ST>(a, o, done + (size_t)t * kWaveTile, lane);
         }
     }
     const unsigned vec_end = (len / kWaveTile) * kWaveTile;
     if (vec_end < len && gw == 0) {
-        reduce_scalar<C>(a, off + vec_end, off + len, lane);
+        reduce_scalar<C>(a, o, vec_end, len, lane);
     }
 }
 
@@ -471,16 +499,16 @@ __device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a) {
     const int lane = threadIdx.x & (kWave - 1);
     const unsigned gw = blockIdx.x * wpb + threadIdx.x / kWave;
     const unsigned nw = a.waves;
-    size_t off;
+    RangeOff o;
     unsigned len;
-    range_of<SLICED>(a, off, len);
+    range_of<SLICED>(a, o, len);
 
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
     for (unsigned t = gw; t < n_big; t += nw) {
-        reduce_tiles<C, U, NT, ST>(a, off + (size_t)t * big, lane);
+        reduce_tiles<C, U, NT, ST>(a, o, (size_t)t * big, lane);
     }
-    reduce_rest<C, U, NT, ST>(a, off, len, n_big * big, gw, nw, lane);
+    reduce_rest<C, U, NT, ST>(a, o, len, n_big * big, gw, nw, lane);
 }
 
 constexpr int kSingleShotBlock = 64;
@@ -570,7 +598,8 @@ constexpr int lds_batch(bool src_is_wire, int rank_bucket) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <class C, int U>
-__device__ __forceinline__ void lds_issue(const LaunchArgs<C::RB> &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+__device__ __forceinline__ void lds_issue(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
+                                          u32x4 (*stage)[kWave]) {
     constexpr int K = C::kSrcRaw;
 #pragma unroll
     for (int r = 0; r < C::RB; ++r) {
@@ -579,7 +608,7 @@ __device__ __forceinline__ void lds_issue(const LaunchArgs<C::RB> &a, size_t t, 
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
-                    const size_t e = C::SW ? t + u * kWaveTile + 8 * lane : t + u * kWaveTile + 256 * j + 4 * lane;
+                    const size_t e = o.src + (C::SW ? t + u * kWaveTile + 8 * lane : t + u * kWaveTile + 256 * j + 4 * lane);
                     const char *g = static_cast<const char *>(a.src[r]) + e * (C::SW ? 2 : 4);
                     __builtin_amdgcn_global_load_lds(g, (lds_void *)(&stage[(r * U + u) * K + j][0]),
                                                      16, 0, MPP_LDS_AUX);
@@ -623,7 +652,8 @@ __device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
 }
 
 template <class C, int U, bool ST>
-__device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, size_t t, int lane, u32x4 (*stage)[kWave]) {
+__device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
+                                            u32x4 (*stage)[kWave]) {
     static_assert(!C::RES, "the LDS-staged kernel has no residual form");
     constexpr int K = C::kSrcRaw;
     const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void *)(&stage[0][lane])));
@@ -637,7 +667,7 @@ __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, size_t t
                 for (int j = 0; j < K; ++j) b.src[r][u][j] = lds_read16(base + ((r * U + u) * K + j) * kWave * 16);
         }
     }
-    fold_store<C, U, ST>(a, t, lane, b);
+    fold_store<C, U, ST>(a, o, t, lane, b);
 }
 
 template <class C, bool ST, bool SLICED>
@@ -646,9 +676,9 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 
     const int lane = threadIdx.x;
     const unsigned gw = blockIdx.x;
     const unsigned nw = a.waves;
-    size_t off;
+    RangeOff o;
     unsigned len;
-    range_of<SLICED>(a, off, len);
+    range_of<SLICED>(a, o, len);
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
 
@@ -659,28 +689,28 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 
     constexpr int kMaxL = C::RB * U * C::kSrcRaw;
 
     unsigned t = gw;
-    if (t < n_big) lds_issue<C, U>(a, off + (size_t)t * big, lane, stage0);
+    if (t < n_big) lds_issue<C, U>(a, o, (size_t)t * big, lane, stage0);
     while (t < n_big) {
         const unsigned t1 = t + nw;
         if (t1 < n_big) {
-            lds_issue<C, U>(a, off + (size_t)t1 * big, lane, stage1);
+            lds_issue<C, U>(a, o, (size_t)t1 * big, lane, stage1);
             wait_stage<kMaxL>(L);
         } else {
             wait_vm<0>();
         }
-        lds_consume<C, U, ST>(a, off + (size_t)t * big, lane, stage0);
+        lds_consume<C, U, ST>(a, o, (size_t)t * big, lane, stage0);
         if (t1 >= n_big) break;
         const unsigned t2 = t1 + nw;
         if (t2 < n_big) {
-            lds_issue<C, U>(a, off + (size_t)t2 * big, lane, stage0);
+            lds_issue<C, U>(a, o, (size_t)t2 * big, lane, stage0);
             wait_stage<kMaxL>(L);
         } else {
             wait_vm<0>();
         }
-        lds_consume<C, U, ST>(a, off + (size_t)t1 * big, lane, stage1);
+        lds_consume<C, U, ST>(a, o, (size_t)t1 * big, lane, stage1);
         t = t2;
     }
-    reduce_rest<C, U, true, ST>(a, off, len, n_big * big, gw, nw, lane);
+    reduce_rest<C, U, true, ST>(a, o, len, n_big * big, gw, nw, lane);
 }
 
 template <class C, bool ST, bool SLICED>

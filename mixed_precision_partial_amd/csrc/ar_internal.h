@@ -23,23 +23,32 @@ constexpr unsigned kWaveTile = 512;
 // few bytes, a quarter of a decode-sized call).  The launch covers R sources
 // and n_dst destinations over gridDim.y ranges, each walked by the `waves`
 // waves of gridDim.x workgroups:
-//   chunk ranges (CHUNKED, SINGLE_SHOT, host-staged chunks): range y is
-//       [y * chunk_elems, min((y + 1) * chunk_elems, n));
+//   strided ranges (every schedule but the broadcast one): range y has
+//       min(cols, n - y * cols) elements and starts at element
+//       y * src_stride / y * dst_stride / y * res_stride of the sources /
+//       destinations / element-wise residual -- consecutive 1-D chunks
+//       (strides = cols) or the rows of row-strided tensors;
 //   slice ranges (RS_BCAST, a separate kernel instance): range y is
-//       [slice_start[y], slice_start[y] + slice_len[y]), gridDim.y <= R.
+//       [slice_start[y], slice_start[y] + slice_len[y]) of every tensor,
+//       gridDim.y <= R.
 // The scalars a wave needs first sit at the front so that one batch of
 // scalar loads fetches them together with the pointers.
 template <int NR>
 struct LaunchArgs {
-    unsigned    n;
-    unsigned    chunk_elems;
+    uint64_t    n;          // elements of the launch (strided ranges)
+    unsigned    cols;       // elements per strided range
     unsigned    waves;      // waves per range: gridDim.x * (block / 64)
     int         R;
     int         n_dst;
     unsigned    active;     // bit r: rank r has a partial; an inactive rank is +0.0
-    unsigned    res_len;    // residual: 0 = element-wise (index = launch element),
-                            // else the broadcast row's length (a multiple of 8)
-    unsigned    res_phase;  // row form: column of launch element 0 in the row
+    unsigned    res_len;    // residual: 0 = element-wise (range offset + element),
+                            // else a 1-D broadcast row of res_len elements (a
+                            // multiple of 8) indexed by call position
+    unsigned    res_phase;  // 1-D row: column of launch element 0 in the row
+    unsigned    res_reuse;  // 1: residual elements are re-read (a broadcast row)
+    uint64_t    src_stride; // strided ranges: elements between range starts
+    uint64_t    dst_stride;
+    uint64_t    res_stride; // 0 with res_len 0: one row added to every range
     const void *res;        // residual in the destination type, or nullptr
     const void *src[NR];
     void       *dst[NR];    // binary32, or 16-bit for a narrow destination

@@ -34,13 +34,17 @@ template <int NR>
 hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &shape, hipStream_t stream) {
     LaunchArgs<NR> b;
     b.n = a.n;
-    b.chunk_elems = a.chunk_elems;
+    b.cols = a.cols;
     b.waves = a.waves;
     b.R = a.R;
     b.n_dst = a.n_dst;
     b.active = a.active;
     b.res_len = a.res_len;
     b.res_phase = a.res_phase;
+    b.res_reuse = a.res_reuse;
+    b.src_stride = a.src_stride;
+    b.dst_stride = a.dst_stride;
+    b.res_stride = a.res_stride;
     b.res = a.res;
     for (int r = 0; r < NR; ++r) {
         b.src[r] = a.src[r];
