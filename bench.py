@@ -508,6 +508,20 @@ def other_schedules(torch, ar, wl):
     out["prefill_bf16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_bf16_dst: {out['prefill_bf16_dst']}")
     del srcs, dsts
+    # row-strided: the prefill block as a view of wider rows (2048 x 4096 in rows of
+    # 4608 for the partials, 4352 for the destination) with a broadcast bias row
+    rows, cols, ss, ds = 2048, 4096, 4608, 4352
+    sets = 6
+    srcs = [[torch.randn(rows * ss, device="cuda") for _ in range(2)] for _ in range(sets)]
+    dsts = [torch.empty(rows * ds, device="cuda") for _ in range(sets)]
+    bias = torch.randn(cols, device="cuda")
+    ms = timed(rot(lambda i: ar.ar_reduce_rows(ctx, [dsts[i]], srcs[i], rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16,
+                                               ar.AR_MODE_CHUNKED, residual=bias, res_stride=0, stream=stream)), 200)
+    b = 2 * rows * cols * 4 + rows * cols * 4 + cols * 4
+    out["rows_prefill_block_bias"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"rows_prefill_block_bias: {out['rows_prefill_block_bias']}")
+    del srcs, dsts
+
     w = wl.WORKLOADS["slice_bcast_f16"]
     srcs = [torch.from_numpy(wl.as_wire_typed(p, ar.AR_F16).view(np.int16)).cuda() for p in wl.partials(w, 0)]
     dsts = [torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(w.R)]

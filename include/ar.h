@@ -200,6 +200,41 @@ int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R,
                   int dst_type, int wire_type, unsigned mode, const void *residual,
                   size_t residual_len, void *hip_stream);
 
+/* Row-strided tensors ("Hexagon allreduce-ops.c" page, allreduce_thread_dma_2d:
+ * rows of ne0 elements fetched with the tensor's row stride nb[1]).  Row i of
+ * every source starts at element i * src_stride, of every destination at
+ * i * dst_stride, of an element-wise residual at i * res_stride; the elements
+ * from cols up to the stride of each row are neither read nor written. */
+typedef struct {
+    size_t rows;
+    size_t cols;        /* elements per row (at most 2^30)                        */
+    size_t src_stride;  /* >= cols; src_stride * source element size % 16 == 0   */
+    size_t dst_stride;  /* >= cols; dst_stride * destination element size % 16 == 0 */
+    size_t res_stride;  /* residual: >= cols (element-wise, same alignment rule),
+                           or 0 = one residual row of cols elements added to every
+                           row (the page's IS_ROW_BCAST form); ignored without one */
+} ar_rows;
+
+/* Enqueue one reduce of row-strided tensors: for every row i and column
+ * j < cols the element at row i, column j is computed exactly as ar_reduce
+ * computes one element (followed, when `residual` is not NULL, by the residual
+ * add of ar_reduce_add with the residual's row i -- or its only row when
+ * res_stride is 0).  n = rows * cols; rows = 0 or cols = 0 is a no-op.
+ *   shape    : the row layout above.
+ *   residual : NULL, or a device buffer of dst_type laid out as shape says.
+ * Every base pointer must be 16-byte aligned and every stride keep row starts
+ * 16-byte aligned (AR_ERR_INVALID otherwise).  AR_MODE_RS_BCAST writes every
+ * row to all R destinations (the rows are spread over the workgroups, not cut
+ * into per-rank slices; the bytes are the same).  AR_MODE_HOST_STAGED copies
+ * chunks of whole rows with 2-D copy-engine transfers (host_path 2: the kernel
+ * reads the pinned rows directly).  Exactly in place needs equal strides;
+ * overlaps are judged on each tensor's span from its first to its last
+ * element.  Ownership and the remaining error codes are those of ar_reduce
+ * and ar_reduce_add; cols > 2^30 -> AR_ERR_UNSUPPORTED. */
+int ar_reduce_rows(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R,
+                   const ar_rows *shape, int dst_type, int wire_type, unsigned mode,
+                   const void *residual, void *hip_stream);
+
 /* Drain the context's internal stream and release everything it owns.
  * NULL is accepted and returns AR_OK.  Work already enqueued by ar_reduce
  * on caller streams must be complete or ordered before any reuse of the
@@ -240,6 +275,13 @@ typedef struct {
 int ar_plan_query(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
                   size_t n, int dst_type, int wire_type, unsigned mode, int srcs_on_host,
                   ar_plan *plan);
+
+/* The same for ar_reduce_rows (slice_start / slice_len stay 0: row-strided
+ * calls are not cut into per-rank slices; chunk_elems is one row on the
+ * device, or the rows of one host-staged copy chunk times cols). */
+int ar_plan_query_rows(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
+                       const ar_rows *shape, int dst_type, int wire_type, unsigned mode,
+                       const void *residual, int srcs_on_host, ar_plan *plan);
 
 /* The same for ar_reduce_add (residual checks included). */
 int ar_plan_query_add(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,

@@ -10,9 +10,11 @@ The functions carry the C names:
     ctx = ar_init(device=0, config=None)
     ar_reduce(ctx, dsts, srcs, n, dst_type, wire_type, mode, stream=None)
     ar_reduce_add(ctx, dsts, srcs, n, dst_type, wire_type, mode, residual, residual_len, stream=None)
+    ar_reduce_rows(ctx, dsts, srcs, rows, cols, src_stride, dst_stride, dst_type, wire_type, mode,
+                   residual=None, res_stride=0, stream=None)
     ar_free(ctx)
     ar_status_str(code)
-    ar_plan_query(...), ar_plan_query_add(...)
+    ar_plan_query(...), ar_plan_query_add(...), ar_plan_query_rows(...)
 
 ``dsts`` / ``srcs`` are sequences of torch tensors or raw integer addresses, or
 ready-made ``ptr_array(...)`` arrays (passed through unchanged, which keeps
@@ -77,6 +79,16 @@ class ArPlan(ctypes.Structure):
     ]
 
 
+class ArRows(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_size_t),
+        ("cols", ctypes.c_size_t),
+        ("src_stride", ctypes.c_size_t),
+        ("dst_stride", ctypes.c_size_t),
+        ("res_stride", ctypes.c_size_t),
+    ]
+
+
 class ArError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -117,6 +129,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.c_int, sz, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
                                       vp, sz, ctypes.c_int, ctypes.POINTER(ArPlan)]
     lib.ar_plan_query_add.restype = ctypes.c_int
+    lib.ar_reduce_rows.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ArRows),
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_uint, vp, vp]
+    lib.ar_reduce_rows.restype = ctypes.c_int
+    lib.ar_plan_query_rows.argtypes = [ctypes.POINTER(ArConfig), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                       ctypes.c_int, ctypes.POINTER(ArRows), ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_uint, vp, ctypes.c_int, ctypes.POINTER(ArPlan)]
+    lib.ar_plan_query_rows.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -206,6 +225,22 @@ def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: 
     return rc
 
 
+def ar_reduce_rows(ctx, dsts, srcs, rows: int, cols: int, src_stride: int, dst_stride: int, dst_type: int,
+                   wire_type: int, mode: int, residual=None, res_stride: int = 0, stream=None,
+                   check: bool = True) -> int:
+    """Enqueue one reduce of row-strided tensors (strides in elements); ``residual``
+    None, or a tensor / address laid out with row stride ``res_stride`` (0 = one row
+    added to every row).  Returns the status (raises ArError on failure if ``check``)."""
+    lib = load_library()
+    R = len(srcs) if srcs is not None else 0
+    shape = ArRows(int(rows), int(cols), int(src_stride), int(dst_stride), int(res_stride))
+    rc = lib.ar_reduce_rows(ctx, _ptr_array(dsts), _ptr_array(srcs), R, ctypes.byref(shape), int(dst_type),
+                            int(wire_type), int(mode), _addr(residual), _stream_handle(stream))
+    if check and rc != AR_OK:
+        raise ArError(rc, "ar_reduce_rows")
+    return rc
+
+
 def ar_free(ctx) -> None:
     rc = load_library().ar_free(ctx)
     if rc != AR_OK:
@@ -237,6 +272,21 @@ def ar_plan_query_add(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: i
                                _ptr_array(srcs), R, int(n), int(dst_type), int(wire_type), int(mode),
                                _addr(residual), int(residual_len), int(bool(srcs_on_host)),
                                ctypes.byref(plan))
+    return rc, plan
+
+
+def ar_plan_query_rows(dsts, srcs, rows: int, cols: int, src_stride: int, dst_stride: int, dst_type: int,
+                       wire_type: int, mode: int, residual=None, res_stride: int = 0, srcs_on_host: bool = False,
+                       config=None, R: int | None = None):
+    """Host-only validation + plan of ar_reduce_rows; returns (status, ArPlan)."""
+    lib = load_library()
+    plan = ArPlan()
+    cfg = _config(config)
+    R = (len(srcs) if srcs is not None else 0) if R is None else R
+    shape = ArRows(int(rows), int(cols), int(src_stride), int(dst_stride), int(res_stride))
+    rc = lib.ar_plan_query_rows(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
+                                _ptr_array(srcs), R, ctypes.byref(shape), int(dst_type), int(wire_type),
+                                int(mode), _addr(residual), int(bool(srcs_on_host)), ctypes.byref(plan))
     return rc, plan
 
 

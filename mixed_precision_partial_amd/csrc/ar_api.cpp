@@ -117,10 +117,29 @@ struct Residual {
     size_t len = 0;
 };
 
-// Everything ar_reduce checks without the HIP runtime, plus the plan.
+// Row-strided tensors of ar_reduce_rows: `rows` rows of `cols` elements, row i
+// of the sources / destinations / element-wise residual at element
+// i * src_stride / i * dst_stride / i * res_stride (res_stride 0: one residual
+// row for every row).
+struct Rows {
+    size_t rows = 0;
+    size_t cols = 0;
+    size_t src_stride = 0;
+    size_t dst_stride = 0;
+    size_t res_stride = 0;
+};
+
+// Elements from the first to the last element of `rows` rows of `cols`.
+size_t extent(size_t rows, size_t cols, size_t stride) {
+    return rows == 0 || cols == 0 ? 0 : (rows - 1) * stride + cols;
+}
+
+// Everything ar_reduce checks without the HIP runtime, plus the plan.  With
+// `rows` the call is row-strided (n = rows x cols); otherwise every tensor is
+// contiguous.
 int validate_and_plan(const Config &cfg, void *const *dst, const void *const *srcs, int R, size_t n,
                       int dst_type, int wire_type, unsigned mode, const Residual &res, bool srcs_on_host,
-                      ar_plan *plan) {
+                      ar_plan *plan, const Rows *rows = nullptr) {
     if (R < 2 || R > AR_MAX_RANKS) return AR_ERR_INVALID;
     if (!valid_type(dst_type) || !valid_type(wire_type)) return AR_ERR_INVALID;
     if ((mode & ~(AR_MODE_MASK | AR_SRC_WIRE | AR_SRC_INACTIVE_NULL)) != 0) return AR_ERR_INVALID;
@@ -140,7 +159,21 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
     const int wire_bytes = elem_bytes(wire_type);
     const int dst_bytes = elem_bytes(dst_type);
     int res_kind = 0;
-    if (res.ptr != nullptr && n > 0) {
+    if (rows != nullptr) {
+        // every row start 16-byte aligned: the kernels move 16 B per lane
+        if (rows->src_stride < rows->cols || rows->dst_stride < rows->cols) return AR_ERR_INVALID;
+        if ((rows->src_stride * static_cast<size_t>(src_bytes)) % 16 != 0 ||
+            (rows->dst_stride * static_cast<size_t>(dst_bytes)) % 16 != 0) {
+            return AR_ERR_INVALID;
+        }
+        if (rows->cols > mpp::kMaxLaunchElems) return AR_ERR_UNSUPPORTED;
+        if (res.ptr != nullptr && n > 0) {
+            if (rows->res_stride != 0 && rows->res_stride < rows->cols) return AR_ERR_INVALID;
+            if ((rows->res_stride * static_cast<size_t>(dst_bytes)) % 16 != 0) return AR_ERR_INVALID;
+            if (reinterpret_cast<uintptr_t>(res.ptr) % 16 != 0) return AR_ERR_INVALID;
+            res_kind = rows->res_stride == 0 ? 2 : 1;
+        }
+    } else if (res.ptr != nullptr && n > 0) {
         if (res.len == 0 || res.len > n || n % res.len != 0) return AR_ERR_INVALID;
         if (reinterpret_cast<uintptr_t>(res.ptr) % 16 != 0) return AR_ERR_INVALID;
         res_kind = res.len == n ? 1 : 2;
@@ -176,9 +209,18 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
     }
     if (n > (SIZE_MAX / 8) / AR_MAX_RANKS) return AR_ERR_INVALID;
 
-    const size_t dst_len = n * static_cast<size_t>(dst_bytes);
-    const size_t src_len = n * static_cast<size_t>(src_bytes);
-    const size_t res_bytes = res_kind != 0 ? res.len * static_cast<size_t>(dst_bytes) : 0;
+    // bytes each tensor spans (row-strided tensors: first to last element)
+    const size_t dst_len = (rows ? extent(rows->rows, rows->cols, rows->dst_stride) : n) * static_cast<size_t>(dst_bytes);
+    const size_t src_len = (rows ? extent(rows->rows, rows->cols, rows->src_stride) : n) * static_cast<size_t>(src_bytes);
+    size_t res_bytes = 0;
+    if (res_kind != 0) {
+        const size_t res_elems = rows ? (res_kind == 2 ? rows->cols : extent(rows->rows, rows->cols, rows->res_stride))
+                                      : res.len;
+        res_bytes = res_elems * static_cast<size_t>(dst_bytes);
+    }
+    // the same layout on both sides of an exact in-place use
+    const bool same_src_layout = rows == nullptr || rows->src_stride == rows->dst_stride;
+    const bool same_res_layout = rows == nullptr || rows->res_stride == rows->dst_stride;
     if (n > 0) {
         for (int d = 0; d < n_dst; ++d) {
             const uintptr_t pd = reinterpret_cast<uintptr_t>(dst[d]);
@@ -193,14 +235,14 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 if (!ranges_overlap(pd, dst_len, ps, src_len)) continue;
                 // exactly in place with equal element width is the one allowed overlap:
                 // every element is read from all sources before the same thread writes it
-                if (!(ps == pd && src_bytes == dst_bytes)) return AR_ERR_INVALID;
+                if (!(ps == pd && src_bytes == dst_bytes && same_src_layout)) return AR_ERR_INVALID;
             }
             if (res_kind != 0) {
                 // an element-wise residual may be a destination itself (x += reduce):
                 // each element's residual is read by the thread that writes it; a
                 // broadcast row is read by every row, so it must not be written
                 const uintptr_t pr = reinterpret_cast<uintptr_t>(res.ptr);
-                if (ranges_overlap(pd, dst_len, pr, res_bytes) && !(res_kind == 1 && pr == pd)) {
+                if (ranges_overlap(pd, dst_len, pr, res_bytes) && !(res_kind == 1 && pr == pd && same_res_layout)) {
                     return AR_ERR_INVALID;
                 }
             }
@@ -214,21 +256,39 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         plan->active_mask = active;
         plan->src_bytes = src_bytes;
         plan->wire_bytes = wire_bytes;
-        size_t chunk;
-        if (resolved == AR_MODE_HOST_STAGED) {
-            size_t hb = cfg.host_chunk_bytes;
-            if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, src_len / 4));
-            chunk = hb / static_cast<size_t>(src_bytes);
+        const size_t algo_src = n * static_cast<size_t>(src_bytes);
+        const size_t algo_dst = n * static_cast<size_t>(dst_bytes);
+        size_t algo_res = 0;
+        if (res_kind == 1) algo_res = n * static_cast<size_t>(dst_bytes);
+        if (res_kind == 2) algo_res = (rows ? rows->cols : res.len) * static_cast<size_t>(dst_bytes);
+        if (rows != nullptr) {
+            // one range per row on the device; host-staged copies move whole rows
+            size_t chunk_rows = 1;
+            if (resolved == AR_MODE_HOST_STAGED && rows->cols > 0) {
+                size_t hb = cfg.host_chunk_bytes;
+                if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, algo_src / 4));
+                chunk_rows = std::max<size_t>(1, hb / (rows->cols * static_cast<size_t>(src_bytes)));
+                chunk_rows = std::min(chunk_rows, std::max<size_t>(1, mpp::kMaxLaunchElems / rows->cols));
+            }
+            plan->chunk_elems = chunk_rows * rows->cols;
+            plan->n_chunks = n == 0 ? 0 : (rows->rows + chunk_rows - 1) / chunk_rows;
         } else {
-            chunk = cfg.chunk_bytes / static_cast<size_t>(wire_bytes);
+            size_t chunk;
+            if (resolved == AR_MODE_HOST_STAGED) {
+                size_t hb = cfg.host_chunk_bytes;
+                if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, src_len / 4));
+                chunk = hb / static_cast<size_t>(src_bytes);
+            } else {
+                chunk = cfg.chunk_bytes / static_cast<size_t>(wire_bytes);
+            }
+            chunk = round_down(chunk, mpp::kWaveTile);
+            if (chunk < mpp::kWaveTile) chunk = mpp::kWaveTile;
+            if (chunk > mpp::kMaxLaunchElems) chunk = mpp::kMaxLaunchElems;
+            if (resolved == AR_MODE_SINGLE_SHOT) chunk = n > 0 ? n : 1;
+            plan->chunk_elems = chunk;
+            plan->n_chunks = n == 0 ? 0 : (n + chunk - 1) / chunk;
         }
-        chunk = round_down(chunk, mpp::kWaveTile);
-        if (chunk < mpp::kWaveTile) chunk = mpp::kWaveTile;
-        if (chunk > mpp::kMaxLaunchElems) chunk = mpp::kMaxLaunchElems;
-        if (resolved == AR_MODE_SINGLE_SHOT) chunk = n > 0 ? n : 1;
-        plan->chunk_elems = chunk;
-        plan->n_chunks = n == 0 ? 0 : (n + chunk - 1) / chunk;
-        if (resolved == AR_MODE_RS_BCAST) {
+        if (resolved == AR_MODE_RS_BCAST && rows == nullptr) {
             // rank r owns [floor(r n / R), floor((r+1) n / R)), boundaries on wave tiles
             for (int r = 0; r < R; ++r) {
                 const size_t s = round_down(static_cast<size_t>(r) * (n / R) + (static_cast<size_t>(r) * (n % R)) / R,
@@ -241,7 +301,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 plan->slice_len[r] = e - s;
             }
         }
-        plan->algo_bytes = static_cast<size_t>(R) * src_len + static_cast<size_t>(n_dst) * dst_len + res_bytes;
+        plan->algo_bytes = static_cast<size_t>(R) * algo_src + static_cast<size_t>(n_dst) * algo_dst + algo_res;
         plan->dst_bytes = dst_bytes;
         plan->residual_kind = res_kind;
         // Automatic store policy, measured on MI355X: when the call writes at
@@ -249,8 +309,8 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // sources at R = 2) non-temporal stores are faster; when reads dominate,
         // ordinary write-back stores drain from L2 / Infinity Cache while the
         // reads stream and are faster.
-        const size_t written = static_cast<size_t>(n_dst) * dst_len;
-        const size_t read = static_cast<size_t>(R) * src_len + (res_kind == 1 ? res_bytes : 0);
+        const size_t written = static_cast<size_t>(n_dst) * algo_dst;
+        const size_t read = static_cast<size_t>(R) * algo_src + (res_kind == 1 ? algo_res : 0);
         plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written >= read);
         // host-staged sources: copy-engine pipeline (1) or the kernel reading
         // the pinned buffers over PCIe directly (2)
@@ -465,6 +525,45 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
     return AR_OK;
 }
 
+// Row-strided calls on the device (SINGLE_SHOT / CHUNKED / RS_BCAST, and
+// host-staged calls that read the pinned rows directly): gridDim.y = rows,
+// at most 65535 per launch, each row walked like a 1-D range.  The broadcast
+// schedule writes every row to all R destinations (its rows are spread over
+// the grid instead of per-rank slices; the bytes are the same).
+int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, const Rows &rw,
+             int wire_type, const Residual &res, hipStream_t stream) {
+    const mpp::Family family = plan.mode == AR_MODE_SINGLE_SHOT ? mpp::Family::SingleShot : stream_family(plan);
+    const mpp::Types types = launch_types(plan, wire_type);
+    const size_t sb = static_cast<size_t>(plan.src_bytes);
+    const size_t db = static_cast<size_t>(plan.dst_bytes);
+    constexpr size_t kMaxRows = 65535;
+    for (size_t r0 = 0; r0 < rw.rows; r0 += kMaxRows) {
+        const size_t nr = std::min(kMaxRows, rw.rows - r0);
+        mpp::KernelArgs a{};
+        a.R = R;
+        a.n_dst = plan.n_dst;
+        a.n = nr * rw.cols;
+        a.cols = static_cast<unsigned>(rw.cols);
+        a.src_stride = rw.src_stride;
+        a.dst_stride = rw.dst_stride;
+        a.store_nt = plan.mode == AR_MODE_SINGLE_SHOT ? 0 : plan.store_nt;
+        a.active = plan.active_mask;
+        for (int r = 0; r < R; ++r) {
+            a.src[r] = srcs[r] == nullptr ? nullptr : static_cast<const char *>(srcs[r]) + r0 * rw.src_stride * sb;
+        }
+        for (int d = 0; d < plan.n_dst; ++d) a.dst[d] = static_cast<char *>(dst[d]) + r0 * rw.dst_stride * db;
+        if (res.ptr != nullptr) {
+            a.res = static_cast<const char *>(res.ptr) + r0 * rw.res_stride * db;
+            a.res_stride = rw.res_stride;
+            a.res_reuse = rw.res_stride == 0 ? 1 : 0;
+        }
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(rw.cols),
+                                                       static_cast<unsigned>(nr), c->cu_count, c->cfg.grid_wgs);
+        if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
+    }
+    return AR_OK;
+}
+
 int ensure_scratch(ar_ctx *c, size_t bytes) {
     if (c->scratch_bytes >= bytes) return AR_OK;
     // the old ring may still be read by enqueued kernels or written by copies
@@ -540,6 +639,64 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(len), 1,
                                                        c->cu_count, c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
+        if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
+        c->slot_used[slot] = 1;
+    }
+    return AR_OK;
+}
+
+// HOST_STAGED for row-strided sources: the copy engine moves chunks of rows
+// with 2-D copies (row pitch = the source stride, packed into HBM scratch at
+// pitch cols), then the add kernel reads the packed rows and writes the
+// strided destination rows -- the same slot / event ring as the 1-D form.
+int run_host_staged_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R,
+                         const Rows &rw, int wire_type, const Residual &res, hipStream_t stream) {
+    const size_t sb = static_cast<size_t>(plan.src_bytes);
+    const size_t chunk_rows = plan.chunk_elems / rw.cols;
+    const size_t K = static_cast<size_t>(c->cfg.host_slots);
+    const size_t rank_stride = chunk_rows * rw.cols * sb;
+    const size_t slot_stride = rank_stride * static_cast<size_t>(R);
+    if (int rc = ensure_scratch(c, slot_stride * K)) return rc;
+
+    if (hipEventRecord(c->ev_start, stream) != hipSuccess) return AR_ERR_RUNTIME;
+    if (hipStreamWaitEvent(c->copy_stream, c->ev_start, 0) != hipSuccess) return AR_ERR_RUNTIME;
+
+    for (size_t r0 = 0; r0 < rw.rows; r0 += chunk_rows) {
+        const size_t nr = std::min(chunk_rows, rw.rows - r0);
+        const unsigned slot = c->next_slot;
+        c->next_slot = (c->next_slot + 1) % static_cast<unsigned>(K);
+        char *slot_base = static_cast<char *>(c->scratch) + slot * slot_stride;
+        if (c->slot_used[slot] && hipStreamWaitEvent(c->copy_stream, c->ev_free[slot], 0) != hipSuccess) {
+            return AR_ERR_RUNTIME;
+        }
+        const void *packed[AR_MAX_RANKS];
+        for (int r = 0; r < R; ++r) {
+            packed[r] = nullptr;
+            if (srcs[r] == nullptr) continue;   // inactive rank: nothing crosses PCIe
+            if (hipMemcpy2DAsync(slot_base + r * rank_stride, rw.cols * sb,
+                                 static_cast<const char *>(srcs[r]) + r0 * rw.src_stride * sb, rw.src_stride * sb,
+                                 rw.cols * sb, nr, hipMemcpyHostToDevice, c->copy_stream) != hipSuccess) {
+                return AR_ERR_RUNTIME;
+            }
+            packed[r] = slot_base + r * rank_stride;
+        }
+        if (hipEventRecord(c->ev_h2d[slot], c->copy_stream) != hipSuccess) return AR_ERR_RUNTIME;
+        if (hipStreamWaitEvent(stream, c->ev_h2d[slot], 0) != hipSuccess) return AR_ERR_RUNTIME;
+
+        Rows part = rw;
+        part.rows = nr;
+        part.src_stride = rw.cols;
+        void *dst_part[AR_MAX_RANKS];
+        for (int d = 0; d < plan.n_dst; ++d) {
+            dst_part[d] = static_cast<char *>(dst[d]) + r0 * rw.dst_stride * static_cast<size_t>(plan.dst_bytes);
+        }
+        Residual res_part = res;
+        if (res.ptr != nullptr) {
+            res_part.ptr = static_cast<const char *>(res.ptr) + r0 * rw.res_stride * static_cast<size_t>(plan.dst_bytes);
+        }
+        ar_plan kernel_plan = plan;
+        kernel_plan.mode = AR_MODE_CHUNKED;
+        if (int rc = run_rows(c, kernel_plan, dst_part, packed, R, part, wire_type, res_part, stream)) return rc;
         if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
         c->slot_used[slot] = 1;
     }
@@ -637,16 +794,23 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
 namespace {
 
 int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
-                int wire_type, unsigned mode, const Residual &res, void *hip_stream) {
+                int wire_type, unsigned mode, const Residual &res, const Rows *rows, void *hip_stream) {
     if (ctx == nullptr) return AR_ERR_INVALID;
     // cheap checks first, without touching the runtime
     ar_plan plan;
     const bool auto_mode = (mode & AR_MODE_MASK) == AR_MODE_AUTO;
-    int rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, res, false, &plan);
+    int rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, res, false, &plan, rows);
     if (rc != AR_OK) return rc;
 
-    const size_t src_len = n * static_cast<size_t>(plan.src_bytes);
-    const size_t dst_len = n * static_cast<size_t>(plan.dst_bytes);
+    // bytes each tensor spans, for the memory-kind and range checks
+    const size_t src_len = (rows ? extent(rows->rows, rows->cols, rows->src_stride) : n) *
+                           static_cast<size_t>(plan.src_bytes);
+    const size_t dst_len = (rows ? extent(rows->rows, rows->cols, rows->dst_stride) : n) *
+                           static_cast<size_t>(plan.dst_bytes);
+    size_t res_len = res.len;
+    if (rows != nullptr) {
+        res_len = rows->res_stride == 0 ? rows->cols : extent(rows->rows, rows->cols, rows->res_stride);
+    }
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return AR_ERR_RUNTIME;
@@ -660,7 +824,7 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
         const Kind k0 = memory_kind(srcs[first_active], src_len, ctx->device);
         if (k0 == Kind::Other) return AR_ERR_INVALID;
         if (auto_mode && k0 == Kind::PinnedHost) {
-            rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, res, true, &plan);
+            rc = validate_and_plan(ctx->cfg, dst, srcs, R, n, dst_type, wire_type, mode, res, true, &plan, rows);
             if (rc != AR_OK) return rc;
         }
     }
@@ -677,11 +841,20 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
         if (memory_kind(dst[d], dst_len, ctx->device) != Kind::Device) return AR_ERR_INVALID;
     }
     if (res.ptr != nullptr &&
-        memory_kind(res.ptr, res.len * static_cast<size_t>(plan.dst_bytes), ctx->device) != Kind::Device) {
+        memory_kind(res.ptr, res_len * static_cast<size_t>(plan.dst_bytes), ctx->device) != Kind::Device) {
         return AR_ERR_INVALID;
     }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (rows != nullptr) {
+        if (plan.mode != AR_MODE_HOST_STAGED) return run_rows(ctx, plan, dst, srcs, R, *rows, wire_type, res, stream);
+        if (plan.host_direct) {
+            ar_plan direct = plan;
+            direct.mode = AR_MODE_CHUNKED;
+            return run_rows(ctx, direct, dst, src_view, R, *rows, wire_type, res, stream);
+        }
+        return run_host_staged_rows(ctx, plan, dst, srcs, R, *rows, wire_type, res, stream);
+    }
     if (plan.mode == AR_MODE_HOST_STAGED) {
         if (plan.host_direct) {
             // one streaming launch whose loads cross PCIe: the kernel reads the
@@ -699,7 +872,7 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
 
 AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
                      int wire_type, unsigned mode, void *hip_stream) {
-    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, hip_stream);
+    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, nullptr, hip_stream);
 }
 
 AR_API int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
@@ -708,7 +881,55 @@ AR_API int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs,
     Residual res;
     res.ptr = residual;
     res.len = residual_len;
-    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, res, hip_stream);
+    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, res, nullptr, hip_stream);
+}
+
+namespace {
+
+// An ar_rows shape as the internal form, with n = rows x cols; false if the
+// element count overflows.
+bool rows_of(const ar_rows *shape, Rows *rw, size_t *n) {
+    rw->rows = shape->rows;
+    rw->cols = shape->cols;
+    rw->src_stride = shape->src_stride;
+    rw->dst_stride = shape->dst_stride;
+    rw->res_stride = shape->res_stride;
+    if (rw->cols != 0 && rw->rows > SIZE_MAX / rw->cols) return false;
+    *n = rw->rows * rw->cols;
+    // the furthest element any tensor reaches must stay addressable
+    const size_t strides[3] = {rw->src_stride, rw->dst_stride, rw->res_stride};
+    for (size_t st : strides) {
+        if (rw->rows > 1 && st > (SIZE_MAX / 16) / rw->rows) return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+AR_API int ar_reduce_rows(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, const ar_rows *shape,
+                          int dst_type, int wire_type, unsigned mode, const void *residual, void *hip_stream) {
+    if (ctx == nullptr || shape == nullptr) return AR_ERR_INVALID;
+    Rows rw;
+    size_t n = 0;
+    if (!rows_of(shape, &rw, &n)) return AR_ERR_INVALID;
+    Residual res;
+    res.ptr = residual;
+    res.len = 0;
+    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, res, &rw, hip_stream);
+}
+
+AR_API int ar_plan_query_rows(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
+                              const ar_rows *shape, int dst_type, int wire_type, unsigned mode, const void *residual,
+                              int srcs_on_host, ar_plan *plan) {
+    Config c;
+    if (int rc = resolve_config(cfg, &c)) return rc;
+    if (shape == nullptr) return AR_ERR_INVALID;
+    Rows rw;
+    size_t n = 0;
+    if (!rows_of(shape, &rw, &n)) return AR_ERR_INVALID;
+    Residual res;
+    res.ptr = residual;
+    return validate_and_plan(c, dst, srcs, R, n, dst_type, wire_type, mode, res, srcs_on_host != 0, plan, &rw);
 }
 
 AR_API int ar_free(ar_ctx *ctx) {

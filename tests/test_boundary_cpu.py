@@ -23,8 +23,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ar.load_library()
     names = declared_functions()
-    assert {"ar_init", "ar_reduce", "ar_reduce_add", "ar_free", "ar_status_str", "ar_plan_query",
-            "ar_plan_query_add"} <= set(names)
+    assert {"ar_init", "ar_reduce", "ar_reduce_add", "ar_reduce_rows", "ar_free", "ar_status_str",
+            "ar_plan_query", "ar_plan_query_add", "ar_plan_query_rows"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in ar.h but not exported"
 
@@ -307,3 +307,57 @@ def test_residual_rules():
     dsts = (ctypes.c_void_p * 1)(A[30])
     assert lib.ar_reduce_add(None, dsts, srcs, 2, 64, ar.AR_F32, ar.AR_BF16, 0, A[35], 64, None) == \
         ar.AR_ERR_INVALID
+
+
+def qr(rows, cols, ss, ds, R=2, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_F32, res=None, rs=0,
+       dsts=None, srcs=None, host=False, config=None):
+    srcs = A[1:1 + R] if srcs is None else srcs
+    dsts = [A[20 + d] for d in range(R)] if dsts is None else dsts
+    return ar.ar_plan_query_rows(dsts, srcs, rows, cols, ss, ds, dst_type, wire, mode, res, rs, host, config,
+                                 R=len(srcs))
+
+
+def test_row_strided_rules():
+    assert ctypes.sizeof(ar.ArRows) == 5 * 8
+    # a 2048 x 4096 block inside rows of 4608: the algorithmic bytes count the block only
+    rc, p = qr(2048, 4096, 4608, 4608)
+    assert rc == ar.AR_OK and p.chunk_elems == 4096 and p.n_chunks == 2048
+    assert p.algo_bytes == 2 * 2048 * 4096 * 4 + 2048 * 4096 * 4
+    # strides shorter than a row, or row starts off 16 bytes
+    assert qr(4, 64, 60, 64)[0] == ar.AR_ERR_INVALID
+    assert qr(4, 64, 64, 60)[0] == ar.AR_ERR_INVALID
+    assert qr(4, 64, 66, 64)[0] == ar.AR_ERR_INVALID            # 66 * 4 B is not a multiple of 16
+    assert qr(4, 64, 68, 64)[0] == ar.AR_OK
+    assert qr(4, 64, 68, 68, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[0] == ar.AR_ERR_INVALID  # 68 * 2 B
+    assert qr(4, 64, 72, 68, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[0] == ar.AR_OK
+    # residual: element-wise stride or one broadcast row
+    rc, p = qr(16, 4096, 4096, 4096, res=A[35], rs=4096)
+    assert rc == ar.AR_OK and p.residual_kind == 1 and p.stream_kernel == 1
+    rc, p = qr(16, 4096, 4096, 4096, res=A[35], rs=0)
+    assert rc == ar.AR_OK and p.residual_kind == 2
+    assert p.algo_bytes == 2 * 16 * 4096 * 4 + 16 * 4096 * 4 + 4096 * 4
+    assert qr(16, 4096, 4096, 4096, res=A[35], rs=100)[0] == ar.AR_ERR_INVALID
+    # overlaps judged on spans: interleaved rows of a source and the destination
+    n_span = 3 * 128 + 64
+    assert qr(4, 64, 128, 128, dsts=[A[1] + 64 * 4])[0] == ar.AR_ERR_INVALID
+    assert qr(4, 64, 128, 128, dsts=[A[1] + n_span * 4])[0] == ar.AR_OK
+    # exactly in place needs equal strides
+    assert qr(4, 64, 128, 128, dsts=[A[1]])[0] == ar.AR_OK
+    assert qr(4, 64, 128, 64, dsts=[A[1]])[0] == ar.AR_ERR_INVALID
+    # broadcast schedule: every row to all R destinations, no per-rank slices
+    rc, p = qr(8, 4096, 4096, 4096, R=4, mode=ar.AR_MODE_RS_BCAST, wire=ar.AR_F16)
+    assert rc == ar.AR_OK and p.n_dst == 4 and all(p.slice_len[r] == 0 for r in range(4))
+    # host-staged: chunks of whole rows
+    rc, p = qr(8192, 8192, 8192, 8192, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE)
+    assert rc == ar.AR_OK and p.chunk_elems % 8192 == 0 and p.chunk_elems // 8192 == (16 * MiB) // (8192 * 2)
+    # a row longer than one launch covers
+    assert qr(1, (1 << 30) + 8, (1 << 30) + 8, (1 << 30) + 8)[0] == ar.AR_ERR_UNSUPPORTED
+    # empty shapes are no-ops
+    assert qr(0, 64, 64, 64)[0] == ar.AR_OK
+    assert qr(5, 0, 0, 0)[0] == ar.AR_OK
+    # a NULL shape
+    lib = ar.load_library()
+    srcs = (ctypes.c_void_p * 2)(*A[1:3])
+    dsts = (ctypes.c_void_p * 1)(A[30])
+    assert lib.ar_plan_query_rows(None, dsts, srcs, 2, None, 0, 2, 2, None, 0, None) == ar.AR_ERR_INVALID
+    assert lib.ar_reduce_rows(None, dsts, srcs, 2, None, 0, 2, 2, None, None) == ar.AR_ERR_INVALID
