@@ -555,8 +555,13 @@ def other_schedules(torch, ar, wl):
         t = torch.empty(p.size, dtype=torch.int16, pin_memory=True)
         t.copy_(torch.from_numpy(p.view(np.int16)))
         pinned.append(t)
-    ms = timed(lambda: ar.ar_reduce(ctx, [dst], pinned, w.n, ar.AR_F32, w.wire,
+    ctx_copy = ar.ar_init(0, {"host_path": 1})
+    ms = timed(lambda: ar.ar_reduce(ctx_copy, [dst], pinned, w.n, ar.AR_F32, w.wire,
                                     ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
+    ms_direct = timed(lambda: ar.ar_reduce(ctx, [dst], pinned, w.n, ar.AR_F32, w.wire,
+                                           ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
+    torch.cuda.synchronize()
+    ar.ar_free(ctx_copy)
     pcie_bytes = w.R * w.n * 2
     # plain pinned H2D copy of the same byte count, for the achievable PCIe ceiling
     big = torch.empty(pcie_bytes // 2, dtype=torch.int16, pin_memory=True)
@@ -564,8 +569,28 @@ def other_schedules(torch, ar, wl):
     ms_copy = timed(lambda: dev_big.copy_(big, non_blocking=True), 5)
     out["host_staged_bf16"] = {"ms": round(ms, 3), "pcie_GB/s": round(pcie_bytes / ms / 1e6, 2),
                                "h2d_copy_GB/s": round(pcie_bytes / ms_copy / 1e6, 2),
-                               "frac_of_h2d_copy": round(ms_copy / ms, 3)}
+                               "frac_of_h2d_copy": round(ms_copy / ms, 3), "path": "copy engine"}
+    out["host_direct_bf16"] = {"ms": round(ms_direct, 3), "pcie_GB/s": round(pcie_bytes / ms_direct / 1e6, 2),
+                               "frac_of_h2d_copy": round(ms_copy / ms_direct, 3), "path": "kernel reads pinned memory"}
     log(f"host_staged_bf16: {out['host_staged_bf16']}")
+    log(f"host_direct_bf16: {out['host_direct_bf16']}")
+    # decode-sized host-staged calls (one hidden vector per rank): latency of each path
+    hw = wl.WORKLOADS["decode_bf16"]
+    hsrc = []
+    for p in wl.partials(hw, 0):
+        t = torch.empty(hw.n, dtype=torch.int16, pin_memory=True)
+        t.copy_(torch.from_numpy(wl.as_wire_typed(p, hw.wire).view(np.int16)))
+        hsrc.append(t)
+    hdst = torch.empty(hw.n, dtype=torch.float32, device="cuda")
+    ctx_copy = ar.ar_init(0, {"host_path": 1})
+    us_copy = timed(lambda: ar.ar_reduce(ctx_copy, [hdst], hsrc, hw.n, ar.AR_F32, hw.wire,
+                                         ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 500) * 1e3
+    us_direct = timed(lambda: ar.ar_reduce(ctx, [hdst], hsrc, hw.n, ar.AR_F32, hw.wire,
+                                           ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 500) * 1e3
+    torch.cuda.synchronize()
+    ar.ar_free(ctx_copy)
+    out["host_decode_bf16"] = {"us_copy_engine": round(us_copy, 2), "us_direct": round(us_direct, 2)}
+    log(f"host_decode_bf16: {out['host_decode_bf16']}")
     ar.ar_free(ctx)
     return out
 

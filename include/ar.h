@@ -80,10 +80,11 @@ typedef enum { AR_F32 = 0, AR_F16 = 1, AR_BF16 = 2 } ar_dtype;
  *   AR_MODE_RS_BCAST     per-rank slice schedule: simulated rank r reduces
  *                        its own slice and writes it to all R destinations
  *                        (n_dst = R; `dst` holds R pointers).
- *   AR_MODE_HOST_STAGED  sources are pinned host buffers; chunks are copied
- *                        to HBM scratch on an internal copy stream while the
- *                        add kernel runs on `hip_stream` (or, with host_path
- *                        2, the kernel reads the pinned buffers directly).
+ *   AR_MODE_HOST_STAGED  sources are pinned host buffers; by default the add
+ *                        kernel reads them directly through their device
+ *                        mapping; with host_path 1, chunks are copied to HBM
+ *                        scratch on an internal copy stream while the add
+ *                        kernel runs on `hip_stream`.
  * The result bytes do not depend on the mode, the chunk size or the launch
  * shape. */
 enum {
@@ -122,7 +123,7 @@ typedef struct {
     size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank; 0 -> 1 MiB */
     size_t chunk_bytes;           /* CHUNKED / RS_BCAST plan unit, wire bytes per rank; 0 -> 4 MiB */
     size_t host_chunk_bytes;      /* HOST_STAGED copy unit, source bytes per rank;
-                                     0 -> clamp(bytes/4, 512 KiB, 16 MiB) per call */
+                                     0 -> clamp(bytes/2, 512 KiB, 64 MiB) per call */
     int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
     int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
     int    stream_kernel;         /* 0 auto (LDS-staged for the broadcast schedule and
@@ -133,9 +134,12 @@ typedef struct {
                                      call writes at least as many bytes as it
                                      reads), 1 cached write-back, 2 streaming
                                      (non-temporal) */
-    int    host_path;             /* HOST_STAGED: 0 auto, 1 copy-engine chunks into HBM
-                                     scratch, 2 the kernel reads the pinned buffers
-                                     directly over PCIe (no scratch) */
+    int    host_path;             /* HOST_STAGED: 0 auto (= 2), 1 copy-engine chunks
+                                     into HBM scratch on the internal copy stream,
+                                     overlapped with the add kernel (the CUs stay
+                                     free while bytes cross PCIe), 2 the kernel reads
+                                     the pinned buffers directly over PCIe (no
+                                     scratch, lowest latency) */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.
@@ -225,9 +229,9 @@ typedef struct {
  * Every base pointer must be 16-byte aligned and every stride keep row starts
  * 16-byte aligned (AR_ERR_INVALID otherwise).  AR_MODE_RS_BCAST writes every
  * row to all R destinations (the rows are spread over the workgroups, not cut
- * into per-rank slices; the bytes are the same).  AR_MODE_HOST_STAGED copies
- * chunks of whole rows with 2-D copy-engine transfers (host_path 2: the kernel
- * reads the pinned rows directly).  Exactly in place needs equal strides;
+ * into per-rank slices; the bytes are the same).  AR_MODE_HOST_STAGED reads the
+ * pinned rows directly, or (host_path 1) copies chunks of whole rows with 2-D
+ * copy-engine transfers.  Exactly in place needs equal strides;
  * overlaps are judged on each tensor's span from its first to its last
  * element.  Ownership and the remaining error codes are those of ar_reduce
  * and ar_reduce_add; cols > 2^30 -> AR_ERR_UNSUPPORTED. */

@@ -38,11 +38,12 @@ namespace {
 constexpr size_t kMiB = size_t(1) << 20;
 constexpr size_t kDefaultSingleShotMax = 1 * kMiB;
 constexpr size_t kDefaultChunkBytes = 4 * kMiB;
-// Host-staged copy chunk: clamp(bytes per rank / 4, 512 KiB, 16 MiB) of source
-// bytes per rank -- about four chunks in flight, each large enough that the
-// fixed cost of a copy is small next to its transfer time over PCIe.
+// Host-staged copy chunk: clamp(bytes per rank / 2, 512 KiB, 64 MiB) of source
+// bytes per rank -- two chunks or more, each large: measured on MI355X the
+// fixed cost per copy outweighs the overlap that many small chunks would buy
+// (the add kernel of a chunk is ~100x shorter than its copy over PCIe).
 constexpr size_t kHostChunkMin = 512 * 1024;
-constexpr size_t kHostChunkMax = 16 * kMiB;
+constexpr size_t kHostChunkMax = 64 * kMiB;
 constexpr int kDefaultHostSlots = 3;
 
 constexpr int kMaxHostSlots = 64;
@@ -266,7 +267,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             size_t chunk_rows = 1;
             if (resolved == AR_MODE_HOST_STAGED && rows->cols > 0) {
                 size_t hb = cfg.host_chunk_bytes;
-                if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, algo_src / 4));
+                if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, algo_src / 2));
                 chunk_rows = std::max<size_t>(1, hb / (rows->cols * static_cast<size_t>(src_bytes)));
                 chunk_rows = std::min(chunk_rows, std::max<size_t>(1, mpp::kMaxLaunchElems / rows->cols));
             }
@@ -276,7 +277,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             size_t chunk;
             if (resolved == AR_MODE_HOST_STAGED) {
                 size_t hb = cfg.host_chunk_bytes;
-                if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, src_len / 4));
+                if (hb == 0) hb = std::min(kHostChunkMax, std::max(kHostChunkMin, src_len / 2));
                 chunk = hb / static_cast<size_t>(src_bytes);
             } else {
                 chunk = cfg.chunk_bytes / static_cast<size_t>(wire_bytes);
@@ -314,7 +315,11 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written >= read);
         // host-staged sources: copy-engine pipeline (1) or the kernel reading
         // the pinned buffers over PCIe directly (2)
-        plan->host_direct = resolved == AR_MODE_HOST_STAGED && cfg.host_path == 2;
+        // (automatic: direct reads -- measured on MI355X they match the best
+        // copy-engine pipeline for large calls and are 7x faster for
+        // decode-sized ones, 5.4 against 37 us; the copy engine leaves the CUs
+        // free for other streams while the bytes cross PCIe)
+        plan->host_direct = resolved == AR_MODE_HOST_STAGED && cfg.host_path != 1;
         // streaming kernel family: explicit choice, else measured on MI355X
         // with inputs that are not in any cache -- the LDS-staged kernel for
         // the broadcast schedule (R loads per lane staged in LDS instead of

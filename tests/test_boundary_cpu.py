@@ -150,19 +150,21 @@ def test_slice_plan_partitions_range():
 
 
 def test_host_chunk_heuristic():
-    # clamp(bytes / 4, 512 KiB, 16 MiB) of source bytes per rank
+    # clamp(bytes / 2, 512 KiB, 64 MiB) of source bytes per rank
     n = 8192 * 8192
     rc, p = q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
-    assert p.chunk_elems == (16 * MiB) // 2 and p.n_chunks == n // ((16 * MiB) // 2)
-    assert p.host_direct == 0
-    rc, p = q(n // 4, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
-    assert p.chunk_elems == (n // 4 * 2 // 4) // 2
-    rc, p = q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, config={"host_path": 2})
-    assert p.host_direct == 1
+    assert p.chunk_elems == (n * 2 // 2) // 2 and p.n_chunks == 2
+    rc, p = q(4 * n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, wire=ar.AR_BF16)
+    assert p.chunk_elems == (64 * MiB) // 2
     rc, p = q(100_000, mode=ar.AR_MODE_HOST_STAGED)
     assert p.chunk_elems == (512 * 1024) // 4
     rc, p = q(n, mode=ar.AR_MODE_HOST_STAGED, config={"host_chunk_bytes": 1 << 16})
     assert p.chunk_elems == (1 << 16) // 4
+    # direct reads of the pinned buffers by default; the copy-engine pipeline on request
+    assert q(n, R=8, mode=ar.AR_MODE_HOST_STAGED)[1].host_direct == 1
+    assert q(n, R=8, mode=ar.AR_MODE_HOST_STAGED, config={"host_path": 2})[1].host_direct == 1
+    assert q(n, R=8, mode=ar.AR_MODE_HOST_STAGED, config={"host_path": 1})[1].host_direct == 0
+    assert q(n, R=8, mode=ar.AR_MODE_CHUNKED)[1].host_direct == 0
 
 
 def test_bad_config_rejected():
@@ -349,7 +351,7 @@ def test_row_strided_rules():
     assert rc == ar.AR_OK and p.n_dst == 4 and all(p.slice_len[r] == 0 for r in range(4))
     # host-staged: chunks of whole rows
     rc, p = qr(8192, 8192, 8192, 8192, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE)
-    assert rc == ar.AR_OK and p.chunk_elems % 8192 == 0 and p.chunk_elems // 8192 == (16 * MiB) // (8192 * 2)
+    assert rc == ar.AR_OK and p.chunk_elems % 8192 == 0 and p.chunk_elems // 8192 == (64 * MiB) // (8192 * 2)
     # a row longer than one launch covers
     assert qr(1, (1 << 30) + 8, (1 << 30) + 8, (1 << 30) + 8)[0] == ar.AR_ERR_UNSUPPORTED
     # empty shapes are no-ops

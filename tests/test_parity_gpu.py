@@ -139,11 +139,11 @@ def test_host_staged_bf16_and_hbm(ctx):
     want_wire = oracle.reduce(pre, w.wire, src_type=w.wire)[0]
     outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_HOST_STAGED, src_wire=True)
     assert_bits_equal(outs[0], want_wire, "host_staged bf16")
-    log_case("host_staged_bf16 direct reads of pinned memory")
-    c = ar.ar_init(0, {"host_path": 2})
+    log_case("host_staged_bf16 copy-engine pipeline")
+    c = ar.ar_init(0, {"host_path": 1})
     try:
         outs, _ = run_case(ctx, pre, w.wire, ar.AR_MODE_HOST_STAGED, src_wire=True, config_ctx=c)
-        assert_bits_equal(outs[0], want_wire, "host_staged bf16 direct")
+        assert_bits_equal(outs[0], want_wire, "host_staged bf16 copy engine")
     finally:
         torch.cuda.synchronize()
         ar.ar_free(c)
@@ -165,11 +165,12 @@ TAIL_N = [1, 3, 7, 8, 9, 63, 64, 65, 511, 512, 513, 1023, 1025, 2047, 2048, 2049
 
 
 # Kernel instances: register / LDS-staged streaming family x cached / streaming stores
+# (host-staged calls in the first four go through the copy-engine pipeline)
 KERNEL_CONFIGS = {
-    "reg_cached": {"stream_kernel": 1, "store_policy": 1},
-    "reg_streaming": {"stream_kernel": 1, "store_policy": 2},
-    "lds_cached": {"stream_kernel": 2, "store_policy": 1},
-    "lds_streaming": {"stream_kernel": 2, "store_policy": 2},
+    "reg_cached": {"stream_kernel": 1, "store_policy": 1, "host_path": 1},
+    "reg_streaming": {"stream_kernel": 1, "store_policy": 2, "host_path": 1},
+    "lds_cached": {"stream_kernel": 2, "store_policy": 1, "host_path": 1},
+    "lds_streaming": {"stream_kernel": 2, "store_policy": 2, "host_path": 1},
     "host_direct": {"host_path": 2},
 }
 
@@ -321,7 +322,7 @@ def test_non_default_stream(ctx):
 def test_host_staged_back_to_back(ctx, slots):
     """Several host-staged calls enqueued without a sync in between, small chunks,
     few slots: a missing wait on slot reuse would mix chunks of different calls."""
-    c = ar.ar_init(0, {"host_slots": slots, "host_chunk_bytes": 1 << 16})
+    c = ar.ar_init(0, {"host_slots": slots, "host_chunk_bytes": 1 << 16, "host_path": 1})
     try:
         n, R, calls = 200_000 + slots, 3, 4
         inputs = [wl.random_partials(7000 + slots, k, R, n) for k in range(calls)]

@@ -28,14 +28,15 @@ MODES = {
 WIRES = {"f32": ar.AR_F32, "bf16": ar.AR_BF16, "f16": ar.AR_F16}
 NARROW = {"bf16": ar.AR_BF16, "f16": ar.AR_F16}
 
+# (host-staged calls go through the copy-engine pipeline where host_path is 1)
 KERNEL_CONFIGS = {
     "default": {},
-    "reg_cached": {"stream_kernel": 1, "store_policy": 1},
-    "reg_streaming": {"stream_kernel": 1, "store_policy": 2},
-    "lds_cached": {"stream_kernel": 2, "store_policy": 1},
-    "lds_streaming": {"stream_kernel": 2, "store_policy": 2},
+    "reg_cached": {"stream_kernel": 1, "store_policy": 1, "host_path": 1},
+    "reg_streaming": {"stream_kernel": 1, "store_policy": 2, "host_path": 1},
+    "lds_cached": {"stream_kernel": 2, "store_policy": 1, "host_path": 1},
+    "lds_streaming": {"stream_kernel": 2, "store_policy": 2, "host_path": 1},
     "host_direct": {"host_path": 2},
-    "small_chunks": {"chunk_bytes": 4096, "host_chunk_bytes": 1 << 14},
+    "small_chunks": {"chunk_bytes": 4096, "host_chunk_bytes": 1 << 14, "host_path": 1},
 }
 
 

@@ -30,12 +30,13 @@ MODES = {
     "host_staged": ar.AR_MODE_HOST_STAGED,
 }
 WIRES = {"f32": ar.AR_F32, "bf16": ar.AR_BF16, "f16": ar.AR_F16}
+# (host-staged calls go through the 2-D copy-engine pipeline where host_path is 1)
 KERNEL_CONFIGS = {
     "default": {},
-    "reg_streaming": {"stream_kernel": 1, "store_policy": 2},
-    "lds_cached": {"stream_kernel": 2, "store_policy": 1},
+    "reg_streaming": {"stream_kernel": 1, "store_policy": 2, "host_path": 1},
+    "lds_cached": {"stream_kernel": 2, "store_policy": 1, "host_path": 1},
     "host_direct": {"host_path": 2},
-    "small_chunks": {"host_chunk_bytes": 1 << 13},
+    "small_chunks": {"host_chunk_bytes": 1 << 13, "host_path": 1},
 }
 
 
