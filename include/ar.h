@@ -132,7 +132,9 @@ typedef struct {
                                      1 register-staged, 2 LDS-staged */
     int    store_policy;          /* destination stores: 0 auto (streaming when the
                                      call writes at least as many bytes as it
-                                     reads), 1 cached write-back, 2 streaming
+                                     reads, kept otherwise), 1 kept in the cache
+                                     hierarchy (device-scope write-through for fp32
+                                     sources, write-back for 16-bit ones), 2 streaming
                                      (non-temporal) */
     int    host_path;             /* HOST_STAGED: 0 auto (= 2), 1 copy-engine chunks
                                      into HBM scratch on the internal copy stream,

@@ -308,8 +308,9 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // Automatic store policy, measured on MI355X: when the call writes at
         // least as many bytes as it reads (broadcast to R destinations, 16-bit
         // sources at R = 2) non-temporal stores are faster; when reads dominate,
-        // ordinary write-back stores drain from L2 / Infinity Cache while the
-        // reads stream and are faster.
+        // stores kept in the cache hierarchy are (write-through for fp32
+        // sources, so the writes overlap the reads instead of waiting in L2
+        // for the end of the kernel; write-back for the 16-bit layouts).
         const size_t written = static_cast<size_t>(n_dst) * algo_dst;
         const size_t read = static_cast<size_t>(R) * algo_src + (res_kind == 1 ? algo_res : 0);
         plan->store_nt = cfg.store_policy == 2 || (cfg.store_policy == 0 && written >= read);

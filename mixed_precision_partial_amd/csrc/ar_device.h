@@ -86,9 +86,45 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
     }
 }
 
-template <bool NT>
+// Destination store policies (a template value along the store path):
+//   kStoreKeep   through the caches: device-scope write-through (sc1) for
+//                binary32 sources, whose store instructions each write 1 KiB
+//                of whole lines; write-back for the 16-bit layouts.  Measured
+//                on MI355X, write-through beats write-back for read-dominated
+//                calls (prefill reduce 16.2 against 16.8 us, R = 8 fp32
+//                partials 368 against 383 us): with write-back the dirty lines
+//                wait in L2 and the end-of-kernel writeback of up to the whole
+//                L2 runs after the last wave, a 3 us gap before the next
+//                kernel; with write-through that traffic overlaps the reads.
+//                16-bit sources into binary32 store half lines per
+//                instruction, which write-back merges in L2 (write-through
+//                doubled their time), and 16-bit destinations measured no
+//                gain.
+//   kStoreStream non-temporal stores (calls that write as much as they read).
+//   kStoreBack   ordinary write-back (the single-shot kernel).
+constexpr int kStoreKeep = 0;
+constexpr int kStoreStream = 1;
+constexpr int kStoreBack = 2;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Third dword of a raw buffer resource on gfx9-family parts (untyped 32-bit
+// data, no swizzle, no thread-id addressing).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// 16-byte store with the device-scope write-through cache policy (sc1): a
+// buffer store, which the compiler schedules and tracks like any other store,
+// through a resource whose base is the wave-uniform start of the stored span
+// (`span_bytes` long) and a per-lane byte offset inside it.
+__device__ __forceinline__ void store16_wt(void *base, int span_bytes, unsigned off, u32x4 v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, span_bytes, kRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, static_cast<int>(off), 0, 16);
+}
+
+// 16-byte store: SP 0 write-back, 1 non-temporal.
+template <int SP>
 __device__ __forceinline__ void store16(void *p, u32x4 v) {
-    if constexpr (NT) {
+    if constexpr (SP == 1) {
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
     } else {
         *reinterpret_cast<u32x4 *>(p) = v;
@@ -264,19 +300,36 @@ __device__ __forceinline__ void round_dst(float (&acc)[8]) {
     }
 }
 
-template <class C, bool ST>
+template <class C, int ST>
 __device__ __forceinline__ void tile_store(void *dst, size_t t, int lane, const float (&acc)[8]) {
+    // write-through for the binary32-source layout (each store instruction
+    // covers 1 KiB contiguous); the 16-bit layouts measured better with
+    // write-back
+    constexpr int SP = ST == kStoreStream ? 1 : (ST == kStoreKeep && !C::SW ? 2 : 0);
     if constexpr (C::DN) {
         // the values already lie in the destination type: the packing is exact
         const u32x4 v = {round_pack<C::W>(acc[0], acc[1]), round_pack<C::W>(acc[2], acc[3]),
                          round_pack<C::W>(acc[4], acc[5]), round_pack<C::W>(acc[6], acc[7])};
-        store16<ST>(static_cast<uint16_t *>(dst) + t + 8 * lane, v);
-    } else {
+        store16<SP>(static_cast<uint16_t *>(dst) + t + 8 * lane, v);
+    } else if constexpr (C::SW) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const u32x4 v = {bits_from_f32(acc[4 * j]), bits_from_f32(acc[4 * j + 1]),
                              bits_from_f32(acc[4 * j + 2]), bits_from_f32(acc[4 * j + 3])};
-            store16<ST>(static_cast<float *>(dst) + part_elem<C>(t, lane, j), v);
+            store16<SP>(static_cast<float *>(dst) + part_elem<C>(t, lane, j), v);
+        }
+    } else {
+        // binary32 layout: the tile's 2 KiB start at the wave-uniform element t
+        float *base = static_cast<float *>(dst) + t;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 v = {bits_from_f32(acc[4 * j]), bits_from_f32(acc[4 * j + 1]),
+                             bits_from_f32(acc[4 * j + 2]), bits_from_f32(acc[4 * j + 3])};
+            if constexpr (SP == 2) {
+                store16_wt(base, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
+            } else {
+                store16<SP>(base + 256 * j + 4 * lane, v);
+            }
         }
     }
 }
@@ -338,7 +391,7 @@ __device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, const Ran
 
 // Fold one tile in rank order (one rounding to the destination type per add),
 // add the residual, and store to every destination at element `td`.
-template <class C, bool ST>
+template <class C, int ST>
 __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size_t td, int lane,
                                                 const u32x4 (&src)[C::RB][C::kSrcRaw], const u32x4 *res) {
     float acc[8];
@@ -380,12 +433,11 @@ __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size
 }
 
 // Fold each tile of the batch and store it before the next tile is folded.
-// Stores use ST (non-temporal for calls that write at least as much as they
-// read, ordinary write-back stores otherwise, which drain from L2 / Infinity
-// Cache while the next kernel reads).  The store policy is a template
-// parameter: two stores that differ only in their cache hint would be merged
-// into one by the compiler.
-template <class C, int U, bool ST>
+// Stores use the policy ST (streaming for calls that write at least as much
+// as they read, kept in the cache hierarchy otherwise; see kStoreKeep).  The
+// policy is a template parameter: two stores that differ only in their cache
+// hint would be merged into one by the compiler.
+template <class C, int U, int ST>
 __device__ __forceinline__ void fold_store(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
                                            const Batch<C, U> &b) {
 #pragma unroll
@@ -399,7 +451,7 @@ __device__ __forceinline__ void fold_store(const LaunchArgs<C::RB> &a, const Ran
     }
 }
 
-template <class C, int U, bool NT, bool ST>
+template <class C, int U, bool NT, int ST>
 __device__ __forceinline__ void reduce_tiles(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane) {
     Batch<C, U> b;
     load_batch<C, U, NT>(a, o, t, lane, b);
@@ -475,7 +527,7 @@ __device__ __forceinline__ void range_of(const A &a, RangeOff &o, unsigned &len)
 
 // Whole wave tiles after the batched part, then the element remainder on
 // wave 0 of workgroup 0 of the range.
-template <class C, int U, bool NT, bool ST>
+template <class C, int U, bool NT, int ST>
 __device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len,
                                             unsigned done, unsigned gw, unsigned nw, int lane) {
     if constexpr (U > 1) {
@@ -493,11 +545,13 @@ __device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, const Ra
 // Walk the wave tiles of this workgroup's range: batches of U tiles strided
 // over the `a.waves` waves of the range, then the remainder.  BLOCK is the
 // workgroup size the kernel is always launched with (no read of blockDim).
-template <class C, int U, bool NT, bool ST, int BLOCK, bool SLICED>
+template <class C, int U, bool NT, int ST, int BLOCK, bool SLICED>
 __device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a) {
     constexpr unsigned wpb = BLOCK / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const unsigned gw = blockIdx.x * wpb + threadIdx.x / kWave;
+    // the wave's index, read from lane 0 so the compiler keeps it (and every
+    // tile address derived from it) in scalar registers
+    const unsigned gw = blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const unsigned nw = a.waves;
     RangeOff o;
     unsigned len;
@@ -555,7 +609,7 @@ constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
     return u < 1 ? 1 : (u > MPP_STREAM_MAXU ? MPP_STREAM_MAXU : u);
 }
 
-template <class C, bool ST, bool SLICED>
+template <class C, int ST, bool SLICED>
 __device__ __forceinline__ void stream_reg(const LaunchArgs<C::RB> &a) {
     reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, stream_block(C::RB), SLICED>(a);
 }
@@ -651,7 +705,7 @@ __device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
     return v;
 }
 
-template <class C, int U, bool ST>
+template <class C, int U, int ST>
 __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
                                             u32x4 (*stage)[kWave]) {
     static_assert(!C::RES, "the LDS-staged kernel has no residual form");
@@ -670,7 +724,7 @@ __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const Ra
     fold_store<C, U, ST>(a, o, t, lane, b);
 }
 
-template <class C, bool ST, bool SLICED>
+template <class C, int ST, bool SLICED>
 __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
     constexpr int U = lds_batch(C::SW, C::RB);
     const int lane = threadIdx.x;
@@ -713,7 +767,7 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 
     reduce_rest<C, U, true, ST>(a, o, len, n_big * big, gw, nw, lane);
 }
 
-template <class C, bool ST, bool SLICED>
+template <class C, int ST, bool SLICED>
 __device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a) {
     constexpr int NB = C::RB * lds_batch(C::SW, C::RB) * C::kSrcRaw;   // 1 KiB blocks per stage
     __shared__ u32x4 stage0[NB][kWave];
@@ -723,12 +777,12 @@ __device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a) {
 
 // ---------------------------------------------------------------------------
 // Kernels.  Single-shot: one wave tile per wave.  Streaming (register-staged
-// or LDS-staged): ST = non-temporal stores, SLICED = the per-rank slice
+// or LDS-staged): ST = the store policy (kStoreKeep / kStoreStream), SLICED = the per-rank slice
 // ranges of the broadcast schedule.
 // ---------------------------------------------------------------------------
 template <class C>
 __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(LaunchArgs<C::RB> a) {
-    reduce_range<C, 1, false, false, kSingleShotBlock, false>(a);
+    reduce_range<C, 1, false, kStoreBack, kSingleShotBlock, false>(a);
 }
 
 #define MPP_STREAM_REG(NAME, ST, SLICED)                                   \
@@ -736,10 +790,10 @@ __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(LaunchArgs<C::
     __global__ __launch_bounds__(stream_block(C::RB)) void NAME(LaunchArgs<C::RB> a) { \
         stream_reg<C, ST, SLICED>(a);                                    \
     }
-MPP_STREAM_REG(k_stream_reg, false, false)
-MPP_STREAM_REG(k_stream_reg_nts, true, false)
-MPP_STREAM_REG(k_stream_reg_sl, false, true)
-MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
+MPP_STREAM_REG(k_stream_reg, kStoreKeep, false)
+MPP_STREAM_REG(k_stream_reg_nts, kStoreStream, false)
+MPP_STREAM_REG(k_stream_reg_sl, kStoreKeep, true)
+MPP_STREAM_REG(k_stream_reg_nts_sl, kStoreStream, true)
 #undef MPP_STREAM_REG
 
 #define MPP_STREAM_LDS(NAME, ST, SLICED)                                \
@@ -747,10 +801,10 @@ MPP_STREAM_REG(k_stream_reg_nts_sl, true, true)
     __global__ __launch_bounds__(kLdsBlock) void NAME(LaunchArgs<C::RB> a) { \
         stream_lds<C, ST, SLICED>(a);                                 \
     }
-MPP_STREAM_LDS(k_stream_lds, false, false)
-MPP_STREAM_LDS(k_stream_lds_nts, true, false)
-MPP_STREAM_LDS(k_stream_lds_sl, false, true)
-MPP_STREAM_LDS(k_stream_lds_nts_sl, true, true)
+MPP_STREAM_LDS(k_stream_lds, kStoreKeep, false)
+MPP_STREAM_LDS(k_stream_lds_nts, kStoreStream, false)
+MPP_STREAM_LDS(k_stream_lds_sl, kStoreKeep, true)
+MPP_STREAM_LDS(k_stream_lds_nts_sl, kStoreStream, true)
 #undef MPP_STREAM_LDS
 
 }  // namespace
