@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for hardware-counter collection: a few reduce steps, then a "
                         "plain elementwise copy of known size used to calibrate the counters")
+    p.add_argument("--profile-workload", default="prefill_bf16", choices=sorted(PROFILE_CASES),
+                   help="configuration the profile pass runs and the summaries describe")
     return p.parse_args()
 
 
@@ -85,9 +87,9 @@ def main() -> int:
     args = parse()
     if args.summarize_trace or args.summarize_pmc:
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace)
+            summarize_trace(args.summarize_trace, args.profile_workload)
         if args.summarize_pmc:
-            summarize_pmc(*args.summarize_pmc)
+            summarize_pmc(*args.summarize_pmc, args.profile_workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the reduce is run with every "
@@ -234,10 +236,45 @@ def _plain_name(name: str) -> str:
 
 def is_reduce_kernel(name: str) -> bool:
     return _plain_name(REDUCE_KERNEL) in _plain_name(name)
-CALIBRATION_KERNEL = "vectorized_elementwise_kernel"
+
+
+def is_library_kernel(name: str) -> bool:
+    """Any kernel of the reduce library (every streaming and single-shot instance)."""
+    plain = _plain_name(name)
+    return "k_stream_" in plain or "k_single_shot" in plain
+
+
+CALIBRATION_KERNEL = "neg_kernel"   # torch.neg, the calibration copy (other elementwise kernels may run)
+
+# Configurations a profile pass can run: ranks, elements, wire type, schedule,
+# source element bytes, destinations, rotated sets, and whether the sources sit
+# in pinned host memory (read by the kernel through their device mapping).
+PROFILE_CASES = {
+    "prefill_bf16": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1, sets=8,
+                         host=False, what="prefill reduce: R=2 fp32 partials [2048x4096], bf16 wire, CHUNKED"),
+    "slice_bcast_f16": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=4, n_dst=4, sets=2,
+                            host=False, what="slice + broadcast: R=4 fp32 partials [2048x8192], fp16 wire, "
+                                             "4 destinations, RS_BCAST"),
+    "r8_hbm_bf16": dict(R=8, n=8192 * 8192, wire="bf16", mode="chunked", src_bytes=4, n_dst=1, sets=1,
+                        host=False, what="R=8 fp32 partials [8192x8192] in HBM, bf16 wire, CHUNKED"),
+    "r8_hbm_bf16_src": dict(R=8, n=8192 * 8192, wire="bf16", mode="chunked", src_bytes=2, n_dst=1, sets=1,
+                            host=False, what="R=8 bf16 partials [8192x8192] in HBM (AR_SRC_WIRE), CHUNKED"),
+    "r8_host_direct_bf16": dict(R=8, n=8192 * 8192, wire="bf16", mode="host_staged", src_bytes=2, n_dst=1,
+                                sets=1, host=True,
+                                what="R=8 bf16 partials [8192x8192] in pinned host memory, HOST_STAGED, "
+                                     "kernel reads them directly over PCIe"),
+}
+
+
+def case_algo_bytes(case: dict) -> int:
+    return case["R"] * case["n"] * case["src_bytes"] + case["n_dst"] * case["n"] * 4
+
+
 TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py"
+TRACE_PASS_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
+                  "python3 bench.py --profile-pass --profile-workload {wl}")
 PMC_CMD = ("cd /tmp && rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {tag} -- "
-           "python3 bench.py --profile-pass")
+           "python3 bench.py --profile-pass{extra}")
 
 
 def _csv_rows(directory: str, suffix: str):
@@ -251,47 +288,75 @@ def _csv_rows(directory: str, suffix: str):
         return list(csv.DictReader(fh))
 
 
-def summarize_trace(directory: str) -> None:
+def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("mpp::", "").replace("|", "/")
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
+    case = PROFILE_CASES[wl]
     rows = _csv_rows(directory, "kernel_stats.csv")
-    out = os.path.join(ROOT, "profiles", "kernel_trace_prefill_bf16.md")
-    lines = ["# rocprofv3 kernel trace: bench.py default run (prefill reduce + decode calls)", "",
-             f"Command: `{TRACE_CMD}`", "",
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{wl}.md")
+    if wl == "prefill_bf16":
+        title = "# rocprofv3 kernel trace: bench.py default run (prefill reduce + decode calls)"
+        cmd = TRACE_CMD
+    else:
+        title = f"# rocprofv3 kernel trace: profile pass of {case['what']}"
+        cmd = TRACE_PASS_CMD.format(wl=wl)
+    lines = [title, "", f"Command: `{cmd}`", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows[:8]:
-        name = r["Name"].replace("(anonymous namespace)::", "").replace("mpp::", "").replace("|", "/")
-        if len(name) > 90:
-            name = name[:87] + "..."
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
-    red = [r for r in rows if is_reduce_kernel(r["Name"])]
-    if red:
-        avg_us = float(red[0]["AverageNs"]) / 1e3
-        algo = 100_663_296
-        lines += ["", f"Prefill reduce kernel `{REDUCE_KERNEL}`: average {avg_us:.3f} us per launch = "
-                      f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch)."]
+    algo = case_algo_bytes(case)
+    if wl == "prefill_bf16":
+        red = [r for r in rows if is_reduce_kernel(r["Name"])]
+        if red:
+            avg_us = float(red[0]["AverageNs"]) / 1e3
+            lines += ["", f"Prefill reduce kernel `{REDUCE_KERNEL}`: average {avg_us:.3f} us per launch = "
+                          f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch)."]
+    else:
+        ours = [r for r in rows if is_library_kernel(r["Name"])]
+        if ours:
+            top = max(ours, key=lambda r: float(r["TotalDurationNs"]))
+            avg_us = float(top["AverageNs"]) / 1e3
+            lines += ["", f"Reduce kernel `{_short(top['Name'])}`: average {avg_us:.3f} us per launch = "
+                          f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch: "
+                          f"{case['R']} x {case['n']} x {case['src_bytes']} B read, {case['n_dst']} x "
+                          f"{case['n']} x 4 B written)."]
+            if case["host"]:
+                host_b = case["R"] * case["n"] * case["src_bytes"]
+                lines += ["", f"The sources cross PCIe: {host_b} B read from pinned host memory per launch = "
+                              f"{host_b / avg_us / 1e3:.1f} GB/s host-to-device."]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out)
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
+def summarize_pmc(fetch_dir: str, write_dir: str, wl: str = "prefill_bf16") -> None:
+    case = PROFILE_CASES[wl]
+    match = is_reduce_kernel if wl == "prefill_bf16" else is_library_kernel
+
     def per_kernel(directory):
         rows = _csv_rows(directory, "counter_collection.csv")
-        red = [float(r["Counter_Value"]) for r in rows if is_reduce_kernel(r["Kernel_Name"])]
+        red = [float(r["Counter_Value"]) for r in rows if match(r["Kernel_Name"])]
+        names = sorted({_short(r["Kernel_Name"]) for r in rows if match(r["Kernel_Name"])})
         cal = [float(r["Counter_Value"]) for r in rows if CALIBRATION_KERNEL in r["Kernel_Name"]]
         if not red or not cal:
             raise RuntimeError(f"missing dispatches in {directory}")
-        return sum(red) / len(red), len(red), sum(cal) / len(cal), len(cal)
+        return sum(red) / len(red), len(red), sum(cal) / len(cal), len(cal), names
 
-    f_red, nf, f_cal, ncf = per_kernel(fetch_dir)
-    w_red, nw, w_cal, ncw = per_kernel(write_dir)
+    f_red, nf, f_cal, ncf, names = per_kernel(fetch_dir)
+    w_red, nw, w_cal, ncw, _ = per_kernel(write_dir)
     known_kib = CALIBRATION_BYTES / 1024
     f_scale, w_scale = known_kib / f_cal, known_kib / w_cal
     fetch_b = f_red * f_scale * 1024
     write_b = w_red * w_scale * 1024
-    algo = 100_663_296
+    algo = case_algo_bytes(case)
+    extra = "" if wl == "prefill_bf16" else f" --profile-workload {wl}"
     traffic = {
-        "kernel": REDUCE_KERNEL,
+        "workload": case["what"],
+        "kernel": REDUCE_KERNEL if wl == "prefill_bf16" else names,
         "kernel_source_sha256_16": kernel_source_hash(),
         "fetch_size_kib_per_dispatch": round(f_red, 1), "fetch_dispatches": nf,
         "write_size_kib_per_dispatch": round(w_red, 1), "write_dispatches": nw,
@@ -301,17 +366,19 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
         "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
         "algo_bytes_per_launch": algo,
         "traffic_over_algo": round((fetch_b + write_b) / algo, 4),
-        "commands": [PMC_CMD.format(counter="FETCH_SIZE", tag="fetch"),
-                     PMC_CMD.format(counter="WRITE_SIZE", tag="write")],
+        "commands": [PMC_CMD.format(counter="FETCH_SIZE", tag="fetch", extra=extra),
+                     PMC_CMD.format(counter="WRITE_SIZE", tag="write", extra=extra)],
     }
-    with open(PROFILE_TRAFFIC, "w") as fh:
+    js = PROFILE_TRAFFIC if wl == "prefill_bf16" else os.path.join(ROOT, "profiles", f"traffic_{wl}.json")
+    with open(js, "w") as fh:
         json.dump(traffic, fh, indent=1)
-    md = os.path.join(ROOT, "profiles", "traffic_prefill_bf16.md")
+    md = os.path.join(ROOT, "profiles", f"traffic_{wl}.md")
     with open(md, "w") as fh:
-        fh.write("# HBM traffic of the prefill reduce kernel (rocprofv3 --pmc)\n\n")
+        fh.write(f"# HBM traffic of the reduce kernel (rocprofv3 --pmc): {case['what']}\n\n")
         for c in traffic["commands"]:
             fh.write(f"- `{c}`\n")
-        fh.write(f"\nKernel `{REDUCE_KERNEL}`, {nf} dispatches (rotated input sets).\n\n")
+        kn = ", ".join(f"`{k}`" for k in ([REDUCE_KERNEL] if wl == "prefill_bf16" else names))
+        fh.write(f"\nKernel {kn}, {nf} dispatches (rotated input sets).\n\n")
         fh.write("| counter | reduce KiB/dispatch | calibration KiB/dispatch (64 MiB known) | scale | "
                  "reduce bytes after scaling |\n|---|---|---|---|---|\n")
         fh.write(f"| FETCH_SIZE | {f_red:.1f} | {f_cal:.1f} | {f_scale:.4f} | {fetch_b:.0f} |\n")
@@ -319,29 +386,54 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
         fh.write(f"HBM traffic per launch {fetch_b + write_b:.0f} B against {algo} algorithmic B "
                  f"(ratio {(fetch_b + write_b) / algo:.4f}); kernel source hash "
                  f"{traffic['kernel_source_sha256_16']}.\n")
-    print(PROFILE_TRAFFIC, md)
+        if case["host"]:
+            fh.write("\nThe sources are pinned host memory: FETCH_SIZE counts the L2's fetches from "
+                     "memory whether HBM or PCIe serves them, so here it is the host bytes that crossed "
+                     "PCIe; HBM sees only the writes.\n")
+    print(js, md)
 
 
 def profile_pass(torch, ar, wl, args):
-    """Counter pass: 8 rotated prefill reduces x 3, then 8 torch.neg launches that
-    read and write CALIBRATION_BYTES each (a plain copy-shaped kernel)."""
-    w = wl.WORKLOADS["prefill_bf16"]
-    S = max(1, args.sets)
-    srcs = [[torch.randn(w.n, device="cuda") for _ in range(w.R)] for _ in range(S)]
-    dsts = [torch.empty(w.n, device="cuda") for _ in range(S)]
+    """Counter / trace pass: rotated reduces of one configuration (at least 12
+    launches), then 8 torch.neg launches that read and write CALIBRATION_BYTES
+    each (a plain copy-shaped kernel)."""
+    case = PROFILE_CASES[args.profile_workload]
+    R, n = case["R"], case["n"]
+    S = max(1, min(args.sets, case["sets"]))
+    wire = {"bf16": ar.AR_BF16, "f16": ar.AR_F16}[case["wire"]]
+    mode = {"chunked": ar.AR_MODE_CHUNKED, "rs_bcast": ar.AR_MODE_RS_BCAST,
+            "host_staged": ar.AR_MODE_HOST_STAGED}[case["mode"]]
+    sdt = torch.float32 if case["src_bytes"] == 4 else torch.bfloat16
+    if case["src_bytes"] == 2:
+        mode |= ar.AR_SRC_WIRE
+
+    def make_src():
+        t = torch.randn(n, device="cuda").to(sdt)
+        if case["host"]:
+            h = torch.empty(n, dtype=sdt, pin_memory=True)
+            h.copy_(t)
+            return h
+        return t
+
+    srcs = [[make_src() for _ in range(R)] for _ in range(S)]
+    dsts = [[torch.empty(n, device="cuda") for _ in range(case["n_dst"])] for _ in range(S)]
+    torch.cuda.synchronize()
     ctx = ar.ar_init(0)
     stream = torch.cuda.current_stream()
-    for k in range(3 * S):
-        ar.ar_reduce(ctx, [dsts[k % S]], srcs[k % S], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED, stream=stream)
+    launches = max(3 * S, 12)
+    for k in range(launches):
+        ar.ar_reduce(ctx, dsts[k % S], srcs[k % S], n, ar.AR_F32, wire, mode, stream=stream)
     torch.cuda.synchronize()
-    n = CALIBRATION_BYTES // 4
-    a = [torch.randn(n, device="cuda") for _ in range(4)]
-    b = [torch.empty(n, device="cuda") for _ in range(4)]
+    ar.ar_free(ctx)
+    del srcs, dsts
+    nc = CALIBRATION_BYTES // 4
+    a = [torch.randn(nc, device="cuda") for _ in range(4)]
+    b = [torch.empty(nc, device="cuda") for _ in range(4)]
     for k in range(8):
         torch.neg(a[k % 4], out=b[k % 4])
     torch.cuda.synchronize()
-    ar.ar_free(ctx)
-    log(f"profile pass done: {3 * S} reduces of {w.n} elements, 8 calibration copies of {CALIBRATION_BYTES} B")
+    log(f"profile pass done ({args.profile_workload}): {launches} reduces of R={R} x {n} elements, "
+        f"8 calibration copies of {CALIBRATION_BYTES} B")
     return 0
 
 

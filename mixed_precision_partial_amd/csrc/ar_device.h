@@ -74,6 +74,10 @@ struct Cfg {
     static constexpr int kDstBytes = DN ? 2 : 4;
 };
 
+// Bit casts take their operand by value.  With this compiler (AMD clang 22,
+// ROCm 7.2), __builtin_bit_cast applied directly to a vector subscript such as
+// `v[q]` reads element 0 whatever q is; passing the element through a scalar
+// parameter first, as these helpers do, gives the intended element.
 __device__ __forceinline__ float f32_from_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t bits_from_f32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
