@@ -47,6 +47,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def measured_traffic(algo_bytes: int):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     when absent or taken on a different kernel source."""
@@ -174,11 +185,16 @@ def main() -> int:
             "unit": "GB/s",
             "cores": 1,
             "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "host_cores_visible": os.cpu_count(),
             "sample": f"{reps + 1} full calls of the same 2048x4096 R=2 bf16-wire reduce "
                       f"({cpu_s + one:.1f} s, single-threaded scalar C oracle)",
         }
 
     extras = {"ceilings_prefill_size": ceilings(torch, n, S)}
+    ceil = extras["ceilings_prefill_size"]
+    ceil["value_over_copy"] = round(gbs / ceil["copy_GB/s"], 3)
+    ceil["value_over_add_2r1w"] = round(gbs / ceil["add_2r1w_GB/s"], 3)
     if not args.no_decode:
         extras["decode_bf16"] = decode_latency(torch, ar, wl)
     if args.extras:
@@ -252,6 +268,9 @@ CALIBRATION_KERNEL = "neg_kernel"   # torch.neg, the calibration copy (other ele
 PROFILE_CASES = {
     "prefill_bf16": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1, sets=8,
                          host=False, what="prefill reduce: R=2 fp32 partials [2048x4096], bf16 wire, CHUNKED"),
+    "prefill_bf16_one_set": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1,
+                                 sets=1, host=False,
+                                 what="prefill reduce without rotation (one input set, MALL-resident)"),
     "slice_bcast_f16": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=4, n_dst=4, sets=2,
                             host=False, what="slice + broadcast: R=4 fp32 partials [2048x8192], fp16 wire, "
                                              "4 destinations, RS_BCAST"),
@@ -523,7 +542,34 @@ def decode_latency(torch, ar, wl):
         torch.cuda.synchronize()
         lat[i] = (time.perf_counter() - t) * 1e6
     ar.ar_free(ctx)
+    # launch floor for context: the smallest torch kernel (a 1-element fill) issued
+    # the same way, async and replayed from a graph
+    one = torch.empty(1, device="cuda")
+    for _ in range(200):
+        one.fill_(1.0)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(calls):
+        one.fill_(1.0)
+    end.record(stream)
+    torch.cuda.synchronize()
+    floor_async = start.elapsed_time(end) * 1e3 / calls
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        for _ in range(graph_calls):
+            one.fill_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    floor_graph = start.elapsed_time(end) * 1e3 / (reps * graph_calls)
+    del g
     res = {
+        "floor_1elem_fill_us_async": round(floor_async, 3),
+        "floor_1elem_fill_us_graph_replay": round(floor_graph, 3),
         "us_per_call_async": round(us_async, 3),
         "us_per_call_graph_replay": round(us_graph, 3),
         "host_enqueue_us_per_call": round(host_s * 1e6 / calls, 3),
@@ -661,7 +707,11 @@ def other_schedules(torch, ar, wl):
     ms_copy = timed(lambda: dev_big.copy_(big, non_blocking=True), 5)
     out["host_staged_bf16"] = {"ms": round(ms, 3), "pcie_GB/s": round(pcie_bytes / ms / 1e6, 2),
                                "h2d_copy_GB/s": round(pcie_bytes / ms_copy / 1e6, 2),
-                               "frac_of_h2d_copy": round(ms_copy / ms, 3), "path": "copy engine"}
+                               "frac_of_h2d_copy": round(ms_copy / ms, 3), "path": "copy engine",
+                               # time beyond one plain copy of the same bytes, against the adds'
+                               # own time on the same data in HBM (kernel time left exposed <= this)
+                               "over_plain_copy_ms": round(ms - ms_copy, 3),
+                               "adds_from_hbm_ms": round(out["r8_hbm_bf16_src"]["us"] / 1e3, 3)}
     out["host_direct_bf16"] = {"ms": round(ms_direct, 3), "pcie_GB/s": round(pcie_bytes / ms_direct / 1e6, 2),
                                "frac_of_h2d_copy": round(ms_copy / ms_direct, 3), "path": "kernel reads pinned memory"}
     log(f"host_staged_bf16: {out['host_staged_bf16']}")
