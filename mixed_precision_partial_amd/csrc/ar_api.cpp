@@ -105,8 +105,11 @@ int resolve_config(const ar_config *cfg, Config *out) {
     return AR_OK;
 }
 
+// [a, a + na) and [b, b + nb) share a byte; exact for any addresses and
+// lengths (no sum that could wrap).
 bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
-    return a < b + nb && b < a + na;
+    if (na == 0 || nb == 0) return false;
+    return a >= b ? a - b < nb : b - a < na;
 }
 
 size_t round_down(size_t x, size_t m) { return x / m * m; }
