@@ -33,10 +33,12 @@ def overlap(a: int, na: int, b: int, nb: int) -> bool:
     return na > 0 and nb > 0 and a < b + nb and b < a + na
 
 
-def expected(R, n, dst_type, wire_type, mode, dsts, srcs, host, res=None, res_len=0):
+def expected(R, n, dst_type, wire_type, mode, dsts, srcs, host, res=None, res_len=0, contiguous=True):
     """(set of reasons the call must be refused, resolved mode or None).
 
-    Each reason is INVALID or UNSUPPORTED, following the rules of include/ar.h."""
+    Each reason is INVALID or UNSUPPORTED, following the rules of include/ar.h.
+    `contiguous` False leaves out the overlap checks (row-strided tensors span
+    more than n elements; the caller checks them)."""
     why = set()
     if not 2 <= R <= 16:
         return {INVALID}, None
@@ -85,7 +87,7 @@ def expected(R, n, dst_type, wire_type, mode, dsts, srcs, host, res=None, res_le
             why.add(INVALID)
     if n > (SIZE_MAX // 8) // 16:
         why.add(INVALID)
-    if n > 0 and not why:
+    if n > 0 and not why and contiguous:
         dl, sl = n * dst_bytes, n * src_bytes
         rl = 0 if res_kind == 0 else (n if res_kind == 1 else res_len) * dst_bytes
         live = dsts[:n_dst]
@@ -237,3 +239,105 @@ def test_overlap_near_the_top_of_the_address_space(a, na, b, nb):
     rc, _ = ar.ar_plan_query([a], [b, 1 << 33], n, F32, F32, ar.AR_MODE_CHUNKED)
     want = ar.AR_ERR_INVALID if overlap(a, na, b, nb) and a != b else ar.AR_OK
     assert rc == want
+
+
+def extent(rows: int, cols: int, stride: int) -> int:
+    return 0 if rows == 0 or cols == 0 else (rows - 1) * stride + cols
+
+
+def expected_rows(R, rows, cols, ss, ds, rs, dst_type, wire_type, mode, dsts, srcs, host, res):
+    """Refusal reasons for ar_plan_query_rows (row-strided tensors, rules of include/ar.h)."""
+    if cols and rows > SIZE_MAX // cols:
+        return {INVALID}, None
+    if rows > 1 and any(st_ > (SIZE_MAX // 16) // rows for st_ in (ss, ds, rs)):
+        return {INVALID}, None
+    n = rows * cols
+    why, resolved = expected(R, n, dst_type, wire_type, mode, dsts, srcs, host, contiguous=False)
+    if resolved is None:
+        return why, None
+    narrow = dst_type != F32
+    src_bytes = ELEM[wire_type] if (mode & ar.AR_SRC_WIRE or narrow) else ELEM[dst_type]
+    dst_bytes = ELEM[dst_type]
+    if ss < cols or ds < cols or (ss * src_bytes) % 16 or (ds * dst_bytes) % 16:
+        why.add(INVALID)
+    if cols > MAX_LAUNCH:
+        why.add(UNSUPPORTED)
+    res_kind = 0
+    if res is not None and n > 0:
+        if (rs != 0 and rs < cols) or (rs * dst_bytes) % 16 or res % 16:
+            why.add(INVALID)
+        res_kind = 2 if rs == 0 else 1
+    if n > 0 and not why:
+        n_dst = R if resolved == ar.AR_MODE_RS_BCAST else 1
+        dl, sl = extent(rows, cols, ds) * dst_bytes, extent(rows, cols, ss) * src_bytes
+        rl = 0 if res_kind == 0 else (cols if res_kind == 2 else extent(rows, cols, rs)) * dst_bytes
+        live = dsts[:n_dst]
+        for i, d in enumerate(live):
+            for e in live[i + 1:]:
+                if overlap(d, dl, e, dl):
+                    why.add(INVALID)
+            for s in srcs:
+                if s is not None and overlap(d, dl, s, sl) and not (s == d and src_bytes == dst_bytes and ss == ds):
+                    why.add(INVALID)
+            if res_kind and overlap(d, dl, res, rl) and not (res_kind == 1 and res == d and rs == ds):
+                why.add(INVALID)
+    return why, (resolved, res_kind)
+
+
+@st.composite
+def row_shape(draw):
+    rows = draw(st.one_of(st.integers(0, 300), st.sampled_from([1, 2, 65535, 65536, 70000, 1 << 40])))
+    cols = draw(st.one_of(st.integers(0, 5000), st.sampled_from([8, 4096, (1 << 30) + 8, 1 << 50])))
+
+    def stride():
+        pad = draw(st.one_of(st.integers(0, 64), st.sampled_from([0, 0, 512, 1 << 20])))
+        s = cols + pad
+        if draw(st.integers(0, 3)):
+            s = -(-s // 8) * 8          # usually a 16-byte row pitch for both element widths
+        if draw(st.integers(0, 15)) == 0:
+            s = max(0, cols - 8)       # rows that would overlap
+        return s
+
+    return rows, cols, stride(), stride(), draw(st.sampled_from([0, 0, stride(), stride()]))
+
+
+@SETTINGS
+@given(call(), row_shape(), st.data())
+def test_plan_query_rows_matches_rules(args, shape, data):
+    R, _, dst_type, wire_type, mode, dsts, srcs, host = args
+    rows, cols, ss, ds, rs = shape
+    res = data.draw(st.sampled_from([None, None, 40 << 36, 40 << 36, (40 << 36) + 8, dsts[0]]))
+    rc, plan = ar.ar_plan_query_rows(dsts, srcs, rows, cols, ss, ds, dst_type, wire_type, mode, residual=res,
+                                     res_stride=rs, srcs_on_host=host, R=max(R, 0) if R <= 16 else R)
+    live_srcs = srcs[:max(R, 0)]
+    why, out = expected_rows(R, rows, cols, ss, ds, rs, dst_type, wire_type, mode, dsts, live_srcs, host, res)
+    event(f"status {ar.ar_status_str(rc)}")
+    if why:
+        if why == {UNSUPPORTED}:
+            assert rc == ar.AR_ERR_UNSUPPORTED
+        elif why == {INVALID}:
+            assert rc == ar.AR_ERR_INVALID
+        else:
+            assert rc in (ar.AR_ERR_INVALID, ar.AR_ERR_UNSUPPORTED)
+        return
+    assert rc == ar.AR_OK, f"refused a valid call: {ar.ar_status_str(rc)}"
+    resolved, res_kind = out
+    n = rows * cols
+    narrow = dst_type != F32
+    src_bytes = ELEM[wire_type] if (mode & ar.AR_SRC_WIRE or narrow) else ELEM[dst_type]
+    n_dst = R if resolved == ar.AR_MODE_RS_BCAST else 1
+    assert plan.mode == resolved and plan.n_dst == n_dst
+    assert plan.residual_kind == (res_kind if n > 0 else 0)
+    res_b = 0 if n == 0 or res_kind == 0 else (n if res_kind == 1 else cols) * ELEM[dst_type]
+    assert plan.algo_bytes == R * n * src_bytes + n_dst * n * ELEM[dst_type] + res_b
+    assert all(plan.slice_start[r] == 0 and plan.slice_len[r] == 0 for r in range(16))
+    if n == 0:
+        assert plan.n_chunks == 0
+        return
+    # device schedules: one range per row; host-staged copies move whole rows
+    assert plan.chunk_elems % cols == 0
+    chunk_rows = plan.chunk_elems // cols
+    assert chunk_rows >= 1 and plan.chunk_elems <= max(MAX_LAUNCH, cols)
+    if resolved != ar.AR_MODE_HOST_STAGED:
+        assert chunk_rows == 1
+    assert plan.n_chunks == -(-rows // chunk_rows)
