@@ -1,0 +1,143 @@
+"""A seeded random sweep over the whole call space, bit for bit against the
+oracle, through the C ABI.
+
+Each case draws a rank count, a length (ragged against every tile and chunk
+size), the wire and destination types, whether the sources hold the wire type
+already, the schedule, a residual (none, element-wise, or a broadcast row),
+inactive ranks, exact in-place use, and a context configuration (kernel
+family, store policy, host path, grid size, chunk sizes, copy slots).  The
+parametrised tests cover each feature on its own; this sweep covers them in
+combination.  Cases are generated from a fixed seed, so a failure names a
+case that reruns identically.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_partial_amd as ar
+import oracle
+import workloads as wl
+from gpu_util import GuardedDst, assert_bits_equal, assert_bits_equal16, log_case, to_device, to_pinned
+
+pytestmark = pytest.mark.gpu
+
+SCHEDULES = [ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED,
+             ar.AR_MODE_AUTO]
+N_CASES = 400
+BATCH = 25
+
+
+def draw_case(i: int) -> dict:
+    rng = np.random.default_rng(np.random.SeedSequence([40_000, i]))
+    R = int(rng.choice([2, 2, 3, 4, 5, 7, 8, 9, 16]))
+    narrow = rng.random() < 0.2
+    if narrow:
+        wire = int(rng.choice([ar.AR_BF16, ar.AR_F16]))
+        dst_type, src_wire = wire, True
+    else:
+        wire = int(rng.choice([ar.AR_F32, ar.AR_BF16, ar.AR_BF16, ar.AR_F16]))
+        dst_type = ar.AR_F32
+        src_wire = wire != ar.AR_F32 and rng.random() < 0.35
+    res_form = rng.choice(["none", "none", "elementwise", "row"])
+    if res_form == "row":
+        L = 8 * int(rng.integers(1, 700))
+        n = L * int(rng.integers(1, max(2, (1 << 21) // L)))
+    else:
+        L = 0
+        n = int(np.exp(rng.uniform(0.0, np.log(1 << 21))))
+    mode = int(rng.choice(SCHEDULES))
+    inactive = rng.random(R) < 0.3 if rng.random() < 0.2 else np.zeros(R, dtype=bool)
+    in_place = (not narrow and not src_wire and res_form != "row" and
+                mode in (ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED) and not inactive[0] and rng.random() < 0.5)
+    cfg = {
+        "stream_kernel": int(rng.choice([0, 0, 1, 2])),
+        "store_policy": int(rng.choice([0, 0, 1, 2])),
+        "host_path": int(rng.choice([0, 1, 2])),
+        "grid_wgs": int(rng.choice([0, 0, 0, 1, 7, 64, 300])),
+        "chunk_bytes": int(rng.choice([0, 0, 4096, 65536])),
+        "host_chunk_bytes": int(rng.choice([0, 0, 1 << 14, 1 << 16])),
+        "host_slots": int(rng.choice([0, 1, 2])),
+    }
+    return dict(i=i, R=R, n=n, wire=wire, dst_type=dst_type, src_wire=src_wire, res_form=str(res_form), L=L,
+                mode=mode, inactive=[bool(x) for x in inactive], in_place=bool(in_place), cfg=cfg,
+                dist=str(rng.choice(["wide", "normal", "normal+outliers"])))
+
+
+def run_case(c: dict) -> None:
+    R, n, wire, dst_type = c["R"], c["n"], c["wire"], c["dst_type"]
+    narrow = dst_type != ar.AR_F32
+    what = (f"random case {c['i']}: R={R} n={n} wire={wire} dst={dst_type} src_wire={c['src_wire']} "
+            f"mode={c['mode']} residual={c['res_form']} L={c['L']} inactive={c['inactive']} "
+            f"in_place={c['in_place']} cfg={c['cfg']}")
+    if narrow:
+        srcs = wl.random_narrow(40_100 + c["i"], 0, R, n, dst_type, dist="wide")
+    else:
+        srcs = wl.random_partials(40_100 + c["i"], 0, R, n, dist=c["dist"])
+        if c["src_wire"]:
+            srcs = [wl.as_wire_typed(s, wire) for s in srcs]
+    residual = None
+    if c["res_form"] == "elementwise":
+        residual = wl.residual(40_200 + c["i"], 0, n, dst_type, dist="wide")
+    elif c["res_form"] == "row":
+        residual = wl.residual(40_200 + c["i"], 0, c["L"], dst_type, dist="wide")
+    active = [not x for x in c["inactive"]]
+    host = c["mode"] == ar.AR_MODE_HOST_STAGED
+    put = to_pinned if host else to_device
+    ts = [put(s) if a else None for s, a in zip(srcs, active)]
+    base = c["mode"]
+    n_dst = R if base == ar.AR_MODE_RS_BCAST else 1
+    flags = (ar.AR_SRC_WIRE if c["src_wire"] else 0) | (0 if all(active) else ar.AR_SRC_INACTIVE_NULL)
+    ctx = ar.ar_init(0, c["cfg"])
+    try:
+        log_case(what)
+        if c["in_place"]:
+            dsts = None
+            dptrs = [ts[0]]
+        else:
+            dsts = [GuardedDst(n, 16 if narrow else 32) for _ in range(n_dst)]
+            dptrs = [d.ptr() for d in dsts]
+        ptrs = [0 if t is None else t for t in ts]
+        if residual is None:
+            ar.ar_reduce(ctx, dptrs, ptrs, n, dst_type, wire, base | flags)
+        else:
+            ar.ar_reduce_add(ctx, dptrs, ptrs, n, dst_type, wire, base | flags, to_device(residual), residual.size)
+        torch.cuda.synchronize()
+    finally:
+        ar.ar_free(ctx)
+    src_type = wire if (c["src_wire"] or narrow) and wire != ar.AR_F32 else None
+    used = [s if a else None for s, a in zip(srcs, active)]
+    if not any(active):
+        used[0] = np.zeros(n, dtype=np.uint16 if src_type is not None else np.float32)
+    want = oracle.reduce(used, wire, src_type=src_type, dst_type=dst_type, residual=residual)[0]
+    if c["in_place"]:
+        assert_bits_equal(ts[0].cpu().numpy(), want, what + " (in place)")
+        return
+    for d, g in enumerate(dsts):
+        got = g.result()
+        if narrow:
+            assert_bits_equal16(got, want, dst_type, f"{what} dst {d}")
+        else:
+            assert_bits_equal(got, want, f"{what} dst {d}")
+
+
+def test_case_generator_is_deterministic_and_varied():
+    cases = [draw_case(i) for i in range(N_CASES)]
+    assert cases[:3] == [draw_case(i) for i in range(3)]
+    seen = {(c["mode"], c["res_form"], c["dst_type"] != ar.AR_F32) for c in cases}
+    assert len(seen) >= 20
+    assert any(c["in_place"] for c in cases) and any(any(c["inactive"]) for c in cases)
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+@pytest.mark.parametrize("start", range(0, N_CASES, BATCH))
+def test_random_sweep(gpu, start):
+    for i in range(start, start + BATCH):
+        run_case(draw_case(i))
+    torch.cuda.empty_cache()
