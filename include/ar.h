@@ -169,6 +169,10 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *   wire_type : AR_F32, AR_F16 or AR_BF16; not wider than dst_type.
  *   mode      : AR_MODE_* | optional AR_SRC_WIRE | optional AR_SRC_INACTIVE_NULL.
  *   hip_stream: hipStream_t to enqueue on (NULL = null stream).
+ * Graph capture: every schedule enqueues kernel launches only (no memsets,
+ * no host synchronisation), so calls can be captured into a HIP graph and
+ * replayed -- except the host-staged copy-engine pipeline, which is refused
+ * under capture (the direct host reads, the default, can be captured).
  * Errors (all detected on the host before anything is enqueued):
  *   AR_ERR_INVALID for a NULL ctx / array / entry, R outside 2..16, a
  *   pointer not 16-byte aligned, an unknown type / mode / flag, a wire type
@@ -177,7 +181,9 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *   some srcs[r], same element width), n * element size overflowing size_t, or
  *   memory of the wrong kind for the mode (device pointers of another device,
  *   pageable host memory, host sources outside AR_MODE_HOST_STAGED);
- *   AR_ERR_UNSUPPORTED for a 16-bit dst_type with a different wire_type;
+ *   AR_ERR_UNSUPPORTED for a 16-bit dst_type with a different wire_type,
+ *   and for a host-staged call on the copy-engine path (host_path 1) while
+ *   hip_stream is being captured into a graph;
  *   AR_ERR_NOMEM if host-staged scratch cannot be allocated;
  *   AR_ERR_RUNTIME if a launch or copy cannot be enqueued.  Faults of
  *   enqueued work surface at the caller's next synchronisation. */

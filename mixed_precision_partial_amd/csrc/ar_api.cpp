@@ -855,6 +855,18 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
     }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (plan.mode == AR_MODE_HOST_STAGED && !plan.host_direct) {
+        // the copy-engine pipeline synchronises when it grows its scratch ring and
+        // chains events across its own stream and calls: it cannot be recorded
+        // into a graph, so a call under stream capture is refused before anything
+        // is enqueued (the direct path and every device schedule are capturable)
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+            (void)hipGetLastError();
+            return AR_ERR_RUNTIME;
+        }
+        if (cs != hipStreamCaptureStatusNone) return AR_ERR_UNSUPPORTED;
+    }
     if (rows != nullptr) {
         if (plan.mode != AR_MODE_HOST_STAGED) return run_rows(ctx, plan, dst, srcs, R, *rows, wire_type, res, stream);
         if (plan.host_direct) {

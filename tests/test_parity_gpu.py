@@ -14,8 +14,8 @@ import torch
 import mixed_precision_partial_amd as ar
 import oracle
 import workloads as wl
-from gpu_util import (GuardedDst, assert_bits_equal, assert_no_sentinel, log_case, oracle_result,
-                      to_device, to_pinned)
+from gpu_util import (GuardedDst, assert_bits_equal, assert_bits_equal16, assert_no_sentinel, log_case,
+                      oracle_result, to_device, to_pinned)
 
 pytestmark = pytest.mark.gpu
 
@@ -417,6 +417,86 @@ def test_graph_capture_replays(ctx):
         torch.cuda.synchronize()
         assert_bits_equal(out.cpu().numpy(), want, f"graph replay {rep} decode")
         assert_bits_equal(big_out.cpu().numpy(), big_want, f"graph replay {rep} chunked")
+
+
+def test_graph_capture_every_capturable_path(ctx):
+    """One graph holding a call of every capturable kind -- slice + broadcast, the
+    residual add (element-wise and broadcast row), a narrow destination, a row-strided
+    call with a bias row, and host-staged sources read directly -- replayed three times
+    with eager work between replays, each replay checked against the oracle.  A
+    host-staged call on the copy-engine path is refused under capture (status
+    AR_ERR_UNSUPPORTED, nothing recorded) and the capture stays usable."""
+    cases = []   # (output tensor, expected, 16-bit?)
+    n = 100_003
+    s3 = wl.random_partials(9200, 0, 3, n, dist="wide")
+    d3 = [torch.empty(n, device="cuda") for _ in range(3)]
+    cases += [(d, oracle.reduce(s3, ar.AR_F16)[0], False) for d in d3]
+    s2 = wl.random_partials(9201, 0, 2, 4096 * 24)
+    ew = wl.residual(9202, 0, s2[0].size)
+    row = wl.residual(9203, 0, 4096)
+    d_ew = torch.empty(s2[0].size, device="cuda")
+    d_row = torch.empty(s2[0].size, device="cuda")
+    cases += [(d_ew, oracle.reduce(s2, ar.AR_BF16, residual=ew)[0], False),
+              (d_row, oracle.reduce(s2, ar.AR_BF16, residual=np.tile(row, 24))[0], False)]
+    sn = wl.random_narrow(9204, 0, 4, 70_001, ar.AR_BF16)
+    d_n = torch.empty(70_001, dtype=torch.int16, device="cuda")
+    cases.append((d_n, oracle.reduce(sn, ar.AR_BF16, src_type=ar.AR_BF16, dst_type=ar.AR_BF16)[0], True))
+    rows, cols, ss, ds = 37, 520, 528, 536
+    sr = wl.random_partials(9205, 0, 2, rows * ss)
+    bias = wl.residual(9206, 0, cols)
+    d_r = torch.zeros(rows * ds, device="cuda")
+    dense = [np.concatenate([x[i * ss:i * ss + cols] for i in range(rows)]) for x in sr]
+    want_r = oracle.reduce(dense, ar.AR_BF16, residual=np.tile(bias, rows))[0]
+    sh = [wl.as_wire_typed(x, ar.AR_BF16) for x in wl.random_partials(9207, 0, 4, 65_536)]
+    d_h = torch.empty(65_536, device="cuda")
+    cases.append((d_h, oracle.reduce(sh, ar.AR_BF16, src_type=ar.AR_BF16)[0], False))
+
+    t3 = [to_device(x) for x in s3]
+    t2 = [to_device(x) for x in s2]
+    t_ew, t_row, t_bias = to_device(ew), to_device(row), to_device(bias)
+    tn = [to_device(x) for x in sn]
+    tr = [to_device(x) for x in sr]
+    th = [to_pinned(x) for x in sh]
+    ctx_copy = ar.ar_init(0, {"host_path": 1})
+    torch.cuda.synchronize()
+    log_case("graph capture: broadcast, residual adds, narrow, rows, host direct; copy-engine refused")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        st = torch.cuda.current_stream()
+        ar.ar_reduce(ctx, d3, t3, n, ar.AR_F32, ar.AR_F16, ar.AR_MODE_RS_BCAST, stream=st)
+        ar.ar_reduce_add(ctx, [d_ew], t2, s2[0].size, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, t_ew, stream=st)
+        ar.ar_reduce_add(ctx, [d_row], t2, s2[0].size, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, t_row, stream=st)
+        ar.ar_reduce(ctx, [d_n], tn, 70_001, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED, stream=st)
+        ar.ar_reduce_rows(ctx, [d_r], tr, rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                          residual=t_bias, res_stride=0, stream=st)
+        ar.ar_reduce(ctx, [d_h], th, 65_536, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE,
+                     stream=st)
+        refused = ar.ar_reduce(ctx_copy, [d_h], th, 65_536, ar.AR_F32, ar.AR_BF16,
+                               ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=st, check=False)
+    assert refused == ar.AR_ERR_UNSUPPORTED
+    for rep in range(3):
+        for out, _, _ in cases:
+            out.fill_(0 if out.dtype == torch.int16 else float("nan"))
+        d_r.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (out, want, is16) in enumerate(cases):
+            if is16:
+                assert_bits_equal16(out.cpu().view(torch.int16).numpy().view(np.uint16), want, ar.AR_BF16,
+                                    f"graph replay {rep} output {k}")
+            else:
+                assert_bits_equal(out.cpu().numpy(), want, f"graph replay {rep} output {k}")
+        got = d_r.cpu().numpy()
+        assert_bits_equal(np.concatenate([got[i * ds:i * ds + cols] for i in range(rows)]), want_r,
+                          f"graph replay {rep} rows")
+    # the refused copy-engine call still works outside a capture
+    d_h.fill_(float("nan"))
+    ar.ar_reduce(ctx_copy, [d_h], th, 65_536, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE)
+    torch.cuda.synchronize()
+    assert_bits_equal(d_h.cpu().numpy(), cases[-1][1], "copy-engine call after the capture")
+    del g
+    ar.ar_free(ctx_copy)
 
 
 @pytest.mark.parametrize("wire_name", ["bf16", "f16"])
