@@ -534,12 +534,12 @@ def decode_latency(torch, ar, wl):
     torch.cuda.synchronize()
     us_graph = start.elapsed_time(end) * 1e3 / (reps * graph_calls)
     del g
-    # per-call round trip: enqueue + stream synchronize, wall clock
+    # per-call round trip, wall clock: enqueue + hipStreamSynchronize on the launch stream
     lat = np.empty(2000)
     for i in range(lat.size):
         t = time.perf_counter()
         call(i)
-        torch.cuda.synchronize()
+        stream.synchronize()
         lat[i] = (time.perf_counter() - t) * 1e6
     ar.ar_free(ctx)
     # launch floor for context: the smallest torch kernel (a 1-element fill) issued
