@@ -503,8 +503,13 @@ def decode_latency(torch, ar, wl):
     def call(c):
         ar.ar_reduce(ctx, dsts[c], srcs[c], n, ar.AR_F32, w.wire, ar.AR_MODE_SINGLE_SHOT, stream=stream)
 
+    # the same calls with their arguments converted to C types once (ar.bind_reduce)
+    bound = [ar.bind_reduce(ctx, dsts[c], srcs[c], n, ar.AR_F32, w.wire, ar.AR_MODE_SINGLE_SHOT, stream=stream)
+             for c in range(calls)]
+
     for c in range(200):
         call(c)
+        bound[c]()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -516,6 +521,15 @@ def decode_latency(torch, ar, wl):
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t0
     us_async = start.elapsed_time(end) * 1e3 / calls
+    t0 = time.perf_counter()
+    start.record(stream)
+    for fn in bound:
+        if fn():
+            raise RuntimeError("bound decode call failed")
+    end.record(stream)
+    torch.cuda.synchronize()
+    host_bound_s = time.perf_counter() - t0
+    us_async_bound = start.elapsed_time(end) * 1e3 / calls
     # the same calls captured once into a HIP graph and replayed: the
     # per-call cost without Python or runtime launch overhead
     graph_calls = 1000
@@ -571,6 +585,8 @@ def decode_latency(torch, ar, wl):
         "floor_1elem_fill_us_async": round(floor_async, 3),
         "floor_1elem_fill_us_graph_replay": round(floor_graph, 3),
         "us_per_call_async": round(us_async, 3),
+        "us_per_call_async_bound": round(us_async_bound, 3),
+        "host_enqueue_us_per_call_bound": round(host_bound_s * 1e6 / calls, 3),
         "us_per_call_graph_replay": round(us_graph, 3),
         "host_enqueue_us_per_call": round(host_s * 1e6 / calls, 3),
         "us_per_call_sync_p50": round(float(np.percentile(lat, 50)), 2),

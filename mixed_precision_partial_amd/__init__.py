@@ -207,6 +207,30 @@ def ar_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = 
     return rc
 
 
+def bind_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = AR_BF16,
+                mode: int = AR_MODE_AUTO, stream=None, residual=None, residual_len: int | None = None):
+    """One reduce with every argument converted to its C type once: returns a
+    callable that enqueues the call again each time it is invoked and returns
+    the status (no Python-side checks per call; the library still validates
+    every call).  For latency-bound callers that issue the same call shape on
+    the same buffers many times.  With ``residual`` it binds ``ar_reduce_add``.
+    The caller keeps the bound buffers alive while the callable is in use."""
+    import functools
+
+    lib = load_library()
+    R = len(srcs)
+    head = (ctypes.c_void_p(ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx), _ptr_array(dsts),
+            _ptr_array(srcs), ctypes.c_int(R), ctypes.c_size_t(int(n)), ctypes.c_int(int(dst_type)),
+            ctypes.c_int(int(wire_type)), ctypes.c_uint(int(mode)))
+    st = ctypes.c_void_p(_stream_handle(stream))
+    if residual is None:
+        return functools.partial(lib.ar_reduce, *head, st)
+    rlen = int(n) if residual_len is None else int(residual_len)
+    if residual_len is None and hasattr(residual, "numel"):
+        rlen = int(residual.numel())
+    return functools.partial(lib.ar_reduce_add, *head, ctypes.c_void_p(_addr(residual)), ctypes.c_size_t(rlen), st)
+
+
 def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual,
                   residual_len: int | None = None, stream=None, check: bool = True) -> int:
     """Enqueue one reduce followed by a residual add (element-wise when

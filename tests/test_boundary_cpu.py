@@ -363,3 +363,15 @@ def test_row_strided_rules():
     dsts = (ctypes.c_void_p * 1)(A[30])
     assert lib.ar_plan_query_rows(None, dsts, srcs, 2, None, 0, 2, 2, None, 0, None) == ar.AR_ERR_INVALID
     assert lib.ar_reduce_rows(None, dsts, srcs, 2, None, 0, 2, 2, None, None) == ar.AR_ERR_INVALID
+
+
+def test_bound_calls_reach_the_library():
+    """ar.bind_reduce converts the arguments once; each invocation is a plain call of
+    ar_reduce / ar_reduce_add, whose validation still runs (a NULL context is refused
+    before any runtime call, so this runs without a GPU)."""
+    fake = [1 << 33, (1 << 33) + (1 << 20)]
+    f = ar.bind_reduce(None, [1 << 34], fake, 4096, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_SINGLE_SHOT)
+    assert f() == ar.AR_ERR_INVALID and f() == ar.AR_ERR_INVALID
+    g = ar.bind_reduce(None, [1 << 34], fake, 4096, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                       residual=1 << 35, residual_len=512)
+    assert g() == ar.AR_ERR_INVALID

@@ -419,6 +419,29 @@ def test_graph_capture_replays(ctx):
         assert_bits_equal(big_out.cpu().numpy(), big_want, f"graph replay {rep} chunked")
 
 
+def test_bound_calls_match_plain_calls(ctx):
+    """ar.bind_reduce: the pre-converted call gives the same bytes as ar_reduce /
+    ar_reduce_add, every time it is invoked."""
+    n = 4096 * 33
+    srcs = [to_device(x) for x in wl.random_partials(9300, 0, 3, n, dist="wide")]
+    row = to_device(wl.residual(9301, 0, 4096))
+    want = torch.empty(n, device="cuda")
+    got = torch.empty(n, device="cuda")
+    log_case("bound calls: plain and residual, single-shot and chunked")
+    for mode in (ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED):
+        for res in (None, row):
+            if res is None:
+                ar.ar_reduce(ctx, [want], srcs, n, ar.AR_F32, ar.AR_BF16, mode)
+            else:
+                ar.ar_reduce_add(ctx, [want], srcs, n, ar.AR_F32, ar.AR_BF16, mode, res)
+            f = ar.bind_reduce(ctx, [got], srcs, n, ar.AR_F32, ar.AR_BF16, mode, residual=res)
+            for _ in range(2):
+                got.fill_(float("nan"))
+                assert f() == ar.AR_OK
+                torch.cuda.synchronize()
+                assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+
+
 def test_graph_capture_every_capturable_path(ctx):
     """One graph holding a call of every capturable kind -- slice + broadcast, the
     residual add (element-wise and broadcast row), a narrow destination, a row-strided
