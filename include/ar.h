@@ -70,9 +70,11 @@ typedef struct ar_ctx ar_ctx;
 typedef enum { AR_F32 = 0, AR_F16 = 1, AR_BF16 = 2 } ar_dtype;
 
 /* Schedules, in the low 8 bits of `mode`.
- *   AR_MODE_AUTO         SINGLE_SHOT when n * sizeof(wire) is below the
- *                        single-shot limit, CHUNKED otherwise; sources in
- *                        pinned host memory select HOST_STAGED.
+ *   AR_MODE_AUTO         SINGLE_SHOT when the wire bytes of all ranks,
+ *                        R * n * sizeof(wire), are below twice the
+ *                        single-shot limit (the limit is per rank at
+ *                        R = 2), CHUNKED otherwise; sources in pinned host
+ *                        memory select HOST_STAGED.
  *   AR_MODE_SINGLE_SHOT  one low-latency launch for decode-sized vectors.
  *   AR_MODE_CHUNKED      one bandwidth-bound launch over the whole tensor,
  *                        work planned in chunks of `chunk_bytes` wire bytes
@@ -120,7 +122,8 @@ typedef enum {
  * AR_STORE_POLICY and AR_HOST_PATH override the defaults when cfg is NULL or
  * the field is zero. */
 typedef struct {
-    size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank; 0 -> 1 MiB */
+    size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank at R = 2
+                                     (2x this over all ranks); 0 -> 1 MiB */
     size_t chunk_bytes;           /* CHUNKED / RS_BCAST plan unit, wire bytes per rank; 0 -> 4 MiB */
     size_t host_chunk_bytes;      /* HOST_STAGED copy unit, source bytes per rank;
                                      0 -> clamp(bytes/2, 512 KiB, 64 MiB) per call */

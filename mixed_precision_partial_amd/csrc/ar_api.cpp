@@ -190,7 +190,13 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
     if (base == AR_MODE_AUTO) {
         if (srcs_on_host) {
             resolved = AR_MODE_HOST_STAGED;
-        } else if (n <= SIZE_MAX / 4 && n * static_cast<size_t>(wire_bytes) < cfg.single_shot_max_bytes) {
+        } else if (n <= SIZE_MAX / (4 * AR_MAX_RANKS) &&
+                   n * static_cast<size_t>(wire_bytes) * static_cast<size_t>(R) <
+                       (cfg.single_shot_max_bytes > SIZE_MAX / 2 ? SIZE_MAX : 2 * cfg.single_shot_max_bytes)) {
+            // the limit is per rank at R = 2 and scales with the total wire bytes
+            // of all ranks: measured on MI355X (graph-replayed kernel time), the
+            // single-shot launch wins below ~2 MiB of wire bytes in total, at
+            // R = 2 (crossing at 1-1.5 MiB per rank) as at R = 8 (256 KiB)
             resolved = AR_MODE_SINGLE_SHOT;
         } else {
             resolved = AR_MODE_CHUNKED;

@@ -121,6 +121,11 @@ def test_auto_mode_threshold():
     assert p.mode == ar.AR_MODE_HOST_STAGED
     rc, p = q(4096, config={"single_shot_max_bytes": 1024})
     assert p.mode == ar.AR_MODE_CHUNKED
+    # more ranks: the limit applies to the wire bytes of all ranks (2 MiB at the default)
+    rc, p = q((2 * MiB) // (8 * 2) - 1, R=8, wire=ar.AR_BF16)
+    assert p.mode == ar.AR_MODE_SINGLE_SHOT
+    rc, p = q((2 * MiB) // (8 * 2), R=8, wire=ar.AR_BF16)
+    assert p.mode == ar.AR_MODE_CHUNKED
 
 
 def test_prefill_chunk_plan():

@@ -22,7 +22,7 @@ F32, F16, BF16 = ar.AR_F32, ar.AR_F16, ar.AR_BF16
 ELEM = {F32: 4, F16: 2, BF16: 2}
 WAVE_TILE = 512                 # elements per wave tile: chunk and slice boundaries
 MAX_LAUNCH = 1 << 30
-SINGLE_SHOT_MAX = 1 << 20       # default AUTO threshold, wire bytes per rank
+SINGLE_SHOT_MAX = 1 << 20       # default AUTO threshold: wire bytes per rank at R = 2
 SIZE_MAX = (1 << 64) - 1
 MODE_BITS = ar.AR_MODE_MASK | ar.AR_SRC_WIRE | ar.AR_SRC_INACTIVE_NULL
 
@@ -69,7 +69,7 @@ def expected(R, n, dst_type, wire_type, mode, dsts, srcs, host, res=None, res_le
     if base == ar.AR_MODE_AUTO:
         if host:
             resolved = ar.AR_MODE_HOST_STAGED
-        elif n * ELEM[wire_type] < SINGLE_SHOT_MAX:
+        elif R * n * ELEM[wire_type] < 2 * SINGLE_SHOT_MAX:
             resolved = ar.AR_MODE_SINGLE_SHOT
         else:
             resolved = ar.AR_MODE_CHUNKED
