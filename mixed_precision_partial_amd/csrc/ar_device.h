@@ -103,12 +103,12 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
 //                16-bit sources into binary32 store half lines per
 //                instruction, which write-back merges in L2 (write-through
 //                doubled their time), and 16-bit destinations measured no
-//                gain.
+//                gain.  The single-shot kernel keeps its stores too: a decode
+//                call then leaves no dirty lines for the end-of-kernel release
+//                (R = 2 x 4096 replayed from a graph: 1.61 against 1.75 us).
 //   kStoreStream non-temporal stores (calls that write as much as they read).
-//   kStoreBack   ordinary write-back (the single-shot kernel).
 constexpr int kStoreKeep = 0;
 constexpr int kStoreStream = 1;
-constexpr int kStoreBack = 2;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -786,7 +786,7 @@ __device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a) {
 // ---------------------------------------------------------------------------
 template <class C>
 __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(LaunchArgs<C::RB> a) {
-    reduce_range<C, 1, false, kStoreBack, kSingleShotBlock, false>(a);
+    reduce_range<C, 1, false, kStoreKeep, kSingleShotBlock, false>(a);
 }
 
 #define MPP_STREAM_REG(NAME, ST, SLICED)                                   \
