@@ -380,3 +380,53 @@ def test_bound_calls_reach_the_library():
     g = ar.bind_reduce(None, [1 << 34], fake, 4096, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
                        residual=1 << 35, residual_len=512)
     assert g() == ar.AR_ERR_INVALID
+
+
+def test_header_is_c_and_matches_the_binding(tmp_path):
+    """tests/c_abi/ar_layout.c, built as C99 with gcc against include/ar.h and
+    linked with libmpp_ar.so, prints the layouts the C compiler chose; every field
+    offset and size must equal the binding's ctypes structures, and a plan computed
+    from C must equal the one the binding returns."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "mixed_precision_partial_amd")
+    exe = str(tmp_path / "ar_layout")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(root, "include"),
+           os.path.join(root, "tests", "c_abi", "ar_layout.c"), "-o", exe, "-L", pkg, "-lmpp_ar",
+           f"-Wl,-rpath,{pkg}"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.splitlines()
+    structs = {"ar_config": ar.ArConfig, "ar_plan": ar.ArPlan, "ar_rows": ar.ArRows}
+    seen = set()
+    for line in out:
+        parts = line.split()
+        if parts[0] == "sizeof":
+            assert ctypes.sizeof(structs[parts[1]]) == int(parts[2]), line
+        elif "." in parts[0] and parts[0].split(".")[0] in structs:
+            sname, field = parts[0].split(".")
+            desc = getattr(structs[sname], field)
+            assert (desc.offset, desc.size) == (int(parts[1]), int(parts[2])), line
+            seen.add((sname, field))
+    for sname, cls in structs.items():
+        assert {f for f, _ in cls._fields_} == {f for s, f in seen if s == sname}, sname
+    status = {int(l.split()[1]): l.split()[2] for l in out if l.startswith("status ")}
+    assert all(status[s] == ar.ar_status_str(s) for s in status)
+    kv = dict(l.split(" ", 1) for l in out if l.startswith(("free_null", "init_null")))
+    assert int(kv["free_null"]) == ar.AR_OK and int(kv["init_null"]) == ar.AR_ERR_INVALID
+    plan_line = next(l for l in out if l.startswith("plan "))
+    vals = plan_line.split()
+    got = {vals[i]: int(vals[i + 1]) for i in range(1, len(vals) - 3, 2)}
+    got["slice1"] = (int(vals[-2]), int(vals[-1]))
+    srcs = [(r + 1) << 36 for r in range(4)]
+    dsts = [(r + 9) << 36 for r in range(4)]
+    rc, p = ar.ar_plan_query(dsts, srcs, 2048 * 8192, ar.AR_F32, ar.AR_F16, ar.AR_MODE_RS_BCAST)
+    assert got["rc"] == rc == ar.AR_OK
+    for k in ("mode", "n_dst", "src_bytes", "wire_bytes", "chunk_elems", "n_chunks", "algo_bytes", "store_nt",
+              "stream_kernel", "active_mask"):
+        assert got[k] == getattr(p, k), k
+    assert got["slice1"] == (p.slice_start[1], p.slice_len[1])
