@@ -442,6 +442,55 @@ def test_bound_calls_match_plain_calls(ctx):
                 assert torch.equal(got.view(torch.int32), want.view(torch.int32))
 
 
+def test_contexts_on_threads_and_streams():
+    """Two host threads, each with its own context and stream, issue interleaved calls
+    (single-shot, chunked, slice + broadcast) at the same time; every result matches the
+    oracle.  The library keeps no global mutable state, so separate contexts need no
+    locking."""
+    import threading
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    cases = []
+    for t in range(2):
+        srcs = wl.random_partials(9400 + t, 0, 4, 200_003, dist="wide")
+        cases.append((srcs, oracle.reduce(srcs, ar.AR_BF16)[0]))
+    errors = []
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(0)
+            c = ar.ar_init(0)
+            stream = torch.cuda.Stream()
+            srcs, want = cases[t]
+            dev = [to_device(x) for x in srcs]
+            outs = [torch.empty(200_003, device="cuda") for _ in range(4)]
+            torch.cuda.synchronize()
+            for k in range(30):
+                mode = (ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST)[k % 3]
+                dsts = outs if mode == ar.AR_MODE_RS_BCAST else outs[:1]
+                with torch.cuda.stream(stream):
+                    for d in dsts:
+                        d.fill_(float("nan"))
+                ar.ar_reduce(c, dsts, dev, 200_003, ar.AR_F32, ar.AR_BF16, mode, stream=stream)
+                stream.synchronize()
+                for d in dsts:
+                    assert_bits_equal(d.cpu().numpy(), want, f"thread {t} call {k} mode {mode}")
+            ar.ar_free(c)
+        except BaseException as e:   # re-raised in the main thread
+            errors.append(e)
+
+    log_case("two threads, two contexts, two streams")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=90)
+    assert not any(th.is_alive() for th in threads), "a worker did not finish"
+    if errors:
+        raise errors[0]
+
+
 def test_graph_capture_every_capturable_path(ctx):
     """One graph holding a call of every capturable kind -- slice + broadcast, the
     residual add (element-wise and broadcast row), a narrow destination, a row-strided
