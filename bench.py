@@ -614,15 +614,34 @@ def other_schedules(torch, ar, wl):
         return s.elapsed_time(e) / reps
 
     ctx = ar.ar_init(0)
+    # the 4-rank broadcast over two rotated sets (1 GiB, beyond the Infinity Cache)
     w = wl.WORKLOADS["slice_bcast_f16"]
-    srcs = [torch.from_numpy(p).cuda() for p in wl.partials(w, 0)]
-    dsts = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.R)]
-    ms = timed(lambda: ar.ar_reduce(ctx, dsts, srcs, w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
-                                    stream=stream), 50)
+    bsets = 2
+    srcs = [[torch.from_numpy(p).cuda() for p in wl.partials(w, k)] for k in range(bsets)]
+    dsts = [[torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.R)] for _ in range(bsets)]
+    kb = [0]
+
+    def brot(fn):
+        def call():
+            i = kb[0] % bsets
+            kb[0] += 1
+            fn(i)
+        return call
+
+    ms = timed(brot(lambda i: ar.ar_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
+                                           stream=stream)), 50)
     b = 2 * w.R * w.n * 4
     out["slice_bcast_f16"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"slice_bcast_f16: {out['slice_bcast_f16']}")
-    del srcs, dsts
+    # the same broadcast with an element-wise fp32 residual (the receiving rank's hidden state)
+    ress = [torch.from_numpy(wl.residual(w.case, 5 + k, w.n)).cuda() for k in range(bsets)]
+    ms = timed(brot(lambda i: ar.ar_reduce_add(ctx, dsts[i], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
+                                               ress[i], stream=stream)), 50)
+    b = 2 * w.R * w.n * 4 + w.n * 4
+    out["slice_bcast_f16_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"slice_bcast_f16_residual: {out['slice_bcast_f16_residual']}")
+    del srcs, dsts, ress
+    torch.cuda.empty_cache()
 
     # fused residual add on the prefill shape (element-wise hidden state, and a
     # broadcast row of 4096), and narrow destinations; rotated sets so the
@@ -653,6 +672,8 @@ def other_schedules(torch, ar, wl):
     out["prefill_row_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_row_residual: {out['prefill_row_residual']}")
     del srcs, dsts, ress
+    # 48 MiB per call: 8 rotated sets (384 MiB) to stay beyond the Infinity Cache
+    sets = 8
     srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_BF16).view(np.int16)).cuda() for p in wl.partials(w, k)]
             for k in range(sets)]
     dsts = [torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(sets)]
@@ -677,10 +698,11 @@ def other_schedules(torch, ar, wl):
     del srcs, dsts
 
     w = wl.WORKLOADS["slice_bcast_f16"]
-    srcs = [torch.from_numpy(wl.as_wire_typed(p, ar.AR_F16).view(np.int16)).cuda() for p in wl.partials(w, 0)]
-    dsts = [torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(w.R)]
-    ms = timed(lambda: ar.ar_reduce(ctx, dsts, srcs, w.n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_RS_BCAST,
-                                    stream=stream), 50)
+    srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_F16).view(np.int16)).cuda() for p in wl.partials(w, k)]
+            for k in range(bsets)]
+    dsts = [[torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(w.R)] for _ in range(bsets)]
+    ms = timed(brot(lambda i: ar.ar_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_RS_BCAST,
+                                           stream=stream)), 50)
     b = w.R * w.n * 2 + w.R * w.n * 2
     out["slice_bcast_f16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"slice_bcast_f16_dst: {out['slice_bcast_f16_dst']}")

@@ -336,14 +336,17 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // VGPRs while R stores stream out: 88 against 95 us at R = 4, fp32
         // sources) and for two 16-bit sources (short tiles, as many bytes
         // written as read), the register kernel elsewhere (up to 16 % faster
-        // for fp32 sources with few destinations).  The LDS-staged kernel has
-        // no residual form.
+        // for fp32 sources with few destinations).  With a residual the
+        // broadcast schedule stays on the LDS-staged kernel (R = 4: 98-102
+        // against 105-108 us element-wise, 88.5 against 90.7 us with a row)
+        // and every other call takes the register kernel (a broadcast row on
+        // the prefill shape: 17.4 against 18.3 us; 8 ranks: 374 against 411 us).
         if (resolved == AR_MODE_SINGLE_SHOT) {
             plan->stream_kernel = 0;
-        } else if (res_kind != 0) {
-            plan->stream_kernel = 1;
         } else if (cfg.stream_kernel != 0) {
             plan->stream_kernel = cfg.stream_kernel;
+        } else if (res_kind != 0) {
+            plan->stream_kernel = resolved == AR_MODE_RS_BCAST ? 2 : 1;
         } else {
             plan->stream_kernel = (resolved == AR_MODE_RS_BCAST || (src_wire && R == 2)) ? 2 : 1;
         }

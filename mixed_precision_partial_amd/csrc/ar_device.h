@@ -625,8 +625,9 @@ __device__ __forceinline__ void stream_reg(const LaunchArgs<C::RB> &a) {
 // flight); while the wave folds and stores the batch in one stage, the loads
 // of its next batch stream into the other.  A lane only ever reads back the
 // 16 B it loaded itself, so the stages need no barrier, only the wait on the
-// wave's own vector-memory counter.  (No residual form: calls with a residual
-// use the register-staged kernel.)
+// wave's own vector-memory counter.  A residual is staged the same way, as
+// U x kResRaw more blocks after the ranks' (cached loads for a broadcast row,
+// which every row reads; non-temporal for an element-wise residual).
 // ---------------------------------------------------------------------------
 #ifndef MPP_LDS_U
 #define MPP_LDS_U 1
@@ -655,6 +656,12 @@ constexpr int lds_batch(bool src_is_wire, int rank_bucket) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// 1 KiB blocks of one LDS stage: the ranks' RB x U x K, then the residual's U x kResRaw.
+template <class C, int U>
+constexpr int lds_rank_blocks() { return C::RB * U * C::kSrcRaw; }
+template <class C, int U>
+constexpr int lds_stage_blocks() { return lds_rank_blocks<C, U>() + (C::RES ? U * C::kResRaw : 0); }
+
 template <class C, int U>
 __device__ __forceinline__ void lds_issue(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
                                           u32x4 (*stage)[kWave]) {
@@ -670,6 +677,23 @@ __device__ __forceinline__ void lds_issue(const LaunchArgs<C::RB> &a, const Rang
                     const char *g = static_cast<const char *>(a.src[r]) + e * (C::SW ? 2 : 4);
                     __builtin_amdgcn_global_load_lds(g, (lds_void *)(&stage[(r * U + u) * K + j][0]),
                                                      16, 0, MPP_LDS_AUX);
+                }
+            }
+        }
+    }
+    if constexpr (C::RES) {
+        constexpr int B0 = lds_rank_blocks<C, U>();
+        const char *base = static_cast<const char *>(a.res);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int j = 0; j < C::kResRaw; ++j) {
+                const char *g = base + res_index(a, o, part_elem<C>(t + u * kWaveTile, lane, j)) * C::kDstBytes;
+                lds_void *l = (lds_void *)(&stage[B0 + u * C::kResRaw + j][0]);
+                if (a.res_reuse) {
+                    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+                } else {
+                    __builtin_amdgcn_global_load_lds(g, l, 16, 0, MPP_LDS_AUX);
                 }
             }
         }
@@ -712,7 +736,6 @@ __device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
 template <class C, int U, int ST>
 __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
                                             u32x4 (*stage)[kWave]) {
-    static_assert(!C::RES, "the LDS-staged kernel has no residual form");
     constexpr int K = C::kSrcRaw;
     const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void *)(&stage[0][lane])));
     Batch<C, U> b;
@@ -724,6 +747,13 @@ __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const Ra
 #pragma unroll
                 for (int j = 0; j < K; ++j) b.src[r][u][j] = lds_read16(base + ((r * U + u) * K + j) * kWave * 16);
         }
+    }
+    if constexpr (C::RES) {
+        constexpr int B0 = lds_rank_blocks<C, U>();
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < C::kResRaw; ++j) b.res[u][j] = lds_read16(base + (B0 + u * C::kResRaw + j) * kWave * 16);
     }
     fold_store<C, U, ST>(a, o, t, lane, b);
 }
@@ -743,8 +773,8 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 
     // loads per stage (vector-memory instructions): active ranks x U x K
     const int RU = a.R < C::RB ? a.R : C::RB;
     const unsigned ranks_mask = RU >= 32 ? ~0u : ((1u << RU) - 1u);
-    const int L = __builtin_popcount(a.active & ranks_mask) * U * C::kSrcRaw;
-    constexpr int kMaxL = C::RB * U * C::kSrcRaw;
+    const int L = __builtin_popcount(a.active & ranks_mask) * U * C::kSrcRaw + (C::RES ? U * C::kResRaw : 0);
+    constexpr int kMaxL = lds_stage_blocks<C, U>();
 
     unsigned t = gw;
     if (t < n_big) lds_issue<C, U>(a, o, (size_t)t * big, lane, stage0);
@@ -773,7 +803,7 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 
 
 template <class C, int ST, bool SLICED>
 __device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a) {
-    constexpr int NB = C::RB * lds_batch(C::SW, C::RB) * C::kSrcRaw;   // 1 KiB blocks per stage
+    constexpr int NB = lds_stage_blocks<C, lds_batch(C::SW, C::RB)>();   // 1 KiB blocks per stage
     __shared__ u32x4 stage0[NB][kWave];
     __shared__ u32x4 stage1[NB][kWave];
     stream_lds_as<C, ST, SLICED>(a, stage0, stage1);
@@ -842,7 +872,8 @@ constexpr int kBuckets = 4;
 // [rank bucket].
 typedef const void *const StreamTable[2][2][kCombos][kBuckets];
 extern const void *const kSingleShot[2][2][kCombos][kBuckets];
-extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM;
+extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,
+    kStreamLdsResM;
 
 #define MPP_STREAM_TABLE(FAMILY, M, RES)                                                         \
     {{MPP_TABLE(k_stream_##FAMILY, M, RES), MPP_TABLE(k_stream_##FAMILY##_sl, M, RES)},          \

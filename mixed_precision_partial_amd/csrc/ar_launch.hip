@@ -116,8 +116,7 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
         fn = res ? (m ? kStreamRegResM : kStreamRegRes)[nt][sl][c][b] : (m ? kStreamRegM : kStreamReg)[nt][sl][c][b];
         break;
     case Family::StreamLds:
-        if (res) return hipErrorNotSupported;
-        fn = (m ? kStreamLdsM : kStreamLds)[nt][sl][c][b];
+        fn = res ? (m ? kStreamLdsResM : kStreamLdsRes)[nt][sl][c][b] : (m ? kStreamLdsM : kStreamLds)[nt][sl][c][b];
         break;
     default: return hipErrorNotSupported;
     }

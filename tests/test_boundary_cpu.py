@@ -298,11 +298,14 @@ def test_residual_rules():
     assert qa(n, A[20], 4096)[0] == ar.AR_ERR_INVALID
     # and it may overlap the sources (read only)
     assert qa(n, A[1], n)[0] == ar.AR_OK
-    # a residual selects the register-staged kernel
+    # with a residual: register-staged automatically (even for two 16-bit sources), LDS-staged
+    # for the broadcast schedule, and an explicit choice is honoured
     rc, p = qa(n, A[35], n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)
     assert p.stream_kernel == 1
     rc, p = qa(n, A[35], n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 2})
-    assert p.stream_kernel == 1
+    assert p.stream_kernel == 2
+    rc, p = qa(n, A[35], n, mode=ar.AR_MODE_RS_BCAST)
+    assert rc == ar.AR_OK and p.stream_kernel == 2
     # narrow destination: the residual has the destination type
     rc, p = qa(n, A[35], n, wire=ar.AR_F16, dst_type=ar.AR_F16)
     assert rc == ar.AR_OK and p.algo_bytes == 2 * n * 2 + n * 2 + n * 2

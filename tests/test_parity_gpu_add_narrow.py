@@ -113,7 +113,8 @@ SHAPES = [(2, 17, 4104), (3, 9, 520), (5, 1001, 8), (8, 3, 65_544), (16, 2, 1_03
 # residual add, binary32 destinations
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kname", ["default", "reg_cached", "reg_streaming", "host_direct", "small_chunks"])
+@pytest.mark.parametrize("kname", ["default", "reg_cached", "reg_streaming", "lds_cached", "lds_streaming",
+                                   "host_direct", "small_chunks"])
 @pytest.mark.parametrize("mode_name", ["single_shot", "chunked", "rs_bcast", "host_staged"])
 def test_residual_every_schedule(kctx, kname, mode_name):
     mode = MODES[mode_name]
@@ -234,7 +235,7 @@ def test_narrow_edge_pairs(kctx, mode_name):
             run_and_check(kctx["default"], srcs, t, MODES[mode_name], what, dst_type=t)
 
 
-@pytest.mark.parametrize("kname", ["default", "reg_streaming", "host_direct"])
+@pytest.mark.parametrize("kname", ["default", "reg_streaming", "lds_cached", "lds_streaming", "host_direct"])
 @pytest.mark.parametrize("mode_name", ["single_shot", "chunked", "rs_bcast", "host_staged"])
 def test_narrow_with_residual_and_inactive(kctx, kname, mode_name):
     rng = np.random.default_rng(15)

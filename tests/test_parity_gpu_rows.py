@@ -138,8 +138,9 @@ def test_rows_every_schedule(kctx, kname, mode_name):
                               src_wire=src_wire, seed=i)
 
 
+@pytest.mark.parametrize("kname", ["default", "lds_cached"])
 @pytest.mark.parametrize("mode_name", list(MODES))
-def test_rows_residual_narrow_inactive(kctx, mode_name):
+def test_rows_residual_narrow_inactive(kctx, kname, mode_name):
     rng = np.random.default_rng(31)
     for i, (rows, cols, ss, ds, rs) in enumerate(SHAPES):
         R = [2, 3, 4, 8, 2, 16][i]
@@ -147,9 +148,9 @@ def test_rows_residual_narrow_inactive(kctx, mode_name):
             for dst_name, dst_type in (("f32", ar.AR_F32), ("bf16", ar.AR_BF16), ("f16", ar.AR_F16)):
                 wire = ar.AR_BF16 if dst_type == ar.AR_F32 else dst_type
                 active = rng.random(R) < 0.75
-                what = (f"rows residual={res_kind} dst={dst_name} {mode_name} {rows}x{cols} R={R} "
+                what = (f"rows residual={res_kind} dst={dst_name} {kname} {mode_name} {rows}x{cols} R={R} "
                         f"active={active.astype(int).tolist()}")
-                run_rows_case(kctx["default"], rows, cols, ss, ds, R, wire, MODES[mode_name], what,
+                run_rows_case(kctx[kname], rows, cols, ss, ds, R, wire, MODES[mode_name], what,
                               dst_type=dst_type, res_kind=res_kind, rs=rs, active=active, seed=100 + i)
 
 

@@ -126,7 +126,8 @@ def check_plan(plan, R, n, dst_type, wire_type, mode, srcs, resolved, res_kind, 
         assert plan.chunk_elems % WAVE_TILE == 0 and plan.chunk_elems <= MAX_LAUNCH
         assert plan.stream_kernel in (1, 2)
         if res_kind:
-            assert plan.stream_kernel == 1     # only the register-staged kernel adds a residual
+            # with a residual: LDS-staged for the broadcast schedule, register-staged otherwise
+            assert plan.stream_kernel == (2 if resolved == ar.AR_MODE_RS_BCAST else 1)
     if resolved == ar.AR_MODE_RS_BCAST:
         pos = 0
         for r in range(R):
