@@ -151,8 +151,9 @@ typedef struct {
  *   out  : receives the context (set to NULL on failure).
  *   cfg  : NULL for defaults (plus AR_* environment overrides).
  * Errors: AR_ERR_INVALID (out NULL, device index out of range, negative or
- *         inconsistent cfg fields), AR_ERR_RUNTIME (stream / event creation),
- *         AR_ERR_NOMEM.  Nothing leaks on failure.
+ *         inconsistent cfg fields), AR_ERR_UNSUPPORTED (the device is not a
+ *         gfx950 part: the library holds gfx950 code only), AR_ERR_RUNTIME
+ *         (stream / event creation), AR_ERR_NOMEM.  Nothing leaks on failure.
  * The context makes `hip_device` current on the calling thread while it
  * creates its resources and restores the previous device afterwards. */
 int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);

@@ -765,6 +765,15 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
     }
     if (hip_device < 0 || hip_device >= count) return AR_ERR_INVALID;
 
+    // the kernels are built for gfx950 only: refuse another part up front
+    // instead of failing at the first launch
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, hip_device) != hipSuccess) {
+        (void)hipGetLastError();
+        return AR_ERR_RUNTIME;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return AR_ERR_UNSUPPORTED;
+
     DeviceGuard guard(hip_device);
     if (!guard.ok) return AR_ERR_RUNTIME;
 
