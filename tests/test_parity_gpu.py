@@ -304,6 +304,24 @@ def test_in_place(ctx):
             assert_bits_equal(d.cpu().numpy(), want, f"in place {mode_name}")
 
 
+def test_aliased_sources(ctx):
+    """The same buffer passed for several ranks (sources are read only, so aliasing them
+    is allowed): the fold sees that partial once per rank that names it."""
+    n = 50_003
+    a, b = wl.random_partials(5100, 0, 2, n, dist="wide")
+    dev_a, dev_b = to_device(a), to_device(b)
+    for mode_name in ("single_shot", "chunked", "rs_bcast"):
+        base = MODES[mode_name]
+        srcs = [dev_a, dev_b, dev_a, dev_a]
+        want = oracle_result([a, b, a, a], ar.AR_F16)
+        dsts = [torch.empty(n, device="cuda") for _ in range(4 if base == ar.AR_MODE_RS_BCAST else 1)]
+        log_case(f"aliased sources {mode_name}")
+        ar.ar_reduce(ctx, dsts, srcs, n, ar.AR_F32, ar.AR_F16, base)
+        torch.cuda.synchronize()
+        for d in dsts:
+            assert_bits_equal(d.cpu().numpy(), want, f"aliased sources {mode_name}")
+
+
 def test_non_default_stream(ctx):
     n = 1 << 20
     srcs = wl.random_partials(6000, 0, 2, n)
