@@ -219,16 +219,40 @@ def bind_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int 
 
     lib = load_library()
     R = len(srcs)
-    head = (ctypes.c_void_p(ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx), _ptr_array(dsts),
-            _ptr_array(srcs), ctypes.c_int(R), ctypes.c_size_t(int(n)), ctypes.c_int(int(dst_type)),
-            ctypes.c_int(int(wire_type)), ctypes.c_uint(int(mode)))
-    st = ctypes.c_void_p(_stream_handle(stream))
+    dst_arr, src_arr = _ptr_array(dsts), _ptr_array(srcs)
+    ctx_val = ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx
+    st_val = _stream_handle(stream)
+    rlen = int(n) if residual_len is None else int(residual_len)
+    if residual is not None and residual_len is None and hasattr(residual, "numel"):
+        rlen = int(residual.numel())
+    fast = _fast_module()
+    if fast is not None:
+        fn = lib.ar_reduce if residual is None else lib.ar_reduce_add
+        return fast.bind(ctypes.cast(fn, ctypes.c_void_p).value, residual is not None, ctx_val or 0,
+                         ctypes.addressof(dst_arr), ctypes.addressof(src_arr), R, int(n), int(dst_type),
+                         int(wire_type), int(mode), _addr(residual) or 0, rlen, st_val or 0,
+                         (dst_arr, src_arr))
+    head = (ctypes.c_void_p(ctx_val), dst_arr, src_arr, ctypes.c_int(R), ctypes.c_size_t(int(n)),
+            ctypes.c_int(int(dst_type)), ctypes.c_int(int(wire_type)), ctypes.c_uint(int(mode)))
+    st = ctypes.c_void_p(st_val)
     if residual is None:
         return functools.partial(lib.ar_reduce, *head, st)
-    rlen = int(n) if residual_len is None else int(residual_len)
-    if residual_len is None and hasattr(residual, "numel"):
-        rlen = int(residual.numel())
     return functools.partial(lib.ar_reduce_add, *head, ctypes.c_void_p(_addr(residual)), ctypes.c_size_t(rlen), st)
+
+
+_fast = None
+
+
+def _fast_module():
+    """The compiled fast-call type (csrc/ar_pycall.c), or None when it was not built."""
+    global _fast
+    if _fast is None:
+        try:
+            from . import _ar_fast
+            _fast = _ar_fast
+        except ImportError:
+            _fast = False
+    return _fast or None
 
 
 def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual,

@@ -85,6 +85,26 @@ def build_library(out: str = LIB_PATH, verbose: bool = False, jobs: int | None =
             if m:
                 print("\n".join(m), file=sys.stderr)
     os.replace(tmp, out)
+    build_fast_call(verbose=verbose)
+    return out
+
+
+def build_fast_call(verbose: bool = False) -> str:
+    """Compile csrc/ar_pycall.c (a CPython type holding one pre-converted call of the
+    C ABI; no GPU code) with the host C compiler into _ar_fast<EXT_SUFFIX>."""
+    import sysconfig
+
+    src = os.path.join(CSRC, "ar_pycall.c")
+    out = os.path.join(HERE, "_ar_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
+    cc = os.environ.get("CC", "gcc")
+    cmd = [cc, "-O2", "-shared", "-fPIC", "-Wall", "-Werror", f"-I{sysconfig.get_paths()['include']}", src,
+           "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    rc, msgs = _run(cmd)
+    if rc != 0:
+        raise RuntimeError("building the fast-call module failed:\n" + "\n".join(msgs))
+    os.replace(out + ".tmp", out)
     return out
 
 

@@ -385,6 +385,19 @@ def test_bound_calls_reach_the_library():
     assert g() == ar.AR_ERR_INVALID
 
 
+def test_bound_calls_use_the_compiled_call_type():
+    """With the fast-call module built (build() builds it), bound calls are instances of
+    its C type, which takes no arguments; without it the binding falls back to ctypes."""
+    fast = ar._fast_module()
+    if fast is None:
+        pytest.skip("fast-call module not built")
+    f = ar.bind_reduce(None, [1 << 34], [1 << 33, (1 << 33) + (1 << 20)], 4096)
+    assert isinstance(f, fast.BoundCall)
+    assert f() == ar.AR_ERR_INVALID
+    with pytest.raises(TypeError):
+        f(1)
+
+
 def test_header_is_c_and_matches_the_binding(tmp_path):
     """tests/c_abi/ar_layout.c, built as C99 with gcc against include/ar.h and
     linked with libmpp_ar.so, prints the layouts the C compiler chose; every field
