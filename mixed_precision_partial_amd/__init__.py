@@ -214,7 +214,7 @@ def bind_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int 
     the status (no Python-side checks per call; the library still validates
     every call).  For latency-bound callers that issue the same call shape on
     the same buffers many times.  With ``residual`` it binds ``ar_reduce_add``.
-    The caller keeps the bound buffers alive while the callable is in use."""
+    The caller keeps the context and the bound buffers alive while the callable is in use."""
     import functools
 
     lib = load_library()
