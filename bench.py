@@ -180,6 +180,18 @@ def main() -> int:
         for _ in range(reps):
             oracle.reduce(host_sets[0], w.wire)
         cpu_s = time.perf_counter() - t
+        # the same oracle on T host threads, each over its own contiguous element range
+        # (the C oracle runs with the interpreter lock released)
+        from concurrent.futures import ThreadPoolExecutor
+
+        T = max(1, min(16, os.cpu_count() or 1))
+        bounds = [(n * k // T, n * (k + 1) // T) for k in range(T)]
+        mt_reps = max(1, min(reps, int(args.cpu_seconds / 2 / max(one / T, 1e-3))))
+        with ThreadPoolExecutor(max_workers=T) as pool:
+            t = time.perf_counter()
+            for _ in range(mt_reps):
+                list(pool.map(lambda b: oracle.reduce([x[b[0]:b[1]] for x in host_sets[0]], w.wire), bounds))
+            mt_s = time.perf_counter() - t
         cpu_baseline = {
             "value": round(algo_bytes * reps / cpu_s / 1e9, 3),
             "unit": "GB/s",
@@ -187,6 +199,8 @@ def main() -> int:
             "kind": "oracle",
             "cpu_model": cpu_model(),
             "host_cores_visible": os.cpu_count(),
+            "all_threads": {"value": round(algo_bytes * mt_reps / mt_s / 1e9, 3), "threads": T,
+                            "sample": f"{mt_reps} full calls split over {T} threads"},
             "sample": f"{reps + 1} full calls of the same 2048x4096 R=2 bf16-wire reduce "
                       f"({cpu_s + one:.1f} s, single-threaded scalar C oracle)",
         }
