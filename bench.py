@@ -296,11 +296,31 @@ PROFILE_CASES = {
                                 sets=1, host=True,
                                 what="R=8 bf16 partials [8192x8192] in pinned host memory, HOST_STAGED, "
                                      "kernel reads them directly over PCIe"),
+    # the adjacent forms: residual add, narrow destination, row-strided view
+    "prefill_residual": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1, sets=4,
+                             host=False, res="elementwise",
+                             what="prefill reduce + element-wise fp32 residual (CHUNKED)"),
+    "prefill_row_residual": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1, sets=8,
+                                 host=False, res=4096,
+                                 what="prefill reduce + broadcast row of 4096 (CHUNKED)"),
+    "prefill_bf16_dst": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=2, n_dst=1, sets=8,
+                             host=False, dst_bytes=2,
+                             what="prefill shape, bf16 partials into a bf16 destination (CHUNKED)"),
+    "slice_bcast_f16_residual": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=4, n_dst=4,
+                                     sets=2, host=False, res="elementwise",
+                                     what="slice + broadcast to 4 destinations + element-wise fp32 residual"),
+    "rows_prefill_block_bias": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1,
+                                    sets=6, host=False, res=4096, rows=(2048, 4096, 4608, 4352),
+                                    what="row-strided prefill block (2048 x 4096 in rows of 4608 / 4352) "
+                                         "+ bias row"),
 }
 
 
 def case_algo_bytes(case: dict) -> int:
-    return case["R"] * case["n"] * case["src_bytes"] + case["n_dst"] * case["n"] * 4
+    db = case.get("dst_bytes", 4)
+    res = case.get("res")
+    res_b = 0 if res is None else (case["n"] if res == "elementwise" else res) * db
+    return case["R"] * case["n"] * case["src_bytes"] + case["n_dst"] * case["n"] * db + res_b
 
 
 TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py"
@@ -356,7 +376,10 @@ def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
             lines += ["", f"Reduce kernel `{_short(top['Name'])}`: average {avg_us:.3f} us per launch = "
                           f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch: "
                           f"{case['R']} x {case['n']} x {case['src_bytes']} B read, {case['n_dst']} x "
-                          f"{case['n']} x 4 B written)."]
+                          f"{case['n']} x {case.get('dst_bytes', 4)} B written"
+                          + ("" if case.get("res") is None else
+                             f", residual {case['res'] if case['res'] != 'elementwise' else case['n']} x "
+                             f"{case.get('dst_bytes', 4)} B read") + ")."]
             if case["host"]:
                 host_b = case["R"] * case["n"] * case["src_bytes"]
                 lines += ["", f"The sources cross PCIe: {host_b} B read from pinned host memory per launch = "
@@ -448,17 +471,47 @@ def profile_pass(torch, ar, wl, args):
             return h
         return t
 
-    srcs = [[make_src() for _ in range(R)] for _ in range(S)]
-    dsts = [[torch.empty(n, device="cuda") for _ in range(case["n_dst"])] for _ in range(S)]
+    narrow = case.get("dst_bytes", 4) == 2
+    ddt = torch.int16 if narrow else torch.float32
+    dst_type = wire if narrow else ar.AR_F32
+    if narrow:
+        mode &= ~ar.AR_SRC_WIRE          # a narrow destination's sources hold its type anyway
+    rows = case.get("rows")
+    src_len = n if rows is None else rows[0] * rows[2]
+    dst_len = n if rows is None else rows[0] * rows[3]
+
+    def make(length, dt):
+        t = torch.randn(length, device="cuda").to(dt)
+        if case["host"]:
+            h = torch.empty(length, dtype=dt, pin_memory=True)
+            h.copy_(t)
+            return h
+        return t
+
+    srcs = [[make(src_len, sdt).view(torch.int16) if narrow else make(src_len, sdt) for _ in range(R)]
+            for _ in range(S)]
+    dsts = [[torch.empty(dst_len, device="cuda", dtype=ddt) for _ in range(case["n_dst"])] for _ in range(S)]
+    res = case.get("res")
+    ress = None
+    if res is not None:
+        rl = n if res == "elementwise" else res
+        ress = [torch.randn(rl, device="cuda") for _ in range(S)]
     torch.cuda.synchronize()
     ctx = ar.ar_init(0)
     stream = torch.cuda.current_stream()
     launches = max(3 * S, 12)
     for k in range(launches):
-        ar.ar_reduce(ctx, dsts[k % S], srcs[k % S], n, ar.AR_F32, wire, mode, stream=stream)
+        i = k % S
+        if rows is not None:
+            ar.ar_reduce_rows(ctx, dsts[i], srcs[i], rows[0], rows[1], rows[2], rows[3], dst_type, wire, mode,
+                              residual=ress[i] if ress else None, res_stride=0, stream=stream)
+        elif ress is not None:
+            ar.ar_reduce_add(ctx, dsts[i], srcs[i], n, dst_type, wire, mode, ress[i], stream=stream)
+        else:
+            ar.ar_reduce(ctx, dsts[i], srcs[i], n, dst_type, wire, mode, stream=stream)
     torch.cuda.synchronize()
     ar.ar_free(ctx)
-    del srcs, dsts
+    del srcs, dsts, ress
     nc = CALIBRATION_BYTES // 4
     a = [torch.randn(nc, device="cuda") for _ in range(4)]
     b = [torch.empty(nc, device="cuda") for _ in range(4)]
