@@ -309,6 +309,9 @@ PROFILE_CASES = {
     "slice_bcast_f16_residual": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=4, n_dst=4,
                                      sets=2, host=False, res="elementwise",
                                      what="slice + broadcast to 4 destinations + element-wise fp32 residual"),
+    "prefill_r4_one_inactive": dict(R=4, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1, sets=4,
+                                    host=False, inactive=(2,),
+                                    what="4 ranks on the prefill shape, rank 2 inactive (+0.0), CHUNKED"),
     "rows_prefill_block_bias": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1,
                                     sets=6, host=False, res=4096, rows=(2048, 4096, 4608, 4352),
                                     what="row-strided prefill block (2048 x 4096 in rows of 4608 / 4352) "
@@ -320,7 +323,8 @@ def case_algo_bytes(case: dict) -> int:
     db = case.get("dst_bytes", 4)
     res = case.get("res")
     res_b = 0 if res is None else (case["n"] if res == "elementwise" else res) * db
-    return case["R"] * case["n"] * case["src_bytes"] + case["n_dst"] * case["n"] * db + res_b
+    active = case["R"] - len(case.get("inactive", ()))   # an inactive rank is not read
+    return active * case["n"] * case["src_bytes"] + case["n_dst"] * case["n"] * db + res_b
 
 
 TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py"
@@ -375,7 +379,8 @@ def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
             avg_us = float(top["AverageNs"]) / 1e3
             lines += ["", f"Reduce kernel `{_short(top['Name'])}`: average {avg_us:.3f} us per launch = "
                           f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch: "
-                          f"{case['R']} x {case['n']} x {case['src_bytes']} B read, {case['n_dst']} x "
+                          f"{case['R'] - len(case.get('inactive', ()))} x {case['n']} x {case['src_bytes']} B read, "
+                          f"{case['n_dst']} x "
                           f"{case['n']} x {case.get('dst_bytes', 4)} B written"
                           + ("" if case.get("res") is None else
                              f", residual {case['res'] if case['res'] != 'elementwise' else case['n']} x "
@@ -488,8 +493,11 @@ def profile_pass(torch, ar, wl, args):
             return h
         return t
 
-    srcs = [[make(src_len, sdt).view(torch.int16) if narrow else make(src_len, sdt) for _ in range(R)]
-            for _ in range(S)]
+    inactive = set(case.get("inactive", ()))
+    if inactive:
+        mode |= ar.AR_SRC_INACTIVE_NULL
+    srcs = [[None if r in inactive else (make(src_len, sdt).view(torch.int16) if narrow else make(src_len, sdt))
+             for r in range(R)] for _ in range(S)]
     dsts = [[torch.empty(dst_len, device="cuda", dtype=ddt) for _ in range(case["n_dst"])] for _ in range(S)]
     res = case.get("res")
     ress = None
@@ -749,6 +757,15 @@ def other_schedules(torch, ar, wl):
     b = w.R * w.n * 2 + w.n * 2
     out["prefill_bf16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_bf16_dst: {out['prefill_bf16_dst']}")
+    del srcs, dsts
+    # four ranks on the prefill shape with rank 2 inactive (it contributes +0.0 and is not read)
+    srcs = [[None if r == 2 else torch.randn(w.n, device="cuda") for r in range(4)] for _ in range(sets)]
+    dsts = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(sets)]
+    ms = timed(rot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire,
+                                          ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL, stream=stream)), 200)
+    b = 3 * w.n * 4 + w.n * 4
+    out["prefill_r4_one_inactive"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"prefill_r4_one_inactive: {out['prefill_r4_one_inactive']}")
     del srcs, dsts
     # row-strided: the prefill block as a view of wider rows (2048 x 4096 in rows of
     # 4608 for the partials, 4352 for the destination) with a broadcast bias row
