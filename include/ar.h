@@ -111,7 +111,7 @@ enum {
 typedef enum {
     AR_OK              = 0,
     AR_ERR_INVALID     = 1,  /* bad argument: see ar_reduce                */
-    AR_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    AR_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement */
     AR_ERR_NOMEM       = 3,  /* allocation failed                           */
     AR_ERR_RUNTIME     = 4   /* a HIP runtime call failed                   */
 } ar_status;
