@@ -306,6 +306,10 @@ PROFILE_CASES = {
     "prefill_bf16_dst": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=2, n_dst=1, sets=8,
                              host=False, dst_bytes=2,
                              what="prefill shape, bf16 partials into a bf16 destination (CHUNKED)"),
+    "slice_bcast_f16_dst": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=2, n_dst=4, sets=4,
+                                host=False, dst_bytes=2,
+                                what="slice + broadcast: R=4 fp16 partials [2048x8192] into 4 fp16 "
+                                     "destinations, RS_BCAST"),
     "slice_bcast_f16_residual": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=4, n_dst=4,
                                      sets=2, host=False, res="elementwise",
                                      what="slice + broadcast to 4 destinations + element-wise fp32 residual"),
@@ -464,7 +468,7 @@ def profile_pass(torch, ar, wl, args):
     wire = {"bf16": ar.AR_BF16, "f16": ar.AR_F16}[case["wire"]]
     mode = {"chunked": ar.AR_MODE_CHUNKED, "rs_bcast": ar.AR_MODE_RS_BCAST,
             "host_staged": ar.AR_MODE_HOST_STAGED}[case["mode"]]
-    sdt = torch.float32 if case["src_bytes"] == 4 else torch.bfloat16
+    sdt = torch.float32 if case["src_bytes"] == 4 else {"bf16": torch.bfloat16, "f16": torch.float16}[case["wire"]]
     if case["src_bytes"] == 2:
         mode |= ar.AR_SRC_WIRE
 
@@ -781,7 +785,11 @@ def other_schedules(torch, ar, wl):
     log(f"rows_prefill_block_bias: {out['rows_prefill_block_bias']}")
     del srcs, dsts
 
+    # 16-bit partials and destinations: a set is half the fp32 one's 512 MiB, so four
+    # sets keep the rotation at 1 GiB (with two, write-through variants read 10-15 %
+    # faster than cold because the Infinity Cache still holds part of the set)
     w = wl.WORKLOADS["slice_bcast_f16"]
+    bsets = 4
     srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_F16).view(np.int16)).cuda() for p in wl.partials(w, k)]
             for k in range(bsets)]
     dsts = [[torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(w.R)] for _ in range(bsets)]
