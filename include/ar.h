@@ -274,8 +274,9 @@ typedef struct {
     size_t n_chunks;      /* ceil(n / chunk_elems)                          */
     size_t slice_start[AR_MAX_RANKS]; /* RS_BCAST: first element of rank r  */
     size_t slice_len[AR_MAX_RANKS];   /* RS_BCAST: elements of rank r       */
-    size_t algo_bytes;    /* algorithmic bytes: R*n*src_bytes + n_dst*n*dst_bytes
-                             (+ residual_len*dst_bytes with a residual)      */
+    size_t algo_bytes;    /* algorithmic bytes: A*n*src_bytes + n_dst*n*dst_bytes
+                             (+ residual_len*dst_bytes with a residual), A =
+                             active ranks (an inactive rank is not read)     */
     int    store_nt;      /* 1: streaming (non-temporal) destination stores */
     int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
     int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged   */

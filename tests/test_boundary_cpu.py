@@ -238,8 +238,14 @@ def test_inactive_ranks_flag():
     assert q(n, srcs=srcs, mode=ar.AR_MODE_CHUNKED)[0] == ar.AR_ERR_INVALID
     rc, p = q(n, srcs=srcs, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL)
     assert rc == ar.AR_OK and p.active_mask == 0b101
+    # inactive ranks are not read: two sources' bytes plus the destination's
+    assert p.algo_bytes == 2 * n * 4 + n * 4
+    # the store policy weighs the call's shape (3 ranks against 1 destination): kept
+    assert p.store_nt == 0
+    rc, p = q(n, srcs=[A[1], 0], mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL)
+    assert rc == ar.AR_OK and p.algo_bytes == n * 4 + n * 4 and p.store_nt == 0
     rc, p = q(n, srcs=[0, 0], mode=ar.AR_MODE_RS_BCAST | ar.AR_SRC_INACTIVE_NULL)
-    assert rc == ar.AR_OK and p.active_mask == 0 and p.n_dst == 2
+    assert rc == ar.AR_OK and p.active_mask == 0 and p.n_dst == 2 and p.algo_bytes == 2 * n * 4
     rc, p = q(n, mode=ar.AR_MODE_CHUNKED)
     assert p.active_mask == 0b11
     # a NULL destination stays invalid
