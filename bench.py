@@ -212,6 +212,8 @@ def main() -> int:
     if not args.no_decode:
         extras["decode_bf16"] = decode_latency(torch, ar, wl)
     if args.extras:
+        # the fp32-wire decode vector: the same latency-bound call without a conversion
+        extras["decode_f32"] = decode_latency(torch, ar, wl, "decode_f32", floors=False)
         extras.update(other_schedules(torch, ar, wl))
 
     traffic = measured_traffic(algo_bytes)
@@ -561,11 +563,12 @@ def ceilings(torch, n, sets):
     return out
 
 
-def decode_latency(torch, ar, wl):
-    """10,000 sequential single-shot calls on fresh seeded data (all pre-staged in HBM)."""
-    w = wl.WORKLOADS["decode_bf16"]
-    calls, n, R = w.calls, w.n, w.R
-    log(f"decode: staging {calls} calls of R={R} x n={n}")
+def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
+    """10,000 sequential single-shot calls on fresh seeded data (all pre-staged in HBM);
+    `floors` adds the smallest torch kernel timed the same way."""
+    w = wl.WORKLOADS[name]
+    calls, n, R = max(w.calls, 10_000), w.n, w.R
+    log(f"{name}: staging {calls} calls of R={R} x n={n}")
     host = np.empty((calls, R, n), dtype=np.float32)
     for c in range(calls):
         for r, p in enumerate(wl.partials(w, c)):
@@ -635,6 +638,19 @@ def decode_latency(torch, ar, wl):
         stream.synchronize()
         lat[i] = (time.perf_counter() - t) * 1e6
     ar.ar_free(ctx)
+    res = {
+        "us_per_call_async": round(us_async, 3),
+        "us_per_call_async_bound": round(us_async_bound, 3),
+        "host_enqueue_us_per_call_bound": round(host_bound_s * 1e6 / calls, 3),
+        "us_per_call_graph_replay": round(us_graph, 3),
+        "host_enqueue_us_per_call": round(host_s * 1e6 / calls, 3),
+        "us_per_call_sync_p50": round(float(np.percentile(lat, 50)), 2),
+        "us_per_call_sync_p99": round(float(np.percentile(lat, 99)), 2),
+        "calls": calls,
+    }
+    if not floors:
+        log(f"{name}: {res}")
+        return res
     # launch floor for context: the smallest torch kernel (a 1-element fill) issued
     # the same way, async and replayed from a graph
     one = torch.empty(1, device="cuda")
@@ -660,19 +676,9 @@ def decode_latency(torch, ar, wl):
     torch.cuda.synchronize()
     floor_graph = start.elapsed_time(end) * 1e3 / (reps * graph_calls)
     del g
-    res = {
-        "floor_1elem_fill_us_async": round(floor_async, 3),
-        "floor_1elem_fill_us_graph_replay": round(floor_graph, 3),
-        "us_per_call_async": round(us_async, 3),
-        "us_per_call_async_bound": round(us_async_bound, 3),
-        "host_enqueue_us_per_call_bound": round(host_bound_s * 1e6 / calls, 3),
-        "us_per_call_graph_replay": round(us_graph, 3),
-        "host_enqueue_us_per_call": round(host_s * 1e6 / calls, 3),
-        "us_per_call_sync_p50": round(float(np.percentile(lat, 50)), 2),
-        "us_per_call_sync_p99": round(float(np.percentile(lat, 99)), 2),
-        "calls": calls,
-    }
-    log(f"decode: {res}")
+    res = {"floor_1elem_fill_us_async": round(floor_async, 3),
+           "floor_1elem_fill_us_graph_replay": round(floor_graph, 3), **res}
+    log(f"{name}: {res}")
     return res
 
 
