@@ -42,6 +42,20 @@ HIPCC_FLAGS = [
 ]
 
 
+# The non-residual streaming kernels' eight leading scalar parameters are
+# preloaded into SGPRs at dispatch.  The residual and single-shot kernels read
+# their arguments from the argument block (the leading parameters stay unused
+# there), so their tables are built without preloading.
+PRELOAD_FLAGS = ["-mllvm", "-amdgpu-kernarg-preload-count=8"]
+
+
+def preload_flags(src: str) -> list[str]:
+    name = os.path.basename(src)
+    if name.startswith("ar_k_") and "_res" not in name and name != "ar_k_single.hip":
+        return PRELOAD_FLAGS
+    return []
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")
@@ -63,7 +77,7 @@ def build_library(out: str = LIB_PATH, verbose: bool = False, jobs: int | None =
     srcs = sources()
     objs = [os.path.join(OBJ_DIR, os.path.basename(s) + ".o") for s in srcs]
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
-    cmds = [[hipcc(), *HIPCC_FLAGS, *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[hipcc(), *HIPCC_FLAGS, *preload_flags(s), *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
     if verbose:
         for c in cmds:
             print(" ".join(c), flush=True)

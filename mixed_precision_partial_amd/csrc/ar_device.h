@@ -360,6 +360,18 @@ __device__ __forceinline__ bool rank_used(const LaunchArgs<C::RB> &a, int r) {
     return r < 2 || r < a.R;
 }
 
+// A launch argument read where it is used: the empty asm keeps the compiler
+// from hoisting work on it above the batch's loads, which would make every
+// wave wait for its scalar fetch before issuing them (the destinations after
+// the first are not among the preloaded parameters).
+__device__ __forceinline__ void *at_use(void *p) {
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v));
+    unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32));
+    asm volatile("" : "+s"(lo), "+s"(hi));
+    return reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Registers of one batch of U wave tiles.
 template <class C, int U>
 struct Batch {
@@ -432,7 +444,7 @@ __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size
     }
 #pragma unroll
     for (int d = 0; d < C::RB; ++d) {
-        if (d < a.n_dst) tile_store<C, ST>(a.dst[d], td, lane, acc);
+        if (d < a.n_dst) tile_store<C, ST>(d == 0 ? a.dst[0] : at_use(a.dst[d]), td, lane, acc);
     }
 }
 
@@ -511,6 +523,9 @@ __device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, const 
 // (stride = cols) and the rows of row-strided tensors alike.  Both forms only
 // read launch arguments at fixed offsets (blockIdx.y is known at wave
 // start), so a wave fetches everything it needs in one batch of scalar loads.
+// Kernels call it on their own argument block for slice ranges (an indexed
+// read of kernel arguments is one scalar load) and never on a local copy of
+// the block, whose arrays would then have to live in scratch memory.
 template <bool SLICED, class A>
 __device__ __forceinline__ void range_of(const A &a, RangeOff &o, unsigned &len) {
     const unsigned y = blockIdx.y;
@@ -550,16 +565,13 @@ __device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, const Ra
 // over the `a.waves` waves of the range, then the remainder.  BLOCK is the
 // workgroup size the kernel is always launched with (no read of blockDim).
 template <class C, int U, bool NT, int ST, int BLOCK, bool SLICED>
-__device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a) {
+__device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len) {
     constexpr unsigned wpb = BLOCK / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     // the wave's index, read from lane 0 so the compiler keeps it (and every
     // tile address derived from it) in scalar registers
     const unsigned gw = blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const unsigned nw = a.waves;
-    RangeOff o;
-    unsigned len;
-    range_of<SLICED>(a, o, len);
 
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
@@ -614,8 +626,8 @@ constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
 }
 
 template <class C, int ST, bool SLICED>
-__device__ __forceinline__ void stream_reg(const LaunchArgs<C::RB> &a) {
-    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, stream_block(C::RB), SLICED>(a);
+__device__ __forceinline__ void stream_reg(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len) {
+    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, stream_block(C::RB), SLICED>(a, o, len);
 }
 
 // ---------------------------------------------------------------------------
@@ -759,14 +771,12 @@ __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const Ra
 }
 
 template <class C, int ST, bool SLICED>
-__device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
+__device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len,
+                                              u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
     constexpr int U = lds_batch(C::SW, C::RB);
     const int lane = threadIdx.x;
     const unsigned gw = blockIdx.x;
     const unsigned nw = a.waves;
-    RangeOff o;
-    unsigned len;
-    range_of<SLICED>(a, o, len);
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
 
@@ -802,44 +812,115 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, u32x4 
 }
 
 template <class C, int ST, bool SLICED>
-__device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a) {
+__device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len) {
     constexpr int NB = lds_stage_blocks<C, lds_batch(C::SW, C::RB)>();   // 1 KiB blocks per stage
     __shared__ u32x4 stage0[NB][kWave];
     __shared__ u32x4 stage1[NB][kWave];
-    stream_lds_as<C, ST, SLICED>(a, stage0, stage1);
+    stream_lds_as<C, ST, SLICED>(a, o, len, stage0, stage1);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameters.  The fields a wave reads before its first load of a
+// strided range -- the launch length, the range length, the wave count, the
+// source and destination strides, the first two sources and the first
+// destination (with the destination count in the wave count's top byte) --
+// come first, as plain scalars (14 dwords), so that the dispatcher preloads
+// them into SGPRs (the non-residual streaming tables are built with kernarg
+// preloading for the leading parameters; an aggregate parameter is never
+// preloaded).  The argument block that follows holds every field, these
+// included.  Measured on MI355X with a minimal kernel of the prefill access
+// pattern: 15.53 against 15.85 us per call -- every wave of a one-shot grid
+// starts together, so the scalar fetch of its arguments sits once on the
+// critical path of the call.
+// ---------------------------------------------------------------------------
+#define MPP_HOT_PARAMS uint64_t hot_n, unsigned hot_cols, unsigned hot_waves_ndst, uint64_t hot_src_stride, \
+                       uint64_t hot_dst_stride, const void *hot_src0, const void *hot_src1, void *hot_dst0
+
+template <int NR>
+__device__ __forceinline__ LaunchArgs<NR> with_hot(const LaunchArgs<NR> &a, uint64_t n, unsigned cols,
+                                                   unsigned waves_ndst, uint64_t src_stride, uint64_t dst_stride,
+                                                   const void *src0, const void *src1, void *dst0) {
+    LaunchArgs<NR> b = a;
+    b.n = n;
+    b.cols = cols;
+    b.waves = waves_ndst & 0xffffffu;
+    b.n_dst = static_cast<int>(waves_ndst >> 24);
+    b.src_stride = src_stride;
+    b.dst_stride = dst_stride;
+    b.src[0] = src0;
+    b.src[1] = src1;
+    b.dst[0] = dst0;
+    return b;
+}
+#define MPP_HOT_ARGS hot_n, hot_cols, hot_waves_ndst, hot_src_stride, hot_dst_stride, hot_src0, hot_src1, hot_dst0
+
+// Entry of a kernel with preloaded fields: its working copy of the arguments
+// with those fields substituted, and its workgroup's range -- slice ranges
+// read from the argument block itself, strided ranges from the copy.
+template <class C, bool SLICED, class F>
+__device__ __forceinline__ void hot_entry(const LaunchArgs<C::RB> &a, uint64_t n, unsigned cols, unsigned waves_ndst,
+                                          uint64_t src_stride, uint64_t dst_stride, const void *src0,
+                                          const void *src1, void *dst0, F &&run) {
+    const LaunchArgs<C::RB> h = with_hot(a, n, cols, waves_ndst, src_stride, dst_stride, src0, src1, dst0);
+    RangeOff o;
+    unsigned len;
+    if constexpr (SLICED) {
+        range_of<true>(a, o, len);
+    } else {
+        range_of<false>(h, o, len);
+    }
+    run(h, o, len);
 }
 
 // ---------------------------------------------------------------------------
 // Kernels.  Single-shot: one wave tile per wave.  Streaming (register-staged
-// or LDS-staged): ST = the store policy (kStoreKeep / kStoreStream), SLICED = the per-rank slice
-// ranges of the broadcast schedule.
+// or LDS-staged): ST = the store policy (kStoreKeep / kStoreStream), SLICED =
+// the per-rank slice ranges of the broadcast schedule.  The plain streaming
+// kernels and the residual ones (`_res`) differ only in their parameters:
+// the plain ones take the preloaded leading fields; the residual and
+// single-shot kernels take the argument block alone and are built without
+// preloading.  Measured on MI355X: the substituted copies held live through
+// the residual loop cost 8 VGPRs and one wave per SIMD (prefill + bias row
+// 17.5 against 17.3 us, the row-strided block + bias 17.7 against 17.4 us),
+// and the decode call does not gain (1.77 against 1.74 us per graph-replayed
+// call), while the plain reduce does (R = 8: 371-378 against 378-386 us;
+// 4-destination fp16 broadcast: 45.7-46.4 against 46.7-47.1 us; prefill:
+// 16.09-16.16 against 16.16-16.20 us).
 // ---------------------------------------------------------------------------
 template <class C>
 __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(LaunchArgs<C::RB> a) {
-    reduce_range<C, 1, false, kStoreKeep, kSingleShotBlock, false>(a);
+    RangeOff o;
+    unsigned len;
+    range_of<false>(a, o, len);
+    reduce_range<C, 1, false, kStoreKeep, kSingleShotBlock, false>(a, o, len);
 }
 
-#define MPP_STREAM_REG(NAME, ST, SLICED)                                   \
-    template <class C>                                                   \
-    __global__ __launch_bounds__(stream_block(C::RB)) void NAME(LaunchArgs<C::RB> a) { \
-        stream_reg<C, ST, SLICED>(a);                                    \
+#define MPP_STREAM_KERNELS(NAME, BLOCK, BODY, ST, SLICED)                                  \
+    template <class C>                                                                  \
+    __global__ __launch_bounds__(BLOCK) void NAME(MPP_HOT_PARAMS, LaunchArgs<C::RB> a) {   \
+        hot_entry<C, SLICED>(a, MPP_HOT_ARGS,                                           \
+                             [](const LaunchArgs<C::RB> &x, const RangeOff &o, unsigned len) { \
+                                 BODY<C, ST, SLICED>(x, o, len);                        \
+                             });                                                        \
+    }                                                                                   \
+    template <class C>                                                                  \
+    __global__ __launch_bounds__(BLOCK) void NAME##_res(LaunchArgs<C::RB> a) {           \
+        RangeOff o;                                                                     \
+        unsigned len;                                                                   \
+        range_of<SLICED>(a, o, len);                                                    \
+        BODY<C, ST, SLICED>(a, o, len);                                                 \
     }
-MPP_STREAM_REG(k_stream_reg, kStoreKeep, false)
-MPP_STREAM_REG(k_stream_reg_nts, kStoreStream, false)
-MPP_STREAM_REG(k_stream_reg_sl, kStoreKeep, true)
-MPP_STREAM_REG(k_stream_reg_nts_sl, kStoreStream, true)
-#undef MPP_STREAM_REG
-
-#define MPP_STREAM_LDS(NAME, ST, SLICED)                                \
-    template <class C>                                                \
-    __global__ __launch_bounds__(kLdsBlock) void NAME(LaunchArgs<C::RB> a) { \
-        stream_lds<C, ST, SLICED>(a);                                 \
-    }
-MPP_STREAM_LDS(k_stream_lds, kStoreKeep, false)
-MPP_STREAM_LDS(k_stream_lds_nts, kStoreStream, false)
-MPP_STREAM_LDS(k_stream_lds_sl, kStoreKeep, true)
-MPP_STREAM_LDS(k_stream_lds_nts_sl, kStoreStream, true)
-#undef MPP_STREAM_LDS
+MPP_STREAM_KERNELS(k_stream_reg, stream_block(C::RB), stream_reg, kStoreKeep, false)
+MPP_STREAM_KERNELS(k_stream_reg_nts, stream_block(C::RB), stream_reg, kStoreStream, false)
+MPP_STREAM_KERNELS(k_stream_reg_sl, stream_block(C::RB), stream_reg, kStoreKeep, true)
+MPP_STREAM_KERNELS(k_stream_reg_nts_sl, stream_block(C::RB), stream_reg, kStoreStream, true)
+MPP_STREAM_KERNELS(k_stream_lds, kLdsBlock, stream_lds, kStoreKeep, false)
+MPP_STREAM_KERNELS(k_stream_lds_nts, kLdsBlock, stream_lds, kStoreStream, false)
+MPP_STREAM_KERNELS(k_stream_lds_sl, kLdsBlock, stream_lds, kStoreKeep, true)
+MPP_STREAM_KERNELS(k_stream_lds_nts_sl, kLdsBlock, stream_lds, kStoreStream, true)
+#undef MPP_STREAM_KERNELS
+#undef MPP_HOT_ARGS
+#undef MPP_HOT_PARAMS
 
 }  // namespace
 
@@ -875,8 +956,8 @@ extern const void *const kSingleShot[2][2][kCombos][kBuckets];
 extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,
     kStreamLdsResM;
 
-#define MPP_STREAM_TABLE(FAMILY, M, RES)                                                         \
-    {{MPP_TABLE(k_stream_##FAMILY, M, RES), MPP_TABLE(k_stream_##FAMILY##_sl, M, RES)},          \
-     {MPP_TABLE(k_stream_##FAMILY##_nts, M, RES), MPP_TABLE(k_stream_##FAMILY##_nts_sl, M, RES)}}
+#define MPP_STREAM_TABLE(FAMILY, M, RES, SUFFIX)                                                      \
+    {{MPP_TABLE(k_stream_##FAMILY##SUFFIX, M, RES), MPP_TABLE(k_stream_##FAMILY##_sl##SUFFIX, M, RES)},     \
+     {MPP_TABLE(k_stream_##FAMILY##_nts##SUFFIX, M, RES), MPP_TABLE(k_stream_##FAMILY##_nts_sl##SUFFIX, M, RES)}}
 
 }  // namespace mpp

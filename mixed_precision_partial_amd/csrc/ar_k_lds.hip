@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamLds = MPP_STREAM_TABLE(lds, false, false);
+StreamTable kStreamLds = MPP_STREAM_TABLE(lds, false, false, );
 
 }  // namespace mpp

@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamLdsM = MPP_STREAM_TABLE(lds, true, false);
+StreamTable kStreamLdsM = MPP_STREAM_TABLE(lds, true, false, );
 
 }  // namespace mpp

@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamLdsRes = MPP_STREAM_TABLE(lds, false, true);
+StreamTable kStreamLdsRes = MPP_STREAM_TABLE(lds, false, true, _res);
 
 }  // namespace mpp

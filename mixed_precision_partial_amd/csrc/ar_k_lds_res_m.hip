@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamLdsResM = MPP_STREAM_TABLE(lds, true, true);
+StreamTable kStreamLdsResM = MPP_STREAM_TABLE(lds, true, true, _res);
 
 }  // namespace mpp

@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamReg = MPP_STREAM_TABLE(reg, false, false);
+StreamTable kStreamReg = MPP_STREAM_TABLE(reg, false, false, );
 
 }  // namespace mpp

@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamRegM = MPP_STREAM_TABLE(reg, true, false);
+StreamTable kStreamRegM = MPP_STREAM_TABLE(reg, true, false, );
 
 }  // namespace mpp

@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamRegRes = MPP_STREAM_TABLE(reg, false, true);
+StreamTable kStreamRegRes = MPP_STREAM_TABLE(reg, false, true, _res);
 
 }  // namespace mpp

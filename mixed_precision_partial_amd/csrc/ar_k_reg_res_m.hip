@@ -3,6 +3,6 @@
 
 namespace mpp {
 
-StreamTable kStreamRegResM = MPP_STREAM_TABLE(reg, true, true);
+StreamTable kStreamRegResM = MPP_STREAM_TABLE(reg, true, true, _res);
 
 }  // namespace mpp

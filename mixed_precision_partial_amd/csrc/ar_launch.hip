@@ -30,8 +30,11 @@ unsigned batch_tiles(Family family, bool src_is_wire, int R) {
     return static_cast<unsigned>(stream_batch(src_is_wire, bucket_ranks(R)));
 }
 
+// `hot`: the kernel takes the preloaded leading fields before the argument
+// block (the plain streaming instances); the residual and single-shot
+// instances take the block alone.
 template <int NR>
-hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &shape, hipStream_t stream) {
+hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &shape, bool hot, hipStream_t stream) {
     LaunchArgs<NR> b;
     b.n = a.n;
     b.cols = a.cols;
@@ -52,9 +55,18 @@ hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &sha
         b.slice_start[r] = a.slice_start[r];
         b.slice_len[r] = a.slice_len[r];
     }
-    void *kargs[] = {&b};
-    return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1), kargs,
-                           shape.lds_bytes, stream);
+    // the leading scalar parameters (preloaded into SGPRs), then the block;
+    // the wave count (below 2^24) carries the destination count in its top byte
+    uint64_t hot_n = b.n, hot_src_stride = b.src_stride, hot_dst_stride = b.dst_stride;
+    unsigned hot_cols = b.cols;
+    unsigned hot_waves_ndst = b.waves | (static_cast<unsigned>(b.n_dst) << 24);
+    const void *hot_src0 = b.src[0], *hot_src1 = b.src[1];
+    void *hot_dst0 = b.dst[0];
+    void *hot_kargs[] = {&hot_n, &hot_cols, &hot_waves_ndst, &hot_src_stride, &hot_dst_stride,
+                         &hot_src0, &hot_src1, &hot_dst0, &b};
+    void *block_kargs[] = {&b};
+    return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1),
+                           hot ? hot_kargs : block_kargs, shape.lds_bytes, stream);
 }
 
 }  // namespace
@@ -122,11 +134,13 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
     }
     if (shape.block % kWave != 0) return hipErrorInvalidValue;
     a.waves = shape.grid_x * (shape.block / kWave);
+    if (a.waves >= (1u << 24) || a.n_dst < 0 || a.n_dst > 255) return hipErrorInvalidValue;
+    const bool hot = family != Family::SingleShot && !res;
     switch (b) {
-    case 0: return launch_as<2>(fn, a, shape, stream);
-    case 1: return launch_as<4>(fn, a, shape, stream);
-    case 2: return launch_as<8>(fn, a, shape, stream);
-    default: return launch_as<16>(fn, a, shape, stream);
+    case 0: return launch_as<2>(fn, a, shape, hot, stream);
+    case 1: return launch_as<4>(fn, a, shape, hot, stream);
+    case 2: return launch_as<8>(fn, a, shape, hot, stream);
+    default: return launch_as<16>(fn, a, shape, hot, stream);
     }
 }
 
