@@ -211,6 +211,25 @@ __device__ __forceinline__ void tile_load(const void *src, size_t t, int lane, u
     }
 }
 
+// Load j of a tile's kSrcRaw loads (the same addresses as tile_load's).
+template <class C, bool NT>
+__device__ __forceinline__ u32x4 part_load(const void *src, size_t t, int lane, int j) {
+    if constexpr (C::SW) {
+        return load16<NT>(reinterpret_cast<const uint16_t *>(src) + t + 8 * lane);
+    } else {
+        return load16<NT>(reinterpret_cast<const float *>(src) + t + 256 * j + 4 * lane);
+    }
+}
+
+// Loads of a binary32-source tile are issued part by part across the ranks
+// (part 0 of every rank, then part 1) rather than rank by rank.  Measured on
+// MI355X, same machine, bit-identical outputs: 4 ranks with one inactive
+// 20.97 against 21.29-21.33 us, R = 8 [8192 x 8192] 366.7-367.5 against
+// 370.3-371.4 us; the prefill call unchanged (16.05-16.07 us).
+#ifndef MPP_PART_MAJOR
+#define MPP_PART_MAJOR 1
+#endif
+
 template <class C>
 __device__ __forceinline__ void tile_values(const u32x4 (&raw)[C::kSrcRaw], float (&v)[8]) {
     if constexpr (C::SW) {
@@ -304,12 +323,19 @@ __device__ __forceinline__ void round_dst(float (&acc)[8]) {
     }
 }
 
+// Store policy of tile_store as a value: 0 write-back, 1 non-temporal, 2
+// device-scope write-through.
+template <class C, int ST>
+constexpr int store_policy() {
+    return ST == kStoreStream ? 1 : (ST == kStoreKeep && !C::SW ? 2 : 0);
+}
+
 template <class C, int ST>
 __device__ __forceinline__ void tile_store(void *dst, size_t t, int lane, const float (&acc)[8]) {
     // write-through for the binary32-source layout (each store instruction
     // covers 1 KiB contiguous); the 16-bit layouts measured better with
     // write-back
-    constexpr int SP = ST == kStoreStream ? 1 : (ST == kStoreKeep && !C::SW ? 2 : 0);
+    constexpr int SP = store_policy<C, ST>();
     if constexpr (C::DN) {
         // the values already lie in the destination type: the packing is exact
         const u32x4 v = {round_pack<C::W>(acc[0], acc[1]), round_pack<C::W>(acc[2], acc[3]),
@@ -380,21 +406,36 @@ struct Batch {
 };
 
 // Issue every load of a batch of U consecutive wave tiles starting at range
-// element `t` for the first R of RB sources, tile by tile: the loads of tile
-// 0 are the oldest in flight, so tile 0 can be folded and stored while the
-// later tiles' loads are still arriving.  The residual loads of the batch
-// come last.
+// element `t` for the first R of RB sources, tile by tile (and within a tile
+// part by part, see MPP_PART_MAJOR): the loads of tile 0 are the oldest in
+// flight, so tile 0 can be folded and stored while the later tiles' loads are
+// still arriving.  The residual loads of the batch come last.
 template <class C, int U, bool NT>
 __device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t t, int lane,
                                            Batch<C, U> &b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+#if MPP_PART_MAJOR
+        // part by part across the ranks: a 1 KiB part can be folded and
+        // stored as soon as its R loads are in
+#pragma unroll
+        for (int j = 0; j < C::kSrcRaw; ++j) {
+#pragma unroll
+            for (int r = 0; r < C::RB; ++r) {
+                if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
+                    b.src[r][u][j] = part_load<C, NT>(a.src[r], o.src + t + u * kWaveTile, lane, j);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#else
 #pragma unroll
         for (int r = 0; r < C::RB; ++r) {
             if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
                 tile_load<C, NT>(a.src[r], o.src + t + u * kWaveTile, lane, b.src[r][u]);
             }
         }
+#endif
         // keep tile order: the scheduler must not hoist a later tile's loads
         // above this one's
         __builtin_amdgcn_sched_barrier(0);
@@ -405,11 +446,91 @@ __device__ __forceinline__ void load_batch(const LaunchArgs<C::RB> &a, const Ran
     }
 }
 
+// Binary32-source tiles of the 8- and 16-rank buckets fold and store each
+// 1 KiB part as soon as its R loads are in (fold_store_part); smaller buckets
+// fold the whole tile first.  Measured on MI355X, same machine, bit-identical
+// outputs: R = 8 [8192 x 8192] 364.6-365.0 against 366.7-367.5 us (whole
+// tiles); with parts stored early at R = 2 the prefill call took 16.24 against
+// 16.15 us and the decode call 2.01 against 1.75 us.
+#ifndef MPP_PART_STORE
+#define MPP_PART_STORE 1
+#endif
+#ifndef MPP_PART_STORE_MIN_RB
+#define MPP_PART_STORE_MIN_RB 8
+#endif
+
+// Fold part j of a binary32-source tile (elements td + 256 j + 4 lane + 0..3)
+// in rank order, add its residual, and store it to every destination.  The
+// same arithmetic per element as fold_store_tile; a part is stored as soon as
+// its R loads are in, ahead of the tile's other part.
+template <class C, int ST>
+__device__ __forceinline__ void fold_store_part(const LaunchArgs<C::RB> &a, size_t td, int lane, int j,
+                                                const u32x4 (&src)[C::RB][C::kSrcRaw], const u32x4 *res) {
+    static_assert(!C::SW && !C::DN, "binary32 sources and destinations only");
+    float acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = 0.0f;
+    if (rank_active<C>(a, 0)) {
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+            float x = f32_from_bits(src[0][j][k]);
+            float y = f32_from_bits(src[0][j][k + 1]);
+            wire_pair<C::W>(x, y);
+            acc[k] = x;
+            acc[k + 1] = y;
+        }
+    }
+#pragma unroll
+    for (int r = 1; r < C::RB; ++r) {
+        if (rank_used<C>(a, r)) {
+            float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (rank_active<C>(a, r)) {
+#pragma unroll
+                for (int k = 0; k < 4; k += 2) {
+                    float x = f32_from_bits(src[r][j][k]);
+                    float y = f32_from_bits(src[r][j][k + 1]);
+                    wire_pair<C::W>(x, y);
+                    w[k] = x;
+                    w[k + 1] = y;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = acc[k] + w[k];
+        }
+    }
+    if constexpr (C::RES) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = acc[k] + f32_from_bits(res[j][k]);
+    }
+    const u32x4 v = {bits_from_f32(acc[0]), bits_from_f32(acc[1]), bits_from_f32(acc[2]), bits_from_f32(acc[3])};
+    constexpr int SP = store_policy<C, ST>();
+#pragma unroll
+    for (int d = 0; d < C::RB; ++d) {
+        if (d < a.n_dst) {
+            float *base = static_cast<float *>(d == 0 ? a.dst[0] : at_use(a.dst[d])) + td;
+            if constexpr (SP == 2) {
+                store16_wt(base, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
+            } else {
+                store16<SP>(base + 256 * j + 4 * lane, v);
+            }
+        }
+    }
+}
+
 // Fold one tile in rank order (one rounding to the destination type per add),
 // add the residual, and store to every destination at element `td`.
 template <class C, int ST>
 __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size_t td, int lane,
                                                 const u32x4 (&src)[C::RB][C::kSrcRaw], const u32x4 *res) {
+    if constexpr (MPP_PART_STORE && !C::SW && !C::DN && C::RB >= MPP_PART_STORE_MIN_RB) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            fold_store_part<C, ST>(a, td, lane, j, src, res);
+            // keep part order: part 1's work must not be hoisted above part 0's stores
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
     float acc[8];
     if (rank_active<C>(a, 0)) {
         tile_values<C>(src[0], acc);
