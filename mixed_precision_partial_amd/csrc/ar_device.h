@@ -504,15 +504,23 @@ __device__ __forceinline__ void fold_store_part(const LaunchArgs<C::RB> &a, size
     }
     const u32x4 v = {bits_from_f32(acc[0]), bits_from_f32(acc[1]), bits_from_f32(acc[2]), bits_from_f32(acc[3])};
     constexpr int SP = store_policy<C, ST>();
+    auto put = [&](void *dst) {
+        float *base = static_cast<float *>(dst) + td;
+        if constexpr (SP == 2) {
+            store16_wt(base, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
+        } else {
+            store16<SP>(base + 256 * j + 4 * lane, v);
+        }
+    };
+    // every launch writes destination 0 (the host never launches without one);
+    // the others sit behind a single branch: per-destination tests around the
+    // first destination's stores cost the prefill call 0.3 us on MI355X
+    // (16.09-16.11 against 15.78-15.79 us, same machine)
+    put(a.dst[0]);
+    if (a.n_dst > 1) {
 #pragma unroll
-    for (int d = 0; d < C::RB; ++d) {
-        if (d < a.n_dst) {
-            float *base = static_cast<float *>(d == 0 ? a.dst[0] : at_use(a.dst[d])) + td;
-            if constexpr (SP == 2) {
-                store16_wt(base, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
-            } else {
-                store16<SP>(base + 256 * j + 4 * lane, v);
-            }
+        for (int d = 1; d < C::RB; ++d) {
+            if (d < a.n_dst) put(at_use(a.dst[d]));
         }
     }
 }
@@ -563,9 +571,13 @@ __device__ __forceinline__ void fold_store_tile(const LaunchArgs<C::RB> &a, size
         for (int k = 0; k < 8; ++k) acc[k] = acc[k] + rv[k];
         round_dst<C>(acc);
     }
+    // destination 0 always, the others behind one branch (see fold_store_part)
+    tile_store<C, ST>(a.dst[0], td, lane, acc);
+    if (a.n_dst > 1) {
 #pragma unroll
-    for (int d = 0; d < C::RB; ++d) {
-        if (d < a.n_dst) tile_store<C, ST>(d == 0 ? a.dst[0] : at_use(a.dst[d]), td, lane, acc);
+        for (int d = 1; d < C::RB; ++d) {
+            if (d < a.n_dst) tile_store<C, ST>(at_use(a.dst[d]), td, lane, acc);
+        }
     }
 }
 

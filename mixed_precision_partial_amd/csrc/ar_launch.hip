@@ -134,7 +134,9 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
     }
     if (shape.block % kWave != 0) return hipErrorInvalidValue;
     a.waves = shape.grid_x * (shape.block / kWave);
-    if (a.waves >= (1u << 24) || a.n_dst < 0 || a.n_dst > 255) return hipErrorInvalidValue;
+    // the kernels write destination 0 unconditionally; the wave count carries
+    // the destination count in its top byte
+    if (a.waves >= (1u << 24) || a.n_dst < 1 || a.n_dst > AR_MAX_RANKS) return hipErrorInvalidValue;
     const bool hot = family != Family::SingleShot && !res;
     switch (b) {
     case 0: return launch_as<2>(fn, a, shape, hot, stream);
