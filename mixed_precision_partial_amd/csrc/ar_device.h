@@ -708,6 +708,15 @@ __device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a, const R
 
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
+    // one-shot grid over whole batches (the common case): a wave's single
+    // batch, then nothing -- no loop back-edge and no remainder tests on its
+    // path.  Measured on MI355X, same machine: prefill 15.70-15.72 against
+    // 15.72-15.74 us; for the 8- and 16-rank buckets the loop form is kept
+    // (R = 8: 370 against 363 us with the shortcut)
+    if (C::RB <= 4 && n_big * big == len && n_big <= nw) {
+        if (gw < n_big) reduce_tiles<C, U, NT, ST>(a, o, (size_t)gw * big, lane);
+        return;
+    }
     for (unsigned t = gw; t < n_big; t += nw) {
         reduce_tiles<C, U, NT, ST>(a, o, (size_t)t * big, lane);
     }
