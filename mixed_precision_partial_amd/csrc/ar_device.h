@@ -912,6 +912,15 @@ __device__ __forceinline__ void lds_consume(const LaunchArgs<C::RB> &a, const Ra
     fold_store<C, U, ST>(a, o, t, lane, b);
 }
 
+// One-shot fast path of the LDS-staged kernel (ranges of whole batches, 2-
+// and 4-rank buckets): the wave's single stage without the double-buffer
+// bookkeeping and the remainder tests.  Measured on MI355X, same machine:
+// bf16 partials into a bf16 destination on the prefill shape 8.85 against
+// 9.09-9.10 us; the 4-rank broadcasts unchanged.
+#ifndef MPP_LDS_FAST
+#define MPP_LDS_FAST 1
+#endif
+
 template <class C, int ST, bool SLICED>
 __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len,
                                               u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
@@ -921,6 +930,17 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, const 
     const unsigned nw = a.waves;
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
+#if MPP_LDS_FAST
+    // one-shot grid over whole batches: the wave's single stage, then nothing
+    if (C::RB <= 4 && n_big * big == len && n_big <= nw) {
+        if (gw < n_big) {
+            lds_issue<C, U>(a, o, (size_t)gw * big, lane, stage0);
+            wait_vm<0>();
+            lds_consume<C, U, ST>(a, o, (size_t)gw * big, lane, stage0);
+        }
+        return;
+    }
+#endif
 
     // loads per stage (vector-memory instructions): active ranks x U x K
     const int RU = a.R < C::RB ? a.R : C::RB;
