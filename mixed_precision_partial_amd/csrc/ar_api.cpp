@@ -196,7 +196,8 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             // the limit is per rank at R = 2 and scales with the total wire bytes
             // of all ranks: measured on MI355X (graph-replayed kernel time), the
             // single-shot launch wins below ~2 MiB of wire bytes in total, at
-            // R = 2 (crossing at 1-1.5 MiB per rank) as at R = 8 (256 KiB)
+            // R = 2 (ahead at 512 KiB per rank, behind at 1 MiB) as at R = 8
+            // (ahead at 128 KiB per rank, behind at 256 KiB)
             resolved = AR_MODE_SINGLE_SHOT;
         } else {
             resolved = AR_MODE_CHUNKED;
