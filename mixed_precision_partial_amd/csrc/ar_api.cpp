@@ -355,7 +355,15 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         } else if (res_kind != 0) {
             plan->stream_kernel = resolved == AR_MODE_RS_BCAST ? 2 : 1;
         } else {
-            plan->stream_kernel = (resolved == AR_MODE_RS_BCAST || (src_wire && R == 2)) ? 2 : 1;
+            // 16-bit sources (no residual): LDS-staged at R = 2 and, into a
+            // binary32 destination, at R = 6..8 (measured on MI355X, CHUNKED:
+            // R = 8 [8192 x 8192] 193.3-193.5 against 202.5-202.8 us, R = 6
+            // 43.6 against 44.1-44.3 us); register-staged at R = 3, 4, 5 and
+            // 9..16 (R = 3: 15.8-16.1 against 17.6 us, R = 16: 57.9 against
+            // 63.4 us)
+            const bool lds_16bit =
+                src_wire && (R == 2 || (!dst_narrow && resolved == AR_MODE_CHUNKED && R >= 6 && R <= 8));
+            plan->stream_kernel = (resolved == AR_MODE_RS_BCAST || lds_16bit) ? 2 : 1;
         }
     }
     return AR_OK;

@@ -220,7 +220,12 @@ def test_stream_kernel_choice():
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
     assert q(n, mode=ar.AR_MODE_CHUNKED)[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 2
-    assert q(n, R=8, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 1
+    # 16-bit sources into a binary32 destination: LDS-staged at R = 2 and 6..8, register-staged else
+    for R, want in ((3, 1), (4, 1), (5, 1), (6, 2), (7, 2), (8, 2), (9, 1), (16, 1)):
+        assert q(n, R=R, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == want, R
+    # (not for host-staged calls or narrow destinations)
+    assert q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, host=True)[1].stream_kernel == 1
+    assert q(n, R=8, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 1})[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_CHUNKED, config={"stream_kernel": 2})[1].stream_kernel == 2
     # broadcast schedule: LDS-staged for any source width
