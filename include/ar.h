@@ -129,11 +129,11 @@ typedef struct {
                                      0 -> clamp(bytes/2, 512 KiB, 64 MiB) per call */
     int    host_slots;            /* HOST_STAGED scratch slots (>= 1); 0 -> 3 */
     int    grid_wgs;              /* CHUNKED / RS_BCAST workgroups; 0 -> tuned per shape */
-    int    stream_kernel;         /* 0 auto (LDS-staged for the broadcast schedule and,
-                                     without a residual, for two 16-bit sources or
-                                     six to eight of them into a binary32
-                                     destination (CHUNKED); register-staged
-                                     otherwise), 1 register-staged, 2 LDS-staged */
+    int    stream_kernel;         /* 0 auto (the family measured faster on MI355X
+                                     for the call's schedule, source and
+                                     destination widths, residual and rank count;
+                                     ar_plan_query reports the choice),
+                                     1 register-staged, 2 LDS-staged */
     int    store_policy;          /* destination stores: 0 auto (streaming when the
                                      call writes at least as many bytes as it
                                      reads, kept otherwise), 1 kept in the cache

@@ -337,33 +337,39 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // decode-sized ones, 5.4 against 37 us; the copy engine leaves the CUs
         // free for other streams while the bytes cross PCIe)
         plan->host_direct = resolved == AR_MODE_HOST_STAGED && cfg.host_path != 1;
-        // streaming kernel family: explicit choice, else measured on MI355X
-        // with inputs that are not in any cache -- the LDS-staged kernel for
-        // the broadcast schedule (R loads per lane staged in LDS instead of
-        // VGPRs while R stores stream out: 88 against 95 us at R = 4, fp32
-        // sources) and for two 16-bit sources (short tiles, as many bytes
-        // written as read), the register kernel elsewhere (up to 16 % faster
-        // for fp32 sources with few destinations).  With a residual the
-        // broadcast schedule stays on the LDS-staged kernel (R = 4: 98-102
-        // against 105-108 us element-wise, 88.5 against 90.7 us with a row)
-        // and every other call takes the register kernel (a broadcast row on
-        // the prefill shape: 17.4 against 18.3 us; 8 ranks: 374 against 411 us).
+        // streaming kernel family: explicit choice, else the family measured
+        // faster on MI355X for the call's kind and rank count (same machine,
+        // inputs not in any cache, bit-identical outputs):
+        //   - with a residual: LDS-staged for the broadcast schedule (R = 4:
+        //     98-102 against 105-108 us element-wise, 88.5 against 90.7 us with
+        //     a row), register-staged otherwise (a broadcast row on the prefill
+        //     shape: 17.4 against 18.3 us; 8 ranks: 374 against 411 us);
+        //   - broadcast schedule: LDS-staged (R = 4, fp32 sources: 88 against
+        //     95 us; 16-bit sources at every R), except R = 2 with fp32 sources
+        //     or a narrow destination (22.7 against 24.3 us; 23.3 against 24.0);
+        //   - CHUNKED: register-staged for fp32 sources (prefill 15.7 against
+        //     16.4 us, R = 8 363 against 416 us); for 16-bit sources the rank
+        //     masks below (R = 8 into fp32: 193.4 against 202.7 us; narrow R = 8:
+        //     48.2 against 51.6 us; narrow R = 3: 22.4 against 23.2 us);
+        //   - host-staged calls: LDS-staged for two 16-bit sources only.
+        constexpr unsigned kLds16ToF32 = (1u << 2) | (1u << 6) | (1u << 7) | (1u << 8);
+        constexpr unsigned kLds16Narrow = (1u << 2) | (1u << 4) | (1u << 6) | (1u << 7) | (1u << 8);
         if (resolved == AR_MODE_SINGLE_SHOT) {
             plan->stream_kernel = 0;
         } else if (cfg.stream_kernel != 0) {
             plan->stream_kernel = cfg.stream_kernel;
-        } else if (res_kind != 0) {
-            plan->stream_kernel = resolved == AR_MODE_RS_BCAST ? 2 : 1;
         } else {
-            // 16-bit sources (no residual): LDS-staged at R = 2 and, into a
-            // binary32 destination, at R = 6..8 (measured on MI355X, CHUNKED:
-            // R = 8 [8192 x 8192] 193.3-193.5 against 202.5-202.8 us, R = 6
-            // 43.6 against 44.1-44.3 us); register-staged at R = 3, 4, 5 and
-            // 9..16 (R = 3: 15.8-16.1 against 17.6 us, R = 16: 57.9 against
-            // 63.4 us)
-            const bool lds_16bit =
-                src_wire && (R == 2 || (!dst_narrow && resolved == AR_MODE_CHUNKED && R >= 6 && R <= 8));
-            plan->stream_kernel = (resolved == AR_MODE_RS_BCAST || lds_16bit) ? 2 : 1;
+            bool lds;
+            if (res_kind != 0) {
+                lds = resolved == AR_MODE_RS_BCAST;
+            } else if (resolved == AR_MODE_RS_BCAST) {
+                lds = R != 2 || (src_wire && !dst_narrow);
+            } else if (resolved == AR_MODE_HOST_STAGED) {
+                lds = src_wire && R == 2;
+            } else {
+                lds = src_wire && (((dst_narrow ? kLds16Narrow : kLds16ToF32) >> R) & 1u) != 0;
+            }
+            plan->stream_kernel = lds ? 2 : 1;
         }
     }
     return AR_OK;

@@ -216,24 +216,29 @@ def test_store_policy_rule():
 
 
 def test_stream_kernel_choice():
+    """The automatic family follows the measured table: CHUNKED fp32 sources register-staged;
+    16-bit sources LDS-staged at R = 2 and 6..8 into binary32, at R = 2, 4 and 6..8 into a narrow
+    destination; the broadcast schedule LDS-staged except R = 2 with fp32 sources or a narrow
+    destination; with a residual LDS-staged only for the broadcast schedule; host-staged calls
+    LDS-staged for two 16-bit sources only."""
     n = 2048 * 4096
+    CH, BC, HS, SW = ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED, ar.AR_SRC_WIRE
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
-    assert q(n, mode=ar.AR_MODE_CHUNKED)[1].stream_kernel == 1
-    assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == 2
-    # 16-bit sources into a binary32 destination: LDS-staged at R = 2 and 6..8, register-staged else
-    for R, want in ((3, 1), (4, 1), (5, 1), (6, 2), (7, 2), (8, 2), (9, 1), (16, 1)):
-        assert q(n, R=R, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[1].stream_kernel == want, R
-    # (not for host-staged calls or narrow destinations)
-    assert q(n, R=8, mode=ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, host=True)[1].stream_kernel == 1
-    assert q(n, R=8, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == 1
-    assert q(n, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, config={"stream_kernel": 1})[1].stream_kernel == 1
-    assert q(n, mode=ar.AR_MODE_CHUNKED, config={"stream_kernel": 2})[1].stream_kernel == 2
-    # broadcast schedule: LDS-staged for any source width
-    assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST, wire=ar.AR_F16)[1].stream_kernel == 2
-    assert q(n, R=4, mode=ar.AR_MODE_RS_BCAST | ar.AR_SRC_WIRE, wire=ar.AR_F16)[1].stream_kernel == 2
-    # two 16-bit sources into a narrow destination: LDS-staged; more ranks: register-staged
-    assert q(n, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == 2
-    assert q(n, R=3, mode=ar.AR_MODE_CHUNKED, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == 1
+    for R in (2, 3, 4, 8, 16):
+        assert q(n, R=R, mode=CH)[1].stream_kernel == 1, R
+    for R in range(2, 17):
+        want16 = 2 if R in (2, 6, 7, 8) else 1
+        wantn = 2 if R in (2, 4, 6, 7, 8) else 1
+        assert q(n, R=R, mode=CH | SW)[1].stream_kernel == want16, R
+        assert q(n, R=R, mode=CH, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == wantn, R
+        assert q(n, R=R, mode=BC, wire=ar.AR_F16)[1].stream_kernel == (1 if R == 2 else 2), R
+        assert q(n, R=R, mode=BC | SW, wire=ar.AR_F16)[1].stream_kernel == 2, R
+        assert q(n, R=R, mode=BC, wire=ar.AR_F16, dst_type=ar.AR_F16)[1].stream_kernel == (1 if R == 2 else 2), R
+        assert q(n, R=R, mode=HS | SW, host=True)[1].stream_kernel == (2 if R == 2 else 1), R
+        assert q(n, R=R, mode=HS, host=True)[1].stream_kernel == 1, R
+    # an explicit choice wins
+    assert q(n, mode=CH | SW, config={"stream_kernel": 1})[1].stream_kernel == 1
+    assert q(n, mode=CH, config={"stream_kernel": 2})[1].stream_kernel == 2
 
 
 def test_inactive_ranks_flag():
