@@ -760,10 +760,20 @@ constexpr int stream_block(int rank_bucket) {
 #endif
 
 // Tiles per batch of the streaming kernel: about MPP_STREAM_LOADS dwordx4
-// loads per lane (R x U x loads-per-tile), at least 1 and at most MAXU tiles.
+// loads per lane (R x U x loads-per-tile) for 16-bit sources and
+// MPP_STREAM_LOADS_F32 for binary32 sources, at least 1 and at most MAXU
+// tiles.  With binary32 sources that makes one tile per wave at every bucket:
+// measured on MI355X, same machine, against two tiles at R = 2 (8 loads):
+// prefill 15.74-15.75 against 15.78-15.81 us, prefill + bias row 16.64
+// against 16.99 us, row-strided block + bias 16.39-16.40 against 16.97-17.00
+// us, element-wise residual 20.44 against 20.31 us.  16-bit sources keep 8
+// (4 measured 17.5 against 15.9-16.0 us at R = 3).
+#ifndef MPP_STREAM_LOADS_F32
+#define MPP_STREAM_LOADS_F32 4
+#endif
 constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
     const int per_tile = (src_is_wire ? 1 : 2) * rank_bucket;
-    const int u = MPP_STREAM_LOADS / per_tile;
+    const int u = (src_is_wire ? MPP_STREAM_LOADS : MPP_STREAM_LOADS_F32) / per_tile;
     return u < 1 ? 1 : (u > MPP_STREAM_MAXU ? MPP_STREAM_MAXU : u);
 }
 
