@@ -529,7 +529,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
                 a.src[r] = srcs[r];
                 a.dst[r] = dst[r];
             }
-            const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, max_len,
+            const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr, max_len,
                                                            static_cast<unsigned>(R), c->cu_count, c->cfg.grid_wgs);
             if (int rc = hip_status(mpp::launch(family, types, true, a, shape, stream))) return rc;
         }
@@ -557,8 +557,9 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         }
         set_ranges_1d(a, res, n, p0, cols, plan.dst_bytes);
         const unsigned n_ranges = static_cast<unsigned>((len + cols - 1) / cols);
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(cols),
-                                                       n_ranges, c->cu_count, c->cfg.grid_wgs);
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
+                                                       static_cast<unsigned>(cols), n_ranges, c->cu_count,
+                                                       c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
     }
     return AR_OK;
@@ -596,8 +597,9 @@ int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const
             a.res_stride = rw.res_stride;
             a.res_reuse = rw.res_stride == 0 ? 1 : 0;
         }
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(rw.cols),
-                                                       static_cast<unsigned>(nr), c->cu_count, c->cfg.grid_wgs);
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
+                                                       static_cast<unsigned>(rw.cols), static_cast<unsigned>(nr),
+                                                       c->cu_count, c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
     }
     return AR_OK;
@@ -675,8 +677,8 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         for (int r = 0; r < R; ++r) a.src[r] = srcs[r] == nullptr ? nullptr : slot_base + r * rank_stride;
         a.dst[0] = static_cast<char *>(dst[0]) + e0 * db;
         set_ranges_1d(a, res, n, e0, len, plan.dst_bytes);
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, static_cast<unsigned>(len), 1,
-                                                       c->cu_count, c->cfg.grid_wgs);
+        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
+                                                       static_cast<unsigned>(len), 1, c->cu_count, c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
         if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
         c->slot_used[slot] = 1;

@@ -730,12 +730,19 @@ constexpr int kLdsBlock = 64;
 // (measured on MI355X): 64-thread workgroups for the 8-rank bucket, whose
 // batches hold 16 loads per lane and so limit how many waves fit on a CU --
 // small workgroups pack the CUs more evenly (cold R = 8 fp32 reduce: 6.38
-// against 6.13 TB/s); 256 threads elsewhere.
+// against 6.13 TB/s); 128 threads for the binary32-source residual instances
+// of the 2- and 4-rank buckets (same machine: element-wise residual 20.11
+// against 20.36 us, bias row 16.44 against 16.62 us, row-strided block + bias
+// 16.23 against 16.35 us; with 16-bit sources no gain); 256 threads elsewhere
+// (prefill 15.78 against 15.89 us with 128).  The host takes the same
+// function for the launch shape, and the launcher refuses a shape that
+// differs from it.
 #ifndef MPP_STREAM_BLOCK
 #define MPP_STREAM_BLOCK 0
 #endif
-constexpr int stream_block(int rank_bucket) {
-    return MPP_STREAM_BLOCK > 0 ? MPP_STREAM_BLOCK : (rank_bucket == 8 ? 64 : 256);
+constexpr int stream_block(int rank_bucket, bool res, bool src_is_wire) {
+    return MPP_STREAM_BLOCK > 0 ? MPP_STREAM_BLOCK
+                                : (rank_bucket == 8 ? 64 : (res && !src_is_wire && rank_bucket <= 4 ? 128 : 256));
 }
 
 // Streaming-kernel tuning (compile-time; measured on MI355X):
@@ -779,7 +786,8 @@ constexpr int stream_batch(bool src_is_wire, int rank_bucket) {
 
 template <class C, int ST, bool SLICED>
 __device__ __forceinline__ void stream_reg(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len) {
-    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, stream_block(C::RB), SLICED>(a, o, len);
+    constexpr int block = stream_block(C::RB, C::RES, C::SW);
+    reduce_range<C, stream_batch(C::SW, C::RB), MPP_STREAM_NT != 0, ST, block, SLICED>(a, o, len);
 }
 
 // ---------------------------------------------------------------------------
@@ -1082,10 +1090,10 @@ __global__ __launch_bounds__(kSingleShotBlock) void k_single_shot(LaunchArgs<C::
         range_of<SLICED>(a, o, len);                                                    \
         BODY<C, ST, SLICED>(a, o, len);                                                 \
     }
-MPP_STREAM_KERNELS(k_stream_reg, stream_block(C::RB), stream_reg, kStoreKeep, false)
-MPP_STREAM_KERNELS(k_stream_reg_nts, stream_block(C::RB), stream_reg, kStoreStream, false)
-MPP_STREAM_KERNELS(k_stream_reg_sl, stream_block(C::RB), stream_reg, kStoreKeep, true)
-MPP_STREAM_KERNELS(k_stream_reg_nts_sl, stream_block(C::RB), stream_reg, kStoreStream, true)
+MPP_STREAM_KERNELS(k_stream_reg, stream_block(C::RB, C::RES, C::SW), stream_reg, kStoreKeep, false)
+MPP_STREAM_KERNELS(k_stream_reg_nts, stream_block(C::RB, C::RES, C::SW), stream_reg, kStoreStream, false)
+MPP_STREAM_KERNELS(k_stream_reg_sl, stream_block(C::RB, C::RES, C::SW), stream_reg, kStoreKeep, true)
+MPP_STREAM_KERNELS(k_stream_reg_nts_sl, stream_block(C::RB, C::RES, C::SW), stream_reg, kStoreStream, true)
 MPP_STREAM_KERNELS(k_stream_lds, kLdsBlock, stream_lds, kStoreKeep, false)
 MPP_STREAM_KERNELS(k_stream_lds_nts, kLdsBlock, stream_lds, kStoreStream, false)
 MPP_STREAM_KERNELS(k_stream_lds_sl, kLdsBlock, stream_lds, kStoreKeep, true)

@@ -97,9 +97,10 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs arg
                   hipStream_t stream);
 
 // Pick a launch shape for `family` covering `max_slice_len` elements per
-// slice.  `cu_count` is the device's compute-unit count; `grid_override`
-// (> 0) fixes the workgroups per slice.
-LaunchShape plan_shape(Family family, bool src_is_wire, int R, unsigned max_slice_len, unsigned n_slices,
+// slice (`res`: the call adds a residual, which selects other kernel
+// instances).  `cu_count` is the device's compute-unit count;
+// `grid_override` (> 0) fixes the workgroups per slice.
+LaunchShape plan_shape(Family family, bool src_is_wire, int R, bool res, unsigned max_slice_len, unsigned n_slices,
                        int cu_count, int grid_override);
 
 // Elements processed per wave per loop iteration (a multiple of kWaveTile).

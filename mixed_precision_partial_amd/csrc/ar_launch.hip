@@ -75,7 +75,7 @@ unsigned stream_tile_elems(Family family, bool src_is_wire, int R) {
     return kWaveTile * batch_tiles(family, src_is_wire, R);
 }
 
-LaunchShape plan_shape(Family family, bool src_is_wire, int R, unsigned max_slice_len, unsigned n_slices,
+LaunchShape plan_shape(Family family, bool src_is_wire, int R, bool res, unsigned max_slice_len, unsigned n_slices,
                        int cu_count, int grid_override) {
     LaunchShape s{};
     s.grid_y = n_slices;
@@ -91,7 +91,8 @@ LaunchShape plan_shape(Family family, bool src_is_wire, int R, unsigned max_slic
         s.grid_x = grid_override > 0 ? static_cast<unsigned>(grid_override) : g;
         return s;
     }
-    s.block = family == Family::StreamLds ? kLdsBlock : static_cast<unsigned>(stream_block(bucket_ranks(R)));
+    s.block = family == Family::StreamLds ? kLdsBlock
+                                          : static_cast<unsigned>(stream_block(bucket_ranks(R), res, src_is_wire));
     const unsigned wpb = s.block / kWave;
     const unsigned per_wave = stream_tile_elems(family, src_is_wire, R);
     const unsigned batches = (max_slice_len + per_wave - 1) / per_wave;
@@ -132,7 +133,13 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
         break;
     default: return hipErrorNotSupported;
     }
-    if (shape.block % kWave != 0) return hipErrorInvalidValue;
+    // the kernels index their waves with the workgroup size they were built for
+    const unsigned want_block =
+        family == Family::SingleShot ? kSingleShotBlock
+        : family == Family::StreamLds
+            ? kLdsBlock
+            : static_cast<unsigned>(stream_block(bucket_ranks(a.R), res != 0, types.src_is_wire));
+    if (shape.block != want_block) return hipErrorInvalidValue;
     a.waves = shape.grid_x * (shape.block / kWave);
     // the kernels write destination 0 unconditionally; the wave count carries
     // the destination count in its top byte
