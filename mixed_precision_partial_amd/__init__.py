@@ -21,6 +21,13 @@ ready-made ``ptr_array(...)`` arrays (passed through unchanged, which keeps
 the per-call marshalling cost low for latency-bound callers); ``stream`` is a
 ``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None for the null
 stream.
+
+The library sees only pointers, so it cannot tell how large a buffer is.  With
+``validate=True`` (the default) the enqueueing calls check, before calling it,
+that every tensor argument spans the bytes the call will read or write from its
+data pointer (and, for the 1-D calls, that it is contiguous), raising
+``ValueError`` otherwise; integer addresses and ``ptr_array`` arrays are the
+caller's responsibility, as in C.  ``bind_reduce`` checks once, when it binds.
 """
 from __future__ import annotations
 
@@ -163,6 +170,59 @@ def ptr_array(xs):
 
 _ptr_array = ptr_array
 
+_TYPE_BYTES = {AR_F32: 4, AR_F16: 2, AR_BF16: 2}
+
+
+def _tensors(xs):
+    """The tensor entries of a dsts / srcs argument (addresses, None and
+    ready-made pointer arrays are not checkable)."""
+    if xs is None or isinstance(xs, ctypes.Array):
+        return ()
+    return [x for x in xs if x is not None and not isinstance(x, int)]
+
+
+def _check_flat(xs, need: int, what: str) -> None:
+    """1-D calls: each tensor is contiguous and holds at least ``need`` bytes."""
+    for x in _tensors(xs):
+        if x.nbytes < need or not x.is_contiguous():
+            raise ValueError(f"{what}: a tensor of {x.nbytes} bytes{'' if x.is_contiguous() else ' (not contiguous)'}"
+                             f" where the call reads or writes {need} contiguous bytes")
+
+
+def _check_span(xs, need: int, what: str) -> None:
+    """Row-strided calls: each tensor's storage holds ``need`` bytes from its data pointer."""
+    for x in _tensors(xs):
+        have = x.untyped_storage().nbytes() - x.storage_offset() * x.element_size()
+        if have < need:
+            raise ValueError(f"{what}: {have} bytes from the tensor's data pointer where the call spans {need}")
+
+
+def _validate_flat(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual=None,
+                   residual_len: int = 0) -> None:
+    dst_b = _TYPE_BYTES.get(int(dst_type))
+    src_b = _TYPE_BYTES.get(int(wire_type) if int(mode) & AR_SRC_WIRE else int(dst_type))
+    if dst_b is None or src_b is None or int(n) <= 0:
+        return                                  # the library rejects or skips the call itself
+    _check_flat(dsts, int(n) * dst_b, "dsts")
+    _check_flat(srcs, int(n) * src_b, "srcs")
+    if residual is not None:
+        _check_flat((residual,), int(residual_len) * dst_b, "residual")
+
+
+def _validate_rows(dsts, srcs, rows: int, cols: int, src_stride: int, dst_stride: int, dst_type: int,
+                   wire_type: int, mode: int, residual, res_stride: int) -> None:
+    dst_b = _TYPE_BYTES.get(int(dst_type))
+    src_b = _TYPE_BYTES.get(int(wire_type) if int(mode) & AR_SRC_WIRE else int(dst_type))
+    if dst_b is None or src_b is None or int(rows) <= 0 or int(cols) <= 0:
+        return
+
+    def extent(stride):
+        return ((int(rows) - 1) * int(stride) + int(cols)) if int(stride) > 0 else int(cols)
+    _check_span(dsts, extent(dst_stride) * dst_b, "dsts")
+    _check_span(srcs, extent(src_stride) * src_b, "srcs")
+    if residual is not None:
+        _check_span((residual,), extent(res_stride) * dst_b, "residual")
+
 
 def _stream_handle(stream) -> int | None:
     if stream is None:
@@ -196,9 +256,12 @@ def ar_init(device: int = 0, config=None) -> ctypes.c_void_p:
 
 
 def ar_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = AR_BF16,
-              mode: int = AR_MODE_AUTO, stream=None, check: bool = True) -> int:
-    """Enqueue one reduce; returns the status (raises ArError on failure if ``check``)."""
+              mode: int = AR_MODE_AUTO, stream=None, check: bool = True, validate: bool = True) -> int:
+    """Enqueue one reduce; returns the status (raises ArError on failure if
+    ``check``; ValueError before the call if ``validate`` finds a tensor too small)."""
     lib = load_library()
+    if validate:
+        _validate_flat(dsts, srcs, n, dst_type, wire_type, mode)
     R = len(srcs) if srcs is not None else 0
     rc = lib.ar_reduce(ctx, _ptr_array(dsts), _ptr_array(srcs), R, int(n), int(dst_type),
                        int(wire_type), int(mode), _stream_handle(stream))
@@ -219,12 +282,13 @@ def bind_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int 
 
     lib = load_library()
     R = len(srcs)
-    dst_arr, src_arr = _ptr_array(dsts), _ptr_array(srcs)
     ctx_val = ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx
     st_val = _stream_handle(stream)
     rlen = int(n) if residual_len is None else int(residual_len)
     if residual is not None and residual_len is None and hasattr(residual, "numel"):
         rlen = int(residual.numel())
+    _validate_flat(dsts, srcs, n, dst_type, wire_type, mode, residual, rlen)
+    dst_arr, src_arr = _ptr_array(dsts), _ptr_array(srcs)
     fast = _fast_module()
     if fast is not None:
         fn = lib.ar_reduce if residual is None else lib.ar_reduce_add
@@ -256,15 +320,20 @@ def _fast_module():
 
 
 def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual,
-                  residual_len: int | None = None, stream=None, check: bool = True) -> int:
+                  residual_len: int | None = None, stream=None, check: bool = True,
+                  validate: bool = True) -> int:
     """Enqueue one reduce followed by a residual add (element-wise when
     ``residual_len == n``, else one broadcast row); ``residual_len`` defaults to
     the residual tensor's element count.  Returns the status (raises ArError on
-    failure if ``check``)."""
+    failure if ``check``; ValueError before the call if ``validate`` finds a tensor too small)."""
     lib = load_library()
     R = len(srcs) if srcs is not None else 0
     if residual_len is None:
+        if not hasattr(residual, "numel"):
+            raise TypeError("residual_len is required when the residual is given as an address")
         residual_len = residual.numel()
+    if validate:
+        _validate_flat(dsts, srcs, n, dst_type, wire_type, mode, residual, residual_len)
     rc = lib.ar_reduce_add(ctx, _ptr_array(dsts), _ptr_array(srcs), R, int(n), int(dst_type),
                            int(wire_type), int(mode), _addr(residual), int(residual_len),
                            _stream_handle(stream))
@@ -275,12 +344,16 @@ def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: 
 
 def ar_reduce_rows(ctx, dsts, srcs, rows: int, cols: int, src_stride: int, dst_stride: int, dst_type: int,
                    wire_type: int, mode: int, residual=None, res_stride: int = 0, stream=None,
-                   check: bool = True) -> int:
+                   check: bool = True, validate: bool = True) -> int:
     """Enqueue one reduce of row-strided tensors (strides in elements); ``residual``
     None, or a tensor / address laid out with row stride ``res_stride`` (0 = one row
-    added to every row).  Returns the status (raises ArError on failure if ``check``)."""
+    added to every row).  Returns the status (raises ArError on failure if ``check``;
+    ValueError before the call if ``validate`` finds a tensor's storage too small)."""
     lib = load_library()
     R = len(srcs) if srcs is not None else 0
+    if validate:
+        _validate_rows(dsts, srcs, rows, cols, src_stride, dst_stride, dst_type, wire_type, mode, residual,
+                       res_stride)
     shape = ArRows(int(rows), int(cols), int(src_stride), int(dst_stride), int(res_stride))
     rc = lib.ar_reduce_rows(ctx, _ptr_array(dsts), _ptr_array(srcs), R, ctypes.byref(shape), int(dst_type),
                             int(wire_type), int(mode), _addr(residual), _stream_handle(stream))
@@ -347,7 +420,10 @@ class Reducer:
     def __call__(self, dsts, srcs, n=None, dst_type=AR_F32, wire_type=AR_BF16,
                  mode=AR_MODE_AUTO, stream=None):
         if n is None:
-            n = srcs[0].numel()
+            first = next((s for s in srcs if s is not None), None)
+            if first is None:
+                raise ValueError("n is required when every source is inactive")
+            n = first.numel()
         return ar_reduce(self.ctx, dsts, srcs, n, dst_type, wire_type, mode, stream)
 
     def close(self):

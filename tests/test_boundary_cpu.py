@@ -401,6 +401,57 @@ def test_bound_calls_reach_the_library():
     assert g() == ar.AR_ERR_INVALID
 
 
+def test_binding_checks_tensor_sizes_before_the_call():
+    """The library sees pointers only; the binding checks each tensor argument's byte
+    span (and contiguity for the 1-D calls) before calling it.  Host tensors stand in
+    for device ones: the check runs before the call, and with a NULL context the call
+    itself is refused without touching the GPU."""
+    import torch
+    n = 1000
+    f32 = [torch.empty(n) for _ in range(3)]
+    F, B, C = ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED
+    assert ar.ar_reduce(None, f32[:1], f32[1:], n, F, B, C, check=False) == ar.AR_ERR_INVALID
+    with pytest.raises(ValueError, match="srcs"):
+        ar.ar_reduce(None, f32[:1], [f32[1], torch.empty(n - 1)], n, F, B, C)
+    with pytest.raises(ValueError, match="dsts"):
+        ar.ar_reduce(None, [torch.empty(n // 2)], f32[1:], n, F, B, C)
+    with pytest.raises(ValueError, match="not contiguous"):
+        ar.ar_reduce(None, f32[:1], [torch.empty(2 * n)[::2], f32[2]], n, F, B, C)
+    # sources in the wire type are read at 2 bytes per element
+    half = [torch.empty(n, dtype=torch.int16) for _ in range(2)]
+    assert ar.ar_reduce(None, f32[:1], half, n, F, B, C | ar.AR_SRC_WIRE, check=False) == ar.AR_ERR_INVALID
+    with pytest.raises(ValueError, match="srcs"):
+        ar.ar_reduce(None, f32[:1], half, n, F, B, C, check=False)
+    # addresses and inactive (None) ranks are not checked; validate=False skips the check
+    assert ar.ar_reduce(None, f32[:1], [1 << 33, None], n, F, B, C | ar.AR_SRC_INACTIVE_NULL,
+                        check=False) == ar.AR_ERR_INVALID
+    assert ar.ar_reduce(None, [torch.empty(1)], f32[1:], n, F, B, C, check=False,
+                        validate=False) == ar.AR_ERR_INVALID
+    # residuals: element-wise and one row
+    with pytest.raises(ValueError, match="residual"):
+        ar.ar_reduce_add(None, f32[:1], f32[1:], n, F, B, C, torch.empty(100), n)
+    assert ar.ar_reduce_add(None, f32[:1], f32[1:], n, F, B, C, torch.empty(100), check=False) == ar.AR_ERR_INVALID
+    with pytest.raises(TypeError, match="residual_len"):
+        ar.ar_reduce_add(None, f32[:1], f32[1:], n, F, B, C, 1 << 35)
+    with pytest.raises(ValueError, match="residual"):
+        ar.bind_reduce(None, f32[:1], f32[1:], n, F, B, C, residual=torch.empty(10), residual_len=100)
+    with pytest.raises(ValueError, match="srcs"):
+        ar.bind_reduce(None, f32[:1], [f32[1], torch.empty(10)], n, F, B, C)
+    # row-strided: a view of rows inside a wider buffer is fine; its span decides
+    rows, cols, ss, ds = 4, 16, 24, 20
+    srcs = [torch.empty(rows, ss)[:, :cols] for _ in range(2)]
+    dst = torch.empty((rows - 1) * ds + cols)
+    assert ar.ar_reduce_rows(None, [dst], srcs, rows, cols, ss, ds, F, B, C, check=False) == ar.AR_ERR_INVALID
+    with pytest.raises(ValueError, match="dsts"):
+        ar.ar_reduce_rows(None, [dst[1:]], srcs, rows, cols, ss, ds, F, B, C)
+    with pytest.raises(ValueError, match="srcs"):
+        ar.ar_reduce_rows(None, [dst], [srcs[0], torch.empty(rows, ss)[1:, :cols]], rows, cols, ss, ds, F, B, C)
+    with pytest.raises(ValueError, match="residual"):
+        ar.ar_reduce_rows(None, [dst], srcs, rows, cols, ss, ds, F, B, C, residual=torch.empty(cols - 1))
+    assert ar.ar_reduce_rows(None, [dst], srcs, rows, cols, ss, ds, F, B, C, residual=torch.empty(cols),
+                             check=False) == ar.AR_ERR_INVALID
+
+
 def test_bound_calls_use_the_compiled_call_type():
     """With the fast-call module built (build() builds it), bound calls are instances of
     its C type, which takes no arguments; without it the binding falls back to ctypes."""
