@@ -197,16 +197,32 @@ def _check_span(xs, need: int, what: str) -> None:
             raise ValueError(f"{what}: {have} bytes from the tensor's data pointer where the call spans {need}")
 
 
-def _validate_flat(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, residual=None,
-                   residual_len: int = 0) -> None:
-    dst_b = _TYPE_BYTES.get(int(dst_type))
-    src_b = _TYPE_BYTES.get(int(wire_type) if int(mode) & AR_SRC_WIRE else int(dst_type))
-    if dst_b is None or src_b is None or int(n) <= 0:
-        return                                  # the library rejects or skips the call itself
-    _check_flat(dsts, int(n) * dst_b, "dsts")
-    _check_flat(srcs, int(n) * src_b, "srcs")
-    if residual is not None:
-        _check_flat((residual,), int(residual_len) * dst_b, "residual")
+def _flat_arrays(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, validate: bool):
+    """ptr_array(dsts), ptr_array(srcs) of a 1-D call, checking each tensor on the
+    way (one pass: the check costs little beyond the pointer conversion); returns
+    the arrays and the element width of the destination type (0 when unchecked)."""
+    dst_b = src_b = 0
+    if validate and n > 0:
+        dst_b = _TYPE_BYTES.get(dst_type, 0)
+        src_b = _TYPE_BYTES.get(wire_type if mode & AR_SRC_WIRE else dst_type, 0)
+        if not dst_b or not src_b:              # the library rejects the call itself
+            dst_b = src_b = 0
+    return _checked_array(dsts, n * dst_b, "dsts"), _checked_array(srcs, n * src_b, "srcs"), dst_b
+
+
+def _checked_array(xs, need: int, what: str):
+    """ptr_array(xs); with ``need`` > 0 every tensor must be contiguous and hold that many bytes."""
+    if xs is None or isinstance(xs, ctypes.Array):
+        return xs
+    vals = []
+    for x in xs:
+        if x is None or isinstance(x, int):
+            vals.append(x)
+            continue
+        vals.append(_addr(x))
+        if need and (x.nbytes < need or not x.is_contiguous()):
+            _check_flat((x,), need, what)
+    return (ctypes.c_void_p * max(1, len(vals)))(*vals)
 
 
 def _validate_rows(dsts, srcs, rows: int, cols: int, src_stride: int, dst_stride: int, dst_type: int,
@@ -260,11 +276,10 @@ def ar_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = 
     """Enqueue one reduce; returns the status (raises ArError on failure if
     ``check``; ValueError before the call if ``validate`` finds a tensor too small)."""
     lib = load_library()
-    if validate:
-        _validate_flat(dsts, srcs, n, dst_type, wire_type, mode)
+    n, dst_type, wire_type, mode = int(n), int(dst_type), int(wire_type), int(mode)
+    dst_arr, src_arr, _ = _flat_arrays(dsts, srcs, n, dst_type, wire_type, mode, validate)
     R = len(srcs) if srcs is not None else 0
-    rc = lib.ar_reduce(ctx, _ptr_array(dsts), _ptr_array(srcs), R, int(n), int(dst_type),
-                       int(wire_type), int(mode), _stream_handle(stream))
+    rc = lib.ar_reduce(ctx, dst_arr, src_arr, R, n, dst_type, wire_type, mode, _stream_handle(stream))
     if check and rc != AR_OK:
         raise ArError(rc, "ar_reduce")
     return rc
@@ -287,8 +302,9 @@ def bind_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int 
     rlen = int(n) if residual_len is None else int(residual_len)
     if residual is not None and residual_len is None and hasattr(residual, "numel"):
         rlen = int(residual.numel())
-    _validate_flat(dsts, srcs, n, dst_type, wire_type, mode, residual, rlen)
-    dst_arr, src_arr = _ptr_array(dsts), _ptr_array(srcs)
+    dst_arr, src_arr, dst_b = _flat_arrays(dsts, srcs, int(n), int(dst_type), int(wire_type), int(mode), True)
+    if residual is not None and dst_b:
+        _check_flat((residual,), rlen * dst_b, "residual")
     fast = _fast_module()
     if fast is not None:
         fn = lib.ar_reduce if residual is None else lib.ar_reduce_add
@@ -332,9 +348,10 @@ def ar_reduce_add(ctx, dsts, srcs, n: int, dst_type: int, wire_type: int, mode: 
         if not hasattr(residual, "numel"):
             raise TypeError("residual_len is required when the residual is given as an address")
         residual_len = residual.numel()
-    if validate:
-        _validate_flat(dsts, srcs, n, dst_type, wire_type, mode, residual, residual_len)
-    rc = lib.ar_reduce_add(ctx, _ptr_array(dsts), _ptr_array(srcs), R, int(n), int(dst_type),
+    dst_arr, src_arr, dst_b = _flat_arrays(dsts, srcs, int(n), int(dst_type), int(wire_type), int(mode), validate)
+    if dst_b:
+        _check_flat((residual,), int(residual_len) * dst_b, "residual")
+    rc = lib.ar_reduce_add(ctx, dst_arr, src_arr, R, int(n), int(dst_type),
                            int(wire_type), int(mode), _addr(residual), int(residual_len),
                            _stream_handle(stream))
     if check and rc != AR_OK:
