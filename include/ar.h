@@ -119,8 +119,8 @@ typedef enum {
 /* Optional tuning, read once by ar_init.  Zero fields take the defaults;
  * environment variables AR_SINGLE_SHOT_MAX_BYTES, AR_CHUNK_BYTES,
  * AR_HOST_CHUNK_BYTES, AR_HOST_SLOTS, AR_GRID_WGS, AR_STREAM_KERNEL,
- * AR_STORE_POLICY and AR_HOST_PATH override the defaults when cfg is NULL or
- * the field is zero. */
+ * AR_STORE_POLICY, AR_HOST_PATH and AR_XCD_RUN_ELEMS override the defaults when
+ * cfg is NULL or the field is zero. */
 typedef struct {
     size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank at R = 2
                                      (2x this over all ranks); 0 -> 1 MiB */
@@ -146,6 +146,15 @@ typedef struct {
                                      free while bytes cross PCIe), 2 the kernel reads
                                      the pinned buffers directly over PCIe (no
                                      scratch, lowest latency) */
+    size_t xcd_run_elems;         /* workgroup placement of the streaming kernels
+                                     over MI355X's 8 XCDs (the dispatcher gives
+                                     workgroup b to XCD b mod 8): workgroups are
+                                     renumbered so that each XCD streams runs of
+                                     about this many elements of every source, the
+                                     8 XCDs' runs side by side, round after round.
+                                     0 -> automatic (2^17 for R <= 4, none beyond);
+                                     a value below one workgroup's share (e.g. 1)
+                                     -> no renumbering.  No effect on any result */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.

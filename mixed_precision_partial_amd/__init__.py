@@ -63,6 +63,7 @@ class ArConfig(ctypes.Structure):
         ("stream_kernel", ctypes.c_int),
         ("store_policy", ctypes.c_int),
         ("host_path", ctypes.c_int),
+        ("xcd_run_elems", ctypes.c_size_t),
     ]
 
 

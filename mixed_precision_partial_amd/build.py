@@ -19,12 +19,17 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmpp_ar.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# reference streaming kernels of the benchmark's ceilings (not part of the reduce)
+CEILING_SRC = os.path.join(CSRC, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libmpp_ceiling.so")
 
 OBJ_DIR = os.path.join(HERE, "_build")
 
 
 def sources() -> list[str]:
-    return [os.path.join(CSRC, "ar_api.cpp")] + sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """Sources of the reduce library (the ceiling kernels build on their own)."""
+    hip = [s for s in sorted(glob.glob(os.path.join(CSRC, "*.hip"))) if s != CEILING_SRC]
+    return [os.path.join(CSRC, "ar_api.cpp")] + hip
 
 
 HIPCC_FLAGS = [
@@ -53,6 +58,8 @@ def preload_flags(src: str) -> list[str]:
     name = os.path.basename(src)
     if name.startswith("ar_k_") and "_res" not in name and name != "ar_k_single.hip":
         return PRELOAD_FLAGS
+    if src == CEILING_SRC:
+        return PRELOAD_FLAGS
     return []
 
 
@@ -74,7 +81,7 @@ def _run(cmd: list[str]) -> tuple[int, list[str]]:
 
 def build_library(out: str = LIB_PATH, verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
+    srcs = sources() + [CEILING_SRC]
     objs = [os.path.join(OBJ_DIR, os.path.basename(s) + ".o") for s in srcs]
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     cmds = [[hipcc(), *HIPCC_FLAGS, *preload_flags(s), *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
@@ -88,12 +95,15 @@ def build_library(out: str = LIB_PATH, verbose: bool = False, jobs: int | None =
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join("\n".join(m) for _, m in failed))
     tmp = out + ".tmp"
-    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(link), flush=True)
-    rc, msgs = _run(link)
-    if rc != 0:
-        raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs[:-1], "-o", tmp]
+    ceil_link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", objs[-1], "-o", CEILING_LIB + ".tmp"]
+    for cmd in (link, ceil_link):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        rc, msgs = _run(cmd)
+        if rc != 0:
+            raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
+    os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
     if verbose:
         for _, m in results:
             if m:

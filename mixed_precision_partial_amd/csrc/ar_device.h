@@ -701,10 +701,12 @@ template <class C, int U, bool NT, int ST, int BLOCK, bool SLICED>
 __device__ __forceinline__ void reduce_range(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len) {
     constexpr unsigned wpb = BLOCK / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    // the wave's index, read from lane 0 so the compiler keeps it (and every
-    // tile address derived from it) in scalar registers
-    const unsigned gw = blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const unsigned nw = a.waves;
+    // the wave's index, read from lane 0 so the compiler keeps it (and every
+    // tile address derived from it) in scalar registers; the workgroup's
+    // index is its place in the XCD placement map
+    const unsigned gw = xcd_virtual_block(blockIdx.x, nw / wpb, a.map_lc) * wpb +
+                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
@@ -944,8 +946,8 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, const 
                                               u32x4 (*stage0)[kWave], u32x4 (*stage1)[kWave]) {
     constexpr int U = lds_batch(C::SW, C::RB);
     const int lane = threadIdx.x;
-    const unsigned gw = blockIdx.x;
     const unsigned nw = a.waves;
+    const unsigned gw = xcd_virtual_block(blockIdx.x, nw, a.map_lc);
     constexpr unsigned big = kWaveTile * U;
     const unsigned n_big = len / big;
 #if MPP_LDS_FAST
@@ -1003,7 +1005,8 @@ __device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a, const Ran
 // Kernel parameters.  The fields a wave reads before its first load of a
 // strided range -- the launch length, the range length, the wave count, the
 // source and destination strides, the first two sources and the first
-// destination (with the destination count in the wave count's top byte) --
+// destination, and one "shape" dword (bits 0-23 the wave count, 24-27 the
+// destination count minus one, 28-31 the XCD placement exponent map_lc) --
 // come first, as plain scalars (14 dwords), so that the dispatcher preloads
 // them into SGPRs (the non-residual streaming tables are built with kernarg
 // preloading for the leading parameters; an aggregate parameter is never
@@ -1013,18 +1016,19 @@ __device__ __forceinline__ void stream_lds(const LaunchArgs<C::RB> &a, const Ran
 // starts together, so the scalar fetch of its arguments sits once on the
 // critical path of the call.
 // ---------------------------------------------------------------------------
-#define MPP_HOT_PARAMS uint64_t hot_n, unsigned hot_cols, unsigned hot_waves_ndst, uint64_t hot_src_stride, \
+#define MPP_HOT_PARAMS uint64_t hot_n, unsigned hot_cols, unsigned hot_shape, uint64_t hot_src_stride, \
                        uint64_t hot_dst_stride, const void *hot_src0, const void *hot_src1, void *hot_dst0
 
 template <int NR>
 __device__ __forceinline__ LaunchArgs<NR> with_hot(const LaunchArgs<NR> &a, uint64_t n, unsigned cols,
-                                                   unsigned waves_ndst, uint64_t src_stride, uint64_t dst_stride,
+                                                   unsigned shape, uint64_t src_stride, uint64_t dst_stride,
                                                    const void *src0, const void *src1, void *dst0) {
     LaunchArgs<NR> b = a;
     b.n = n;
     b.cols = cols;
-    b.waves = waves_ndst & 0xffffffu;
-    b.n_dst = static_cast<int>(waves_ndst >> 24);
+    b.waves = shape & 0xffffffu;
+    b.n_dst = static_cast<int>((shape >> 24) & 15u) + 1;
+    b.map_lc = shape >> 28;
     b.src_stride = src_stride;
     b.dst_stride = dst_stride;
     b.src[0] = src0;
@@ -1032,16 +1036,16 @@ __device__ __forceinline__ LaunchArgs<NR> with_hot(const LaunchArgs<NR> &a, uint
     b.dst[0] = dst0;
     return b;
 }
-#define MPP_HOT_ARGS hot_n, hot_cols, hot_waves_ndst, hot_src_stride, hot_dst_stride, hot_src0, hot_src1, hot_dst0
+#define MPP_HOT_ARGS hot_n, hot_cols, hot_shape, hot_src_stride, hot_dst_stride, hot_src0, hot_src1, hot_dst0
 
 // Entry of a kernel with preloaded fields: its working copy of the arguments
 // with those fields substituted, and its workgroup's range -- slice ranges
 // read from the argument block itself, strided ranges from the copy.
 template <class C, bool SLICED, class F>
-__device__ __forceinline__ void hot_entry(const LaunchArgs<C::RB> &a, uint64_t n, unsigned cols, unsigned waves_ndst,
+__device__ __forceinline__ void hot_entry(const LaunchArgs<C::RB> &a, uint64_t n, unsigned cols, unsigned shape,
                                           uint64_t src_stride, uint64_t dst_stride, const void *src0,
                                           const void *src1, void *dst0, F &&run) {
-    const LaunchArgs<C::RB> h = with_hot(a, n, cols, waves_ndst, src_stride, dst_stride, src0, src1, dst0);
+    const LaunchArgs<C::RB> h = with_hot(a, n, cols, shape, src_stride, dst_stride, src0, src1, dst0);
     RangeOff o;
     unsigned len;
     if constexpr (SLICED) {

@@ -54,13 +54,38 @@ struct LaunchArgs {
     void       *dst[NR];    // binary32, or 16-bit for a narrow destination
     uint64_t    slice_start[NR];
     unsigned    slice_len[NR];
+    unsigned    map_lc;     // workgroup placement over the XCDs: log2 of the
+                            // run of consecutive workgroups' tiles an XCD takes
+                            // per round (see xcd_virtual_block); 0 = the
+                            // hardware's own one-by-one round robin
 };
+
+// Workgroup placement over the 8 XCDs.  The dispatcher hands workgroup b of
+// a launch to XCD b mod 8.  With runs of C = 2^lc workgroups, the grid's
+// first 8C x floor(G / 8C) workgroups are renumbered so that XCD x processes,
+// in each round, the tiles of C consecutive virtual workgroups (its run of
+// the round), and the runs of successive rounds follow each other through
+// the tensor:  b = 8 j + x  ->  v = (8 floor(j / C) + x) C + (j mod C).
+// The remaining workgroups keep their index, so the map is a permutation of
+// [0, G): every tile is still processed exactly once (which workgroup does it
+// has no effect on any value).  lc = 0 is the identity.
+__host__ __device__ inline unsigned xcd_virtual_block(unsigned b, unsigned G, unsigned lc) {
+    const unsigned full = G & ~((8u << lc) - 1u);
+    if (b >= full) return b;
+    const unsigned x = b & 7u;
+    const unsigned j = b >> 3;
+    return ((((j >> lc) << 3) + x) << lc) + (j & ((1u << lc) - 1u));
+}
 
 // What the host fills in for any rank count; launch() copies it into the
 // LaunchArgs of the chosen kernel's bucket.
 struct KernelArgs : LaunchArgs<AR_MAX_RANKS> {
     int store_nt;   // 1: non-temporal stores, 0: ordinary (cached) stores;
                     // selects the kernel instance, not passed to the GPU
+    size_t xcd_run_elems; // placement: elements of each source an XCD
+                          // streams per run (launch() derives map_lc from
+                          // it); below one workgroup's share keeps the
+                          // identity placement
 };
 
 // Largest element count one launch covers (32-bit element indices inside the
@@ -102,6 +127,17 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs arg
 // `grid_override` (> 0) fixes the workgroups per slice.
 LaunchShape plan_shape(Family family, bool src_is_wire, int R, bool res, unsigned max_slice_len, unsigned n_slices,
                        int cu_count, int grid_override);
+
+// Placement exponent for a streaming launch whose workgroups each process
+// `wg_elems` elements, grid_x workgroups per range: the largest lc < 16 with
+// 2^lc workgroups' share <= run_elems and 8 runs <= grid_x (one whole round
+// inside a range); 0 (identity) otherwise.
+inline unsigned xcd_map_lc(unsigned grid_x, size_t wg_elems, size_t run_elems) {
+    if (wg_elems == 0) return 0;
+    unsigned lc = 0;
+    while (lc < 15 && (wg_elems << (lc + 1)) <= run_elems && (uint64_t(8) << (lc + 1)) <= grid_x) ++lc;
+    return lc;
+}
 
 // Elements processed per wave per loop iteration (a multiple of kWaveTile).
 unsigned stream_tile_elems(Family family, bool src_is_wire, int R);

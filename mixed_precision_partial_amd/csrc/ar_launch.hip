@@ -49,6 +49,7 @@ hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &sha
     b.dst_stride = a.dst_stride;
     b.res_stride = a.res_stride;
     b.res = a.res;
+    b.map_lc = a.map_lc;
     for (int r = 0; r < NR; ++r) {
         b.src[r] = a.src[r];
         b.dst[r] = a.dst[r];
@@ -56,13 +57,14 @@ hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &sha
         b.slice_len[r] = a.slice_len[r];
     }
     // the leading scalar parameters (preloaded into SGPRs), then the block;
-    // the wave count (below 2^24) carries the destination count in its top byte
+    // the shape dword packs the wave count (below 2^24), the destination
+    // count minus one (1 .. 16) and the placement exponent (below 16)
     uint64_t hot_n = b.n, hot_src_stride = b.src_stride, hot_dst_stride = b.dst_stride;
     unsigned hot_cols = b.cols;
-    unsigned hot_waves_ndst = b.waves | (static_cast<unsigned>(b.n_dst) << 24);
+    unsigned hot_shape = b.waves | (static_cast<unsigned>(b.n_dst - 1) << 24) | (b.map_lc << 28);
     const void *hot_src0 = b.src[0], *hot_src1 = b.src[1];
     void *hot_dst0 = b.dst[0];
-    void *hot_kargs[] = {&hot_n, &hot_cols, &hot_waves_ndst, &hot_src_stride, &hot_dst_stride,
+    void *hot_kargs[] = {&hot_n, &hot_cols, &hot_shape, &hot_src_stride, &hot_dst_stride,
                          &hot_src0, &hot_src1, &hot_dst0, &b};
     void *block_kargs[] = {&b};
     return hipLaunchKernel(fn, dim3(shape.grid_x, shape.grid_y, 1), dim3(shape.block, 1, 1),
@@ -141,9 +143,13 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
             : static_cast<unsigned>(stream_block(bucket_ranks(a.R), res != 0, types.src_is_wire));
     if (shape.block != want_block) return hipErrorInvalidValue;
     a.waves = shape.grid_x * (shape.block / kWave);
-    // the kernels write destination 0 unconditionally; the wave count carries
-    // the destination count in its top byte
+    // the kernels write destination 0 unconditionally; the shape dword carries
+    // the wave count, the destination count and the placement exponent
     if (a.waves >= (1u << 24) || a.n_dst < 1 || a.n_dst > AR_MAX_RANKS) return hipErrorInvalidValue;
+    // elements one workgroup processes (its waves' batches)
+    const size_t wg_elems = static_cast<size_t>(shape.block / kWave) * batch_tiles(family, types.src_is_wire, a.R) *
+                            kWaveTile;
+    a.map_lc = family == Family::SingleShot ? 0u : xcd_map_lc(shape.grid_x, wg_elems, a.xcd_run_elems);
     const bool hot = family != Family::SingleShot && !res;
     switch (b) {
     case 0: return launch_as<2>(fn, a, shape, hot, stream);

@@ -23,6 +23,7 @@ int main(void) {
     FIELD(ar_config, stream_kernel);
     FIELD(ar_config, store_policy);
     FIELD(ar_config, host_path);
+    FIELD(ar_config, xcd_run_elems);
     printf("sizeof ar_plan %zu\n", sizeof(ar_plan));
     FIELD(ar_plan, mode);
     FIELD(ar_plan, n_dst);

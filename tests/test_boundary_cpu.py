@@ -45,7 +45,7 @@ def test_status_strings():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 5 * 4 + 4   # padded to 8
+    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 6 * 4 + 8   # six ints, then xcd_run_elems
     assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 4 * 4 + 2 * 4
 
 
@@ -513,3 +513,22 @@ def test_header_is_c_and_matches_the_binding(tmp_path):
               "stream_kernel", "active_mask"):
         assert got[k] == getattr(p, k), k
     assert got["slice1"] == (p.slice_start[1], p.slice_len[1])
+
+
+def test_xcd_placement_map_is_a_permutation(tmp_path):
+    """tests/c_abi/xcd_map_check.cpp, built with hipcc as host code against the
+    library's internal header: the workgroup renumbering of the streaming kernels
+    is a permutation of the grid for every size and exponent tried, the identity
+    at exponent 0, walks runs of consecutive tiles per XCD, and the exponent the
+    launcher picks never exceeds the requested run or one round per range."""
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "xcd_map_check")
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    cmd = [hipcc, "-O1", "-std=c++17", "-I", os.path.join(root, "include"),
+           "-I", os.path.join(root, "mixed_precision_partial_amd", "csrc"),
+           os.path.join(root, "tests", "c_abi", "xcd_map_check.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr

@@ -667,3 +667,54 @@ def test_inactive_ranks(kctx, kname, mode_name):
                         want = np.zeros(n, dtype=np.float32)   # +0.0 everywhere
                     for d in dsts:
                         assert_bits_equal(d.result(), want, what)
+
+
+# XCD placement: runs from one workgroup's share up to far beyond the grid, with
+# grids that are and are not multiples of 8 runs (the tail keeps its numbering),
+# through both streaming families, every streaming schedule, 16-bit sources, a
+# residual and 8 ranks -- every result bit-exact against the oracle.
+PLACEMENT_RUNS = [1, 512, 2048, 1 << 13, 1 << 17, 1 << 24]
+
+
+@pytest.mark.parametrize("run", PLACEMENT_RUNS)
+def test_xcd_placement_every_run(run):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    cases = [
+        # (R, n, wire, mode, extra config, src_wire)
+        (2, (1 << 21) + 77, ar.AR_BF16, ar.AR_MODE_CHUNKED, {}, False),
+        (3, 1_000_003, ar.AR_F16, ar.AR_MODE_CHUNKED, {"grid_wgs": 9}, False),
+        (4, (1 << 20) + 4 * 512 + 3, ar.AR_F16, ar.AR_MODE_RS_BCAST, {}, False),
+        (4, 777_777, ar.AR_BF16, ar.AR_MODE_RS_BCAST, {"stream_kernel": 2, "grid_wgs": 100}, False),
+        (2, (1 << 20) + 5, ar.AR_BF16, ar.AR_MODE_CHUNKED, {"stream_kernel": 2, "chunk_bytes": 1 << 16}, True),
+        (8, 600_001, ar.AR_BF16, ar.AR_MODE_CHUNKED, {"stream_kernel": 1}, False),
+        (2, 3 * 1024 * 512, ar.AR_F32, ar.AR_MODE_CHUNKED, {"grid_wgs": 1000}, False),
+    ]
+    for i, (R, n, wire, mode, extra, src_wire) in enumerate(cases):
+        c = ar.ar_init(0, {"xcd_run_elems": run, **extra})
+        try:
+            log_case(f"placement run={run} case {i}: R={R} n={n} wire={wire} mode={mode} cfg={extra} "
+                     f"src_wire={src_wire}")
+            srcs = wl.random_partials(70_000 + i, run % 997, R, n, dist="normal+outliers")
+            got, used = run_case(None, srcs, wire, mode, src_wire=src_wire, config_ctx=c)
+        finally:
+            torch.cuda.synchronize()
+            ar.ar_free(c)
+        want = oracle_result(used, wire, src_type=wire if src_wire else None)
+        for d, g in enumerate(got):
+            assert_bits_equal(g, want, f"placement run={run} case {i} dst {d}")
+    # a residual (register family, 128-thread workgroups) and a row-strided call
+    c = ar.ar_init(0, {"xcd_run_elems": run})
+    try:
+        n = (1 << 21) + 8 * 3
+        srcs = wl.random_partials(70_100, 1, 2, n, dist="normal")
+        res = wl.residual(70_101, 0, n)
+        dst = GuardedDst(n)
+        log_case(f"placement run={run}: residual n={n}")
+        ar.ar_reduce_add(c, [dst.ptr()], [to_device(s) for s in srcs], n, ar.AR_F32, ar.AR_BF16,
+                         ar.AR_MODE_CHUNKED, to_device(res), n)
+        torch.cuda.synchronize()
+        assert_bits_equal(dst.result(), oracle.reduce(srcs, oracle.BF16, residual=res)[0], f"placement {run} res")
+    finally:
+        torch.cuda.synchronize()
+        ar.ar_free(c)

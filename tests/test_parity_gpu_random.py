@@ -12,6 +12,8 @@ case that reruns identically.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -27,6 +29,10 @@ SCHEDULES = [ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar
              ar.AR_MODE_AUTO]
 N_CASES = 400
 BATCH = 25
+# MPP_RANDOM_CASES="start:stop" runs another range of the same generator
+# (e.g. MPP_RANDOM_CASES=400:3400); the default is cases 0-399
+_range = os.environ.get("MPP_RANDOM_CASES", "")
+CASE_START, CASE_STOP = (int(x) for x in _range.split(":")) if _range else (0, N_CASES)
 
 
 def draw_case(i: int) -> dict:
@@ -59,6 +65,8 @@ def draw_case(i: int) -> dict:
         "chunk_bytes": int(rng.choice([0, 0, 4096, 65536])),
         "host_chunk_bytes": int(rng.choice([0, 0, 1 << 14, 1 << 16])),
         "host_slots": int(rng.choice([0, 1, 2])),
+        # XCD placement runs: automatic, none, and runs from one workgroup to 4 Mi elements
+        "xcd_run_elems": int(rng.choice([0, 0, 1, 512, 4096, 1 << 15, 1 << 17, 1 << 22])),
     }
     return dict(i=i, R=R, n=n, wire=wire, dst_type=dst_type, src_wire=src_wire, res_form=str(res_form), L=L,
                 mode=mode, inactive=[bool(x) for x in inactive], in_place=bool(in_place), cfg=cfg,
@@ -136,8 +144,8 @@ def gpu():
         pytest.skip("no GPU visible")
 
 
-@pytest.mark.parametrize("start", range(0, N_CASES, BATCH))
+@pytest.mark.parametrize("start", range(CASE_START, CASE_STOP, BATCH))
 def test_random_sweep(gpu, start):
-    for i in range(start, start + BATCH):
+    for i in range(start, min(start + BATCH, CASE_STOP)):
         run_case(draw_case(i))
     torch.cuda.empty_cache()
