@@ -204,6 +204,28 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
 int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
               int dst_type, int wire_type, unsigned mode, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under graph-free
+ * tight loops, harnesses that forbid hipMalloc): the host-staged reduce of
+ * ar_reduce through the copy-engine pipeline, with its staging ring in the
+ * library's static device array (64 MiB per device, part of the code object,
+ * held until the process ends) instead of the context's hipMalloc'd ring.
+ * It calls no hipMalloc / hipFree and allocates nothing else.
+ *   Arguments, ownership and results are those of ar_reduce for a
+ *   host-staged call; mode must be AR_MODE_HOST_STAGED (or AR_MODE_AUTO
+ *   with pinned host sources) plus optional AR_SRC_WIRE /
+ *   AR_SRC_INACTIVE_NULL, whatever the context's host_path.
+ *   The copy chunk shrinks so that host_slots x R chunks fit the array
+ *   (any n is accepted); a host_chunk_bytes set in the context's ar_config
+ *   whose ring would not fit -> AR_ERR_NOMEM, nothing enqueued.
+ *   Every call on a device shares that device's array: calls through one
+ *   context are ordered by its slot events, but calls of different contexts
+ *   that overlap on one device race on the array.  Nothing in it needs to
+ *   start at zero (every byte a kernel reads was copied in by the same call).
+ * Errors: those of ar_reduce; another resolved mode -> AR_ERR_INVALID; under
+ * stream capture -> AR_ERR_UNSUPPORTED. */
+int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
+                            int dst_type, int wire_type, unsigned mode, void *hip_stream);
+
 /* Enqueue one reduce followed by a residual add: after the last rank,
  * res[i mod residual_len] is added in the destination type, element-wise
  * (residual_len == n) or as one row broadcast to every row (residual_len

@@ -122,6 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ar_reduce.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, sz,
                               ctypes.c_int, ctypes.c_int, ctypes.c_uint, vp]
     lib.ar_reduce.restype = ctypes.c_int
+    lib.ar_reduce_staged_static.argtypes = lib.ar_reduce.argtypes
+    lib.ar_reduce_staged_static.restype = ctypes.c_int
     lib.ar_free.argtypes = [vp]
     lib.ar_free.restype = ctypes.c_int
     lib.ar_status_str.argtypes = [ctypes.c_int]
@@ -283,6 +285,21 @@ def ar_reduce(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = 
     rc = lib.ar_reduce(ctx, dst_arr, src_arr, R, n, dst_type, wire_type, mode, _stream_handle(stream))
     if check and rc != AR_OK:
         raise ArError(rc, "ar_reduce")
+    return rc
+
+
+def ar_reduce_staged_static(ctx, dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = AR_BF16,
+                            mode: int = AR_MODE_HOST_STAGED, stream=None, check: bool = True,
+                            validate: bool = True) -> int:
+    """The host-staged reduce with its staging ring in the library's static device
+    array (no device allocation); arguments and checks as ar_reduce."""
+    lib = load_library()
+    n, dst_type, wire_type, mode = int(n), int(dst_type), int(wire_type), int(mode)
+    dst_arr, src_arr, _ = _flat_arrays(dsts, srcs, n, dst_type, wire_type, mode, validate)
+    R = len(srcs) if srcs is not None else 0
+    rc = lib.ar_reduce_staged_static(ctx, dst_arr, src_arr, R, n, dst_type, wire_type, mode, _stream_handle(stream))
+    if check and rc != AR_OK:
+        raise ArError(rc, "ar_reduce_staged_static")
     return rc
 
 

@@ -410,6 +410,9 @@ struct ar_ctx {
     std::vector<char> slot_used;
     hipEvent_t ev_start = nullptr;     // caller-stream order point before the copies
     unsigned next_slot = 0;
+    // device address of the library's static staging array on this device
+    // (ar_reduce_staged_static); shared by every context on the device
+    void *static_scratch = nullptr;
 };
 
 namespace {
@@ -655,28 +658,43 @@ int ensure_scratch(ar_ctx *c, size_t bytes) {
 // the internal copy stream; the caller's stream waits for that slot's copies,
 // runs the add kernel over the slot and marks the slot free again.  The copy
 // of a later chunk into the same slot waits for that mark, so copies run ahead
-// of the adds by up to K chunks.
+// of the adds by up to K chunks.  The ring is the context's (grown with
+// hipMalloc when too small), or, with `fixed`, the `fixed_bytes` at `fixed`:
+// the chunk then shrinks to what K slots of R ranks fit there, and nothing is
+// allocated; a configured copy chunk whose ring does not fit is AR_ERR_NOMEM.
 int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
-                    int wire_type, const Residual &res, hipStream_t stream) {
+                    int wire_type, const Residual &res, hipStream_t stream, void *fixed = nullptr,
+                    size_t fixed_bytes = 0) {
     const mpp::Types types = launch_types(plan, wire_type);
     const size_t sb = static_cast<size_t>(plan.src_bytes);
     const size_t db = static_cast<size_t>(plan.dst_bytes);
-    const size_t chunk = plan.chunk_elems;
     const size_t K = static_cast<size_t>(c->cfg.host_slots);
+    size_t chunk = plan.chunk_elems;
+    if (fixed != nullptr) {
+        const size_t fit = round_down(fixed_bytes / (K * static_cast<size_t>(R) * sb), mpp::kWaveTile);
+        if (fit < mpp::kWaveTile) return AR_ERR_NOMEM;
+        if (c->cfg.host_chunk_bytes != 0 && chunk > fit) return AR_ERR_NOMEM;
+        chunk = std::min(chunk, fit);
+    }
+    const size_t n_chunks = (n + chunk - 1) / chunk;
     const size_t rank_stride = chunk * sb;
     const size_t slot_stride = rank_stride * static_cast<size_t>(R);
-    if (int rc = ensure_scratch(c, slot_stride * K)) return rc;
+    char *ring = static_cast<char *>(fixed);
+    if (ring == nullptr) {
+        if (int rc = ensure_scratch(c, slot_stride * K)) return rc;
+        ring = static_cast<char *>(c->scratch);
+    }
 
     if (hipEventRecord(c->ev_start, stream) != hipSuccess) return AR_ERR_RUNTIME;
     if (hipStreamWaitEvent(c->copy_stream, c->ev_start, 0) != hipSuccess) return AR_ERR_RUNTIME;
 
     const mpp::Family family = stream_family(plan);
-    for (size_t ch = 0; ch < plan.n_chunks; ++ch) {
+    for (size_t ch = 0; ch < n_chunks; ++ch) {
         const size_t e0 = ch * chunk;
         const size_t len = std::min(chunk, n - e0);
         const unsigned slot = c->next_slot;
         c->next_slot = (c->next_slot + 1) % static_cast<unsigned>(K);
-        char *slot_base = static_cast<char *>(c->scratch) + slot * slot_stride;
+        char *slot_base = ring + slot * slot_stride;
 
         if (c->slot_used[slot] && hipStreamWaitEvent(c->copy_stream, c->ev_free[slot], 0) != hipSuccess) {
             return AR_ERR_RUNTIME;
@@ -841,6 +859,12 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
         c->ev_start = nullptr;
         rc = AR_ERR_RUNTIME;
     }
+    // the static staging array's address on this device (the guard above made
+    // it current); looked up once per device and shared by its contexts
+    if (rc == AR_OK && mpp::static_scratch(hip_device, &c->static_scratch) != hipSuccess) {
+        c->static_scratch = nullptr;
+        rc = AR_ERR_RUNTIME;
+    }
     if (rc == AR_OK) {
         const size_t K = static_cast<size_t>(conf.host_slots);
         c->ev_h2d.assign(K, nullptr);
@@ -867,8 +891,11 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
 
 namespace {
 
+// `static_staging`: ar_reduce_staged_static -- a host-staged call only, always
+// through the copy engine, its ring in the static staging array.
 int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
-                int wire_type, unsigned mode, const Residual &res, const Rows *rows, void *hip_stream) {
+                int wire_type, unsigned mode, const Residual &res, const Rows *rows, void *hip_stream,
+                bool static_staging = false) {
     if (ctx == nullptr) return AR_ERR_INVALID;
     // cheap checks first, without touching the runtime
     ar_plan plan;
@@ -903,6 +930,10 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
         }
     }
     if (n == 0) return AR_OK;
+    if (static_staging) {
+        if (plan.mode != AR_MODE_HOST_STAGED) return AR_ERR_INVALID;
+        plan.host_direct = 0;
+    }
 
     const Kind want_src = plan.mode == AR_MODE_HOST_STAGED ? Kind::PinnedHost : Kind::Device;
     const void *src_view[AR_MAX_RANKS];
@@ -949,6 +980,10 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
             direct.mode = AR_MODE_CHUNKED;
             return run_device(ctx, direct, dst, src_view, R, n, wire_type, res, stream);
         }
+        if (static_staging) {
+            return run_host_staged(ctx, plan, dst, srcs, R, n, wire_type, res, stream, ctx->static_scratch,
+                                   mpp::kStaticScratchBytes);
+        }
         return run_host_staged(ctx, plan, dst, srcs, R, n, wire_type, res, stream);
     }
     return run_device(ctx, plan, dst, srcs, R, n, wire_type, res, stream);
@@ -959,6 +994,11 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
 AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
                      int wire_type, unsigned mode, void *hip_stream) {
     return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, nullptr, hip_stream);
+}
+
+AR_API int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
+                                   int dst_type, int wire_type, unsigned mode, void *hip_stream) {
+    return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, nullptr, hip_stream, true);
 }
 
 AR_API int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,

@@ -139,6 +139,16 @@ inline unsigned xcd_map_lc(unsigned grid_x, size_t wg_elems, size_t run_elems) {
     return lc;
 }
 
+// Size of the library's static staging array (one per device), the only
+// device memory ar_reduce_staged_static uses beyond the caller's buffers.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxStaticScratchDevices = 64;
+
+// Device address of the static staging array on `device`, which the caller
+// has made current.  Looked up with hipGetSymbolAddress the first time per
+// device and kept; returns the runtime's error when the lookup fails.
+hipError_t static_scratch(int device, void **out);
+
 // Elements processed per wave per loop iteration (a multiple of kWaveTile).
 unsigned stream_tile_elems(Family family, bool src_is_wire, int R);
 

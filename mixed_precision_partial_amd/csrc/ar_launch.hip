@@ -1,6 +1,8 @@
 // ar_launch.hip -- launch shapes and kernel selection for the tables that
-// the ar_k_*.hip files define.
+// the ar_k_*.hip files define, and the library's static staging array.
 #include "ar_device.h"
+
+#include <mutex>
 
 namespace mpp {
 namespace {
@@ -71,7 +73,32 @@ hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &sha
                            hot ? hot_kargs : block_kargs, shape.lds_bytes, stream);
 }
 
+// Staging memory of ar_reduce_staged_static: one array per device, part of
+// the code object (the loader places it on every device the library runs
+// on, where it stays until the process ends).  Host code never passes the
+// name `scratch` itself to a kernel or a copy -- on the host it is only a
+// stand-in for the symbol -- but the device address static_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 }  // namespace
+
+hipError_t static_scratch(int device, void **out) {
+    static std::mutex mu;
+    static void *addr[kMaxStaticScratchDevices] = {};
+    if (out == nullptr || device < 0 || device >= kMaxStaticScratchDevices) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[device] == nullptr) {
+        // the caller has made `device` current: each device has its own copy
+        // of the array at its own address
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[device] = p;
+    }
+    *out = addr[device];
+    return hipSuccess;
+}
 
 unsigned stream_tile_elems(Family family, bool src_is_wire, int R) {
     return kWaveTile * batch_tiles(family, src_is_wire, R);
