@@ -8,10 +8,17 @@ plan, load, cast-to-wire, ordered fp32 fold, store -- all in one launch).
 Inputs are resident in HBM before the timed region and rotate over several
 sets so that the 256 MiB Infinity Cache cannot serve them.
 
+Before the timed steps: the ceiling kernels over the same buffers (reported),
+the warmup steps, and one lead-in call (reported).  The K timed steps lie
+between two HIP events on the launch stream.  Afterwards: per-step times in a
+pass of their own, parity against the oracle, the oracle's own throughput on
+the host cores, decode-size latency (fp32 and bf16 wire), and the other
+configurations beside their own ceilings (skipped with --quick).
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S]
-                    [--no-cpu-baseline] [--no-decode] [--extras]
+                    [--no-cpu-baseline] [--no-decode] [--quick]
 """
 from __future__ import annotations
 
@@ -34,6 +41,71 @@ CSRC = os.path.join(ROOT, "mixed_precision_partial_amd", "csrc")
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvent:
+    """A HIP event created with hipEventDisableSystemFence, recorded on a given
+    stream.  HIP's own documentation gives this flag for events that only
+    measure time: recording it skips the system-scope cache writeback and
+    invalidation that a default event performs, which on this part costs
+    ~2.6 us per event (measured: an empty interval between two default events
+    reads 4.3-7.3 us, between two of these 3.2 us) and would otherwise sit
+    inside every timed interval.  Uses the HIP runtime torch has loaded."""
+
+    FLAG_DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime already loaded by torch
+            vp = ctypes.c_void_p
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [vp, vp]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            hip.hipEventDestroy.argtypes = [vp]
+            HipEvent._hip = hip
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAG_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream) -> None:
+        rc = HipEvent._hip.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        """Milliseconds from this event to `end` (both complete: call after a synchronize)."""
+        f = self._ct.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._ct.byref(f), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(f.value)
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.h:
+            HipEvent._hip.hipEventDestroy(self.h)
+
+
+def timed_us(torch, stream, fn, reps: int, lead: int = 1) -> float:
+    """Mean microseconds per call of `fn(k)` over `reps` back-to-back calls on
+    `stream`, between two HipEvents.  `lead` untimed calls are enqueued just
+    before the start event so that the GPU queue is not empty when it is
+    reached (otherwise the first timed call's host-side enqueue lands inside
+    the interval)."""
+    torch.cuda.synchronize()
+    for k in range(lead):
+        fn(k)
+    a, b = HipEvent(), HipEvent()
+    a.record(stream)
+    for k in range(reps):
+        fn(lead + k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_ms(b) * 1e3 / reps
 
 
 def kernel_source_hash() -> str:
@@ -81,7 +153,9 @@ def parse():
     p.add_argument("--sets", type=int, default=8, help="rotated input/output sets (>= 6 defeats the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
-    p.add_argument("--extras", action="store_true", help="also time the other schedules (stderr lines)")
+    p.add_argument("--quick", action="store_true",
+                   help="skip the other configurations (slice + broadcast, R=8 from HBM and from host memory, "
+                        "residual, narrow and row-strided forms) that the default run also measures")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--summarize-trace", metavar="DIR",
                    help="write profiles/ summary of a rocprofv3 --kernel-trace --stats output dir")
@@ -141,26 +215,49 @@ def main() -> int:
         s = k % S
         ar.ar_reduce(ctx, [dev_dst[s]], dev_src[s], n, ar.AR_F32, w.wire, mode, stream=stream)
 
+    # Reported measurement before the timed steps: the achievable ceilings of
+    # this call's access pattern on the same rotated buffers (plain 16-byte
+    # copy and 2-read / 1-write kernels of the benchmark's own, and the
+    # runtime's device-to-device copy).  It also brings the GPU out of its idle
+    # clocks, which a cold start costs (measured: the first 20 steps after 1 s
+    # idle ran at 20.2 us/step, the next 20 at 16.1).
+    ceil = ceilings(torch, stream, dev_src, dev_dst, n, S)
+
     log(f"warmup {args.warmup} steps")
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} steps")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # One more untimed call, enqueued just before the start event (reported as
+    # lead_in_calls): the timed calls then find the GPU busy, so the interval
+    # holds K whole calls -- host path and kernel -- and not also the idle gap
+    # before the first one reaches the queue.
+    log(f"timing {args.steps} steps (1 lead-in call)")
+    start, end = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    step(args.warmup)
+    host_t = [0.0] * (args.steps + 1)
     start.record(stream)
+    host_t[0] = time.perf_counter()
     for k in range(args.steps):
-        step(k)
+        step(args.warmup + 1 + k)
+        host_t[k + 1] = time.perf_counter()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(end)
+    ms_total = start.elapsed_ms(end)
     ms_per_step = ms_total / args.steps
     gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"{ms_per_step * 1e3:.2f} us/step, {gbs:.1f} GB/s effective (wall {wall:.3f} s)")
+    enqueue_us = [round((host_t[i + 1] - host_t[i]) * 1e6, 2) for i in range(args.steps)]
+    log(f"{ms_per_step * 1e3:.3f} us/step, {gbs:.1f} GB/s effective (wall {wall:.4f} s); host enqueue per "
+        f"step: median {np.median(enqueue_us):.2f} us, max {max(enqueue_us):.2f} us")
+
+    # Per-step times, in a pass of their own after the timed one (an event
+    # between every two steps adds its own cost to each step, so these are
+    # not the timed figure): the same K steps, each between two events.
+    per_step = per_step_times(torch, stream, step, args.steps)
+    log("per-step us (own pass, an event between steps): " + " ".join(f"{x:.2f}" for x in per_step))
 
     # parity of the timed path on set 0 against the oracle (outside the timed region)
     parity = None
@@ -205,17 +302,24 @@ def main() -> int:
                             "sample": f"{mt_reps} full calls split over {T} threads"},
             "sample": f"{reps + 1} full calls of the same 2048x4096 R=2 bf16-wire reduce "
                       f"({cpu_s + one:.1f} s, single-threaded scalar C oracle)",
+            "decode_us_per_call": oracle_decode_latency(oracle, wl),
         }
 
-    extras = {"ceilings_prefill_size": ceilings(torch, n, S)}
-    ceil = extras["ceilings_prefill_size"]
-    ceil["value_over_copy"] = round(gbs / ceil["copy_GB/s"], 3)
-    ceil["value_over_add_2r1w"] = round(gbs / ceil["add_2r1w_GB/s"], 3)
+    extras = {"ceilings_prefill_size": ceil}
+    best_2r1w = max(v for k, v in ceil.items() if k.startswith("kernel_2r1w"))
+    extras["value_over_ceiling_2r1w"] = round(gbs / best_2r1w, 4)
+    extras["timing"] = {
+        "method": "HIP events created with hipEventDisableSystemFence, recorded on the launch stream",
+        "lead_in_calls": 1,
+        "host_enqueue_us_per_step": enqueue_us,
+        "per_step_us_separate_pass": [round(x, 3) for x in per_step],
+        "before_timed_steps": "ceiling kernels over the same rotated buffers (reported in "
+                              "ceilings_prefill_size), then the warmup steps, then the lead-in call",
+    }
     if not args.no_decode:
-        extras["decode_bf16"] = decode_latency(torch, ar, wl)
-    if args.extras:
-        # the fp32-wire decode vector: the same latency-bound call without a conversion
         extras["decode_f32"] = decode_latency(torch, ar, wl, "decode_f32", floors=False)
+        extras["decode_bf16"] = decode_latency(torch, ar, wl)
+    if not args.quick:
         extras.update(other_schedules(torch, ar, wl))
 
     traffic = measured_traffic(algo_bytes)
@@ -255,6 +359,9 @@ def main() -> int:
         "extras": extras,
     }
     print(json.dumps(result), flush=True)
+    if parity == "MISMATCH":
+        log("the timed path's output differs from the oracle: failing the run")
+        return 3
     return 0
 
 
@@ -539,30 +646,105 @@ def profile_pass(torch, ar, wl, args):
     return 0
 
 
-def ceilings(torch, n, sets):
-    """Achievable rates at the prefill size on random data, same rotation: a
-    plain device copy and torch's two-read / one-write add (GB/s of bytes moved)."""
-    stream = torch.cuda.current_stream()
-    a = [torch.rand(n, device="cuda") - 0.5 for _ in range(sets)]
-    b = [torch.rand(n, device="cuda") - 0.5 for _ in range(sets)]
-    c = [torch.empty(n, device="cuda") for _ in range(sets)]
+CEILING_LIB = os.path.join(ROOT, "mixed_precision_partial_amd", "libmpp_ceiling.so")
 
-    def rate(fn, nbytes, reps=400):
-        for i in range(sets):
-            fn(i)
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        for k in range(reps):
-            fn(k % sets)
-        e.record(stream)
-        torch.cuda.synchronize()
-        return round(nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9, 1)
 
-    out = {"copy_GB/s": rate(lambda i: c[i].copy_(a[i]), 2 * 4 * n),
-           "add_2r1w_GB/s": rate(lambda i: torch.add(a[i], b[i], out=c[i]), 3 * 4 * n)}
+def ceiling_lib():
+    import ctypes
+
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is missing: build with `python -m mixed_precision_partial_amd.build`")
+    lib = ctypes.CDLL(CEILING_LIB)
+    vp = ctypes.c_void_p
+    lib.mpp_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
+                                       ctypes.POINTER(vp), ctypes.c_size_t, ctypes.c_size_t, vp]
+    lib.mpp_ceiling_launch.restype = ctypes.c_int
+    return lib
+
+
+def pattern_ceiling(torch, stream, R, D, src_sets, dst_sets, nbytes, reps):
+    """Best GB/s (bytes moved) of the ceiling kernel with the (R reads, D writes)
+    pattern over the given rotated tensors, `nbytes` per stream: every store
+    policy, with and without the XCD runs."""
+    import ctypes
+
+    lib = ceiling_lib()
+    vp = ctypes.c_void_p
+    sh = vp(stream.cuda_stream)
+    arrays = [((vp * R)(*[t.data_ptr() for t in srcs]), (vp * D)(*[t.data_ptr() for t in dsts]))
+              for srcs, dsts in zip(src_sets, dst_sets)]
+    best = 0.0
+    for sp in (0, 1, 2):
+        for run in (0, 512 << 10):
+            def fn(k, sp=sp, run=run):
+                a, b = arrays[k % len(arrays)]
+                if lib.mpp_ceiling_launch(R, D, sp, a, b, nbytes, run, sh) != 0:
+                    raise RuntimeError("ceiling kernel launch failed")
+            best = max(best, (R + D) * nbytes / timed_us(torch, stream, fn, reps) / 1e3)
+    return round(best, 1)
+
+
+def ceilings(torch, stream, dev_src, dev_dst, n, sets, reps=300):
+    """Achievable rates at the prefill size over the benchmark's own rotated
+    buffers (GB/s of bytes moved): the reference kernels of libmpp_ceiling.so --
+    a 16-byte copy (1 read : 1 write) and a 2-read : 1-write stream, each with
+    every store policy, with the hardware's placement and with the reduce's XCD
+    runs -- and the runtime's device-to-device copy (torch copy_).  The
+    reduce is compared with the best 2-read : 1-write figure."""
+    import ctypes
+
+    lib = ceiling_lib()
+    vp = ctypes.c_void_p
+    sh = vp(stream.cuda_stream)
+    arrays = [((vp * 2)(dev_src[i][0].data_ptr(), dev_src[i][1].data_ptr()), (vp * 1)(dev_dst[i].data_ptr()))
+              for i in range(sets)]
+    out = {}
+    for R, name in ((1, "copy_1r1w"), (2, "2r1w")):
+        for sp, sp_name in ((0, "wb"), (1, "nt"), (2, "wt")):
+            for run, run_name in ((0, "hw"), (512 << 10, "xcd512k")):
+                def fn(k, R=R, sp=sp, run=run):
+                    src, dst = arrays[k % sets]
+                    rc = lib.mpp_ceiling_launch(R, 1, sp, src, dst, n * 4, run, sh)
+                    if rc != 0:
+                        raise RuntimeError(f"ceiling kernel launch failed ({rc})")
+                us = timed_us(torch, stream, fn, reps)
+                out[f"kernel_{name}_{sp_name}_{run_name}_GB/s"] = round((R + 1) * 4 * n / us / 1e3, 1)
+    us = timed_us(torch, stream, lambda k: dev_dst[k % sets].copy_(dev_src[k % sets][0]), reps)
+    out["runtime_d2d_copy_GB/s"] = round(2 * 4 * n / us / 1e3, 1)
     log(f"ceilings at the prefill size: {out}")
     return out
+
+
+def per_step_times(torch, stream, step, K):
+    """Microseconds of each of K steps, each step between two HipEvents (a
+    pass of its own: the events between steps add their own cost)."""
+    torch.cuda.synchronize()
+    step(0)
+    ev = [HipEvent() for _ in range(K + 1)]
+    ev[0].record(stream)
+    for k in range(K):
+        step(1 + k)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[k].elapsed_ms(ev[k + 1]) * 1e3 for k in range(K)]
+
+
+def oracle_decode_latency(oracle, wl):
+    """The CPU oracle at decode size: microseconds per call over all 10,000
+    seeded calls of the bf16-wire decode configuration, and over 2,000 calls
+    of the fp32-wire one, single-threaded (the host arrays of each call are
+    generated beforehand, outside the timing)."""
+    res = {}
+    for name, calls in (("decode_bf16", 10_000), ("decode_f32", 2_000)):
+        w = wl.WORKLOADS[name]
+        inputs = [wl.partials(w, c) for c in range(calls)]
+        t = time.perf_counter()
+        for srcs in inputs:
+            oracle.reduce(srcs, w.wire)
+        res[f"{name}_us_per_call"] = round((time.perf_counter() - t) * 1e6 / calls, 2)
+        res[f"{name}_calls"] = calls
+    log(f"oracle at decode size: {res}")
+    return res
 
 
 def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
@@ -595,8 +777,7 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
         call(c)
         bound[c]()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    start, end = HipEvent(), HipEvent()
     t0 = time.perf_counter()
     start.record(stream)
     for c in range(calls):
@@ -604,7 +785,7 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
     end.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t0
-    us_async = start.elapsed_time(end) * 1e3 / calls
+    us_async = start.elapsed_ms(end) * 1e3 / calls
     t0 = time.perf_counter()
     start.record(stream)
     for fn in bound:
@@ -613,7 +794,7 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
     end.record(stream)
     torch.cuda.synchronize()
     host_bound_s = time.perf_counter() - t0
-    us_async_bound = start.elapsed_time(end) * 1e3 / calls
+    us_async_bound = start.elapsed_ms(end) * 1e3 / calls
     # the same calls captured once into a HIP graph and replayed: the
     # per-call cost without Python or runtime launch overhead
     graph_calls = 1000
@@ -630,7 +811,7 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
         g.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    us_graph = start.elapsed_time(end) * 1e3 / (reps * graph_calls)
+    us_graph = start.elapsed_ms(end) * 1e3 / (reps * graph_calls)
     del g
     # per-call round trip, wall clock: enqueue + hipStreamSynchronize on the launch stream
     lat = np.empty(2000)
@@ -664,7 +845,7 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
         one.fill_(1.0)
     end.record(stream)
     torch.cuda.synchronize()
-    floor_async = start.elapsed_time(end) * 1e3 / calls
+    floor_async = start.elapsed_ms(end) * 1e3 / calls
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, capture_error_mode="relaxed"):
         for _ in range(graph_calls):
@@ -676,7 +857,7 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
         g.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    floor_graph = start.elapsed_time(end) * 1e3 / (reps * graph_calls)
+    floor_graph = start.elapsed_ms(end) * 1e3 / (reps * graph_calls)
     del g
     res = {"floor_1elem_fill_us_async": round(floor_async, 3),
            "floor_1elem_fill_us_graph_replay": round(floor_graph, 3), **res}
@@ -684,21 +865,25 @@ def decode_latency(torch, ar, wl, name="decode_bf16", floors=True):
     return res
 
 
+def with_ceiling(entry: dict, ceiling_gbs: float) -> None:
+    entry["ceiling_GB/s"] = ceiling_gbs
+    entry["frac_of_ceiling"] = round(entry["GB/s"] / ceiling_gbs, 4)
+    entry["frac_of_hbm_peak"] = round(entry["GB/s"] / HBM_PEAK_GBS, 4)
+
+
 def other_schedules(torch, ar, wl):
-    """Broadcast-slice and R=8 shapes from HBM plus the host-staged mode (stderr + extras)."""
+    """The other configurations and adjacent forms: the 4-rank slice + broadcast,
+    residual adds, narrow destinations, inactive ranks, row-strided tensors, R=8
+    from HBM (fp32 and bf16 partials) and from pinned host memory (direct reads,
+    copy-engine pipeline, static staging) -- each beside the ceiling kernel run
+    at its own bytes and access pattern where one exists (stderr + extras)."""
     out = {}
     stream = torch.cuda.current_stream()
 
     def timed(fn, reps):
+        """milliseconds per call (one lead-in call, HipEvents on the stream)"""
         fn()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        for _ in range(reps):
-            fn()
-        e.record(stream)
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / reps
+        return timed_us(torch, stream, lambda k: fn(), reps) / 1e3
 
     ctx = ar.ar_init(0)
     # the 4-rank broadcast over two rotated sets (1 GiB, beyond the Infinity Cache)
@@ -719,6 +904,7 @@ def other_schedules(torch, ar, wl):
                                            stream=stream)), 50)
     b = 2 * w.R * w.n * 4
     out["slice_bcast_f16"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    with_ceiling(out["slice_bcast_f16"], pattern_ceiling(torch, stream, 4, 4, srcs, dsts, w.n * 4, 30))
     log(f"slice_bcast_f16: {out['slice_bcast_f16']}")
     # the same broadcast with an element-wise fp32 residual (the receiving rank's hidden state)
     ress = [torch.from_numpy(wl.residual(w.case, 5 + k, w.n)).cuda() for k in range(bsets)]
@@ -768,6 +954,8 @@ def other_schedules(torch, ar, wl):
                                           stream=stream)), 200)
     b = w.R * w.n * 2 + w.n * 2
     out["prefill_bf16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    with_ceiling(out["prefill_bf16_dst"],
+                 pattern_ceiling(torch, stream, 2, 1, srcs, [[d] for d in dsts], w.n * 2, 200))
     log(f"prefill_bf16_dst: {out['prefill_bf16_dst']}")
     del srcs, dsts
     # four ranks on the prefill shape with rank 2 inactive (it contributes +0.0 and is not read)
@@ -805,6 +993,7 @@ def other_schedules(torch, ar, wl):
                                            stream=stream)), 50)
     b = w.R * w.n * 2 + w.R * w.n * 2
     out["slice_bcast_f16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    with_ceiling(out["slice_bcast_f16_dst"], pattern_ceiling(torch, stream, 4, 4, srcs, dsts, w.n * 2, 50))
     log(f"slice_bcast_f16_dst: {out['slice_bcast_f16_dst']}")
     del srcs, dsts
 
@@ -816,6 +1005,7 @@ def other_schedules(torch, ar, wl):
                                     stream=stream), 20)
     b = w.R * w.n * 4 + w.n * 4
     out["r8_hbm_fp32_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    with_ceiling(out["r8_hbm_fp32_src"], pattern_ceiling(torch, stream, 8, 1, [srcs32], [[dst]], w.n * 4, 10))
     log(f"r8_hbm_fp32_src: {out['r8_hbm_fp32_src']}")
     del srcs32
     pre = [wl.as_wire_typed(p, w.wire) for p in parts]
@@ -836,6 +1026,10 @@ def other_schedules(torch, ar, wl):
                                     ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
     ms_direct = timed(lambda: ar.ar_reduce(ctx, [dst], pinned, w.n, ar.AR_F32, w.wire,
                                            ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
+    # the allocation-free entry point: the same copy-engine pipeline staged in the
+    # library's 64 MiB static array (smaller chunks than the context's ring)
+    ms_static = timed(lambda: ar.ar_reduce_staged_static(ctx_copy, [dst], pinned, w.n, ar.AR_F32, w.wire,
+                                                         ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
     torch.cuda.synchronize()
     ar.ar_free(ctx_copy)
     pcie_bytes = w.R * w.n * 2
@@ -852,6 +1046,10 @@ def other_schedules(torch, ar, wl):
                                "adds_from_hbm_ms": round(out["r8_hbm_bf16_src"]["us"] / 1e3, 3)}
     out["host_direct_bf16"] = {"ms": round(ms_direct, 3), "pcie_GB/s": round(pcie_bytes / ms_direct / 1e6, 2),
                                "frac_of_h2d_copy": round(ms_copy / ms_direct, 3), "path": "kernel reads pinned memory"}
+    out["host_static_staging_bf16"] = {"ms": round(ms_static, 3), "pcie_GB/s": round(pcie_bytes / ms_static / 1e6, 2),
+                                       "frac_of_h2d_copy": round(ms_copy / ms_static, 3),
+                                       "path": "copy engine into the static 64 MiB array (ar_reduce_staged_static)"}
+    log(f"host_static_staging_bf16: {out['host_static_staging_bf16']}")
     log(f"host_staged_bf16: {out['host_staged_bf16']}")
     log(f"host_direct_bf16: {out['host_direct_bf16']}")
     # decode-sized host-staged calls (one hidden vector per rank): latency of each path

@@ -17,11 +17,15 @@
 //
 // The stream pointers are scalar parameters ahead of everything else, so the
 // dispatcher can preload the first ones into SGPRs, as it does for the
-// reduce's own streaming kernels.
+// reduce's own streaming kernels.  Workgroups can be renumbered with the
+// reduce's XCD placement map (runs of 2^lc workgroups per XCD), so that the
+// ceiling is taken with the same placement as the kernel it is compared with.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
+
+#include "ar_internal.h"
 
 namespace {
 
@@ -53,9 +57,12 @@ __device__ __forceinline__ void store(char *base, unsigned off, u32x4 v) {
 template <int R, int D, int SP>
 __global__ __launch_bounds__(kBlock) void k_pattern(unsigned tiles, char *d0, const char *s0, const char *s1,
                                                     const char *s2, const char *s3, const char *s4, const char *s5,
-                                                    const char *s6, const char *s7, char *d1, char *d2, char *d3) {
+                                                    const char *s6, const char *s7, char *d1, char *d2, char *d3,
+                                                    unsigned lc) {
     const unsigned lane = threadIdx.x & 63u;
-    const unsigned w = blockIdx.x * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const unsigned G = (tiles + kBlock / 64 - 1) / (kBlock / 64);
+    const unsigned w = mpp::xcd_virtual_block(blockIdx.x, G, lc) * (kBlock / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     if (w >= tiles) return;
     const size_t t = static_cast<size_t>(w) * kTileBytes;
     const char *s[kMaxR] = {s0, s1, s2, s3, s4, s5, s6, s7};
@@ -95,12 +102,14 @@ int pattern_index(int R, int D) {
 // Enqueue one pass of the (R, D) pattern over `bytes` of every stream on
 // `stream` (a hipStream_t; NULL = the null stream).  Every pointer is device
 // memory, 16-byte aligned, `bytes` long; `bytes` is a multiple of 2048 and at
-// most 2^31 tiles.  Returns 0 when enqueued, 1 for an unsupported or invalid
-// request (nothing enqueued), 4 for a HIP error.
+// most 2^31 tiles.  `run_bytes`: XCD placement runs of about this many bytes
+// of every stream (0 = the hardware's own placement).  Returns 0 when
+// enqueued, 1 for an unsupported or invalid request (nothing enqueued), 4 for
+// a HIP error.
 extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, int D, int store_policy,
                                                                          const void *const *srcs,
                                                                          void *const *dsts, size_t bytes,
-                                                                         void *stream) {
+                                                                         size_t run_bytes, void *stream) {
     const int p = pattern_index(R, D);
     if (p < 0 || store_policy < 0 || store_policy > 2 || srcs == nullptr || dsts == nullptr) return 1;
     if (bytes == 0 || bytes % kTileBytes != 0 || bytes / kTileBytes >= (size_t(1) << 31)) return 1;
@@ -117,7 +126,8 @@ extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, 
     unsigned tiles = static_cast<unsigned>(bytes / kTileBytes);
     const unsigned wpb = kBlock / 64;
     const unsigned grid = (tiles + wpb - 1) / wpb;
-    void *args[] = {&tiles, &d[0], &s[0], &s[1], &s[2], &s[3], &s[4], &s[5], &s[6], &s[7], &d[1], &d[2], &d[3]};
+    unsigned lc = mpp::xcd_map_lc(grid, size_t(wpb) * kTileBytes, run_bytes);
+    void *args[] = {&tiles, &d[0], &s[0], &s[1], &s[2], &s[3], &s[4], &s[5], &s[6], &s[7], &d[1], &d[2], &d[3], &lc};
     const hipError_t e = hipLaunchKernel(kPatterns[p][store_policy], dim3(grid), dim3(kBlock), args, 0,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : 4;
