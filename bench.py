@@ -162,6 +162,8 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/ HBM-traffic summary from two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, WRITE_SIZE) of --profile-pass")
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                   help="write profiles/counters_<workload>.md from the rocprofv3 --pmc runs of COUNTER_PASSES")
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for hardware-counter collection: a few reduce steps, then a "
                         "plain elementwise copy of known size used to calibrate the counters")
@@ -172,11 +174,13 @@ def parse():
 
 def main() -> int:
     args = parse()
-    if args.summarize_trace or args.summarize_pmc:
+    if args.summarize_trace or args.summarize_pmc or args.summarize_counters:
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, args.profile_workload)
         if args.summarize_pmc:
             summarize_pmc(*args.summarize_pmc, args.profile_workload)
+        if args.summarize_counters:
+            summarize_counters(args.summarize_counters, args.profile_workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the reduce is run with every "
@@ -442,11 +446,11 @@ def case_algo_bytes(case: dict) -> int:
     return active * case["n"] * case["src_bytes"] + case["n_dst"] * case["n"] * db + res_b
 
 
-TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py"
+TRACE_CMD = "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 /root/repo/bench.py"
 TRACE_PASS_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- "
-                  "python3 bench.py --profile-pass --profile-workload {wl}")
+                  "python3 /root/repo/bench.py --profile-pass --profile-workload {wl}")
 PMC_CMD = ("cd /tmp && rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {tag} -- "
-           "python3 bench.py --profile-pass{extra}")
+           "python3 /root/repo/bench.py --profile-pass{extra}")
 
 
 def _csv_rows(directory: str, suffix: str):
@@ -504,6 +508,47 @@ def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
                 host_b = case["R"] * case["n"] * case["src_bytes"]
                 lines += ["", f"The sources cross PCIe: {host_b} B read from pinned host memory per launch = "
                               f"{host_b / avg_us / 1e3:.1f} GB/s host-to-device."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
+
+
+# Further counter passes, each within one pass's hardware limits (at most 4 TCC,
+# 4 TCP, 2 TA, 2 TD, 8 SQ and 2 GRBM counters), for locating where a kernel's
+# time goes beyond its byte counts.
+COUNTER_PASSES = {
+    "l2": "TCC_HIT_sum TCC_MISS_sum TCC_REQ_sum",
+    "l2_mem": "TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_sum TCC_TAG_STALL_sum TCC_BUSY_sum",
+    "core": "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TA_TA_BUSY_sum TD_TD_BUSY_sum SQ_WAVE_CYCLES "
+            "SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE",
+}
+COUNTER_CMD = ("cd /tmp && rocprofv3 --pmc {counters} --output-format csv -d <dir> -o {tag} -- "
+               "python3 /root/repo/bench.py --profile-pass --profile-workload {wl}")
+
+
+def summarize_counters(dirs: list, wl: str) -> None:
+    """profiles/counters_<wl>.md: per-dispatch averages of the COUNTER_PASSES counters
+    for the reduce kernel of a profile pass (one directory per pass, in order)."""
+    case = PROFILE_CASES[wl]
+    match = is_reduce_kernel if wl == "prefill_bf16" else is_library_kernel
+    vals, names = {}, set()
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if match(r["Kernel_Name"]):
+                names.add(_short(r["Kernel_Name"]))
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise RuntimeError(f"no reduce-kernel dispatches in {dirs}")
+    out = os.path.join(ROOT, "profiles", f"counters_{wl}.md")
+    lines = [f"# Hardware counters of the reduce kernel: {case['what']}", ""]
+    for tag, counters in COUNTER_PASSES.items():
+        lines.append(f"- `{COUNTER_CMD.format(counters=counters, tag=tag, wl=wl)}`")
+    lines += ["", "Kernel " + ", ".join(f"`{k}`" for k in sorted(names)) +
+              f"; kernel source hash {kernel_source_hash()}.", "",
+              "| counter | per dispatch (mean) | dispatches |", "|---|---|---|"]
+    for c in sorted(vals):
+        v = vals[c]
+        lines.append(f"| {c} | {sum(v) / len(v):.1f} | {len(v)} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out)
@@ -570,9 +615,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, wl: str = "prefill_bf16") -> N
 
 
 def profile_pass(torch, ar, wl, args):
-    """Counter / trace pass: rotated reduces of one configuration (at least 12
-    launches), then 8 torch.neg launches that read and write CALIBRATION_BYTES
-    each (a plain copy-shaped kernel)."""
+    """Counter / trace pass: ~20 ms of fill kernels (clock warm-up), rotated reduces
+    of one configuration (at least 48 launches), then 8 torch.neg launches that
+    read and write CALIBRATION_BYTES each (a plain copy-shaped kernel)."""
     case = PROFILE_CASES[args.profile_workload]
     R, n = case["R"], case["n"]
     S = max(1, min(args.sets, case["sets"]))
@@ -622,7 +667,15 @@ def profile_pass(torch, ar, wl, args):
     torch.cuda.synchronize()
     ctx = ar.ar_init(0)
     stream = torch.cuda.current_stream()
-    launches = max(3 * S, 12)
+    # bring the GPU out of its idle clocks first (the first calls after idle run
+    # up to 25 % slower), with kernels that are not the reduce's: ~20 ms of fills
+    # of a 64 MiB buffer
+    scratch = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(200):
+        scratch.fill_(1)
+    torch.cuda.synchronize()
+    del scratch
+    launches = max(6 * S, 48)
     for k in range(launches):
         i = k % S
         if rows is not None:

@@ -152,12 +152,17 @@ typedef struct {
                                      renumbered so that each XCD streams runs of
                                      about this many elements of every source, the
                                      8 XCDs' runs side by side, round after round.
-                                     0 -> automatic (2^17 for R <= 4, none beyond);
+                                     0 -> automatic (for R <= 4: 2^17, or 2^18 in the
+                                     broadcast schedule; none beyond);
                                      a value below one workgroup's share (e.g. 1)
                                      -> no renumbering.  No effect on any result */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.
+ * Follows the "CUDA allreduce.cu" page's ggml_cuda_ar_pipeline_init: set-up
+ * either yields a usable handle or reports failure (that function returns
+ * nullptr so the caller falls back, and releases whatever it had created
+ * first); here the failure is a status code and nothing is left allocated.
  *   out  : receives the context (set to NULL on failure).
  *   cfg  : NULL for defaults (plus AR_* environment overrides).
  * Errors: AR_ERR_INVALID (out NULL, device index out of range, negative or
@@ -169,6 +174,13 @@ typedef struct {
 int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
 
 /* Enqueue one reduce.
+ * The operation is the one in this file's header, as the "CUDA
+ * allreduce.cu" page's ggml_cuda_ar_allreduce performs it between two ranks
+ * (the accepted element types F32 / F16 / BF16, a non-empty tensor, the
+ * wire-type narrowing of large F32 inputs) and the "Hexagon allreduce-ops.c"
+ * page's allreduce_thread_dma_1d for any rank count (fixed-order sum, each
+ * block written to every destination).  Where that page asserts on a bad
+ * argument, this call returns a status and enqueues nothing.
  *   dst       : array of n_dst pointers to buffers of n dst_type elements
  *               (n_dst = R for AR_MODE_RS_BCAST, else 1); device memory of
  *               the context's device.
@@ -202,7 +214,7 @@ int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg);
  *   AR_ERR_RUNTIME if a launch or copy cannot be enqueued.  Faults of
  *   enqueued work surface at the caller's next synchronisation. */
 int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
-              int dst_type, int wire_type, unsigned mode, void *hip_stream);
+              ar_dtype dst_type, ar_dtype wire_type, unsigned mode, void *hip_stream);
 
 /* For callers that cannot allocate device memory (code under graph-free
  * tight loops, harnesses that forbid hipMalloc): the host-staged reduce of
@@ -224,7 +236,7 @@ int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, siz
  * Errors: those of ar_reduce; another resolved mode -> AR_ERR_INVALID; under
  * stream capture -> AR_ERR_UNSUPPORTED. */
 int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
-                            int dst_type, int wire_type, unsigned mode, void *hip_stream);
+                            ar_dtype dst_type, ar_dtype wire_type, unsigned mode, void *hip_stream);
 
 /* Enqueue one reduce followed by a residual add: after the last rank,
  * res[i mod residual_len] is added in the destination type, element-wise
@@ -245,7 +257,7 @@ int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *sr
  * with a residual run on the register-staged kernels (stream_kernel 2 is
  * not used for them). */
 int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
-                  int dst_type, int wire_type, unsigned mode, const void *residual,
+                  ar_dtype dst_type, ar_dtype wire_type, unsigned mode, const void *residual,
                   size_t residual_len, void *hip_stream);
 
 /* Row-strided tensors ("Hexagon allreduce-ops.c" page, allreduce_thread_dma_2d:
@@ -280,16 +292,23 @@ typedef struct {
  * element.  Ownership and the remaining error codes are those of ar_reduce
  * and ar_reduce_add; cols > 2^30 -> AR_ERR_UNSUPPORTED. */
 int ar_reduce_rows(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R,
-                   const ar_rows *shape, int dst_type, int wire_type, unsigned mode,
+                   const ar_rows *shape, ar_dtype dst_type, ar_dtype wire_type, unsigned mode,
                    const void *residual, void *hip_stream);
 
 /* Drain the context's internal stream and release everything it owns.
  * NULL is accepted and returns AR_OK.  Work already enqueued by ar_reduce
  * on caller streams must be complete or ordered before any reuse of the
- * buffers, as usual; ar_free waits for the context's own copy stream. */
+ * buffers, as usual; ar_free waits for the context's own copy stream.
+ * Follows the "CUDA allreduce.cu" page's ggml_cuda_ar_pipeline_free, which
+ * returns at once for a null handle and synchronises its streams before it
+ * frees buffers and events. */
 int ar_free(ar_ctx *ctx);
 
-/* Static, human-readable name of a status code ("AR_OK", ...). */
+/* Static, human-readable name of a status code ("AR_OK", ...).  The codes
+ * follow the status style of the "Hexagon allreduce-ops.c" page's
+ * validate_allreduce / op_allreduce: invalid parameters, a valid request the
+ * implementation does not support (the caller falls back), not enough memory,
+ * and an internal (runtime) error are distinct results. */
 const char *ar_status_str(int status);
 
 /* ---------------------------------------------------------------------
@@ -322,19 +341,19 @@ typedef struct {
  * `srcs_on_host` != 0 tells AUTO that the sources are pinned host memory.
  * `cfg` NULL means defaults.  Returns an ar_status code. */
 int ar_plan_query(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
-                  size_t n, int dst_type, int wire_type, unsigned mode, int srcs_on_host,
+                  size_t n, ar_dtype dst_type, ar_dtype wire_type, unsigned mode, int srcs_on_host,
                   ar_plan *plan);
 
 /* The same for ar_reduce_rows (slice_start / slice_len stay 0: row-strided
  * calls are not cut into per-rank slices; chunk_elems is one row on the
  * device, or the rows of one host-staged copy chunk times cols). */
 int ar_plan_query_rows(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
-                       const ar_rows *shape, int dst_type, int wire_type, unsigned mode,
+                       const ar_rows *shape, ar_dtype dst_type, ar_dtype wire_type, unsigned mode,
                        const void *residual, int srcs_on_host, ar_plan *plan);
 
 /* The same for ar_reduce_add (residual checks included). */
 int ar_plan_query_add(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
-                      size_t n, int dst_type, int wire_type, unsigned mode,
+                      size_t n, ar_dtype dst_type, ar_dtype wire_type, unsigned mode,
                       const void *residual, size_t residual_len, int srcs_on_host,
                       ar_plan *plan);
 

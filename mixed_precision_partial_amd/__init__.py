@@ -200,10 +200,27 @@ def _check_span(xs, need: int, what: str) -> None:
             raise ValueError(f"{what}: {have} bytes from the tensor's data pointer where the call spans {need}")
 
 
+def _check_counts(dsts, srcs, mode: int, R: int | None = None) -> None:
+    """The library reads R source pointers and n_dst destination pointers (n_dst = R
+    for AR_MODE_RS_BCAST, else 1) from the arrays it is given: refuse lists shorter
+    than that before building them (ctypes arrays and raw addresses are passed
+    through as given, as in C).  Counts outside 2..AR_MAX_RANKS are left to the
+    library, which rejects them before reading any pointer."""
+    R = (len(srcs) if srcs is not None and not isinstance(srcs, ctypes.Array) else None) if R is None else R
+    if R is None or not 2 <= R <= AR_MAX_RANKS:
+        return
+    if srcs is not None and not isinstance(srcs, ctypes.Array) and len(srcs) < R:
+        raise ValueError(f"srcs has {len(srcs)} entries for R = {R}")
+    n_dst = R if (int(mode) & AR_MODE_MASK) == AR_MODE_RS_BCAST else 1
+    if dsts is not None and not isinstance(dsts, ctypes.Array) and len(dsts) < n_dst:
+        raise ValueError(f"dsts has {len(dsts)} entries; this mode writes {n_dst} destinations")
+
+
 def _flat_arrays(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: int, validate: bool):
     """ptr_array(dsts), ptr_array(srcs) of a 1-D call, checking each tensor on the
     way (one pass: the check costs little beyond the pointer conversion); returns
     the arrays and the element width of the destination type (0 when unchecked)."""
+    _check_counts(dsts, srcs, mode)
     dst_b = src_b = 0
     if validate and n > 0:
         dst_b = _TYPE_BYTES.get(dst_type, 0)
@@ -386,6 +403,7 @@ def ar_reduce_rows(ctx, dsts, srcs, rows: int, cols: int, src_stride: int, dst_s
     ValueError before the call if ``validate`` finds a tensor's storage too small)."""
     lib = load_library()
     R = len(srcs) if srcs is not None else 0
+    _check_counts(dsts, srcs, mode)
     if validate:
         _validate_rows(dsts, srcs, rows, cols, src_stride, dst_stride, dst_type, wire_type, mode, residual,
                        res_stride)
@@ -411,6 +429,7 @@ def ar_plan_query(dsts, srcs, n: int, dst_type: int = AR_F32, wire_type: int = A
     plan = ArPlan()
     cfg = _config(config)
     R = (len(srcs) if srcs is not None else 0) if R is None else R
+    _check_counts(dsts, srcs, mode, R)
     rc = lib.ar_plan_query(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
                            _ptr_array(srcs), R, int(n), int(dst_type), int(wire_type), int(mode),
                            int(bool(srcs_on_host)), ctypes.byref(plan))
@@ -424,6 +443,7 @@ def ar_plan_query_add(dsts, srcs, n: int, dst_type: int, wire_type: int, mode: i
     plan = ArPlan()
     cfg = _config(config)
     R = (len(srcs) if srcs is not None else 0) if R is None else R
+    _check_counts(dsts, srcs, mode, R)
     rc = lib.ar_plan_query_add(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
                                _ptr_array(srcs), R, int(n), int(dst_type), int(wire_type), int(mode),
                                _addr(residual), int(residual_len), int(bool(srcs_on_host)),
@@ -439,6 +459,7 @@ def ar_plan_query_rows(dsts, srcs, rows: int, cols: int, src_stride: int, dst_st
     plan = ArPlan()
     cfg = _config(config)
     R = (len(srcs) if srcs is not None else 0) if R is None else R
+    _check_counts(dsts, srcs, mode, R)
     shape = ArRows(int(rows), int(cols), int(src_stride), int(dst_stride), int(res_stride))
     rc = lib.ar_plan_query_rows(ctypes.byref(cfg) if cfg is not None else None, _ptr_array(dsts),
                                 _ptr_array(srcs), R, ctypes.byref(shape), int(dst_type), int(wire_type),

@@ -49,8 +49,9 @@ constexpr int kDefaultHostSlots = 3;
 constexpr int kMaxHostSlots = 64;
 // Workgroup placement over the XCDs (see xcd_virtual_block): each XCD
 // streams runs of this many elements of every source (512 KiB of a binary32
-// source, 256 KiB of a 16-bit one).
+// source, 256 KiB of a 16-bit one); twice that in the broadcast schedule.
 constexpr size_t kDefaultXcdRunElems = size_t(1) << 17;
+constexpr size_t kDefaultXcdRunElemsBcast = size_t(1) << 18;
 
 int elem_bytes(int t) { return t == AR_F32 ? 4 : 2; }
 bool valid_type(int t) { return t == AR_F32 || t == AR_F16 || t == AR_BF16; }
@@ -121,17 +122,20 @@ bool ranges_overlap(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
 
 size_t round_down(size_t x, size_t m) { return x / m * m; }
 
-// Placement run of a streaming launch: the configured value, else 2^17
-// elements of each source for up to four ranks and the hardware's own
-// placement beyond.  Measured on MI355X against the identity placement, same
-// machine each time, bit-identical outputs: prefill reduce 15.69 against
-// 15.90 us, prefill + element-wise residual 19.80 against 20.25 us, 4-rank
-// broadcast into fp16 destinations 43.55 against 46.33 us, bf16 partials into
-// a bf16 destination 8.68 against 8.78 us; but R = 8 fp32 partials
+// Placement run of a streaming launch: the configured value, else, for up to
+// four ranks, 2^17 elements of each source (2^18 in the broadcast schedule),
+// and the hardware's own placement beyond.  Measured on MI355X against the
+// identity placement, same machine each time, bit-identical outputs: prefill
+// reduce 15.69 against 15.90 us, prefill + element-wise residual 19.80
+// against 20.25 us, bf16 partials into a bf16 destination 8.68 against
+// 8.78 us (8.85 with 2^18), 4-rank broadcast into fp16 destinations 43.55
+// against 46.33 us (44.78 with 2^17; on another machine 43.61 against 44.82),
+// fp32 partials 86.3 against 87.2 us with 2^17; but R = 8 fp32 partials
 // [8192 x 8192] 373-387 against 360 us at every run length tried.
-size_t xcd_run_for(const Config &cfg, int R) {
+size_t xcd_run_for(const Config &cfg, int R, bool bcast) {
     if (cfg.xcd_run_elems) return cfg.xcd_run_elems;
-    return R <= 4 ? kDefaultXcdRunElems : 0;
+    if (R > 4) return 0;
+    return bcast ? kDefaultXcdRunElemsBcast : kDefaultXcdRunElems;
 }
 
 // The optional residual of ar_reduce_add: `len` elements of the destination
@@ -538,7 +542,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         for (int r = 0; r < R; ++r) longest = std::max(longest, static_cast<size_t>(plan.slice_len[r]));
         for (size_t p0 = 0; p0 < longest; p0 += mpp::kMaxLaunchElems) {
             mpp::KernelArgs a{};
-            a.xcd_run_elems = xcd_run_for(c->cfg, R);
+            a.xcd_run_elems = xcd_run_for(c->cfg, R, true);
             a.R = R;
             a.n_dst = R;
             a.store_nt = plan.store_nt;
@@ -563,7 +567,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
     for (size_t p0 = 0; p0 < n; p0 += mpp::kMaxLaunchElems) {
         const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);
         mpp::KernelArgs a{};
-        a.xcd_run_elems = xcd_run_for(c->cfg, R);
+        a.xcd_run_elems = xcd_run_for(c->cfg, R, false);
         a.R = R;
         a.n_dst = 1;
         a.n = len;
@@ -605,7 +609,7 @@ int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const
     for (size_t r0 = 0; r0 < rw.rows; r0 += kMaxRows) {
         const size_t nr = std::min(kMaxRows, rw.rows - r0);
         mpp::KernelArgs a{};
-        a.xcd_run_elems = xcd_run_for(c->cfg, R);
+        a.xcd_run_elems = xcd_run_for(c->cfg, R, plan.mode == AR_MODE_RS_BCAST);
         a.R = R;
         a.n_dst = plan.n_dst;
         a.n = nr * rw.cols;
@@ -710,7 +714,7 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         if (hipStreamWaitEvent(stream, c->ev_h2d[slot], 0) != hipSuccess) return AR_ERR_RUNTIME;
 
         mpp::KernelArgs a{};
-        a.xcd_run_elems = xcd_run_for(c->cfg, R);
+        a.xcd_run_elems = xcd_run_for(c->cfg, R, false);
         a.R = R;
         a.n_dst = 1;
         a.n = len;
@@ -729,15 +733,18 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
 }
 
 // HOST_STAGED for row-strided sources: the copy engine moves chunks of rows
-// with 2-D copies (row pitch = the source stride, packed into HBM scratch at
-// pitch cols), then the add kernel reads the packed rows and writes the
-// strided destination rows -- the same slot / event ring as the 1-D form.
+// with 2-D copies (row pitch = the source stride), packing them into HBM
+// scratch at a pitch of cols elements rounded up to 16 bytes (the kernels
+// read every row start with 16-byte loads), then the add kernel reads the
+// packed rows and writes the strided destination rows -- the same slot /
+// event ring as the 1-D form.
 int run_host_staged_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R,
                          const Rows &rw, int wire_type, const Residual &res, hipStream_t stream) {
     const size_t sb = static_cast<size_t>(plan.src_bytes);
     const size_t chunk_rows = plan.chunk_elems / rw.cols;
     const size_t K = static_cast<size_t>(c->cfg.host_slots);
-    const size_t rank_stride = chunk_rows * rw.cols * sb;
+    const size_t pitch_bytes = (rw.cols * sb + 15) / 16 * 16;   // packed row pitch
+    const size_t rank_stride = chunk_rows * pitch_bytes;
     const size_t slot_stride = rank_stride * static_cast<size_t>(R);
     if (int rc = ensure_scratch(c, slot_stride * K)) return rc;
 
@@ -756,7 +763,7 @@ int run_host_staged_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const
         for (int r = 0; r < R; ++r) {
             packed[r] = nullptr;
             if (srcs[r] == nullptr) continue;   // inactive rank: nothing crosses PCIe
-            if (hipMemcpy2DAsync(slot_base + r * rank_stride, rw.cols * sb,
+            if (hipMemcpy2DAsync(slot_base + r * rank_stride, pitch_bytes,
                                  static_cast<const char *>(srcs[r]) + r0 * rw.src_stride * sb, rw.src_stride * sb,
                                  rw.cols * sb, nr, hipMemcpyHostToDevice, c->copy_stream) != hipSuccess) {
                 return AR_ERR_RUNTIME;
@@ -768,7 +775,7 @@ int run_host_staged_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const
 
         Rows part = rw;
         part.rows = nr;
-        part.src_stride = rw.cols;
+        part.src_stride = pitch_bytes / sb;
         void *dst_part[AR_MAX_RANKS];
         for (int d = 0; d < plan.n_dst; ++d) {
             dst_part[d] = static_cast<char *>(dst[d]) + r0 * rw.dst_stride * static_cast<size_t>(plan.dst_bytes);
@@ -800,14 +807,14 @@ AR_API const char *ar_status_str(int status) {
 }
 
 AR_API int ar_plan_query(const ar_config *cfg, void *const *dst, const void *const *srcs, int R, size_t n,
-                         int dst_type, int wire_type, unsigned mode, int srcs_on_host, ar_plan *plan) {
+                         ar_dtype dst_type, ar_dtype wire_type, unsigned mode, int srcs_on_host, ar_plan *plan) {
     Config c;
     if (int rc = resolve_config(cfg, &c)) return rc;
     return validate_and_plan(c, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, srcs_on_host != 0, plan);
 }
 
 AR_API int ar_plan_query_add(const ar_config *cfg, void *const *dst, const void *const *srcs, int R, size_t n,
-                             int dst_type, int wire_type, unsigned mode, const void *residual, size_t residual_len,
+                             ar_dtype dst_type, ar_dtype wire_type, unsigned mode, const void *residual, size_t residual_len,
                              int srcs_on_host, ar_plan *plan) {
     Config c;
     if (int rc = resolve_config(cfg, &c)) return rc;
@@ -991,18 +998,18 @@ int reduce_impl(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, s
 
 }  // namespace
 
-AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
-                     int wire_type, unsigned mode, void *hip_stream) {
+AR_API int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, ar_dtype dst_type,
+                     ar_dtype wire_type, unsigned mode, void *hip_stream) {
     return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, nullptr, hip_stream);
 }
 
 AR_API int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
-                                   int dst_type, int wire_type, unsigned mode, void *hip_stream) {
+                                   ar_dtype dst_type, ar_dtype wire_type, unsigned mode, void *hip_stream) {
     return reduce_impl(ctx, dst, srcs, R, n, dst_type, wire_type, mode, Residual{}, nullptr, hip_stream, true);
 }
 
-AR_API int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, int dst_type,
-                         int wire_type, unsigned mode, const void *residual, size_t residual_len, void *hip_stream) {
+AR_API int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n, ar_dtype dst_type,
+                         ar_dtype wire_type, unsigned mode, const void *residual, size_t residual_len, void *hip_stream) {
     if (residual == nullptr) return AR_ERR_INVALID;
     Residual res;
     res.ptr = residual;
@@ -1033,7 +1040,7 @@ bool rows_of(const ar_rows *shape, Rows *rw, size_t *n) {
 }  // namespace
 
 AR_API int ar_reduce_rows(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, const ar_rows *shape,
-                          int dst_type, int wire_type, unsigned mode, const void *residual, void *hip_stream) {
+                          ar_dtype dst_type, ar_dtype wire_type, unsigned mode, const void *residual, void *hip_stream) {
     if (ctx == nullptr || shape == nullptr) return AR_ERR_INVALID;
     Rows rw;
     size_t n = 0;
@@ -1045,7 +1052,7 @@ AR_API int ar_reduce_rows(ar_ctx *ctx, void *const *dst, const void *const *srcs
 }
 
 AR_API int ar_plan_query_rows(const ar_config *cfg, void *const *dst, const void *const *srcs, int R,
-                              const ar_rows *shape, int dst_type, int wire_type, unsigned mode, const void *residual,
+                              const ar_rows *shape, ar_dtype dst_type, ar_dtype wire_type, unsigned mode, const void *residual,
                               int srcs_on_host, ar_plan *plan) {
     Config c;
     if (int rc = resolve_config(cfg, &c)) return rc;

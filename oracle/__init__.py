@@ -153,7 +153,7 @@ def add_f32(a: np.ndarray, b: np.ndarray, lib=None) -> np.ndarray:
 # --- the reduce ------------------------------------------------------------
 
 def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
-           lib=None, dst_type: int = F32, residual=None) -> np.ndarray:
+           lib=None, dst_type: int = F32, residual=None, n: int | None = None) -> np.ndarray:
     """Reference result of the partial-sum reduce.
 
     ``srcs``: sequence of R equally sized 1-D arrays.  float32 arrays are the
@@ -164,6 +164,8 @@ def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
     ``residual``: None, or a 1-D array of the destination type (float32, or
     uint16 bit patterns for a narrow destination) whose length is n (added
     element-wise) or divides n (one row added to every row).
+    ``n``: the element count; needed only when every rank is inactive (the
+    sources then carry no length), else it must match them.
     Returns an ``(n_dst, n)`` array of the destination type (float32, or
     uint16 bit patterns); every row holds the same bits.
     """
@@ -171,11 +173,13 @@ def reduce(srcs, wire_type: int, n_dst: int = 1, src_type: int | None = None,
     srcs = [None if s is None else np.ascontiguousarray(s) for s in srcs]
     R = len(srcs)
     live = [s for s in srcs if s is not None]
-    if not live:
-        raise ValueError("at least one active source is needed to know n")
-    n = live[0].size
+    if not live and n is None:
+        raise ValueError("every rank is inactive: pass n")
+    if live and n is not None and int(n) != live[0].size:
+        raise ValueError("n differs from the sources' length")
+    n = int(n) if n is not None else live[0].size
     if src_type is None:
-        src_type = F32 if live[0].dtype == np.float32 else wire_type
+        src_type = wire_type if live and live[0].dtype == np.uint16 else F32
     want = np.float32 if src_type == F32 else np.uint16
     for s in live:
         if s.size != n:

@@ -218,6 +218,28 @@ def check_inactive_ranks(lib, seed: int = 31) -> None:
                     want = fp64_route_fold([lib_wire_value(z, wire) for z in zeros])
                 assert_same_f32(got[0], want, f"inactive R={R} wire={wire} active={active.tolist()}")
                 assert np.array_equal(got[0].view(np.uint32), got[1].view(np.uint32))
+    # every rank inactive, through the wrapper with an explicit n: +0.0 everywhere
+    # (a zeroed shard, never -0), in every destination; with a residual the result
+    # is 0 + residual (so -0 in the residual becomes +0); the same in 16-bit types
+    n = 777
+    for wire in (F32, BF16, F16):
+        got = oracle.reduce([None] * 3, wire, n_dst=2, lib=lib, n=n)
+        assert got.shape == (2, n) and not got.view(np.uint32).any(), f"all inactive, wire {wire}"
+    res = workloads.random_partials(961, 0, 1, n, dist="wide")[0]
+    res[:g.size] = g
+    got = oracle.reduce([None, None], BF16, lib=lib, residual=res, n=n)[0]
+    with np.errstate(all="ignore"):
+        want = (np.float64(0.0) + res.astype(np.float64)).astype(np.float32)
+    assert_same_f32(got, want, "all inactive + residual")
+    for w in (F16, BF16):
+        got16 = oracle.reduce([None, None, None, None], w, src_type=w, dst_type=w, lib=lib, n=n)[0]
+        assert got16.dtype == np.uint16 and not got16.any(), f"all inactive narrow {w}"
+    try:
+        oracle.reduce([None, None], F32, lib=lib)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("all-inactive call without n must be refused")
 
 
 # --- conversions -------------------------------------------------------------

@@ -532,3 +532,33 @@ def test_xcd_placement_map_is_a_permutation(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     out = subprocess.run([exe], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr
+
+
+def test_binding_refuses_short_pointer_lists():
+    """The library reads R destination pointers in the broadcast schedule (and R
+    source pointers always): the binding refuses shorter lists before the call,
+    instead of letting the library read past the end of the array it built."""
+    srcs = [0x10000, 0x20000, 0x30000, 0x40000]
+    dsts = [0x50000, 0x60000]
+    bcast = ar.AR_MODE_RS_BCAST
+    with pytest.raises(ValueError, match="destinations"):
+        ar.ar_plan_query(dsts, srcs, 4096, ar.AR_F32, ar.AR_F16, bcast)
+    with pytest.raises(ValueError, match="destinations"):
+        ar.ar_plan_query_add(dsts, srcs, 4096, ar.AR_F32, ar.AR_F16, bcast, 0x70000, 4096)
+    with pytest.raises(ValueError, match="destinations"):
+        ar.ar_plan_query_rows(dsts, srcs, 4, 1024, 1024, 1024, ar.AR_F32, ar.AR_F16, bcast)
+    with pytest.raises(ValueError, match="destinations"):
+        ar.ar_reduce(None, dsts, srcs, 4096, ar.AR_F32, ar.AR_F16, bcast, validate=False)
+    with pytest.raises(ValueError, match="destinations"):
+        ar.ar_reduce_rows(None, dsts, srcs, 4, 1024, 1024, 1024, ar.AR_F32, ar.AR_F16, bcast, validate=False)
+    with pytest.raises(ValueError, match="srcs has"):
+        ar.ar_plan_query([0x50000], srcs[:2], 4096, ar.AR_F32, ar.AR_F16, ar.AR_MODE_CHUNKED, R=4)
+    # enough destinations: the library plans the call (made-up addresses, never dereferenced)
+    rc, plan = ar.ar_plan_query(dsts + [0x80000, 0x90000], srcs, 4096, ar.AR_F32, ar.AR_F16, bcast)
+    assert rc == ar.AR_OK and plan.n_dst == 4
+    # one destination is enough outside the broadcast schedule
+    rc, _ = ar.ar_plan_query([0x50000], srcs, 4096, ar.AR_F32, ar.AR_F16, ar.AR_MODE_CHUNKED)
+    assert rc == ar.AR_OK
+    # ctypes arrays pass through as given, as in C; out-of-range R is the library's to reject
+    rc, _ = ar.ar_plan_query([0x50000], srcs * 5, 4096, ar.AR_F32, ar.AR_F16, bcast)
+    assert rc == ar.AR_ERR_INVALID

@@ -660,11 +660,8 @@ def test_inactive_ranks(kctx, kname, mode_name):
                     ar.ar_reduce(c, [d.ptr() for d in dsts], [0 if t is None else t for t in ts], n,
                                  ar.AR_F32, wire, mode | flags)
                     torch.cuda.synchronize()
-                    if active.any():
-                        want = oracle.reduce([s if a else None for s, a in zip(used, active)], wire,
-                                             src_type=wire if src_wire else None)[0]
-                    else:
-                        want = np.zeros(n, dtype=np.float32)   # +0.0 everywhere
+                    want = oracle.reduce([s if a else None for s, a in zip(used, active)], wire,
+                                         src_type=wire if src_wire else None, n=n)[0]
                     for d in dsts:
                         assert_bits_equal(d.result(), want, what)
 

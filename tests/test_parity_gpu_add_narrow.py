@@ -79,13 +79,7 @@ def run_and_check(ctx, srcs, wire, mode, what, dst_type=ar.AR_F32, src_wire=Fals
     torch.cuda.synchronize()
     used = [s if a else None for s, a in zip(srcs, active)]
     src_type = wire if (src_wire or narrow) and wire != ar.AR_F32 else None
-    if any(active):
-        want = oracle.reduce(used, wire, src_type=src_type, dst_type=dst_type, residual=residual)[0]
-    else:
-        # no active rank: the fold is +0; the oracle needs one array to know n
-        zero = np.zeros(n, dtype=np.uint16 if src_type is not None else np.float32)
-        want = oracle.reduce([zero] + [None] * (R - 1), wire, src_type=src_type, dst_type=dst_type,
-                             residual=residual)[0]
+    want = oracle.reduce(used, wire, src_type=src_type, dst_type=dst_type, residual=residual, n=n)[0]
     for d, g in enumerate(dsts):
         got = g.result()
         if narrow:

@@ -116,9 +116,7 @@ def run_case(c: dict) -> None:
         ar.ar_free(ctx)
     src_type = wire if (c["src_wire"] or narrow) and wire != ar.AR_F32 else None
     used = [s if a else None for s, a in zip(srcs, active)]
-    if not any(active):
-        used[0] = np.zeros(n, dtype=np.uint16 if src_type is not None else np.float32)
-    want = oracle.reduce(used, wire, src_type=src_type, dst_type=dst_type, residual=residual)[0]
+    want = oracle.reduce(used, wire, src_type=src_type, dst_type=dst_type, residual=residual, n=n)[0]
     if c["in_place"]:
         assert_bits_equal(ts[0].cpu().numpy(), want, what + " (in place)")
         return
