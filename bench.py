@@ -162,6 +162,10 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/ HBM-traffic summary from two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, WRITE_SIZE) of --profile-pass")
+    p.add_argument("--timing-study", action="store_true",
+                   help="instead of the benchmark: how the timing method changes a 20-step figure of the prefill "
+                        "reduce (default events vs fence-free events, with and without a lead-in call, the cost "
+                        "of an empty event interval, and the first steps after the GPU idled); one JSON line")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="write profiles/counters_<workload>.md from the rocprofv3 --pmc runs of COUNTER_PASSES")
     p.add_argument("--profile-pass", action="store_true",
@@ -198,6 +202,8 @@ def main() -> int:
     ar.load_library()   # fails loudly when the HIP library was not built
     if args.profile_pass:
         return profile_pass(torch, ar, wl, args)
+    if args.timing_study:
+        return timing_study(torch, ar, wl, args)
     w = wl.WORKLOADS["prefill_bf16"]
     R, n = w.R, w.n
     S = max(1, args.sets)
@@ -702,6 +708,63 @@ def profile_pass(torch, ar, wl, args):
 CEILING_LIB = os.path.join(ROOT, "mixed_precision_partial_amd", "libmpp_ceiling.so")
 
 
+def timing_study(torch, ar, wl, args, reps: int = 6) -> int:
+    """The 20-step prefill figure under each timing method, interleaved rep by rep
+    on the same rotated buffers, plus what an event costs on its own and what an
+    idle GPU costs the first steps.  Prints one JSON line."""
+    w = wl.WORKLOADS["prefill_bf16"]
+    n, S = w.n, max(1, args.sets)
+    src = [[torch.from_numpy(p).cuda() for p in wl.partials(w, s)] for s in range(S)]
+    dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(S)]
+    ctx = ar.ar_init(0)
+    stream = torch.cuda.current_stream()
+
+    def step(k):
+        ar.ar_reduce(ctx, [dst[k % S]], src[k % S], n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED, stream=stream)
+
+    def block(K, lead, fenced):
+        torch.cuda.synchronize()
+        for k in range(lead):
+            step(k)
+        if fenced:   # torch's events: default HIP events (system-scope fence on record)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        else:
+            a, b = HipEvent(), HipEvent()
+        a.record(stream)
+        for k in range(K):
+            step(lead + k)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return (a.elapsed_time(b) if fenced else a.elapsed_ms(b)) * 1e3 / max(K, 1)
+
+    for k in range(200):
+        step(k)
+    methods = {"default_events_no_lead_in": (0, True), "default_events_lead_in": (1, True),
+               "fence_free_events_no_lead_in": (0, False), "fence_free_events_lead_in": (1, False)}
+    res = {m: [] for m in methods}
+    for _ in range(reps):
+        for m, (lead, fenced) in methods.items():
+            res[m].append(block(args.steps, lead, fenced))
+    out = {"metric": "prefill reduce us/step by timing method", "steps": args.steps, "reps": reps,
+           "k20_us_per_step": {m: {"median": round(float(np.median(v)), 3), "min": round(min(v), 3),
+                                   "max": round(max(v), 3)} for m, v in res.items()},
+           "k2000_fence_free_lead_in_us": round(block(2000, 1, False), 3),
+           "empty_interval_us": {"default_events": round(float(np.median([block(0, 0, True) for _ in range(5)])), 2),
+                                 "fence_free_events": round(float(np.median([block(0, 0, False) for _ in range(5)])), 2)}}
+    idle = {}
+    for sec in (0.2, 1.0):
+        torch.cuda.synchronize()
+        time.sleep(sec)
+        first = block(args.steps, 1, False)
+        second = block(args.steps, 1, False)
+        idle[f"after_{sec}s_idle"] = {"first_block_us": round(first, 3), "second_block_us": round(second, 3)}
+    out["idle_then_20_steps"] = idle
+    torch.cuda.synchronize()
+    ar.ar_free(ctx)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def ceiling_lib():
     import ctypes
 
@@ -709,7 +772,7 @@ def ceiling_lib():
         raise RuntimeError(f"{CEILING_LIB} is missing: build with `python -m mixed_precision_partial_amd.build`")
     lib = ctypes.CDLL(CEILING_LIB)
     vp = ctypes.c_void_p
-    lib.mpp_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
+    lib.mpp_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), ctypes.c_size_t, ctypes.c_size_t, vp]
     lib.mpp_ceiling_launch.restype = ctypes.c_int
     return lib
@@ -717,8 +780,9 @@ def ceiling_lib():
 
 def pattern_ceiling(torch, stream, R, D, src_sets, dst_sets, nbytes, reps):
     """Best GB/s (bytes moved) of the ceiling kernel with the (R reads, D writes)
-    pattern over the given rotated tensors, `nbytes` per stream: every store
-    policy, with and without the XCD runs."""
+    pattern over the given rotated tensors, `nbytes` per stream: 256- and
+    64-thread workgroups, every store policy, without and with XCD runs of
+    512 KiB and 1 MiB."""
     import ctypes
 
     lib = ceiling_lib()
@@ -727,13 +791,14 @@ def pattern_ceiling(torch, stream, R, D, src_sets, dst_sets, nbytes, reps):
     arrays = [((vp * R)(*[t.data_ptr() for t in srcs]), (vp * D)(*[t.data_ptr() for t in dsts]))
               for srcs, dsts in zip(src_sets, dst_sets)]
     best = 0.0
-    for sp in (0, 1, 2):
-        for run in (0, 512 << 10):
-            def fn(k, sp=sp, run=run):
-                a, b = arrays[k % len(arrays)]
-                if lib.mpp_ceiling_launch(R, D, sp, a, b, nbytes, run, sh) != 0:
-                    raise RuntimeError("ceiling kernel launch failed")
-            best = max(best, (R + D) * nbytes / timed_us(torch, stream, fn, reps) / 1e3)
+    for block in (256, 64):
+        for sp in (0, 1, 2):
+            for run in (0, 512 << 10, 1 << 20):
+                def fn(k, sp=sp, run=run, block=block):
+                    a, b = arrays[k % len(arrays)]
+                    if lib.mpp_ceiling_launch(R, D, sp, block, a, b, nbytes, run, sh) != 0:
+                        raise RuntimeError("ceiling kernel launch failed")
+                best = max(best, (R + D) * nbytes / timed_us(torch, stream, fn, reps) / 1e3)
     return round(best, 1)
 
 
@@ -757,7 +822,7 @@ def ceilings(torch, stream, dev_src, dev_dst, n, sets, reps=300):
             for run, run_name in ((0, "hw"), (512 << 10, "xcd512k")):
                 def fn(k, R=R, sp=sp, run=run):
                     src, dst = arrays[k % sets]
-                    rc = lib.mpp_ceiling_launch(R, 1, sp, src, dst, n * 4, run, sh)
+                    rc = lib.mpp_ceiling_launch(R, 1, sp, 256, src, dst, n * 4, run, sh)
                     if rc != 0:
                         raise RuntimeError(f"ceiling kernel launch failed ({rc})")
                 us = timed_us(torch, stream, fn, reps)

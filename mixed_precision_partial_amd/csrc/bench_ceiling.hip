@@ -7,8 +7,9 @@
 // integer add across the R loaded words, which keeps every loaded byte live.
 // The layout and launch shape are the reduce's binary32 wave tile: one wave
 // covers 2 KiB of every stream as two 1 KiB instructions (lane l at byte
-// 16 l and 1024 + 16 l), one tile per wave, 256-thread workgroups, a grid
-// sized to the work.  Loads are non-temporal; stores follow SP (0 write-back,
+// 16 l and 1024 + 16 l), one tile per wave, 256- or 64-thread workgroups
+// (the reduce's register- and LDS-staged families use both), a grid sized to
+// the work.  Loads are non-temporal; stores follow SP (0 write-back,
 // 1 non-temporal, 2 device-scope write-through).  R = 1, D = 1 is the plain
 // 16-byte copy kernel; R = 2, D = 1 the two-read / one-write stream of the
 // prefill reduce; R = 4, D = 4 the slice + broadcast pattern; R = 8, D = 1 the
@@ -32,7 +33,6 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 256;
 constexpr unsigned kTileBytes = 2048;   // per stream per wave
 constexpr int kMaxR = 8;
 constexpr int kMaxD = 4;
@@ -54,14 +54,14 @@ __device__ __forceinline__ void store(char *base, unsigned off, u32x4 v) {
     }
 }
 
-template <int R, int D, int SP>
-__global__ __launch_bounds__(kBlock) void k_pattern(unsigned tiles, char *d0, const char *s0, const char *s1,
-                                                    const char *s2, const char *s3, const char *s4, const char *s5,
-                                                    const char *s6, const char *s7, char *d1, char *d2, char *d3,
-                                                    unsigned lc) {
+template <int R, int D, int SP, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_pattern(unsigned tiles, char *d0, const char *s0, const char *s1,
+                                                   const char *s2, const char *s3, const char *s4, const char *s5,
+                                                   const char *s6, const char *s7, char *d1, char *d2, char *d3,
+                                                   unsigned lc) {
     const unsigned lane = threadIdx.x & 63u;
-    const unsigned G = (tiles + kBlock / 64 - 1) / (kBlock / 64);
-    const unsigned w = mpp::xcd_virtual_block(blockIdx.x, G, lc) * (kBlock / 64) +
+    const unsigned G = (tiles + BLOCK / 64 - 1) / (BLOCK / 64);
+    const unsigned w = mpp::xcd_virtual_block(blockIdx.x, G, lc) * (BLOCK / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     if (w >= tiles) return;
     const size_t t = static_cast<size_t>(w) * kTileBytes;
@@ -82,11 +82,14 @@ __global__ __launch_bounds__(kBlock) void k_pattern(unsigned tiles, char *d0, co
     }
 }
 
-// Instances: [pattern][store policy]; patterns (R, D) = (1,1), (2,1), (4,4), (8,1).
-#define MPP_CEIL_ROW(R, D) \
-    {reinterpret_cast<const void *>(&k_pattern<R, D, 0>), reinterpret_cast<const void *>(&k_pattern<R, D, 1>), \
-     reinterpret_cast<const void *>(&k_pattern<R, D, 2>)}
-const void *const kPatterns[4][3] = {MPP_CEIL_ROW(1, 1), MPP_CEIL_ROW(2, 1), MPP_CEIL_ROW(4, 4), MPP_CEIL_ROW(8, 1)};
+// Instances: [workgroup size: 256, 64][pattern][store policy]; patterns (R, D) =
+// (1,1), (2,1), (4,4), (8,1).
+#define MPP_CEIL_ROW(R, D, B) \
+    {reinterpret_cast<const void *>(&k_pattern<R, D, 0, B>), reinterpret_cast<const void *>(&k_pattern<R, D, 1, B>), \
+     reinterpret_cast<const void *>(&k_pattern<R, D, 2, B>)}
+#define MPP_CEIL_TABLE(B) {MPP_CEIL_ROW(1, 1, B), MPP_CEIL_ROW(2, 1, B), MPP_CEIL_ROW(4, 4, B), MPP_CEIL_ROW(8, 1, B)}
+const void *const kPatterns[2][4][3] = {MPP_CEIL_TABLE(256), MPP_CEIL_TABLE(64)};
+#undef MPP_CEIL_TABLE
 #undef MPP_CEIL_ROW
 
 int pattern_index(int R, int D) {
@@ -102,16 +105,17 @@ int pattern_index(int R, int D) {
 // Enqueue one pass of the (R, D) pattern over `bytes` of every stream on
 // `stream` (a hipStream_t; NULL = the null stream).  Every pointer is device
 // memory, 16-byte aligned, `bytes` long; `bytes` is a multiple of 2048 and at
-// most 2^31 tiles.  `run_bytes`: XCD placement runs of about this many bytes
-// of every stream (0 = the hardware's own placement).  Returns 0 when
-// enqueued, 1 for an unsupported or invalid request (nothing enqueued), 4 for
-// a HIP error.
-extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, int D, int store_policy,
+// most 2^31 tiles.  `block`: 256 or 64 threads per workgroup.  `run_bytes`:
+// XCD placement runs of about this many bytes of every stream (0 = the
+// hardware's own placement).  Returns 0 when enqueued, 1 for an unsupported
+// or invalid request (nothing enqueued), 4 for a HIP error.
+extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, int D, int store_policy, int block,
                                                                          const void *const *srcs,
                                                                          void *const *dsts, size_t bytes,
                                                                          size_t run_bytes, void *stream) {
     const int p = pattern_index(R, D);
     if (p < 0 || store_policy < 0 || store_policy > 2 || srcs == nullptr || dsts == nullptr) return 1;
+    if (block != 256 && block != 64) return 1;
     if (bytes == 0 || bytes % kTileBytes != 0 || bytes / kTileBytes >= (size_t(1) << 31)) return 1;
     const char *s[kMaxR] = {};
     char *d[kMaxD] = {};
@@ -124,11 +128,11 @@ extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, 
         d[q] = static_cast<char *>(dsts[q]);
     }
     unsigned tiles = static_cast<unsigned>(bytes / kTileBytes);
-    const unsigned wpb = kBlock / 64;
+    const unsigned wpb = static_cast<unsigned>(block) / 64;
     const unsigned grid = (tiles + wpb - 1) / wpb;
     unsigned lc = mpp::xcd_map_lc(grid, size_t(wpb) * kTileBytes, run_bytes);
     void *args[] = {&tiles, &d[0], &s[0], &s[1], &s[2], &s[3], &s[4], &s[5], &s[6], &s[7], &d[1], &d[2], &d[3], &lc};
-    const hipError_t e = hipLaunchKernel(kPatterns[p][store_policy], dim3(grid), dim3(kBlock), args, 0,
-                                         static_cast<hipStream_t>(stream));
+    const hipError_t e = hipLaunchKernel(kPatterns[block == 64 ? 1 : 0][p][store_policy], dim3(grid), dim3(block),
+                                         args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : 4;
 }
