@@ -1052,6 +1052,12 @@ def other_schedules(torch, ar, wl):
             fn(i)
         return call
 
+    # the same reduce with an fp32 wire: the difference to the headline is the narrowing's cost
+    ms = timed(rot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, ar.AR_F32, ar.AR_MODE_CHUNKED,
+                                          stream=stream)), 200)
+    b = w.R * w.n * 4 + w.n * 4
+    out["prefill_f32_wire"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    log(f"prefill_f32_wire: {out['prefill_f32_wire']}")
     ms = timed(rot(lambda i: ar.ar_reduce_add(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
                                               ress[i], w.n, stream=stream)), 200)
     b = w.R * w.n * 4 + w.n * 4 + w.n * 4
