@@ -376,9 +376,9 @@ def main() -> int:
 
 
 CALIBRATION_BYTES = 64 << 20   # read and written once per calibration launch
-# the prefill reduce's kernel instance: register-staged, bf16 wire, fp32 sources,
-# fp32 destination, rank bucket 2, every rank active, no residual, cached stores
-REDUCE_KERNEL = "k_stream_reg<Cfg<2, false, false, 2, false, false>>"
+# the prefill reduce's kernel instance: the two-rank contiguous kernel, bf16 wire
+# (two fp32 sources, one fp32 destination, no residual)
+REDUCE_KERNEL = "k_pair<2>"
 
 
 def _plain_name(name: str) -> str:
@@ -392,7 +392,7 @@ def is_reduce_kernel(name: str) -> bool:
 def is_library_kernel(name: str) -> bool:
     """Any kernel of the reduce library (every streaming and single-shot instance)."""
     plain = _plain_name(name)
-    return "k_stream_" in plain or "k_single_shot" in plain
+    return "k_stream_" in plain or "k_single_shot" in plain or "k_pair<" in plain
 
 
 CALIBRATION_KERNEL = "neg_kernel"   # torch.neg, the calibration copy (other elementwise kernels may run)

@@ -82,6 +82,22 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 }  // namespace
 
+hipError_t launch_pair(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
+                       hipStream_t stream) {
+    if (wire < AR_F32 || wire > AR_BF16 || n == 0 || n > kMaxLaunchElems) return hipErrorInvalidValue;
+    unsigned tiles = static_cast<unsigned>(n / kWaveTile);
+    unsigned rem = static_cast<unsigned>(n % kWaveTile);
+    const unsigned waves = tiles + (rem != 0 ? 1u : 0u);
+    const unsigned wpb = kPairBlock / kWave;
+    const unsigned grid = (waves + wpb - 1) / wpb;
+    unsigned lc = xcd_map_lc(grid, static_cast<size_t>(wpb) * kWaveTile, run_elems);
+    float *d = static_cast<float *>(dst);
+    const float *a = static_cast<const float *>(src0);
+    const float *b = static_cast<const float *>(src1);
+    void *args[] = {&tiles, &rem, &d, &a, &b, &lc};
+    return hipLaunchKernel(kPair[wire], dim3(grid), dim3(kPairBlock), args, 0, stream);
+}
+
 hipError_t static_scratch(int device, void **out) {
     static std::mutex mu;
     static void *addr[kMaxStaticScratchDevices] = {};

@@ -16,9 +16,11 @@
 // eight-rank reduce.  A narrow-destination pattern is the same kernel at the
 // 16-bit byte counts (the data are bits either way).
 //
-// The stream pointers are scalar parameters ahead of everything else, so the
-// dispatcher can preload the first ones into SGPRs, as it does for the
-// reduce's own streaming kernels.  Workgroups can be renumbered with the
+// The tile count, the placement exponent and the stream pointers are scalar
+// parameters in that order, so the dispatcher preloads everything a wave of
+// the one- and two-source patterns needs into SGPRs (eight dwords), as it
+// does for the reduce's own streaming kernels: no wave waits on an argument
+// load before its first address.  Workgroups can be renumbered with the
 // reduce's XCD placement map (runs of 2^lc workgroups per XCD), so that the
 // ceiling is taken with the same placement as the kernel it is compared with.
 #include <hip/hip_runtime.h>
@@ -55,11 +57,13 @@ __device__ __forceinline__ void store(char *base, unsigned off, u32x4 v) {
 }
 
 template <int R, int D, int SP, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_pattern(unsigned tiles, char *d0, const char *s0, const char *s1,
-                                                   const char *s2, const char *s3, const char *s4, const char *s5,
-                                                   const char *s6, const char *s7, char *d1, char *d2, char *d3,
-                                                   unsigned lc) {
+__global__ __launch_bounds__(BLOCK) void k_pattern(unsigned tiles, unsigned lc, char *d0, const char *s0,
+                                                   const char *s1, const char *s2, const char *s3, const char *s4,
+                                                   const char *s5, const char *s6, const char *s7, char *d1,
+                                                   char *d2, char *d3) {
     const unsigned lane = threadIdx.x & 63u;
+    // the grid size from the tile count (a shift), not from the dispatch's
+    // hidden arguments, which lie beyond the preloaded dwords
     const unsigned G = (tiles + BLOCK / 64 - 1) / (BLOCK / 64);
     const unsigned w = mpp::xcd_virtual_block(blockIdx.x, G, lc) * (BLOCK / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -131,7 +135,7 @@ extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, 
     const unsigned wpb = static_cast<unsigned>(block) / 64;
     const unsigned grid = (tiles + wpb - 1) / wpb;
     unsigned lc = mpp::xcd_map_lc(grid, size_t(wpb) * kTileBytes, run_bytes);
-    void *args[] = {&tiles, &d[0], &s[0], &s[1], &s[2], &s[3], &s[4], &s[5], &s[6], &s[7], &d[1], &d[2], &d[3], &lc};
+    void *args[] = {&tiles, &lc, &d[0], &s[0], &s[1], &s[2], &s[3], &s[4], &s[5], &s[6], &s[7], &d[1], &d[2], &d[3]};
     const hipError_t e = hipLaunchKernel(kPatterns[block == 64 ? 1 : 0][p][store_policy], dim3(grid), dim3(block),
                                          args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : 4;

@@ -104,7 +104,7 @@ def test_counter_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
 def test_counters_missing_a_dispatch_are_refused(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     os.makedirs(tmp_path / "profiles")
-    kernel = "void mpp::k_stream_reg<Cfg<2, false, false, 2, false, false> >(...)"
+    kernel = "void mpp::(anonymous namespace)::k_pair<2>(unsigned int, unsigned int, float*, float const*, float const*, unsigned int)"
     write_counters(tmp_path / "f", "FETCH_SIZE", [(kernel, 1.0)])     # no calibration launch
     write_counters(tmp_path / "w", "WRITE_SIZE", [(kernel, 1.0)])
     with pytest.raises(RuntimeError, match="missing dispatches"):
@@ -133,8 +133,10 @@ def test_committed_headline_traffic_summary_is_consistent():
 
 
 def test_kernel_name_matchers():
-    assert bench.is_reduce_kernel("void mpp::(anonymous namespace)::k_stream_reg<mpp::(anonymous namespace)::"
-                                  "Cfg<2, false, false, 2, false, false> >(mpp::LaunchArgs<2>)")
-    assert not bench.is_reduce_kernel("void k_stream_reg<Cfg<1, false, false, 2, false, false> >(...)")
+    assert bench.is_reduce_kernel("void mpp::(anonymous namespace)::k_pair<2>(unsigned int, unsigned int, float*, "
+                                  "float const*, float const*, unsigned int)")
+    assert not bench.is_reduce_kernel("void mpp::(anonymous namespace)::k_pair<0>(unsigned int, unsigned int, ...)")
+    assert not bench.is_reduce_kernel("void k_stream_reg<Cfg<2, false, false, 2, false, false> >(...)")
+    assert bench.is_library_kernel("void mpp::(anonymous namespace)::k_pair<1>(unsigned int, ...)")
     assert bench.is_library_kernel("void k_single_shot<Cfg<0, false, false, 2, false, false> >(...)")
     assert not bench.is_library_kernel("void at::native::vectorized_elementwise_kernel<4, neg_kernel_cuda>")

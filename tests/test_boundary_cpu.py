@@ -220,12 +220,23 @@ def test_stream_kernel_choice():
     16-bit sources LDS-staged at R = 2 and 6..8 into binary32, at R = 2, 4 and 6..8 into a narrow
     destination; the broadcast schedule LDS-staged except R = 2 with fp32 sources or a narrow
     destination; with a residual LDS-staged only for the broadcast schedule; host-staged calls
-    LDS-staged for two 16-bit sources only."""
+    LDS-staged for two 16-bit sources only; two active fp32 sources into one fp32 destination
+    without a residual, kept stores and no forced grid take the two-rank contiguous kernel (3)."""
     n = 2048 * 4096
     CH, BC, HS, SW = ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED, ar.AR_SRC_WIRE
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
     for R in (2, 3, 4, 8, 16):
-        assert q(n, R=R, mode=CH)[1].stream_kernel == 1, R
+        assert q(n, R=R, mode=CH)[1].stream_kernel == (3 if R == 2 else 1), R
+    # the two-rank kernel only for its exact case: every wire type, automatic choice only
+    for wire in (ar.AR_F32, ar.AR_F16, ar.AR_BF16):
+        assert q(n, mode=CH, wire=wire)[1].stream_kernel == 3
+        assert q(n, mode=ar.AR_MODE_AUTO, wire=wire)[1].stream_kernel == 3   # AUTO resolves to CHUNKED
+    assert q(4097, mode=CH)[1].stream_kernel == 3
+    assert q(n, mode=CH, config={"stream_kernel": 1})[1].stream_kernel == 1
+    assert q(n, mode=CH, config={"grid_wgs": 7})[1].stream_kernel == 1
+    assert q(n, mode=CH, config={"store_policy": 2})[1].stream_kernel == 1
+    assert q(n, srcs=[A[1], 0], mode=CH | ar.AR_SRC_INACTIVE_NULL)[1].stream_kernel == 1
+    assert q(n, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
     for R in range(2, 17):
         want16 = 2 if R in (2, 6, 7, 8) else 1
         wantn = 2 if R in (2, 4, 6, 7, 8) else 1

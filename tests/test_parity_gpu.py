@@ -218,6 +218,33 @@ def test_every_kernel_instance(kctx, kname, mode_name):
                 check_against_oracle(kctx[kname], srcs, wire, mode, src_wire, what)
 
 
+PAIR_N = [1, 2, 63, 64, 511, 512, 513, 1023, 2047, 2048, 2049, 4097, 131_072 + 511, (1 << 20) + 3,
+          2048 * 4096]
+
+
+def test_two_rank_contiguous_kernel(ctx):
+    """The two-rank contiguous kernel (plan stream_kernel 3): every wire type, tiles with and
+    without a remainder, grids below and above one placement run, the prefill size, in place."""
+    for i, n in enumerate(PAIR_N):
+        rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_F32, ar.AR_BF16,
+                                    ar.AR_MODE_CHUNKED)
+        assert rc == ar.AR_OK and plan.stream_kernel == 3, (n, plan.stream_kernel)
+        for wire_name, wire in WIRES.items():
+            what = f"pair n={n} wire={wire_name}"
+            log_case(what)
+            srcs = wl.random_partials(9100 + i, wire, 2, n, dist="wide")
+            check_against_oracle(ctx, srcs, wire, ar.AR_MODE_CHUNKED, what=what)
+    # in place: the destination is the first source
+    n = (1 << 18) + 77
+    srcs = wl.random_partials(9199, 0, 2, n, dist="normal+outliers")
+    want = oracle_result(srcs, ar.AR_BF16)
+    a, b = to_device(srcs[0]), to_device(srcs[1])
+    log_case(f"pair in place n={n}")
+    ar.ar_reduce(ctx, [a], [a, b], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED)
+    torch.cuda.synchronize()
+    assert_bits_equal(a.cpu().numpy(), want, "pair in place")
+
+
 def test_small_chunks_many_ranges(ctx):
     """Chunk plan with many chunks and a ragged last chunk."""
     cfg = ar.ar_init(0, {"chunk_bytes": 4096})
