@@ -392,7 +392,7 @@ def is_reduce_kernel(name: str) -> bool:
 def is_library_kernel(name: str) -> bool:
     """Any kernel of the reduce library (every streaming and single-shot instance)."""
     plain = _plain_name(name)
-    return "k_stream_" in plain or "k_single_shot" in plain or "k_pair<" in plain
+    return "k_stream_" in plain or "k_single_shot" in plain or "k_pair" in plain
 
 
 CALIBRATION_KERNEL = "neg_kernel"   # torch.neg, the calibration copy (other elementwise kernels may run)

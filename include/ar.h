@@ -332,8 +332,9 @@ typedef struct {
     int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
     int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged,
                              3 the two-rank contiguous kernel (two active
-                             binary32 partials, one binary32 destination, no
-                             residual; chosen automatically)                */
+                             binary32 partials, one binary32 destination,
+                             contiguous, optionally an element-wise or
+                             broadcast-row residual; chosen automatically) */
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
     int    dst_bytes;     /* bytes per destination element                  */
     int    residual_kind; /* 0 none, 1 element-wise, 2 broadcast row        */

@@ -394,13 +394,13 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 lds = src_wire && (((dst_narrow ? kLds16Narrow : kLds16ToF32) >> R) & 1u) != 0;
             }
             plan->stream_kernel = lds ? 2 : 1;
-            // the two-rank contiguous kernel for the commonest call: two active
-            // binary32 partials into one binary32 destination, no residual,
-            // kept stores, the launch shape left to the library (prefill call
-            // 15.55 against 15.68 us with the register-staged kernel, same
-            // machine, bit-identical outputs)
-            if (!lds && resolved == AR_MODE_CHUNKED && rows == nullptr && R == 2 && active == 0x3u &&
-                res_kind == 0 && !src_wire && dst_bytes == 4 && !plan->store_nt && cfg.grid_wgs == 0) {
+            // the two-rank contiguous kernels for the commonest call: two
+            // active binary32 partials into one binary32 destination (with or
+            // without a residual), kept stores, the launch shape left to the
+            // library (prefill call 15.36 against 15.66 us with the
+            // register-staged kernel, same machine, bit-identical outputs)
+            if (resolved == AR_MODE_CHUNKED && rows == nullptr && R == 2 && active == 0x3u && !src_wire &&
+                dst_bytes == 4 && !plan->store_nt && cfg.grid_wgs == 0) {
                 plan->stream_kernel = 3;
             }
         }
@@ -574,12 +574,17 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
     }
 
     if (plan.stream_kernel == 3) {
-        // two-rank contiguous kernel: one 1-D launch per launch piece
+        // two-rank contiguous kernels: one 1-D launch per launch piece; an
+        // element-wise residual moves with the piece, a broadcast row keeps
+        // its base and takes the piece's phase in it
+        const int rk = res.ptr == nullptr ? 0 : (res.len == n ? 1 : 2);
         for (size_t p0 = 0; p0 < n; p0 += mpp::kMaxLaunchElems) {
             const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);
-            if (int rc = hip_status(mpp::launch_pair(wire_type, len, static_cast<char *>(dst[0]) + p0 * db,
+            const void *rp = rk == 1 ? static_cast<const char *>(res.ptr) + p0 * db : res.ptr;
+            if (int rc = hip_status(mpp::launch_pair(wire_type, rk, len, static_cast<char *>(dst[0]) + p0 * db,
                                                      static_cast<const char *>(srcs[0]) + p0 * sb,
-                                                     static_cast<const char *>(srcs[1]) + p0 * sb,
+                                                     static_cast<const char *>(srcs[1]) + p0 * sb, rp,
+                                                     rk == 2 ? res.len : 0, rk == 2 ? p0 % res.len : 0,
                                                      xcd_run_for(c->cfg, R, false), stream))) {
                 return rc;
             }

@@ -1107,60 +1107,129 @@ MPP_STREAM_KERNELS(k_stream_lds_nts_sl, kLdsBlock, stream_lds, kStoreStream, tru
 #undef MPP_HOT_PARAMS
 
 // ---------------------------------------------------------------------------
-// Two-rank contiguous kernel: the commonest call -- two active binary32
-// partials, one binary32 destination, no residual, one contiguous range
-// (the pages' own tensor-parallel case is two ranks) -- as a 1-D grid whose
-// parameters are all a wave needs before its loads: the tile count, the
-// remainder, the destination, the two sources and the placement exponent,
-// every one preloaded into SGPRs.  A wave reduces one wave tile with the
+// Two-rank contiguous kernels: the commonest call -- two active binary32
+// partials, one binary32 destination, one contiguous range (the pages' own
+// tensor-parallel case is two ranks) -- as a 1-D grid whose parameters are
+// all a wave needs before its loads, every one preloaded into SGPRs: the tile
+// count, the remainder, the destination, the two sources and the placement
+// exponent (then, for the residual forms, the residual, its length and the
+// launch piece's phase in it).  A wave reduces one wave tile with the
 // arithmetic of the streaming kernels' binary32 path (acc = wire(src0),
-// acc = RN32(acc + wire(src1)), write-through stores); the wave after the
-// last tile reduces the remainder element by element.  Measured on MI355X
-// against the general streaming kernel on the prefill call (same machine,
-// same placement, bit-identical outputs): the general kernel's range and
-// destination bookkeeping cost 0.13 us of its 15.68 us.
+// acc = RN32(acc + wire(src1)), then acc = RN32(acc + res[i]) with a
+// residual; write-through stores); the wave after the last tile reduces the
+// remainder element by element.  Measured on MI355X against the general
+// streaming kernels on the prefill call (same machine, same placement,
+// bit-identical outputs): 15.36 us against 15.66 us (register-staged) and
+// 15.46 us (LDS-staged) -- the general kernels' range, rank-mask and
+// destination bookkeeping sits on every wave's path to its first load.
+//
+// RK: 0 no residual, 1 element-wise residual (read once, non-temporal), 2-4
+// a broadcast row of res_len elements (a multiple of 8; cached loads, the row
+// is read by every row of the call): element i adds res[(i + phase) mod
+// res_len].  The column of a lane part takes one AND for a power-of-two row
+// (4), at most one wrap for a row of at least one wave tile (2), a remainder
+// for a shorter row (3); the wave's first column takes one scalar remainder.
+// Measured on MI355X on the prefill call with a 4096-element row: the
+// remainder sequence ahead of the row loads costs 0.03 us; issuing the row
+// loads first, or interleaved with the partials' loads, costs 0.04-0.08 us
+// (a part's fold waits for every load issued before its own).
 // ---------------------------------------------------------------------------
 constexpr int kPairBlock = 256;
 
 template <int W>
-__global__ __launch_bounds__(kPairBlock) void k_pair(unsigned tiles, unsigned rem, float *dst, const float *src0,
-                                                     const float *src1, unsigned lc) {
+__device__ __forceinline__ u32x4 pair_part(u32x4 a, u32x4 b) {
+    float x[4], y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[k] = f32_from_bits(a[k]);
+        y[k] = f32_from_bits(b[k]);
+    }
+    wire_pair<W>(x[0], x[1]);
+    wire_pair<W>(x[2], x[3]);
+    wire_pair<W>(y[0], y[1]);
+    wire_pair<W>(y[2], y[3]);
+    return u32x4{bits_from_f32(x[0] + y[0]), bits_from_f32(x[1] + y[1]), bits_from_f32(x[2] + y[2]),
+                 bits_from_f32(x[3] + y[3])};
+}
+
+__device__ __forceinline__ u32x4 add_res(u32x4 v, u32x4 r) {
+    return u32x4{bits_from_f32(f32_from_bits(v[0]) + f32_from_bits(r[0])),
+                 bits_from_f32(f32_from_bits(v[1]) + f32_from_bits(r[1])),
+                 bits_from_f32(f32_from_bits(v[2]) + f32_from_bits(r[2])),
+                 bits_from_f32(f32_from_bits(v[3]) + f32_from_bits(r[3]))};
+}
+
+// Column of element i + phase in a row of res_len elements, as the row kind
+// RK computes it: c0 = the wave's first column (t + phase, below 2^31: both
+// are below one launch piece), off < one wave tile.
+template <int RK>
+__device__ __forceinline__ unsigned pair_column(unsigned c0, unsigned off, unsigned res_len) {
+    const unsigned c = c0 + off;
+    if constexpr (RK == 4) return c & (res_len - 1);
+    if constexpr (RK == 2) return c >= res_len ? c - res_len : c;
+    return c % res_len;
+}
+
+template <int W, int RK>
+__device__ __forceinline__ void pair_body(unsigned tiles, unsigned rem, float *dst, const float *src0,
+                                          const float *src1, unsigned lc, const float *res, unsigned res_len,
+                                          unsigned res_phase) {
     constexpr unsigned wpb = kPairBlock / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const unsigned w = xcd_virtual_block(blockIdx.x, gridDim.x, lc) * wpb +
+    // the grid size from the preloaded counts (the dispatch's own grid size
+    // is a hidden argument past the preloaded dwords of the residual forms)
+    const unsigned grid = (tiles + (rem != 0 ? 1u : 0u) + wpb - 1) / wpb;
+    const unsigned w = xcd_virtual_block(blockIdx.x, grid, lc) * wpb +
                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (w < tiles) {
-        const size_t t = static_cast<size_t>(w) * kWaveTile;
-        u32x4 a[2], b[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            a[j] = load16<true>(src0 + t + 256 * j + 4 * lane);
-            b[j] = load16<true>(src1 + t + 256 * j + 4 * lane);
-        }
-        float *base = dst + t;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float x[4], y[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[k] = f32_from_bits(a[j][k]);
-                y[k] = f32_from_bits(b[j][k]);
+    if (w >= tiles) {
+        if (w == tiles && rem != 0) {
+            const size_t t = static_cast<size_t>(tiles) * kWaveTile;
+            for (unsigned e = lane; e < rem; e += kWave) {
+                float acc = wire_one<W, false>(src0, t + e);
+                acc = acc + wire_one<W, false>(src1, t + e);
+                if constexpr (RK == 1) acc = acc + res[t + e];
+                if constexpr (RK >= 2) acc = acc + res[(static_cast<unsigned>(t) + e + res_phase) % res_len];
+                dst[t + e] = acc;
             }
-            wire_pair<W>(x[0], x[1]);
-            wire_pair<W>(x[2], x[3]);
-            wire_pair<W>(y[0], y[1]);
-            wire_pair<W>(y[2], y[3]);
-            const u32x4 v = {bits_from_f32(x[0] + y[0]), bits_from_f32(x[1] + y[1]), bits_from_f32(x[2] + y[2]),
-                             bits_from_f32(x[3] + y[3])};
-            store16_wt(base, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
         }
-    } else if (w == tiles && rem != 0) {
-        const size_t t = static_cast<size_t>(tiles) * kWaveTile;
-        for (unsigned e = lane; e < rem; e += kWave) {
-            const float acc = wire_one<W, false>(src0, t + e);
-            dst[t + e] = acc + wire_one<W, false>(src1, t + e);
-        }
+        return;
     }
+    const size_t t = static_cast<size_t>(w) * kWaveTile;
+    u32x4 a[2], b[2], r[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        a[j] = load16<true>(src0 + t + 256 * j + 4 * lane);
+        b[j] = load16<true>(src1 + t + 256 * j + 4 * lane);
+    }
+    if constexpr (RK == 1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) r[j] = load16<true>(res + t + 256 * j + 4 * lane);
+    } else if constexpr (RK >= 2) {
+        const unsigned base = static_cast<unsigned>(t) + res_phase;
+        const unsigned c0 = RK == 4 ? base : base % res_len;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) r[j] = load16<false>(res + pair_column<RK>(c0, 256 * j + 4 * lane, res_len));
+    }
+    float *out = dst + t;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        u32x4 v = pair_part<W>(a[j], b[j]);
+        if constexpr (RK != 0) v = add_res(v, r[j]);
+        store16_wt(out, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(kPairBlock) void k_pair(unsigned tiles, unsigned rem, float *dst, const float *src0,
+                                                     const float *src1, unsigned lc) {
+    pair_body<W, 0>(tiles, rem, dst, src0, src1, lc, nullptr, 1, 0);
+}
+
+template <int W, int RK>
+__global__ __launch_bounds__(kPairBlock) void k_pair_res(unsigned tiles, unsigned rem, float *dst,
+                                                         const float *src0, const float *src1, unsigned lc,
+                                                         const float *res, unsigned res_len, unsigned res_phase) {
+    pair_body<W, RK>(tiles, rem, dst, src0, src1, lc, res, res_len, res_phase);
 }
 
 }  // namespace
@@ -1194,8 +1263,8 @@ constexpr int kBuckets = 4;
 // [rank bucket].
 typedef const void *const StreamTable[2][2][kCombos][kBuckets];
 extern const void *const kSingleShot[2][2][kCombos][kBuckets];
-// two-rank contiguous kernel, indexed by wire type (ar_dtype)
-extern const void *const kPair[3];
+// two-rank contiguous kernels, indexed by [residual kind][wire type (ar_dtype)]
+extern const void *const kPair[5][3];
 extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,
     kStreamLdsResM;
 

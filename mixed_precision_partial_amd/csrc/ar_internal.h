@@ -139,12 +139,14 @@ inline unsigned xcd_map_lc(unsigned grid_x, size_t wg_elems, size_t run_elems) {
     return lc;
 }
 
-// The two-rank contiguous kernel (k_pair): dst[i] = wire(src0[i]) + wire(src1[i])
-// in binary32 for i < n (n <= kMaxLaunchElems), one 1-D launch on `stream`,
-// XCD runs of about run_elems elements.  All three pointers are binary32
-// device arrays, 16-byte aligned.
-hipError_t launch_pair(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
-                       hipStream_t stream);
+// The two-rank contiguous kernels (k_pair, k_pair_res): dst[i] = wire(src0[i])
+// + wire(src1[i]) in binary32, then + res[i] (res_kind 1, element-wise) or
+// + res[(i + res_phase) mod res_len] (res_kind 2, a broadcast row of res_len
+// elements, a multiple of 8, res_phase < res_len), for i < n (n <=
+// kMaxLaunchElems); one 1-D launch on `stream`, XCD runs of about run_elems
+// elements.  Every pointer is a binary32 device array, 16-byte aligned.
+hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
+                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, hipStream_t stream);
 
 // Size of the library's static staging array (one per device), the only
 // device memory ar_reduce_staged_static uses beyond the caller's buffers.

@@ -82,9 +82,15 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 }  // namespace
 
-hipError_t launch_pair(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
-                       hipStream_t stream) {
-    if (wire < AR_F32 || wire > AR_BF16 || n == 0 || n > kMaxLaunchElems) return hipErrorInvalidValue;
+hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
+                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, hipStream_t stream) {
+    if (wire < AR_F32 || wire > AR_BF16 || res_kind < 0 || res_kind > 2 || n == 0 || n > kMaxLaunchElems) {
+        return hipErrorInvalidValue;
+    }
+    if (res_kind == 2 && (res_len == 0 || res_len % 8 != 0 || res_len > kMaxLaunchElems || res_phase >= res_len)) {
+        return hipErrorInvalidValue;
+    }
+    if (res_kind != 0 && res == nullptr) return hipErrorInvalidValue;
     unsigned tiles = static_cast<unsigned>(n / kWaveTile);
     unsigned rem = static_cast<unsigned>(n % kWaveTile);
     const unsigned waves = tiles + (rem != 0 ? 1u : 0u);
@@ -94,8 +100,13 @@ hipError_t launch_pair(int wire, size_t n, void *dst, const void *src0, const vo
     float *d = static_cast<float *>(dst);
     const float *a = static_cast<const float *>(src0);
     const float *b = static_cast<const float *>(src1);
-    void *args[] = {&tiles, &rem, &d, &a, &b, &lc};
-    return hipLaunchKernel(kPair[wire], dim3(grid), dim3(kPairBlock), args, 0, stream);
+    const float *r = static_cast<const float *>(res);
+    unsigned rl = static_cast<unsigned>(res_kind == 2 ? res_len : 0);
+    unsigned ph = static_cast<unsigned>(res_kind == 2 ? res_phase : 0);
+    // row kinds: 4 a power of two, 2 at least one wave tile, 3 shorter
+    const int kind = res_kind < 2 ? res_kind : ((res_len & (res_len - 1)) == 0 ? 4 : (res_len >= kWaveTile ? 2 : 3));
+    void *args[] = {&tiles, &rem, &d, &a, &b, &lc, &r, &rl, &ph};
+    return hipLaunchKernel(kPair[kind][wire], dim3(grid), dim3(kPairBlock), args, 0, stream);
 }
 
 hipError_t static_scratch(int device, void **out) {

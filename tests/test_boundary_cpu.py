@@ -220,8 +220,9 @@ def test_stream_kernel_choice():
     16-bit sources LDS-staged at R = 2 and 6..8 into binary32, at R = 2, 4 and 6..8 into a narrow
     destination; the broadcast schedule LDS-staged except R = 2 with fp32 sources or a narrow
     destination; with a residual LDS-staged only for the broadcast schedule; host-staged calls
-    LDS-staged for two 16-bit sources only; two active fp32 sources into one fp32 destination
-    without a residual, kept stores and no forced grid take the two-rank contiguous kernel (3)."""
+    LDS-staged for two 16-bit sources only; two active fp32 sources into one contiguous fp32
+    destination, with or without a residual, kept stores and no forced grid take the two-rank
+    contiguous kernels (3)."""
     n = 2048 * 4096
     CH, BC, HS, SW = ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED, ar.AR_SRC_WIRE
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
@@ -237,6 +238,19 @@ def test_stream_kernel_choice():
     assert q(n, mode=CH, config={"store_policy": 2})[1].stream_kernel == 1
     assert q(n, srcs=[A[1], 0], mode=CH | ar.AR_SRC_INACTIVE_NULL)[1].stream_kernel == 1
     assert q(n, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    # with a residual (element-wise or a broadcast row): the two-rank kernels for R = 2
+    # CHUNKED; the general kernels otherwise, and never for row-strided tensors
+    res = [0x7_0000_0000]
+    for res_len in (n, 4096):
+        rc, p = ar.ar_plan_query_add(A[20:21], A[1:3], n, ar.AR_F32, ar.AR_BF16, CH, res[0], res_len)
+        assert rc == ar.AR_OK and p.stream_kernel == 3 and p.residual_kind == (1 if res_len == n else 2)
+        rc, p = ar.ar_plan_query_add(A[20:21], A[1:4], n, ar.AR_F32, ar.AR_BF16, CH, res[0], res_len)
+        assert rc == ar.AR_OK and p.stream_kernel == 1
+        rc, p = ar.ar_plan_query_add(A[20:22], A[1:3], n, ar.AR_F32, ar.AR_BF16, BC, res[0], res_len)
+        assert rc == ar.AR_OK and p.stream_kernel == 2
+    rc, p = ar.ar_plan_query_rows(A[20:21], A[1:3], 2048, 4096, 4608, 4352, ar.AR_F32, ar.AR_BF16, CH,
+                                  residual=res[0], res_stride=0)
+    assert rc == ar.AR_OK and p.stream_kernel == 1
     for R in range(2, 17):
         want16 = 2 if R in (2, 6, 7, 8) else 1
         wantn = 2 if R in (2, 4, 6, 7, 8) else 1

@@ -164,6 +164,36 @@ def test_residual_in_place(kctx):
                           "residual aliasing a source")
 
 
+# two-rank kernels with a residual: broadcast rows shorter than, equal to and longer
+# than one 512-element wave tile (several wraps per tile, none, at most one), ragged
+# row counts, element-wise, in place
+PAIR_ROWS = [(8, 3001), (24, 999), (504, 33), (512, 17), (520, 9), (4096, 5), (4104, 3), (12_288, 2)]
+
+
+def test_two_rank_kernel_with_residual(kctx):
+    for i, (L, rows) in enumerate(PAIR_ROWS):
+        n = L * rows
+        rc, plan = ar.ar_plan_query_add([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_F32,
+                                        ar.AR_BF16, ar.AR_MODE_CHUNKED, 0x40_0000_0000, L)
+        assert rc == ar.AR_OK and plan.stream_kernel == 3 and plan.residual_kind == 2, (L, rows)
+        srcs = wl.random_partials(14_000 + i, 0, 2, n, dist="wide")
+        for wire_name, wire in WIRES.items():
+            for form, res in (("row", residual_for(14_100 + i, n, L)), ("elementwise", residual_for(14_200 + i, n, n))):
+                what = f"pair residual {form} n={n} L={res.size} wire={wire_name}"
+                run_and_check(kctx["default"], srcs, wire, ar.AR_MODE_CHUNKED, what, residual=res)
+    # in place: x = reduce(partials) + x
+    n = (1 << 18) + 40
+    srcs = wl.random_partials(14_300, 0, 2, n, dist="normal+outliers")
+    res = wl.residual(14_300, 1, n)
+    want = oracle.reduce(srcs, ar.AR_BF16, residual=res)[0]
+    dev = [to_device(s) for s in srcs]
+    x = to_device(res)
+    log_case(f"pair residual in place n={n}")
+    ar.ar_reduce_add(kctx["default"], [x], dev, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, x, n)
+    torch.cuda.synchronize()
+    assert_bits_equal(x.cpu().numpy(), want, "pair residual in place")
+
+
 def test_residual_errors(kctx):
     n = 4096
     dev = [to_device(np.ones(n, dtype=np.float32)) for _ in range(2)]

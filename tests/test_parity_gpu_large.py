@@ -94,6 +94,32 @@ def test_beyond_one_launch(ctx):
     free()
 
 
+def test_beyond_one_launch_row_residual(ctx):
+    """n = 2^30 + 8 with a broadcast row of 24 elements (which does not divide 2^30): the
+    second launch piece starts 16 elements into the row.  Two fp32 partials, bf16 wire."""
+    n, L = LAUNCH + 8, 24
+    assert n % L == 0 and LAUNCH % L != 0
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20_002)
+    srcs = [torch.randn(n, device="cuda", generator=g) for _ in range(2)]
+    row = torch.randn(L, device="cuda", generator=g)
+    rc, plan = ar.ar_plan_query_add([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_F32,
+                                    ar.AR_BF16, ar.AR_MODE_CHUNKED, 0x40_0000_0000, L)
+    assert rc == ar.AR_OK and plan.stream_kernel == 3 and plan.residual_kind == 2
+    idx = sample_indices(n, [LAUNCH, LAUNCH - 512, 1 << 29], 8)
+    s_host = [gather(s, idx) for s in srcs]
+    want = oracle.reduce(s_host, ar.AR_BF16, residual=row.cpu().numpy()[idx % L])[0]
+    out = torch.empty(n, device="cuda")
+    out.fill_(float("nan"))
+    log_case(f"n={n} chunked row residual L={L}")
+    ar.ar_reduce_add(ctx, [out], srcs, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, row, L)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "some element left unwritten"
+    assert_bits_equal(gather(out, idx), want, "row residual beyond one launch")
+    del out, srcs
+    free()
+
+
 def test_slice_broadcast_past_2_32(ctx):
     """n = 8200 x 523,779 (past 2^32) bf16 partials (R=2), slice + broadcast to 2 fp32
     destinations, with a broadcast row of 8200 elements (which does not divide 2^32, so a
