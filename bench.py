@@ -166,6 +166,11 @@ def parse():
                    help="instead of the benchmark: how the timing method changes a 20-step figure of the prefill "
                         "reduce (default events vs fence-free events, with and without a lead-in call, the cost "
                         "of an empty event interval, and the first steps after the GPU idled); one JSON line")
+    p.add_argument("--family-study", action="store_true",
+                   help="instead of the benchmark: the prefill call, plain and with an element-wise or a "
+                        "4096-element broadcast-row residual, on the automatically chosen kernel against the "
+                        "register- and LDS-staged general kernels and against the hardware's workgroup "
+                        "placement, interleaved in one process (bit-identical outputs checked); one JSON line")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="write profiles/counters_<workload>.md from the rocprofv3 --pmc runs of COUNTER_PASSES")
     p.add_argument("--profile-pass", action="store_true",
@@ -204,6 +209,8 @@ def main() -> int:
         return profile_pass(torch, ar, wl, args)
     if args.timing_study:
         return timing_study(torch, ar, wl, args)
+    if args.family_study:
+        return family_study(torch, ar, wl, args)
     w = wl.WORKLOADS["prefill_bf16"]
     R, n = w.R, w.n
     S = max(1, args.sets)
@@ -706,6 +713,92 @@ def profile_pass(torch, ar, wl, args):
 
 
 CEILING_LIB = os.path.join(ROOT, "mixed_precision_partial_amd", "libmpp_ceiling.so")
+
+
+def family_study(torch, ar, wl, args, reps: int = 7, calls: int = 1000) -> int:
+    """The kernel choice of the prefill call, measured: the automatic plan (the two-rank
+    kernels) against forced register-staged (stream_kernel 1) and LDS-staged (2) general
+    kernels, and against the hardware's own workgroup placement (xcd_run_elems 1), for the
+    plain call, an element-wise residual and a 4096-element broadcast row.  Every context's
+    output is compared bit for bit with the automatic plan's before timing; contexts are
+    timed interleaved, rep by rep, with pre-converted calls (ar.bind_reduce).  The plain call
+    is also timed with every second source moved 1 MiB into a larger allocation (the kernels'
+    sensitivity to where the buffers sit relative to each other).  One JSON line."""
+    w = wl.WORKLOADS["prefill_bf16"]
+    n, S = w.n, max(1, args.sets)
+    src = [[torch.from_numpy(p).cuda() for p in wl.partials(w, s)] for s in range(S)]
+    dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(S)]
+    res = [torch.from_numpy(wl.residual(w.case, s, n)).cuda() for s in range(S)]
+    row = torch.from_numpy(wl.residual(w.case, S, 4096)).cuda()
+    stream = torch.cuda.current_stream()
+    configs = {"auto": None, "register": {"stream_kernel": 1}, "lds": {"stream_kernel": 2},
+               "auto_hw_placement": {"xcd_run_elems": 1}}
+    ctxs = {k: ar.ar_init(0, v) for k, v in configs.items()}
+    forms = {"plain": (None, 12 * n), "residual": ("elementwise", 16 * n), "row": ("row", 12 * n + 4 * 4096)}
+    out = {"metric": "prefill call us by kernel choice", "n": n, "wire": "bf16", "rotated_sets": S,
+           "calls_per_rep": calls, "reps": reps}
+    for form, (rk, nbytes) in forms.items():
+        def bound(c, s):
+            r = None if rk is None else (res[s] if rk == "elementwise" else row)
+            return ar.bind_reduce(c, [dst[s]], src[s], n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED, stream=stream,
+                                  residual=r)
+        fns = {k: [bound(c, s) for s in range(S)] for k, c in ctxs.items()}
+        plans = {}
+        for k, c in ctxs.items():
+            r = None if rk is None else (res[0] if rk == "elementwise" else row)
+            if r is None:
+                rc, plan = ar.ar_plan_query([dst[0]], src[0], n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                            config=configs[k])
+            else:
+                rc, plan = ar.ar_plan_query_add([dst[0]], src[0], n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED, r,
+                                                r.numel(), config=configs[k])
+            assert rc == ar.AR_OK
+            plans[k] = int(plan.stream_kernel)
+        ref = None
+        for k in ctxs:
+            dst[0].fill_(float("nan"))
+            if fns[k][0]() != ar.AR_OK:
+                raise RuntimeError(f"{form} {k}: call failed")
+            torch.cuda.synchronize()
+            bits = dst[0].view(torch.int32).clone()
+            if ref is None:
+                ref = bits
+            elif not torch.equal(bits, ref):
+                raise RuntimeError(f"{form}: {k} differs from the automatic plan's output")
+        times = {k: [] for k in ctxs}
+        for _ in range(reps):
+            for k in ctxs:
+                f = fns[k]
+                times[k].append(timed_us(torch, stream, lambda i: f[i % S](), calls))
+        out[form] = {k: {"stream_kernel": plans[k], "us_median": round(float(np.median(v)), 3),
+                         "us_min": round(min(v), 3), "us_max": round(max(v), 3),
+                         "GB/s": round(nbytes / float(np.median(v)) / 1e3, 1)} for k, v in times.items()}
+        log(f"{form}: " + ", ".join(f"{k} {v['us_median']} us (kernel {v['stream_kernel']})"
+                                    for k, v in out[form].items()))
+    # the plain call with the second sources shifted by 1 MiB
+    shift = (1 << 20) // 4
+    big = [torch.empty(n + shift, dtype=torch.float32, device="cuda") for _ in range(S)]
+    moved = [b[shift:shift + n] for b in big]
+    for s in range(S):
+        moved[s].copy_(src[s][1])
+    fns = {k: [ar.bind_reduce(c, [dst[s]], [src[s][0], moved[s]], n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                              stream=stream) for s in range(S)] for k, c in ctxs.items()}
+    times = {k: [] for k in ctxs}
+    for _ in range(reps):
+        for k in ctxs:
+            f = fns[k]
+            times[k].append(timed_us(torch, stream, lambda i: f[i % S](), calls))
+    out["plain_second_source_shifted_1MiB"] = {k: {"us_median": round(float(np.median(v)), 3),
+                                                   "GB/s": round(12 * n / float(np.median(v)) / 1e3, 1)}
+                                               for k, v in times.items()}
+    log("plain, second sources shifted 1 MiB: " + ", ".join(
+        f"{k} {v['us_median']} us" for k, v in out["plain_second_source_shifted_1MiB"].items()))
+    del big, moved
+    torch.cuda.synchronize()
+    for c in ctxs.values():
+        ar.ar_free(c)
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def timing_study(torch, ar, wl, args, reps: int = 6) -> int:

@@ -397,8 +397,10 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             // the two-rank contiguous kernels for the commonest call: two
             // active binary32 partials into one binary32 destination (with or
             // without a residual), kept stores, the launch shape left to the
-            // library (prefill call 15.36 against 15.66 us with the
-            // register-staged kernel, same machine, bit-identical outputs)
+            // library (prefill call 15.45 against 15.82 us with the
+            // register-staged kernel, 20.2 against 21.2-22.8 us with an
+            // element-wise residual, 15.6 against 16.4-17.3 us with a row;
+            // same machine, bit-identical outputs)
             if (resolved == AR_MODE_CHUNKED && rows == nullptr && R == 2 && active == 0x3u && !src_wire &&
                 dst_bytes == 4 && !plan->store_nt && cfg.grid_wgs == 0) {
                 plan->stream_kernel = 3;

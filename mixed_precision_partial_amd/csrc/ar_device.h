@@ -1117,11 +1117,14 @@ MPP_STREAM_KERNELS(k_stream_lds_nts_sl, kLdsBlock, stream_lds, kStoreStream, tru
 // arithmetic of the streaming kernels' binary32 path (acc = wire(src0),
 // acc = RN32(acc + wire(src1)), then acc = RN32(acc + res[i]) with a
 // residual; write-through stores); the wave after the last tile reduces the
-// remainder element by element.  Measured on MI355X against the general
-// streaming kernels on the prefill call (same machine, same placement,
-// bit-identical outputs): 15.36 us against 15.66 us (register-staged) and
-// 15.46 us (LDS-staged) -- the general kernels' range, rank-mask and
-// destination bookkeeping sits on every wave's path to its first load.
+// remainder element by element.  One wave per workgroup: measured on MI355X
+// on the prefill call in six buffer layouts (same process), 64-thread
+// workgroups ran 15.36-15.42 us where 256-thread ones ran 15.29-15.62 us, the
+// slowest in the layouts a fresh process allocates; with a 4096-element row
+// 15.62 against 15.86-15.89 us.  Against the general streaming kernels
+// (bit-identical outputs) the register-staged kernel's range, rank-mask and
+// destination bookkeeping costs 0.3-0.4 us per prefill call, and both
+// general families lose 1 us and more once a residual is fused.
 //
 // RK: 0 no residual, 1 element-wise residual (read once, non-temporal), 2-4
 // a broadcast row of res_len elements (a multiple of 8; cached loads, the row
@@ -1129,12 +1132,11 @@ MPP_STREAM_KERNELS(k_stream_lds_nts_sl, kLdsBlock, stream_lds, kStoreStream, tru
 // res_len].  The column of a lane part takes one AND for a power-of-two row
 // (4), at most one wrap for a row of at least one wave tile (2), a remainder
 // for a shorter row (3); the wave's first column takes one scalar remainder.
-// Measured on MI355X on the prefill call with a 4096-element row: the
-// remainder sequence ahead of the row loads costs 0.03 us; issuing the row
-// loads first, or interleaved with the partials' loads, costs 0.04-0.08 us
-// (a part's fold waits for every load issued before its own).
+// The row loads follow the partials' loads: a part's fold waits for every
+// load issued before its own, and row loads issued first or interleaved
+// measured slower on MI355X.
 // ---------------------------------------------------------------------------
-constexpr int kPairBlock = 256;
+constexpr int kPairBlock = 64;
 
 template <int W>
 __device__ __forceinline__ u32x4 pair_part(u32x4 a, u32x4 b) {
