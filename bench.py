@@ -108,16 +108,44 @@ def timed_us(torch, stream, fn, reps: int, lead: int = 1) -> float:
     return a.elapsed_ms(b) * 1e3 / reps
 
 
+def code_tokens(text: str) -> str:
+    """C/C++ source text without its comments, whitespace runs collapsed to one space: what
+    the compiler sees, so that an edited comment does not count as a changed kernel.  String
+    and character literals are kept verbatim (a "//" inside one is not a comment)."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
     """Hash of every device-code source of the reduce library (the kernel templates and their
-    instance files; the benchmark's own ceiling kernels are not part of it)."""
+    instance files; the benchmark's own ceiling kernels are not part of it), over the code
+    tokens only: comments and layout do not change it."""
     import glob
 
     h = hashlib.sha256()
     paths = glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
     for path in sorted(p for p in paths if os.path.basename(p) != "bench_ceiling.hip"):
-        with open(path, "rb") as fh:
-            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+        with open(path, encoding="utf-8") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

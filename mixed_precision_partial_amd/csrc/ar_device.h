@@ -1118,13 +1118,13 @@ MPP_STREAM_KERNELS(k_stream_lds_nts_sl, kLdsBlock, stream_lds, kStoreStream, tru
 // acc = RN32(acc + wire(src1)), then acc = RN32(acc + res[i]) with a
 // residual; write-through stores); the wave after the last tile reduces the
 // remainder element by element.  One wave per workgroup: measured on MI355X
-// on the prefill call in six buffer layouts (same process), 64-thread
-// workgroups ran 15.36-15.42 us where 256-thread ones ran 15.29-15.62 us, the
-// slowest in the layouts a fresh process allocates; with a 4096-element row
-// 15.62 against 15.86-15.89 us.  Against the general streaming kernels
+// on the prefill call, 15.44-15.45 us against 15.48-15.50 us with four waves
+// per workgroup, and 15.62 against 15.86-15.89 us with a 4096-element row
+// (the four-wave form was also the more sensitive to where the buffers sit
+// relative to each other).  Against the general streaming kernels
 // (bit-identical outputs) the register-staged kernel's range, rank-mask and
-// destination bookkeeping costs 0.3-0.4 us per prefill call, and both
-// general families lose 1 us and more once a residual is fused.
+// destination bookkeeping costs 0.3-0.45 us per prefill call, and both
+// general families lose 0.9 us and more once a residual is fused.
 //
 // RK: 0 no residual, 1 element-wise residual (read once, non-temporal), 2-4
 // a broadcast row of res_len elements (a multiple of 8; cached loads, the row

@@ -142,3 +142,13 @@ def test_kernel_name_matchers():
     assert not bench.is_reduce_kernel("void mpp::(anonymous namespace)::k_pair_res<2, 2>(unsigned int, ...)")
     assert bench.is_library_kernel("void k_single_shot<Cfg<0, false, false, 2, false, false> >(...)")
     assert not bench.is_library_kernel("void at::native::vectorized_elementwise_kernel<4, neg_kernel_cuda>")
+
+
+def test_kernel_hash_ignores_comments_not_code():
+    src = 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char *s = "a // b /* c */";\n'
+    same = 'int f(int a) {\n\n  return a + 1;  }   // other words\nconst char *s = "a // b /* c */";'
+    other = 'int f(int a) { return a + 2; }\nconst char *s = "a // b /* c */";'
+    assert bench.code_tokens(src) == bench.code_tokens(same)
+    assert bench.code_tokens(src) != bench.code_tokens(other)
+    assert '"a // b /* c */"' in bench.code_tokens(src)
+    assert bench.code_tokens("char c = '/'; // x") == "char c = '/';"
