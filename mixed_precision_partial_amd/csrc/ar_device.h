@@ -729,22 +729,23 @@ constexpr int kSingleShotBlock = 64;
 constexpr int kLdsBlock = 64;
 
 // Workgroup size of the register-staged streaming kernel per rank bucket
-// (measured on MI355X): 64-thread workgroups for the 8-rank bucket, whose
-// batches hold 16 loads per lane and so limit how many waves fit on a CU --
-// small workgroups pack the CUs more evenly (cold R = 8 fp32 reduce: 6.38
-// against 6.13 TB/s); 128 threads for the binary32-source residual instances
-// of the 2- and 4-rank buckets (same machine: element-wise residual 20.11
-// against 20.36 us, bias row 16.44 against 16.62 us, row-strided block + bias
-// 16.23 against 16.35 us; with 16-bit sources no gain); 256 threads elsewhere
-// (prefill 15.78 against 15.89 us with 128).  The host takes the same
-// function for the launch shape, and the launcher refuses a shape that
-// differs from it.
+// (measured on MI355X, with the XCD placement runs): one wave per workgroup
+// up to the 8-rank bucket -- small workgroups pack the CUs more evenly and
+// keep each XCD's run of tiles spread over its CUs (same machine against 256
+// threads, bit-identical: 4 ranks 25.71 against 25.94 us, 3 ranks 20.11
+// against 20.40, 4 ranks with one inactive 20.33 against 20.69, two-rank
+// slice + broadcast 23.99 against 24.56, row-strided block + bias 16.12
+// against 16.28, 3 ranks + bias row 20.63 against 20.95; 4 bf16 partials
+// 17.51 against 17.63; the prefill call and 3-rank narrow destinations
+// unchanged); 256 threads for the 16-rank bucket (27.52 against 27.92 us with
+// one wave per workgroup on a quarter of the prefill shape).  The host takes
+// the same function for the launch shape, and the launcher refuses a shape
+// that differs from it.
 #ifndef MPP_STREAM_BLOCK
 #define MPP_STREAM_BLOCK 0
 #endif
 constexpr int stream_block(int rank_bucket, bool res, bool src_is_wire) {
-    return MPP_STREAM_BLOCK > 0 ? MPP_STREAM_BLOCK
-                                : (rank_bucket == 8 ? 64 : (res && !src_is_wire && rank_bucket <= 4 ? 128 : 256));
+    return MPP_STREAM_BLOCK > 0 ? MPP_STREAM_BLOCK : (rank_bucket == 16 ? 256 : 64);
 }
 
 // Streaming-kernel tuning (compile-time; measured on MI355X):
