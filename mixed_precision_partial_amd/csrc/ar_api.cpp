@@ -373,11 +373,15 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         //     or a narrow destination (22.7 against 24.3 us; 23.3 against 24.0);
         //   - CHUNKED: register-staged for fp32 sources (prefill 15.7 against
         //     16.4 us, R = 8 363 against 416 us); for 16-bit sources the rank
-        //     masks below (R = 8 into fp32: 193.4 against 202.7 us; narrow R = 8:
-        //     48.2 against 51.6 us; narrow R = 3: 22.4 against 23.2 us);
+        //     masks below, from a sweep of R on the prefill shape with one-wave
+        //     register workgroups (into fp32, register against LDS-staged:
+        //     R = 2 13.44 / 12.73 us, 3 15.55 / 16.64, 4 17.71 / 17.89, 5 22.67
+        //     / 22.38, 6-8 0.6-1.4 us slower, 12 and 16 faster; narrow: R = 2
+        //     9.08 / 8.54, 3 11.50 / 12.37, 4 14.12 / 14.59, 5 20.03 / 20.51,
+        //     6-8 0.7-2.0 us slower, 12 and 16 faster);
         //   - host-staged calls: LDS-staged for two 16-bit sources only.
-        constexpr unsigned kLds16ToF32 = (1u << 2) | (1u << 6) | (1u << 7) | (1u << 8);
-        constexpr unsigned kLds16Narrow = (1u << 2) | (1u << 4) | (1u << 6) | (1u << 7) | (1u << 8);
+        constexpr unsigned kLds16ToF32 = (1u << 2) | (1u << 5) | (1u << 6) | (1u << 7) | (1u << 8);
+        constexpr unsigned kLds16Narrow = (1u << 2) | (1u << 6) | (1u << 7) | (1u << 8);
         if (resolved == AR_MODE_SINGLE_SHOT) {
             plan->stream_kernel = 0;
         } else if (cfg.stream_kernel != 0) {
