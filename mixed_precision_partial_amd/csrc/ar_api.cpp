@@ -369,8 +369,9 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         //     a row), register-staged otherwise (a broadcast row on the prefill
         //     shape: 17.4 against 18.3 us; 8 ranks: 374 against 411 us);
         //   - broadcast schedule: LDS-staged (R = 4, fp32 sources: 88 against
-        //     95 us; 16-bit sources at every R), except R = 2 with fp32 sources
-        //     or a narrow destination (22.7 against 24.3 us; 23.3 against 24.0);
+        //     95 us; 16-bit sources at every R; R = 2 on the prefill shape with
+        //     one-wave register workgroups: fp32 sources 22.54-22.68 against
+        //     22.91-23.04 us, bf16 into bf16 11.52 against 12.94 us);
         //   - CHUNKED: register-staged for fp32 sources (prefill 15.7 against
         //     16.4 us, R = 8 363 against 416 us); for 16-bit sources the rank
         //     masks below, from a sweep of R on the prefill shape with one-wave
@@ -391,7 +392,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             if (res_kind != 0) {
                 lds = resolved == AR_MODE_RS_BCAST;
             } else if (resolved == AR_MODE_RS_BCAST) {
-                lds = R != 2 || (src_wire && !dst_narrow);
+                lds = true;
             } else if (resolved == AR_MODE_HOST_STAGED) {
                 lds = src_wire && R == 2;
             } else {

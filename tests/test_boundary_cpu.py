@@ -218,8 +218,8 @@ def test_store_policy_rule():
 def test_stream_kernel_choice():
     """The automatic family follows the measured table: CHUNKED fp32 sources register-staged;
     16-bit sources LDS-staged at R = 2 and 5..8 into binary32, at R = 2 and 6..8 into a narrow
-    destination; the broadcast schedule LDS-staged except R = 2 with fp32 sources or a narrow
-    destination; with a residual LDS-staged only for the broadcast schedule; host-staged calls
+    destination; the broadcast schedule LDS-staged; with a residual LDS-staged only for the
+    broadcast schedule; host-staged calls
     LDS-staged for two 16-bit sources only; two active fp32 sources into one contiguous fp32
     destination, with or without a residual, kept stores and no forced grid take the two-rank
     contiguous kernels (3)."""
@@ -256,9 +256,9 @@ def test_stream_kernel_choice():
         wantn = 2 if R in (2, 6, 7, 8) else 1
         assert q(n, R=R, mode=CH | SW)[1].stream_kernel == want16, R
         assert q(n, R=R, mode=CH, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == wantn, R
-        assert q(n, R=R, mode=BC, wire=ar.AR_F16)[1].stream_kernel == (1 if R == 2 else 2), R
+        assert q(n, R=R, mode=BC, wire=ar.AR_F16)[1].stream_kernel == 2, R
         assert q(n, R=R, mode=BC | SW, wire=ar.AR_F16)[1].stream_kernel == 2, R
-        assert q(n, R=R, mode=BC, wire=ar.AR_F16, dst_type=ar.AR_F16)[1].stream_kernel == (1 if R == 2 else 2), R
+        assert q(n, R=R, mode=BC, wire=ar.AR_F16, dst_type=ar.AR_F16)[1].stream_kernel == 2, R
         assert q(n, R=R, mode=HS | SW, host=True)[1].stream_kernel == (2 if R == 2 else 1), R
         assert q(n, R=R, mode=HS, host=True)[1].stream_kernel == 1, R
     # an explicit choice wins

@@ -135,6 +135,9 @@ def check_plan(plan, R, n, dst_type, wire_type, mode, srcs, resolved, res_kind, 
         if res_kind and not pair:
             # with a residual: LDS-staged for the broadcast schedule, register-staged otherwise
             assert plan.stream_kernel == (2 if resolved == ar.AR_MODE_RS_BCAST else 1)
+        if resolved == ar.AR_MODE_RS_BCAST:
+            # the broadcast schedule is LDS-staged for every rank count and width
+            assert plan.stream_kernel == 2
     if resolved == ar.AR_MODE_RS_BCAST:
         pos = 0
         for r in range(R):
