@@ -1114,8 +1114,9 @@ def other_schedules(torch, ar, wl):
     """The other configurations and adjacent forms: the 4-rank slice + broadcast,
     residual adds, narrow destinations, inactive ranks, row-strided tensors, R=8
     from HBM (fp32 and bf16 partials) and from pinned host memory (direct reads,
-    copy-engine pipeline, static staging) -- each beside the ceiling kernel run
-    at its own bytes and access pattern where one exists (stderr + extras)."""
+    copy-engine pipeline, static staging), and the two-rank reduce on a 768 MiB
+    call -- each beside the ceiling kernel run at its own bytes and access
+    pattern where one exists (stderr + extras)."""
     out = {}
     stream = torch.cuda.current_stream()
 
@@ -1252,6 +1253,14 @@ def other_schedules(torch, ar, wl):
     out["r8_hbm_fp32_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     with_ceiling(out["r8_hbm_fp32_src"], pattern_ceiling(torch, stream, 8, 1, [srcs32], [[dst]], w.n * 4, 10))
     log(f"r8_hbm_fp32_src: {out['r8_hbm_fp32_src']}")
+    # the prefill reduce's kernel on a call 8 x larger (two of the same [8192 x 8192] fp32
+    # partials, 768 MiB per call): the per-call fixed cost amortised, beside its ceiling kernel
+    ms = timed(lambda: ar.ar_reduce(ctx, [dst], srcs32[:2], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                    stream=stream), 30)
+    b = 2 * w.n * 4 + w.n * 4
+    out["r2_large_fp32_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1), "n": w.n}
+    with_ceiling(out["r2_large_fp32_src"], pattern_ceiling(torch, stream, 2, 1, [srcs32[:2]], [[dst]], w.n * 4, 10))
+    log(f"r2_large_fp32_src: {out['r2_large_fp32_src']}")
     del srcs32
     pre = [wl.as_wire_typed(p, w.wire) for p in parts]
     srcs16 = [torch.from_numpy(p.view(np.int16)).cuda() for p in pre]
