@@ -1281,7 +1281,7 @@ def other_schedules(torch, ar, wl):
     ms_direct = timed(lambda: ar.ar_reduce(ctx, [dst], pinned, w.n, ar.AR_F32, w.wire,
                                            ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
     # the allocation-free entry point: the same copy-engine pipeline staged in the
-    # library's 64 MiB static array (smaller chunks than the context's ring)
+    # library's 64 MiB static array (one slot: smaller copies than the context's ring)
     ms_static = timed(lambda: ar.ar_reduce_staged_static(ctx_copy, [dst], pinned, w.n, ar.AR_F32, w.wire,
                                                          ar.AR_MODE_HOST_STAGED | ar.AR_SRC_WIRE, stream=stream), 5)
     torch.cuda.synchronize()
@@ -1302,7 +1302,7 @@ def other_schedules(torch, ar, wl):
                                "frac_of_h2d_copy": round(ms_copy / ms_direct, 3), "path": "kernel reads pinned memory"}
     out["host_static_staging_bf16"] = {"ms": round(ms_static, 3), "pcie_GB/s": round(pcie_bytes / ms_static / 1e6, 2),
                                        "frac_of_h2d_copy": round(ms_copy / ms_static, 3),
-                                       "path": "copy engine into the static 64 MiB array (ar_reduce_staged_static)"}
+                                       "path": "copy engine into the static 64 MiB array, one slot (ar_reduce_staged_static)"}
     log(f"host_static_staging_bf16: {out['host_static_staging_bf16']}")
     log(f"host_staged_bf16: {out['host_staged_bf16']}")
     log(f"host_direct_bf16: {out['host_direct_bf16']}")

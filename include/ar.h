@@ -226,12 +226,13 @@ int ar_reduce(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, siz
  *   host-staged call; mode must be AR_MODE_HOST_STAGED (or AR_MODE_AUTO
  *   with pinned host sources) plus optional AR_SRC_WIRE /
  *   AR_SRC_INACTIVE_NULL, whatever the context's host_path.
- *   The copy chunk shrinks so that host_slots x R chunks fit the array
- *   (any n is accepted); a host_chunk_bytes set in the context's ar_config
- *   whose ring would not fit -> AR_ERR_NOMEM, nothing enqueued.
+ *   The array is one staging slot: the copy chunk is the largest whose R
+ *   rank chunks fit it (any n is accepted; host_slots does not apply); a
+ *   host_chunk_bytes set in the context's ar_config whose R chunks would not
+ *   fit -> AR_ERR_NOMEM, nothing enqueued.
  *   Every call on a device shares that device's array: calls through one
- *   context are ordered by its slot events, but calls of different contexts
- *   that overlap on one device race on the array.  Nothing in it needs to
+ *   context are ordered by the context's event on the array, but calls of
+ *   different contexts that overlap on one device race on the array.  Nothing in it needs to
  *   start at zero (every byte a kernel reads was copied in by the same call).
  * Errors: those of ar_reduce; another resolved mode -> AR_ERR_INVALID; under
  * stream capture -> AR_ERR_UNSUPPORTED. */
@@ -254,8 +255,10 @@ int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *sr
  * Every other argument, the ownership rules and the error codes are those
  * of ar_reduce; residual NULL, residual_len 0 or not dividing n ->
  * AR_ERR_INVALID (n = 0 is a no-op and checks only residual != NULL).  Calls
- * with a residual run on the register-staged kernels (stream_kernel 2 is
- * not used for them). */
+ * with a residual run on the two-rank kernels (two fp32 partials into one
+ * fp32 destination, CHUNKED), on the LDS-staged kernels in the broadcast
+ * schedule, and on the register-staged kernels otherwise (unless
+ * stream_kernel forces a family). */
 int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
                   ar_dtype dst_type, ar_dtype wire_type, unsigned mode, const void *residual,
                   size_t residual_len, void *hip_stream);

@@ -431,8 +431,14 @@ struct ar_ctx {
     hipEvent_t ev_start = nullptr;     // caller-stream order point before the copies
     unsigned next_slot = 0;
     // device address of the library's static staging array on this device
-    // (ar_reduce_staged_static); shared by every context on the device
+    // (ar_reduce_staged_static); shared by every context on the device.  The
+    // array is one slot of this context's own bookkeeping, apart from the ring
+    // above: its copies landed / the add kernel reading it finished.
     void *static_scratch = nullptr;
+    hipEvent_t ev_static_h2d = nullptr;
+    hipEvent_t ev_static_free = nullptr;
+    char static_used = 0;
+    unsigned static_next = 0;
 };
 
 namespace {
@@ -463,9 +469,12 @@ void destroy(ar_ctx *c) {
     for (hipEvent_t e : c->ev_free) {
         if (e) (void)hipEventSynchronize(e);
     }
+    if (c->ev_static_free) (void)hipEventSynchronize(c->ev_static_free);
     if (c->scratch) (void)hipFree(c->scratch);
     for (hipEvent_t e : c->ev_h2d) if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->ev_free) if (e) (void)hipEventDestroy(e);
+    if (c->ev_static_h2d) (void)hipEventDestroy(c->ev_static_h2d);
+    if (c->ev_static_free) (void)hipEventDestroy(c->ev_static_free);
     if (c->ev_start) (void)hipEventDestroy(c->ev_start);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
     delete c;
@@ -696,23 +705,41 @@ int ensure_scratch(ar_ctx *c, size_t bytes) {
 // the internal copy stream; the caller's stream waits for that slot's copies,
 // runs the add kernel over the slot and marks the slot free again.  The copy
 // of a later chunk into the same slot waits for that mark, so copies run ahead
-// of the adds by up to K chunks.  The ring is the context's (grown with
-// hipMalloc when too small), or, with `fixed`, the `fixed_bytes` at `fixed`:
-// the chunk then shrinks to what K slots of R ranks fit there, and nothing is
-// allocated; a configured copy chunk whose ring does not fit is AR_ERR_NOMEM.
+// of the adds by up to K chunks.  The ring is the context's (K = host_slots,
+// grown with hipMalloc when too small), or, with `fixed`, the `fixed_bytes`
+// at `fixed` as one slot with its own events: the chunk is then what R ranks
+// fit there, and nothing is allocated; a configured copy chunk that does not
+// fit is AR_ERR_NOMEM.  One slot for the fixed array, because the chunk size
+// decides the copy engine's rate: measured on MI355X, R = 8 bf16 partials
+// [8192 x 8192] (1 GiB over PCIe) took 20.7 ms with one 8 MiB-per-rank slot,
+// 25.5 ms with two 4 MiB slots and 28.4 ms with three 2.7 MiB slots in the
+// same 64 MiB, against 18.7 ms for one plain 1 GiB copy; the context's ring
+// at 8 MiB chunks takes 20.5 ms with three slots and 20.7 with one.
+struct SlotRing {
+    unsigned K;
+    unsigned *next;
+    char *used;
+    hipEvent_t *h2d;
+    hipEvent_t *free;
+};
+
 int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const *srcs, int R, size_t n,
                     int wire_type, const Residual &res, hipStream_t stream, void *fixed = nullptr,
                     size_t fixed_bytes = 0) {
     const mpp::Types types = launch_types(plan, wire_type);
     const size_t sb = static_cast<size_t>(plan.src_bytes);
     const size_t db = static_cast<size_t>(plan.dst_bytes);
-    const size_t K = static_cast<size_t>(c->cfg.host_slots);
+    const SlotRing slots = fixed != nullptr
+                               ? SlotRing{1u, &c->static_next, &c->static_used, &c->ev_static_h2d, &c->ev_static_free}
+                               : SlotRing{static_cast<unsigned>(c->cfg.host_slots), &c->next_slot,
+                                          c->slot_used.data(), c->ev_h2d.data(), c->ev_free.data()};
+    const size_t K = slots.K;
     size_t chunk = plan.chunk_elems;
     if (fixed != nullptr) {
         const size_t fit = round_down(fixed_bytes / (K * static_cast<size_t>(R) * sb), mpp::kWaveTile);
         if (fit < mpp::kWaveTile) return AR_ERR_NOMEM;
         if (c->cfg.host_chunk_bytes != 0 && chunk > fit) return AR_ERR_NOMEM;
-        chunk = std::min(chunk, fit);
+        chunk = c->cfg.host_chunk_bytes != 0 ? chunk : fit;
     }
     const size_t n_chunks = (n + chunk - 1) / chunk;
     const size_t rank_stride = chunk * sb;
@@ -730,11 +757,11 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
     for (size_t ch = 0; ch < n_chunks; ++ch) {
         const size_t e0 = ch * chunk;
         const size_t len = std::min(chunk, n - e0);
-        const unsigned slot = c->next_slot;
-        c->next_slot = (c->next_slot + 1) % static_cast<unsigned>(K);
+        const unsigned slot = *slots.next % static_cast<unsigned>(K);
+        *slots.next = (slot + 1) % static_cast<unsigned>(K);
         char *slot_base = ring + slot * slot_stride;
 
-        if (c->slot_used[slot] && hipStreamWaitEvent(c->copy_stream, c->ev_free[slot], 0) != hipSuccess) {
+        if (slots.used[slot] && hipStreamWaitEvent(c->copy_stream, slots.free[slot], 0) != hipSuccess) {
             return AR_ERR_RUNTIME;
         }
         for (int r = 0; r < R; ++r) {
@@ -744,8 +771,8 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
                 return AR_ERR_RUNTIME;
             }
         }
-        if (hipEventRecord(c->ev_h2d[slot], c->copy_stream) != hipSuccess) return AR_ERR_RUNTIME;
-        if (hipStreamWaitEvent(stream, c->ev_h2d[slot], 0) != hipSuccess) return AR_ERR_RUNTIME;
+        if (hipEventRecord(slots.h2d[slot], c->copy_stream) != hipSuccess) return AR_ERR_RUNTIME;
+        if (hipStreamWaitEvent(stream, slots.h2d[slot], 0) != hipSuccess) return AR_ERR_RUNTIME;
 
         mpp::KernelArgs a{};
         a.xcd_run_elems = xcd_run_for(c->cfg, R, false);
@@ -760,8 +787,8 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
                                                        static_cast<unsigned>(len), 1, c->cu_count, c->cfg.grid_wgs);
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
-        if (hipEventRecord(c->ev_free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
-        c->slot_used[slot] = 1;
+        if (hipEventRecord(slots.free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
+        slots.used[slot] = 1;
     }
     return AR_OK;
 }
@@ -904,6 +931,14 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
     // it current); looked up once per device and shared by its contexts
     if (rc == AR_OK && mpp::static_scratch(hip_device, &c->static_scratch) != hipSuccess) {
         c->static_scratch = nullptr;
+        rc = AR_ERR_RUNTIME;
+    }
+    if (rc == AR_OK && hipEventCreateWithFlags(&c->ev_static_h2d, hipEventDisableTiming) != hipSuccess) {
+        c->ev_static_h2d = nullptr;
+        rc = AR_ERR_RUNTIME;
+    }
+    if (rc == AR_OK && hipEventCreateWithFlags(&c->ev_static_free, hipEventDisableTiming) != hipSuccess) {
+        c->ev_static_free = nullptr;
         rc = AR_ERR_RUNTIME;
     }
     if (rc == AR_OK) {

@@ -28,9 +28,10 @@ def ctx():
 
 
 # (R, n, wire, sources already in the wire type): the first call needs several
-# chunks per slot of the static ring (8 ranks x 3 slots of fp32 chunks in 64 MiB);
-# the second is smaller, with 16-bit sources
-CALLS = [(8, 4_000_037, ar.AR_BF16, False), (3, 40_009, ar.AR_F16, True)]
+# chunks through the static array (one slot of 8 fp32 rank chunks in 64 MiB, so
+# each chunk waits for the previous chunk's add); the second is smaller, with
+# 16-bit sources
+CALLS = [(8, 6_000_037, ar.AR_BF16, False), (3, 40_009, ar.AR_F16, True)]
 
 
 def test_static_staging_matches_copy_engine_path(ctx):
@@ -61,7 +62,7 @@ def test_static_staging_refusals(ctx):
     pinned = [to_pinned(s.cpu().numpy()) for s in srcs]
     assert ar.ar_reduce_staged_static(ctx, [out], pinned, n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
                                       check=False) == ar.AR_ERR_INVALID
-    # a configured copy chunk whose ring (3 slots x 2 ranks x 64 MiB) exceeds the array
+    # a configured copy chunk whose rank chunks (2 ranks x 64 MiB) exceed the array
     big = ar.ar_init(0, {"host_chunk_bytes": 64 << 20})
     try:
         n2 = 1 << 20
