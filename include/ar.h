@@ -336,8 +336,9 @@ typedef struct {
     int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged,
                              3 the two-rank contiguous kernel (two active
                              binary32 partials, one binary32 destination,
-                             contiguous, optionally an element-wise or
-                             broadcast-row residual; chosen automatically) */
+                             contiguous, CHUNKED or SINGLE_SHOT, optionally
+                             an element-wise or broadcast-row residual;
+                             chosen automatically)                        */
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
     int    dst_bytes;     /* bytes per destination element                  */
     int    residual_kind; /* 0 none, 1 element-wise, 2 broadcast row        */

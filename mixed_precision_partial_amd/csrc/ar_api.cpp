@@ -399,17 +399,19 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
                 lds = src_wire && (((dst_narrow ? kLds16Narrow : kLds16ToF32) >> R) & 1u) != 0;
             }
             plan->stream_kernel = lds ? 2 : 1;
-            // the two-rank contiguous kernels for the commonest call: two
-            // active binary32 partials into one binary32 destination (with or
-            // without a residual), kept stores, the launch shape left to the
-            // library (prefill call 15.45 against 15.82 us with the
-            // register-staged kernel, 20.2 against 21.2-22.8 us with an
-            // element-wise residual, 15.6 against 16.4-17.3 us with a row;
-            // same machine, bit-identical outputs)
-            if (resolved == AR_MODE_CHUNKED && rows == nullptr && R == 2 && active == 0x3u && !src_wire &&
-                dst_bytes == 4 && !plan->store_nt && cfg.grid_wgs == 0) {
-                plan->stream_kernel = 3;
-            }
+        }
+        // the two-rank contiguous kernels for the commonest call: two active
+        // binary32 partials into one binary32 destination (with or without a
+        // residual), kept stores, the launch shape left to the library, chunked
+        // or single-shot (prefill call 15.45 against 15.82 us with the
+        // register-staged kernel, 20.2 against 21.2-22.8 us with an
+        // element-wise residual, 15.6 against 16.4-17.3 us with a row; a decode
+        // vector of 4096, replayed from a HIP graph, 1.68 against 1.74-1.78 us
+        // with the single-shot kernel; same machine, bit-identical outputs)
+        if ((resolved == AR_MODE_CHUNKED || resolved == AR_MODE_SINGLE_SHOT) && cfg.stream_kernel == 0 &&
+            rows == nullptr && R == 2 && active == 0x3u && !src_wire && dst_bytes == 4 && !plan->store_nt &&
+            cfg.grid_wgs == 0) {
+            plan->stream_kernel = 3;
         }
     }
     return AR_OK;

@@ -222,10 +222,16 @@ def test_stream_kernel_choice():
     broadcast schedule; host-staged calls
     LDS-staged for two 16-bit sources only; two active fp32 sources into one contiguous fp32
     destination, with or without a residual, kept stores and no forced grid take the two-rank
-    contiguous kernels (3)."""
+    contiguous kernels (3), chunked or single-shot."""
     n = 2048 * 4096
     CH, BC, HS, SW = ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED, ar.AR_SRC_WIRE
-    assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    # single-shot: the two-rank kernel for its case, the single-shot kernel otherwise
+    assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 3
+    assert q(4096, mode=ar.AR_MODE_AUTO)[1].stream_kernel == 3          # AUTO resolves to SINGLE_SHOT
+    assert q(4096, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT | ar.AR_SRC_WIRE)[1].stream_kernel == 0
+    assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT, config={"stream_kernel": 1})[1].stream_kernel == 0
+    assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT, config={"grid_wgs": 3})[1].stream_kernel == 0
     for R in (2, 3, 4, 8, 16):
         assert q(n, R=R, mode=CH)[1].stream_kernel == (3 if R == 2 else 1), R
     # the two-rank kernel only for its exact case: every wire type, automatic choice only
@@ -237,7 +243,7 @@ def test_stream_kernel_choice():
     assert q(n, mode=CH, config={"grid_wgs": 7})[1].stream_kernel == 1
     assert q(n, mode=CH, config={"store_policy": 2})[1].stream_kernel == 1
     assert q(n, srcs=[A[1], 0], mode=CH | ar.AR_SRC_INACTIVE_NULL)[1].stream_kernel == 1
-    assert q(n, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    assert q(n, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
     # with a residual (element-wise or a broadcast row): the two-rank kernels for R = 2
     # CHUNKED; the general kernels otherwise, and never for row-strided tensors
     res = [0x7_0000_0000]

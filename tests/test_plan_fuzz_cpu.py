@@ -121,16 +121,16 @@ def check_plan(plan, R, n, dst_type, wire_type, mode, srcs, resolved, res_kind, 
         return
     assert plan.chunk_elems >= 1
     assert plan.n_chunks == -(-n // plan.chunk_elems)
+    # the two-rank contiguous kernels: exactly two active binary32 partials (not flagged as
+    # wire-typed) into one binary32 destination, with or without a residual (kept stores, the
+    # default for that shape), chunked or single-shot
+    pair = (resolved in (ar.AR_MODE_CHUNKED, ar.AR_MODE_SINGLE_SHOT) and R == 2 and n_active == 2 and
+            not mode & ar.AR_SRC_WIRE and dst_type == F32)
+    assert (plan.stream_kernel == 3) == pair
     if resolved == ar.AR_MODE_SINGLE_SHOT:
-        assert plan.chunk_elems == n and plan.stream_kernel == 0
+        assert plan.chunk_elems == n and plan.stream_kernel == (3 if pair else 0)
     else:
         assert plan.chunk_elems % WAVE_TILE == 0 and plan.chunk_elems <= MAX_LAUNCH
-        # the two-rank contiguous kernels: exactly two active binary32 partials (not flagged
-        # as wire-typed) into one binary32 destination, with or without a residual (kept
-        # stores, the default for that shape)
-        pair = (resolved == ar.AR_MODE_CHUNKED and R == 2 and n_active == 2 and
-                not mode & ar.AR_SRC_WIRE and dst_type == F32)
-        assert (plan.stream_kernel == 3) == pair
         assert plan.stream_kernel in ((3,) if pair else (1, 2))
         if res_kind and not pair:
             # with a residual: LDS-staged for the broadcast schedule, register-staged otherwise
