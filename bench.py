@@ -505,6 +505,21 @@ def _csv_rows(directory: str, suffix: str):
         return list(csv.DictReader(fh))
 
 
+def _dispatch_rows(directory: str):
+    """Per-dispatch records of a rocprofv3 --kernel-trace output (kernel name, start and
+    end timestamps in ns, grid size in work-items)."""
+    try:
+        return _csv_rows(directory, "kernel_trace.csv")
+    except FileNotFoundError:
+        return []
+
+
+def prefill_grid_items(n: int) -> int:
+    """Work-items of the prefill call's launch: one 64-lane wave per 512-element wave tile
+    (the two-rank kernel's one-wave workgroups, the remainder in one more wave)."""
+    return (n + 511) // 512 * 64
+
+
 def _short(name: str) -> str:
     name = name.replace("(anonymous namespace)::", "").replace("mpp::", "").replace("|", "/")
     return name if len(name) <= 90 else name[:87] + "..."
@@ -527,11 +542,20 @@ def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
     algo = case_algo_bytes(case)
     if wl == "prefill_bf16":
-        red = [r for r in rows if is_reduce_kernel(r["Name"])]
-        if red:
-            avg_us = float(red[0]["AverageNs"]) / 1e3
-            lines += ["", f"Prefill reduce kernel `{REDUCE_KERNEL}`: average {avg_us:.3f} us per launch = "
-                          f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch)."]
+        # the default run also launches the same kernel for decode-sized calls and a 768 MiB
+        # call: the prefill call's own dispatches are those of its grid, taken from the
+        # per-dispatch records of the same trace
+        grid = prefill_grid_items(case["n"])
+        disp = [r for r in _dispatch_rows(directory)
+                if is_reduce_kernel(r["Kernel_Name"]) and int(r["Grid_Size_X"]) == grid]
+        if disp:
+            dur = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp])
+            avg_us = float(dur.mean())
+            lines += ["", f"Prefill reduce kernel `{REDUCE_KERNEL}` at the prefill call's grid ({grid} work-items): "
+                          f"{dur.size} dispatches, average {avg_us:.3f} us (median {float(np.median(dur)):.3f}, "
+                          f"min {float(dur.min()):.3f}, max {float(dur.max()):.3f}) = "
+                          f"{algo / avg_us / 1e3:.1f} GB/s of algorithmic bytes ({algo} B per launch). The "
+                          f"table's row for the kernel also holds its decode-sized and 768 MiB calls."]
     else:
         ours = [r for r in rows if is_library_kernel(r["Name"])]
         if ours:

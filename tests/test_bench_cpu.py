@@ -152,3 +152,28 @@ def test_kernel_hash_ignores_comments_not_code():
     assert bench.code_tokens(src) != bench.code_tokens(other)
     assert '"a // b /* c */"' in bench.code_tokens(src)
     assert bench.code_tokens("char c = '/'; // x") == "char c = '/';"
+
+
+def test_headline_trace_takes_the_prefill_grid_only(tmp_path, monkeypatch):
+    """The default run launches the prefill's kernel for decode-sized and 768 MiB calls too:
+    the headline average comes from the dispatches at the prefill call's grid."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    d = tmp_path / "trace"
+    os.makedirs(d)
+    name = "void mpp::(anonymous namespace)::k_pair<2>(unsigned int, unsigned int, float*, float const*, float const*, unsigned int)"
+    with open(d / "trace_kernel_stats.csv", "w") as fh:
+        fh.write('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n')
+        fh.write(f'"{name}",5,100000,20000,100.0,2000,60000,1\n')
+    grid = bench.prefill_grid_items(2048 * 4096)
+    assert grid == 1048576
+    rows = [(grid, 15_000), (grid, 16_000), (512, 2_000), (grid * 8, 60_000), (grid, 17_000)]
+    with open(d / "trace_kernel_trace.csv", "w") as fh:
+        fh.write('"Kernel_Name","Start_Timestamp","End_Timestamp","Workgroup_Size_X","Grid_Size_X"\n')
+        t = 1_000_000
+        for g, dur in rows:
+            fh.write(f'"{name}",{t},{t + dur},64,{g}\n')
+            t += 100_000
+    bench.summarize_trace(str(d), "prefill_bf16")
+    text = (tmp_path / "profiles" / "kernel_trace_prefill_bf16.md").read_text()
+    assert "3 dispatches, average 16.000 us" in text
