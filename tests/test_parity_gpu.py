@@ -226,14 +226,17 @@ def test_two_rank_contiguous_kernel(ctx):
     """The two-rank contiguous kernel (plan stream_kernel 3): every wire type, tiles with and
     without a remainder, grids below and above one placement run, the prefill size, in place."""
     for i, n in enumerate(PAIR_N):
-        rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_F32, ar.AR_BF16,
-                                    ar.AR_MODE_CHUNKED)
-        assert rc == ar.AR_OK and plan.stream_kernel == 3, (n, plan.stream_kernel)
-        for wire_name, wire in WIRES.items():
-            what = f"pair n={n} wire={wire_name}"
-            log_case(what)
-            srcs = wl.random_partials(9100 + i, wire, 2, n, dist="wide")
-            check_against_oracle(ctx, srcs, wire, ar.AR_MODE_CHUNKED, what=what)
+        # chunked at every size; single-shot (the decode form) at the smaller ones
+        modes = [("chunked", ar.AR_MODE_CHUNKED)] + ([("single_shot", ar.AR_MODE_SINGLE_SHOT)] if n <= 4097 else [])
+        for mode_name, mode in modes:
+            rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_F32,
+                                        ar.AR_BF16, mode)
+            assert rc == ar.AR_OK and plan.stream_kernel == 3, (n, mode_name, plan.stream_kernel)
+            for wire_name, wire in WIRES.items():
+                what = f"pair {mode_name} n={n} wire={wire_name}"
+                log_case(what)
+                srcs = wl.random_partials(9100 + i, wire, 2, n, dist="wide")
+                check_against_oracle(ctx, srcs, wire, mode, what=what)
     # in place: the destination is the first source
     n = (1 << 18) + 77
     srcs = wl.random_partials(9199, 0, 2, n, dist="normal+outliers")
