@@ -952,8 +952,9 @@ def ceilings(torch, stream, dev_src, dev_dst, n, sets, reps=300):
     buffers (GB/s of bytes moved): the reference kernels of libmpp_ceiling.so --
     a 16-byte copy (1 read : 1 write) and a 2-read : 1-write stream, each with
     every store policy, with the hardware's placement and with the reduce's XCD
-    runs -- and the runtime's device-to-device copy (torch copy_).  The
-    reduce is compared with the best 2-read : 1-write figure."""
+    runs, in 256-thread workgroups and in the one-wave workgroups the prefill's
+    own kernel uses -- and the runtime's device-to-device copy (torch copy_).
+    The reduce is compared with the best 2-read : 1-write figure."""
     import ctypes
 
     lib = ceiling_lib()
@@ -965,13 +966,14 @@ def ceilings(torch, stream, dev_src, dev_dst, n, sets, reps=300):
     for R, name in ((1, "copy_1r1w"), (2, "2r1w")):
         for sp, sp_name in ((0, "wb"), (1, "nt"), (2, "wt")):
             for run, run_name in ((0, "hw"), (512 << 10, "xcd512k")):
-                def fn(k, R=R, sp=sp, run=run):
-                    src, dst = arrays[k % sets]
-                    rc = lib.mpp_ceiling_launch(R, 1, sp, 256, src, dst, n * 4, run, sh)
-                    if rc != 0:
-                        raise RuntimeError(f"ceiling kernel launch failed ({rc})")
-                us = timed_us(torch, stream, fn, reps)
-                out[f"kernel_{name}_{sp_name}_{run_name}_GB/s"] = round((R + 1) * 4 * n / us / 1e3, 1)
+                for block, wg_name in ((256, ""), (64, "_wg64")):
+                    def fn(k, R=R, sp=sp, run=run, block=block):
+                        src, dst = arrays[k % sets]
+                        rc = lib.mpp_ceiling_launch(R, 1, sp, block, src, dst, n * 4, run, sh)
+                        if rc != 0:
+                            raise RuntimeError(f"ceiling kernel launch failed ({rc})")
+                    us = timed_us(torch, stream, fn, reps)
+                    out[f"kernel_{name}_{sp_name}_{run_name}{wg_name}_GB/s"] = round((R + 1) * 4 * n / us / 1e3, 1)
     us = timed_us(torch, stream, lambda k: dev_dst[k % sets].copy_(dev_src[k % sets][0]), reps)
     out["runtime_d2d_copy_GB/s"] = round(2 * 4 * n / us / 1e3, 1)
     log(f"ceilings at the prefill size: {out}")
