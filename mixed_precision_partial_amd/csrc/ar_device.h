@@ -1110,11 +1110,12 @@ MPP_STREAM_KERNELS(k_stream_lds_nts_sl, kLdsBlock, stream_lds, kStoreStream, tru
 // ---------------------------------------------------------------------------
 // Two-rank contiguous kernels: the commonest call -- two active binary32
 // partials, one binary32 destination, one contiguous range (the pages' own
-// tensor-parallel case is two ranks) -- as a 1-D grid whose parameters are
-// all a wave needs before its loads, every one preloaded into SGPRs: the tile
-// count, the remainder, the destination, the two sources and the placement
-// exponent (then, for the residual forms, the residual, its length and the
-// launch piece's phase in it).  A wave reduces one wave tile with the
+// tensor-parallel case is two ranks) -- as a 1-D grid whose leading
+// parameters are all a wave needs before its loads, every one preloaded into
+// SGPRs: the tile count, the remainder, the destination, the two sources and
+// the placement exponent (then, for the residual forms, the residual and its
+// length, also preloaded, and the launch piece's phase in the row, read from
+// the argument block while the partials' loads are in flight).  A wave reduces one wave tile with the
 // arithmetic of the streaming kernels' binary32 path (acc = wire(src0),
 // acc = RN32(acc + wire(src1)), then acc = RN32(acc + res[i]) with a
 // residual; write-through stores); the wave after the last tile reduces the
