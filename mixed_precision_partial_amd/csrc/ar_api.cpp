@@ -408,9 +408,18 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // element-wise residual, 15.6 against 16.4-17.3 us with a row; a decode
         // vector of 4096, replayed from a HIP graph, 1.68 against 1.74-1.78 us
         // with the single-shot kernel; same machine, bit-identical outputs)
+        // Row-strided tensors take them when every row is whole wave tiles and
+        // the strides fit 32 bits (a 2048 x 4096 block in rows of 4608 / 4352,
+        // same machine: 15.40 against 15.82 us on the register-staged kernel,
+        // 15.57 against 16.17 us with a bias row, 20.13 against 21.48-23.20 us
+        // with a strided element-wise residual; the general kernels' few
+        // workgroups per row keep the hardware's XCD order).
+        const bool pair_rows = rows != nullptr && rows->cols > 0 && rows->cols % mpp::kWaveTile == 0 &&
+                               rows->src_stride < (size_t(1) << 32) && rows->dst_stride < (size_t(1) << 32) &&
+                               rows->res_stride < (size_t(1) << 32);
         if ((resolved == AR_MODE_CHUNKED || resolved == AR_MODE_SINGLE_SHOT) && cfg.stream_kernel == 0 &&
-            rows == nullptr && R == 2 && active == 0x3u && !src_wire && dst_bytes == 4 && !plan->store_nt &&
-            cfg.grid_wgs == 0) {
+            (rows == nullptr || pair_rows) && R == 2 && active == 0x3u && !src_wire && dst_bytes == 4 &&
+            !plan->store_nt && cfg.grid_wgs == 0) {
             plan->stream_kernel = 3;
         }
     }
@@ -650,6 +659,24 @@ int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const
     const mpp::Types types = launch_types(plan, wire_type);
     const size_t sb = static_cast<size_t>(plan.src_bytes);
     const size_t db = static_cast<size_t>(plan.dst_bytes);
+    if (plan.stream_kernel == 3) {
+        // two-rank row-strided kernel: one 1-D launch per piece of whole rows
+        const int rk = res.ptr == nullptr ? 0 : (rw.res_stride == 0 ? 2 : 1);
+        const size_t piece = std::max<size_t>(1, mpp::kMaxLaunchElems / rw.cols);
+        for (size_t r0 = 0; r0 < rw.rows; r0 += piece) {
+            const size_t nr = std::min(piece, rw.rows - r0);
+            const void *rp = rk == 1 ? static_cast<const char *>(res.ptr) + r0 * rw.res_stride * db : res.ptr;
+            if (int rc = hip_status(mpp::launch_pair_rows(
+                    wire_type, rk, nr, rw.cols, rw.src_stride, rw.dst_stride,
+                    static_cast<char *>(dst[0]) + r0 * rw.dst_stride * db,
+                    static_cast<const char *>(srcs[0]) + r0 * rw.src_stride * sb,
+                    static_cast<const char *>(srcs[1]) + r0 * rw.src_stride * sb, rp, rw.res_stride,
+                    xcd_run_for(c->cfg, R, false), stream))) {
+                return rc;
+            }
+        }
+        return AR_OK;
+    }
     constexpr size_t kMaxRows = 65535;
     for (size_t r0 = 0; r0 < rw.rows; r0 += kMaxRows) {
         const size_t nr = std::min(kMaxRows, rw.rows - r0);

@@ -1236,6 +1236,58 @@ __global__ __launch_bounds__(kPairBlock) void k_pair_res(unsigned tiles, unsigne
     pair_body<W, RK>(tiles, rem, dst, src0, src1, lc, res, res_len, res_phase);
 }
 
+// Two-rank kernels over row-strided tensors whose rows are whole wave tiles
+// (cols a multiple of 512): the same per-tile work as the contiguous ones,
+// over one 1-D grid of every row's tiles, so that the XCD placement runs span
+// consecutive rows (a 2-D grid of a few workgroups per row would give each
+// XCD the same column block of every row: the hardware's one-by-one order).
+// Tile w is column block w mod tpr of row w / tpr (a shift when tpr, the
+// tiles per row, is a power of two: P2, `tpr` then holding its log2).  The
+// strides are in elements and below 2^32.  RK: 0 no residual, 1 an
+// element-wise residual with its own row stride, 2 one bias row of cols
+// elements (cached loads).
+template <int W, int RK, bool P2>
+__device__ __forceinline__ void pair_rows_body(unsigned tiles, unsigned tpr, unsigned src_stride,
+                                               unsigned dst_stride, float *dst, const float *src0,
+                                               const float *src1, unsigned lc, const float *res,
+                                               unsigned res_stride) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned w = xcd_virtual_block(blockIdx.x, tiles, lc);
+    if (w >= tiles) return;
+    const unsigned row = P2 ? w >> tpr : w / tpr;
+    const unsigned col = (w - (P2 ? row << tpr : row * tpr)) * kWaveTile;
+    const size_t s_off = static_cast<size_t>(row) * src_stride + col;
+    u32x4 a[2], b[2], r[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        a[j] = load16<true>(src0 + s_off + 256 * j + 4 * lane);
+        b[j] = load16<true>(src1 + s_off + 256 * j + 4 * lane);
+    }
+    if constexpr (RK == 1) {
+        const size_t r_off = static_cast<size_t>(row) * res_stride + col;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) r[j] = load16<true>(res + r_off + 256 * j + 4 * lane);
+    } else if constexpr (RK == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) r[j] = load16<false>(res + col + 256 * j + 4 * lane);
+    }
+    float *out = dst + static_cast<size_t>(row) * dst_stride + col;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        u32x4 v = pair_part<W>(a[j], b[j]);
+        if constexpr (RK != 0) v = add_res(v, r[j]);
+        store16_wt(out, kWaveTile * 4, (256 * j + 4 * lane) * 4, v);
+    }
+}
+
+template <int W, int RK, bool P2>
+__global__ __launch_bounds__(kPairBlock) void k_pair_rows(unsigned tiles, unsigned tpr, unsigned src_stride,
+                                                          unsigned dst_stride, float *dst, const float *src0,
+                                                          const float *src1, unsigned lc, const float *res,
+                                                          unsigned res_stride) {
+    pair_rows_body<W, RK, P2>(tiles, tpr, src_stride, dst_stride, dst, src0, src1, lc, res, res_stride);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1269,6 +1321,8 @@ typedef const void *const StreamTable[2][2][kCombos][kBuckets];
 extern const void *const kSingleShot[2][2][kCombos][kBuckets];
 // two-rank contiguous kernels, indexed by [residual kind][wire type (ar_dtype)]
 extern const void *const kPair[5][3];
+// two-rank row-strided kernels, [residual kind][power-of-two tiles per row][wire type]
+extern const void *const kPairRows[3][2][3];
 extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,
     kStreamLdsResM;
 

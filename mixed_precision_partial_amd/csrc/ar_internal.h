@@ -148,6 +148,16 @@ inline unsigned xcd_map_lc(unsigned grid_x, size_t wg_elems, size_t run_elems) {
 hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
                        const void *res, size_t res_len, size_t res_phase, size_t run_elems, hipStream_t stream);
 
+// The two-rank kernels over row-strided tensors (k_pair_rows): row i, column
+// j of the destination = wire(src0) + wire(src1) (+ the residual: res_kind 1
+// element-wise with its own row stride, 2 one bias row of cols elements) at
+// row i·stride + j of each tensor, for rows x cols elements (cols a multiple
+// of 512, rows·cols <= kMaxLaunchElems, strides in elements, below 2^32);
+// one 1-D launch on `stream`, XCD runs of about run_elems elements.
+hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
+                            void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
+                            size_t run_elems, hipStream_t stream);
+
 // Size of the library's static staging array (one per device), the only
 // device memory ar_reduce_staged_static uses beyond the caller's buffers.
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;

@@ -1,4 +1,5 @@
-// ar_k_pair.hip -- two-rank contiguous kernel instances: [residual kind][wire type].
+// ar_k_pair.hip -- two-rank kernel instances: contiguous [residual kind][wire type], row-strided
+// [residual kind][power-of-two tiles per row][wire type].
 #include "ar_device.h"
 
 namespace mpp {
@@ -12,5 +13,14 @@ const void *const kPair[5][3] = {{reinterpret_cast<const void *>(&k_pair<AR_F32>
                                  MPP_PAIR_ROW(1), MPP_PAIR_ROW(2), MPP_PAIR_ROW(3),
                                  MPP_PAIR_ROW(4)};
 #undef MPP_PAIR_ROW
+
+#define MPP_PAIR_ROWS_W(RK, P2)                                                           \
+    {reinterpret_cast<const void *>(&k_pair_rows<AR_F32, RK, P2>),                      \
+     reinterpret_cast<const void *>(&k_pair_rows<AR_F16, RK, P2>),                      \
+     reinterpret_cast<const void *>(&k_pair_rows<AR_BF16, RK, P2>)}
+#define MPP_PAIR_ROWS(RK) {MPP_PAIR_ROWS_W(RK, false), MPP_PAIR_ROWS_W(RK, true)}
+const void *const kPairRows[3][2][3] = {MPP_PAIR_ROWS(0), MPP_PAIR_ROWS(1), MPP_PAIR_ROWS(2)};
+#undef MPP_PAIR_ROWS
+#undef MPP_PAIR_ROWS_W
 
 }  // namespace mpp

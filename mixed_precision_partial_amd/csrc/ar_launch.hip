@@ -109,6 +109,32 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
     return hipLaunchKernel(kPair[kind][wire], dim3(grid), dim3(kPairBlock), args, 0, stream);
 }
 
+hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
+                            void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
+                            size_t run_elems, hipStream_t stream) {
+    if (wire < AR_F32 || wire > AR_BF16 || res_kind < 0 || res_kind > 2 || rows == 0 || cols == 0 ||
+        cols % kWaveTile != 0 || rows * cols > kMaxLaunchElems || src_stride < cols || dst_stride < cols ||
+        src_stride >= (size_t(1) << 32) || dst_stride >= (size_t(1) << 32) || res_stride >= (size_t(1) << 32)) {
+        return hipErrorInvalidValue;
+    }
+    if (res_kind != 0 && res == nullptr) return hipErrorInvalidValue;
+    if (res_kind == 1 && res_stride < cols) return hipErrorInvalidValue;
+    const size_t tpr = cols / kWaveTile;
+    unsigned tiles = static_cast<unsigned>(rows * tpr);
+    const bool p2 = (tpr & (tpr - 1)) == 0;
+    unsigned tpr_arg = static_cast<unsigned>(p2 ? __builtin_ctzll(tpr) : tpr);
+    unsigned ss = static_cast<unsigned>(src_stride), ds = static_cast<unsigned>(dst_stride);
+    unsigned rs = static_cast<unsigned>(res_kind == 1 ? res_stride : 0);
+    // one wave per workgroup: the grid is the tile count
+    unsigned lc = xcd_map_lc(tiles, kWaveTile, run_elems);
+    float *d = static_cast<float *>(dst);
+    const float *a = static_cast<const float *>(src0);
+    const float *b = static_cast<const float *>(src1);
+    const float *r = static_cast<const float *>(res);
+    void *args[] = {&tiles, &tpr_arg, &ss, &ds, &d, &a, &b, &lc, &r, &rs};
+    return hipLaunchKernel(kPairRows[res_kind][p2 ? 1 : 0][wire], dim3(tiles), dim3(kPairBlock), args, 0, stream);
+}
+
 hipError_t static_scratch(int device, void **out) {
     static std::mutex mu;
     static void *addr[kMaxStaticScratchDevices] = {};

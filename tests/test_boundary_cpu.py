@@ -245,7 +245,7 @@ def test_stream_kernel_choice():
     assert q(n, srcs=[A[1], 0], mode=CH | ar.AR_SRC_INACTIVE_NULL)[1].stream_kernel == 1
     assert q(n, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
     # with a residual (element-wise or a broadcast row): the two-rank kernels for R = 2
-    # CHUNKED; the general kernels otherwise, and never for row-strided tensors
+    # CHUNKED; the general kernels otherwise
     res = [0x7_0000_0000]
     for res_len in (n, 4096):
         rc, p = ar.ar_plan_query_add(A[20:21], A[1:3], n, ar.AR_F32, ar.AR_BF16, CH, res[0], res_len)
@@ -254,8 +254,14 @@ def test_stream_kernel_choice():
         assert rc == ar.AR_OK and p.stream_kernel == 1
         rc, p = ar.ar_plan_query_add(A[20:22], A[1:3], n, ar.AR_F32, ar.AR_BF16, BC, res[0], res_len)
         assert rc == ar.AR_OK and p.stream_kernel == 2
+    # row-strided: the two-rank kernels when every row is whole wave tiles
     rc, p = ar.ar_plan_query_rows(A[20:21], A[1:3], 2048, 4096, 4608, 4352, ar.AR_F32, ar.AR_BF16, CH,
                                   residual=res[0], res_stride=0)
+    assert rc == ar.AR_OK and p.stream_kernel == 3
+    rc, p = ar.ar_plan_query_rows(A[20:21], A[1:3], 2048, 4100, 4608, 4352, ar.AR_F32, ar.AR_BF16, CH,
+                                  residual=res[0], res_stride=0)
+    assert rc == ar.AR_OK and p.stream_kernel == 1
+    rc, p = ar.ar_plan_query_rows(A[20:21], A[1:4], 2048, 4096, 4608, 4352, ar.AR_F32, ar.AR_BF16, CH)
     assert rc == ar.AR_OK and p.stream_kernel == 1
     for R in range(2, 17):
         want16 = 2 if R in (2, 5, 6, 7, 8) else 1
@@ -389,7 +395,9 @@ def test_row_strided_rules():
     assert qr(4, 64, 72, 68, mode=ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE)[0] == ar.AR_OK
     # residual: element-wise stride or one broadcast row
     rc, p = qr(16, 4096, 4096, 4096, res=A[35], rs=4096)
-    assert rc == ar.AR_OK and p.residual_kind == 1 and p.stream_kernel == 1
+    assert rc == ar.AR_OK and p.residual_kind == 1 and p.stream_kernel == 3     # two-rank rows kernel
+    rc, p = qr(16, 4000, 4096, 4096, res=A[35], rs=4096)
+    assert rc == ar.AR_OK and p.residual_kind == 1 and p.stream_kernel == 1     # rows not whole tiles
     rc, p = qr(16, 4096, 4096, 4096, res=A[35], rs=0)
     assert rc == ar.AR_OK and p.residual_kind == 2
     assert p.algo_bytes == 2 * 16 * 4096 * 4 + 16 * 4096 * 4 + 4096 * 4

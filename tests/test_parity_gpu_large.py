@@ -149,3 +149,38 @@ def test_slice_broadcast_past_2_32(ctx):
     assert_bits_equal(gather(dsts[0], idx), want, "past 2^32 rs_bcast row residual")
     del dsts, srcs
     free()
+
+
+def test_beyond_one_launch_rows(ctx):
+    """Row-strided two-rank reduce of 2^18 + 3 rows of 4096 (past one launch: the rows are
+    cut into launch pieces of 2^18 rows) with padded strides and a bias row; sampled rows
+    around the piece boundary and at random against the oracle, and the padding after
+    them untouched."""
+    rows, cols, ss, ds = (1 << 18) + 3, 4096, 4096 + 64, 4096 + 128
+    rc, plan = ar.ar_plan_query_rows([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], rows, cols, ss, ds,
+                                     ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, residual=0x40_0000_0000,
+                                     res_stride=0)
+    assert rc == ar.AR_OK and plan.stream_kernel == 3
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20_003)
+    src_len, dst_len = (rows - 1) * ss + cols, (rows - 1) * ds + cols
+    srcs = [torch.randn(src_len, device="cuda", generator=g) for _ in range(2)]
+    bias = torch.randn(cols, device="cuda", generator=g)
+    out = torch.empty(dst_len, device="cuda")
+    out.fill_(float("nan"))
+    log_case(f"rows {rows}x{cols} strides {ss}/{ds} bias row, two-rank kernel in launch pieces")
+    ar.ar_reduce_rows(ctx, [out], srcs, rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                      residual=bias, res_stride=0)
+    torch.cuda.synchronize()
+    pick = np.unique(np.concatenate([np.arange(4), np.arange((1 << 18) - 3, (1 << 18) + 3),
+                                     np.arange(rows - 3, rows),
+                                     np.random.default_rng(9).integers(0, rows, 40)]))
+    idx_src = (pick[:, None] * ss + np.arange(cols)[None, :]).ravel()
+    idx_dst = (pick[:, None] * ds + np.arange(cols)[None, :]).ravel()
+    s_host = [gather(s, idx_src) for s in srcs]
+    want = oracle.reduce(s_host, ar.AR_BF16, residual=np.tile(bias.cpu().numpy(), pick.size))[0]
+    assert_bits_equal(gather(out, idx_dst), want, "rows beyond one launch")
+    gap = (pick[pick < rows - 1][:, None] * ds + cols + np.arange(ds - cols)[None, :]).ravel()
+    assert np.isnan(gather(out, gap)).all(), "written between rows"
+    del srcs, out
+    free()

@@ -154,6 +154,35 @@ def test_rows_residual_narrow_inactive(kctx, kname, mode_name):
                               dst_type=dst_type, res_kind=res_kind, rs=rs, active=active, seed=100 + i)
 
 
+# rows of whole wave tiles for the two-rank row-strided kernel: tiles per row a power of two
+# (shift) and not (division), dense and padded strides
+PAIR_SHAPES = [(9, 512, 520, 528, 536), (17, 1024, 1024, 1100, 1028), (5, 2560, 2568, 2560, 2576),
+               (4, 5120, 5200, 5124, 5120), (3, 7168, 7168, 7168, 7172), (100, 4096, 4608, 4352, 4160)]
+
+
+@pytest.mark.parametrize("mode_name", ["chunked", "single_shot"])
+def test_rows_two_rank_kernel(kctx, mode_name):
+    for i, (rows, cols, ss, ds, rs) in enumerate(PAIR_SHAPES):
+        rc, plan = ar.ar_plan_query_rows([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], rows, cols, ss, ds,
+                                         ar.AR_F32, ar.AR_BF16, MODES[mode_name])
+        assert rc == ar.AR_OK and plan.stream_kernel == 3, (rows, cols, plan.stream_kernel)
+        for wire_name, wire in WIRES.items():
+            for res_kind in (None, "strided", "row"):
+                what = f"rows two-rank {mode_name} {rows}x{cols} strides {ss}/{ds}/{rs} wire={wire_name} res={res_kind}"
+                run_rows_case(kctx["default"], rows, cols, ss, ds, 2, wire, MODES[mode_name], what,
+                              res_kind=res_kind, rs=rs, seed=200 + i)
+    # in place: the destination is the first source (equal strides)
+    rows, cols, st = 6, 1536, 1600
+    dense = wl.random_partials(30_300, 0, 2, rows * cols, dist="normal+outliers")
+    flats = [strided(rows, cols, st, d, np.float32(np.nan)) for d in dense]
+    want = oracle.reduce_rows(flats, ar.AR_BF16, rows, cols, st, st, dst_init=flats[0].copy())[0]
+    a, b = to_device(flats[0]), to_device(flats[1])
+    log_case(f"rows two-rank in place {rows}x{cols} stride {st}")
+    ar.ar_reduce_rows(kctx["default"], [a], [a, b], rows, cols, st, st, ar.AR_F32, ar.AR_BF16, MODES[mode_name])
+    torch.cuda.synchronize()
+    assert_bits_equal(a.cpu().numpy(), want, "rows two-rank in place")
+
+
 def test_rows_empty_and_errors(kctx):
     c = kctx["default"]
     dev = [to_device(np.ones(64, dtype=np.float32)) for _ in range(2)]

@@ -346,6 +346,12 @@ def test_plan_query_rows_matches_rules(args, shape, data):
     if n == 0:
         assert plan.n_chunks == 0
         return
+    # the two-rank row-strided kernels: two active binary32 partials into one binary32
+    # destination, rows of whole wave tiles, strides below 2^32 elements
+    pair = (resolved in (ar.AR_MODE_CHUNKED, ar.AR_MODE_SINGLE_SHOT) and R == 2 and n_active == 2 and
+            not mode & ar.AR_SRC_WIRE and dst_type == F32 and cols % WAVE_TILE == 0 and
+            max(ss, ds, rs) < (1 << 32))
+    assert (plan.stream_kernel == 3) == pair
     # device schedules: one range per row; host-staged copies move whole rows
     assert plan.chunk_elems % cols == 0
     chunk_rows = plan.chunk_elems // cols
