@@ -256,7 +256,8 @@ int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *sr
  * of ar_reduce; residual NULL, residual_len 0 or not dividing n ->
  * AR_ERR_INVALID (n = 0 is a no-op and checks only residual != NULL).  Calls
  * with a residual run on the two-rank kernels (two fp32 partials into one
- * fp32 destination, CHUNKED), on the LDS-staged kernels in the broadcast
+ * fp32 destination, CHUNKED or SINGLE_SHOT), on the single-shot kernel in
+ * other SINGLE_SHOT calls, on the LDS-staged kernels in the broadcast
  * schedule, and on the register-staged kernels otherwise (unless
  * stream_kernel forces a family). */
 int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
@@ -334,9 +335,10 @@ typedef struct {
     int    store_nt;      /* 1: streaming (non-temporal) destination stores */
     int    host_direct;   /* HOST_STAGED: 1 = kernel reads host memory directly */
     int    stream_kernel; /* 0 single-shot, 1 register-staged, 2 LDS-staged,
-                             3 the two-rank contiguous kernel (two active
-                             binary32 partials, one binary32 destination,
-                             contiguous, CHUNKED or SINGLE_SHOT, optionally
+                             3 the two-rank kernels (two active binary32
+                             partials, one binary32 destination, contiguous
+                             or rows of whole 512-element tiles with strides
+                             below 2^32, CHUNKED or SINGLE_SHOT, optionally
                              an element-wise or broadcast-row residual;
                              chosen automatically)                        */
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
