@@ -187,6 +187,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--summarize-trace", metavar="DIR",
                    help="write profiles/ summary of a rocprofv3 --kernel-trace --stats output dir")
+    p.add_argument("--summarize-pass-trace", metavar="DIR",
+                   help="the same for a traced --profile-pass of the prefill reduce (the prefill's own "
+                        "summary describes the traced default run), written as "
+                        "profiles/kernel_trace_prefill_bf16_profile_pass.md")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/ HBM-traffic summary from two rocprofv3 --pmc runs "
                         "(FETCH_SIZE, WRITE_SIZE) of --profile-pass")
@@ -211,9 +215,11 @@ def parse():
 
 def main() -> int:
     args = parse()
-    if args.summarize_trace or args.summarize_pmc or args.summarize_counters:
+    if args.summarize_trace or args.summarize_pass_trace or args.summarize_pmc or args.summarize_counters:
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, args.profile_workload)
+        if args.summarize_pass_trace:
+            summarize_trace(args.summarize_pass_trace, "prefill_bf16", bench_run=False)
         if args.summarize_pmc:
             summarize_pmc(*args.summarize_pmc, args.profile_workload)
         if args.summarize_counters:
@@ -525,11 +531,17 @@ def _short(name: str) -> str:
     return name if len(name) <= 90 else name[:87] + "..."
 
 
-def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
+def summarize_trace(directory: str, wl: str = "prefill_bf16", bench_run: bool | None = None) -> None:
+    """profiles/kernel_trace_<wl>.md from a rocprofv3 kernel-trace directory: the traced
+    default bench run for the prefill reduce, a traced --profile-pass otherwise
+    (``bench_run=False`` for a profile pass of the prefill reduce, written under its
+    own name)."""
     case = PROFILE_CASES[wl]
+    bench_run = wl == "prefill_bf16" if bench_run is None else bench_run
     rows = _csv_rows(directory, "kernel_stats.csv")
-    out = os.path.join(ROOT, "profiles", f"kernel_trace_{wl}.md")
-    if wl == "prefill_bf16":
+    name = wl if bench_run or wl != "prefill_bf16" else f"{wl}_profile_pass"
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
+    if bench_run:
         title = "# rocprofv3 kernel trace: bench.py default run (prefill reduce + decode calls)"
         cmd = TRACE_CMD
     else:
@@ -541,7 +553,7 @@ def summarize_trace(directory: str, wl: str = "prefill_bf16") -> None:
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
     algo = case_algo_bytes(case)
-    if wl == "prefill_bf16":
+    if bench_run:
         # the default run also launches the same kernel for decode-sized calls and a 768 MiB
         # call: the prefill call's own dispatches are those of its grid, taken from the
         # per-dispatch records of the same trace

@@ -177,3 +177,10 @@ def test_headline_trace_takes_the_prefill_grid_only(tmp_path, monkeypatch):
     bench.summarize_trace(str(d), "prefill_bf16")
     text = (tmp_path / "profiles" / "kernel_trace_prefill_bf16.md").read_text()
     assert "3 dispatches, average 16.000 us" in text
+    # a traced profile pass of the same call is summarised under its own name, from the
+    # kernel statistics (every dispatch there is the prefill call), without touching the above
+    bench.summarize_trace(str(d), "prefill_bf16", bench_run=False)
+    pass_text = (tmp_path / "profiles" / "kernel_trace_prefill_bf16_profile_pass.md").read_text()
+    assert "profile pass of" in pass_text and "--profile-workload prefill_bf16" in pass_text
+    assert "average 20.000 us per launch" in pass_text
+    assert (tmp_path / "profiles" / "kernel_trace_prefill_bf16.md").read_text() == text
