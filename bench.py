@@ -930,16 +930,21 @@ def ceiling_lib():
     lib = ctypes.CDLL(CEILING_LIB)
     vp = ctypes.c_void_p
     lib.mpp_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
-                                       ctypes.POINTER(vp), ctypes.c_size_t, ctypes.c_size_t, vp]
+                                       ctypes.POINTER(vp), ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, vp]
     lib.mpp_ceiling_launch.restype = ctypes.c_int
     return lib
+
+
+# resident waves per CU the ceiling kernels are also timed at (0: not held); the
+# reduce's two-rank kernels are held to 18 (no residual) and 14 (residual)
+CEILING_HOLDS = (0, 10, 14, 18)
 
 
 def pattern_ceiling(torch, stream, R, D, src_sets, dst_sets, nbytes, reps):
     """Best GB/s (bytes moved) of the ceiling kernel with the (R reads, D writes)
     pattern over the given rotated tensors, `nbytes` per stream: 256- and
     64-thread workgroups, every store policy, without and with XCD runs of
-    512 KiB and 1 MiB."""
+    512 KiB and 1 MiB, each CU unheld and held to CEILING_HOLDS resident waves."""
     import ctypes
 
     lib = ceiling_lib()
@@ -951,11 +956,12 @@ def pattern_ceiling(torch, stream, R, D, src_sets, dst_sets, nbytes, reps):
     for block in (256, 64):
         for sp in (0, 1, 2):
             for run in (0, 512 << 10, 1 << 20):
-                def fn(k, sp=sp, run=run, block=block):
-                    a, b = arrays[k % len(arrays)]
-                    if lib.mpp_ceiling_launch(R, D, sp, block, a, b, nbytes, run, sh) != 0:
-                        raise RuntimeError("ceiling kernel launch failed")
-                best = max(best, (R + D) * nbytes / timed_us(torch, stream, fn, reps) / 1e3)
+                for hold in CEILING_HOLDS:
+                    def fn(k, sp=sp, run=run, block=block, hold=hold):
+                        a, b = arrays[k % len(arrays)]
+                        if lib.mpp_ceiling_launch(R, D, sp, block, a, b, nbytes, run, hold, sh) != 0:
+                            raise RuntimeError("ceiling kernel launch failed")
+                    best = max(best, (R + D) * nbytes / timed_us(torch, stream, fn, reps) / 1e3)
     return round(best, 1)
 
 
@@ -965,8 +971,9 @@ def ceilings(torch, stream, dev_src, dev_dst, n, sets, reps=300):
     a 16-byte copy (1 read : 1 write) and a 2-read : 1-write stream, each with
     every store policy, with the hardware's placement and with the reduce's XCD
     runs, in 256-thread workgroups and in the one-wave workgroups the prefill's
-    own kernel uses -- and the runtime's device-to-device copy (torch copy_).
-    The reduce is compared with the best 2-read : 1-write figure."""
+    own kernel uses, each CU unheld and held to CEILING_HOLDS resident waves
+    (key suffix _hold<waves>) -- and the runtime's device-to-device copy (torch
+    copy_).  The reduce is compared with the best 2-read : 1-write figure."""
     import ctypes
 
     lib = ceiling_lib()
@@ -979,13 +986,15 @@ def ceilings(torch, stream, dev_src, dev_dst, n, sets, reps=300):
         for sp, sp_name in ((0, "wb"), (1, "nt"), (2, "wt")):
             for run, run_name in ((0, "hw"), (512 << 10, "xcd512k")):
                 for block, wg_name in ((256, ""), (64, "_wg64")):
-                    def fn(k, R=R, sp=sp, run=run, block=block):
-                        src, dst = arrays[k % sets]
-                        rc = lib.mpp_ceiling_launch(R, 1, sp, block, src, dst, n * 4, run, sh)
-                        if rc != 0:
-                            raise RuntimeError(f"ceiling kernel launch failed ({rc})")
-                    us = timed_us(torch, stream, fn, reps)
-                    out[f"kernel_{name}_{sp_name}_{run_name}{wg_name}_GB/s"] = round((R + 1) * 4 * n / us / 1e3, 1)
+                    for hold in CEILING_HOLDS:
+                        def fn(k, R=R, sp=sp, run=run, block=block, hold=hold):
+                            src, dst = arrays[k % sets]
+                            rc = lib.mpp_ceiling_launch(R, 1, sp, block, src, dst, n * 4, run, hold, sh)
+                            if rc != 0:
+                                raise RuntimeError(f"ceiling kernel launch failed ({rc})")
+                        us = timed_us(torch, stream, fn, reps)
+                        key = f"kernel_{name}_{sp_name}_{run_name}{wg_name}{f'_hold{hold}' if hold else ''}_GB/s"
+                        out[key] = round((R + 1) * 4 * n / us / 1e3, 1)
     us = timed_us(torch, stream, lambda k: dev_dst[k % sets].copy_(dev_src[k % sets][0]), reps)
     out["runtime_d2d_copy_GB/s"] = round(2 * 4 * n / us / 1e3, 1)
     log(f"ceilings at the prefill size: {out}")

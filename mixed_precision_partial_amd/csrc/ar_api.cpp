@@ -431,6 +431,7 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
 struct ar_ctx {
     int device = -1;
     int cu_count = 0;
+    unsigned lds_per_cu = 0;   // LDS bytes per CU (0: unknown)
     Config cfg;
     hipStream_t copy_stream = nullptr;
     // host-staged scratch ring: slots x R x chunk source elements
@@ -453,6 +454,10 @@ struct ar_ctx {
 };
 
 namespace {
+
+mpp::CuLimits cu_limits(const ar_ctx *c) {
+    return mpp::CuLimits{static_cast<unsigned>(c->cu_count), c->lds_per_cu};
+}
 
 // Makes `dev` current for the scope and restores the caller's device; no
 // runtime call beyond the query when `dev` is already current (the common
@@ -612,7 +617,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
                                                      static_cast<const char *>(srcs[0]) + p0 * sb,
                                                      static_cast<const char *>(srcs[1]) + p0 * sb, rp,
                                                      rk == 2 ? res.len : 0, rk == 2 ? p0 % res.len : 0,
-                                                     xcd_run_for(c->cfg, R, false), stream))) {
+                                                     xcd_run_for(c->cfg, R, false), cu_limits(c), stream))) {
                 return rc;
             }
         }
@@ -671,7 +676,7 @@ int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const
                     static_cast<char *>(dst[0]) + r0 * rw.dst_stride * db,
                     static_cast<const char *>(srcs[0]) + r0 * rw.src_stride * sb,
                     static_cast<const char *>(srcs[1]) + r0 * rw.src_stride * sb, rp, rw.res_stride,
-                    xcd_run_for(c->cfg, R, false), stream))) {
+                    xcd_run_for(c->cfg, R, false), cu_limits(c), stream))) {
                 return rc;
             }
         }
@@ -947,6 +952,14 @@ AR_API int ar_init(ar_ctx **out, int hip_device, const ar_config *cfg) {
     if (hipDeviceGetAttribute(&c->cu_count, hipDeviceAttributeMultiprocessorCount, hip_device) != hipSuccess ||
         c->cu_count <= 0) {
         rc = AR_ERR_RUNTIME;
+    }
+    // LDS per CU, for the two-rank kernels' occupancy hold (left at 0, no
+    // hold, when the runtime does not report it)
+    int lds_cu = 0;
+    if (rc == AR_OK &&
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, hip_device) == hipSuccess &&
+        lds_cu > 0) {
+        c->lds_per_cu = static_cast<unsigned>(lds_cu);
     }
     if (rc == AR_OK && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess) {
         c->copy_stream = nullptr;

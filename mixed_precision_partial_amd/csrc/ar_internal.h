@@ -139,24 +139,57 @@ inline unsigned xcd_map_lc(unsigned grid_x, size_t wg_elems, size_t run_elems) {
     return lc;
 }
 
+// A device's CU count and LDS bytes per CU, for launches that hold a CU below
+// its full wave occupancy.
+struct CuLimits {
+    unsigned cu_count;
+    unsigned lds_bytes;   // 0: unknown (no hold)
+};
+
+// Dynamic LDS per one-wave workgroup that lets at most `waves` of them reside
+// on a CU; the kernel never touches it.  0 (no hold) when the CU's LDS is
+// unknown or the grid's `wgs` workgroups would not fill every CU to `waves`
+// anyway.  The bytes are the smallest multiple of 512 with
+// floor(lds_bytes / bytes) == waves.
+inline unsigned hold_lds_bytes(const CuLimits &cu, uint64_t wgs, unsigned waves) {
+    if (waves == 0 || cu.lds_bytes == 0 || cu.cu_count == 0) return 0;
+    if (wgs < uint64_t(cu.cu_count) * waves) return 0;
+    const unsigned bytes = (cu.lds_bytes / (waves + 1) / 512u + 1u) * 512u;
+    return bytes <= 65536u && cu.lds_bytes / bytes == waves ? bytes : 0u;
+}
+
+// Resident waves per CU the two-rank kernels are held to, without and with a
+// residual.  One-wave workgroups would otherwise fill a CU to 32 waves; fewer
+// loads in flight per CU stream faster on MI355X (prefill call, 2 x [2048 x
+// 4096] fp32 -> fp32, bf16 wire, on two boxes: 15.30-15.33 us held at 16-20
+// waves against 15.45-15.52 us unheld; with an element-wise residual
+// 19.68-19.80 us at 14 against 20.12-20.22; with a 4096-element row
+// 15.46-15.47 us at 14 against 15.70-15.74; a plain call held at 14 ran
+// 15.49 us, a residual call held at 18 19.93-20.06 us: bit-identical outputs).
+constexpr unsigned kPairWaves = 18;
+constexpr unsigned kPairResWaves = 14;
+
 // The two-rank contiguous kernels (k_pair, k_pair_res): dst[i] = wire(src0[i])
 // + wire(src1[i]) in binary32, then + res[i] (res_kind 1, element-wise) or
 // + res[(i + res_phase) mod res_len] (res_kind 2, a broadcast row of res_len
 // elements, a multiple of 8, res_phase < res_len), for i < n (n <=
 // kMaxLaunchElems); one 1-D launch on `stream`, XCD runs of about run_elems
-// elements.  Every pointer is a binary32 device array, 16-byte aligned.
+// elements, CUs held to kPairWaves / kPairResWaves resident waves.  Every
+// pointer is a binary32 device array, 16-byte aligned.
 hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
-                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, hipStream_t stream);
+                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, const CuLimits &cu,
+                       hipStream_t stream);
 
 // The two-rank kernels over row-strided tensors (k_pair_rows): row i, column
 // j of the destination = wire(src0) + wire(src1) (+ the residual: res_kind 1
 // element-wise with its own row stride, 2 one bias row of cols elements) at
 // row i·stride + j of each tensor, for rows x cols elements (cols a multiple
 // of 512, rows·cols <= kMaxLaunchElems, strides in elements, below 2^32);
-// one 1-D launch on `stream`, XCD runs of about run_elems elements.
+// one 1-D launch on `stream`, XCD runs of about run_elems elements, CUs held
+// as launch_pair holds them.
 hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
                             void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
-                            size_t run_elems, hipStream_t stream);
+                            size_t run_elems, const CuLimits &cu, hipStream_t stream);
 
 // Size of the library's static staging array (one per device), the only
 // device memory ar_reduce_staged_static uses beyond the caller's buffers.

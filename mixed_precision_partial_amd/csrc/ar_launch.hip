@@ -83,7 +83,8 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 }  // namespace
 
 hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
-                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, hipStream_t stream) {
+                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, const CuLimits &cu,
+                       hipStream_t stream) {
     if (wire < AR_F32 || wire > AR_BF16 || res_kind < 0 || res_kind > 2 || n == 0 || n > kMaxLaunchElems) {
         return hipErrorInvalidValue;
     }
@@ -106,12 +107,13 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
     // row kinds: 4 a power of two, 2 at least one wave tile, 3 shorter
     const int kind = res_kind < 2 ? res_kind : ((res_len & (res_len - 1)) == 0 ? 4 : (res_len >= kWaveTile ? 2 : 3));
     void *args[] = {&tiles, &rem, &d, &a, &b, &lc, &r, &rl, &ph};
-    return hipLaunchKernel(kPair[kind][wire], dim3(grid), dim3(kPairBlock), args, 0, stream);
+    const unsigned hold = hold_lds_bytes(cu, grid, res_kind == 0 ? kPairWaves : kPairResWaves);
+    return hipLaunchKernel(kPair[kind][wire], dim3(grid), dim3(kPairBlock), args, hold, stream);
 }
 
 hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
                             void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
-                            size_t run_elems, hipStream_t stream) {
+                            size_t run_elems, const CuLimits &cu, hipStream_t stream) {
     if (wire < AR_F32 || wire > AR_BF16 || res_kind < 0 || res_kind > 2 || rows == 0 || cols == 0 ||
         cols % kWaveTile != 0 || rows * cols > kMaxLaunchElems || src_stride < cols || dst_stride < cols ||
         src_stride >= (size_t(1) << 32) || dst_stride >= (size_t(1) << 32) || res_stride >= (size_t(1) << 32)) {
@@ -132,7 +134,8 @@ hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, si
     const float *b = static_cast<const float *>(src1);
     const float *r = static_cast<const float *>(res);
     void *args[] = {&tiles, &tpr_arg, &ss, &ds, &d, &a, &b, &lc, &r, &rs};
-    return hipLaunchKernel(kPairRows[res_kind][p2 ? 1 : 0][wire], dim3(tiles), dim3(kPairBlock), args, 0, stream);
+    const unsigned hold = hold_lds_bytes(cu, tiles, res_kind == 0 ? kPairWaves : kPairResWaves);
+    return hipLaunchKernel(kPairRows[res_kind][p2 ? 1 : 0][wire], dim3(tiles), dim3(kPairBlock), args, hold, stream);
 }
 
 hipError_t static_scratch(int device, void **out) {

@@ -111,15 +111,20 @@ int pattern_index(int R, int D) {
 // memory, 16-byte aligned, `bytes` long; `bytes` is a multiple of 2048 and at
 // most 2^31 tiles.  `block`: 256 or 64 threads per workgroup.  `run_bytes`:
 // XCD placement runs of about this many bytes of every stream (0 = the
-// hardware's own placement).  Returns 0 when enqueued, 1 for an unsupported
-// or invalid request (nothing enqueued), 4 for a HIP error.
+// hardware's own placement).  `waves_per_cu`: 0, or hold every CU to that
+// many resident waves (rounded down to whole workgroups) with dynamic LDS the
+// kernel does not use, as the reduce's two-rank kernels are held.  Returns 0
+// when enqueued, 1 for an unsupported or invalid request (nothing enqueued),
+// 4 for a HIP error.
 extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, int D, int store_policy, int block,
                                                                          const void *const *srcs,
                                                                          void *const *dsts, size_t bytes,
-                                                                         size_t run_bytes, void *stream) {
+                                                                         size_t run_bytes, int waves_per_cu,
+                                                                         void *stream) {
     const int p = pattern_index(R, D);
     if (p < 0 || store_policy < 0 || store_policy > 2 || srcs == nullptr || dsts == nullptr) return 1;
     if (block != 256 && block != 64) return 1;
+    if (waves_per_cu < 0 || waves_per_cu > 64) return 1;
     if (bytes == 0 || bytes % kTileBytes != 0 || bytes / kTileBytes >= (size_t(1) << 31)) return 1;
     const char *s[kMaxR] = {};
     char *d[kMaxD] = {};
@@ -135,8 +140,19 @@ extern "C" __attribute__((visibility("default"))) int mpp_ceiling_launch(int R, 
     const unsigned wpb = static_cast<unsigned>(block) / 64;
     const unsigned grid = (tiles + wpb - 1) / wpb;
     unsigned lc = mpp::xcd_map_lc(grid, size_t(wpb) * kTileBytes, run_bytes);
+    unsigned hold = 0;
+    if (waves_per_cu > 0) {
+        int dev = 0, cus = 0, lds = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess) {
+            return 4;
+        }
+        const mpp::CuLimits cu{static_cast<unsigned>(cus), static_cast<unsigned>(lds)};
+        hold = mpp::hold_lds_bytes(cu, grid, static_cast<unsigned>(waves_per_cu) / wpb);
+    }
     void *args[] = {&tiles, &lc, &d[0], &s[0], &s[1], &s[2], &s[3], &s[4], &s[5], &s[6], &s[7], &d[1], &d[2], &d[3]};
     const hipError_t e = hipLaunchKernel(kPatterns[block == 64 ? 1 : 0][p][store_policy], dim3(grid), dim3(block),
-                                         args, 0, static_cast<hipStream_t>(stream));
+                                         args, hold, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : 4;
 }

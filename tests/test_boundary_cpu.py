@@ -573,6 +573,24 @@ def test_xcd_placement_map_is_a_permutation(tmp_path):
     assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr
 
 
+def test_occupancy_hold_bytes(tmp_path):
+    """tests/c_abi/hold_check.cpp, built with hipcc as host code against the
+    library's internal header: the dynamic LDS that holds a CU to N one-wave
+    workgroups is the smallest multiple of 512 bytes giving exactly N per CU,
+    and no hold is asked for when the grid would not fill the CUs to N."""
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "hold_check")
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    cmd = [hipcc, "-O1", "-std=c++17", "-I", os.path.join(root, "include"),
+           "-I", os.path.join(root, "mixed_precision_partial_amd", "csrc"),
+           os.path.join(root, "tests", "c_abi", "hold_check.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr
+
+
 def test_binding_refuses_short_pointer_lists():
     """The library reads R destination pointers in the broadcast schedule (and R
     source pointers always): the binding refuses shorter lists before the call,
