@@ -203,6 +203,11 @@ def parse():
                         "4096-element broadcast-row residual, on the automatically chosen kernel against the "
                         "register- and LDS-staged general kernels and against the hardware's workgroup "
                         "placement, interleaved in one process (bit-identical outputs checked); one JSON line")
+    p.add_argument("--hold-study", action="store_true",
+                   help="instead of the benchmark: the two-rank calls (prefill plain / residual / row and the "
+                        "row-strided block) and three general-kernel calls (cfg 4, the bf16 -> bf16 prefill "
+                        "shape, R = 8 fp32) by occupancy hold, interleaved in one process (bit-identical "
+                        "outputs checked); one JSON line")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="write profiles/counters_<workload>.md from the rocprofv3 --pmc runs of COUNTER_PASSES")
     p.add_argument("--profile-pass", action="store_true",
@@ -245,6 +250,8 @@ def main() -> int:
         return timing_study(torch, ar, wl, args)
     if args.family_study:
         return family_study(torch, ar, wl, args)
+    if args.hold_study:
+        return hold_study(torch, ar, wl, args)
     w = wl.WORKLOADS["prefill_bf16"]
     R, n = w.R, w.n
     S = max(1, args.sets)
@@ -858,6 +865,108 @@ def family_study(torch, ar, wl, args, reps: int = 7, calls: int = 1000) -> int:
     log("plain, second sources shifted 1 MiB: " + ", ".join(
         f"{k} {v['us_median']} us" for k, v in out["plain_second_source_shifted_1MiB"].items()))
     del big, moved
+    torch.cuda.synchronize()
+    for c in ctxs.values():
+        ar.ar_free(c)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def hold_study(torch, ar, wl, args, reps: int = 7) -> int:
+    """The occupancy hold (ar_config.occupancy_hold), measured: the prefill call (plain,
+    element-wise residual, 4096-element broadcast row) and the row-strided prefill block
+    (2048 x 4096 in rows of 4608 / 4352: plain, strided residual, bias row), each on the
+    two-rank kernels unheld (-1), held to 14, 16, 18 or 20 waves per CU, and automatic (0);
+    the 4-rank broadcast (cfg 4), the bf16 -> bf16 prefill shape and R = 8 fp32 partials on
+    their automatic general kernels unheld and held to 8, 12 or 16 waves.  Outputs are
+    compared bit for bit across holds before timing; holds are timed interleaved, rep by
+    rep, medians reported.  One JSON line."""
+    stream = torch.cuda.current_stream()
+    holds = sorted({-1, 0, 8, 12, 14, 16, 18, 20})
+    ctxs = {h: ar.ar_init(0, {"occupancy_hold": h} if h else None) for h in holds}
+    out = {"metric": "us per call by occupancy hold (waves per CU; -1 none, 0 automatic)", "reps": reps}
+
+    def measure(name, hs, calls, fn, nbytes, check):
+        """fn(h, k) enqueues call k under hold h; check() returns the output bits of call 0."""
+        ref = None
+        for h in hs:
+            fn(h, 0)
+            torch.cuda.synchronize()
+            bits = check().clone()
+            if ref is None:
+                ref = bits
+            elif not torch.equal(bits, ref):
+                raise RuntimeError(f"{name}: hold {h} changes the output")
+        times = {h: [] for h in hs}
+        for _ in range(reps):
+            for h in hs:
+                times[h].append(timed_us(torch, stream, lambda k, h=h: fn(h, k), calls))
+        out[name] = {str(h): {"us_median": round(float(np.median(v)), 3), "us_min": round(min(v), 3),
+                              "GB/s": round(nbytes / float(np.median(v)) / 1e3, 1)} for h, v in times.items()}
+        log(f"{name}: " + ", ".join(f"{h}: {out[name][str(h)]['us_median']}" for h in hs))
+
+    pair_holds = [-1, 14, 16, 18, 20, 0]
+    w = wl.WORKLOADS["prefill_bf16"]
+    n, S = w.n, max(1, args.sets)
+    src = [[torch.from_numpy(p).cuda() for p in wl.partials(w, s)] for s in range(S)]
+    dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(S)]
+    res = [torch.from_numpy(wl.residual(w.case, s, n)).cuda() for s in range(S)]
+    row = torch.from_numpy(wl.residual(w.case, S, 4096)).cuda()
+    bound = {}
+    for h, c in ctxs.items():
+        for form in ("plain", "residual", "row"):
+            bound[(h, form)] = [ar.bind_reduce(c, [dst[s]], src[s], n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                               stream=stream,
+                                               residual={"plain": None, "residual": res[s], "row": row}[form])
+                                for s in range(S)]
+    for form, nbytes in (("plain", 12 * n), ("residual", 16 * n), ("row", 12 * n + 4 * 4096)):
+        measure(f"prefill_{form}", pair_holds, 1000, lambda h, k, form=form: bound[(h, form)][k % S](), nbytes,
+                lambda: dst[0].view(torch.int32))
+    del src, dst, res, bound
+    torch.cuda.empty_cache()
+    rows, cols, ss, ds = 2048, 4096, 4608, 4352
+    R6 = 6
+    rs_src = [[torch.randn(rows * ss, device="cuda") for _ in range(2)] for _ in range(R6)]
+    rs_dst = [torch.empty(rows * ds, device="cuda") for _ in range(R6)]
+    rs_res = [torch.randn(rows * ss, device="cuda") for _ in range(R6)]
+    bias = torch.randn(cols, device="cuda")
+    for form, nbytes in (("plain", 12 * rows * cols), ("residual", 16 * rows * cols),
+                         ("bias_row", 12 * rows * cols + 4 * cols)):
+        def call(h, k, form=form):
+            i = k % R6
+            r = {"plain": None, "residual": rs_res[i], "bias_row": bias}[form]
+            ar.ar_reduce_rows(ctxs[h], [rs_dst[i]], rs_src[i], rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16,
+                              ar.AR_MODE_CHUNKED, residual=r, res_stride=ss if form == "residual" else 0,
+                              stream=stream)
+        measure(f"rows_block_{form}", pair_holds, 1000, call, nbytes, lambda: rs_dst[0].view(torch.int32))
+    del rs_src, rs_dst, rs_res
+    torch.cuda.empty_cache()
+    gen_holds = [-1, 8, 12, 16]
+    n4 = 2048 * 8192
+    b4_src = [[torch.randn(n4, device="cuda") for _ in range(4)] for _ in range(2)]
+    b4_dst = [[torch.empty(n4, device="cuda") for _ in range(4)] for _ in range(2)]
+    measure("slice_bcast_f16", gen_holds, 50,
+            lambda h, k: ar.ar_reduce(ctxs[h], b4_dst[k % 2], b4_src[k % 2], n4, ar.AR_F32, ar.AR_F16,
+                                      ar.AR_MODE_RS_BCAST, stream=stream),
+            8 * n4 * 4, lambda: b4_dst[0][3].view(torch.int32))
+    del b4_src, b4_dst
+    torch.cuda.empty_cache()
+    h_src = [[torch.randn(n, device="cuda").bfloat16() for _ in range(2)] for _ in range(S)]
+    h_dst = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    measure("prefill_bf16_dst", gen_holds, 500,
+            lambda h, k: ar.ar_reduce(ctxs[h], [h_dst[k % S]], h_src[k % S], n, ar.AR_BF16, ar.AR_BF16,
+                                      ar.AR_MODE_CHUNKED, stream=stream),
+            6 * n, lambda: h_dst[0].view(torch.int16))
+    del h_src, h_dst
+    torch.cuda.empty_cache()
+    n8 = 8192 * 8192
+    s8 = [torch.randn(n8, device="cuda") for _ in range(8)]
+    d8 = torch.empty(n8, device="cuda")
+    measure("r8_hbm_fp32_src", gen_holds, 20,
+            lambda h, k: ar.ar_reduce(ctxs[h], [d8], s8, n8, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                                      stream=stream),
+            9 * n8 * 4, lambda: d8.view(torch.int32))
+    del s8, d8
     torch.cuda.synchronize()
     for c in ctxs.values():
         ar.ar_free(c)

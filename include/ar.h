@@ -119,8 +119,8 @@ typedef enum {
 /* Optional tuning, read once by ar_init.  Zero fields take the defaults;
  * environment variables AR_SINGLE_SHOT_MAX_BYTES, AR_CHUNK_BYTES,
  * AR_HOST_CHUNK_BYTES, AR_HOST_SLOTS, AR_GRID_WGS, AR_STREAM_KERNEL,
- * AR_STORE_POLICY, AR_HOST_PATH and AR_XCD_RUN_ELEMS override the defaults when
- * cfg is NULL or the field is zero. */
+ * AR_STORE_POLICY, AR_HOST_PATH, AR_XCD_RUN_ELEMS and AR_OCCUPANCY_HOLD
+ * override the defaults when cfg is NULL or the field is zero. */
 typedef struct {
     size_t single_shot_max_bytes; /* AUTO threshold, wire bytes per rank at R = 2
                                      (2x this over all ranks); 0 -> 1 MiB */
@@ -156,6 +156,17 @@ typedef struct {
                                      broadcast schedule; none beyond);
                                      a value below one workgroup's share (e.g. 1)
                                      -> no renumbering.  No effect on any result */
+    int    occupancy_hold;        /* resident waves per CU the streaming launches
+                                     are held to, by dynamic LDS the kernels do
+                                     not use (asked for only when a launch's grid
+                                     fills every CU beyond the hold): 0 automatic
+                                     (the two-rank kernels 18, 14 with a
+                                     residual -- fewer loads in flight per CU
+                                     stream faster on MI355X -- and the general
+                                     kernels unheld), -1 no hold, 1..32 every
+                                     register-, LDS-staged and two-rank launch
+                                     held to that many (single-shot launches are
+                                     never held).  No effect on any result */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.
@@ -344,6 +355,9 @@ typedef struct {
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
     int    dst_bytes;     /* bytes per destination element                  */
     int    residual_kind; /* 0 none, 1 element-wise, 2 broadcast row        */
+    int    hold_waves;    /* resident waves per CU the launch is held to when
+                             its grid fills every CU beyond that (0: none;
+                             see ar_config.occupancy_hold)                  */
 } ar_plan;
 
 /* Validate the arguments exactly as ar_reduce does, except the memory-kind

@@ -64,6 +64,7 @@ class ArConfig(ctypes.Structure):
         ("store_policy", ctypes.c_int),
         ("host_path", ctypes.c_int),
         ("xcd_run_elems", ctypes.c_size_t),
+        ("occupancy_hold", ctypes.c_int),
     ]
 
 
@@ -84,6 +85,7 @@ class ArPlan(ctypes.Structure):
         ("active_mask", ctypes.c_uint),
         ("dst_bytes", ctypes.c_int),
         ("residual_kind", ctypes.c_int),
+        ("hold_waves", ctypes.c_int),
     ]
 
 

@@ -64,6 +64,15 @@ size_t env_size(const char *name, size_t fallback) {
     return end != v ? static_cast<size_t>(x) : fallback;
 }
 
+// A signed integer variable (out of int's range: an invalid value)
+long env_long(const char *name, long fallback) {
+    const char *v = std::getenv(name);
+    if (v == nullptr || *v == '\0') return fallback;
+    char *end = nullptr;
+    const long x = std::strtol(v, &end, 10);
+    return end != v ? x : fallback;
+}
+
 // Resolved configuration: explicit fields first, then AR_* environment
 // variables, then the defaults.
 struct Config {
@@ -76,6 +85,7 @@ struct Config {
     int store_policy = 0;
     int host_path = 0;
     size_t xcd_run_elems = 0;   // 0: automatic per call (xcd_run_for)
+    long occupancy_hold = 0;    // 0 automatic, -1 none, 1..32 every streaming launch
 };
 
 int resolve_config(const ar_config *cfg, Config *out) {
@@ -89,6 +99,7 @@ int resolve_config(const ar_config *cfg, Config *out) {
     c.store_policy = static_cast<int>(env_size("AR_STORE_POLICY", 0));
     c.host_path = static_cast<int>(env_size("AR_HOST_PATH", 0));
     c.xcd_run_elems = env_size("AR_XCD_RUN_ELEMS", 0);
+    c.occupancy_hold = env_long("AR_OCCUPANCY_HOLD", 0);
     if (cfg != nullptr) {
         if (cfg->host_slots < 0 || cfg->grid_wgs < 0 || cfg->stream_kernel < 0 || cfg->stream_kernel > 2 ||
             cfg->store_policy < 0 || cfg->store_policy > 2 || cfg->host_path < 0 || cfg->host_path > 2) {
@@ -103,12 +114,14 @@ int resolve_config(const ar_config *cfg, Config *out) {
         if (cfg->stream_kernel) c.stream_kernel = cfg->stream_kernel;
         if (cfg->store_policy) c.store_policy = cfg->store_policy;
         if (cfg->host_path) c.host_path = cfg->host_path;
+        if (cfg->occupancy_hold) c.occupancy_hold = cfg->occupancy_hold;
     }
     if (c.host_slots < 1 || c.host_slots > kMaxHostSlots) return AR_ERR_INVALID;
     if (c.stream_kernel < 0 || c.stream_kernel > 2) return AR_ERR_INVALID;
     if (c.grid_wgs < 0 || c.grid_wgs > 65535) return AR_ERR_INVALID;
     if (c.store_policy < 0 || c.store_policy > 2) return AR_ERR_INVALID;
     if (c.host_path < 0 || c.host_path > 2) return AR_ERR_INVALID;
+    if (c.occupancy_hold < -1 || c.occupancy_hold > 32) return AR_ERR_INVALID;
     *out = c;
     return AR_OK;
 }
@@ -403,7 +416,8 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         // the two-rank contiguous kernels for the commonest call: two active
         // binary32 partials into one binary32 destination (with or without a
         // residual), kept stores, the launch shape left to the library, chunked
-        // or single-shot (prefill call 15.45 against 15.82 us with the
+        // or single-shot (measured before the occupancy hold below, which
+        // widened the lead: prefill call 15.45 against 15.82 us with the
         // register-staged kernel, 20.2 against 21.2-22.8 us with an
         // element-wise residual, 15.6 against 16.4-17.3 us with a row; a decode
         // vector of 4096, replayed from a HIP graph, 1.68 against 1.74-1.78 us
@@ -421,6 +435,16 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             (rows == nullptr || pair_rows) && R == 2 && active == 0x3u && !src_wire && dst_bytes == 4 &&
             !plan->store_nt && cfg.grid_wgs == 0) {
             plan->stream_kernel = 3;
+        }
+        // occupancy hold: an explicit one holds every streaming launch; the
+        // automatic one holds the two-rank kernels only (18 waves, 14 with a
+        // residual: the figures are at kPairWaves); the general kernels gained
+        // nothing from one (bench.py --hold-study)
+        plan->hold_waves = 0;
+        if (cfg.occupancy_hold > 0) {
+            plan->hold_waves = plan->stream_kernel == 0 ? 0 : static_cast<int>(cfg.occupancy_hold);
+        } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 3) {
+            plan->hold_waves = static_cast<int>(res_kind != 0 ? mpp::kPairResWaves : mpp::kPairWaves);
         }
     }
     return AR_OK;
@@ -457,6 +481,13 @@ namespace {
 
 mpp::CuLimits cu_limits(const ar_ctx *c) {
     return mpp::CuLimits{static_cast<unsigned>(c->cu_count), c->lds_per_cu};
+}
+
+// A general launch shape with the plan's occupancy hold and the device's limits.
+mpp::LaunchShape held(const ar_ctx *c, const ar_plan &plan, mpp::LaunchShape s) {
+    s.hold_waves = static_cast<unsigned>(plan.hold_waves);
+    s.cu = cu_limits(c);
+    return s;
 }
 
 // Makes `dev` current for the scope and restores the caller's device; no
@@ -598,8 +629,8 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
                 a.src[r] = srcs[r];
                 a.dst[r] = dst[r];
             }
-            const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr, max_len,
-                                                           static_cast<unsigned>(R), c->cu_count, c->cfg.grid_wgs);
+            const mpp::LaunchShape shape = held(c, plan, mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr, max_len,
+                                                           static_cast<unsigned>(R), c->cu_count, c->cfg.grid_wgs));
             if (int rc = hip_status(mpp::launch(family, types, true, a, shape, stream))) return rc;
         }
         return AR_OK;
@@ -617,7 +648,9 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
                                                      static_cast<const char *>(srcs[0]) + p0 * sb,
                                                      static_cast<const char *>(srcs[1]) + p0 * sb, rp,
                                                      rk == 2 ? res.len : 0, rk == 2 ? p0 % res.len : 0,
-                                                     xcd_run_for(c->cfg, R, false), cu_limits(c), stream))) {
+                                                     xcd_run_for(c->cfg, R, false),
+                                                     static_cast<unsigned>(plan.hold_waves), cu_limits(c),
+                                                     stream))) {
                 return rc;
             }
         }
@@ -645,9 +678,9 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         }
         set_ranges_1d(a, res, n, p0, cols, plan.dst_bytes);
         const unsigned n_ranges = static_cast<unsigned>((len + cols - 1) / cols);
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
+        const mpp::LaunchShape shape = held(c, plan, mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
                                                        static_cast<unsigned>(cols), n_ranges, c->cu_count,
-                                                       c->cfg.grid_wgs);
+                                                       c->cfg.grid_wgs));
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
     }
     return AR_OK;
@@ -676,7 +709,8 @@ int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const
                     static_cast<char *>(dst[0]) + r0 * rw.dst_stride * db,
                     static_cast<const char *>(srcs[0]) + r0 * rw.src_stride * sb,
                     static_cast<const char *>(srcs[1]) + r0 * rw.src_stride * sb, rp, rw.res_stride,
-                    xcd_run_for(c->cfg, R, false), cu_limits(c), stream))) {
+                    xcd_run_for(c->cfg, R, false), static_cast<unsigned>(plan.hold_waves), cu_limits(c),
+                    stream))) {
                 return rc;
             }
         }
@@ -704,9 +738,9 @@ int run_rows(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *const
             a.res_stride = rw.res_stride;
             a.res_reuse = rw.res_stride == 0 ? 1 : 0;
         }
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
+        const mpp::LaunchShape shape = held(c, plan, mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
                                                        static_cast<unsigned>(rw.cols), static_cast<unsigned>(nr),
-                                                       c->cu_count, c->cfg.grid_wgs);
+                                                       c->cu_count, c->cfg.grid_wgs));
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
     }
     return AR_OK;
@@ -818,8 +852,8 @@ int run_host_staged(ar_ctx *c, const ar_plan &plan, void *const *dst, const void
         for (int r = 0; r < R; ++r) a.src[r] = srcs[r] == nullptr ? nullptr : slot_base + r * rank_stride;
         a.dst[0] = static_cast<char *>(dst[0]) + e0 * db;
         set_ranges_1d(a, res, n, e0, len, plan.dst_bytes);
-        const mpp::LaunchShape shape = mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
-                                                       static_cast<unsigned>(len), 1, c->cu_count, c->cfg.grid_wgs);
+        const mpp::LaunchShape shape = held(c, plan, mpp::plan_shape(family, types.src_is_wire, R, res.ptr != nullptr,
+                                                       static_cast<unsigned>(len), 1, c->cu_count, c->cfg.grid_wgs));
         if (int rc = hip_status(mpp::launch(family, types, false, a, shape, stream))) return rc;
         if (hipEventRecord(slots.free[slot], stream) != hipSuccess) return AR_ERR_RUNTIME;
         slots.used[slot] = 1;

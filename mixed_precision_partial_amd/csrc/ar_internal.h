@@ -98,11 +98,20 @@ enum class Family : int {
     StreamLds  = 2,   // persistent waves, double-buffered LDS staging
 };
 
+// A device's CU count and LDS bytes per CU, for launches that hold a CU below
+// its full wave occupancy.
+struct CuLimits {
+    unsigned cu_count;
+    unsigned lds_bytes;   // 0: unknown (no hold)
+};
+
 struct LaunchShape {
     unsigned grid_x;      // workgroups per slice
     unsigned grid_y;      // slices
     unsigned block;       // threads per workgroup
     unsigned lds_bytes;   // dynamic LDS per workgroup
+    unsigned hold_waves;  // 0, or resident waves per CU to hold the launch to
+    CuLimits cu;          // the device, for the hold
 };
 
 // Element types of a launch: wire type (ar_dtype), 16-bit sources, and a
@@ -139,13 +148,6 @@ inline unsigned xcd_map_lc(unsigned grid_x, size_t wg_elems, size_t run_elems) {
     return lc;
 }
 
-// A device's CU count and LDS bytes per CU, for launches that hold a CU below
-// its full wave occupancy.
-struct CuLimits {
-    unsigned cu_count;
-    unsigned lds_bytes;   // 0: unknown (no hold)
-};
-
 // Dynamic LDS per one-wave workgroup that lets at most `waves` of them reside
 // on a CU; the kernel never touches it.  0 (no hold) when the CU's LDS is
 // unknown or the grid's `wgs` workgroups would not fill every CU to `waves`
@@ -158,8 +160,8 @@ inline unsigned hold_lds_bytes(const CuLimits &cu, uint64_t wgs, unsigned waves)
     return bytes <= 65536u && cu.lds_bytes / bytes == waves ? bytes : 0u;
 }
 
-// Resident waves per CU the two-rank kernels are held to, without and with a
-// residual.  One-wave workgroups would otherwise fill a CU to 32 waves; fewer
+// Resident waves per CU the two-rank kernels are held to by default, without
+// and with a residual.  One-wave workgroups would otherwise fill a CU to 32 waves; fewer
 // loads in flight per CU stream faster on MI355X (prefill call, 2 x [2048 x
 // 4096] fp32 -> fp32, bf16 wire, on two boxes: 15.30-15.33 us held at 16-20
 // waves against 15.45-15.52 us unheld; with an element-wise residual
@@ -174,22 +176,22 @@ constexpr unsigned kPairResWaves = 14;
 // + res[(i + res_phase) mod res_len] (res_kind 2, a broadcast row of res_len
 // elements, a multiple of 8, res_phase < res_len), for i < n (n <=
 // kMaxLaunchElems); one 1-D launch on `stream`, XCD runs of about run_elems
-// elements, CUs held to kPairWaves / kPairResWaves resident waves.  Every
-// pointer is a binary32 device array, 16-byte aligned.
+// elements, every CU held to `hold_waves` resident waves (0: no hold).
+// Every pointer is a binary32 device array, 16-byte aligned.
 hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
-                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, const CuLimits &cu,
-                       hipStream_t stream);
+                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, unsigned hold_waves,
+                       const CuLimits &cu, hipStream_t stream);
 
 // The two-rank kernels over row-strided tensors (k_pair_rows): row i, column
 // j of the destination = wire(src0) + wire(src1) (+ the residual: res_kind 1
 // element-wise with its own row stride, 2 one bias row of cols elements) at
 // row i·stride + j of each tensor, for rows x cols elements (cols a multiple
 // of 512, rows·cols <= kMaxLaunchElems, strides in elements, below 2^32);
-// one 1-D launch on `stream`, XCD runs of about run_elems elements, CUs held
-// as launch_pair holds them.
+// one 1-D launch on `stream`, XCD runs of about run_elems elements, every
+// CU held to `hold_waves` resident waves (0: no hold).
 hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
                             void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
-                            size_t run_elems, const CuLimits &cu, hipStream_t stream);
+                            size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream);
 
 // Size of the library's static staging array (one per device), the only
 // device memory ar_reduce_staged_static uses beyond the caller's buffers.

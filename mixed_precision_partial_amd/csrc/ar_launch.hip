@@ -2,7 +2,9 @@
 // the ar_k_*.hip files define, and the library's static staging array.
 #include "ar_device.h"
 
+#include <algorithm>
 #include <mutex>
+#include <unordered_map>
 
 namespace mpp {
 namespace {
@@ -73,6 +75,23 @@ hipError_t launch_as(const void *fn, const KernelArgs &a, const LaunchShape &sha
                            hot ? hot_kargs : block_kargs, shape.lds_bytes, stream);
 }
 
+// Static LDS bytes of a kernel (its own __shared__ arrays), looked up once per
+// kernel: the occupancy hold adds dynamic LDS on top of it.
+hipError_t static_lds_bytes(const void *fn, unsigned *out) {
+    static std::mutex mu;
+    static std::unordered_map<const void *, unsigned> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = seen.find(fn);
+    if (it == seen.end()) {
+        hipFuncAttributes fa{};
+        const hipError_t e = hipFuncGetAttributes(&fa, fn);
+        if (e != hipSuccess) return e;
+        it = seen.emplace(fn, static_cast<unsigned>(fa.sharedSizeBytes)).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
+
 // Staging memory of ar_reduce_staged_static: one array per device, part of
 // the code object (the loader places it on every device the library runs
 // on, where it stays until the process ends).  Host code never passes the
@@ -83,8 +102,8 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 }  // namespace
 
 hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *src0, const void *src1,
-                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, const CuLimits &cu,
-                       hipStream_t stream) {
+                       const void *res, size_t res_len, size_t res_phase, size_t run_elems, unsigned hold_waves,
+                       const CuLimits &cu, hipStream_t stream) {
     if (wire < AR_F32 || wire > AR_BF16 || res_kind < 0 || res_kind > 2 || n == 0 || n > kMaxLaunchElems) {
         return hipErrorInvalidValue;
     }
@@ -107,13 +126,13 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
     // row kinds: 4 a power of two, 2 at least one wave tile, 3 shorter
     const int kind = res_kind < 2 ? res_kind : ((res_len & (res_len - 1)) == 0 ? 4 : (res_len >= kWaveTile ? 2 : 3));
     void *args[] = {&tiles, &rem, &d, &a, &b, &lc, &r, &rl, &ph};
-    const unsigned hold = hold_lds_bytes(cu, grid, res_kind == 0 ? kPairWaves : kPairResWaves);
+    const unsigned hold = hold_lds_bytes(cu, grid, hold_waves);
     return hipLaunchKernel(kPair[kind][wire], dim3(grid), dim3(kPairBlock), args, hold, stream);
 }
 
 hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
                             void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
-                            size_t run_elems, const CuLimits &cu, hipStream_t stream) {
+                            size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream) {
     if (wire < AR_F32 || wire > AR_BF16 || res_kind < 0 || res_kind > 2 || rows == 0 || cols == 0 ||
         cols % kWaveTile != 0 || rows * cols > kMaxLaunchElems || src_stride < cols || dst_stride < cols ||
         src_stride >= (size_t(1) << 32) || dst_stride >= (size_t(1) << 32) || res_stride >= (size_t(1) << 32)) {
@@ -134,7 +153,7 @@ hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, si
     const float *b = static_cast<const float *>(src1);
     const float *r = static_cast<const float *>(res);
     void *args[] = {&tiles, &tpr_arg, &ss, &ds, &d, &a, &b, &lc, &r, &rs};
-    const unsigned hold = hold_lds_bytes(cu, tiles, res_kind == 0 ? kPairWaves : kPairResWaves);
+    const unsigned hold = hold_lds_bytes(cu, tiles, hold_waves);
     return hipLaunchKernel(kPairRows[res_kind][p2 ? 1 : 0][wire], dim3(tiles), dim3(kPairBlock), args, hold, stream);
 }
 
@@ -234,11 +253,24 @@ hipError_t launch(Family family, const Types &types, bool sliced, KernelArgs a, 
                             kWaveTile;
     a.map_lc = family == Family::SingleShot ? 0u : xcd_map_lc(shape.grid_x, wg_elems, a.xcd_run_elems);
     const bool hot = family != Family::SingleShot && !res;
+    // occupancy hold: dynamic LDS on top of the kernel's own, so that at most
+    // hold_waves (rounded down to whole workgroups) share a CU
+    LaunchShape held = shape;
+    if (shape.hold_waves > 0 && family != Family::SingleShot) {
+        const unsigned wgs = std::max(1u, shape.hold_waves / (shape.block / kWave));
+        const unsigned want = hold_lds_bytes(shape.cu, uint64_t(shape.grid_x) * shape.grid_y, wgs);
+        unsigned own = 0;
+        if (want > 0) {
+            const hipError_t e = static_lds_bytes(fn, &own);
+            if (e != hipSuccess) return e;
+        }
+        if (want > own) held.lds_bytes = std::max(held.lds_bytes, want - own);
+    }
     switch (b) {
-    case 0: return launch_as<2>(fn, a, shape, hot, stream);
-    case 1: return launch_as<4>(fn, a, shape, hot, stream);
-    case 2: return launch_as<8>(fn, a, shape, hot, stream);
-    default: return launch_as<16>(fn, a, shape, hot, stream);
+    case 0: return launch_as<2>(fn, a, held, hot, stream);
+    case 1: return launch_as<4>(fn, a, held, hot, stream);
+    case 2: return launch_as<8>(fn, a, held, hot, stream);
+    default: return launch_as<16>(fn, a, held, hot, stream);
     }
 }
 

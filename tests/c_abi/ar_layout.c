@@ -24,6 +24,7 @@ int main(void) {
     FIELD(ar_config, store_policy);
     FIELD(ar_config, host_path);
     FIELD(ar_config, xcd_run_elems);
+    FIELD(ar_config, occupancy_hold);
     printf("sizeof ar_plan %zu\n", sizeof(ar_plan));
     FIELD(ar_plan, mode);
     FIELD(ar_plan, n_dst);
@@ -40,6 +41,7 @@ int main(void) {
     FIELD(ar_plan, active_mask);
     FIELD(ar_plan, dst_bytes);
     FIELD(ar_plan, residual_kind);
+    FIELD(ar_plan, hold_waves);
     printf("sizeof ar_rows %zu\n", sizeof(ar_rows));
     FIELD(ar_rows, rows);
     FIELD(ar_rows, cols);

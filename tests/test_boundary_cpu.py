@@ -45,8 +45,9 @@ def test_status_strings():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 6 * 4 + 8   # six ints, then xcd_run_elems
-    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 4 * 4 + 2 * 4
+    # six ints, xcd_run_elems, then occupancy_hold padded to 8
+    assert ctypes.sizeof(ar.ArConfig) == 3 * 8 + 6 * 4 + 8 + 8
+    assert ctypes.sizeof(ar.ArPlan) == 4 * 4 + 2 * 8 + 2 * 16 * 8 + 8 + 4 * 4 + 3 * 4 + 4
 
 
 def q(n, R=2, mode=ar.AR_MODE_AUTO, wire=ar.AR_BF16, dst_type=ar.AR_F32, dsts=None, srcs=None,
@@ -571,6 +572,41 @@ def test_xcd_placement_map_is_a_permutation(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     out = subprocess.run([exe], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr
+
+
+def test_occupancy_hold_in_plans(monkeypatch):
+    """The plan reports the occupancy hold its launches take: by default the two-rank
+    kernels only (18 waves, 14 with a residual); an explicit ar_config.occupancy_hold
+    (or AR_OCCUPANCY_HOLD) holds every streaming launch but never a single-shot one; -1
+    holds none; values outside -1..32 are refused."""
+    monkeypatch.delenv("AR_OCCUPANCY_HOLD", raising=False)
+    n = 2048 * 4096
+    two = dict(dsts=[A[20]], srcs=A[1:3], mode=ar.AR_MODE_CHUNKED)
+    assert q(n, **two)[1].hold_waves == 18
+    rc, p = ar.ar_plan_query_add([A[20]], A[1:3], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, A[30], n)
+    assert rc == ar.AR_OK and p.stream_kernel == 3 and p.hold_waves == 14
+    rc, p = ar.ar_plan_query_add([A[20]], A[1:3], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, A[30], 4096)
+    assert rc == ar.AR_OK and p.hold_waves == 14
+    rc, p = ar.ar_plan_query_rows([A[20]], A[1:3], 2048, 4096, 4608, 4352, ar.AR_F32, ar.AR_BF16,
+                                  ar.AR_MODE_CHUNKED)
+    assert rc == ar.AR_OK and p.stream_kernel == 3 and p.hold_waves == 18
+    three = dict(dsts=[A[20]], srcs=A[1:4], mode=ar.AR_MODE_CHUNKED)
+    assert q(n, **three)[1].stream_kernel in (1, 2) and q(n, **three)[1].hold_waves == 0
+    assert q(n, **two, config={"occupancy_hold": -1})[1].hold_waves == 0
+    assert q(n, **two, config={"occupancy_hold": 12})[1].hold_waves == 12
+    assert q(n, **three, config={"occupancy_hold": 12})[1].hold_waves == 12
+    ss = dict(dsts=[A[20]], srcs=A[1:4], mode=ar.AR_MODE_SINGLE_SHOT)
+    assert q(4096, **ss, config={"occupancy_hold": 12})[1].stream_kernel == 0
+    assert q(4096, **ss, config={"occupancy_hold": 12})[1].hold_waves == 0
+    for bad in (-2, 33):
+        assert q(n, **two, config={"occupancy_hold": bad})[0] == ar.AR_ERR_INVALID
+    monkeypatch.setenv("AR_OCCUPANCY_HOLD", "-1")
+    assert q(n, **two)[1].hold_waves == 0
+    monkeypatch.setenv("AR_OCCUPANCY_HOLD", "20")
+    assert q(n, **three)[1].hold_waves == 20
+    assert q(n, **two, config={"occupancy_hold": 16})[1].hold_waves == 16   # the field wins
+    monkeypatch.setenv("AR_OCCUPANCY_HOLD", "40")
+    assert q(n, **two)[0] == ar.AR_ERR_INVALID
 
 
 def test_occupancy_hold_bytes(tmp_path):

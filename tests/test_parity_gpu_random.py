@@ -5,7 +5,8 @@ Each case draws a rank count, a length (ragged against every tile and chunk
 size), the wire and destination types, whether the sources hold the wire type
 already, the schedule, a residual (none, element-wise, or a broadcast row),
 inactive ranks, exact in-place use, and a context configuration (kernel
-family, store policy, host path, grid size, chunk sizes, copy slots).  The
+family, store policy, host path, grid size, chunk sizes, copy slots, XCD
+placement, occupancy hold).  The
 parametrised tests cover each feature on its own; this sweep covers them in
 combination.  Cases are generated from a fixed seed, so a failure names a
 case that reruns identically.
@@ -67,6 +68,8 @@ def draw_case(i: int) -> dict:
         "host_slots": int(rng.choice([0, 1, 2])),
         # XCD placement runs: automatic, none, and runs from one workgroup to 4 Mi elements
         "xcd_run_elems": int(rng.choice([0, 0, 1, 512, 4096, 1 << 15, 1 << 17, 1 << 22])),
+        # the occupancy hold, from a generator of its own so the other draws stay as they were
+        "occupancy_hold": int(np.random.default_rng([40_001, i]).choice([0, 0, 0, -1, 2, 6, 10, 14, 18, 32])),
     }
     return dict(i=i, R=R, n=n, wire=wire, dst_type=dst_type, src_wire=src_wire, res_form=str(res_form), L=L,
                 mode=mode, inactive=[bool(x) for x in inactive], in_place=bool(in_place), cfg=cfg,

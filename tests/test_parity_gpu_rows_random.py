@@ -6,7 +6,8 @@ wave tiles, multiples of 8, or any length), padded or dense strides for the
 sources, the destination and a strided residual, the wire and destination
 types, 16-bit sources, a residual (none, strided, or one broadcast row),
 inactive ranks, the schedule and a context configuration (kernel family,
-store policy, host path, grid size, chunk sizes, copy slots, XCD placement).
+store policy, host path, grid size, chunk sizes, copy slots, XCD placement,
+occupancy hold).
 The parametrised row tests cover each feature on its own; this sweep covers
 them in combination, including the two-rank row-strided kernel under every
 configuration that leaves it eligible.  Sources carry NaN between rows and
@@ -66,6 +67,7 @@ def draw_rows_case(i: int) -> dict:
         "host_chunk_bytes": int(rng.choice([0, 0, 1 << 14, 1 << 16])),
         "host_slots": int(rng.choice([0, 1, 2])),
         "xcd_run_elems": int(rng.choice([0, 0, 1, 512, 4096, 1 << 15, 1 << 17])),
+        "occupancy_hold": int(np.random.default_rng([41_001, i]).choice([0, 0, 0, -1, 2, 6, 10, 14, 18, 32])),
     }
     mode = int(rng.choice(MODES))
     if rng.random() < 0.25:

@@ -127,6 +127,8 @@ def check_plan(plan, R, n, dst_type, wire_type, mode, srcs, resolved, res_kind, 
     pair = (resolved in (ar.AR_MODE_CHUNKED, ar.AR_MODE_SINGLE_SHOT) and R == 2 and n_active == 2 and
             not mode & ar.AR_SRC_WIRE and dst_type == F32)
     assert (plan.stream_kernel == 3) == pair
+    # the default occupancy hold: the two-rank kernels only, 18 waves, 14 with a residual
+    assert plan.hold_waves == ((14 if res_kind else 18) if pair else 0)
     if resolved == ar.AR_MODE_SINGLE_SHOT:
         assert plan.chunk_elems == n and plan.stream_kernel == (3 if pair else 0)
     else:
@@ -352,6 +354,7 @@ def test_plan_query_rows_matches_rules(args, shape, data):
             not mode & ar.AR_SRC_WIRE and dst_type == F32 and cols % WAVE_TILE == 0 and
             max(ss, ds, rs) < (1 << 32))
     assert (plan.stream_kernel == 3) == pair
+    assert plan.hold_waves == ((14 if res_kind else 18) if pair else 0)
     # device schedules: one range per row; host-staged copies move whole rows
     assert plan.chunk_elems % cols == 0
     chunk_rows = plan.chunk_elems // cols
