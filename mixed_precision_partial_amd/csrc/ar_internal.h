@@ -161,13 +161,12 @@ inline unsigned hold_lds_bytes(const CuLimits &cu, uint64_t wgs, unsigned waves)
 }
 
 // Resident waves per CU the two-rank kernels are held to by default, without
-// and with a residual.  One-wave workgroups would otherwise fill a CU to 32 waves; fewer
-// loads in flight per CU stream faster on MI355X (prefill call, 2 x [2048 x
-// 4096] fp32 -> fp32, bf16 wire, on two boxes: 15.30-15.33 us held at 16-20
-// waves against 15.45-15.52 us unheld; with an element-wise residual
-// 19.68-19.80 us at 14 against 20.12-20.22; with a 4096-element row
-// 15.46-15.47 us at 14 against 15.70-15.74; a plain call held at 14 ran
-// 15.49 us, a residual call held at 18 19.93-20.06 us: bit-identical outputs).
+// and with a residual.  One-wave workgroups would otherwise fill a CU to 32
+// waves; fewer loads in flight per CU stream faster on MI355X (bench.py
+// --hold-study, one box, bit-identical outputs: the prefill call 15.42 us
+// unheld, 15.21 held at 18-20 waves, 15.42 at 14; with an element-wise
+// residual 20.21 unheld, 19.62 at 14, 19.91 at 18; with a 4096-element row
+// 15.63 unheld, 15.38 at 14, 15.52 at 18; the row-strided forms alike).
 constexpr unsigned kPairWaves = 18;
 constexpr unsigned kPairResWaves = 14;
 
