@@ -208,6 +208,10 @@ def parse():
                         "row-strided block) and three general-kernel calls (cfg 4, the bf16 -> bf16 prefill "
                         "shape, R = 8 fp32) by occupancy hold, interleaved in one process (bit-identical "
                         "outputs checked); one JSON line")
+    p.add_argument("--size-study", action="store_true",
+                   help="instead of the benchmark: the prefill call's reduce and its 2 : 1 ceiling kernel at "
+                        "n = 2^20 ... 2^26 elements, with a fitted fixed per-call cost and streaming rate; "
+                        "one JSON line")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="write profiles/counters_<workload>.md from the rocprofv3 --pmc runs of COUNTER_PASSES")
     p.add_argument("--profile-pass", action="store_true",
@@ -252,6 +256,8 @@ def main() -> int:
         return family_study(torch, ar, wl, args)
     if args.hold_study:
         return hold_study(torch, ar, wl, args)
+    if args.size_study:
+        return size_study(torch, ar, wl, args)
     w = wl.WORKLOADS["prefill_bf16"]
     R, n = w.R, w.n
     S = max(1, args.sets)
@@ -974,6 +980,129 @@ def hold_study(torch, ar, wl, args, reps: int = 7) -> int:
     return 0
 
 
+def size_study(torch, ar, wl, args, reps: int = 5) -> int:
+    """How the prefill call's time splits into a fixed per-call cost and streaming: the
+    two-rank reduce (R = 2 fp32 partials, bf16 wire, CHUNKED) and the 2 : 1 ceiling kernel
+    (write-through, XCD runs, one-wave workgroups, held to 18 waves: the reduce's own
+    launch) at n = 2^20 ... 2^26 elements, each size over 768 MiB of rotated sets (the
+    headline's footprint: past the Infinity Cache, below the ~1 GiB where every kernel
+    slows), back to back between two HIP events; a least-squares line
+    us = fixed + bytes / rate over the sizes from 2^22 up (smaller calls can be limited by
+    the Python enqueue).  Then the prefill size by footprint: the reduce and the ceiling
+    kernel over 4 ... 24 rotated sets, and the reduce over 8 or 16 sets touching only the
+    first half of every buffer (is it the bytes touched or the allocations?).  Last, the
+    768 MiB call and its ceiling with the three buffers at five relative placements.  One
+    JSON line."""
+    import ctypes
+
+    stream = torch.cuda.current_stream()
+    ctx = ar.ar_init(0)
+    lib = ceiling_lib()
+    vp = ctypes.c_void_p
+    sh = vp(stream.cuda_stream)
+    out = {"metric": "us per call by size (R = 2 fp32 partials, bf16 wire)", "reps": reps, "sizes": {}}
+    xs, ys, yc = [], [], []
+    for k in range(20, 27):
+        n = 1 << k
+        nbytes = 12 * n
+        sets = max(1, (768 << 20) // nbytes)   # 768 MiB touched at every size, as in the headline
+        src = [[torch.randn(n, device="cuda") for _ in range(2)] for _ in range(sets)]
+        dst = [torch.empty(n, device="cuda") for _ in range(sets)]
+        calls = max(20, min(2000, int(30e3 / (nbytes / 6.5e6 + 2.0))))
+        fns = [ar.bind_reduce(ctx, [dst[i]], src[i], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, stream=stream)
+               for i in range(sets)]
+        arrs = [((vp * 2)(src[i][0].data_ptr(), src[i][1].data_ptr()), (vp * 1)(dst[i].data_ptr()))
+                for i in range(sets)]
+
+        def ceil_call(i):
+            a, b = arrs[i % sets]
+            if lib.mpp_ceiling_launch(2, 1, 2, 64, a, b, n * 4, 512 << 10, 18, sh) != 0:
+                raise RuntimeError("ceiling kernel launch failed")
+        tr, tc = [], []
+        for _ in range(reps):
+            tr.append(timed_us(torch, stream, lambda i: fns[i % sets](), calls))
+            tc.append(timed_us(torch, stream, ceil_call, calls))
+        r, c = float(np.median(tr)), float(np.median(tc))
+        out["sizes"][str(n)] = {"bytes": nbytes, "sets": sets, "calls": calls, "reduce_us": round(r, 3),
+                                "reduce_GB/s": round(nbytes / r / 1e3, 1), "ceiling_us": round(c, 3),
+                                "ceiling_GB/s": round(nbytes / c / 1e3, 1)}
+        log(f"n = 2^{k}: reduce {r:.3f} us ({nbytes / r / 1e3:.0f} GB/s), ceiling {c:.3f} us "
+            f"({nbytes / c / 1e3:.0f} GB/s), {sets} sets")
+        if k >= 22:    # below ~10 us per call the Python enqueue can be the limit
+            xs.append(nbytes)
+            ys.append(r)
+            yc.append(c)
+        del src, dst, fns, arrs
+        torch.cuda.empty_cache()
+    for name, y in (("reduce", ys), ("ceiling", yc)):
+        slope, fixed = np.polyfit(np.array(xs, dtype=float), np.array(y), 1)
+        out[f"{name}_fit"] = {"fixed_us": round(float(fixed), 3), "streaming_GB/s": round(1e-3 / float(slope), 1)}
+        log(f"{name}: us = {fixed:.3f} + bytes / {1e-3 / slope:.1f} GB/s")
+    # the prefill size by footprint: 4 ... 24 rotated sets (384 MiB ... 2.25 GiB touched), and
+    # 8 or 16 sets of which each call touches only the first half of every buffer
+    n = 1 << 23
+    smax = 24
+    src = [[torch.randn(n, device="cuda") for _ in range(2)] for _ in range(smax)]
+    dst = [torch.empty(n, device="cuda") for _ in range(smax)]
+    full = [ar.bind_reduce(ctx, [dst[i]], src[i], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, stream=stream)
+            for i in range(smax)]
+    half = [ar.bind_reduce(ctx, [dst[i][:n // 2]], [t[:n // 2] for t in src[i]], n // 2, ar.AR_F32, ar.AR_BF16,
+                           ar.AR_MODE_CHUNKED, stream=stream) for i in range(smax)]
+    arrs = [((vp * 2)(src[i][0].data_ptr(), src[i][1].data_ptr()), (vp * 1)(dst[i].data_ptr()))
+            for i in range(smax)]
+
+    def ceil_at(i):
+        a, b = arrs[i]
+        if lib.mpp_ceiling_launch(2, 1, 2, 64, a, b, n * 4, 512 << 10, 18, sh) != 0:
+            raise RuntimeError("ceiling kernel launch failed")
+    cases = {}
+    for sets in (4, 8, 12, 16, 24):
+        cases[f"reduce_{sets}_sets"] = (lambda k, sets=sets: full[k % sets](), 12 * n, sets * 96)
+        cases[f"ceiling_{sets}_sets"] = (lambda k, sets=sets: ceil_at(k % sets), 12 * n, sets * 96)
+    for sets in (8, 16):
+        cases[f"reduce_half_touched_{sets}_sets"] = (lambda k, sets=sets: half[k % sets](), 6 * n, sets * 48)
+    times = {k: [] for k in cases}
+    for _ in range(reps):
+        for k, (fn, _, _) in cases.items():
+            times[k].append(timed_us(torch, stream, fn, 1000))
+    out["footprint"] = {}
+    for k, (fn, nbytes, mib) in cases.items():
+        m = float(np.median(times[k]))
+        out["footprint"][k] = {"touched_MiB": mib, "us": round(m, 3), "GB/s": round(nbytes / m / 1e3, 1)}
+        log(f"{k} ({mib} MiB touched): {m:.3f} us, {nbytes / m / 1e3:.0f} GB/s")
+    del src, dst, full, half, arrs
+    torch.cuda.empty_cache()
+    # the 768 MiB call with its three buffers carved from one pool at different relative
+    # offsets (the second source and the destination moved by d1, d1 + d2 bytes)
+    n = 1 << 26
+    out["placement_768MiB"] = {}
+    for d1, d2 in ((0, 0), (1 << 18, 1 << 19), (1 << 20, 3 << 20), (5 << 20, 1 << 22), (3 << 12, 7 << 12)):
+        pool = torch.empty(3 * n + (16 << 20) // 4, device="cuda")
+        a, b = pool[:n], pool[n + d1 // 4:2 * n + d1 // 4]
+        d = pool[2 * n + (d1 + d2) // 4:3 * n + (d1 + d2) // 4]
+        a.normal_()
+        b.normal_()
+        fn = ar.bind_reduce(ctx, [d], [a, b], n, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED, stream=stream)
+        pa = ((vp * 2)(a.data_ptr(), b.data_ptr()), (vp * 1)(d.data_ptr()))
+
+        def ceil_p(i, pa=pa):
+            if lib.mpp_ceiling_launch(2, 1, 2, 64, pa[0], pa[1], n * 4, 512 << 10, 18, sh) != 0:
+                raise RuntimeError("ceiling kernel launch failed")
+        tr, tc = [], []
+        for _ in range(reps):
+            tr.append(timed_us(torch, stream, lambda i: fn(), 100))
+            tc.append(timed_us(torch, stream, ceil_p, 100))
+        key = f"offsets_{d1}_{d1 + d2}"
+        out["placement_768MiB"][key] = {"reduce_us": round(float(np.median(tr)), 3),
+                                        "ceiling_us": round(float(np.median(tc)), 3)}
+        log(f"768 MiB call, second source +{d1} B, destination +{d1 + d2} B: reduce "
+            f"{np.median(tr):.2f} us, ceiling {np.median(tc):.2f} us")
+        del pool, a, b, d, fn
+    ar.ar_free(ctx)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def timing_study(torch, ar, wl, args, reps: int = 6) -> int:
     """The 20-step prefill figure under each timing method, interleaved rep by rep
     on the same rotated buffers, plus what an event costs on its own and what an
@@ -1270,9 +1399,10 @@ def other_schedules(torch, ar, wl):
     """The other configurations and adjacent forms: the 4-rank slice + broadcast,
     residual adds, narrow destinations, inactive ranks, row-strided tensors, R=8
     from HBM (fp32 and bf16 partials) and from pinned host memory (direct reads,
-    copy-engine pipeline, static staging), and the two-rank reduce on a 768 MiB
-    call -- each beside the ceiling kernel run at its own bytes and access
-    pattern where one exists (stderr + extras)."""
+    copy-engine pipeline, static staging), the two-rank reduce on a 768 MiB
+    call, and the headline call over 1.5 GiB of rotated sets -- each beside the
+    ceiling kernel run at its own bytes and access pattern where one exists
+    (stderr + extras)."""
     out = {}
     stream = torch.cuda.current_stream()
 
@@ -1347,6 +1477,32 @@ def other_schedules(torch, ar, wl):
     out["prefill_row_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_row_residual: {out['prefill_row_residual']}")
     del srcs, dsts, ress
+    # the headline call over 16 rotated sets (1.5 GiB touched): past about 1 GiB of touched
+    # memory every streaming kernel here, the ceiling kernel included, runs ~8 % slower than
+    # at the headline's 768 MiB (translation reach, not the 256 MiB Infinity Cache: the step
+    # lies between 768 MiB and 1152 MiB and does not move when only half of each buffer is
+    # touched); reported beside its own ceiling kernel
+    big = 16
+    srcs = [[torch.randn(w.n, device="cuda") for _ in range(2)] for _ in range(big)]
+    dsts = [torch.empty(w.n, device="cuda") for _ in range(big)]
+    kf = [0]
+
+    def frot(fn):
+        def call():
+            i = kf[0] % big
+            kf[0] += 1
+            fn(i)
+        return call
+
+    ms = timed(frot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                           stream=stream)), 400)
+    b = w.R * w.n * 4 + w.n * 4
+    out["prefill_footprint_1536MiB"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1), "sets": big}
+    with_ceiling(out["prefill_footprint_1536MiB"],
+                 pattern_ceiling(torch, stream, 2, 1, srcs, [[d] for d in dsts], w.n * 4, 400))
+    log(f"prefill_footprint_1536MiB: {out['prefill_footprint_1536MiB']}")
+    del srcs, dsts
+    torch.cuda.empty_cache()
     # 48 MiB per call: 8 rotated sets (384 MiB) to stay beyond the Infinity Cache
     sets = 8
     srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_BF16).view(np.int16)).cuda() for p in wl.partials(w, k)]
