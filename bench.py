@@ -9,7 +9,7 @@ Inputs are resident in HBM before the timed region and rotate over several
 sets so that the 256 MiB Infinity Cache cannot serve them.
 
 Before the timed steps: the ceiling kernels over the same buffers (reported),
-the warmup steps, and one lead-in call (reported).  The K timed steps lie
+the warmup steps, and three lead-in calls (reported).  The K timed steps lie
 between two HIP events on the launch stream.  Afterwards: per-step times in a
 pass of their own, parity against the oracle, the oracle's own throughput on
 the host cores, decode-size latency (fp32 and bf16 wire), and the other
@@ -222,6 +222,10 @@ def parse():
     return p.parse_args()
 
 
+# untimed calls enqueued right before the timed region's start event
+LEAD_IN_CALLS = 3
+
+
 def main() -> int:
     args = parse()
     if args.summarize_trace or args.summarize_pass_trace or args.summarize_pmc or args.summarize_counters:
@@ -292,20 +296,24 @@ def main() -> int:
         step(k)
     torch.cuda.synchronize()
 
-    # One more untimed call, enqueued just before the start event (reported as
-    # lead_in_calls): the timed calls then find the GPU busy, so the interval
-    # holds K whole calls -- host path and kernel -- and not also the idle gap
-    # before the first one reaches the queue.
-    log(f"timing {args.steps} steps (1 lead-in call)")
+    # LEAD_IN_CALLS more untimed calls, enqueued just before the start event
+    # (reported as lead_in_calls): the timed calls then find the GPU busy, so the
+    # interval holds K whole calls -- host path and kernel -- and not also an idle
+    # gap before the first ones reach the queue.  After the synchronize the host
+    # can be slow to start (the first timed call's enqueue measured up to 20 us,
+    # the second 9 us, then 6-7 us, on one box), longer than one call of queued
+    # GPU work (15 us).
+    log(f"timing {args.steps} steps ({LEAD_IN_CALLS} lead-in calls)")
     start, end = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step(args.warmup)
+    for k in range(LEAD_IN_CALLS):
+        step(args.warmup + k)
     host_t = [0.0] * (args.steps + 1)
     start.record(stream)
     host_t[0] = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + 1 + k)
+        step(args.warmup + LEAD_IN_CALLS + k)
         host_t[k + 1] = time.perf_counter()
     end.record(stream)
     torch.cuda.synchronize()
@@ -374,11 +382,11 @@ def main() -> int:
     extras["value_over_ceiling_2r1w"] = round(gbs / best_2r1w, 4)
     extras["timing"] = {
         "method": "HIP events created with hipEventDisableSystemFence, recorded on the launch stream",
-        "lead_in_calls": 1,
+        "lead_in_calls": LEAD_IN_CALLS,
         "host_enqueue_us_per_step": enqueue_us,
         "per_step_us_separate_pass": [round(x, 3) for x in per_step],
         "before_timed_steps": "ceiling kernels over the same rotated buffers (reported in "
-                              "ceilings_prefill_size), then the warmup steps, then the lead-in call",
+                              "ceilings_prefill_size), then the warmup steps, then the lead-in calls",
     }
     if not args.no_decode:
         extras["decode_f32"] = decode_latency(torch, ar, wl, "decode_f32", floors=False)
@@ -1135,7 +1143,8 @@ def timing_study(torch, ar, wl, args, reps: int = 6) -> int:
     for k in range(200):
         step(k)
     methods = {"default_events_no_lead_in": (0, True), "default_events_lead_in": (1, True),
-               "fence_free_events_no_lead_in": (0, False), "fence_free_events_lead_in": (1, False)}
+               "fence_free_events_no_lead_in": (0, False), "fence_free_events_lead_in": (1, False),
+               "fence_free_events_3_lead_in": (LEAD_IN_CALLS, False)}
     res = {m: [] for m in methods}
     for _ in range(reps):
         for m, (lead, fenced) in methods.items():
