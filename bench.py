@@ -808,7 +808,9 @@ def family_study(torch, ar, wl, args, reps: int = 7, calls: int = 1000) -> int:
     output is compared bit for bit with the automatic plan's before timing; contexts are
     timed interleaved, rep by rep, with pre-converted calls (ar.bind_reduce).  The plain call
     is also timed with every second source moved 1 MiB into a larger allocation (the kernels'
-    sensitivity to where the buffers sit relative to each other).  One JSON line."""
+    sensitivity to where the buffers sit relative to each other), and two bf16 partials
+    into a bf16 destination (the two-rank 16-bit kernel) with and without a ragged tail.
+    One JSON line."""
     w = wl.WORKLOADS["prefill_bf16"]
     n, S = w.n, max(1, args.sets)
     src = [[torch.from_numpy(p).cuda() for p in wl.partials(w, s)] for s in range(S)]
@@ -879,6 +881,33 @@ def family_study(torch, ar, wl, args, reps: int = 7, calls: int = 1000) -> int:
     log("plain, second sources shifted 1 MiB: " + ", ".join(
         f"{k} {v['us_median']} us" for k, v in out["plain_second_source_shifted_1MiB"].items()))
     del big, moved
+    # two bf16 partials into a bf16 destination (the two-rank 16-bit kernel on the automatic
+    # plan), on the prefill shape and with a 1000-element ragged tail
+    for name, m in (("narrow_bf16", n), ("narrow_bf16_ragged", n + 1000)):
+        hs = [[torch.randn(m, device="cuda").bfloat16() for _ in range(2)] for _ in range(S)]
+        hd = [torch.empty(m, dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+        fns = {k: [ar.bind_reduce(c, [hd[s]], hs[s], m, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED, stream=stream)
+                   for s in range(S)] for k, c in ctxs.items()}
+        ref = None
+        for k in ctxs:
+            hd[0].fill_(0)
+            if fns[k][0]() != ar.AR_OK:
+                raise RuntimeError(f"{name} {k}: call failed")
+            torch.cuda.synchronize()
+            bits = hd[0].view(torch.int16).clone()
+            if ref is None:
+                ref = bits
+            elif not torch.equal(bits, ref):
+                raise RuntimeError(f"{name}: {k} differs from the automatic plan's output")
+        times = {k: [] for k in ctxs}
+        for _ in range(reps):
+            for k in ctxs:
+                f = fns[k]
+                times[k].append(timed_us(torch, stream, lambda i: f[i % S](), calls))
+        out[name] = {k: {"us_median": round(float(np.median(v)), 3),
+                         "GB/s": round(6 * m / float(np.median(v)) / 1e3, 1)} for k, v in times.items()}
+        log(f"{name}: " + ", ".join(f"{k} {v['us_median']} us" for k, v in out[name].items()))
+        del hs, hd, fns
     torch.cuda.synchronize()
     for c in ctxs.values():
         ar.ar_free(c)
@@ -998,9 +1027,9 @@ def size_study(torch, ar, wl, args, reps: int = 5) -> int:
     us = fixed + bytes / rate over the sizes from 2^22 up (smaller calls can be limited by
     the Python enqueue).  Then the prefill size by footprint: the reduce and the ceiling
     kernel over 4 ... 24 rotated sets, and the reduce over 8 or 16 sets touching only the
-    first half of every buffer (is it the bytes touched or the allocations?).  Last, the
-    768 MiB call and its ceiling with the three buffers at five relative placements.  One
-    JSON line."""
+    first half of every buffer (is it the bytes touched or the allocations?).  Then the
+    cost of a ragged tail (n = 2^23 + k) on each kernel family.  Last, the 768 MiB call and
+    its ceiling with the three buffers at five relative placements.  One JSON line."""
     import ctypes
 
     stream = torch.cuda.current_stream()
@@ -1079,6 +1108,29 @@ def size_study(torch, ar, wl, args, reps: int = 5) -> int:
         out["footprint"][k] = {"touched_MiB": mib, "us": round(m, 3), "GB/s": round(nbytes / m / 1e3, 1)}
         log(f"{k} ({mib} MiB touched): {m:.3f} us, {nbytes / m / 1e3:.0f} GB/s")
     del src, dst, full, half, arrs
+    torch.cuda.empty_cache()
+    # the tail: the prefill call with n = 2^23 + k on the automatic plan (the two-rank kernel)
+    # and on the forced register- and LDS-staged kernels (the LDS-staged kernels keep the
+    # per-element tail)
+    tail_ctx = {"auto": ctx, "register": ar.ar_init(0, {"stream_kernel": 1}),
+                "lds": ar.ar_init(0, {"stream_kernel": 2})}
+    n = 1 << 23
+    src = [[torch.randn(n + 512, device="cuda") for _ in range(2)] for _ in range(8)]
+    dst = [torch.empty(n + 512, device="cuda") for _ in range(8)]
+    out["tail"] = {}
+    for k in (0, 200, 488):
+        m = n + k
+        row = {}
+        for name, c in tail_ctx.items():
+            fns = [ar.bind_reduce(c, [dst[i][:m]], [t[:m] for t in src[i]], m, ar.AR_F32, ar.AR_BF16,
+                                  ar.AR_MODE_CHUNKED, stream=stream) for i in range(8)]
+            row[name] = round(float(np.median([timed_us(torch, stream, lambda i: fns[i % 8](), 1000)
+                                               for _ in range(reps)])), 3)
+        out["tail"][str(k)] = row
+        log(f"n = 2^23 + {k}: " + ", ".join(f"{name} {v:.3f} us" for name, v in row.items()))
+    for name in ("register", "lds"):
+        ar.ar_free(tail_ctx[name])
+    del src, dst
     torch.cuda.empty_cache()
     # the 768 MiB call with its three buffers carved from one pool at different relative
     # offsets (the second source and the destination moved by d1, d1 + d2 bytes)

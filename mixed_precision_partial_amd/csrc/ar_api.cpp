@@ -436,14 +436,24 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             !plan->store_nt && cfg.grid_wgs == 0) {
             plan->stream_kernel = 3;
         }
+        // and the two-rank 16-bit kernel: two active 16-bit partials into a
+        // contiguous destination of their type, no residual, same conditions
+        // otherwise (bf16 prefill shape, 2 x [2048 x 4096] into bf16:
+        // bench.py --family-study measures it against the LDS-staged kernel)
+        if ((resolved == AR_MODE_CHUNKED || resolved == AR_MODE_SINGLE_SHOT) && cfg.stream_kernel == 0 &&
+            rows == nullptr && R == 2 && active == 0x3u && dst_narrow && res_kind == 0 && !plan->store_nt &&
+            cfg.grid_wgs == 0) {
+            plan->stream_kernel = 3;
+        }
         // occupancy hold: an explicit one holds every streaming launch; the
-        // automatic one holds the two-rank kernels only (18 waves, 14 with a
-        // residual: the figures are at kPairWaves); the general kernels gained
-        // nothing from one (bench.py --hold-study)
+        // automatic one holds the binary32 two-rank kernels only (18 waves, 14
+        // with a residual: the figures are at kPairWaves); the general kernels
+        // and the 16-bit two-rank kernel gained nothing from one (bench.py
+        // --hold-study)
         plan->hold_waves = 0;
         if (cfg.occupancy_hold > 0) {
             plan->hold_waves = plan->stream_kernel == 0 ? 0 : static_cast<int>(cfg.occupancy_hold);
-        } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 3) {
+        } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 3 && dst_bytes == 4) {
             plan->hold_waves = static_cast<int>(res_kind != 0 ? mpp::kPairResWaves : mpp::kPairWaves);
         }
     }
@@ -636,6 +646,21 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         return AR_OK;
     }
 
+    if (plan.stream_kernel == 3 && plan.dst_bytes == 2) {
+        // the two-rank 16-bit kernel: one 1-D launch per launch piece
+        for (size_t p0 = 0; p0 < n; p0 += mpp::kMaxLaunchElems) {
+            const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);
+            if (int rc = hip_status(mpp::launch_pair16(wire_type, len, static_cast<char *>(dst[0]) + p0 * db,
+                                                       static_cast<const char *>(srcs[0]) + p0 * sb,
+                                                       static_cast<const char *>(srcs[1]) + p0 * sb,
+                                                       xcd_run_for(c->cfg, R, false),
+                                                       static_cast<unsigned>(plan.hold_waves), cu_limits(c),
+                                                       stream))) {
+                return rc;
+            }
+        }
+        return AR_OK;
+    }
     if (plan.stream_kernel == 3) {
         // two-rank contiguous kernels: one 1-D launch per launch piece; an
         // element-wise residual moves with the piece, a broadcast row keeps

@@ -610,8 +610,129 @@ __device__ __forceinline__ void reduce_tiles(const LaunchArgs<C::RB> &a, const R
 // Range elements [begin, end), one per lane per step (end - begin is below one
 // wave tile, so this is at most 8 steps).
 template <class C>
-__device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t begin,
-                                              size_t end, int lane) {
+__device__ __forceinline__ void reduce_tail(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t begin,
+                                            size_t end, int lane) {
+    // end - begin < one wave tile, so a lane owns at most kTileLane elements
+    // (begin + lane + kWave k).  The tail's loads are issued without a branch,
+    // KB elements' worth at a time (at most 16 per lane), and folded
+    // afterwards; the stores come after every fold, guarded.  With a load and
+    // its use inside one guarded branch per element, every element waited for
+    // its own loads: the tail then cost one memory round trip per element (up
+    // to 1.8 us on a prefill-sized call).  The sources are read through buffer
+    // loads over [begin, end) of each, so a lane's load past the end returns 0
+    // (the hardware's range check); the residual at an index clamped into the
+    // range.  Each element is read and written by this lane alone and every
+    // load precedes every store, so in-place calls stay exact.
+    constexpr int kTileLane = kWaveTile / kWave;
+    constexpr int KB = C::RB >= 16 ? 1 : (16 / C::RB < kTileLane ? 16 / C::RB : kTileLane);
+    float acc[kTileLane];
+    constexpr unsigned kSrcBytes = C::SW ? 2u : 4u;
+    const unsigned span = static_cast<unsigned>(end - begin) * kSrcBytes;
+#pragma unroll
+    for (int k0 = 0; k0 < kTileLane; k0 += KB) {
+        float v[KB][C::RB];
+        float rv[KB];
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+            const size_t e0 = begin + lane + static_cast<size_t>(kWave) * (k0 + q);
+            const size_t e = e0 < end ? e0 : end - 1;
+            const int off = (lane + kWave * (k0 + q)) * static_cast<int>(kSrcBytes);
+#pragma unroll
+            for (int r = 0; r < C::RB; ++r) {
+                v[q][r] = 0.0f;
+                if (rank_used<C>(a, r) && rank_active<C>(a, r)) {
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<char *>(static_cast<const char *>(a.src[r])) + (o.src + begin) * kSrcBytes, 0,
+                        span, kRsrcWord3);
+                    if constexpr (C::SW) {
+                        v[q][r] = f32_from_bits(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+                    } else {
+                        v[q][r] = f32_from_bits(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+                    }
+                }
+            }
+            rv[q] = 0.0f;
+            if constexpr (C::RES) {
+                const size_t ri = res_index(a, o, e);
+                if constexpr (C::DN) {
+                    rv[q] = f32_from_bits(static_cast<const uint16_t *>(a.res)[ri]);
+                } else {
+                    rv[q] = static_cast<const float *>(a.res)[ri];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+            // the raw values become the wire-rounded terms (16-bit sources and a
+            // narrow residual were loaded as their bit patterns)
+            float term[C::RB];
+#pragma unroll
+            for (int r = 0; r < C::RB; ++r) {
+                if constexpr (C::SW) {
+                    float x, unused;
+                    widen_pair<C::W>(bits_from_f32(v[q][r]), x, unused);
+                    term[r] = x;
+                } else {
+                    float x = v[q][r], y = 0.0f;
+                    wire_pair<C::W>(x, y);
+                    term[r] = x;
+                }
+            }
+            float t0 = rank_active<C>(a, 0) ? term[0] : 0.0f;
+#pragma unroll
+            for (int r = 1; r < C::RB; ++r) {
+                if (rank_used<C>(a, r)) {
+                    t0 = t0 + (rank_active<C>(a, r) ? term[r] : 0.0f);
+                    if constexpr (C::DN) {
+                        float y = 0.0f;
+                        wire_pair<C::W>(t0, y);
+                    }
+                }
+            }
+            if constexpr (C::RES) {
+                if constexpr (C::DN) {
+                    float x, unused;
+                    widen_pair<C::W>(bits_from_f32(rv[q]), x, unused);
+                    t0 = t0 + x;
+                    float y = 0.0f;
+                    wire_pair<C::W>(t0, y);
+                } else {
+                    t0 = t0 + rv[q];
+                }
+            }
+            acc[k0 + q] = t0;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kTileLane; ++k) {
+        const size_t e = begin + lane + static_cast<size_t>(kWave) * k;
+        if (e < end) {
+            const size_t ed = o.dst + e;
+#pragma unroll
+            for (int d = 0; d < C::RB; ++d) {
+                if (d < a.n_dst) {
+                    if constexpr (C::DN) {
+                        static_cast<uint16_t *>(a.dst[d])[ed] =
+                            static_cast<uint16_t>(round_pack<C::W>(acc[k], 0.0f));
+                    } else {
+                        static_cast<float *>(a.dst[d])[ed] = acc[k];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The tail one element at a time, each element's loads, fold and stores in
+// turn: the LDS-staged kernels keep this form.  Inlined into them, the
+// batched tail above keeps the backend from folding the LDS stage pointers'
+// address-space casts in the plain (unmasked, no residual) instances, and the
+// compare against the shared aperture it leaves fails to compile for gfx950
+// ("Operand has incorrect register class"); out of line it gives every
+// LDS-staged kernel a private stack.
+template <class C>
+__device__ __forceinline__ void reduce_tail_each(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t begin,
+                                                 size_t end, int lane) {
     for (size_t e = begin + lane; e < end; e += kWave) {
         const size_t es = o.src + e;
         float acc = rank_active<C>(a, 0) ? wire_one<C::W, C::SW>(a.src[0], es) : 0.0f;
@@ -649,6 +770,16 @@ __device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, const 
     }
 }
 
+template <class C, bool LDS_FAMILY>
+__device__ __forceinline__ void reduce_scalar(const LaunchArgs<C::RB> &a, const RangeOff &o, size_t begin,
+                                              size_t end, int lane) {
+    if constexpr (LDS_FAMILY) {
+        reduce_tail_each<C>(a, o, begin, end, lane);
+    } else {
+        reduce_tail<C>(a, o, begin, end, lane);
+    }
+}
+
 // Offsets and length of this workgroup's gridDim.y range.  Slice ranges
 // (broadcast schedule): [slice_start[y], + slice_len[y]) of every tensor.
 // Strided ranges (everything else): range y has min(cols, n - y * cols)
@@ -679,7 +810,7 @@ __device__ __forceinline__ void range_of(const A &a, RangeOff &o, unsigned &len)
 
 // Whole wave tiles after the batched part, then the element remainder on
 // wave 0 of workgroup 0 of the range.
-template <class C, int U, bool NT, int ST>
+template <class C, int U, bool NT, int ST, bool LDS_FAMILY = false>
 __device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, const RangeOff &o, unsigned len,
                                             unsigned done, unsigned gw, unsigned nw, int lane) {
     if constexpr (U > 1) {
@@ -690,7 +821,7 @@ __device__ __forceinline__ void reduce_rest(const LaunchArgs<C::RB> &a, const Ra
     }
     const unsigned vec_end = (len / kWaveTile) * kWaveTile;
     if (vec_end < len && gw == 0) {
-        reduce_scalar<C>(a, o, vec_end, len, lane);
+        reduce_scalar<C, LDS_FAMILY>(a, o, vec_end, len, lane);
     }
 }
 
@@ -991,7 +1122,7 @@ __device__ __forceinline__ void stream_lds_as(const LaunchArgs<C::RB> &a, const 
         lds_consume<C, U, ST>(a, o, (size_t)t1 * big, lane, stage1);
         t = t2;
     }
-    reduce_rest<C, U, true, ST>(a, o, len, n_big * big, gw, nw, lane);
+    reduce_rest<C, U, true, ST, true>(a, o, len, n_big * big, gw, nw, lane);
 }
 
 template <class C, int ST, bool SLICED>
@@ -1187,13 +1318,32 @@ __device__ __forceinline__ void pair_body(unsigned tiles, unsigned rem, float *d
                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (w >= tiles) {
         if (w == tiles && rem != 0) {
+            // the tail: every load issued unguarded at a clamped index, then the
+            // folds, then the guarded stores (see reduce_scalar)
+            constexpr int K = kWaveTile / kWave;
             const size_t t = static_cast<size_t>(tiles) * kWaveTile;
-            for (unsigned e = lane; e < rem; e += kWave) {
-                float acc = wire_one<W, false>(src0, t + e);
-                acc = acc + wire_one<W, false>(src1, t + e);
-                if constexpr (RK == 1) acc = acc + res[t + e];
-                if constexpr (RK >= 2) acc = acc + res[(static_cast<unsigned>(t) + e + res_phase) % res_len];
-                dst[t + e] = acc;
+            float x[K], y[K], r[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const unsigned e0 = lane + kWave * k;
+                const unsigned e = e0 < rem ? e0 : rem - 1;
+                x[k] = src0[t + e];
+                y[k] = src1[t + e];
+                if constexpr (RK == 1) r[k] = res[t + e];
+                if constexpr (RK >= 2) r[k] = res[(static_cast<unsigned>(t) + e + res_phase) % res_len];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float z = 0.0f, u = 0.0f;
+                wire_pair<W>(x[k], z);
+                wire_pair<W>(y[k], u);
+                x[k] = x[k] + y[k];
+                if constexpr (RK != 0) x[k] = x[k] + r[k];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const unsigned e = lane + kWave * k;
+                if (e < rem) dst[t + e] = x[k];
             }
         }
         return;
@@ -1280,6 +1430,64 @@ __device__ __forceinline__ void pair_rows_body(unsigned tiles, unsigned tpr, uns
     }
 }
 
+// Two-rank kernel for 16-bit partials into a destination of the same 16-bit
+// type W (bf16 or fp16; no residual): per element, both values widened
+// exactly, one binary32 add, one rounding to W (binary32 has more than
+// 2p + 2 bits for both types, so this is the correctly rounded add in W).
+// One wave tile is 512 elements, lane l holding elements t + 8 l .. t + 8 l
+// + 7 of each source in one 16-byte load; stores write-back, as the 16-bit
+// layouts of the general kernels.  The same 1-D grid of one-wave workgroups,
+// preloaded parameters and placement as k_pair; the wave after the last tile
+// does the remainder.
+template <int W>
+__global__ __launch_bounds__(kPairBlock) void k_pair16(unsigned tiles, unsigned rem, uint16_t *dst,
+                                                       const uint16_t *src0, const uint16_t *src1, unsigned lc) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned grid = tiles + (rem != 0 ? 1u : 0u);
+    const unsigned w = xcd_virtual_block(blockIdx.x, grid, lc);
+    if (w >= tiles) {
+        if (w == tiles && rem != 0) {
+            // the tail: every load issued unguarded at a clamped index, then the
+            // adds, then the guarded stores (see reduce_scalar)
+            constexpr int K = kWaveTile / kWave;
+            const size_t t = static_cast<size_t>(tiles) * kWaveTile;
+            uint32_t p[K], q[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const unsigned e0 = lane + kWave * k;
+                const unsigned e = e0 < rem ? e0 : rem - 1;
+                p[k] = src0[t + e];
+                q[k] = src1[t + e];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float x, y, unused;
+                widen_pair<W>(p[k], x, unused);
+                widen_pair<W>(q[k], y, unused);
+                p[k] = round_pack<W>(x + y, 0.0f);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const unsigned e = lane + kWave * k;
+                if (e < rem) dst[t + e] = static_cast<uint16_t>(p[k]);
+            }
+        }
+        return;
+    }
+    const size_t e0 = static_cast<size_t>(w) * kWaveTile + 8 * lane;
+    const u32x4 a = load16<true>(src0 + e0);
+    const u32x4 b = load16<true>(src1 + e0);
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float x0, x1, y0, y1;
+        widen_pair<W>(a[k], x0, x1);
+        widen_pair<W>(b[k], y0, y1);
+        v[k] = round_pack<W>(x0 + y0, x1 + y1);
+    }
+    store16<0>(dst + e0, v);
+}
+
 template <int W, int RK, bool P2>
 __global__ __launch_bounds__(kPairBlock) void k_pair_rows(unsigned tiles, unsigned tpr, unsigned src_stride,
                                                           unsigned dst_stride, float *dst, const float *src0,
@@ -1321,6 +1529,7 @@ typedef const void *const StreamTable[2][2][kCombos][kBuckets];
 extern const void *const kSingleShot[2][2][kCombos][kBuckets];
 // two-rank contiguous kernels, indexed by [residual kind][wire type (ar_dtype)]
 extern const void *const kPair[5][3];
+extern const void *const kPair16[2];   // [0] fp16, [1] bf16
 // two-rank row-strided kernels, [residual kind][power-of-two tiles per row][wire type]
 extern const void *const kPairRows[3][2][3];
 extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,

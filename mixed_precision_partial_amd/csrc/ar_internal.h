@@ -181,6 +181,15 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
                        const void *res, size_t res_len, size_t res_phase, size_t run_elems, unsigned hold_waves,
                        const CuLimits &cu, hipStream_t stream);
 
+// The two-rank kernel for 16-bit partials into the same 16-bit type
+// (k_pair16): dst[i] = RN_W(widen(src0[i]) + widen(src1[i])) for i < n (n <=
+// kMaxLaunchElems), wire = destination type W (AR_F16 or AR_BF16), no
+// residual; one 1-D launch on `stream`, XCD runs of about run_elems elements,
+// every CU held to `hold_waves` resident waves (0: no hold).  Every pointer is
+// a 16-bit device array, 16-byte aligned.
+hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
+                         unsigned hold_waves, const CuLimits &cu, hipStream_t stream);
+
 // The two-rank kernels over row-strided tensors (k_pair_rows): row i, column
 // j of the destination = wire(src0) + wire(src1) (+ the residual: res_kind 1
 // element-wise with its own row stride, 2 one bias row of cols elements) at

@@ -1,5 +1,5 @@
 // ar_k_pair.hip -- two-rank kernel instances: contiguous [residual kind][wire type], row-strided
-// [residual kind][power-of-two tiles per row][wire type].
+// [residual kind][power-of-two tiles per row][wire type], 16-bit into 16-bit [fp16, bf16].
 #include "ar_device.h"
 
 namespace mpp {
@@ -22,5 +22,8 @@ const void *const kPair[5][3] = {{reinterpret_cast<const void *>(&k_pair<AR_F32>
 const void *const kPairRows[3][2][3] = {MPP_PAIR_ROWS(0), MPP_PAIR_ROWS(1), MPP_PAIR_ROWS(2)};
 #undef MPP_PAIR_ROWS
 #undef MPP_PAIR_ROWS_W
+
+const void *const kPair16[2] = {reinterpret_cast<const void *>(&k_pair16<AR_F16>),
+                                reinterpret_cast<const void *>(&k_pair16<AR_BF16>)};
 
 }  // namespace mpp

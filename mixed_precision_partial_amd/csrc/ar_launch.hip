@@ -130,6 +130,21 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
     return hipLaunchKernel(kPair[kind][wire], dim3(grid), dim3(kPairBlock), args, hold, stream);
 }
 
+hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
+                         unsigned hold_waves, const CuLimits &cu, hipStream_t stream) {
+    if ((wire != AR_F16 && wire != AR_BF16) || n == 0 || n > kMaxLaunchElems) return hipErrorInvalidValue;
+    unsigned tiles = static_cast<unsigned>(n / kWaveTile);
+    unsigned rem = static_cast<unsigned>(n % kWaveTile);
+    const unsigned grid = tiles + (rem != 0 ? 1u : 0u);
+    unsigned lc = xcd_map_lc(grid, kWaveTile, run_elems);
+    uint16_t *d = static_cast<uint16_t *>(dst);
+    const uint16_t *a = static_cast<const uint16_t *>(src0);
+    const uint16_t *b = static_cast<const uint16_t *>(src1);
+    void *args[] = {&tiles, &rem, &d, &a, &b, &lc};
+    return hipLaunchKernel(kPair16[wire == AR_BF16 ? 1 : 0], dim3(grid), dim3(kPairBlock), args,
+                           hold_lds_bytes(cu, grid, hold_waves), stream);
+}
+
 hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
                             void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
                             size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream) {

@@ -264,9 +264,21 @@ def test_stream_kernel_choice():
     assert rc == ar.AR_OK and p.stream_kernel == 1
     rc, p = ar.ar_plan_query_rows(A[20:21], A[1:4], 2048, 4096, 4608, 4352, ar.AR_F32, ar.AR_BF16, CH)
     assert rc == ar.AR_OK and p.stream_kernel == 1
+    # two 16-bit partials into their own type, no residual: the two-rank 16-bit kernel,
+    # contiguous and unheld; with a residual the register-staged kernel (the residual rule),
+    # row-strided the LDS-staged one (R = 2 in the table)
+    for wire in (ar.AR_BF16, ar.AR_F16):
+        for mode in (CH, ar.AR_MODE_SINGLE_SHOT):
+            rc, p = q(n if mode == CH else 4097, mode=mode, wire=wire, dst_type=wire)
+            assert rc == ar.AR_OK and p.stream_kernel == 3 and p.hold_waves == 0, (wire, mode)
+        rc, p = ar.ar_plan_query_add(A[20:21], A[1:3], n, wire, wire, CH, res[0], n)
+        assert rc == ar.AR_OK and p.stream_kernel == 1
+        rc, p = ar.ar_plan_query_rows(A[20:21], A[1:3], 2048, 4096, 4608, 4352, wire, wire, CH)
+        assert rc == ar.AR_OK and p.stream_kernel == 2
+        assert q(n, mode=CH, wire=wire, dst_type=wire, config={"occupancy_hold": 12})[1].hold_waves == 12
     for R in range(2, 17):
         want16 = 2 if R in (2, 5, 6, 7, 8) else 1
-        wantn = 2 if R in (2, 6, 7, 8) else 1
+        wantn = 3 if R == 2 else (2 if R in (6, 7, 8) else 1)
         assert q(n, R=R, mode=CH | SW)[1].stream_kernel == want16, R
         assert q(n, R=R, mode=CH, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel == wantn, R
         assert q(n, R=R, mode=BC, wire=ar.AR_F16)[1].stream_kernel == 2, R

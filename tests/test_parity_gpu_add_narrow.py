@@ -289,6 +289,33 @@ def test_narrow_in_place(kctx):
         assert_bits_equal16(dev[1].cpu().numpy().view(np.uint16), want, t, f"narrow in place {t_name}")
 
 
+def test_two_rank_16bit_kernel(kctx):
+    """Two 16-bit partials into their own type without a residual take the two-rank 16-bit
+    kernel (k_pair16): sizes around the 512-element tile, a ragged prefill shape, single-shot
+    and chunked, in place too; bit for bit against the oracle."""
+    sizes = [1, 7, 511, 512, 513, 4097, 65_536 + 5, (1 << 20) + 123, 2048 * 4096 + 1000]
+    for t_name, t in NARROW.items():
+        g = np.concatenate([wl.special_values16(t), wl.nan_values16(t)])
+        for i, n in enumerate(sizes):
+            srcs = wl.random_narrow(17_000 + i, 0, 2, n, t, dist="wide")
+            k = min(g.size, n)
+            srcs[0][:k] = g[:k]
+            srcs[1][:k] = g[::-1][:k]
+            for mode in ((ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED) if n < (1 << 21) else (ar.AR_MODE_CHUNKED,)):
+                rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, t, t, mode)
+                assert rc == ar.AR_OK and plan.stream_kernel == 3, (t_name, n, mode)
+                run_and_check(kctx["default"], srcs, t, mode, f"two-rank 16-bit {t_name} n={n} mode={mode}",
+                              dst_type=t)
+        n = 100_003
+        srcs = wl.random_narrow(17_100, 0, 2, n, t)
+        want = oracle.reduce(srcs, t, src_type=t, dst_type=t)[0]
+        dev = [to_device(s) for s in srcs]
+        log_case(f"two-rank 16-bit in place {t_name}")
+        ar.ar_reduce(kctx["default"], [dev[0]], dev, n, t, t, ar.AR_MODE_CHUNKED)
+        torch.cuda.synchronize()
+        assert_bits_equal16(dev[0].cpu().numpy().view(np.uint16), want, t, f"two-rank 16-bit in place {t_name}")
+
+
 # --------------------------------------------------------------------------
 # the workload shapes at full size
 # --------------------------------------------------------------------------
