@@ -2,9 +2,10 @@
 what they compute: calls large enough for every hold to apply (the grid fills
 each CU beyond it) give bit-identical outputs with no hold, the automatic hold
 and explicit holds, on the two-rank kernels (plain, element-wise residual,
-broadcast row, row-strided), the register-staged and the LDS-staged kernels
-(contiguous and broadcast schedules, 16-bit layouts), and the automatic one
-matches the oracle.
+broadcast row, row-strided, 16-bit), the register-staged and the LDS-staged
+kernels (contiguous and broadcast schedules, 16-bit layouts), and the automatic
+one matches the oracle.  Each call's plan is checked to name the kernel family
+the case is about.
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import torch
 import mixed_precision_partial_amd as ar
 import oracle
 import workloads as wl
-from gpu_util import assert_bits_equal, log_case, to_device
+from gpu_util import assert_bits_equal, assert_bits_equal16, log_case, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -23,15 +24,37 @@ HOLDS = [0, -1, 6, 12, 18, 32]
 N = (1 << 22) + 1000           # 8194 two-rank workgroups: beyond 256 CUs x 32 waves; a ragged tail
 
 
-@pytest.fixture(scope="module")
-def ctxs():
+def _contexts(extra):
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
-    made = {h: ar.ar_init(0, {"occupancy_hold": h} if h else None) for h in HOLDS}
-    yield made
+    return {h: ar.ar_init(0, {**extra, "occupancy_hold": h} if h or extra else None) for h in HOLDS}
+
+
+def _free(made):
     torch.cuda.synchronize()
     for c in made.values():
         ar.ar_free(c)
+
+
+@pytest.fixture(scope="module")
+def ctxs():
+    made = _contexts({})
+    yield made
+    _free(made)
+
+
+@pytest.fixture(scope="module")
+def lds_ctxs():
+    """The same holds with the LDS-staged family forced (stream_kernel 2)."""
+    made = _contexts({"stream_kernel": 2})
+    yield made
+    _free(made)
+
+
+def planned_kernel(dsts, srcs, n, dst_type, wire, mode, config=None):
+    rc, plan = ar.ar_plan_query(dsts, srcs, n, dst_type, wire, mode, config=config)
+    assert rc == ar.AR_OK, ar.ar_status_str(rc)
+    return int(plan.stream_kernel)
 
 
 def same_everywhere(ctxs, what, run, out):
@@ -80,11 +103,24 @@ def test_two_rank_kernels_every_hold(ctxs):
                                                 ar.AR_MODE_CHUNKED, residual=rw, res_stride=0), outr)
 
 
-def test_general_kernels_every_hold(ctxs):
+def test_16bit_two_rank_kernel_every_hold(ctxs):
+    # two bf16 partials into bf16 (512 elements per wave), a ragged tail; every hold applies
+    h = [torch.randn(N, device="cuda").bfloat16().view(torch.int16) for _ in range(2)]
+    outh = torch.empty(N, dtype=torch.int16, device="cuda")
+    assert planned_kernel([outh], h, N, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED) == 3
+    got = same_everywhere(ctxs, "bf16 -> bf16 (two-rank 16-bit)",
+                          lambda c: ar.ar_reduce(c, [outh], h, N, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED), outh)
+    srcs = [t.cpu().numpy().view(np.uint16) for t in h]
+    want = oracle.reduce(srcs, ar.AR_BF16, dst_type=ar.AR_BF16)[0]
+    assert_bits_equal16(got.view(np.uint16), want, ar.AR_BF16, "two-rank 16-bit vs oracle")
+
+
+def test_general_kernels_every_hold(ctxs, lds_ctxs):
     # register-staged: eight fp32 partials; LDS-staged: two bf16 partials into bf16
     srcs = wl.random_partials(50_010, 0, 8, N, dist="normal")
     dev = [to_device(s) for s in srcs]
     out = torch.empty(N, dtype=torch.float32, device="cuda")
+    assert planned_kernel([out], dev, N, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED) == 1
     got = same_everywhere(ctxs, "R=8 fp32 (register-staged)",
                           lambda c: ar.ar_reduce(c, [out], dev, N, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED), out)
     assert_bits_equal(got, oracle.reduce(srcs, ar.AR_BF16)[0], "R=8 vs oracle")
@@ -93,7 +129,8 @@ def test_general_kernels_every_hold(ctxs):
     n16 = 1 << 25
     h = [torch.randn(n16, device="cuda").bfloat16().view(torch.int16) for _ in range(2)]
     outh = torch.empty(n16, dtype=torch.int16, device="cuda")
-    same_everywhere(ctxs, "bf16 -> bf16 (LDS-staged)",
+    assert planned_kernel([outh], h, n16, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED, {"stream_kernel": 2}) == 2
+    same_everywhere(lds_ctxs, "bf16 -> bf16 (LDS-staged)",
                     lambda c: ar.ar_reduce(c, [outh], h, n16, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED), outh)
     del h, outh
     # the broadcast schedule: four fp32 partials into four destinations, fp16 wire

@@ -6,10 +6,12 @@ size), the wire and destination types, whether the sources hold the wire type
 already, the schedule, a residual (none, element-wise, or a broadcast row),
 inactive ranks, exact in-place use, and a context configuration (kernel
 family, store policy, host path, grid size, chunk sizes, copy slots, XCD
-placement, occupancy hold).  The
-parametrised tests cover each feature on its own; this sweep covers them in
-combination.  Cases are generated from a fixed seed, so a failure names a
-case that reruns identically.
+placement, occupancy hold).  A quarter of the cases are drawn so that the
+two-rank kernels take them (binary32 with each residual form, and 16-bit).
+The parametrised tests cover each feature on its own; this sweep covers them
+in combination.  Cases are generated from a fixed seed, so a failure names a
+case that reruns identically.  The CPU half checks that every drawn call is
+valid and which kernel each plan picks.
 """
 from __future__ import annotations
 
@@ -23,8 +25,6 @@ import mixed_precision_partial_amd as ar
 import oracle
 import workloads as wl
 from gpu_util import GuardedDst, assert_bits_equal, assert_bits_equal16, log_case, to_device, to_pinned
-
-pytestmark = pytest.mark.gpu
 
 SCHEDULES = [ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED,
              ar.AR_MODE_AUTO]
@@ -71,9 +71,39 @@ def draw_case(i: int) -> dict:
         # the occupancy hold, from a generator of its own so the other draws stay as they were
         "occupancy_hold": int(np.random.default_rng([40_001, i]).choice([0, 0, 0, -1, 2, 6, 10, 14, 18, 32])),
     }
+    dist = str(rng.choice(["wide", "normal", "normal+outliers"]))
+    # a quarter of the cases are redrawn as calls the two-rank kernels take, from a generator of
+    # their own so the other draws stay as they were: two active ranks, single-shot, chunked or
+    # automatic schedule, library-chosen kernel and grid, kept stores; binary32 partials into
+    # binary32 with the drawn residual form, or two 16-bit partials into their own type without one
+    pr = np.random.default_rng([40_002, i])
+    if pr.random() < 0.25:
+        R, inactive = 2, np.zeros(2, dtype=bool)
+        mode = int(pr.choice([ar.AR_MODE_SINGLE_SHOT, ar.AR_MODE_CHUNKED, ar.AR_MODE_AUTO]))
+        cfg.update(stream_kernel=0, grid_wgs=0, store_policy=int(pr.choice([0, 1])))
+        if narrow:
+            res_form, L = "none", 0
+        src_wire = False if not narrow else src_wire
+        in_place = (not narrow and res_form != "row" and mode != ar.AR_MODE_AUTO and pr.random() < 0.3)
     return dict(i=i, R=R, n=n, wire=wire, dst_type=dst_type, src_wire=src_wire, res_form=str(res_form), L=L,
-                mode=mode, inactive=[bool(x) for x in inactive], in_place=bool(in_place), cfg=cfg,
-                dist=str(rng.choice(["wide", "normal", "normal+outliers"])))
+                mode=mode, inactive=[bool(x) for x in inactive], in_place=bool(in_place), cfg=cfg, dist=dist)
+
+
+def plan_of(c: dict):
+    """The library's plan for the case's call (host-only; far-apart fake addresses)."""
+    base = [0x20_0000_0000 + k * 0x4_0000_0000 for k in range(40)]
+    R = c["R"]
+    n_dst = R if c["mode"] == ar.AR_MODE_RS_BCAST else 1
+    srcs = [0 if off else base[k] for k, off in enumerate(c["inactive"])]
+    dsts = [srcs[0]] if c["in_place"] else base[20:20 + n_dst]
+    flags = (ar.AR_SRC_WIRE if c["src_wire"] else 0) | (ar.AR_SRC_INACTIVE_NULL if any(c["inactive"]) else 0)
+    host = c["mode"] == ar.AR_MODE_HOST_STAGED
+    if c["res_form"] == "none":
+        return ar.ar_plan_query(dsts, srcs, c["n"], c["dst_type"], c["wire"], c["mode"] | flags,
+                                srcs_on_host=host, config=c["cfg"], R=R)
+    rl = c["n"] if c["res_form"] == "elementwise" else c["L"]
+    return ar.ar_plan_query_add(dsts, srcs, c["n"], c["dst_type"], c["wire"], c["mode"] | flags, base[39], rl,
+                                srcs_on_host=host, config=c["cfg"], R=R)
 
 
 def run_case(c: dict) -> None:
@@ -137,6 +167,18 @@ def test_case_generator_is_deterministic_and_varied():
     seen = {(c["mode"], c["res_form"], c["dst_type"] != ar.AR_F32) for c in cases}
     assert len(seen) >= 20
     assert any(c["in_place"] for c in cases) and any(any(c["inactive"]) for c in cases)
+    # every plan is valid; the two-rank kernels (binary32, with each residual form, and 16-bit)
+    # occur beside the single-shot and both streaming families
+    kinds = []
+    for c in cases:
+        rc, plan = plan_of(c)
+        assert rc == ar.AR_OK, (c, ar.ar_status_str(rc))
+        kinds.append((int(plan.stream_kernel), int(plan.dst_bytes), c["res_form"]))
+    kernels = {k for k, _, _ in kinds}
+    assert {0, 1, 2, 3} <= kernels
+    pair32 = [r for k, b, r in kinds if k == 3 and b == 4]
+    assert len(pair32) >= 40 and {"none", "elementwise", "row"} <= set(pair32)
+    assert sum(1 for k, b, _ in kinds if k == 3 and b == 2) >= 5
 
 
 @pytest.fixture(scope="module")
@@ -145,6 +187,7 @@ def gpu():
         pytest.skip("no GPU visible")
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("start", range(CASE_START, CASE_STOP, BATCH))
 def test_random_sweep(gpu, start):
     for i in range(start, min(start + BATCH, CASE_STOP)):
