@@ -212,6 +212,9 @@ def parse():
                    help="instead of the benchmark: the prefill call's reduce and its 2 : 1 ceiling kernel at "
                         "n = 2^20 ... 2^26 elements, with a fitted fixed per-call cost and streaming rate; "
                         "one JSON line")
+    p.add_argument("--summarize-footprint", metavar="ROOT",
+                   help="write profiles/counters_prefill_footprint.md from the FOOTPRINT_PASSES runs and "
+                        "kernel traces under ROOT (8 and 16 rotated sets)")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="write profiles/counters_<workload>.md from the rocprofv3 --pmc runs of COUNTER_PASSES")
     p.add_argument("--profile-pass", action="store_true",
@@ -228,7 +231,10 @@ LEAD_IN_CALLS = 3
 
 def main() -> int:
     args = parse()
-    if args.summarize_trace or args.summarize_pass_trace or args.summarize_pmc or args.summarize_counters:
+    if (args.summarize_trace or args.summarize_pass_trace or args.summarize_pmc or args.summarize_counters or
+            args.summarize_footprint):
+        if args.summarize_footprint:
+            summarize_footprint(args.summarize_footprint)
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, args.profile_workload)
         if args.summarize_pass_trace:
@@ -468,6 +474,9 @@ PROFILE_CASES = {
     "prefill_bf16_one_set": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1,
                                  sets=1, host=False,
                                  what="prefill reduce without rotation (one input set, MALL-resident)"),
+    "prefill_bf16_16_sets": dict(R=2, n=2048 * 4096, wire="bf16", mode="chunked", src_bytes=4, n_dst=1,
+                                 sets=16, host=False,
+                                 what="prefill reduce over 16 rotated sets (1.5 GiB touched; run with --sets 16)"),
     "slice_bcast_f16": dict(R=4, n=2048 * 8192, wire="f16", mode="rs_bcast", src_bytes=4, n_dst=4, sets=2,
                             host=False, what="slice + broadcast: R=4 fp32 partials [2048x8192], fp16 wire, "
                                              "4 destinations, RS_BCAST"),
@@ -622,6 +631,68 @@ COUNTER_PASSES = {
 }
 COUNTER_CMD = ("cd /tmp && rocprofv3 --pmc {counters} --output-format csv -d <dir> -o {tag} -- "
                "python3 /root/repo/bench.py --profile-pass --profile-workload {wl}")
+
+
+# Counter passes that compare the prefill call at two footprints (the default 8
+# rotated sets, 768 MiB touched per cycle, and 16 sets, 1.5 GiB): per-CU address
+# translation (UTCL1) and the shared translation cache's activity, and the L2's
+# memory requests.  Each pass, and a kernel trace, runs once per footprint.
+FOOTPRINT_PASSES = {
+    "utcl": "TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum TCP_UTCL1_REQUEST_sum "
+            "TCP_UTCL1_PERMISSION_MISS_sum",
+    "utcl_stall": "TCP_CLIENT_UTCL1_INFLIGHT_sum TCP_UTCL1_TRANSLATION_MISS_UNDER_MISS_sum "
+                  "TCP_UTCL1_STALL_MULTI_MISS_sum TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS_sum GRBM_UTCL2_BUSY "
+                  "GRBM_GUI_ACTIVE",
+    "dram": "TCC_EA0_RDREQ_DRAM_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_DRAM_sum TCC_EA0_WRREQ_sum "
+            "TCP_UTCL1_STALL_INFLIGHT_MAX_sum TCP_UTCL1_STALL_LRU_INFLIGHT_sum TCP_UTCL1_THRASHING_STALL_sum "
+            "TCP_UTCL1_LFIFO_FULL_sum",
+}
+FOOTPRINT_SETS = {8: "prefill_bf16", 16: "prefill_bf16_16_sets"}
+FOOTPRINT_CMD = ("cd /tmp && rocprofv3 {what} --output-format csv -d <root>/{tag}{sets} -o {tag} -- "
+                 "python3 /root/repo/bench.py --profile-pass --profile-workload {wl} --sets {sets}")
+
+
+def summarize_footprint(root: str) -> str:
+    """profiles/counters_prefill_footprint.md from <root>/<pass><sets> directories
+    (FOOTPRINT_PASSES and a kernel trace "trace", for 8 and 16 sets): the prefill
+    kernel's per-dispatch counters and traced duration at both footprints."""
+    vals = {}
+    for sets in FOOTPRINT_SETS:
+        for tag in FOOTPRINT_PASSES:
+            for r in _csv_rows(os.path.join(root, f"{tag}{sets}"), "counter_collection.csv"):
+                if is_reduce_kernel(r["Kernel_Name"]):
+                    vals.setdefault(r["Counter_Name"], {}).setdefault(sets, []).append(float(r["Counter_Value"]))
+    durs = {}
+    for sets in FOOTPRINT_SETS:
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in _dispatch_rows(os.path.join(root, f"trace{sets}")) if is_reduce_kernel(r["Kernel_Name"])]
+        if not d:
+            raise RuntimeError(f"no prefill dispatches in {root}/trace{sets}")
+        durs[sets] = (sum(d) / len(d), len(d))
+    if not vals:
+        raise RuntimeError(f"no prefill dispatches in the counter passes under {root}")
+    lines = ["# Prefill reduce at two footprints: 8 rotated sets (768 MiB touched) against 16 (1.5 GiB)", "",
+             "Commands (one per footprint; `{sets}` 8 with workload `prefill_bf16`, 16 with "
+             "`prefill_bf16_16_sets`):", ""]
+    lines.append(f"- `{FOOTPRINT_CMD.format(what='--kernel-trace --stats', tag='trace', sets='{sets}', wl='<workload>')}`")
+    for tag, counters in FOOTPRINT_PASSES.items():
+        lines.append(f"- `{FOOTPRINT_CMD.format(what='--pmc ' + counters, tag=tag, sets='{sets}', wl='<workload>')}`")
+    lines += ["", f"Kernel `{REDUCE_KERNEL}`; kernel source hash {kernel_source_hash()}.", "",
+              "| per dispatch (mean) | 8 sets | 16 sets | 16 / 8 |", "|---|---|---|---|"]
+    a, b = durs[8][0], durs[16][0]
+    lines.append(f"| traced duration, us ({durs[8][1]} / {durs[16][1]} dispatches) | {a:.3f} | {b:.3f} | {b / a:.3f} |")
+    for c in sorted(vals):
+        v8, v16 = vals[c].get(8), vals[c].get(16)
+        if not v8 or not v16:
+            continue
+        m8, m16 = sum(v8) / len(v8), sum(v16) / len(v16)
+        ratio = f"{m16 / m8:.3f}" if m8 else "—"
+        lines.append(f"| {c} | {m8:.1f} | {m16:.1f} | {ratio} |")
+    out = os.path.join(ROOT, "profiles", "counters_prefill_footprint.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
+    return out
 
 
 def summarize_counters(dirs: list, wl: str) -> None:

@@ -184,3 +184,27 @@ def test_headline_trace_takes_the_prefill_grid_only(tmp_path, monkeypatch):
     assert "profile pass of" in pass_text and "--profile-workload prefill_bf16" in pass_text
     assert "average 20.000 us per launch" in pass_text
     assert (tmp_path / "profiles" / "kernel_trace_prefill_bf16.md").read_text() == text
+
+
+def test_footprint_summary_compares_the_two_footprints(tmp_path, monkeypatch):
+    """The footprint summary averages the prefill kernel's counters per footprint (other
+    kernels ignored) and its traced durations, and writes both beside their ratio."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    root = tmp_path / "fp"
+    pair = "void mpp::(anonymous namespace)::k_pair<2>(unsigned int, unsigned int, float*, float const*, float const*, unsigned int)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
+    for sets, scale in ((8, 1.0), (16, 1.5)):
+        for tag in bench.FOOTPRINT_PASSES:
+            write_counters(root / f"{tag}{sets}", "TCP_UTCL1_TRANSLATION_MISS_sum" if tag == "utcl" else f"X_{tag}",
+                           [(pair, 100.0 * scale), (pair, 300.0 * scale), (neg, 1e6)])
+        d = root / f"trace{sets}"
+        os.makedirs(d)
+        with open(d / "trace_kernel_trace.csv", "w") as fh:
+            fh.write('"Kernel_Name","Start_Timestamp","End_Timestamp","Workgroup_Size_X","Grid_Size_X"\n')
+            fh.write(f'"{pair}",1000,{1000 + int(15_000 * scale)},64,1048576\n')
+            fh.write(f'"{neg}",90000,190000,256,1048576\n')
+    text = open(bench.summarize_footprint(str(root))).read()
+    assert "| traced duration, us (1 / 1 dispatches) | 15.000 | 22.500 | 1.500 |" in text
+    assert "| TCP_UTCL1_TRANSLATION_MISS_sum | 200.0 | 300.0 | 1.500 |" in text
+    assert "--profile-workload <workload> --sets {sets}" in text and bench.kernel_source_hash() in text
