@@ -15,7 +15,7 @@ import torch
 
 import mixed_precision_partial_amd as ar
 import oracle
-from gpu_util import assert_bits_equal, log_case
+from gpu_util import assert_bits_equal, assert_bits_equal16, log_case
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,31 @@ def test_beyond_one_launch(ctx):
     assert torch.equal(dsts[0].view(torch.int32), dsts[1].view(torch.int32))
     assert_bits_equal(gather(dsts[1], idx), want_res, "rs_bcast residual")
     del dsts, srcs, res
+    free()
+
+
+def test_two_rank_16bit_beyond_one_launch(ctx):
+    """n = 2^30 + 2^20 + 4099 bf16 partials into a bf16 destination, on the two-rank 16-bit
+    kernel: both schedules cut the call into launch pieces, the last one with a ragged tail."""
+    n = LAUNCH + (1 << 20) + 4099
+    rc, plan = ar.ar_plan_query([0x10_0000_0000], [0x20_0000_0000, 0x30_0000_0000], n, ar.AR_BF16, ar.AR_BF16,
+                                ar.AR_MODE_CHUNKED)
+    assert rc == ar.AR_OK and plan.stream_kernel == 3
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20_005)
+    srcs = [torch.randn(n, device="cuda", generator=g).bfloat16().view(torch.int16) for _ in range(2)]
+    idx = sample_indices(n, [LAUNCH, LAUNCH - 512, 1 << 29, n - 4099], 9)
+    want = oracle.reduce([gather(s, idx) for s in srcs], ar.AR_BF16, dst_type=ar.AR_BF16)[0]
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    for mode_name, mode in (("chunked", ar.AR_MODE_CHUNKED), ("single_shot", ar.AR_MODE_SINGLE_SHOT)):
+        what = f"n={n} bf16 -> bf16 {mode_name}"
+        log_case(what)
+        out.fill_(-1)         # 0xffff, a NaN pattern the finite inputs never produce
+        ar.ar_reduce(ctx, [out], srcs, n, ar.AR_BF16, ar.AR_BF16, mode)
+        torch.cuda.synchronize()
+        assert not (out == -1).any().item(), f"{what}: some element left unwritten"
+        assert_bits_equal16(gather(out, idx), want, ar.AR_BF16, what)
+    del out, srcs
     free()
 
 
