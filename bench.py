@@ -1539,9 +1539,22 @@ def other_schedules(torch, ar, wl):
     stream = torch.cuda.current_stream()
 
     def timed(fn, reps):
-        """milliseconds per call (one lead-in call, HipEvents on the stream)"""
+        """milliseconds per call (one warm-up call, the headline's lead-in calls, HipEvents
+        on the stream)"""
         fn()
-        return timed_us(torch, stream, lambda k: fn(), reps) / 1e3
+        return timed_us(torch, stream, lambda k: fn(), reps, lead=LEAD_IN_CALLS) / 1e3
+
+    def rotating(calls):
+        """One call of a rotation over pre-bound calls (arguments converted to C types once,
+        as in the headline's timed region); a failed status raises."""
+        k = [0]
+
+        def call():
+            rc = calls[k[0] % len(calls)]()
+            k[0] += 1
+            if rc != ar.AR_OK:
+                raise ar.ArError(rc, "bound reduce")
+        return call
 
     ctx = ar.ar_init(0)
     # the 4-rank broadcast over two rotated sets (1 GiB, beyond the Infinity Cache)
@@ -1549,25 +1562,17 @@ def other_schedules(torch, ar, wl):
     bsets = 2
     srcs = [[torch.from_numpy(p).cuda() for p in wl.partials(w, k)] for k in range(bsets)]
     dsts = [[torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.R)] for _ in range(bsets)]
-    kb = [0]
 
-    def brot(fn):
-        def call():
-            i = kb[0] % bsets
-            kb[0] += 1
-            fn(i)
-        return call
-
-    ms = timed(brot(lambda i: ar.ar_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
-                                           stream=stream)), 50)
+    ms = timed(rotating([ar.bind_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
+                                        stream=stream) for i in range(bsets)]), 50)
     b = 2 * w.R * w.n * 4
     out["slice_bcast_f16"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     with_ceiling(out["slice_bcast_f16"], pattern_ceiling(torch, stream, 4, 4, srcs, dsts, w.n * 4, 30))
     log(f"slice_bcast_f16: {out['slice_bcast_f16']}")
     # the same broadcast with an element-wise fp32 residual (the receiving rank's hidden state)
     ress = [torch.from_numpy(wl.residual(w.case, 5 + k, w.n)).cuda() for k in range(bsets)]
-    ms = timed(brot(lambda i: ar.ar_reduce_add(ctx, dsts[i], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
-                                               ress[i], stream=stream)), 50)
+    ms = timed(rotating([ar.bind_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_RS_BCAST,
+                                        stream=stream, residual=ress[i]) for i in range(bsets)]), 50)
     b = 2 * w.R * w.n * 4 + w.n * 4
     out["slice_bcast_f16_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"slice_bcast_f16_residual: {out['slice_bcast_f16_residual']}")
@@ -1583,51 +1588,37 @@ def other_schedules(torch, ar, wl):
     dsts = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(sets)]
     ress = [torch.from_numpy(wl.residual(w.case, k, w.n)).cuda() for k in range(sets)]
     row = torch.from_numpy(wl.residual(w.case, 9, 4096)).cuda()
-    k = [0]
-
-    def rot(fn):
-        def call():
-            i = k[0] % sets
-            k[0] += 1
-            fn(i)
-        return call
 
     # the same reduce with an fp32 wire: the difference to the headline is the narrowing's cost
-    ms = timed(rot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, ar.AR_F32, ar.AR_MODE_CHUNKED,
-                                          stream=stream)), 200)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, ar.AR_F32, ar.AR_MODE_CHUNKED,
+                                        stream=stream) for i in range(sets)]), 200)
     b = w.R * w.n * 4 + w.n * 4
     out["prefill_f32_wire"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_f32_wire: {out['prefill_f32_wire']}")
-    ms = timed(rot(lambda i: ar.ar_reduce_add(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
-                                              ress[i], w.n, stream=stream)), 200)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                        stream=stream, residual=ress[i], residual_len=w.n)
+                         for i in range(sets)]), 200)
     b = w.R * w.n * 4 + w.n * 4 + w.n * 4
     out["prefill_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_residual: {out['prefill_residual']}")
-    ms = timed(rot(lambda i: ar.ar_reduce_add(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
-                                              row, 4096, stream=stream)), 200)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                        stream=stream, residual=row, residual_len=4096) for i in range(sets)]), 200)
     b = w.R * w.n * 4 + w.n * 4 + 4096 * 4
     out["prefill_row_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_row_residual: {out['prefill_row_residual']}")
     del srcs, dsts, ress
     # the headline call over 16 rotated sets (1.5 GiB touched): past about 1 GiB of touched
     # memory every streaming kernel here, the ceiling kernel included, runs ~8 % slower than
-    # at the headline's 768 MiB (translation reach, not the 256 MiB Infinity Cache: the step
-    # lies between 768 MiB and 1152 MiB and does not move when only half of each buffer is
-    # touched); reported beside its own ceiling kernel
+    # at the headline's 768 MiB (not the 256 MiB Infinity Cache: the step lies between 768 MiB
+    # and 1152 MiB and does not move when only half of each buffer is touched; not extra DRAM
+    # requests or translation misses either, by the counters of --summarize-footprint);
+    # reported beside its own ceiling kernel
     big = 16
     srcs = [[torch.randn(w.n, device="cuda") for _ in range(2)] for _ in range(big)]
     dsts = [torch.empty(w.n, device="cuda") for _ in range(big)]
-    kf = [0]
 
-    def frot(fn):
-        def call():
-            i = kf[0] % big
-            kf[0] += 1
-            fn(i)
-        return call
-
-    ms = timed(frot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
-                                           stream=stream)), 400)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                        stream=stream) for i in range(big)]), 400)
     b = w.R * w.n * 4 + w.n * 4
     out["prefill_footprint_1536MiB"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1), "sets": big}
     with_ceiling(out["prefill_footprint_1536MiB"],
@@ -1640,8 +1631,8 @@ def other_schedules(torch, ar, wl):
     srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_BF16).view(np.int16)).cuda() for p in wl.partials(w, k)]
             for k in range(sets)]
     dsts = [torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(sets)]
-    ms = timed(rot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED,
-                                          stream=stream)), 200)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_BF16, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                                        stream=stream) for i in range(sets)]), 200)
     b = w.R * w.n * 2 + w.n * 2
     out["prefill_bf16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     with_ceiling(out["prefill_bf16_dst"],
@@ -1651,8 +1642,9 @@ def other_schedules(torch, ar, wl):
     # four ranks on the prefill shape with rank 2 inactive (it contributes +0.0 and is not read)
     srcs = [[None if r == 2 else torch.randn(w.n, device="cuda") for r in range(4)] for _ in range(sets)]
     dsts = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(sets)]
-    ms = timed(rot(lambda i: ar.ar_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire,
-                                          ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL, stream=stream)), 200)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire,
+                                        ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL, stream=stream)
+                         for i in range(sets)]), 200)
     b = 3 * w.n * 4 + w.n * 4
     out["prefill_r4_one_inactive"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"prefill_r4_one_inactive: {out['prefill_r4_one_inactive']}")
@@ -1664,8 +1656,9 @@ def other_schedules(torch, ar, wl):
     srcs = [[torch.randn(rows * ss, device="cuda") for _ in range(2)] for _ in range(sets)]
     dsts = [torch.empty(rows * ds, device="cuda") for _ in range(sets)]
     bias = torch.randn(cols, device="cuda")
-    ms = timed(rot(lambda i: ar.ar_reduce_rows(ctx, [dsts[i]], srcs[i], rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16,
-                                               ar.AR_MODE_CHUNKED, residual=bias, res_stride=0, stream=stream)), 200)
+    ms = timed(rotating([ar.bind_reduce_rows(ctx, [dsts[i]], srcs[i], rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16,
+                                             ar.AR_MODE_CHUNKED, residual=bias, res_stride=0, stream=stream)
+                         for i in range(sets)]), 200)
     b = 2 * rows * cols * 4 + rows * cols * 4 + cols * 4
     out["rows_prefill_block_bias"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"rows_prefill_block_bias: {out['rows_prefill_block_bias']}")
@@ -1679,8 +1672,8 @@ def other_schedules(torch, ar, wl):
     srcs = [[torch.from_numpy(wl.as_wire_typed(p, ar.AR_F16).view(np.int16)).cuda() for p in wl.partials(w, k)]
             for k in range(bsets)]
     dsts = [[torch.empty(w.n, dtype=torch.int16, device="cuda") for _ in range(w.R)] for _ in range(bsets)]
-    ms = timed(brot(lambda i: ar.ar_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_RS_BCAST,
-                                           stream=stream)), 50)
+    ms = timed(rotating([ar.bind_reduce(ctx, dsts[i], srcs[i], w.n, ar.AR_F16, ar.AR_F16, ar.AR_MODE_RS_BCAST,
+                                        stream=stream) for i in range(bsets)]), 50)
     b = w.R * w.n * 2 + w.R * w.n * 2
     out["slice_bcast_f16_dst"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     with_ceiling(out["slice_bcast_f16_dst"], pattern_ceiling(torch, stream, 4, 4, srcs, dsts, w.n * 2, 50))
@@ -1691,16 +1684,16 @@ def other_schedules(torch, ar, wl):
     parts = wl.partials(w, 0)
     srcs32 = [torch.from_numpy(p).cuda() for p in parts]
     dst = torch.empty(w.n, dtype=torch.float32, device="cuda")
-    ms = timed(lambda: ar.ar_reduce(ctx, [dst], srcs32, w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
-                                    stream=stream), 20)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dst], srcs32, w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                        stream=stream)]), 20)
     b = w.R * w.n * 4 + w.n * 4
     out["r8_hbm_fp32_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     with_ceiling(out["r8_hbm_fp32_src"], pattern_ceiling(torch, stream, 8, 1, [srcs32], [[dst]], w.n * 4, 10))
     log(f"r8_hbm_fp32_src: {out['r8_hbm_fp32_src']}")
     # the prefill reduce's kernel on a call 8 x larger (two of the same [8192 x 8192] fp32
     # partials, 768 MiB per call): the per-call fixed cost amortised, beside its ceiling kernel
-    ms = timed(lambda: ar.ar_reduce(ctx, [dst], srcs32[:2], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
-                                    stream=stream), 30)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dst], srcs32[:2], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
+                                        stream=stream)]), 30)
     b = 2 * w.n * 4 + w.n * 4
     out["r2_large_fp32_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1), "n": w.n}
     with_ceiling(out["r2_large_fp32_src"], pattern_ceiling(torch, stream, 2, 1, [srcs32[:2]], [[dst]], w.n * 4, 10))
@@ -1708,8 +1701,8 @@ def other_schedules(torch, ar, wl):
     del srcs32
     pre = [wl.as_wire_typed(p, w.wire) for p in parts]
     srcs16 = [torch.from_numpy(p.view(np.int16)).cuda() for p in pre]
-    ms = timed(lambda: ar.ar_reduce(ctx, [dst], srcs16, w.n, ar.AR_F32, w.wire,
-                                    ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, stream=stream), 20)
+    ms = timed(rotating([ar.bind_reduce(ctx, [dst], srcs16, w.n, ar.AR_F32, w.wire,
+                                        ar.AR_MODE_CHUNKED | ar.AR_SRC_WIRE, stream=stream)]), 20)
     b = w.R * w.n * 2 + w.n * 4
     out["r8_hbm_bf16_src"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
     log(f"r8_hbm_bf16_src: {out['r8_hbm_bf16_src']}")

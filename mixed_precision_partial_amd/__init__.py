@@ -27,7 +27,8 @@ The library sees only pointers, so it cannot tell how large a buffer is.  With
 that every tensor argument spans the bytes the call will read or write from its
 data pointer (and, for the 1-D calls, that it is contiguous), raising
 ``ValueError`` otherwise; integer addresses and ``ptr_array`` arrays are the
-caller's responsibility, as in C.  ``bind_reduce`` checks once, when it binds.
+caller's responsibility, as in C.  ``bind_reduce`` and ``bind_reduce_rows`` check once,
+when they bind.
 """
 from __future__ import annotations
 
@@ -415,6 +416,27 @@ def ar_reduce_rows(ctx, dsts, srcs, rows: int, cols: int, src_stride: int, dst_s
     if check and rc != AR_OK:
         raise ArError(rc, "ar_reduce_rows")
     return rc
+
+
+def bind_reduce_rows(ctx, dsts, srcs, rows: int, cols: int, src_stride: int, dst_stride: int, dst_type: int,
+                     wire_type: int, mode: int, residual=None, res_stride: int = 0, stream=None):
+    """ar_reduce_rows with every argument converted to its C type once (the tensors'
+    spans checked once, as ar_reduce_rows checks them): returns a callable that
+    enqueues the call again each time it is invoked and returns the status (the
+    library still validates every call).  The caller keeps the context and the
+    bound buffers alive while the callable is in use."""
+    import functools
+
+    lib = load_library()
+    R = len(srcs) if srcs is not None else 0
+    _check_counts(dsts, srcs, mode)
+    _validate_rows(dsts, srcs, rows, cols, src_stride, dst_stride, dst_type, wire_type, mode, residual, res_stride)
+    shape = ctypes.pointer(ArRows(int(rows), int(cols), int(src_stride), int(dst_stride), int(res_stride)))
+    ctx_val = ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx
+    return functools.partial(lib.ar_reduce_rows, ctypes.c_void_p(ctx_val), _ptr_array(dsts), _ptr_array(srcs),
+                             ctypes.c_int(R), shape, ctypes.c_int(int(dst_type)), ctypes.c_int(int(wire_type)),
+                             ctypes.c_uint(int(mode)), ctypes.c_void_p(_addr(residual)),
+                             ctypes.c_void_p(_stream_handle(stream)))
 
 
 def ar_free(ctx) -> None:

@@ -451,6 +451,9 @@ def test_bound_calls_reach_the_library():
     g = ar.bind_reduce(None, [1 << 34], fake, 4096, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
                        residual=1 << 35, residual_len=512)
     assert g() == ar.AR_ERR_INVALID
+    h = ar.bind_reduce_rows(None, [1 << 34], fake, 4, 512, 640, 576, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                            residual=1 << 35)
+    assert h() == ar.AR_ERR_INVALID and h() == ar.AR_ERR_INVALID
 
 
 def test_binding_checks_tensor_sizes_before_the_call():
@@ -502,6 +505,8 @@ def test_binding_checks_tensor_sizes_before_the_call():
         ar.ar_reduce_rows(None, [dst], srcs, rows, cols, ss, ds, F, B, C, residual=torch.empty(cols - 1))
     assert ar.ar_reduce_rows(None, [dst], srcs, rows, cols, ss, ds, F, B, C, residual=torch.empty(cols),
                              check=False) == ar.AR_ERR_INVALID
+    with pytest.raises(ValueError, match="srcs"):
+        ar.bind_reduce_rows(None, [dst], [srcs[0], torch.empty(rows, ss)[1:, :cols]], rows, cols, ss, ds, F, B, C)
 
 
 def test_bound_calls_use_the_compiled_call_type():

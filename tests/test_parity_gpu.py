@@ -490,6 +490,20 @@ def test_bound_calls_match_plain_calls(ctx):
                 assert f() == ar.AR_OK
                 torch.cuda.synchronize()
                 assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+    # row-strided: rows of 4096 inside 4608-wide partial rows, with a bias row
+    rows, cols, ss, ds = 33, 4096, 4608, 4352
+    rsrcs = [torch.randn(rows * ss, device="cuda") for _ in range(2)]
+    rwant = torch.full((rows * ds,), float("nan"), device="cuda")
+    rgot = torch.full((rows * ds,), float("nan"), device="cuda")
+    ar.ar_reduce_rows(ctx, [rwant], rsrcs, rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                      residual=row, res_stride=0)
+    f = ar.bind_reduce_rows(ctx, [rgot], rsrcs, rows, cols, ss, ds, ar.AR_F32, ar.AR_BF16, ar.AR_MODE_CHUNKED,
+                            residual=row, res_stride=0)
+    for _ in range(2):
+        assert f() == ar.AR_OK
+        torch.cuda.synchronize()
+        assert torch.equal(rgot.view(torch.int32), rwant.view(torch.int32))
+        rgot.fill_(float("nan"))
 
 
 def test_contexts_on_threads_and_streams():
