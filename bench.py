@@ -460,7 +460,7 @@ def is_reduce_kernel(name: str) -> bool:
 def is_library_kernel(name: str) -> bool:
     """Any kernel of the reduce library (every streaming and single-shot instance)."""
     plain = _plain_name(name)
-    return "k_stream_" in plain or "k_single_shot" in plain or "k_pair" in plain
+    return "k_stream_" in plain or "k_single_shot" in plain or "k_pair" in plain or "k_few" in plain
 
 
 CALIBRATION_KERNEL = "neg_kernel"   # torch.neg, the calibration copy (other elementwise kernels may run)
@@ -991,12 +991,14 @@ def hold_study(torch, ar, wl, args, reps: int = 7) -> int:
     element-wise residual, 4096-element broadcast row) and the row-strided prefill block
     (2048 x 4096 in rows of 4608 / 4352: plain, strided residual, bias row), each on the
     two-rank kernels unheld (-1), held to 14, 16, 18 or 20 waves per CU, and automatic (0);
+    the prefill shape with three ranks, four with rank 2 inactive, four, and two active of
+    four, on the kernels for a few active partials unheld, held to 10, 14 or 18, and automatic;
     the 4-rank broadcast (cfg 4), the bf16 -> bf16 prefill shape and R = 8 fp32 partials on
     their automatic general kernels unheld and held to 8, 12 or 16 waves.  Outputs are
     compared bit for bit across holds before timing; holds are timed interleaved, rep by
     rep, medians reported.  One JSON line."""
     stream = torch.cuda.current_stream()
-    holds = sorted({-1, 0, 8, 12, 14, 16, 18, 20})
+    holds = sorted({-1, 0, 8, 10, 12, 14, 16, 18, 20})
     ctxs = {h: ar.ar_init(0, {"occupancy_hold": h} if h else None) for h in holds}
     out = {"metric": "us per call by occupancy hold (waves per CU; -1 none, 0 automatic)", "reps": reps}
 
@@ -1037,6 +1039,20 @@ def hold_study(torch, ar, wl, args, reps: int = 7) -> int:
         measure(f"prefill_{form}", pair_holds, 1000, lambda h, k, form=form: bound[(h, form)][k % S](), nbytes,
                 lambda: dst[0].view(torch.int32))
     del src, dst, res, bound
+    torch.cuda.empty_cache()
+    few_holds = [-1, 10, 14, 18, 0]
+    f_src = [[torch.randn(n, device="cuda") for _ in range(4)] for _ in range(S)]
+    f_dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(S)]
+    inact = ar.AR_SRC_INACTIVE_NULL
+    for form, pick, flags, nbytes in (("r3", lambda q: q[:3], 0, 16 * n),
+                                      ("r4_rank2_inactive", lambda q: [q[0], q[1], None, q[3]], inact, 16 * n),
+                                      ("r4", lambda q: q, 0, 20 * n),
+                                      ("r4_two_active", lambda q: [None, q[1], None, q[3]], inact, 12 * n)):
+        fb = {h: [ar.bind_reduce(ctxs[h], [f_dst[i]], pick(f_src[i]), n, ar.AR_F32, w.wire,
+                                 ar.AR_MODE_CHUNKED | flags, stream=stream) for i in range(S)] for h in few_holds}
+        measure(f"few_{form}", few_holds, 1000, lambda h, k, fb=fb: fb[h][k % S](), nbytes,
+                lambda: f_dst[0].view(torch.int32))
+    del f_src, f_dst
     torch.cuda.empty_cache()
     rows, cols, ss, ds = 2048, 4096, 4608, 4352
     R6 = 6
@@ -1600,6 +1616,10 @@ def other_schedules(torch, ar, wl):
                          for i in range(sets)]), 200)
     b = w.R * w.n * 4 + w.n * 4 + w.n * 4
     out["prefill_residual"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    # its ceiling: three read streams (the partials and the residual) and one write
+    with_ceiling(out["prefill_residual"],
+                 pattern_ceiling(torch, stream, 3, 1, [srcs[i] + [ress[i]] for i in range(sets)],
+                                 [[d] for d in dsts], w.n * 4, 200))
     log(f"prefill_residual: {out['prefill_residual']}")
     ms = timed(rotating([ar.bind_reduce(ctx, [dsts[i]], srcs[i], w.n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED,
                                         stream=stream, residual=row, residual_len=4096) for i in range(sets)]), 200)
@@ -1647,6 +1667,9 @@ def other_schedules(torch, ar, wl):
                          for i in range(sets)]), 200)
     b = 3 * w.n * 4 + w.n * 4
     out["prefill_r4_one_inactive"] = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1)}
+    with_ceiling(out["prefill_r4_one_inactive"],
+                 pattern_ceiling(torch, stream, 3, 1, [[t for t in s if t is not None] for s in srcs],
+                                 [[d] for d in dsts], w.n * 4, 200))
     log(f"prefill_r4_one_inactive: {out['prefill_r4_one_inactive']}")
     del srcs, dsts
     # row-strided: the prefill block as a view of wider rows (2048 x 4096 in rows of

@@ -445,16 +445,26 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             cfg.grid_wgs == 0) {
             plan->stream_kernel = 3;
         }
+        // the kernels for two to four active binary32 partials: three or four
+        // ranks, or two to four active ones among more, no residual,
+        // contiguous, the two-rank kernels' conditions otherwise
+        if ((resolved == AR_MODE_CHUNKED || resolved == AR_MODE_SINGLE_SHOT) && cfg.stream_kernel == 0 &&
+            rows == nullptr && res_kind == 0 && !src_wire && dst_bytes == 4 && !plan->store_nt &&
+            cfg.grid_wgs == 0 && n_active >= 2 && n_active <= 4 && !(R == 2 && active == 0x3u)) {
+            plan->stream_kernel = 4;
+        }
         // occupancy hold: an explicit one holds every streaming launch; the
-        // automatic one holds the binary32 two-rank kernels only (18 waves, 14
-        // with a residual: the figures are at kPairWaves); the general kernels
-        // and the 16-bit two-rank kernel gained nothing from one (bench.py
-        // --hold-study)
+        // automatic one holds the binary32 two-rank kernels (18 waves, 14 with
+        // a residual: the figures are at kPairWaves) and the kernels for two to
+        // four active partials (kFewWaves); the general kernels and the 16-bit
+        // two-rank kernel gained nothing from one (bench.py --hold-study)
         plan->hold_waves = 0;
         if (cfg.occupancy_hold > 0) {
             plan->hold_waves = plan->stream_kernel == 0 ? 0 : static_cast<int>(cfg.occupancy_hold);
         } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 3 && dst_bytes == 4) {
             plan->hold_waves = static_cast<int>(res_kind != 0 ? mpp::kPairResWaves : mpp::kPairWaves);
+        } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 4) {
+            plan->hold_waves = static_cast<int>(mpp::kFewWaves[n_active - 2]);
         }
     }
     return AR_OK;
@@ -656,6 +666,32 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
                                                        xcd_run_for(c->cfg, R, false),
                                                        static_cast<unsigned>(plan.hold_waves), cu_limits(c),
                                                        stream))) {
+                return rc;
+            }
+        }
+        return AR_OK;
+    }
+    if (plan.stream_kernel == 4) {
+        // two to four active binary32 partials: compacted in rank order, with
+        // the gaps where inactive ranks add +0.0; one 1-D launch per piece
+        const void *act[4] = {};
+        unsigned zmask = 0;
+        int A = 0;
+        for (int r = 0; r < R; ++r) {
+            if (srcs[r] == nullptr) {
+                zmask |= 1u << A;
+            } else {
+                act[A++] = srcs[r];
+            }
+        }
+        if (A < 2 || A > 4) return AR_ERR_INVALID;
+        for (size_t p0 = 0; p0 < n; p0 += mpp::kMaxLaunchElems) {
+            const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);
+            const void *piece[4] = {};
+            for (int a = 0; a < A; ++a) piece[a] = static_cast<const char *>(act[a]) + p0 * sb;
+            if (int rc = hip_status(mpp::launch_few(wire_type, A, len, static_cast<char *>(dst[0]) + p0 * db, piece,
+                                                    zmask, xcd_run_for(c->cfg, A, false),
+                                                    static_cast<unsigned>(plan.hold_waves), cu_limits(c), stream))) {
                 return rc;
             }
         }

@@ -1386,6 +1386,94 @@ __global__ __launch_bounds__(kPairBlock) void k_pair_res(unsigned tiles, unsigne
     pair_body<W, RK>(tiles, rem, dst, src0, src1, lc, res, res_len, res_phase);
 }
 
+// Kernels for two to four active binary32 partials (A) among more ranks, or
+// for three or four ranks, into one binary32 destination, contiguous, no
+// residual: the two-rank kernels' grid, preloaded parameters, placement and
+// stores, with the active partials passed compacted in rank order.  An
+// inactive rank contributes +0.0 at its place in the fold; adding +0.0 leaves
+// every value but -0.0 unchanged (-0.0 becomes +0.0), and adding -0.0 leaves
+// every value unchanged, so the fold adds z[g] = +0.0 or -0.0 at each gap g
+// (before active partial g, and after the last at g = A) according to
+// whether an inactive rank lies there (bit g of zmask): bit-identical with
+// the fold over all R ranks, with no branch between the loads.
+template <int W, int A>
+__device__ __forceinline__ u32x4 few_part(const u32x4 (&v)[A], const float (&z)[A + 1]) {
+    float x[A][4];
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[a][k] = f32_from_bits(v[a][k]);
+        wire_pair<W>(x[a][0], x[a][1]);
+        wire_pair<W>(x[a][2], x[a][3]);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float acc = x[0][k] + z[0];
+#pragma unroll
+        for (int a = 1; a < A; ++a) acc = (acc + z[a]) + x[a][k];
+        o[k] = bits_from_f32(acc + z[A]);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+template <int W, int A>
+__global__ __launch_bounds__(kPairBlock) void k_few(unsigned tiles, unsigned rem, float *dst, const float *s0,
+                                                    const float *s1, unsigned lc, const float *s2,
+                                                    const float *s3, unsigned zmask) {
+    static_assert(A >= 2 && A <= 4, "two to four active partials");
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned grid = tiles + (rem != 0 ? 1u : 0u);
+    const unsigned w = xcd_virtual_block(blockIdx.x, grid, lc);
+    const float *const s[4] = {s0, s1, s2, s3};
+    float z[A + 1];
+#pragma unroll
+    for (int g = 0; g <= A; ++g) z[g] = ((zmask >> g) & 1u) != 0 ? 0.0f : -0.0f;
+    if (w >= tiles) {
+        if (w == tiles && rem != 0) {
+            // the tail: every load issued unguarded at a clamped index, then the
+            // folds, then the guarded stores (see reduce_scalar)
+            constexpr int K = kWaveTile / kWave;
+            const size_t t = static_cast<size_t>(tiles) * kWaveTile;
+            float x[A][K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const unsigned e0 = lane + kWave * k;
+                const unsigned e = e0 < rem ? e0 : rem - 1;
+#pragma unroll
+                for (int a = 0; a < A; ++a) x[a][k] = s[a][t + e];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+#pragma unroll
+                for (int a = 0; a < A; ++a) {
+                    float unused = 0.0f;
+                    wire_pair<W>(x[a][k], unused);
+                }
+                float acc = x[0][k] + z[0];
+#pragma unroll
+                for (int a = 1; a < A; ++a) acc = (acc + z[a]) + x[a][k];
+                x[0][k] = acc + z[A];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const unsigned e = lane + kWave * k;
+                if (e < rem) dst[t + e] = x[0][k];
+            }
+        }
+        return;
+    }
+    const size_t t = static_cast<size_t>(w) * kWaveTile;
+    u32x4 v[2][A];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int a = 0; a < A; ++a) v[j][a] = load16<true>(s[a] + t + 256 * j + 4 * lane);
+    float *out = dst + t;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) store16_wt(out, kWaveTile * 4, (256 * j + 4 * lane) * 4, few_part<W, A>(v[j], z));
+}
+
 // Two-rank kernels over row-strided tensors whose rows are whole wave tiles
 // (cols a multiple of 512): the same per-tile work as the contiguous ones,
 // over one 1-D grid of every row's tiles, so that the XCD placement runs span
@@ -1530,6 +1618,8 @@ extern const void *const kSingleShot[2][2][kCombos][kBuckets];
 // two-rank contiguous kernels, indexed by [residual kind][wire type (ar_dtype)]
 extern const void *const kPair[5][3];
 extern const void *const kPair16[2];   // [0] fp16, [1] bf16
+// kernels for two to four active binary32 partials, [active partials - 2][wire type]
+extern const void *const kFew[3][3];
 // two-rank row-strided kernels, [residual kind][power-of-two tiles per row][wire type]
 extern const void *const kPairRows[3][2][3];
 extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,

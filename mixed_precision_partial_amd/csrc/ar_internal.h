@@ -169,6 +169,13 @@ inline unsigned hold_lds_bytes(const CuLimits &cu, uint64_t wgs, unsigned waves)
 // 15.63 unheld, 15.38 at 14, 15.52 at 18; the row-strided forms alike).
 constexpr unsigned kPairWaves = 18;
 constexpr unsigned kPairResWaves = 14;
+// Resident waves per CU the kernels for two to four active partials are held to
+// by default, by active partials (2, 3, 4): fewer streams in flight per wave
+// leave room for more waves (bench.py --hold-study, the prefill shape on one
+// box, bit-identical outputs: two active of four ranks 15.67 us unheld, 15.45
+// at 18 waves; three ranks 20.26 unheld, 19.76 at 14, 20.03 at 18; four
+// ranks 25.75 unheld, 25.11 at 10, 25.56 at 14).
+constexpr unsigned kFewWaves[3] = {18, 14, 10};
 
 // The two-rank contiguous kernels (k_pair, k_pair_res): dst[i] = wire(src0[i])
 // + wire(src1[i]) in binary32, then + res[i] (res_kind 1, element-wise) or
@@ -189,6 +196,17 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
 // a 16-bit device array, 16-byte aligned.
 hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
                          unsigned hold_waves, const CuLimits &cu, hipStream_t stream);
+
+// The kernels for two to four active binary32 partials (k_few): dst[i] = the
+// fold in rank order of wire(srcs[a][i]) over the `active` compacted active
+// partials, with +0.0 added at every gap g (before active partial g; g =
+// active after the last) whose bit g is set in zmask, where the fold over all
+// ranks meets inactive ones, for i < n (n <= kMaxLaunchElems), wire AR_F32,
+// AR_F16 or AR_BF16; one 1-D launch on `stream`, XCD runs of about run_elems
+// elements, every CU held to `hold_waves` resident waves (0: no hold).  Every
+// pointer is a binary32 device array, 16-byte aligned.
+hipError_t launch_few(int wire, int active, size_t n, void *dst, const void *const *srcs, unsigned zmask,
+                      size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream);
 
 // The two-rank kernels over row-strided tensors (k_pair_rows): row i, column
 // j of the destination = wire(src0) + wire(src1) (+ the residual: res_kind 1

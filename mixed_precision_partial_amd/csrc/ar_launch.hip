@@ -145,6 +145,27 @@ hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const 
                            hold_lds_bytes(cu, grid, hold_waves), stream);
 }
 
+hipError_t launch_few(int wire, int active, size_t n, void *dst, const void *const *srcs, unsigned zmask,
+                      size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream) {
+    if (wire < AR_F32 || wire > AR_BF16 || active < 2 || active > 4 || n == 0 || n > kMaxLaunchElems ||
+        srcs == nullptr || zmask >= (1u << (active + 1))) {
+        return hipErrorInvalidValue;
+    }
+    const float *s[4] = {};
+    for (int a = 0; a < active; ++a) {
+        if (srcs[a] == nullptr) return hipErrorInvalidValue;
+        s[a] = static_cast<const float *>(srcs[a]);
+    }
+    unsigned tiles = static_cast<unsigned>(n / kWaveTile);
+    unsigned rem = static_cast<unsigned>(n % kWaveTile);
+    const unsigned grid = tiles + (rem != 0 ? 1u : 0u);
+    unsigned lc = xcd_map_lc(grid, kWaveTile, run_elems);
+    float *d = static_cast<float *>(dst);
+    void *args[] = {&tiles, &rem, &d, &s[0], &s[1], &lc, &s[2], &s[3], &zmask};
+    return hipLaunchKernel(kFew[active - 2][wire], dim3(grid), dim3(kPairBlock), args,
+                           hold_lds_bytes(cu, grid, hold_waves), stream);
+}
+
 hipError_t launch_pair_rows(int wire, int res_kind, size_t rows, size_t cols, size_t src_stride, size_t dst_stride,
                             void *dst, const void *src0, const void *src1, const void *res, size_t res_stride,
                             size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream) {

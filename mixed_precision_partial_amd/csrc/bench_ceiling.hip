@@ -12,8 +12,9 @@
 // the work.  Loads are non-temporal; stores follow SP (0 write-back,
 // 1 non-temporal, 2 device-scope write-through).  R = 1, D = 1 is the plain
 // 16-byte copy kernel; R = 2, D = 1 the two-read / one-write stream of the
-// prefill reduce; R = 4, D = 4 the slice + broadcast pattern; R = 8, D = 1 the
-// eight-rank reduce.  A narrow-destination pattern is the same kernel at the
+// prefill reduce; R = 3, D = 1 the same with an element-wise residual, or
+// three active ranks; R = 4, D = 4 the slice + broadcast pattern; R = 8, D = 1
+// the eight-rank reduce.  A narrow-destination pattern is the same kernel at the
 // 16-bit byte counts (the data are bits either way).
 //
 // The tile count, the placement exponent and the stream pointers are scalar
@@ -87,12 +88,13 @@ __global__ __launch_bounds__(BLOCK) void k_pattern(unsigned tiles, unsigned lc, 
 }
 
 // Instances: [workgroup size: 256, 64][pattern][store policy]; patterns (R, D) =
-// (1,1), (2,1), (4,4), (8,1).
+// (1,1), (2,1), (4,4), (8,1), (3,1).
 #define MPP_CEIL_ROW(R, D, B) \
     {reinterpret_cast<const void *>(&k_pattern<R, D, 0, B>), reinterpret_cast<const void *>(&k_pattern<R, D, 1, B>), \
      reinterpret_cast<const void *>(&k_pattern<R, D, 2, B>)}
-#define MPP_CEIL_TABLE(B) {MPP_CEIL_ROW(1, 1, B), MPP_CEIL_ROW(2, 1, B), MPP_CEIL_ROW(4, 4, B), MPP_CEIL_ROW(8, 1, B)}
-const void *const kPatterns[2][4][3] = {MPP_CEIL_TABLE(256), MPP_CEIL_TABLE(64)};
+#define MPP_CEIL_TABLE(B) \
+    {MPP_CEIL_ROW(1, 1, B), MPP_CEIL_ROW(2, 1, B), MPP_CEIL_ROW(4, 4, B), MPP_CEIL_ROW(8, 1, B), MPP_CEIL_ROW(3, 1, B)}
+const void *const kPatterns[2][5][3] = {MPP_CEIL_TABLE(256), MPP_CEIL_TABLE(64)};
 #undef MPP_CEIL_TABLE
 #undef MPP_CEIL_ROW
 
@@ -101,6 +103,7 @@ int pattern_index(int R, int D) {
     if (R == 2 && D == 1) return 1;
     if (R == 4 && D == 4) return 2;
     if (R == 8 && D == 1) return 3;
+    if (R == 3 && D == 1) return 4;
     return -1;
 }
 

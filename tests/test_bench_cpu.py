@@ -141,6 +141,8 @@ def test_kernel_name_matchers():
     assert bench.is_library_kernel("void mpp::(anonymous namespace)::k_pair_res<2, 2>(unsigned int, ...)")
     assert not bench.is_reduce_kernel("void mpp::(anonymous namespace)::k_pair_res<2, 2>(unsigned int, ...)")
     assert bench.is_library_kernel("void k_single_shot<Cfg<0, false, false, 2, false, false> >(...)")
+    assert bench.is_library_kernel("void mpp::(anonymous namespace)::k_few<2, 3>(unsigned int, ...)")
+    assert not bench.is_reduce_kernel("void mpp::(anonymous namespace)::k_few<2, 3>(unsigned int, ...)")
     assert not bench.is_library_kernel("void at::native::vectorized_elementwise_kernel<4, neg_kernel_cuda>")
 
 

@@ -223,18 +223,21 @@ def test_stream_kernel_choice():
     broadcast schedule; host-staged calls
     LDS-staged for two 16-bit sources only; two active fp32 sources into one contiguous fp32
     destination, with or without a residual, kept stores and no forced grid take the two-rank
-    contiguous kernels (3), chunked or single-shot."""
+    contiguous kernels (3), chunked or single-shot; two to four active fp32 sources otherwise
+    (three or four ranks, or inactive ones among more), no residual, contiguous, the same
+    conditions, take the kernels for a few active partials (4)."""
     n = 2048 * 4096
     CH, BC, HS, SW = ar.AR_MODE_CHUNKED, ar.AR_MODE_RS_BCAST, ar.AR_MODE_HOST_STAGED, ar.AR_SRC_WIRE
     # single-shot: the two-rank kernel for its case, the single-shot kernel otherwise
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 3
     assert q(4096, mode=ar.AR_MODE_AUTO)[1].stream_kernel == 3          # AUTO resolves to SINGLE_SHOT
-    assert q(4096, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    assert q(4096, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 4
+    assert q(4096, R=5, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT | ar.AR_SRC_WIRE)[1].stream_kernel == 0
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT, config={"stream_kernel": 1})[1].stream_kernel == 0
     assert q(4096, mode=ar.AR_MODE_SINGLE_SHOT, config={"grid_wgs": 3})[1].stream_kernel == 0
-    for R in (2, 3, 4, 8, 16):
-        assert q(n, R=R, mode=CH)[1].stream_kernel == (3 if R == 2 else 1), R
+    for R in (2, 3, 4, 5, 8, 16):
+        assert q(n, R=R, mode=CH)[1].stream_kernel == {2: 3, 3: 4, 4: 4}.get(R, 1), R
     # the two-rank kernel only for its exact case: every wire type, automatic choice only
     for wire in (ar.AR_F32, ar.AR_F16, ar.AR_BF16):
         assert q(n, mode=CH, wire=wire)[1].stream_kernel == 3
@@ -244,7 +247,22 @@ def test_stream_kernel_choice():
     assert q(n, mode=CH, config={"grid_wgs": 7})[1].stream_kernel == 1
     assert q(n, mode=CH, config={"store_policy": 2})[1].stream_kernel == 1
     assert q(n, srcs=[A[1], 0], mode=CH | ar.AR_SRC_INACTIVE_NULL)[1].stream_kernel == 1
-    assert q(n, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 0
+    # two to four active fp32 partials among any rank count, automatic choice only, held
+    IN = CH | ar.AR_SRC_INACTIVE_NULL
+    for srcs in ([A[1], A[2], 0, A[4]], [0, A[2], A[3]], [A[1], 0, 0, 0, 0, 0, 0, A[8]],
+                 [0, A[2], 0, A[4], A[5], 0, A[7], 0], [A[i] for i in range(1, 5)]):
+        rc, p = q(n, srcs=srcs, mode=IN)
+        held = {2: 18, 3: 14, 4: 10}[sum(1 for x in srcs if x)]
+        assert rc == ar.AR_OK and p.stream_kernel == 4 and p.hold_waves == held, srcs
+        assert q(n, srcs=srcs, mode=IN, config={"stream_kernel": 1})[1].stream_kernel == 1
+        assert q(n, srcs=srcs, mode=IN, config={"grid_wgs": 7})[1].stream_kernel == 1
+        assert q(n, srcs=srcs, mode=IN, config={"store_policy": 2})[1].stream_kernel == 1
+        assert q(n, srcs=srcs, mode=IN, config={"occupancy_hold": -1})[1].hold_waves == 0
+    for srcs in ([A[1], 0, 0, 0], [0, A[2], A[3], A[4], A[5], A[6]], [A[i] for i in range(1, 6)]):
+        assert q(n, srcs=srcs, mode=IN)[1].stream_kernel == 1, srcs
+    assert q(n, R=3, mode=CH | ar.AR_SRC_WIRE)[1].stream_kernel == 1
+    assert q(n, R=3, mode=CH, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel != 4
+    assert q(n, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 4
     # with a residual (element-wise or a broadcast row): the two-rank kernels for R = 2
     # CHUNKED; the general kernels otherwise
     res = [0x7_0000_0000]
@@ -592,8 +610,9 @@ def test_xcd_placement_map_is_a_permutation(tmp_path):
 
 
 def test_occupancy_hold_in_plans(monkeypatch):
-    """The plan reports the occupancy hold its launches take: by default the two-rank
-    kernels only (18 waves, 14 with a residual); an explicit ar_config.occupancy_hold
+    """The plan reports the occupancy hold its launches take: by default the binary32
+    two-rank kernels (18 waves, 14 with a residual) and the kernels for a few active
+    partials (18, 14 or 10 for two, three or four) only; an explicit ar_config.occupancy_hold
     (or AR_OCCUPANCY_HOLD) holds every streaming launch but never a single-shot one; -1
     holds none; values outside -1..32 are refused."""
     monkeypatch.delenv("AR_OCCUPANCY_HOLD", raising=False)
@@ -608,11 +627,14 @@ def test_occupancy_hold_in_plans(monkeypatch):
                                   ar.AR_MODE_CHUNKED)
     assert rc == ar.AR_OK and p.stream_kernel == 3 and p.hold_waves == 18
     three = dict(dsts=[A[20]], srcs=A[1:4], mode=ar.AR_MODE_CHUNKED)
-    assert q(n, **three)[1].stream_kernel in (1, 2) and q(n, **three)[1].hold_waves == 0
+    assert q(n, **three)[1].stream_kernel == 4 and q(n, **three)[1].hold_waves == 14
+    five = dict(dsts=[A[20]], srcs=A[1:6], mode=ar.AR_MODE_CHUNKED)
+    assert q(n, **five)[1].stream_kernel in (1, 2) and q(n, **five)[1].hold_waves == 0
+    assert q(n, **five, config={"occupancy_hold": 12})[1].hold_waves == 12
     assert q(n, **two, config={"occupancy_hold": -1})[1].hold_waves == 0
     assert q(n, **two, config={"occupancy_hold": 12})[1].hold_waves == 12
     assert q(n, **three, config={"occupancy_hold": 12})[1].hold_waves == 12
-    ss = dict(dsts=[A[20]], srcs=A[1:4], mode=ar.AR_MODE_SINGLE_SHOT)
+    ss = dict(dsts=[A[20]], srcs=A[1:6], mode=ar.AR_MODE_SINGLE_SHOT)
     assert q(4096, **ss, config={"occupancy_hold": 12})[1].stream_kernel == 0
     assert q(4096, **ss, config={"occupancy_hold": 12})[1].hold_waves == 0
     for bad in (-2, 33):

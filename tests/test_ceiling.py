@@ -19,7 +19,7 @@ import pytest
 
 import bench
 
-PATTERNS = [(1, 1), (2, 1), (4, 4), (8, 1)]
+PATTERNS = [(1, 1), (2, 1), (3, 1), (4, 4), (8, 1)]
 TILE = 2048
 
 
@@ -33,7 +33,7 @@ def test_launcher_refuses_invalid_requests_before_any_gpu_call():
     a = [0x10_0000_0000 + i * 0x1_0000_0000 for i in range(12)]   # 16-byte aligned, never dereferenced
     s8, d4 = _arrays(a[:8], a[8:12])
     bad = [
-        (3, 1, 0, 256, 4 * TILE, 0, 0),         # no such pattern
+        (3, 2, 0, 256, 4 * TILE, 0, 0),         # no such pattern
         (2, 2, 0, 256, 4 * TILE, 0, 0),
         (2, 1, 3, 256, 4 * TILE, 0, 0),         # store policy
         (2, 1, 0, 128, 4 * TILE, 0, 0),         # workgroup size
@@ -55,6 +55,8 @@ def test_launcher_refuses_invalid_requests_before_any_gpu_call():
 def test_every_pattern_writes_the_word_sum_to_every_destination():
     import torch
 
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
     lib = bench.ceiling_lib()
     # several placement runs of 512 KiB, a ragged end, and more one-wave workgroups
     # than 256 CUs hold at 14 waves each (below that the hold is not applied)

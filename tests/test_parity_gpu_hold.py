@@ -2,7 +2,8 @@
 what they compute: calls large enough for every hold to apply (the grid fills
 each CU beyond it) give bit-identical outputs with no hold, the automatic hold
 and explicit holds, on the two-rank kernels (plain, element-wise residual,
-broadcast row, row-strided, 16-bit), the register-staged and the LDS-staged
+broadcast row, row-strided, 16-bit), the kernel for a few active partials, the
+register-staged and the LDS-staged
 kernels (contiguous and broadcast schedules, 16-bit layouts), and the automatic
 one matches the oracle.  Each call's plan is checked to name the kernel family
 the case is about.
@@ -113,6 +114,20 @@ def test_16bit_two_rank_kernel_every_hold(ctxs):
     srcs = [t.cpu().numpy().view(np.uint16) for t in h]
     want = oracle.reduce(srcs, ar.AR_BF16, dst_type=ar.AR_BF16)[0]
     assert_bits_equal16(got.view(np.uint16), want, ar.AR_BF16, "two-rank 16-bit vs oracle")
+
+
+def test_few_rank_kernel_every_hold(ctxs):
+    # four ranks, rank 2 inactive: the kernel for a few active partials
+    srcs = wl.random_partials(50_020, 0, 4, N, dist="normal+outliers")
+    srcs[2] = None
+    dev = [None if s is None else to_device(s) for s in srcs]
+    ptrs = [0 if d is None else d for d in dev]
+    out = torch.empty(N, dtype=torch.float32, device="cuda")
+    mode = ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL
+    assert planned_kernel([out], ptrs, N, ar.AR_F32, ar.AR_BF16, mode) == 4
+    got = same_everywhere(ctxs, "four ranks, one inactive (few active partials)",
+                          lambda c: ar.ar_reduce(c, [out], ptrs, N, ar.AR_F32, ar.AR_BF16, mode), out)
+    assert_bits_equal(got, oracle.reduce(srcs, ar.AR_BF16)[0], "few active partials vs oracle")
 
 
 def test_general_kernels_every_hold(ctxs, lds_ctxs):

@@ -175,7 +175,7 @@ def test_case_generator_is_deterministic_and_varied():
         assert rc == ar.AR_OK, (c, ar.ar_status_str(rc))
         kinds.append((int(plan.stream_kernel), int(plan.dst_bytes), c["res_form"]))
     kernels = {k for k, _, _ in kinds}
-    assert {0, 1, 2, 3} <= kernels
+    assert {0, 1, 2, 3, 4} <= kernels
     pair32 = [r for k, b, r in kinds if k == 3 and b == 4]
     assert len(pair32) >= 40 and {"none", "elementwise", "row"} <= set(pair32)
     assert sum(1 for k, b, _ in kinds if k == 3 and b == 2) >= 5
