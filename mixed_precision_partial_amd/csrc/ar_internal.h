@@ -172,9 +172,10 @@ constexpr unsigned kPairResWaves = 14;
 // Resident waves per CU the kernels for two to four active partials are held to
 // by default, by active partials (2, 3, 4): fewer streams in flight per wave
 // leave room for more waves (bench.py --hold-study, the prefill shape on one
-// box, bit-identical outputs: two active of four ranks 15.67 us unheld, 15.45
-// at 18 waves; three ranks 20.26 unheld, 19.76 at 14, 20.03 at 18; four
-// ranks 25.75 unheld, 25.11 at 10, 25.56 at 14).
+// box, bit-identical outputs: two active of four ranks 15.53 us unheld, 15.33
+// at 18 waves, 15.68 at 14; three ranks 20.16 unheld, 19.68 at 14, 19.94 at
+// 18; four ranks with one inactive 20.13 unheld, 19.64 at 14; four ranks
+// 25.42 unheld, 24.83 at 10, 25.28 at 14).
 constexpr unsigned kFewWaves[3] = {18, 14, 10};
 
 // The two-rank contiguous kernels (k_pair, k_pair_res): dst[i] = wire(src0[i])
