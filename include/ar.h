@@ -160,13 +160,16 @@ typedef struct {
                                      are held to, by dynamic LDS the kernels do
                                      not use (asked for only when a launch's grid
                                      fills every CU beyond the hold): 0 automatic
-                                     (the two-rank kernels 18, 14 with a
-                                     residual -- fewer loads in flight per CU
-                                     stream faster on MI355X -- and the general
-                                     kernels unheld), -1 no hold, 1..32 every
-                                     register-, LDS-staged and two-rank launch
-                                     held to that many (single-shot launches are
-                                     never held).  No effect on any result */
+                                     (the binary32 two-rank kernels 18, 14 with
+                                     a residual, the kernels for two to four
+                                     active partials 18, 14 or 10 -- fewer
+                                     loads in flight per CU stream faster on
+                                     MI355X -- and the general kernels and the
+                                     16-bit two-rank kernel unheld), -1 no
+                                     hold, 1..32 every register-, LDS-staged,
+                                     two-rank and few-partial launch held to
+                                     that many (single-shot launches are never
+                                     held).  No effect on any result */
 } ar_config;
 
 /* Create a context on HIP device `hip_device`.
@@ -349,9 +352,16 @@ typedef struct {
                              3 the two-rank kernels (two active binary32
                              partials, one binary32 destination, contiguous
                              or rows of whole 512-element tiles with strides
-                             below 2^32, CHUNKED or SINGLE_SHOT, optionally
-                             an element-wise or broadcast-row residual;
-                             chosen automatically)                        */
+                             below 2^32, optionally an element-wise or
+                             broadcast-row residual; or two active 16-bit
+                             partials into a contiguous destination of
+                             their type, no residual),
+                             4 the kernels for two to four active binary32
+                             partials (three or four ranks, or inactive
+                             ranks among more; one binary32 destination,
+                             contiguous, no residual); 3 and 4 for CHUNKED
+                             or SINGLE_SHOT calls with kept stores and no
+                             forced grid, chosen automatically           */
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */
     int    dst_bytes;     /* bytes per destination element                  */
     int    residual_kind; /* 0 none, 1 element-wise, 2 broadcast row        */
