@@ -880,8 +880,9 @@ def family_study(torch, ar, wl, args, reps: int = 7, calls: int = 1000) -> int:
     timed interleaved, rep by rep, with pre-converted calls (ar.bind_reduce).  The plain call
     is also timed with every second source moved 1 MiB into a larger allocation (the kernels'
     sensitivity to where the buffers sit relative to each other), and two bf16 partials
-    into a bf16 destination (the two-rank 16-bit kernel) with and without a ragged tail.
-    One JSON line."""
+    into a bf16 destination (the two-rank 16-bit kernel) with and without a ragged tail, and
+    three or four fp32 partials (the kernels for a few active partials: three ranks, four with
+    rank 2 inactive, four, three and four with an element-wise residual).  One JSON line."""
     w = wl.WORKLOADS["prefill_bf16"]
     n, S = w.n, max(1, args.sets)
     src = [[torch.from_numpy(p).cuda() for p in wl.partials(w, s)] for s in range(S)]
@@ -979,6 +980,41 @@ def family_study(torch, ar, wl, args, reps: int = 7, calls: int = 1000) -> int:
                          "GB/s": round(6 * m / float(np.median(v)) / 1e3, 1)} for k, v in times.items()}
         log(f"{name}: " + ", ".join(f"{k} {v['us_median']} us" for k, v in out[name].items()))
         del hs, hd, fns
+    # three or four fp32 partials on the prefill shape: the kernels for a few active partials
+    del src, res
+    torch.cuda.empty_cache()
+    fsrc = [[torch.randn(n, device="cuda") for _ in range(4)] for _ in range(S)]
+    fres = [torch.randn(n, device="cuda") for _ in range(S)]
+    inact = ar.AR_SRC_INACTIVE_NULL
+    for name, pick, flags, with_res, nbytes in (
+            ("few_r3", lambda q: q[:3], 0, False, 16 * n),
+            ("few_r4_rank2_inactive", lambda q: [q[0], q[1], None, q[3]], inact, False, 16 * n),
+            ("few_r4", lambda q: q, 0, False, 20 * n),
+            ("few_r3_residual", lambda q: q[:3], 0, True, 20 * n),
+            ("few_r4_residual", lambda q: q, 0, True, 24 * n)):
+        fns = {k: [ar.bind_reduce(c, [dst[s]], pick(fsrc[s]), n, ar.AR_F32, w.wire, ar.AR_MODE_CHUNKED | flags,
+                                  stream=stream, residual=fres[s] if with_res else None) for s in range(S)]
+               for k, c in ctxs.items()}
+        ref = None
+        for k in ctxs:
+            dst[0].fill_(float("nan"))
+            if fns[k][0]() != ar.AR_OK:
+                raise RuntimeError(f"{name} {k}: call failed")
+            torch.cuda.synchronize()
+            bits = dst[0].view(torch.int32).clone()
+            if ref is None:
+                ref = bits
+            elif not torch.equal(bits, ref):
+                raise RuntimeError(f"{name}: {k} differs from the automatic plan's output")
+        times = {k: [] for k in ctxs}
+        for _ in range(reps):
+            for k in ctxs:
+                f = fns[k]
+                times[k].append(timed_us(torch, stream, lambda i: f[i % S](), calls))
+        out[name] = {k: {"us_median": round(float(np.median(v)), 3),
+                         "GB/s": round(nbytes / float(np.median(v)) / 1e3, 1)} for k, v in times.items()}
+        log(f"{name}: " + ", ".join(f"{k} {v['us_median']} us" for k, v in out[name].items()))
+        del fns
     torch.cuda.synchronize()
     for c in ctxs.values():
         ar.ar_free(c)
@@ -992,7 +1028,8 @@ def hold_study(torch, ar, wl, args, reps: int = 7) -> int:
     (2048 x 4096 in rows of 4608 / 4352: plain, strided residual, bias row), each on the
     two-rank kernels unheld (-1), held to 14, 16, 18 or 20 waves per CU, and automatic (0);
     the prefill shape with three ranks, four with rank 2 inactive, four, and two active of
-    four, on the kernels for a few active partials unheld, held to 10, 14 or 18, and automatic;
+    four, and with an element-wise residual, on the kernels for a few active partials unheld,
+    held to 8, 10, 14 or 18, and automatic;
     the 4-rank broadcast (cfg 4), the bf16 -> bf16 prefill shape and R = 8 fp32 partials on
     their automatic general kernels unheld and held to 8, 12 or 16 waves.  Outputs are
     compared bit for bit across holds before timing; holds are timed interleaved, rep by
@@ -1040,19 +1077,26 @@ def hold_study(torch, ar, wl, args, reps: int = 7) -> int:
                 lambda: dst[0].view(torch.int32))
     del src, dst, res, bound
     torch.cuda.empty_cache()
-    few_holds = [-1, 10, 14, 18, 0]
+    few_holds = [-1, 8, 10, 14, 18, 0]
     f_src = [[torch.randn(n, device="cuda") for _ in range(4)] for _ in range(S)]
     f_dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(S)]
     inact = ar.AR_SRC_INACTIVE_NULL
-    for form, pick, flags, nbytes in (("r3", lambda q: q[:3], 0, 16 * n),
-                                      ("r4_rank2_inactive", lambda q: [q[0], q[1], None, q[3]], inact, 16 * n),
-                                      ("r4", lambda q: q, 0, 20 * n),
-                                      ("r4_two_active", lambda q: [None, q[1], None, q[3]], inact, 12 * n)):
+    f_res = [torch.randn(n, device="cuda") for _ in range(S)]
+    for form, pick, flags, nbytes, with_res in (
+            ("r3", lambda q: q[:3], 0, 16 * n, False),
+            ("r4_rank2_inactive", lambda q: [q[0], q[1], None, q[3]], inact, 16 * n, False),
+            ("r4", lambda q: q, 0, 20 * n, False),
+            ("r4_two_active", lambda q: [None, q[1], None, q[3]], inact, 12 * n, False),
+            ("r4_two_active_residual", lambda q: [None, q[1], None, q[3]], inact, 16 * n, True),
+            ("r3_residual", lambda q: q[:3], 0, 20 * n, True),
+            ("r4_residual", lambda q: q, 0, 24 * n, True)):
         fb = {h: [ar.bind_reduce(ctxs[h], [f_dst[i]], pick(f_src[i]), n, ar.AR_F32, w.wire,
-                                 ar.AR_MODE_CHUNKED | flags, stream=stream) for i in range(S)] for h in few_holds}
+                                 ar.AR_MODE_CHUNKED | flags, stream=stream,
+                                 residual=f_res[i] if with_res else None) for i in range(S)]
+              for h in few_holds}
         measure(f"few_{form}", few_holds, 1000, lambda h, k, fb=fb: fb[h][k % S](), nbytes,
                 lambda: f_dst[0].view(torch.int32))
-    del f_src, f_dst
+    del f_src, f_dst, f_res
     torch.cuda.empty_cache()
     rows, cols, ss, ds = 2048, 4096, 4608, 4352
     R6 = 6

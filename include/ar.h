@@ -162,7 +162,8 @@ typedef struct {
                                      fills every CU beyond the hold): 0 automatic
                                      (the binary32 two-rank kernels 18, 14 with
                                      a residual, the kernels for two to four
-                                     active partials 18, 14 or 10 -- fewer
+                                     active partials 18, 14 or 10, with a
+                                     residual 14, 10 or 8 -- fewer
                                      loads in flight per CU stream faster on
                                      MI355X -- and the general kernels and the
                                      16-bit two-rank kernel unheld), -1 no
@@ -270,9 +271,11 @@ int ar_reduce_staged_static(ar_ctx *ctx, void *const *dst, const void *const *sr
  * of ar_reduce; residual NULL, residual_len 0 or not dividing n ->
  * AR_ERR_INVALID (n = 0 is a no-op and checks only residual != NULL).  Calls
  * with a residual run on the two-rank kernels (two fp32 partials into one
- * fp32 destination, CHUNKED or SINGLE_SHOT), on the single-shot kernel in
- * other SINGLE_SHOT calls, on the LDS-staged kernels in the broadcast
- * schedule, and on the register-staged kernels otherwise (unless
+ * fp32 destination, CHUNKED or SINGLE_SHOT), on the kernels for two to four
+ * active fp32 partials (an element-wise residual, three or four ranks or
+ * inactive ones among more, CHUNKED or SINGLE_SHOT), on the single-shot
+ * kernel in other SINGLE_SHOT calls, on the LDS-staged kernels in the
+ * broadcast schedule, and on the register-staged kernels otherwise (unless
  * stream_kernel forces a family). */
 int ar_reduce_add(ar_ctx *ctx, void *const *dst, const void *const *srcs, int R, size_t n,
                   ar_dtype dst_type, ar_dtype wire_type, unsigned mode, const void *residual,
@@ -359,7 +362,8 @@ typedef struct {
                              4 the kernels for two to four active binary32
                              partials (three or four ranks, or inactive
                              ranks among more; one binary32 destination,
-                             contiguous, no residual); 3 and 4 for CHUNKED
+                             contiguous, no residual or an element-wise
+                             one); 3 and 4 for CHUNKED
                              or SINGLE_SHOT calls with kept stores and no
                              forced grid, chosen automatically           */
     unsigned active_mask; /* bit r set: rank r has a partial (not inactive)   */

@@ -446,10 +446,11 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
             plan->stream_kernel = 3;
         }
         // the kernels for two to four active binary32 partials: three or four
-        // ranks, or two to four active ones among more, no residual,
-        // contiguous, the two-rank kernels' conditions otherwise
+        // ranks, or two to four active ones among more, no residual or an
+        // element-wise one, contiguous, the two-rank kernels' conditions
+        // otherwise
         if ((resolved == AR_MODE_CHUNKED || resolved == AR_MODE_SINGLE_SHOT) && cfg.stream_kernel == 0 &&
-            rows == nullptr && res_kind == 0 && !src_wire && dst_bytes == 4 && !plan->store_nt &&
+            rows == nullptr && res_kind <= 1 && !src_wire && dst_bytes == 4 && !plan->store_nt &&
             cfg.grid_wgs == 0 && n_active >= 2 && n_active <= 4 && !(R == 2 && active == 0x3u)) {
             plan->stream_kernel = 4;
         }
@@ -464,7 +465,8 @@ int validate_and_plan(const Config &cfg, void *const *dst, const void *const *sr
         } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 3 && dst_bytes == 4) {
             plan->hold_waves = static_cast<int>(res_kind != 0 ? mpp::kPairResWaves : mpp::kPairWaves);
         } else if (cfg.occupancy_hold == 0 && plan->stream_kernel == 4) {
-            plan->hold_waves = static_cast<int>(mpp::kFewWaves[n_active - 2]);
+            plan->hold_waves = static_cast<int>(res_kind != 0 ? mpp::kFewResWaves[n_active - 2]
+                                                              : mpp::kFewWaves[n_active - 2]);
         }
     }
     return AR_OK;
@@ -689,8 +691,9 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
             const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);
             const void *piece[4] = {};
             for (int a = 0; a < A; ++a) piece[a] = static_cast<const char *>(act[a]) + p0 * sb;
+            const void *rp = res.ptr == nullptr ? nullptr : static_cast<const char *>(res.ptr) + p0 * db;
             if (int rc = hip_status(mpp::launch_few(wire_type, A, len, static_cast<char *>(dst[0]) + p0 * db, piece,
-                                                    zmask, xcd_run_for(c->cfg, A, false),
+                                                    zmask, rp, xcd_run_for(c->cfg, A, false),
                                                     static_cast<unsigned>(plan.hold_waves), cu_limits(c), stream))) {
                 return rc;
             }

@@ -1395,7 +1395,9 @@ __global__ __launch_bounds__(kPairBlock) void k_pair_res(unsigned tiles, unsigne
 // every value unchanged, so the fold adds z[g] = +0.0 or -0.0 at each gap g
 // (before active partial g, and after the last at g = A) according to
 // whether an inactive rank lies there (bit g of zmask): bit-identical with
-// the fold over all R ranks, with no branch between the loads.
+// the fold over all R ranks, with no branch between the loads.  RES: an
+// element-wise binary32 residual added after the fold, read once like the
+// partials.
 template <int W, int A>
 __device__ __forceinline__ u32x4 few_part(const u32x4 (&v)[A], const float (&z)[A + 1]) {
     float x[A][4];
@@ -1417,10 +1419,10 @@ __device__ __forceinline__ u32x4 few_part(const u32x4 (&v)[A], const float (&z)[
     return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-template <int W, int A>
+template <int W, int A, bool RES>
 __global__ __launch_bounds__(kPairBlock) void k_few(unsigned tiles, unsigned rem, float *dst, const float *s0,
                                                     const float *s1, unsigned lc, const float *s2,
-                                                    const float *s3, unsigned zmask) {
+                                                    const float *s3, unsigned zmask, const float *res) {
     static_assert(A >= 2 && A <= 4, "two to four active partials");
     const int lane = threadIdx.x & (kWave - 1);
     const unsigned grid = tiles + (rem != 0 ? 1u : 0u);
@@ -1435,13 +1437,14 @@ __global__ __launch_bounds__(kPairBlock) void k_few(unsigned tiles, unsigned rem
             // folds, then the guarded stores (see reduce_scalar)
             constexpr int K = kWaveTile / kWave;
             const size_t t = static_cast<size_t>(tiles) * kWaveTile;
-            float x[A][K];
+            float x[A][K], r[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const unsigned e0 = lane + kWave * k;
                 const unsigned e = e0 < rem ? e0 : rem - 1;
 #pragma unroll
                 for (int a = 0; a < A; ++a) x[a][k] = s[a][t + e];
+                if constexpr (RES) r[k] = res[t + e];
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -1454,6 +1457,7 @@ __global__ __launch_bounds__(kPairBlock) void k_few(unsigned tiles, unsigned rem
 #pragma unroll
                 for (int a = 1; a < A; ++a) acc = (acc + z[a]) + x[a][k];
                 x[0][k] = acc + z[A];
+                if constexpr (RES) x[0][k] = x[0][k] + r[k];
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -1464,14 +1468,22 @@ __global__ __launch_bounds__(kPairBlock) void k_few(unsigned tiles, unsigned rem
         return;
     }
     const size_t t = static_cast<size_t>(w) * kWaveTile;
-    u32x4 v[2][A];
+    u32x4 v[2][A], rv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int a = 0; a < A; ++a) v[j][a] = load16<true>(s[a] + t + 256 * j + 4 * lane);
+    if constexpr (RES) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) rv[j] = load16<true>(res + t + 256 * j + 4 * lane);
+    }
     float *out = dst + t;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) store16_wt(out, kWaveTile * 4, (256 * j + 4 * lane) * 4, few_part<W, A>(v[j], z));
+    for (int j = 0; j < 2; ++j) {
+        u32x4 o = few_part<W, A>(v[j], z);
+        if constexpr (RES) o = add_res(o, rv[j]);
+        store16_wt(out, kWaveTile * 4, (256 * j + 4 * lane) * 4, o);
+    }
 }
 
 // Two-rank kernels over row-strided tensors whose rows are whole wave tiles
@@ -1618,8 +1630,8 @@ extern const void *const kSingleShot[2][2][kCombos][kBuckets];
 // two-rank contiguous kernels, indexed by [residual kind][wire type (ar_dtype)]
 extern const void *const kPair[5][3];
 extern const void *const kPair16[2];   // [0] fp16, [1] bf16
-// kernels for two to four active binary32 partials, [active partials - 2][wire type]
-extern const void *const kFew[3][3];
+// kernels for two to four active binary32 partials, [element-wise residual][active partials - 2][wire type]
+extern const void *const kFew[2][3][3];
 // two-rank row-strided kernels, [residual kind][power-of-two tiles per row][wire type]
 extern const void *const kPairRows[3][2][3];
 extern StreamTable kStreamReg, kStreamRegM, kStreamRegRes, kStreamRegResM, kStreamLds, kStreamLdsM, kStreamLdsRes,

@@ -177,6 +177,10 @@ constexpr unsigned kPairResWaves = 14;
 // 18; four ranks with one inactive 20.13 unheld, 19.64 at 14; four ranks
 // 25.42 unheld, 24.83 at 10, 25.28 at 14).
 constexpr unsigned kFewWaves[3] = {18, 14, 10};
+// and with an element-wise residual, one more read stream (the same study:
+// two active of four 20.32 us unheld, 19.99 at 14; three ranks 25.80 unheld,
+// 25.12 at 10; four ranks 31.47 unheld, 30.48 at 8, 30.70 at 10)
+constexpr unsigned kFewResWaves[3] = {14, 10, 8};
 
 // The two-rank contiguous kernels (k_pair, k_pair_res): dst[i] = wire(src0[i])
 // + wire(src1[i]) in binary32, then + res[i] (res_kind 1, element-wise) or
@@ -202,12 +206,14 @@ hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const 
 // fold in rank order of wire(srcs[a][i]) over the `active` compacted active
 // partials, with +0.0 added at every gap g (before active partial g; g =
 // active after the last) whose bit g is set in zmask, where the fold over all
-// ranks meets inactive ones, for i < n (n <= kMaxLaunchElems), wire AR_F32,
+// ranks meets inactive ones, then + res[i] when res is not NULL (an
+// element-wise residual), for i < n (n <= kMaxLaunchElems), wire AR_F32,
 // AR_F16 or AR_BF16; one 1-D launch on `stream`, XCD runs of about run_elems
 // elements, every CU held to `hold_waves` resident waves (0: no hold).  Every
 // pointer is a binary32 device array, 16-byte aligned.
 hipError_t launch_few(int wire, int active, size_t n, void *dst, const void *const *srcs, unsigned zmask,
-                      size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream);
+                      const void *res, size_t run_elems, unsigned hold_waves, const CuLimits &cu,
+                      hipStream_t stream);
 
 // The two-rank kernels over row-strided tensors (k_pair_rows): row i, column
 // j of the destination = wire(src0) + wire(src1) (+ the residual: res_kind 1

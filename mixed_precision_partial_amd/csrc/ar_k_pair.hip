@@ -1,6 +1,6 @@
 // ar_k_pair.hip -- two-rank kernel instances: contiguous [residual kind][wire type], row-strided
 // [residual kind][power-of-two tiles per row][wire type], 16-bit into 16-bit [fp16, bf16]; and the
-// kernels for two to four active binary32 partials [active partials - 2][wire type].
+// kernels for two to four active binary32 partials [element-wise residual][active partials - 2][wire type].
 #include "ar_device.h"
 
 namespace mpp {
@@ -27,10 +27,11 @@ const void *const kPairRows[3][2][3] = {MPP_PAIR_ROWS(0), MPP_PAIR_ROWS(1), MPP_
 const void *const kPair16[2] = {reinterpret_cast<const void *>(&k_pair16<AR_F16>),
                                 reinterpret_cast<const void *>(&k_pair16<AR_BF16>)};
 
-#define MPP_FEW_ROW(A)                                                                          \
-    {reinterpret_cast<const void *>(&k_few<AR_F32, A>), reinterpret_cast<const void *>(&k_few<AR_F16, A>), \
-     reinterpret_cast<const void *>(&k_few<AR_BF16, A>)}
-const void *const kFew[3][3] = {MPP_FEW_ROW(2), MPP_FEW_ROW(3), MPP_FEW_ROW(4)};
+#define MPP_FEW_ROW(A, RES)                                                                       \
+    {reinterpret_cast<const void *>(&k_few<AR_F32, A, RES>), reinterpret_cast<const void *>(&k_few<AR_F16, A, RES>), \
+     reinterpret_cast<const void *>(&k_few<AR_BF16, A, RES>)}
+const void *const kFew[2][3][3] = {{MPP_FEW_ROW(2, false), MPP_FEW_ROW(3, false), MPP_FEW_ROW(4, false)},
+                                   {MPP_FEW_ROW(2, true), MPP_FEW_ROW(3, true), MPP_FEW_ROW(4, true)}};
 #undef MPP_FEW_ROW
 
 }  // namespace mpp

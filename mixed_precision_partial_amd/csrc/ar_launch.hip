@@ -146,7 +146,8 @@ hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const 
 }
 
 hipError_t launch_few(int wire, int active, size_t n, void *dst, const void *const *srcs, unsigned zmask,
-                      size_t run_elems, unsigned hold_waves, const CuLimits &cu, hipStream_t stream) {
+                      const void *res, size_t run_elems, unsigned hold_waves, const CuLimits &cu,
+                      hipStream_t stream) {
     if (wire < AR_F32 || wire > AR_BF16 || active < 2 || active > 4 || n == 0 || n > kMaxLaunchElems ||
         srcs == nullptr || zmask >= (1u << (active + 1))) {
         return hipErrorInvalidValue;
@@ -161,8 +162,9 @@ hipError_t launch_few(int wire, int active, size_t n, void *dst, const void *con
     const unsigned grid = tiles + (rem != 0 ? 1u : 0u);
     unsigned lc = xcd_map_lc(grid, kWaveTile, run_elems);
     float *d = static_cast<float *>(dst);
-    void *args[] = {&tiles, &rem, &d, &s[0], &s[1], &lc, &s[2], &s[3], &zmask};
-    return hipLaunchKernel(kFew[active - 2][wire], dim3(grid), dim3(kPairBlock), args,
+    const float *r = static_cast<const float *>(res);
+    void *args[] = {&tiles, &rem, &d, &s[0], &s[1], &lc, &s[2], &s[3], &zmask, &r};
+    return hipLaunchKernel(kFew[res != nullptr ? 1 : 0][active - 2][wire], dim3(grid), dim3(kPairBlock), args,
                            hold_lds_bytes(cu, grid, hold_waves), stream);
 }
 

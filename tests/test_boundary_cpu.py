@@ -264,13 +264,15 @@ def test_stream_kernel_choice():
     assert q(n, R=3, mode=CH, wire=ar.AR_BF16, dst_type=ar.AR_BF16)[1].stream_kernel != 4
     assert q(n, R=3, mode=ar.AR_MODE_SINGLE_SHOT)[1].stream_kernel == 4
     # with a residual (element-wise or a broadcast row): the two-rank kernels for R = 2
-    # CHUNKED; the general kernels otherwise
+    # CHUNKED; for R = 3 the kernel for a few active partials with an element-wise one (held
+    # to 10 waves), the general kernels with a row
     res = [0x7_0000_0000]
     for res_len in (n, 4096):
         rc, p = ar.ar_plan_query_add(A[20:21], A[1:3], n, ar.AR_F32, ar.AR_BF16, CH, res[0], res_len)
         assert rc == ar.AR_OK and p.stream_kernel == 3 and p.residual_kind == (1 if res_len == n else 2)
         rc, p = ar.ar_plan_query_add(A[20:21], A[1:4], n, ar.AR_F32, ar.AR_BF16, CH, res[0], res_len)
-        assert rc == ar.AR_OK and p.stream_kernel == 1
+        assert rc == ar.AR_OK and p.stream_kernel == (4 if res_len == n else 1)
+        assert p.hold_waves == (10 if res_len == n else 0)
         rc, p = ar.ar_plan_query_add(A[20:22], A[1:3], n, ar.AR_F32, ar.AR_BF16, BC, res[0], res_len)
         assert rc == ar.AR_OK and p.stream_kernel == 2
     # row-strided: the two-rank kernels when every row is whole wave tiles

@@ -58,26 +58,39 @@ def partials(seed: int, R: int, n: int) -> list[np.ndarray]:
     return p
 
 
-def run(ctx, active, n, wire, mode, seed, in_place=False):
+def run(ctx, active, n, wire, mode, seed, in_place=False, with_res=False):
     R = len(active)
     srcs = partials(seed, R, n)
+    residual = None
+    if with_res:
+        residual = wl.residual(seed + 1, 0, n, ar.AR_F32, dist="wide")
+        residual[:32] = -0.0          # -0.0 + -0.0 keeps the sign; +0.0 + -0.0 does not
+
     used = [s if a else None for s, a in zip(srcs, active)]
     ts = [to_device(s) if a else None for s, a in zip(srcs, active)]
     flags = 0 if all(active) else ar.AR_SRC_INACTIVE_NULL
     first = next(r for r, a in enumerate(active) if a)
     dst = None if in_place else GuardedDst(n)
     dptr = ts[first] if in_place else dst.ptr()
-    rc, plan = ar.ar_plan_query([dptr], [0 if t is None else t for t in ts], n, ar.AR_F32, wire, mode | flags)
-    what = f"active={active} n={n} wire={wire} mode={mode} in_place={in_place}"
+    ptrs = [0 if t is None else t for t in ts]
+    what = f"active={active} n={n} wire={wire} mode={mode} in_place={in_place} residual={with_res}"
+    if residual is None:
+        rc, plan = ar.ar_plan_query([dptr], ptrs, n, ar.AR_F32, wire, mode | flags)
+    else:
+        rd = to_device(residual)
+        rc, plan = ar.ar_plan_query_add([dptr], ptrs, n, ar.AR_F32, wire, mode | flags, rd, n)
     assert rc == ar.AR_OK and plan.stream_kernel == 4, what
     log_case(what)
-    ar.ar_reduce(ctx, [dptr], [0 if t is None else t for t in ts], n, ar.AR_F32, wire, mode | flags)
+    if residual is None:
+        ar.ar_reduce(ctx, [dptr], ptrs, n, ar.AR_F32, wire, mode | flags)
+    else:
+        ar.ar_reduce_add(ctx, [dptr], ptrs, n, ar.AR_F32, wire, mode | flags, rd, n)
     torch.cuda.synchronize()
-    want = oracle.reduce(used, wire)[0]
+    want = oracle.reduce(used, wire, residual=residual)[0]
     got = ts[first].cpu().numpy() if in_place else dst.result()
     assert_bits_equal(got, want, what)
     # the signed zeros are compared bit for bit too: -0.0 survives only without inactive ranks
-    assert np.signbit(want[:64]).all() == all(active), what
+    assert np.signbit(want[:32]).all() == all(active), what
 
 
 @pytest.mark.parametrize("active", PATTERNS, ids=lambda a: "".join(map(str, a)))
@@ -86,6 +99,9 @@ def test_rank_patterns(ctx, active):
         for wire in WIRES:
             for mode in (ar.AR_MODE_CHUNKED, ar.AR_MODE_SINGLE_SHOT):
                 run(ctx, active, n, wire, mode, seed=60_000 + 97 * i + wire)
+        # with an element-wise residual
+        run(ctx, active, n, ar.AR_BF16, ar.AR_MODE_CHUNKED, seed=62_000 + 97 * i, with_res=True)
+        run(ctx, active, n, ar.AR_F16, ar.AR_MODE_SINGLE_SHOT, seed=62_500 + 97 * i, with_res=True)
 
 
 def test_prefill_size_and_in_place(ctx):
@@ -95,4 +111,7 @@ def test_prefill_size_and_in_place(ctx):
     run(ctx, (1, 1, 0, 1), n + 1000, ar.AR_F16, ar.AR_MODE_AUTO, seed=61_100)
     for active in ((1, 1, 1), (0, 1, 1, 1), (1, 0, 1, 1, 0)):
         run(ctx, active, (1 << 20) + 37, ar.AR_BF16, ar.AR_MODE_CHUNKED, seed=61_200, in_place=True)
+        run(ctx, active, (1 << 20) + 37, ar.AR_BF16, ar.AR_MODE_CHUNKED, seed=61_300, in_place=True,
+            with_res=True)
+    run(ctx, (1, 1, 1, 1), n, ar.AR_BF16, ar.AR_MODE_CHUNKED, seed=61_400, with_res=True)
     torch.cuda.empty_cache()

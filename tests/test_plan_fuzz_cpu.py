@@ -131,20 +131,23 @@ def check_plan(plan, R, n, dst_type, wire_type, mode, srcs, resolved, res_kind, 
               narrow and res_kind == 0)
     assert (plan.stream_kernel == 3) == (pair or pair16)
     # the kernels for a few active partials: two to four active binary32 partials (other than
-    # the two-rank case) into one binary32 destination, no residual, kept stores
+    # the two-rank case) into one binary32 destination, no residual or an element-wise one,
+    # kept stores
     few = (resolved in (ar.AR_MODE_CHUNKED, ar.AR_MODE_SINGLE_SHOT) and 2 <= n_active <= 4 and
            not (R == 2 and n_active == 2) and not mode & ar.AR_SRC_WIRE and dst_type == F32 and
-           res_kind == 0 and not plan.store_nt)
+           res_kind <= 1 and not plan.store_nt)
     assert (plan.stream_kernel == 4) == few
     # the default occupancy hold: the binary32 two-rank kernels, 18 waves, 14 with a residual,
-    # and the kernels for a few active partials, 18, 14 or 10 for two, three or four
-    assert plan.hold_waves == ((14 if res_kind else 18) if pair else ({2: 18, 3: 14, 4: 10}[n_active] if few else 0))
+    # and the kernels for a few active partials, 18, 14 or 10 for two, three or four (14, 10
+    # or 8 with a residual)
+    few_hold = ({2: 14, 3: 10, 4: 8} if res_kind else {2: 18, 3: 14, 4: 10}).get(n_active, 0)
+    assert plan.hold_waves == ((14 if res_kind else 18) if pair else (few_hold if few else 0))
     if resolved == ar.AR_MODE_SINGLE_SHOT:
         assert plan.chunk_elems == n and plan.stream_kernel == (3 if pair or pair16 else 4 if few else 0)
     else:
         assert plan.chunk_elems % WAVE_TILE == 0 and plan.chunk_elems <= MAX_LAUNCH
         assert plan.stream_kernel in ((3,) if pair or pair16 else (4,) if few else (1, 2))
-        if res_kind and not pair:
+        if res_kind and not pair and not few:
             # with a residual: LDS-staged for the broadcast schedule, register-staged otherwise
             assert plan.stream_kernel == (2 if resolved == ar.AR_MODE_RS_BCAST else 1)
         if resolved == ar.AR_MODE_RS_BCAST:
