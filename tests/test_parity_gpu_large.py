@@ -119,6 +119,42 @@ def test_two_rank_16bit_beyond_one_launch(ctx):
     free()
 
 
+def test_few_partials_beyond_one_launch(ctx):
+    """n = 2^30 + 2^20 + 4099, four fp32 partials with rank 2 inactive (the kernel for a few
+    active partials), with and without an element-wise residual: every launch piece takes
+    its own slice of the compacted sources and of the residual."""
+    n = LAUNCH + (1 << 20) + 4099
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20_006)
+    srcs = [None if r == 2 else torch.randn(n, device="cuda", generator=g) for r in range(4)]
+    res = torch.randn(n, device="cuda", generator=g)
+    ptrs = [0 if s is None else s for s in srcs]
+    mode = ar.AR_MODE_CHUNKED | ar.AR_SRC_INACTIVE_NULL
+    fake = [0x20_0000_0000, 0x30_0000_0000, 0, 0x40_0000_0000]
+    rc, plan = ar.ar_plan_query([0x10_0000_0000], fake, n, ar.AR_F32, ar.AR_BF16, mode)
+    assert rc == ar.AR_OK and plan.stream_kernel == 4
+    rc, plan = ar.ar_plan_query_add([0x10_0000_0000], fake, n, ar.AR_F32, ar.AR_BF16, mode, 0x50_0000_0000, n)
+    assert rc == ar.AR_OK and plan.stream_kernel == 4
+    idx = sample_indices(n, [LAUNCH, LAUNCH - 512, 1 << 29, n - 4099], 10)
+    s_host = [None if s is None else gather(s, idx) for s in srcs]
+    r_host = gather(res, idx)
+    out = torch.empty(n, device="cuda")
+    for with_res in (False, True):
+        what = f"n={n} four ranks, rank 2 inactive, residual={with_res}"
+        log_case(what)
+        out.fill_(float("nan"))
+        if with_res:
+            ar.ar_reduce_add(ctx, [out], ptrs, n, ar.AR_F32, ar.AR_BF16, mode, res, n)
+        else:
+            ar.ar_reduce(ctx, [out], ptrs, n, ar.AR_F32, ar.AR_BF16, mode)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any().item(), f"{what}: some element left unwritten"
+        want = oracle.reduce(s_host, ar.AR_BF16, residual=r_host if with_res else None)[0]
+        assert_bits_equal(gather(out, idx), want, what)
+    del out, srcs, res
+    free()
+
+
 def test_beyond_one_launch_row_residual(ctx):
     """n = 2^30 + 8 with a broadcast row of 24 elements (which does not divide 2^30): the
     second launch piece starts 16 elements into the row.  Two fp32 partials, bf16 wire."""
