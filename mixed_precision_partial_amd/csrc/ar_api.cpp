@@ -678,14 +678,7 @@ int run_device(ar_ctx *c, const ar_plan &plan, void *const *dst, const void *con
         // the gaps where inactive ranks add +0.0; one 1-D launch per piece
         const void *act[4] = {};
         unsigned zmask = 0;
-        int A = 0;
-        for (int r = 0; r < R; ++r) {
-            if (srcs[r] == nullptr) {
-                zmask |= 1u << A;
-            } else {
-                act[A++] = srcs[r];
-            }
-        }
+        const int A = mpp::few_compact(srcs, R, act, &zmask);
         if (A < 2 || A > 4) return AR_ERR_INVALID;
         for (size_t p0 = 0; p0 < n; p0 += mpp::kMaxLaunchElems) {
             const size_t len = std::min(mpp::kMaxLaunchElems, n - p0);

@@ -202,6 +202,25 @@ hipError_t launch_pair(int wire, int res_kind, size_t n, void *dst, const void *
 hipError_t launch_pair16(int wire, size_t n, void *dst, const void *src0, const void *src1, size_t run_elems,
                          unsigned hold_waves, const CuLimits &cu, hipStream_t stream);
 
+// The active partials of a call with R ranks (srcs[r] == nullptr: inactive),
+// compacted in rank order into act[0 .. min(A, 4)), and the gaps that hold
+// inactive ranks: bit g of *zmask is set when an inactive rank lies before
+// active partial g (g = A: after the last).  Returns A, the active count.
+inline int few_compact(const void *const *srcs, int R, const void *act[4], unsigned *zmask) {
+    int A = 0;
+    unsigned z = 0;
+    for (int r = 0; r < R; ++r) {
+        if (srcs[r] == nullptr) {
+            z |= 1u << A;
+        } else {
+            if (A < 4) act[A] = srcs[r];
+            ++A;
+        }
+    }
+    *zmask = z;
+    return A;
+}
+
 // The kernels for two to four active binary32 partials (k_few): dst[i] = the
 // fold in rank order of wire(srcs[a][i]) over the `active` compacted active
 // partials, with +0.0 added at every gap g (before active partial g; g =

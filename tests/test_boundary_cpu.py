@@ -668,6 +668,24 @@ def test_occupancy_hold_bytes(tmp_path):
     assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr
 
 
+def test_few_partial_gaps():
+    """tests/c_abi/few_check.cpp, built with hipcc as host code against the library's
+    internal header: for every placement of 2 to 4 active ranks among 2 to 16, the
+    compacted fold with +0.0 at the gaps that hold inactive ranks gives the bits of the
+    fold over every rank with +0.0 for the inactive ones, signed zeros included."""
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(__import__("tempfile").mkdtemp()) + "/few_check"
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    cmd = [hipcc, "-O1", "-std=c++17", "-ffp-contract=off", "-I", os.path.join(root, "include"),
+           "-I", os.path.join(root, "mixed_precision_partial_amd", "csrc"),
+           os.path.join(root, "tests", "c_abi", "few_check.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.startswith("OK"), out.stdout + out.stderr
+
+
 def test_binding_refuses_short_pointer_lists():
     """The library reads R destination pointers in the broadcast schedule (and R
     source pointers always): the binding refuses shorter lists before the call,
